@@ -1,0 +1,281 @@
+#!/usr/bin/env python3
+"""Paged decode benchmark on one MI355X.
+
+A step is one decode step of one attention layer over the whole batch,
+through every stage of the path:
+  1. host allocator: one new slot per sequence (batch append, all or
+     nothing; copy-on-write pairs if a shared block is hit);
+  2. block tables, lengths and slots to the device (pinned, asynchronous);
+  3. block copies for copy-on-write pairs (none unless blocks are shared);
+  4. paged_kv_append of the step's new K/V rows;
+  5. paged_attention_decode: split-K partition kernel, then the merge.
+The cache is resident in HBM before timing starts.  ``value`` is the KV
+bytes the decode reads per step (sum over sequences of context_len * Hkv *
+head_dim * 2 * element size) divided by the wall time of a whole step.
+``roofline`` reports the partition kernel alone, timed with HIP events on
+the stream it runs on.  ``cpu_baseline`` times the float64 CPU oracle on a
+small sample of the same workload (reported only).
+
+Usage: python bench.py [--steps K] [--warmup W] [--workload NAME]
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, published
+METRIC = ("paged decode KV-read GB/s (% of HBM peak) + tokens/s, LLaMA-7B layer, batch 64")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama7b_bf16")
+    ap.add_argument("--partition-size", type=int, default=None,
+                    help="split-K partition in tokens (default: the workload's, else the library's)")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle timing (profiling runs)")
+    return ap.parse_args()
+
+
+def kv_bytes(w, lens):
+    return int(np.sum(lens, dtype=np.int64)) * w.num_kv_heads * w.head_dim * 2 * w.elem_bytes
+
+
+def setup(w, pkv, workloads, torch, dev):
+    p = workloads.plan(w)
+    shape = (p.num_blocks, w.num_kv_heads, w.block_size, w.head_dim)
+    kc = torch.zeros(shape, dtype=w.dtype, device=dev)
+    vc = torch.zeros(shape, dtype=w.dtype, device=dev)
+    alloc = pkv.BlockAllocator(p.num_blocks, w.block_size, p.free_order)
+
+    def on_copy(pairs):
+        src = torch.tensor([a for a, _ in pairs], dtype=torch.int32, device=dev)
+        dst = torch.tensor([b for _, b in pairs], dtype=torch.int32, device=dev)
+        pkv.copy_blocks(kc, vc, src, dst)
+
+    def on_append(i, seq, n, slots):
+        k, v = workloads.kv_rows(w, i, n)
+        pkv.paged_kv_append(workloads.to_dtype(k, w.dtype).to(dev),
+                            workloads.to_dtype(v, w.dtype).to(dev), kc, vc,
+                            torch.from_numpy(slots).to(dev))
+
+    workloads.run_schedule(p.ops, alloc, on_append, on_copy)
+    torch.cuda.synchronize()
+    return p, kc, vc, alloc
+
+
+def gpu_run(args, w, torch, pkv, workloads):
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    part = w.partition_size if args.partition_size is None else args.partition_size
+    p, kc, vc, alloc = setup(w, pkv, workloads, torch, dev)
+    seqs = p.seqs
+    b = len(seqs)
+    total_steps = args.warmup + args.steps
+    max_len = int(max(alloc.seq_len(s) for s in seqs)) + total_steps
+    max_blocks = -(-max_len // w.block_size)
+
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed + 99)
+    k_new = (torch.randn((total_steps, b, w.num_kv_heads, w.head_dim), generator=gen, device=dev)
+             * w.std).to(w.dtype)
+    v_new = (torch.randn((total_steps, b, w.num_kv_heads, w.head_dim), generator=gen, device=dev)
+             * w.std).to(w.dtype)
+    q = (torch.randn((total_steps, b, w.num_heads, w.head_dim), generator=gen, device=dev)
+         * w.std).to(w.dtype)
+    out = torch.empty((b, w.num_heads, w.head_dim), dtype=torch.float32, device=dev)
+    ws_bytes = pkv.paged_attention_decode_workspace_size(b, w.num_heads, w.head_dim, max_len, part)
+    workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+
+    tables_d = torch.empty((b, max_blocks), dtype=torch.int32, device=dev)
+    lens_d = torch.empty(b, dtype=torch.int32, device=dev)
+    slots_d = torch.empty(b, dtype=torch.int32, device=dev)
+    pinned = [dict(tables=torch.empty((b, max_blocks), dtype=torch.int32, pin_memory=True),
+                   lens=torch.empty(b, dtype=torch.int32, pin_memory=True),
+                   slots=torch.empty(b, dtype=torch.int32, pin_memory=True),
+                   done=torch.cuda.Event()) for _ in range(2)]
+    for buf in pinned:
+        buf["done"].record()
+    ones = np.ones(b, dtype=np.int32)
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(total_steps)]
+    step_bytes = []
+
+    def step(i):
+        slots, pairs = alloc.append_batch(seqs, ones)                      # 1
+        tables, lens = alloc.build_block_tables(seqs, max_blocks)
+        buf = pinned[i % 2]
+        buf["done"].synchronize()            # the copy issued two steps ago is done
+        buf["tables"].numpy()[:] = tables
+        buf["lens"].numpy()[:] = lens
+        buf["slots"].numpy()[:] = slots
+        tables_d.copy_(buf["tables"], non_blocking=True)                  # 2
+        lens_d.copy_(buf["lens"], non_blocking=True)
+        slots_d.copy_(buf["slots"], non_blocking=True)
+        buf["done"].record(stream)
+        if pairs:                                                          # 3
+            src = torch.tensor([a for a, _ in pairs], dtype=torch.int32).to(dev)
+            dst = torch.tensor([c for _, c in pairs], dtype=torch.int32).to(dev)
+            pkv.copy_blocks(kc, vc, src, dst)
+        pkv.paged_kv_append(k_new[i], v_new[i], kc, vc, slots_d)          # 4
+        mc = int(lens.max())
+        e0, e1, e2 = ev[i]
+        e0.record(stream)
+        pkv.paged_attention_decode_partials(q[i], kc, vc, tables_d, lens_d, w.scale, mc,  # 5
+                                            part, out, workspace)
+        e1.record(stream)
+        pkv.paged_attention_decode_merge(lens_d, w.num_kv_heads, w.block_size, max_blocks, mc,
+                                         part, out, workspace)
+        e2.record(stream)
+        step_bytes.append(kv_bytes(w, lens))
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.warmup, total_steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    timed = range(args.warmup, total_steps)
+    part_ms = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in timed])
+    merge_ms = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in timed])
+    bytes_timed = np.array(step_bytes[args.warmup:], dtype=np.float64)
+    if not torch.isfinite(out).all():
+        raise RuntimeError("decode produced non-finite output")
+    return dict(wall=wall, part_ms=part_ms, merge_ms=merge_ms, bytes=bytes_timed, batch=b,
+                part=part, max_len=max_len)
+
+
+def cpu_baseline(w, workloads):
+    """The float64 oracle on a sample of the workload's sequences."""
+    import threadpoolctl
+    from oracle import RefAllocator, copy_blocks, kv_append, paged_decode
+
+    sample = min(6, w.num_seqs)
+    p = workloads.plan(w)
+    keep = set(p.seqs[:sample])
+
+    def wanted(op):
+        if op[0] == "fork":
+            return op[2] in keep
+        return op[1] in keep or op[1] == workloads.PREFIX_SEQ
+
+    need = sum(-(-int(n) // w.block_size) for n in p.lens[:sample]) + \
+        -(-w.prefix // w.block_size) + 4
+    ref = RefAllocator(need, w.block_size)
+    shape = (need, w.num_kv_heads, w.block_size, w.head_dim)
+    kc, vc = np.full(shape, np.nan), np.full(shape, np.nan)
+    for i, op in enumerate(p.ops):
+        if not wanted(op):
+            continue
+        if op[0] == "append":
+            k, v = workloads.kv_rows(w, i, op[2])
+            slots, pairs = ref.append(op[1], op[2])
+            if pairs:
+                copy_blocks(kc, vc, [a for a, _ in pairs], [c for _, c in pairs])
+            kv_append(kc, vc, workloads.as_f64(workloads.to_dtype(k, w.dtype)),
+                      workloads.as_f64(workloads.to_dtype(v, w.dtype)), slots, w.block_size)
+        else:
+            workloads.run_schedule([op], ref)
+    seqs = sorted(keep)
+    tables, lens = ref.build_tables(seqs, max(len(ref.tables[s]) for s in seqs))
+    q = np.stack([workloads.as_f64(workloads.to_dtype(workloads.decode_query(w, s), w.dtype))
+                  for s in seqs])
+    info = threadpoolctl.threadpool_info()
+    threads = max([d.get("num_threads", 1) for d in info] or [1])
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        paged_decode(q, kc, vc, np.array(tables), lens, w.scale, w.block_size)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el > 10.0 or reps >= 50:
+            break
+    per = el / reps
+    gbps = kv_bytes(w, np.array(lens)) / per / 1e9
+    return {"value": round(gbps, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "tokens_per_s": round(len(seqs) / per, 2),
+            "sample": f"{len(seqs)} of {w.num_seqs} sequences (context lens "
+                      f"{[int(x) for x in lens]}), float64 numpy gather-then-attend, "
+                      f"{reps} repetitions, {el:.1f} s; host has "
+                      f"{len(os.sched_getaffinity(0))} cores available"}
+
+
+def traffic_from_profiles(w, kernel_src):
+    """HBM bytes per launch from the committed PMC summary, when it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"decode_partition_{w.name}_pmc.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    digest = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
+    if rec.get("kernel_source_sha256") != digest:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the path has no "
+              "multi-GPU mode", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import paged_kv_cache_420_amd as pkv
+    import workloads
+
+    w = workloads.get(args.workload)
+    if w.chunk:
+        w = workloads.scaled(w, chunk=0)
+    r = gpu_run(args, w, torch, pkv, workloads)
+    ms_step = r["wall"] / args.steps * 1e3
+    mean_bytes = float(r["bytes"].mean())
+    value = mean_bytes / (ms_step * 1e-3) / 1e9
+    part_ms = float(r["part_ms"].mean())
+    achieved = mean_bytes / (part_ms * 1e-3) / 1e9
+    src = os.path.join(ROOT, "paged_kv_cache_420_amd", "csrc", "decode.hip")
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {torch.bfloat16: "bf16", torch.float16: "fp16", torch.float32: "fp32"}[w.dtype],
+        "data": "synthetic",
+        "config": {"workload": w.name, "num_seqs": w.num_seqs, "num_heads": w.num_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                   "block_size": w.block_size, "context_lens": w.lens,
+                   "shared_prefix": w.prefix, "partition_size": r["part"] or 512},
+        "hbm_peak_frac": round(value / HBM_PEAK_GBPS, 4),
+        "tokens_per_s": round(r["batch"] / (ms_step * 1e-3), 1),
+        "kv_bytes_per_step": int(mean_bytes),
+        "decode_partition_us": round(part_ms * 1e3, 2),
+        "decode_merge_us": round(float(r["merge_ms"].mean()) * 1e3, 2),
+        "roofline": {"bound": "hbm", "kernel": "decode_partition_kernel",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic_from_profiles(w, src)},
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(w, workloads),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,292 @@
+/*
+ * pkv.h -- paged KV-cache attention for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libpkv.so.  Plain pointers and sizes only; no C++ or framework
+ * types cross this boundary.
+ *
+ * What the library implements, by the pages that define it:
+ *   - "vLLM 初探" tutorial, §1.4 (PagedAttention principle, figure): the KV
+ *     cache is cut into fixed-size blocks held in one shared physical pool;
+ *     each sequence reaches its blocks through a logical page table; blocks
+ *     of an identical prefix may be shared.
+ *   - vLLM explainer (openEuler/CSDN summary), sections "vLLM的核心创新：
+ *     PagedAttention" and "PagedAttention带来的额外红利：内存共享": blocks are
+ *     taken on demand, released to the pool when a request ends, and shared
+ *     by sequences with a common prefix (or common beam history).
+ *   - KV-cache article (intelliparadigm), §2.1 design and pseudo-code: the
+ *     token at position p is in logical block p / block_size, whose physical
+ *     block is block_tables[seq][p / block_size]; attention gathers those
+ *     non-contiguous blocks and computes softmax(q K^T) V.  §4.1/§4.2: long
+ *     prompts are processed in chunks (chunked prefill).
+ *
+ * Conventions shared by every entry point
+ *   - Every function returns an int32 status (pkv_status).  On failure a
+ *     description is available from pkv_last_error() (per thread, valid
+ *     until the next failing call on that thread).
+ *   - Ownership: the caller owns every buffer passed in.  The library keeps
+ *     no pointer after a call returns and never allocates device memory.
+ *   - Host calls (allocator) are synchronous and not thread-safe per handle.
+ *   - Device calls take device pointers and a HIP stream (hipStream_t passed
+ *     as void*, NULL = the null stream).  They validate every host-visible
+ *     argument, enqueue kernels and return without synchronising.  Values
+ *     that live on the device (block-table entries, slots, lengths) are
+ *     range-checked inside the kernels: an out-of-range slot or block id is
+ *     never dereferenced; attention rows whose inputs are inconsistent are
+ *     written as NaN (documented per call).
+ *   - Cache layout (both K and V):
+ *         [num_blocks][num_kv_heads][block_size][head_dim]
+ *     row-major, elements of the cache dtype; one (block, kv-head) tile of
+ *     block_size x head_dim elements is contiguous.
+ *   - Flat slot number of position p of a sequence with table T:
+ *         slot = T[p / block_size] * block_size + p % block_size.
+ *   - Query head h reads KV head h / (num_heads / num_kv_heads).
+ *   - Attention outputs are float32, whatever the cache dtype.
+ *   - The Python binding (package paged_kv_cache_420_amd) exposes each call
+ *     under the same name without the "pkv_" prefix.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pkv_status {
+  PKV_OK = 0,
+  PKV_ERR_INVALID = 1,          /* bad argument, shape, alignment or layout   */
+  PKV_ERR_OUT_OF_BLOCKS = 2,    /* pool exhausted; allocator state unchanged   */
+  PKV_ERR_NO_SUCH_SEQ = 3,      /* unknown sequence id                         */
+  PKV_ERR_SEQ_EXISTS = 4,       /* sequence id already in use                  */
+  PKV_ERR_BUFFER_TOO_SMALL = 5, /* an output or workspace buffer is too small  */
+  PKV_ERR_HIP = 6,              /* a HIP runtime call or kernel launch failed  */
+  PKV_ERR_UNSUPPORTED = 7       /* valid request this build does not handle    */
+} pkv_status;
+
+typedef enum pkv_dtype {
+  PKV_F32 = 0,
+  PKV_F16 = 1,
+  PKV_BF16 = 2
+} pkv_dtype;
+
+/* Description of the last failure on the calling thread ("" if none). */
+const char* pkv_last_error(void);
+
+/* Library version as "major.minor.patch". */
+const char* pkv_version(void);
+
+/* ======================================================================
+ * Host block allocator
+ *
+ * Mechanism: tutorial §1.4; explainer, PagedAttention and memory-sharing
+ * sections (blocks on demand, immediate release to the shared pool, shared
+ * prefixes point at the same blocks).  The pages fix no ordering; this
+ * library fixes the following, and keeps it bit for bit:
+ *   - Free blocks form a stack.  create() pushes init_free_order so that
+ *     init_free_order[0] is popped first; a released block goes on top.
+ *   - Each block carries a reference count = number of tables holding it.
+ *   - append(seq, n): if n > 0, the length is not a multiple of block_size
+ *     and the last block's count is above 1 (shared), a fresh block is
+ *     popped first and replaces the last entry (copy-on-write: the caller
+ *     must copy the data with pkv_copy_blocks before writing, pair = (old,
+ *     new)); then every position that starts a block pops a fresh block.
+ *   - free(seq) releases the blocks in logical order; a block whose count
+ *     reaches 0 is pushed on the free stack.
+ *   - A call that needs more blocks than are free fails with
+ *     PKV_ERR_OUT_OF_BLOCKS and changes nothing.
+ * Sequence ids are arbitrary int64 values chosen by the caller.
+ * ====================================================================== */
+
+typedef struct pkv_allocator pkv_allocator;
+
+/* Create an allocator over num_blocks blocks of block_size tokens.
+ * init_free_order: NULL (order 0..num_blocks-1) or a host array of
+ * num_blocks ints holding a permutation of 0..num_blocks-1; it is copied.
+ * num_blocks * block_size must be below 2^31 (slots are int32).
+ * *out receives the handle; destroy it with pkv_allocator_destroy. */
+int32_t pkv_allocator_create(int32_t num_blocks, int32_t block_size,
+                             const int32_t* init_free_order,
+                             pkv_allocator** out);
+void pkv_allocator_destroy(pkv_allocator* alloc);
+
+/* Register an empty sequence.  PKV_ERR_SEQ_EXISTS if the id is in use. */
+int32_t pkv_seq_add(pkv_allocator* alloc, int64_t seq);
+
+/* Drop a sequence and release its blocks (explainer, PagedAttention
+ * section: blocks return to the shared pool when a request ends). */
+int32_t pkv_seq_free(pkv_allocator* alloc, int64_t seq);
+
+/* New sequence `child` sharing every block of `parent` (same table, same
+ * length; each block's count +1).  Explainer, memory-sharing section:
+ * identical prefixes and beam histories point at the same blocks. */
+int32_t pkv_seq_fork(pkv_allocator* alloc, int64_t parent, int64_t child);
+
+/* Grow `seq` by n >= 0 tokens (article §2.1/§2.2: positions map to
+ * table[p / block_size]; growth only takes new blocks and updates the
+ * table).  Outputs (host arrays, caller-owned):
+ *   slots_out[n]      flat slot of positions len .. len+n-1, in order;
+ *   cow_src[1], cow_dst[1], *n_cow (0 or 1): the copy-on-write pair.
+ * slots_out may be NULL only when n == 0. */
+int32_t pkv_seq_append(pkv_allocator* alloc, int64_t seq, int32_t n,
+                       int32_t* slots_out, int32_t* cow_src,
+                       int32_t* cow_dst, int32_t* n_cow);
+
+/* Append counts[i] tokens to seqs[i] for i in order, all or nothing (one
+ * decode step of a batch, or one chunk per sequence).  A sequence may
+ * appear only once.  slots_out receives sum(counts) slots in batch order
+ * (capacity slots_cap); cow_src/cow_dst receive *n_cow pairs in order
+ * (capacity cow_cap; at most num_seqs pairs).  Capacities are checked
+ * before any state changes (PKV_ERR_BUFFER_TOO_SMALL). */
+int32_t pkv_append_batch(pkv_allocator* alloc, const int64_t* seqs,
+                         const int32_t* counts, int32_t num_seqs,
+                         int32_t* slots_out, int64_t slots_cap,
+                         int32_t* cow_src, int32_t* cow_dst, int32_t cow_cap,
+                         int32_t* n_cow);
+
+/* Queries (host outputs). */
+int32_t pkv_seq_len(const pkv_allocator* alloc, int64_t seq, int32_t* len);
+/* Copies the table into out[cap]; *n = its length (checked against cap). */
+int32_t pkv_seq_block_table(const pkv_allocator* alloc, int64_t seq,
+                            int32_t* out, int32_t cap, int32_t* n);
+int32_t pkv_num_free_blocks(const pkv_allocator* alloc, int32_t* n);
+int32_t pkv_num_blocks(const pkv_allocator* alloc, int32_t* n);
+int32_t pkv_block_size(const pkv_allocator* alloc, int32_t* n);
+int32_t pkv_block_refcount(const pkv_allocator* alloc, int32_t block,
+                           int32_t* count);
+/* free_stack[num_blocks] receives the free blocks, top of the stack first,
+ * *n_free their number; refcounts[num_blocks] every block's count. */
+int32_t pkv_allocator_snapshot(const pkv_allocator* alloc,
+                               int32_t* free_stack, int32_t* n_free,
+                               int32_t* refcounts);
+/* Pack the tables of seqs[0..num_seqs) into block_tables[num_seqs]
+ * [max_blocks] (row-major, -1 after each table's end) and their lengths
+ * into context_lens[num_seqs] -- the host images of the device arrays the
+ * attention calls read.  PKV_ERR_BUFFER_TOO_SMALL if a table is longer
+ * than max_blocks. */
+int32_t pkv_build_block_tables(const pkv_allocator* alloc,
+                               const int64_t* seqs, int32_t num_seqs,
+                               int32_t max_blocks, int32_t* block_tables,
+                               int32_t* context_lens);
+
+/* ======================================================================
+ * Device calls (gfx950 HIP kernels)
+ * ====================================================================== */
+
+/* Scatter new K/V rows into the caches through a slot mapping (article
+ * §2.1: slot = table[p / bs] * bs + p % bs; explainer, serving section:
+ * each stored token adds one K and one V vector).
+ *   key, value      [num_tokens][num_kv_heads][head_dim]  cache dtype
+ *   key_cache, value_cache   layout above, num_blocks blocks
+ *   slot_mapping    [num_tokens] int32 device array; a negative slot skips
+ *                   the row; a slot >= num_blocks * block_size is skipped
+ *                   too (never written).  Slots must be distinct.
+ * Bitwise copy.  head_dim * sizeof(dtype) must be a multiple of 16 bytes
+ * and every pointer 16-byte aligned. */
+int32_t pkv_paged_kv_append(const void* key, const void* value,
+                            void* key_cache, void* value_cache,
+                            const int32_t* slot_mapping, int32_t num_tokens,
+                            int32_t num_kv_heads, int32_t head_dim,
+                            int32_t block_size, int32_t num_blocks,
+                            int32_t dtype, void* stream);
+
+/* Copy whole blocks: for each i, block dst[i] := block src[i] in both
+ * caches (the data side of copy-on-write; explainer, memory-sharing
+ * section).  src/dst: device int32[num_pairs].  Pairs whose ids fall
+ * outside [0, num_blocks) are skipped.  A block must not be a destination
+ * twice nor both a source and a destination in one call. */
+int32_t pkv_copy_blocks(void* key_cache, void* value_cache,
+                        const int32_t* src, const int32_t* dst,
+                        int32_t num_pairs, int32_t num_blocks,
+                        int32_t num_kv_heads, int32_t block_size,
+                        int32_t head_dim, int32_t dtype, void* stream);
+
+/* Workspace needed by pkv_paged_attention_decode for these sizes, in
+ * bytes (0 when no sequence needs more than one partition). */
+int32_t pkv_paged_attention_decode_workspace_size(
+    int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+    int32_t max_context_len, int32_t partition_size, size_t* bytes);
+
+/* PagedAttention decode: one query row per sequence over its paged KV
+ * (article §2.1 pseudo-code: gather the sequence's blocks through its
+ * table, softmax(scale * q K^T) V; explainer, serving section: every
+ * decode step attends over all cached tokens, its own included).
+ *   query          [num_seqs][num_heads][head_dim], cache dtype
+ *   block_tables   [num_seqs][max_blocks_per_seq] int32 device
+ *   context_lens   [num_seqs] int32 device; 0 gives a zero output row
+ *   max_context_len  host-known upper bound of context_lens (sizes the
+ *                  grid); a sequence longer than it, or longer than
+ *                  max_blocks_per_seq * block_size, or whose used table
+ *                  entries fall outside [0, num_blocks), gets NaN rows
+ *   partition_size tokens per split-K partition: 0 = automatic, else a
+ *                  multiple of block_size, at least 64, at most 1024
+ *   out            [num_seqs][num_heads][head_dim] float32
+ *   workspace      device buffer of at least the size reported by
+ *                  pkv_paged_attention_decode_workspace_size (may be NULL
+ *                  when that size is 0)
+ * Supported: head_dim in {64, 128}; num_heads / num_kv_heads in
+ * {1, 2, 4, 8}; block_size a power of two in [8, 256]; the scale is any
+ * finite float.  Row h reads KV head h / (num_heads / num_kv_heads). */
+int32_t pkv_paged_attention_decode(
+    const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, const int32_t* context_lens,
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+    int32_t num_blocks, int32_t max_context_len, float scale,
+    int32_t partition_size, float* out, void* workspace,
+    size_t workspace_bytes, int32_t dtype, void* stream);
+
+/* The two stages of pkv_paged_attention_decode, for callers that schedule
+ * or time them separately (same arguments, same semantics):
+ *   _partials launches the split-K partition kernel: sequences that fit in
+ *   one partition get their final rows in `out`; longer ones leave
+ *   per-partition (max, sum, unnormalised output) in `workspace`.
+ *   _merge launches the log-sum-exp merge of those partials into `out`
+ *   (nothing to do when no sequence spans two partitions).
+ * Calling _partials then _merge on one stream, with identical sizes,
+ * partition_size and buffers, is exactly pkv_paged_attention_decode. */
+int32_t pkv_paged_attention_decode_partials(
+    const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, const int32_t* context_lens,
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+    int32_t num_blocks, int32_t max_context_len, float scale,
+    int32_t partition_size, float* out, void* workspace,
+    size_t workspace_bytes, int32_t dtype, void* stream);
+int32_t pkv_paged_attention_decode_merge(
+    const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t max_blocks_per_seq, int32_t max_context_len,
+    int32_t partition_size, float* out, void* workspace,
+    size_t workspace_bytes, void* stream);
+
+/* Causal chunked prefill against the same paged cache (article §4.1/§4.2:
+ * long prompts in chunks).  The chunk's K/V must already be appended.
+ *   query        [total_q][num_heads][head_dim], rows cu_query_lens[b] ..
+ *                cu_query_lens[b+1]-1 belong to sequence b
+ *   cu_query_lens [num_seqs + 1] int32 device, non-decreasing, from 0
+ *   context_lens [num_seqs] int32 device, cached tokens INCLUDING the
+ *                chunk; chunk row i sits at position
+ *                context_lens[b] - c_b + i and attends to positions
+ *                0 .. context_lens[b] - c_b + i
+ *   max_query_len host-known bound of every c_b (sizes the grid)
+ *   out          [total_q][num_heads][head_dim] float32
+ * Rows of a sequence whose chunk is longer than its context, longer than
+ * max_query_len, or whose table is inconsistent are written as NaN.
+ * Supported: dtype F16 or BF16 (matrix-core path); head_dim 128 (and 64);
+ * num_heads / num_kv_heads in {1, 2, 4, 8}; block_size a power of two in
+ * [16, 256]. */
+int32_t pkv_paged_attention_prefill(
+    const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, const int32_t* context_lens,
+    const int32_t* cu_query_lens, int32_t num_seqs, int32_t num_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t max_blocks_per_seq, int32_t num_blocks, int32_t max_query_len,
+    float scale, float* out, int32_t dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -1,0 +1,428 @@
+"""paged_kv_cache_420_amd -- paged KV-cache attention for AMD MI355X (gfx950).
+
+Thin Python binding over libpkv.so (C ABI declared in include/pkv.h).  Each
+function here has the name of a C entry point without its "pkv_" prefix and
+only marshals arguments: shapes and dtypes are read from torch tensors,
+pointers and the current HIP stream are passed down, and status codes become
+exceptions.  Every step of the computation runs in the library's HIP
+kernels; torch provides device memory and streams, nothing else.  There is
+no fallback: importing this package fails if libpkv.so has not been built
+(python paged_kv_cache_420_amd/_build.py).
+
+Cache layout (K and V alike): [num_blocks, num_kv_heads, block_size, head_dim],
+a tensor of the cache dtype (float32, float16 or bfloat16) on the GPU.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+__all__ = [
+    "PkvError", "InvalidArgument", "OutOfBlocks", "NoSuchSequence",
+    "SequenceExists", "BufferTooSmall", "HipError", "Unsupported",
+    "BlockAllocator", "paged_kv_append", "copy_blocks",
+    "paged_attention_decode_workspace_size", "paged_attention_decode",
+    "paged_attention_decode_partials", "paged_attention_decode_merge",
+    "paged_attention_prefill", "library_path", "version",
+]
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
+
+
+class PkvError(RuntimeError):
+    """Base class of errors reported by libpkv."""
+
+
+class InvalidArgument(PkvError, ValueError):
+    pass
+
+
+class OutOfBlocks(PkvError):
+    """The block pool is exhausted; the allocator state is unchanged."""
+
+
+class NoSuchSequence(PkvError, KeyError):
+    pass
+
+
+class SequenceExists(PkvError, ValueError):
+    pass
+
+
+class BufferTooSmall(PkvError, ValueError):
+    pass
+
+
+class HipError(PkvError):
+    pass
+
+
+class Unsupported(PkvError, NotImplementedError):
+    pass
+
+
+_ERRORS = {1: InvalidArgument, 2: OutOfBlocks, 3: NoSuchSequence,
+           4: SequenceExists, 5: BufferTooSmall, 6: HipError, 7: Unsupported}
+
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_P = ctypes.c_void_p
+_PI32 = ctypes.POINTER(ctypes.c_int32)
+_PI64 = ctypes.POINTER(ctypes.c_int64)
+
+_SIGNATURES = {
+    "pkv_last_error": (ctypes.c_char_p, []),
+    "pkv_version": (ctypes.c_char_p, []),
+    "pkv_allocator_create": (_I32, [_I32, _I32, _PI32, ctypes.POINTER(_P)]),
+    "pkv_allocator_destroy": (None, [_P]),
+    "pkv_seq_add": (_I32, [_P, _I64]),
+    "pkv_seq_free": (_I32, [_P, _I64]),
+    "pkv_seq_fork": (_I32, [_P, _I64, _I64]),
+    "pkv_seq_append": (_I32, [_P, _I64, _I32, _PI32, _PI32, _PI32, _PI32]),
+    "pkv_append_batch": (_I32, [_P, _PI64, _PI32, _I32, _PI32, _I64, _PI32, _PI32, _I32, _PI32]),
+    "pkv_seq_len": (_I32, [_P, _I64, _PI32]),
+    "pkv_seq_block_table": (_I32, [_P, _I64, _PI32, _I32, _PI32]),
+    "pkv_num_free_blocks": (_I32, [_P, _PI32]),
+    "pkv_num_blocks": (_I32, [_P, _PI32]),
+    "pkv_block_size": (_I32, [_P, _PI32]),
+    "pkv_block_refcount": (_I32, [_P, _I32, _PI32]),
+    "pkv_allocator_snapshot": (_I32, [_P, _PI32, _PI32, _PI32]),
+    "pkv_build_block_tables": (_I32, [_P, _PI64, _I32, _I32, _PI32, _PI32]),
+    "pkv_paged_kv_append": (_I32, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P]),
+    "pkv_copy_blocks": (_I32, [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P]),
+    "pkv_paged_attention_decode_workspace_size": (_I32, [_I32, _I32, _I32, _I32, _I32, ctypes.POINTER(ctypes.c_size_t)]),
+    "pkv_paged_attention_decode": (_I32, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                                          ctypes.c_float, _I32, _P, _P, ctypes.c_size_t, _I32, _P]),
+    "pkv_paged_attention_decode_partials": (_I32, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                                                   _I32, ctypes.c_float, _I32, _P, _P, ctypes.c_size_t, _I32, _P]),
+    "pkv_paged_attention_decode_merge": (_I32, [_P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P,
+                                                ctypes.c_size_t, _P]),
+    "pkv_paged_attention_prefill": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                                           ctypes.c_float, _P, _I32, _P]),
+}
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"{_LIB_PATH} is not built; run `python paged_kv_cache_420_amd/_build.py` "
+            "(there is no non-HIP fallback)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+def library_path():
+    return _LIB_PATH
+
+
+def version():
+    return _lib.pkv_version().decode()
+
+
+def _check(status):
+    if status != 0:
+        msg = _lib.pkv_last_error().decode()
+        raise _ERRORS.get(status, PkvError)(msg or f"libpkv status {status}")
+
+
+def _i32p(arr):
+    return arr.ctypes.data_as(_PI32)
+
+
+# ---------------------------------------------------------------------------
+# Host block allocator
+# ---------------------------------------------------------------------------
+
+class BlockAllocator:
+    """Handle on a pkv_allocator (free stack, refcounts, block tables).
+
+    Semantics are those of include/pkv.h: blocks on demand, LIFO free stack
+    seeded by ``init_free_order``, refcounted fork, copy-on-write pair
+    reported by append, release in logical order, all-or-nothing failure.
+    """
+
+    def __init__(self, num_blocks, block_size, init_free_order=None):
+        handle = _P()
+        order = None
+        if init_free_order is not None:
+            order = np.ascontiguousarray(np.asarray(init_free_order, dtype=np.int32))
+            if order.shape != (num_blocks,):
+                raise InvalidArgument("init_free_order must hold num_blocks entries")
+        _check(_lib.pkv_allocator_create(num_blocks, block_size,
+                                         _i32p(order) if order is not None else None,
+                                         ctypes.byref(handle)))
+        self._h = handle
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+
+    def close(self):
+        if getattr(self, "_h", None):
+            _lib.pkv_allocator_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def add(self, seq):
+        _check(_lib.pkv_seq_add(self._h, seq))
+
+    def free(self, seq):
+        _check(_lib.pkv_seq_free(self._h, seq))
+
+    def fork(self, parent, child):
+        _check(_lib.pkv_seq_fork(self._h, parent, child))
+
+    def append(self, seq, n):
+        """Returns (slots: int32 array [n], cow: list of (src, dst))."""
+        slots = np.empty(max(n, 1), dtype=np.int32)
+        src, dst, cnt = _I32(), _I32(), _I32()
+        _check(_lib.pkv_seq_append(self._h, seq, n, _i32p(slots), ctypes.byref(src),
+                                   ctypes.byref(dst), ctypes.byref(cnt)))
+        return slots[:n], ([(src.value, dst.value)] if cnt.value else [])
+
+    def append_batch(self, seqs, counts):
+        """All-or-nothing append; returns (slots int32 [sum counts], cow pairs)."""
+        seqs = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64))
+        counts = np.ascontiguousarray(np.asarray(counts, dtype=np.int32))
+        if seqs.shape != counts.shape:
+            raise InvalidArgument("seqs and counts differ in length")
+        total = int(counts.astype(np.int64).sum())
+        slots = np.empty(max(total, 1), dtype=np.int32)
+        cap = max(len(seqs), 1)
+        src = np.empty(cap, dtype=np.int32)
+        dst = np.empty(cap, dtype=np.int32)
+        cnt = _I32()
+        _check(_lib.pkv_append_batch(self._h, seqs.ctypes.data_as(_PI64), _i32p(counts), len(seqs),
+                                     _i32p(slots), total, _i32p(src), _i32p(dst), len(seqs),
+                                     ctypes.byref(cnt)))
+        return slots[:total], list(zip(src[:cnt.value].tolist(), dst[:cnt.value].tolist()))
+
+    def seq_len(self, seq):
+        out = _I32()
+        _check(_lib.pkv_seq_len(self._h, seq, ctypes.byref(out)))
+        return out.value
+
+    def block_table(self, seq):
+        n = _I32()
+        st = _lib.pkv_seq_block_table(self._h, seq, None, 0, ctypes.byref(n))
+        if st not in (0, 5):
+            _check(st)
+        buf = np.empty(max(n.value, 1), dtype=np.int32)
+        _check(_lib.pkv_seq_block_table(self._h, seq, _i32p(buf), n.value, ctypes.byref(n)))
+        return buf[:n.value].tolist()
+
+    def num_free(self):
+        out = _I32()
+        _check(_lib.pkv_num_free_blocks(self._h, ctypes.byref(out)))
+        return out.value
+
+    def refcount(self, block):
+        out = _I32()
+        _check(_lib.pkv_block_refcount(self._h, block, ctypes.byref(out)))
+        return out.value
+
+    def snapshot(self):
+        """(free stack top first, refcounts) as lists."""
+        free = np.empty(self.num_blocks, dtype=np.int32)
+        ref = np.empty(self.num_blocks, dtype=np.int32)
+        nf = _I32()
+        _check(_lib.pkv_allocator_snapshot(self._h, _i32p(free), ctypes.byref(nf), _i32p(ref)))
+        return free[:nf.value].tolist(), ref.tolist()
+
+    def build_block_tables(self, seqs, max_blocks):
+        """Host int32 arrays (block_tables [B, max_blocks] -1 padded, context_lens [B])."""
+        seqs = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64))
+        b = len(seqs)
+        tables = np.empty((max(b, 1), max(max_blocks, 1)), dtype=np.int32)
+        lens = np.empty(max(b, 1), dtype=np.int32)
+        _check(_lib.pkv_build_block_tables(self._h, seqs.ctypes.data_as(_PI64), b, max_blocks,
+                                           _i32p(tables), _i32p(lens)))
+        return tables[:b, :max_blocks], lens[:b]
+
+
+# ---------------------------------------------------------------------------
+# Device calls
+# ---------------------------------------------------------------------------
+
+_DTYPES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+
+
+def _dtype_code(t):
+    try:
+        return _DTYPES[t.dtype]
+    except KeyError:
+        raise InvalidArgument(f"unsupported dtype {t.dtype}") from None
+
+
+def _dev(t, name, dtype=None, ndim=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise InvalidArgument(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise InvalidArgument(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise InvalidArgument(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise InvalidArgument(f"{name} must have {ndim} dimensions")
+    return t.data_ptr()
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _cache_dims(key_cache, value_cache):
+    _dev(key_cache, "key_cache", ndim=4)
+    _dev(value_cache, "value_cache", dtype=key_cache.dtype, ndim=4)
+    if key_cache.shape != value_cache.shape:
+        raise InvalidArgument("key_cache and value_cache differ in shape")
+    return tuple(key_cache.shape)  # (num_blocks, num_kv_heads, block_size, head_dim)
+
+
+def paged_kv_append(key, value, key_cache, value_cache, slot_mapping):
+    """Scatter key/value [T, Hkv, D] into the caches at int32 slot_mapping [T]
+    (negative slot = skip).  pkv_paged_kv_append."""
+    nb, hkv, bs, d = _cache_dims(key_cache, value_cache)
+    _dev(key, "key", dtype=key_cache.dtype, ndim=3)
+    _dev(value, "value", dtype=key_cache.dtype, ndim=3)
+    _dev(slot_mapping, "slot_mapping", dtype=torch.int32, ndim=1)
+    t = key.shape[0]
+    if key.shape != (t, hkv, d) or value.shape != key.shape or slot_mapping.shape[0] != t:
+        raise InvalidArgument("key/value must be [T, num_kv_heads, head_dim] with T slots")
+    _check(_lib.pkv_paged_kv_append(key.data_ptr(), value.data_ptr(), key_cache.data_ptr(),
+                                    value_cache.data_ptr(), slot_mapping.data_ptr(), t, hkv, d, bs,
+                                    nb, _dtype_code(key_cache), _stream(key_cache)))
+
+
+def copy_blocks(key_cache, value_cache, src, dst):
+    """Block dst[i] := block src[i] in both caches (int32 GPU tensors).
+    pkv_copy_blocks."""
+    nb, hkv, bs, d = _cache_dims(key_cache, value_cache)
+    _dev(src, "src", dtype=torch.int32, ndim=1)
+    _dev(dst, "dst", dtype=torch.int32, ndim=1)
+    if src.shape != dst.shape:
+        raise InvalidArgument("src and dst differ in length")
+    _check(_lib.pkv_copy_blocks(key_cache.data_ptr(), value_cache.data_ptr(), src.data_ptr(),
+                                dst.data_ptr(), src.shape[0], nb, hkv, bs, d,
+                                _dtype_code(key_cache), _stream(key_cache)))
+
+
+def paged_attention_decode_workspace_size(num_seqs, num_heads, head_dim, max_context_len,
+                                          partition_size=0):
+    out = ctypes.c_size_t()
+    _check(_lib.pkv_paged_attention_decode_workspace_size(num_seqs, num_heads, head_dim,
+                                                          max_context_len, partition_size,
+                                                          ctypes.byref(out)))
+    return out.value
+
+
+def _decode_args(query, key_cache, value_cache, block_tables, context_lens, max_context_len,
+                 partition_size, out, workspace):
+    nb, hkv, bs, d = _cache_dims(key_cache, value_cache)
+    _dev(query, "query", dtype=key_cache.dtype, ndim=3)
+    _dev(block_tables, "block_tables", dtype=torch.int32, ndim=2)
+    _dev(context_lens, "context_lens", dtype=torch.int32, ndim=1)
+    b, hq, dq = query.shape
+    if dq != d or block_tables.shape[0] != b or context_lens.shape[0] != b:
+        raise InvalidArgument("query, block_tables and context_lens disagree on shape")
+    if out is None:
+        out = torch.empty((b, hq, d), dtype=torch.float32, device=query.device)
+    _dev(out, "out", dtype=torch.float32, ndim=3)
+    if tuple(out.shape) != (b, hq, d):
+        raise InvalidArgument("out must be [B, Hq, D]")
+    need = paged_attention_decode_workspace_size(b, hq, d, int(max_context_len), partition_size)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
+    ws_ptr, ws_bytes = (None, 0)
+    if workspace is not None:
+        _dev(workspace, "workspace")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    return (nb, hkv, bs, d, b, hq), out, workspace, ws_ptr, ws_bytes
+
+
+def paged_attention_decode(query, key_cache, value_cache, block_tables, context_lens, scale,
+                           max_context_len, partition_size=0, out=None, workspace=None):
+    """Decode attention (pkv_paged_attention_decode).
+
+    query [B, Hq, D] (cache dtype); block_tables [B, max_blocks] int32;
+    context_lens [B] int32; returns out [B, Hq, D] float32.
+    ``max_context_len`` is a host-side bound on context_lens (sizes the grid).
+    """
+    (nb, hkv, bs, d, b, hq), out, workspace, ws_ptr, ws_bytes = _decode_args(
+        query, key_cache, value_cache, block_tables, context_lens, max_context_len,
+        partition_size, out, workspace)
+    _check(_lib.pkv_paged_attention_decode(
+        query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(), block_tables.data_ptr(),
+        context_lens.data_ptr(), b, hq, hkv, d, bs, block_tables.shape[1], nb,
+        int(max_context_len), float(scale), int(partition_size), out.data_ptr(), ws_ptr, ws_bytes,
+        _dtype_code(key_cache), _stream(query)))
+    return out
+
+
+def paged_attention_decode_partials(query, key_cache, value_cache, block_tables, context_lens,
+                                    scale, max_context_len, partition_size, out, workspace):
+    """First stage of decode (pkv_paged_attention_decode_partials); pass the
+    same ``out``/``workspace`` to paged_attention_decode_merge."""
+    (nb, hkv, bs, d, b, hq), out, workspace, ws_ptr, ws_bytes = _decode_args(
+        query, key_cache, value_cache, block_tables, context_lens, max_context_len,
+        partition_size, out, workspace)
+    _check(_lib.pkv_paged_attention_decode_partials(
+        query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(), block_tables.data_ptr(),
+        context_lens.data_ptr(), b, hq, hkv, d, bs, block_tables.shape[1], nb,
+        int(max_context_len), float(scale), int(partition_size), out.data_ptr(), ws_ptr, ws_bytes,
+        _dtype_code(key_cache), _stream(query)))
+    return out
+
+
+def paged_attention_decode_merge(context_lens, num_kv_heads, block_size, max_blocks_per_seq,
+                                 max_context_len, partition_size, out, workspace):
+    """Second stage of decode (pkv_paged_attention_decode_merge)."""
+    _dev(context_lens, "context_lens", dtype=torch.int32, ndim=1)
+    _dev(out, "out", dtype=torch.float32, ndim=3)
+    b, hq, d = out.shape
+    ws_ptr, ws_bytes = (None, 0)
+    if workspace is not None:
+        _dev(workspace, "workspace")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    _check(_lib.pkv_paged_attention_decode_merge(
+        context_lens.data_ptr(), b, hq, num_kv_heads, d, block_size, max_blocks_per_seq,
+        int(max_context_len), int(partition_size), out.data_ptr(), ws_ptr, ws_bytes,
+        _stream(out)))
+    return out
+
+
+def paged_attention_prefill(query, key_cache, value_cache, block_tables, context_lens,
+                            cu_query_lens, scale, max_query_len, out=None):
+    """Causal chunked prefill (pkv_paged_attention_prefill).
+
+    query [sum c_b, Hq, D] (cache dtype); cu_query_lens [B+1] int32;
+    context_lens [B] int32 counting the chunk; returns out float32.
+    """
+    nb, hkv, bs, d = _cache_dims(key_cache, value_cache)
+    _dev(query, "query", dtype=key_cache.dtype, ndim=3)
+    _dev(block_tables, "block_tables", dtype=torch.int32, ndim=2)
+    _dev(context_lens, "context_lens", dtype=torch.int32, ndim=1)
+    _dev(cu_query_lens, "cu_query_lens", dtype=torch.int32, ndim=1)
+    b = context_lens.shape[0]
+    total, hq, dq = query.shape
+    if dq != d or block_tables.shape[0] != b or cu_query_lens.shape[0] != b + 1:
+        raise InvalidArgument("query, block_tables, context_lens and cu_query_lens disagree")
+    if out is None:
+        out = torch.empty((total, hq, d), dtype=torch.float32, device=query.device)
+    _dev(out, "out", dtype=torch.float32, ndim=3)
+    if tuple(out.shape) != (total, hq, d):
+        raise InvalidArgument("out must be [sum c_b, Hq, D]")
+    _check(_lib.pkv_paged_attention_prefill(
+        query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(), block_tables.data_ptr(),
+        context_lens.data_ptr(), cu_query_lens.data_ptr(), b, hq, hkv, d, bs,
+        block_tables.shape[1], nb, int(max_query_len), float(scale), out.data_ptr(),
+        _dtype_code(key_cache), _stream(query)))
+    return out

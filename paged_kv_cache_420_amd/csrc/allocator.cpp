@@ -1,0 +1,172 @@
+// Host block allocator (see allocator.h for the contract and sources).
+#include "allocator.h"
+
+#include <unordered_set>
+
+#include "common.h"
+
+namespace pkv {
+
+namespace {
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+}  // namespace
+
+BlockAllocator::BlockAllocator(int32_t num_blocks, int32_t block_size,
+                               const std::vector<int32_t>& order)
+    : num_blocks_(num_blocks),
+      block_size_(block_size),
+      free_(order.rbegin(), order.rend()),
+      ref_(num_blocks, 0) {}
+
+void BlockAllocator::free_stack(int32_t* out) const {
+  int32_t i = 0;
+  for (auto it = free_.rbegin(); it != free_.rend(); ++it) out[i++] = *it;
+}
+
+int32_t BlockAllocator::pop() {
+  int32_t b = free_.back();
+  free_.pop_back();
+  ref_[b] = 1;
+  return b;
+}
+
+int32_t BlockAllocator::add(int64_t seq) {
+  if (has(seq))
+    return fail(PKV_ERR_SEQ_EXISTS, "sequence %lld already exists",
+                static_cast<long long>(seq));
+  seqs_.emplace(seq, Seq{});
+  return ok();
+}
+
+int32_t BlockAllocator::release(int64_t seq) {
+  auto it = seqs_.find(seq);
+  if (it == seqs_.end())
+    return fail(PKV_ERR_NO_SUCH_SEQ, "no sequence %lld",
+                static_cast<long long>(seq));
+  // Logical order: a block reaching zero goes on top of the free stack.
+  for (int32_t b : it->second.table)
+    if (--ref_[b] == 0) free_.push_back(b);
+  seqs_.erase(it);
+  return ok();
+}
+
+int32_t BlockAllocator::fork(int64_t parent, int64_t child) {
+  auto it = seqs_.find(parent);
+  if (it == seqs_.end())
+    return fail(PKV_ERR_NO_SUCH_SEQ, "no parent sequence %lld",
+                static_cast<long long>(parent));
+  if (has(child))
+    return fail(PKV_ERR_SEQ_EXISTS, "child sequence %lld already exists",
+                static_cast<long long>(child));
+  Seq copy = it->second;
+  for (int32_t b : copy.table) ++ref_[b];
+  seqs_.emplace(child, std::move(copy));
+  return ok();
+}
+
+int64_t BlockAllocator::blocks_needed(const Seq& s, int32_t n,
+                                      int32_t last_ref, bool* cow) const {
+  int64_t fresh = cdiv(int64_t(s.len) + n, block_size_) -
+                  cdiv(s.len, block_size_);
+  *cow = n > 0 && s.len % block_size_ != 0 && last_ref > 1;
+  return fresh + (*cow ? 1 : 0);
+}
+
+void BlockAllocator::grow(Seq& s, int32_t n, int32_t* slots,
+                          std::vector<CowPair>* cow) {
+  bool do_cow = false;
+  if (n > 0 && s.len % block_size_ != 0) do_cow = ref_[s.table.back()] > 1;
+  if (do_cow) {
+    int32_t old = s.table.back();
+    int32_t fresh = pop();
+    --ref_[old];
+    s.table.back() = fresh;
+    cow->push_back({old, fresh});
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    int32_t p = s.len + i;
+    if (p % block_size_ == 0) s.table.push_back(pop());
+    slots[i] = s.table[p / block_size_] * block_size_ + p % block_size_;
+  }
+  s.len += n;
+}
+
+int32_t BlockAllocator::append(int64_t seq, int32_t n, int32_t* slots,
+                               std::vector<CowPair>* cow) {
+  auto it = seqs_.find(seq);
+  if (it == seqs_.end())
+    return fail(PKV_ERR_NO_SUCH_SEQ, "no sequence %lld",
+                static_cast<long long>(seq));
+  if (n < 0) return fail(PKV_ERR_INVALID, "negative token count %d", n);
+  Seq& s = it->second;
+  bool c = false;
+  int32_t last_ref = s.table.empty() ? 0 : ref_[s.table.back()];
+  int64_t need = blocks_needed(s, n, last_ref, &c);
+  if (need > num_free())
+    return fail(PKV_ERR_OUT_OF_BLOCKS, "need %lld blocks, %d free",
+                static_cast<long long>(need), num_free());
+  grow(s, n, slots, cow);
+  return ok();
+}
+
+int32_t BlockAllocator::append_batch(const int64_t* seqs,
+                                     const int32_t* counts, int32_t num_seqs,
+                                     int32_t* slots, int64_t slots_cap,
+                                     CowPair* cow, int32_t cow_cap,
+                                     int32_t* n_cow) {
+  if (num_seqs < 0) return fail(PKV_ERR_INVALID, "negative batch size");
+  // Validate everything, and count the blocks the whole batch needs in
+  // batch order: a copy-on-write of one sequence lowers the count of a
+  // block other members of the batch may still share.
+  std::unordered_set<int64_t> seen;
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    if (!has(seqs[i]))
+      return fail(PKV_ERR_NO_SUCH_SEQ, "no sequence %lld",
+                  static_cast<long long>(seqs[i]));
+    if (!seen.insert(seqs[i]).second)
+      return fail(PKV_ERR_INVALID, "sequence %lld appears twice in a batch",
+                  static_cast<long long>(seqs[i]));
+    if (counts[i] < 0)
+      return fail(PKV_ERR_INVALID, "negative token count %d", counts[i]);
+  }
+  std::unordered_map<int32_t, int32_t> dropped;  // block -> refs given up
+  int64_t total_slots = 0, need = 0;
+  int32_t cows = 0;
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    const Seq& s = seqs_.at(seqs[i]);
+    int32_t last_ref = 0;
+    if (!s.table.empty()) {
+      int32_t last = s.table.back();
+      auto d = dropped.find(last);
+      last_ref = ref_[last] - (d == dropped.end() ? 0 : d->second);
+    }
+    bool c = false;
+    need += blocks_needed(s, counts[i], last_ref, &c);
+    if (c) {
+      ++dropped[s.table.back()];
+      ++cows;
+    }
+    total_slots += counts[i];
+  }
+  if (total_slots > slots_cap)
+    return fail(PKV_ERR_BUFFER_TOO_SMALL, "slots buffer holds %lld, need %lld",
+                static_cast<long long>(slots_cap),
+                static_cast<long long>(total_slots));
+  if (cows > cow_cap)
+    return fail(PKV_ERR_BUFFER_TOO_SMALL, "cow buffer holds %d, need %d",
+                cow_cap, cows);
+  if (need > num_free())
+    return fail(PKV_ERR_OUT_OF_BLOCKS, "batch needs %lld blocks, %d free",
+                static_cast<long long>(need), num_free());
+  std::vector<CowPair> pairs;
+  int64_t off = 0;
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    grow(seqs_.at(seqs[i]), counts[i], slots + off, &pairs);
+    off += counts[i];
+  }
+  for (size_t k = 0; k < pairs.size(); ++k) cow[k] = pairs[k];
+  *n_cow = static_cast<int32_t>(pairs.size());
+  return ok();
+}
+
+}  // namespace pkv

@@ -1,0 +1,696 @@
+// PagedAttention decode on gfx950 (CDNA4).
+//
+// What is computed (KV-cache article, intelliparadigm, §2.1 and its
+// pseudo-code): for each sequence b and query head h, gather the sequence's
+// keys and values through its block table -- position p lives at row
+// p % block_size of physical block block_tables[b][p / block_size] -- and
+// return softmax(scale * q K^T) V over all context_lens[b] cached tokens
+// (explainer, openEuler/CSDN, serving section: each decode step attends over
+// every token before it, its own K/V stored first).  The article names
+// prefetching and on-chip staging as the way the kernel hides the scattered
+// page accesses; here that becomes: many workgroups per CU with 16-byte
+// loads in flight, block ids staged in LDS, and scores/weights in LDS.
+//
+// Work split (split-K): one workgroup of 4 wavefronts per (partition of
+// `part` tokens, kv head, sequence).  It serves all G = Hq / Hkv query heads
+// that read this kv head, so each K/V tile is fetched from HBM once per
+// group (GQA reuse).  Within the workgroup:
+//   1. block ids of the partition -> LDS (range-checked);
+//   2. QK pass: a "unit" is one 16-byte load per lane = 1 KiB per wavefront,
+//      covering TPL consecutive tokens of one (block, kv-head) tile (LPT
+//      lanes per token row); a chunk is 4 units.  Each lane takes packed
+//      dot products of its slice of q with its slice of K, then the LPT
+//      lanes of a row reduce them with a transposed butterfly (each step
+//      halves the values a lane holds, so the 4*G partial sums end up
+//      spread over the lanes instead of replicated); scaled scores -> LDS;
+//   3. softmax over the partition in LDS (per-head max, exp2, sum);
+//   4. PV pass: same unit walk over V; each lane scales its slice of V by
+//      the weight of its token and accumulates G x EPL floats;
+//   5. lanes of different token rows and the 4 wavefronts are summed
+//      (shuffles, then LDS) and the partition's result is written either
+//      as the final row (one partition) or as (acc, max, sum) partials that
+//      decode_reduce_kernel merges with a log-sum-exp.
+// Memory-bound for G <= 8 (1..8 flop per KV byte against a ~20 flop/B VALU
+// ridge), so no matrix cores: the loads and the reduction cost are what
+// matter.  Tokens past the context are excluded by select, never by
+// multiplying with zero, so stale or NaN cache contents never leak.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+
+#include "common.h"
+
+namespace pkv {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kUnitsPerChunk = 4;
+constexpr float kLog2e = 1.4426950408889634f;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// ---- element traits: packed dot product of a 16-byte q slice with a
+// ---- 16-byte K slice, and widening of a 16-byte V slice to floats.
+template <int DT>
+struct Elem;
+
+template <>
+struct Elem<PKV_BF16> {
+  static constexpr int kBytes = 2;
+  static constexpr int kPerLane = 8;
+  __device__ static float dot(const uint4& q, const uint4& k, float acc) {
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.x),
+                                          __builtin_bit_cast(bf16x2_t, k.x), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.y),
+                                          __builtin_bit_cast(bf16x2_t, k.y), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.z),
+                                          __builtin_bit_cast(bf16x2_t, k.z), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.w),
+                                          __builtin_bit_cast(bf16x2_t, k.w), acc, false);
+    return acc;
+  }
+  __device__ static void widen(const uint4& v, float (&f)[8]) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+};
+
+template <>
+struct Elem<PKV_F16> {
+  static constexpr int kBytes = 2;
+  static constexpr int kPerLane = 8;
+  __device__ static float dot(const uint4& q, const uint4& k, float acc) {
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, q.x),
+                                 __builtin_bit_cast(f16x2_t, k.x), acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, q.y),
+                                 __builtin_bit_cast(f16x2_t, k.y), acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, q.z),
+                                 __builtin_bit_cast(f16x2_t, k.z), acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, q.w),
+                                 __builtin_bit_cast(f16x2_t, k.w), acc, false);
+    return acc;
+  }
+  __device__ static void widen(const uint4& v, float (&f)[8]) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f16x2_t h = __builtin_bit_cast(f16x2_t, w[i]);
+      f[2 * i] = float(h.x);
+      f[2 * i + 1] = float(h.y);
+    }
+  }
+};
+
+template <>
+struct Elem<PKV_F32> {
+  static constexpr int kBytes = 4;
+  static constexpr int kPerLane = 4;
+  __device__ static float dot(const uint4& q, const uint4& k, float acc) {
+    acc = fmaf(__uint_as_float(q.x), __uint_as_float(k.x), acc);
+    acc = fmaf(__uint_as_float(q.y), __uint_as_float(k.y), acc);
+    acc = fmaf(__uint_as_float(q.z), __uint_as_float(k.z), acc);
+    acc = fmaf(__uint_as_float(q.w), __uint_as_float(k.w), acc);
+    return acc;
+  }
+  __device__ static void widen(const uint4& v, float (&f)[4]) {
+    f[0] = __uint_as_float(v.x);
+    f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z);
+    f[3] = __uint_as_float(v.w);
+  }
+};
+
+// ---- cross-lane exchange for butterfly steps.  Steps run from the highest
+// ---- lane bit to the lowest; within a row of 16 lanes the DPP mirror
+// ---- patterns flip exactly the bit being reduced while keeping the higher
+// ---- ones, which is all a butterfly step needs.
+template <int M>
+__device__ __forceinline__ float lane_swap(float x) {
+  int v = __float_as_int(x);
+  if constexpr (M == 1) {
+    v = __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
+  } else if constexpr (M == 2) {
+    v = __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
+  } else if constexpr (M == 4) {
+    v = __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);  // row_half_mirror
+  } else if constexpr (M == 8) {
+    v = __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);  // row_mirror
+  } else {
+    v = __shfl_xor(v, M);
+  }
+  return __int_as_float(v);
+}
+
+// Transposed butterfly over the lane bits M, M/2, ..., 1 of `n` values per
+// lane.  While a lane holds more than one value, each step keeps one half
+// (chosen by the lane's bit M) and adds the partner's copy of that half, so
+// the partial sums end up distributed; once one value is left, the
+// remaining steps are plain butterflies.  Afterwards value i of a lane is
+// original value ((lane & (2M-1)) >> plain_steps) * n_left + i.
+template <int M, int N>
+__device__ __forceinline__ void transpose_reduce(float* v, int lane) {
+  if constexpr (M >= 1) {
+    if constexpr (N > 1) {
+      const bool hi = (lane & M) != 0;
+#pragma unroll
+      for (int i = 0; i < N / 2; ++i) {
+        float keep = hi ? v[i + N / 2] : v[i];
+        float send = hi ? v[i] : v[i + N / 2];
+        v[i] = keep + lane_swap<M>(send);
+      }
+      transpose_reduce<M / 2, N / 2>(v, lane);
+    } else {
+      v[0] += lane_swap<M>(v[0]);
+      transpose_reduce<M / 2, 1>(v, lane);
+    }
+  }
+}
+
+__device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
+
+template <int DT, int D, int G>
+struct Cfg {
+  static constexpr int kEs = Elem<DT>::kBytes;
+  static constexpr int kEpl = Elem<DT>::kPerLane;     // elements per lane
+  static constexpr int kRow = D * kEs;                // bytes per token row
+  static constexpr int kLpt = kRow / 16;              // lanes per token row
+  static constexpr int kTpl = 64 / kLpt;              // tokens per unit
+  static constexpr int kChunkTok = kUnitsPerChunk * kTpl;
+  static constexpr int kNv = kUnitsPerChunk * G;      // partial sums per lane
+  // values left per lane after the transposed butterfly, and plain steps
+  static constexpr int kLeft = kNv > kLpt ? kNv / kLpt : 1;
+  static constexpr int kPlainLog = kNv >= kLpt ? 0 : ilog2(kLpt) - ilog2(kNv);
+  static_assert(kRow % 16 == 0 && 64 % kLpt == 0, "row must split across lanes");
+};
+
+// Dynamic LDS: [scores: max(part*G, kWaves*G*D) floats][block ids][m/l].
+template <int DT, int D, int G>
+__global__ __launch_bounds__(kThreads) void decode_partition_kernel(
+    const uint8_t* __restrict__ query, const uint8_t* __restrict__ key_cache,
+    const uint8_t* __restrict__ value_cache,
+    const int32_t* __restrict__ block_tables,
+    const int32_t* __restrict__ context_lens, int32_t num_kv_heads,
+    int32_t log2_bs, int32_t max_blocks, int32_t num_blocks,
+    int32_t max_ctx, int32_t part, int32_t max_parts, float scale_log2,
+    float* __restrict__ out, float* __restrict__ ws_acc,
+    float* __restrict__ ws_ml) {
+  using C = Cfg<DT, D, G>;
+  using E = Elem<DT>;
+  extern __shared__ float smem[];
+
+  const int p_idx = blockIdx.x;
+  const int kvh = blockIdx.y;
+  const int b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int bs = 1 << log2_bs;
+  const int num_heads = num_kv_heads * G;
+
+  const int n = context_lens[b];
+  const bool bad_len =
+      n < 0 || n > max_ctx || int64_t(n) > int64_t(max_blocks) * bs;
+  const int nparts = bad_len ? 1 : max(1, cdiv(n, part));
+  if (p_idx >= nparts) return;
+
+  float* out_row = out + (int64_t(b) * num_heads + int64_t(kvh) * G) * D;
+  if (bad_len || n == 0) {
+    const float fill = bad_len ? __builtin_nanf("") : 0.0f;
+    for (int i = tid; i < G * D; i += kThreads) out_row[i] = fill;
+    return;
+  }
+
+  const int score_floats = max(part * G, kWaves * G * D);
+  float* s_score = smem;
+  int* s_blk = reinterpret_cast<int*>(smem + score_floats);
+  float* s_red = reinterpret_cast<float*>(s_blk + (part >> 3));  // [2][kWaves][G]
+
+  const int p0 = p_idx * part;
+  const int ntok = min(part, n - p0);
+  const int nblk = (ntok + bs - 1) >> log2_bs;
+  const int32_t* table = block_tables + int64_t(b) * max_blocks + (p0 >> log2_bs);
+  bool bad_blk = false;
+  if (tid < nblk) {
+    int id = table[tid];
+    if (id < 0 || id >= num_blocks) {
+      bad_blk = true;
+      id = 0;
+    }
+    s_blk[tid] = id;
+  }
+  bad_blk = __syncthreads_or(bad_blk);
+
+  // q slices of the G heads: lane covers bytes (lane % LPT) * 16 of the row.
+  const int dl = lane % C::kLpt;
+  const int tok_in_unit = lane / C::kLpt;
+  uint4 q[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+    q[g] = *reinterpret_cast<const uint4*>(
+        query + ((int64_t(b) * num_heads + int64_t(kvh) * G + g) * C::kRow) + dl * 16);
+
+  const int64_t tile_bytes = int64_t(bs) * C::kRow;           // one (block, head) tile
+  const int64_t blk_stride = tile_bytes * num_kv_heads;
+  const uint8_t* kbase = key_cache + int64_t(kvh) * tile_bytes + dl * 16;
+  const uint8_t* vbase = value_cache + int64_t(kvh) * tile_bytes + dl * 16;
+  const int nchunks = cdiv(ntok, C::kChunkTok);
+
+  // ---- QK pass --------------------------------------------------------
+  for (int c = wave; c < nchunks; c += kWaves) {
+    const int t0 = c * C::kChunkTok;  // relative to p0
+    uint4 k[kUnitsPerChunk];
+#pragma unroll
+    for (int u = 0; u < kUnitsPerChunk; ++u) {
+      const int tu = t0 + u * C::kTpl;
+      if (tu < ntok) {
+        const int blk = __builtin_amdgcn_readfirstlane(s_blk[tu >> log2_bs]);
+        const int row = ((p0 + tu) & (bs - 1)) + tok_in_unit;
+        k[u] = *reinterpret_cast<const uint4*>(kbase + int64_t(blk) * blk_stride +
+                                               int64_t(row) * C::kRow);
+      } else {
+        k[u] = make_uint4(0, 0, 0, 0);
+      }
+    }
+    float v[C::kNv];
+#pragma unroll
+    for (int u = 0; u < kUnitsPerChunk; ++u)
+#pragma unroll
+      for (int g = 0; g < G; ++g) v[u * G + g] = E::dot(q[g], k[u], 0.0f);
+    transpose_reduce<C::kLpt / 2, C::kNv>(v, lane);
+    const int sub = lane & (C::kLpt - 1);
+    if ((sub & ((1 << C::kPlainLog) - 1)) == 0) {
+#pragma unroll
+      for (int i = 0; i < C::kLeft; ++i) {
+        const int idx = (sub >> C::kPlainLog) * C::kLeft + i;
+        const int u = idx / G, g = idx - (idx / G) * G;
+        const int t = t0 + u * C::kTpl + tok_in_unit;
+        s_score[t * G + g] = t < ntok ? v[i] * scale_log2 : -INFINITY;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- softmax over the partition (entries e = t * G + g; a thread only
+  // ---- ever sees head tid % G because kThreads is a multiple of G) ----
+  const int nent = nchunks * C::kChunkTok * G;
+  float mx = -INFINITY;
+  for (int e = tid; e < nent; e += kThreads) mx = fmaxf(mx, s_score[e]);
+#pragma unroll
+  for (int m = G; m < 64; m <<= 1) mx = fmaxf(mx, __shfl_xor(mx, m));
+  if (lane < G) s_red[wave * G + lane] = mx;
+  __syncthreads();
+  const int my_head = tid % G;
+  float head_max = s_red[my_head];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) head_max = fmaxf(head_max, s_red[w * G + my_head]);
+  float sum = 0.0f;
+  for (int e = tid; e < nent; e += kThreads) {
+    const float p = __builtin_amdgcn_exp2f(s_score[e] - head_max);
+    s_score[e] = p;
+    sum += p;
+  }
+#pragma unroll
+  for (int m = G; m < 64; m <<= 1) sum += __shfl_xor(sum, m);
+  if (lane < G) s_red[kWaves * G + wave * G + lane] = sum;
+  __syncthreads();
+
+  // ---- PV pass ----------------------------------------------------------
+  float acc[G][C::kEpl];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int e = 0; e < C::kEpl; ++e) acc[g][e] = 0.0f;
+
+  for (int c = wave; c < nchunks; c += kWaves) {
+    const int t0 = c * C::kChunkTok;
+    uint4 vv[kUnitsPerChunk];
+#pragma unroll
+    for (int u = 0; u < kUnitsPerChunk; ++u) {
+      const int tu = t0 + u * C::kTpl;
+      if (tu < ntok) {
+        const int blk = __builtin_amdgcn_readfirstlane(s_blk[tu >> log2_bs]);
+        const int row = ((p0 + tu) & (bs - 1)) + tok_in_unit;
+        vv[u] = *reinterpret_cast<const uint4*>(vbase + int64_t(blk) * blk_stride +
+                                                int64_t(row) * C::kRow);
+      } else {
+        vv[u] = make_uint4(0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnitsPerChunk; ++u) {
+      const int t = t0 + u * C::kTpl + tok_in_unit;
+      const bool live = t < ntok;
+      float f[C::kEpl];
+      E::widen(vv[u], f);
+#pragma unroll
+      for (int e = 0; e < C::kEpl; ++e) f[e] = live ? f[e] : 0.0f;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float p = s_score[t * G + g];
+#pragma unroll
+        for (int e = 0; e < C::kEpl; ++e) acc[g][e] = fmaf(p, f[e], acc[g][e]);
+      }
+    }
+  }
+
+  // ---- combine token rows within the wave, then the waves ----------------
+#pragma unroll
+  for (int m = C::kLpt; m < 64; m <<= 1)
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int e = 0; e < C::kEpl; ++e) acc[g][e] += __shfl_xor(acc[g][e], m);
+  __syncthreads();  // everyone is done reading weights from s_score
+  if (lane < C::kLpt) {
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int e = 0; e < C::kEpl; ++e)
+        s_score[(wave * G + g) * D + lane * C::kEpl + e] = acc[g][e];
+  }
+  __syncthreads();
+
+  const float nan = __builtin_nanf("");
+  for (int i = tid; i < G * D; i += kThreads) {
+    const int g = i / D;
+    float a = 0.0f, l = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      a += s_score[w * G * D + i];
+      l += s_red[kWaves * G + w * G + g];
+    }
+    float m = s_red[g];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) m = fmaxf(m, s_red[w * G + g]);
+    if (nparts == 1) {
+      out_row[i] = bad_blk ? nan : a / l;
+    } else {
+      const int64_t row = (int64_t(b) * num_heads + int64_t(kvh) * G + g) * max_parts + p_idx;
+      ws_acc[row * D + (i - g * D)] = bad_blk ? nan : a;
+      if (i - g * D == 0) {
+        ws_ml[row * 2] = bad_blk ? nan : m;
+        ws_ml[row * 2 + 1] = bad_blk ? nan : l;
+      }
+    }
+  }
+}
+
+// Merge the partitions of one (sequence, head): with per-partition max m_p
+// (log2 units), sum l_p and unnormalised acc_p,
+//   out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p,  M = max_p m_p.
+template <int D>
+__global__ __launch_bounds__(64) void decode_reduce_kernel(
+    const int32_t* __restrict__ context_lens, int32_t num_heads,
+    int32_t log2_bs, int32_t max_blocks, int32_t max_ctx, int32_t part,
+    int32_t max_parts, const float* __restrict__ ws_acc,
+    const float* __restrict__ ws_ml, float* __restrict__ out) {
+  const int h = blockIdx.x;
+  const int b = blockIdx.y;
+  const int n = context_lens[b];
+  const bool bad_len = n < 0 || n > max_ctx ||
+                       int64_t(n) > (int64_t(max_blocks) << log2_bs);
+  if (bad_len) return;
+  const int nparts = cdiv(n, part);
+  if (nparts <= 1) return;
+  const int64_t row0 = (int64_t(b) * num_heads + h) * max_parts;
+  float big = -INFINITY;
+  bool any_nan = false;
+  for (int p = 0; p < nparts; ++p) {
+    const float m = ws_ml[(row0 + p) * 2];
+    any_nan |= m != m;
+    big = fmaxf(big, m);
+  }
+  float den = 0.0f;
+  float num[D / 64];
+#pragma unroll
+  for (int j = 0; j < D / 64; ++j) num[j] = 0.0f;
+  for (int p = 0; p < nparts; ++p) {
+    const float w = __builtin_amdgcn_exp2f(ws_ml[(row0 + p) * 2] - big);
+    den = fmaf(w, ws_ml[(row0 + p) * 2 + 1], den);
+#pragma unroll
+    for (int j = 0; j < D / 64; ++j)
+      num[j] = fmaf(w, ws_acc[(row0 + p) * D + j * 64 + threadIdx.x], num[j]);
+  }
+  float* o = out + (int64_t(b) * num_heads + h) * D;
+#pragma unroll
+  for (int j = 0; j < D / 64; ++j)
+    o[j * 64 + threadIdx.x] = any_nan ? __builtin_nanf("") : num[j] / den;
+}
+
+int auto_partition(int max_ctx) {
+  (void)max_ctx;
+  return 512;
+}
+
+int32_t resolve_partition(int32_t partition_size, int32_t block_size,
+                          int32_t max_ctx, int32_t* part) {
+  int32_t p = partition_size == 0 ? auto_partition(max_ctx) : partition_size;
+  if (p < 64 || p > 1024 || p % 64 != 0)
+    return fail(PKV_ERR_INVALID,
+                "partition_size %d must be a multiple of 64 in [64, 1024]",
+                partition_size);
+  if (p < block_size) p = block_size;  // a partition holds whole blocks
+  if (p % block_size != 0)
+    return fail(PKV_ERR_INVALID, "partition_size %d is not a multiple of block_size %d",
+                p, block_size);
+  *part = p;
+  return PKV_OK;
+}
+
+template <int DT, int D, int G>
+hipError_t launch_decode(const void* q, const void* kc, const void* vc,
+                         const int32_t* tables, const int32_t* lens, int B,
+                         int Hkv, int log2_bs, int max_blocks, int num_blocks,
+                         int max_ctx, int part, int max_parts, float scale_log2,
+                         float* out, float* ws_acc, float* ws_ml,
+                         hipStream_t stream) {
+  const int score_floats = std::max(part * G, kWaves * G * D);
+  const size_t lds = size_t(score_floats) * 4 + size_t(part >> 3) * 4 +
+                     size_t(2 * kWaves * G) * 4;
+  hipLaunchKernelGGL((decode_partition_kernel<DT, D, G>),
+                     dim3(max_parts, Hkv, B), dim3(kThreads), lds, stream,
+                     static_cast<const uint8_t*>(q), static_cast<const uint8_t*>(kc),
+                     static_cast<const uint8_t*>(vc), tables, lens, Hkv, log2_bs,
+                     max_blocks, num_blocks, max_ctx, part, max_parts, scale_log2,
+                     out, ws_acc, ws_ml);
+  return hipGetLastError();
+}
+
+template <int DT, int D>
+hipError_t dispatch_group(int G, const void* q, const void* kc, const void* vc,
+                          const int32_t* tables, const int32_t* lens, int B,
+                          int Hkv, int log2_bs, int max_blocks, int num_blocks,
+                          int max_ctx, int part, int max_parts, float sl2,
+                          float* out, float* wa, float* wm, hipStream_t s) {
+  switch (G) {
+    case 1: return launch_decode<DT, D, 1>(q, kc, vc, tables, lens, B, Hkv, log2_bs, max_blocks, num_blocks, max_ctx, part, max_parts, sl2, out, wa, wm, s);
+    case 2: return launch_decode<DT, D, 2>(q, kc, vc, tables, lens, B, Hkv, log2_bs, max_blocks, num_blocks, max_ctx, part, max_parts, sl2, out, wa, wm, s);
+    case 4: return launch_decode<DT, D, 4>(q, kc, vc, tables, lens, B, Hkv, log2_bs, max_blocks, num_blocks, max_ctx, part, max_parts, sl2, out, wa, wm, s);
+    case 8: return launch_decode<DT, D, 8>(q, kc, vc, tables, lens, B, Hkv, log2_bs, max_blocks, num_blocks, max_ctx, part, max_parts, sl2, out, wa, wm, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int DT>
+hipError_t dispatch_dim(int D, int G, const void* q, const void* kc,
+                        const void* vc, const int32_t* tables,
+                        const int32_t* lens, int B, int Hkv, int log2_bs,
+                        int max_blocks, int num_blocks, int max_ctx, int part,
+                        int max_parts, float sl2, float* out, float* wa,
+                        float* wm, hipStream_t s) {
+  if (D == 64)
+    return dispatch_group<DT, 64>(G, q, kc, vc, tables, lens, B, Hkv, log2_bs, max_blocks, num_blocks, max_ctx, part, max_parts, sl2, out, wa, wm, s);
+  return dispatch_group<DT, 128>(G, q, kc, vc, tables, lens, B, Hkv, log2_bs, max_blocks, num_blocks, max_ctx, part, max_parts, sl2, out, wa, wm, s);
+}
+
+size_t workspace_bytes(int B, int Hq, int D, int max_parts) {
+  if (max_parts <= 1) return 0;
+  return size_t(B) * Hq * max_parts * (size_t(D) + 2) * sizeof(float);
+}
+
+}  // namespace
+}  // namespace pkv
+
+using namespace pkv;
+
+extern "C" int32_t pkv_paged_attention_decode_workspace_size(
+    int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+    int32_t max_context_len, int32_t partition_size, size_t* bytes) {
+  if (!bytes) return fail(PKV_ERR_INVALID, "bytes is NULL");
+  if (num_seqs < 0 || num_heads <= 0 || head_dim <= 0 || max_context_len < 0)
+    return fail(PKV_ERR_INVALID, "invalid sizes");
+  int32_t part = 0;
+  // block size does not change the partition count unless it exceeds the
+  // partition; 1 keeps the size an upper bound for every block size.
+  int32_t st = resolve_partition(partition_size, 1, max_context_len, &part);
+  if (st != PKV_OK) return st;
+  const int max_parts = std::max(1, (max_context_len + part - 1) / part);
+  *bytes = workspace_bytes(num_seqs, num_heads, head_dim, max_parts);
+  return ok();
+}
+
+namespace pkv {
+namespace {
+
+struct DecodeArgs {
+  int32_t G = 0, part = 0, max_parts = 0, log2_bs = 0;
+  float* ws_acc = nullptr;
+  float* ws_ml = nullptr;
+};
+
+// Checks every host-visible argument of the decode calls and derives the
+// launch geometry.  `need_inputs` is false for the merge stage, which reads
+// only lengths, workspace and output.
+int32_t prepare_decode(const void* query, const void* key_cache,
+                       const void* value_cache, const int32_t* block_tables,
+                       const int32_t* context_lens, int32_t num_seqs,
+                       int32_t num_heads, int32_t num_kv_heads,
+                       int32_t head_dim, int32_t block_size,
+                       int32_t max_blocks_per_seq, int32_t num_blocks,
+                       int32_t max_context_len, float scale,
+                       int32_t partition_size, float* out, void* workspace,
+                       size_t workspace_bytes_given, int32_t dtype,
+                       bool need_inputs, DecodeArgs* a) {
+  if (dtype_bytes(dtype) == 0) return fail(PKV_ERR_INVALID, "unknown dtype %d", dtype);
+  if (num_seqs < 0) return fail(PKV_ERR_INVALID, "negative num_seqs");
+  if (num_seqs > 65535) return fail(PKV_ERR_UNSUPPORTED, "at most 65535 sequences per call");
+  if (num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID, "num_heads %d must be a positive multiple of num_kv_heads %d",
+                num_heads, num_kv_heads);
+  if (num_kv_heads > 65535) return fail(PKV_ERR_UNSUPPORTED, "too many kv heads");
+  a->G = num_heads / num_kv_heads;
+  if (a->G != 1 && a->G != 2 && a->G != 4 && a->G != 8)
+    return fail(PKV_ERR_UNSUPPORTED, "heads per kv head must be 1, 2, 4 or 8 (got %d)", a->G);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", head_dim);
+  if (!is_pow2(block_size) || block_size < 8 || block_size > 256)
+    return fail(PKV_ERR_UNSUPPORTED, "block_size must be a power of two in [8, 256]");
+  if (max_blocks_per_seq <= 0 || num_blocks <= 0 || max_context_len < 0)
+    return fail(PKV_ERR_INVALID, "invalid table/pool sizes");
+  if (int64_t(num_blocks) * block_size >= (int64_t(1) << 31))
+    return fail(PKV_ERR_INVALID, "num_blocks * block_size must be below 2^31");
+  if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID, "scale must be finite");
+  if (num_seqs > 0) {
+    if (!context_lens || !out) return fail(PKV_ERR_INVALID, "NULL pointer argument");
+    if (need_inputs && (!query || !key_cache || !value_cache || !block_tables))
+      return fail(PKV_ERR_INVALID, "NULL pointer argument");
+    if (need_inputs && (!aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache)))
+      return fail(PKV_ERR_INVALID, "query and caches must be 16-byte aligned");
+    if (!aligned16(out)) return fail(PKV_ERR_INVALID, "out must be 16-byte aligned");
+  }
+  int32_t st = resolve_partition(partition_size, block_size, max_context_len, &a->part);
+  if (st != PKV_OK) return st;
+  a->max_parts = std::max(1, (max_context_len + a->part - 1) / a->part);
+  if (a->max_parts > 65535) return fail(PKV_ERR_UNSUPPORTED, "context too long");
+  const size_t need = workspace_bytes(num_seqs, num_heads, head_dim, a->max_parts);
+  if (need > 0 && (!workspace || workspace_bytes_given < need))
+    return fail(PKV_ERR_BUFFER_TOO_SMALL, "workspace needs %zu bytes, got %zu", need,
+                workspace ? workspace_bytes_given : size_t(0));
+  if (need > 0 && !aligned16(workspace))
+    return fail(PKV_ERR_INVALID, "workspace must be 16-byte aligned");
+  a->ws_acc = need ? static_cast<float*>(workspace) : nullptr;
+  a->ws_ml = need ? a->ws_acc + size_t(num_seqs) * num_heads * a->max_parts * head_dim
+                  : nullptr;
+  a->log2_bs = 0;
+  while ((1 << a->log2_bs) < block_size) ++a->log2_bs;
+  return PKV_OK;
+}
+
+template <int D>
+hipError_t launch_merge(const int32_t* lens, int B, int Hq, int log2_bs,
+                        int max_blocks, int max_ctx, int part, int max_parts,
+                        const float* ws_acc, const float* ws_ml, float* out,
+                        hipStream_t s) {
+  hipLaunchKernelGGL((decode_reduce_kernel<D>), dim3(Hq, B), dim3(64), 0, s, lens,
+                     Hq, log2_bs, max_blocks, max_ctx, part, max_parts, ws_acc,
+                     ws_ml, out);
+  return hipGetLastError();
+}
+
+}  // namespace
+}  // namespace pkv
+
+extern "C" int32_t pkv_paged_attention_decode_partials(
+    const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, const int32_t* context_lens,
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+    int32_t num_blocks, int32_t max_context_len, float scale,
+    int32_t partition_size, float* out, void* workspace,
+    size_t workspace_bytes_given, int32_t dtype, void* stream) {
+  DecodeArgs a;
+  int32_t st = prepare_decode(query, key_cache, value_cache, block_tables, context_lens,
+                              num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                              max_blocks_per_seq, num_blocks, max_context_len, scale,
+                              partition_size, out, workspace, workspace_bytes_given, dtype,
+                              true, &a);
+  if (st != PKV_OK) return st;
+  if (num_seqs == 0) return ok();
+  const float sl2 = scale * kLog2e;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  switch (dtype) {
+    case PKV_BF16:
+      e = dispatch_dim<PKV_BF16>(head_dim, a.G, query, key_cache, value_cache, block_tables, context_lens, num_seqs, num_kv_heads, a.log2_bs, max_blocks_per_seq, num_blocks, max_context_len, a.part, a.max_parts, sl2, out, a.ws_acc, a.ws_ml, s);
+      break;
+    case PKV_F16:
+      e = dispatch_dim<PKV_F16>(head_dim, a.G, query, key_cache, value_cache, block_tables, context_lens, num_seqs, num_kv_heads, a.log2_bs, max_blocks_per_seq, num_blocks, max_context_len, a.part, a.max_parts, sl2, out, a.ws_acc, a.ws_ml, s);
+      break;
+    default:
+      e = dispatch_dim<PKV_F32>(head_dim, a.G, query, key_cache, value_cache, block_tables, context_lens, num_seqs, num_kv_heads, a.log2_bs, max_blocks_per_seq, num_blocks, max_context_len, a.part, a.max_parts, sl2, out, a.ws_acc, a.ws_ml, s);
+      break;
+  }
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+extern "C" int32_t pkv_paged_attention_decode_merge(
+    const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t max_blocks_per_seq, int32_t max_context_len,
+    int32_t partition_size, float* out, void* workspace,
+    size_t workspace_bytes_given, void* stream) {
+  DecodeArgs a;
+  int32_t st = prepare_decode(nullptr, nullptr, nullptr, nullptr, context_lens, num_seqs,
+                              num_heads, num_kv_heads, head_dim, block_size,
+                              max_blocks_per_seq, 1, max_context_len, 1.0f, partition_size,
+                              out, workspace, workspace_bytes_given, PKV_F32, false, &a);
+  if (st != PKV_OK) return st;
+  if (num_seqs == 0 || a.max_parts <= 1) return ok();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = head_dim == 64
+      ? launch_merge<64>(context_lens, num_seqs, num_heads, a.log2_bs, max_blocks_per_seq,
+                         max_context_len, a.part, a.max_parts, a.ws_acc, a.ws_ml, out, s)
+      : launch_merge<128>(context_lens, num_seqs, num_heads, a.log2_bs, max_blocks_per_seq,
+                          max_context_len, a.part, a.max_parts, a.ws_acc, a.ws_ml, out, s);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "decode merge launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+extern "C" int32_t pkv_paged_attention_decode(
+    const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, const int32_t* context_lens,
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+    int32_t num_blocks, int32_t max_context_len, float scale,
+    int32_t partition_size, float* out, void* workspace,
+    size_t workspace_bytes_given, int32_t dtype, void* stream) {
+  int32_t st = pkv_paged_attention_decode_partials(
+      query, key_cache, value_cache, block_tables, context_lens, num_seqs, num_heads,
+      num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, max_context_len,
+      scale, partition_size, out, workspace, workspace_bytes_given, dtype, stream);
+  if (st != PKV_OK) return st;
+  return pkv_paged_attention_decode_merge(context_lens, num_seqs, num_heads, num_kv_heads,
+                                          head_dim, block_size, max_blocks_per_seq,
+                                          max_context_len, partition_size, out, workspace,
+                                          workspace_bytes_given, stream);
+}

@@ -1,0 +1,156 @@
+// Cache writes on gfx950: slot-mapped append of new K/V rows and whole-block
+// copy (the data side of copy-on-write).
+//
+// Append: KV-cache article (intelliparadigm) §2.1 -- position p of a sequence
+// is row p % block_size of physical block table[p / block_size]; the host
+// allocator turns that into one flat slot per new token.  Explainer
+// (openEuler/CSDN), serving section: each stored token adds one K and one V
+// vector to the cache.  Copy: explainer, memory-sharing section -- shared
+// blocks are duplicated before a sequence writes into a shared, partly
+// filled block.
+//
+// Both kernels are pure data movement (HBM-bound): every lane moves one
+// 16-byte vector, consecutive lanes move consecutive 16-byte pieces of the
+// same row, so a wavefront reads and writes whole 1 KiB spans.
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+
+namespace pkv {
+namespace {
+
+// One lane per 16-byte piece of a (token, kv-head) row.
+//   key/value   [T][H][row]           row = head_dim * elem bytes
+//   caches      [NB][H][BS][row]
+__global__ __launch_bounds__(256) void append_kernel(
+    const uint4* __restrict__ key, const uint4* __restrict__ value,
+    uint4* __restrict__ key_cache, uint4* __restrict__ value_cache,
+    const int32_t* __restrict__ slots, int64_t total_pieces,
+    int32_t pieces_per_row, int32_t num_kv_heads, int32_t block_size,
+    int64_t num_slots) {
+  int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= total_pieces) return;
+  int64_t row = i / pieces_per_row;            // (token, head) row index
+  int32_t piece = int32_t(i - row * pieces_per_row);
+  int64_t token = row / num_kv_heads;
+  int32_t head = int32_t(row - token * num_kv_heads);
+  int32_t slot = slots[token];
+  if (slot < 0 || slot >= num_slots) return;   // skipped row / out of pool
+  int32_t blk = slot / block_size;
+  int32_t off = slot - blk * block_size;
+  int64_t dst = ((int64_t(blk) * num_kv_heads + head) * block_size + off) *
+                    pieces_per_row + piece;
+  key_cache[dst] = key[i];
+  value_cache[dst] = value[i];
+}
+
+// grid.y = pair; each lane copies 16-byte pieces of one block, strided.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(
+    uint4* __restrict__ key_cache, uint4* __restrict__ value_cache,
+    const int32_t* __restrict__ src, const int32_t* __restrict__ dst,
+    int32_t num_blocks, int64_t pieces_per_block) {
+  int32_t s = src[blockIdx.y];
+  int32_t d = dst[blockIdx.y];
+  if (s < 0 || s >= num_blocks || d < 0 || d >= num_blocks) return;
+  const uint4* ks = key_cache + int64_t(s) * pieces_per_block;
+  const uint4* vs = value_cache + int64_t(s) * pieces_per_block;
+  uint4* kd = key_cache + int64_t(d) * pieces_per_block;
+  uint4* vd = value_cache + int64_t(d) * pieces_per_block;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+       i < pieces_per_block; i += int64_t(gridDim.x) * blockDim.x) {
+    kd[i] = ks[i];
+    vd[i] = vs[i];
+  }
+}
+
+int32_t check_cache_args(int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int32_t num_blocks,
+                         int32_t dtype) {
+  if (dtype_bytes(dtype) == 0)
+    return fail(PKV_ERR_INVALID, "unknown dtype %d", dtype);
+  if (num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      num_blocks <= 0)
+    return fail(PKV_ERR_INVALID,
+                "sizes must be positive (kv_heads %d, head_dim %d, "
+                "block_size %d, num_blocks %d)",
+                num_kv_heads, head_dim, block_size, num_blocks);
+  if ((int64_t(head_dim) * dtype_bytes(dtype)) % 16 != 0)
+    return fail(PKV_ERR_INVALID,
+                "head_dim * element size must be a multiple of 16 bytes");
+  if (int64_t(num_blocks) * block_size >= (int64_t(1) << 31))
+    return fail(PKV_ERR_INVALID, "num_blocks * block_size must be below 2^31");
+  return PKV_OK;
+}
+
+}  // namespace
+}  // namespace pkv
+
+using namespace pkv;
+
+extern "C" int32_t pkv_paged_kv_append(
+    const void* key, const void* value, void* key_cache, void* value_cache,
+    const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t dtype,
+    void* stream) {
+  int32_t st = check_cache_args(num_kv_heads, head_dim, block_size,
+                                num_blocks, dtype);
+  if (st != PKV_OK) return st;
+  if (num_tokens < 0)
+    return fail(PKV_ERR_INVALID, "negative num_tokens %d", num_tokens);
+  if (num_tokens == 0) return ok();
+  if (!key || !value || !key_cache || !value_cache || !slot_mapping)
+    return fail(PKV_ERR_INVALID, "NULL pointer argument");
+  if (!aligned16(key) || !aligned16(value) || !aligned16(key_cache) ||
+      !aligned16(value_cache))
+    return fail(PKV_ERR_INVALID, "K/V buffers must be 16-byte aligned");
+  const int32_t pieces = head_dim * dtype_bytes(dtype) / 16;
+  const int64_t total = int64_t(num_tokens) * num_kv_heads * pieces;
+  const int64_t blocks = (total + 255) / 256;
+  if (blocks >= (int64_t(1) << 31))
+    return fail(PKV_ERR_INVALID, "append too large for one launch");
+  hipLaunchKernelGGL(append_kernel, dim3(unsigned(blocks)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream),
+                     static_cast<const uint4*>(key),
+                     static_cast<const uint4*>(value),
+                     static_cast<uint4*>(key_cache),
+                     static_cast<uint4*>(value_cache), slot_mapping, total,
+                     pieces, num_kv_heads, block_size,
+                     int64_t(num_blocks) * block_size);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return fail(PKV_ERR_HIP, "append launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+extern "C" int32_t pkv_copy_blocks(void* key_cache, void* value_cache,
+                                   const int32_t* src, const int32_t* dst,
+                                   int32_t num_pairs, int32_t num_blocks,
+                                   int32_t num_kv_heads, int32_t block_size,
+                                   int32_t head_dim, int32_t dtype,
+                                   void* stream) {
+  int32_t st = check_cache_args(num_kv_heads, head_dim, block_size,
+                                num_blocks, dtype);
+  if (st != PKV_OK) return st;
+  if (num_pairs < 0)
+    return fail(PKV_ERR_INVALID, "negative num_pairs %d", num_pairs);
+  if (num_pairs == 0) return ok();
+  if (!key_cache || !value_cache || !src || !dst)
+    return fail(PKV_ERR_INVALID, "NULL pointer argument");
+  if (!aligned16(key_cache) || !aligned16(value_cache))
+    return fail(PKV_ERR_INVALID, "caches must be 16-byte aligned");
+  if (num_pairs > 65535)
+    return fail(PKV_ERR_INVALID, "at most 65535 pairs per call");
+  const int64_t pieces = int64_t(num_kv_heads) * block_size * head_dim *
+                         dtype_bytes(dtype) / 16;
+  int64_t gx = (pieces + 255) / 256;
+  if (gx > 64) gx = 64;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(unsigned(gx), unsigned(num_pairs)),
+                     dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<uint4*>(key_cache),
+                     static_cast<uint4*>(value_cache), src, dst, num_blocks,
+                     pieces);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return fail(PKV_ERR_HIP, "copy_blocks launch: %s", hipGetErrorString(e));
+  return ok();
+}
