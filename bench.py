@@ -95,7 +95,8 @@ def gpu_run(args, w, torch, pkv, workloads):
     q = (torch.randn((total_steps, b, w.num_heads, w.head_dim), generator=gen, device=dev)
          * w.std).to(w.dtype)
     out = torch.empty((b, w.num_heads, w.head_dim), dtype=torch.float32, device=dev)
-    ws_bytes = pkv.paged_attention_decode_workspace_size(b, w.num_heads, w.head_dim, max_len, part)
+    ws_bytes = pkv.paged_attention_decode_workspace_size(b, w.num_heads, w.num_kv_heads, w.head_dim,
+                                                         max_len, part)
     workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
 
     tables_d = torch.empty((b, max_blocks), dtype=torch.int32, device=dev)

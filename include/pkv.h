@@ -203,10 +203,13 @@ int32_t pkv_copy_blocks(void* key_cache, void* value_cache,
                         int32_t head_dim, int32_t dtype, void* stream);
 
 /* Workspace needed by pkv_paged_attention_decode for these sizes, in
- * bytes (0 when no sequence needs more than one partition). */
+ * bytes (0 when no sequence needs more than one partition).  Pass the same
+ * partition_size as to the decode call (0 = automatic: the choice depends
+ * on num_seqs, num_kv_heads and max_context_len). */
 int32_t pkv_paged_attention_decode_workspace_size(
-    int32_t num_seqs, int32_t num_heads, int32_t head_dim,
-    int32_t max_context_len, int32_t partition_size, size_t* bytes);
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t max_context_len, int32_t partition_size,
+    size_t* bytes);
 
 /* PagedAttention decode: one query row per sequence over its paged KV
  * (article §2.1 pseudo-code: gather the sequence's blocks through its

@@ -92,7 +92,8 @@ _SIGNATURES = {
     "pkv_build_block_tables": (_I32, [_P, _PI64, _I32, _I32, _PI32, _PI32]),
     "pkv_paged_kv_append": (_I32, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P]),
     "pkv_copy_blocks": (_I32, [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P]),
-    "pkv_paged_attention_decode_workspace_size": (_I32, [_I32, _I32, _I32, _I32, _I32, ctypes.POINTER(ctypes.c_size_t)]),
+    "pkv_paged_attention_decode_workspace_size": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32,
+                                                         ctypes.POINTER(ctypes.c_size_t)]),
     "pkv_paged_attention_decode": (_I32, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                                           ctypes.c_float, _I32, _P, _P, ctypes.c_size_t, _I32, _P]),
     "pkv_paged_attention_decode_partials": (_I32, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
@@ -315,12 +316,13 @@ def copy_blocks(key_cache, value_cache, src, dst):
                                 _dtype_code(key_cache), _stream(key_cache)))
 
 
-def paged_attention_decode_workspace_size(num_seqs, num_heads, head_dim, max_context_len,
-                                          partition_size=0):
+def paged_attention_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim,
+                                          max_context_len, partition_size=0):
+    """Bytes of workspace pkv_paged_attention_decode needs for these sizes."""
     out = ctypes.c_size_t()
-    _check(_lib.pkv_paged_attention_decode_workspace_size(num_seqs, num_heads, head_dim,
-                                                          max_context_len, partition_size,
-                                                          ctypes.byref(out)))
+    _check(_lib.pkv_paged_attention_decode_workspace_size(num_seqs, num_heads, num_kv_heads,
+                                                          head_dim, max_context_len,
+                                                          partition_size, ctypes.byref(out)))
     return out.value
 
 
@@ -338,7 +340,8 @@ def _decode_args(query, key_cache, value_cache, block_tables, context_lens, max_
     _dev(out, "out", dtype=torch.float32, ndim=3)
     if tuple(out.shape) != (b, hq, d):
         raise InvalidArgument("out must be [B, Hq, D]")
-    need = paged_attention_decode_workspace_size(b, hq, d, int(max_context_len), partition_size)
+    need = paged_attention_decode_workspace_size(b, hq, hkv, d, int(max_context_len),
+                                                 partition_size)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
     ws_ptr, ws_bytes = (None, 0)

@@ -48,11 +48,21 @@ def test_device_calls_reject_bad_arguments_before_launch():
     assert lib.pkv_paged_attention_decode(null, null, null, null, null, 2, 6, 2, 128, 16, 8, 64,
                                           100, 1.0, 0, null, null, 0, 2, null) == 7
     # decode: partition size not a multiple of 64
-    assert lib.pkv_paged_attention_decode_workspace_size(2, 4, 128, 100, 100, ctypes.byref(ws)) == 1
-    assert lib.pkv_paged_attention_decode_workspace_size(2, 4, 128, 100, 0, ctypes.byref(ws)) == 0
+    assert lib.pkv_paged_attention_decode_workspace_size(2, 4, 4, 128, 100, 100,
+                                                         ctypes.byref(ws)) == 1
+    assert lib.pkv_paged_attention_decode_workspace_size(2, 4, 4, 128, 100, 0,
+                                                         ctypes.byref(ws)) == 0
     assert ws.value == 0                     # one partition: no workspace
-    assert lib.pkv_paged_attention_decode_workspace_size(2, 4, 128, 1000, 512, ctypes.byref(ws)) == 0
+    assert lib.pkv_paged_attention_decode_workspace_size(2, 4, 4, 128, 1000, 512,
+                                                         ctypes.byref(ws)) == 0
     assert ws.value == 2 * 4 * 2 * (128 + 2) * 4
+    # automatic partition: small grids get shorter partitions (more of them)
+    assert lib.pkv_paged_attention_decode_workspace_size(1, 8, 8, 128, 4096, 0,
+                                                         ctypes.byref(ws)) == 0
+    assert ws.value == 1 * 8 * (4096 // 128) * (128 + 2) * 4
+    assert lib.pkv_paged_attention_decode_workspace_size(64, 32, 32, 128, 2000, 0,
+                                                         ctypes.byref(ws)) == 0
+    assert ws.value == 64 * 32 * 2 * (128 + 2) * 4
     # decode: NULL pointers with otherwise valid sizes
     assert lib.pkv_paged_attention_decode(null, null, null, null, null, 2, 4, 4, 128, 16, 8, 64,
                                           100, 1.0, 0, null, null, 0, 2, null) == 1
