@@ -265,28 +265,36 @@ int32_t pkv_paged_attention_decode_merge(
     size_t workspace_bytes, void* stream);
 
 /* Causal chunked prefill against the same paged cache (article §4.1/§4.2:
- * long prompts in chunks).  The chunk's K/V must already be appended.
- *   query        [total_q][num_heads][head_dim], rows cu_query_lens[b] ..
- *                cu_query_lens[b+1]-1 belong to sequence b
- *   cu_query_lens [num_seqs + 1] int32 device, non-decreasing, from 0
+ * long prompts in chunks; §2.1: the same block-table gather and softmax).
+ * The chunk's K/V must already be appended.
+ *   query        [total_query_rows][num_heads][head_dim], cache dtype; rows
+ *                cu_query_lens[b] .. cu_query_lens[b+1]-1 belong to
+ *                sequence b (its chunk of c_b rows)
+ *   cu_query_lens [num_seqs + 1] int32 device, non-decreasing, from 0,
+ *                at most total_query_rows
  *   context_lens [num_seqs] int32 device, cached tokens INCLUDING the
  *                chunk; chunk row i sits at position
  *                context_lens[b] - c_b + i and attends to positions
  *                0 .. context_lens[b] - c_b + i
  *   max_query_len host-known bound of every c_b (sizes the grid)
- *   out          [total_q][num_heads][head_dim] float32
- * Rows of a sequence whose chunk is longer than its context, longer than
- * max_query_len, or whose table is inconsistent are written as NaN.
- * Supported: dtype F16 or BF16 (matrix-core path); head_dim 128 (and 64);
- * num_heads / num_kv_heads in {1, 2, 4, 8}; block_size a power of two in
- * [16, 256]. */
+ *   out          [total_query_rows][num_heads][head_dim] float32
+ * Rows of a sequence whose chunk is longer than its context or than
+ * max_query_len, whose context exceeds max_blocks_per_seq * block_size,
+ * or whose used table entries fall outside [0, num_blocks), are written as
+ * NaN.  A sequence whose cu_query_lens entries are decreasing, negative or
+ * past total_query_rows has no rows that can be located: nothing is
+ * written for it.  Rows the chunks do not cover are left untouched.
+ * Supported: dtype F16 or BF16 (matrix-core path, float32 softmax and
+ * accumulation); head_dim 128; num_heads a multiple of num_kv_heads;
+ * block_size a power of two in [16, 256]. */
 int32_t pkv_paged_attention_prefill(
     const void* query, const void* key_cache, const void* value_cache,
     const int32_t* block_tables, const int32_t* context_lens,
     const int32_t* cu_query_lens, int32_t num_seqs, int32_t num_heads,
     int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-    int32_t max_blocks_per_seq, int32_t num_blocks, int32_t max_query_len,
-    float scale, float* out, int32_t dtype, void* stream);
+    int32_t max_blocks_per_seq, int32_t num_blocks, int32_t total_query_rows,
+    int32_t max_query_len, float scale, float* out, int32_t dtype,
+    void* stream);
 
 #ifdef __cplusplus
 }

@@ -101,7 +101,7 @@ _SIGNATURES = {
     "pkv_paged_attention_decode_merge": (_I32, [_P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P,
                                                 ctypes.c_size_t, _P]),
     "pkv_paged_attention_prefill": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
-                                           ctypes.c_float, _P, _I32, _P]),
+                                           _I32, ctypes.c_float, _P, _I32, _P]),
 }
 
 
@@ -426,6 +426,6 @@ def paged_attention_prefill(query, key_cache, value_cache, block_tables, context
     _check(_lib.pkv_paged_attention_prefill(
         query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(), block_tables.data_ptr(),
         context_lens.data_ptr(), cu_query_lens.data_ptr(), b, hq, hkv, d, bs,
-        block_tables.shape[1], nb, int(max_query_len), float(scale), out.data_ptr(),
+        block_tables.shape[1], nb, total, int(max_query_len), float(scale), out.data_ptr(),
         _dtype_code(key_cache), _stream(query)))
     return out

@@ -1,16 +1,411 @@
-// Causal chunked prefill against the paged cache (KV-cache article,
-// intelliparadigm, §4.1/§4.2: long prompts are processed in chunks).
-// The matrix-core kernel is not in this build yet: the entry point exists
-// so the C ABI is complete, and reports PKV_ERR_UNSUPPORTED.
+// Causal chunked prefill against the paged cache, on gfx950 matrix cores.
+//
+// What is computed (KV-cache article, intelliparadigm, §2.1 pseudo-code for
+// the paged gather and softmax(q K^T) V; §4.1/§4.2 for chunked prefill): a
+// chunk of c_b new rows of sequence b, whose K/V are already in the cache
+// (n_b tokens cached, chunk included), sits at positions n_b - c_b ..
+// n_b - 1; row i attends to positions 0 .. n_b - c_b + i, gathered through
+// the block table.
+//
+// Unlike decode this is a dense contraction (128 query rows share every
+// K/V tile), so both products run on MFMA (v_mfma_f32_16x16x32_{bf16,f16}):
+//   * one workgroup = 4 wavefronts = 128 query rows of one query head of one
+//     sequence; each wavefront owns 32 rows (two 16-row groups);
+//   * K/V are walked in tiles of 64 keys.  The workgroup gathers a tile
+//     through the block table into LDS -- K row-major, V transposed -- while
+//     the previous tile is being computed (the next tile's global loads are
+//     in flight during the MFMA work);
+//   * S^T = K Q^T (16 keys x 16 rows per MFMA): the accumulator layout puts
+//     one query row per lane column and 4 keys per lane, which is exactly
+//     the B-operand layout of O^T = V^T P^T once the 8 keys a lane holds
+//     for a 32-key step are given consecutive columns of V^T in LDS.  So the
+//     online softmax (running max, rescale, sum) needs only two cross-lane
+//     steps per row and P never leaves registers;
+//   * P is fed to the MFMA as hi + lo halves in the cache's 16-bit type
+//     (hi = round(p), lo = round(p - hi)), which keeps the weights exact to
+//     about 16 bits: a single 16-bit P would put rows with a few dominant
+//     keys past a 2e-3 tolerance.  Accumulation and softmax are float32.
+// Keys past the causal limit are excluded by select (-inf before exp), and
+// keys past the needed range are zero-filled in LDS, so stale or NaN cache
+// contents never reach an output.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
+
 #include "common.h"
+
+namespace pkv {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kD = 128;               // head dim served by this kernel
+constexpr int kQTile = 32 * kWaves;   // query rows per workgroup
+constexpr int kKTile = 64;            // keys per K/V tile
+constexpr int kKRow = kD * 2 + 16;    // LDS bytes per K row (16 B pad)
+constexpr int kVtRow = kKTile * 2 + 16;  // LDS bytes per V^T row (16 B pad)
+constexpr int kLdsK = kKTile * kKRow;
+constexpr int kLdsV = kD * kVtRow;
+constexpr float kLog2e = 1.4426950408889634f;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// 16-bit element type of the cache: the MFMA and the hi/lo split of P.
+template <int DT>
+struct Half;
+
+template <>
+struct Half<PKV_BF16> {
+  __device__ static f32x4 mma(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  // p = hi + lo with both halves representable (round to nearest even).
+  __device__ static void split(float p, uint32_t& hi, uint32_t& lo) {
+    const __bf16 h = static_cast<__bf16>(p);
+    const __bf16 l = static_cast<__bf16>(p - static_cast<float>(h));
+    hi = __builtin_bit_cast(uint16_t, h);
+    lo = __builtin_bit_cast(uint16_t, l);
+  }
+};
+
+template <>
+struct Half<PKV_F16> {
+  __device__ static f32x4 mma(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  __device__ static void split(float p, uint32_t& hi, uint32_t& lo) {
+    const _Float16 h = static_cast<_Float16>(p);
+    const _Float16 l = static_cast<_Float16>(p - static_cast<float>(h));
+    hi = __builtin_bit_cast(uint16_t, h);
+    lo = __builtin_bit_cast(uint16_t, l);
+  }
+};
+
+__device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// Column of V^T (in LDS) that holds key k of a 64-key tile.  Write k as
+// 32 s + 16 t + 4 g + r (s: 32-key MFMA step, t: which 16-key S^T tile of
+// the step, g: lane group, r: accumulator register).  The lanes of group g
+// hold, for step s, the keys with t in {0,1} and r in 0..3 -- eight keys
+// that must sit in consecutive columns for one 16-byte A-operand read.
+__device__ __forceinline__ int vt_col(int k) {
+  const int s = k >> 5, t = (k >> 4) & 1, g = (k >> 2) & 3, r = k & 3;
+  return 32 * s + 8 * g + 4 * t + r;
+}
+
+// Grid: x = query head (permuted so that heads of one KV group share an
+// XCD when num_heads % 8 == 0), y = 128-row tile of the chunk, z = sequence.
+template <int DT>
+__global__ __launch_bounds__(kThreads) void prefill_kernel(
+    const uint16_t* __restrict__ query, const uint16_t* __restrict__ key_cache,
+    const uint16_t* __restrict__ value_cache, const int32_t* __restrict__ block_tables,
+    const int32_t* __restrict__ context_lens, const int32_t* __restrict__ cu_query_lens,
+    int32_t num_heads, int32_t group, int32_t log2_bs, int32_t max_blocks,
+    int32_t num_blocks, int32_t total_q, int32_t max_q, float scale_log2,
+    float* __restrict__ out) {
+  using H = Half<DT>;
+  __shared__ __attribute__((aligned(16))) uint8_t s_k[kLdsK];
+  __shared__ __attribute__((aligned(16))) uint8_t s_vt[kLdsV];
+
+  const int xcd_slice = num_heads >> 3;
+  const int h = (num_heads & 7) == 0
+                    ? (blockIdx.x & 7) * xcd_slice + (blockIdx.x >> 3)
+                    : blockIdx.x;
+  const int qt = blockIdx.y;
+  const int b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kvh = h / group;
+  const int num_kv_heads = num_heads / group;
+  const int bs = 1 << log2_bs;
+
+  const int q0 = cu_query_lens[b], q1 = cu_query_lens[b + 1];
+  if (q0 < 0 || q1 < q0 || q1 > total_q) return;  // rows unknown: nothing written
+  const int c = q1 - q0;
+  const int r0 = qt * kQTile;
+  if (r0 >= c) return;
+  const int n = context_lens[b];
+  const int rows_here = min(kQTile, c - r0);
+
+  const bool bad_len = c > n || c > max_q || int64_t(n) > (int64_t(max_blocks) << log2_bs);
+  if (bad_len) {
+    const float nan = __builtin_nanf("");
+    for (int i = tid; i < rows_here * kD; i += kThreads)
+      out[(int64_t(q0 + r0 + i / kD) * num_heads + h) * kD + (i % kD)] = nan;
+    return;
+  }
+
+  const int pos_base = n - c;                    // position of chunk row 0
+  const int kv_end = pos_base + r0 + rows_here;  // keys [0, kv_end) are needed
+  const int ntiles = cdiv(kv_end, kKTile);
+
+  // ---- this wavefront's rows ------------------------------------------------
+  const int wrows = max(0, min(32, rows_here - 32 * wave));
+  const int pos_first = pos_base + r0 + 32 * wave;  // position of its row 0
+  const int pos_last = pos_first + wrows - 1;
+  const int col = lane & 15;  // query row within a 16-row group / key within 16
+  const int grp = lane >> 4;  // lane group: 8-element k slice, 4-row output slice
+
+  // Q^T as the B operand of S^T = K Q^T: lane holds row (16 qg + col), head
+  // dims 32 ks + 8 grp .. + 7.  Rows past the chunk are zero.
+  u32x4 qf[2][kD / 32];
+#pragma unroll
+  for (int qg = 0; qg < 2; ++qg) {
+    const int i = r0 + 32 * wave + 16 * qg + col;
+#pragma unroll
+    for (int ks = 0; ks < kD / 32; ++ks) {
+      if (i < c) {
+        qf[qg][ks] = *reinterpret_cast<const u32x4*>(
+            query + (int64_t(q0 + i) * num_heads + h) * kD + 32 * ks + 8 * grp);
+      } else {
+        qf[qg][ks] = u32x4{0, 0, 0, 0};
+      }
+    }
+  }
+
+  // ---- tile gather: thread = (16-byte piece pc of a row, key quad kq) -----
+  const int pc = tid & 15;
+  const int kq = tid >> 4;  // keys 4 kq .. 4 kq + 3 of the tile
+  const int64_t tile_elems = int64_t(bs) * kD;
+  const int64_t blk_elems = tile_elems * num_kv_heads;
+  const int32_t* table = block_tables + int64_t(b) * max_blocks;
+  bool bad_blk = false;
+  u32x4 kr[4], vr[4];
+
+  auto load_tile = [&](int j) {
+    const int key = j * kKTile + 4 * kq;  // 4 | bs: the quad is in one block
+    if (key < kv_end) {
+      int id = table[key >> log2_bs];
+      if (id < 0 || id >= num_blocks) {
+        bad_blk = true;
+        id = 0;
+      }
+      const int64_t base = int64_t(id) * blk_elems + int64_t(kvh) * tile_elems +
+                           int64_t(key & (bs - 1)) * kD + 8 * pc;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        // rows past kv_end inside the quad are zeroed at the LDS store
+        kr[jj] = *reinterpret_cast<const u32x4*>(key_cache + base + jj * kD);
+        vr[jj] = *reinterpret_cast<const u32x4*>(value_cache + base + jj * kD);
+      }
+    } else {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        kr[jj] = u32x4{0, 0, 0, 0};
+        vr[jj] = u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+
+  auto store_tile = [&](int j) {
+    const int key = j * kKTile + 4 * kq;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      if (key + jj >= kv_end) {
+        kr[jj] = u32x4{0, 0, 0, 0};
+        vr[jj] = u32x4{0, 0, 0, 0};
+      }
+      *reinterpret_cast<u32x4*>(s_k + (4 * kq + jj) * kKRow + 16 * pc) = kr[jj];
+    }
+    // V^T: element e of the piece is head dim 8 pc + e; the quad's four keys
+    // go to four consecutive columns (one 8-byte store per head dim).
+    const int colb = 2 * vt_col(4 * kq);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int w = e >> 1;
+      const int sh = (e & 1) * 16;
+      const uint32_t a0 = (vr[0][w] >> sh) & 0xffffu, a1 = (vr[1][w] >> sh) & 0xffffu;
+      const uint32_t a2 = (vr[2][w] >> sh) & 0xffffu, a3 = (vr[3][w] >> sh) & 0xffffu;
+      *reinterpret_cast<u32x2*>(s_vt + (8 * pc + e) * kVtRow + colb) =
+          u32x2{a0 | (a1 << 16), a2 | (a3 << 16)};
+    }
+  };
+
+  // ---- running softmax state: per lane, rows 16 qg + col -------------------
+  f32x4 o[2][kD / 16];
+#pragma unroll
+  for (int qg = 0; qg < 2; ++qg)
+#pragma unroll
+    for (int dt = 0; dt < kD / 16; ++dt) o[qg][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[2] = {-INFINITY, -INFINITY};
+  float l_run[2] = {0.f, 0.f};
+
+  auto compute_tile = [&](int j) {
+    const int key0 = j * kKTile;
+    // S^T tiles: kt = 16-key slice, one per (row group, slice)
+    f32x4 s[2][4];
+#pragma unroll
+    for (int qg = 0; qg < 2; ++qg)
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) s[qg][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < kD / 32; ++ks) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(
+            s_k + (16 * kt + col) * kKRow + 64 * ks + 16 * grp);
+#pragma unroll
+        for (int qg = 0; qg < 2; ++qg) s[qg][kt] = H::mma(a, qf[qg][ks], s[qg][kt]);
+      }
+    }
+
+    const bool need_mask = key0 + kKTile - 1 > pos_first;
+    uint32_t phi[2][2][4], plo[2][2][4];  // [qg][step][word]
+#pragma unroll
+    for (int qg = 0; qg < 2; ++qg) {
+      const int pq = pos_first + 16 * qg + col;  // this lane's row position
+      float x[16];
+      float mt = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = key0 + 16 * kt + 4 * grp + r;
+          float v = s[qg][kt][r] * scale_log2;
+          if (need_mask && key > pq) v = -INFINITY;
+          x[4 * kt + r] = v;
+          mt = fmaxf(mt, v);
+        }
+      mt = fmaxf(mt, __shfl_xor(mt, 16));
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      // every row has key 0, so m_run is finite after the first tile
+      const float m_new = fmaxf(m_run[qg], mt);
+      const float alpha = __builtin_amdgcn_exp2f(m_run[qg] - m_new);
+      m_run[qg] = m_new;
+      float sum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        x[e] = __builtin_amdgcn_exp2f(x[e] - m_new);
+        sum += x[e];
+      }
+      l_run[qg] = l_run[qg] * alpha + sum;
+#pragma unroll
+      for (int dt = 0; dt < kD / 16; ++dt) o[qg][dt] *= alpha;
+      // B operand of step st: element e = 4 t + r is key 32 st + 16 t + 4 grp + r,
+      // i.e. S^T slice kt = 2 st + t, register r.
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          uint32_t h0, l0, h1, l1;
+          const int e0 = 2 * w;
+          H::split(x[4 * (2 * st + (e0 >> 2)) + (e0 & 3)], h0, l0);
+          H::split(x[4 * (2 * st + ((e0 + 1) >> 2)) + ((e0 + 1) & 3)], h1, l1);
+          phi[qg][st][w] = h0 | (h1 << 16);
+          plo[qg][st][w] = l0 | (l1 << 16);
+        }
+    }
+
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+#pragma unroll
+      for (int dt = 0; dt < kD / 16; ++dt) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(
+            s_vt + (16 * dt + col) * kVtRow + 64 * st + 16 * grp);
+#pragma unroll
+        for (int qg = 0; qg < 2; ++qg) {
+          const u32x4 bh = {phi[qg][st][0], phi[qg][st][1], phi[qg][st][2], phi[qg][st][3]};
+          const u32x4 bl = {plo[qg][st][0], plo[qg][st][1], plo[qg][st][2], plo[qg][st][3]};
+          o[qg][dt] = H::mma(a, bh, o[qg][dt]);
+          o[qg][dt] = H::mma(a, bl, o[qg][dt]);
+        }
+      }
+    }
+  };
+
+  load_tile(0);
+  for (int j = 0; j < ntiles; ++j) {
+    __syncthreads();  // every wave is done reading the previous tile
+    store_tile(j);
+    __syncthreads();
+    if (j + 1 < ntiles) load_tile(j + 1);  // in flight during the MFMA work
+    if (wrows > 0 && j * kKTile <= pos_last) compute_tile(j);
+  }
+  bad_blk = __syncthreads_or(bad_blk);
+
+  // ---- normalise and store: lane holds rows 16 qg + col, head dims
+  // ---- 16 dt + 4 grp .. + 3 ------------------------------------------------
+#pragma unroll
+  for (int qg = 0; qg < 2; ++qg) {
+    float l = l_run[qg];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    const int i = r0 + 32 * wave + 16 * qg + col;
+    if (i >= c) continue;
+    const float inv = bad_blk ? __builtin_nanf("") : 1.0f / l;
+    float* row = out + (int64_t(q0 + i) * num_heads + h) * kD;
+#pragma unroll
+    for (int dt = 0; dt < kD / 16; ++dt)
+      *reinterpret_cast<f32x4*>(row + 16 * dt + 4 * grp) = o[qg][dt] * inv;
+  }
+}
+
+}  // namespace
+}  // namespace pkv
 
 using namespace pkv;
 
 extern "C" int32_t pkv_paged_attention_prefill(
-    const void*, const void*, const void*, const int32_t*, const int32_t*,
-    const int32_t*, int32_t, int32_t, int32_t, int32_t, int32_t, int32_t,
-    int32_t, int32_t, float, float*, int32_t, void*) {
-  return fail(PKV_ERR_UNSUPPORTED, "chunked prefill is not built yet");
+    const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, const int32_t* context_lens,
+    const int32_t* cu_query_lens, int32_t num_seqs, int32_t num_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t max_blocks_per_seq, int32_t num_blocks, int32_t total_query_rows,
+    int32_t max_query_len, float scale, float* out, int32_t dtype, void* stream) {
+  if (dtype != PKV_BF16 && dtype != PKV_F16) {
+    if (dtype_bytes(dtype) == 0) return fail(PKV_ERR_INVALID, "unknown dtype %d", dtype);
+    return fail(PKV_ERR_UNSUPPORTED, "chunked prefill needs a float16 or bfloat16 cache");
+  }
+  if (num_seqs < 0 || total_query_rows < 0 || max_query_len < 0)
+    return fail(PKV_ERR_INVALID, "negative size");
+  if (num_seqs > 65535) return fail(PKV_ERR_UNSUPPORTED, "at most 65535 sequences per call");
+  if (num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID, "num_heads %d must be a positive multiple of num_kv_heads %d",
+                num_heads, num_kv_heads);
+  if (head_dim != kD)
+    return fail(PKV_ERR_UNSUPPORTED, "chunked prefill supports head_dim 128 (got %d)", head_dim);
+  if (!is_pow2(block_size) || block_size < 16 || block_size > 256)
+    return fail(PKV_ERR_UNSUPPORTED, "block_size must be a power of two in [16, 256]");
+  if (max_blocks_per_seq <= 0 || num_blocks <= 0)
+    return fail(PKV_ERR_INVALID, "invalid table/pool sizes");
+  if (int64_t(num_blocks) * block_size >= (int64_t(1) << 31))
+    return fail(PKV_ERR_INVALID, "num_blocks * block_size must be below 2^31");
+  if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID, "scale must be finite");
+  if (num_seqs == 0 || total_query_rows == 0 || max_query_len == 0) return ok();
+  if (!query || !key_cache || !value_cache || !block_tables || !context_lens ||
+      !cu_query_lens || !out)
+    return fail(PKV_ERR_INVALID, "NULL pointer argument");
+  if (!aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache) || !aligned16(out))
+    return fail(PKV_ERR_INVALID, "query, caches and out must be 16-byte aligned");
+  const int64_t tiles = (int64_t(max_query_len) + kQTile - 1) / kQTile;
+  if (tiles > 65535) return fail(PKV_ERR_UNSUPPORTED, "max_query_len too large");
+  int log2_bs = 0;
+  while ((1 << log2_bs) < block_size) ++log2_bs;
+  const float sl2 = scale * kLog2e;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid(num_heads, unsigned(tiles), num_seqs);
+  const int group = num_heads / num_kv_heads;
+  if (dtype == PKV_BF16) {
+    hipLaunchKernelGGL(prefill_kernel<PKV_BF16>, grid, dim3(kThreads), 0, s,
+                       static_cast<const uint16_t*>(query), static_cast<const uint16_t*>(key_cache),
+                       static_cast<const uint16_t*>(value_cache), block_tables, context_lens,
+                       cu_query_lens, num_heads, group, log2_bs, max_blocks_per_seq, num_blocks,
+                       total_query_rows, max_query_len, sl2, out);
+  } else {
+    hipLaunchKernelGGL(prefill_kernel<PKV_F16>, grid, dim3(kThreads), 0, s,
+                       static_cast<const uint16_t*>(query), static_cast<const uint16_t*>(key_cache),
+                       static_cast<const uint16_t*>(value_cache), block_tables, context_lens,
+                       cu_query_lens, num_heads, group, log2_bs, max_blocks_per_seq, num_blocks,
+                       total_query_rows, max_query_len, sl2, out);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
+  return ok();
 }
