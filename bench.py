@@ -4,8 +4,9 @@
 A step is one decode step of one attention layer over the whole batch,
 through every stage of the path:
   1. host allocator: one new slot per sequence (batch append, all or
-     nothing; copy-on-write pairs if a shared block is hit);
-  2. block tables, lengths and slots to the device (pinned, asynchronous);
+     nothing; copy-on-write pairs if a shared block is hit), written with
+     the block tables and lengths into one pinned staging buffer;
+  2. that buffer to the device in one asynchronous copy;
   3. block copies for copy-on-write pairs (none unless blocks are shared);
   4. paged_kv_append of the step's new K/V rows;
   5. paged_attention_decode: split-K partition kernel, then the merge.
@@ -13,16 +14,23 @@ The cache is resident in HBM before timing starts.  ``value`` is the KV
 bytes the decode reads per step (sum over sequences of context_len * Hkv *
 head_dim * 2 * element size) divided by the wall time of a whole step.
 ``roofline`` reports the partition kernel alone, timed with HIP events on
-the stream it runs on.  ``cpu_baseline`` times the float64 CPU oracle on a
-small sample of the same workload (reported only).
+the stream it runs on; its ``traffic`` comes from the committed rocprofv3
+counter summary of the same kernel source, when there is one.
+``cpu_baseline`` times the float64 CPU oracle on a small sample of the same
+workload (reported only).  For the shared-prefix workload the line also
+carries ``prefill``: one causal 512-row chunked prefill per sequence,
+timed the same way, against the bf16 matrix-core peak.
 
 Usage: python bench.py [--steps K] [--warmup W] [--workload NAME]
+       python bench.py --copy-calibration   (block copy of a known size,
+                                             the scale for HBM counters)
 """
 
 import argparse
-import hashlib
 import json
+import hashlib
 import os
+import re
 import sys
 import time
 
@@ -31,8 +39,10 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, published
+HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16/fp16 matrix peak, published
 METRIC = ("paged decode KV-read GB/s (% of HBM peak) + tokens/s, LLaMA-7B layer, batch 64")
+DTYPE_NAMES = {"torch.bfloat16": "bf16", "torch.float16": "fp16", "torch.float32": "fp32"}
 
 
 def parse():
@@ -42,9 +52,13 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama7b_bf16")
     ap.add_argument("--partition-size", type=int, default=None,
-                    help="split-K partition in tokens (default: the workload's, else the library's)")
+                    help="split-K partition in tokens (default: the workload's, else automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (profiling runs)")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the chunked-prefill leg of the shared-prefix workload")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="time pkv_copy_blocks over a known byte count and exit")
     return ap.parse_args()
 
 
@@ -78,13 +92,15 @@ def setup(w, pkv, workloads, torch, dev):
 def gpu_run(args, w, torch, pkv, workloads):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    part = w.partition_size if args.partition_size is None else args.partition_size
+    part_arg = w.partition_size if args.partition_size is None else args.partition_size
     p, kc, vc, alloc = setup(w, pkv, workloads, torch, dev)
-    seqs = p.seqs
+    seqs = np.asarray(p.seqs, dtype=np.int64)
     b = len(seqs)
     total_steps = args.warmup + args.steps
-    max_len = int(max(alloc.seq_len(s) for s in seqs)) + total_steps
-    max_blocks = -(-max_len // w.block_size)
+    max_len = int(max(alloc.seq_len(s) for s in p.seqs)) + total_steps
+    mb = -(-max_len // w.block_size)
+    part = pkv.paged_attention_decode_partition_size(b, w.num_kv_heads, w.block_size, max_len,
+                                                     part_arg)
 
     gen = torch.Generator(device=dev)
     gen.manual_seed(w.seed + 99)
@@ -95,52 +111,56 @@ def gpu_run(args, w, torch, pkv, workloads):
     q = (torch.randn((total_steps, b, w.num_heads, w.head_dim), generator=gen, device=dev)
          * w.std).to(w.dtype)
     out = torch.empty((b, w.num_heads, w.head_dim), dtype=torch.float32, device=dev)
-    ws_bytes = pkv.paged_attention_decode_workspace_size(b, w.num_heads, w.num_kv_heads, w.head_dim,
-                                                         max_len, part)
+    ws_bytes = pkv.paged_attention_decode_workspace_size(b, w.num_heads, w.num_kv_heads,
+                                                         w.head_dim, max_len, part)
     workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
 
-    tables_d = torch.empty((b, max_blocks), dtype=torch.int32, device=dev)
-    lens_d = torch.empty(b, dtype=torch.int32, device=dev)
-    slots_d = torch.empty(b, dtype=torch.int32, device=dev)
-    pinned = [dict(tables=torch.empty((b, max_blocks), dtype=torch.int32, pin_memory=True),
-                   lens=torch.empty(b, dtype=torch.int32, pin_memory=True),
-                   slots=torch.empty(b, dtype=torch.int32, pin_memory=True),
-                   done=torch.cuda.Event()) for _ in range(2)]
-    for buf in pinned:
-        buf["done"].record()
+    # one staging buffer per step parity: [tables b*mb | lens b | slots b]
+    words = b * mb + 2 * b
+    packed_d = torch.empty(words, dtype=torch.int32, device=dev)
+    tables_d = packed_d[:b * mb].view(b, mb)
+    lens_d = packed_d[b * mb:b * mb + b]
+    slots_d = packed_d[b * mb + b:]
+    staging = []
+    for _ in range(2):
+        buf = torch.empty(words, dtype=torch.int32, pin_memory=True)
+        arr = buf.numpy()
+        staging.append(dict(buf=buf, tables=arr[:b * mb].reshape(b, mb),
+                            lens=arr[b * mb:b * mb + b], slots=arr[b * mb + b:],
+                            done=torch.cuda.Event()))
+    for st in staging:
+        st["done"].record()
     ones = np.ones(b, dtype=np.int32)
     stream = torch.cuda.current_stream(dev)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(total_steps)]
-    step_bytes = []
+    step_bytes = np.zeros(total_steps, dtype=np.float64)
+    step_ctx = np.zeros(total_steps, dtype=np.int64)
 
     def step(i):
-        slots, pairs = alloc.append_batch(seqs, ones)                      # 1
-        tables, lens = alloc.build_block_tables(seqs, max_blocks)
-        buf = pinned[i % 2]
-        buf["done"].synchronize()            # the copy issued two steps ago is done
-        buf["tables"].numpy()[:] = tables
-        buf["lens"].numpy()[:] = lens
-        buf["slots"].numpy()[:] = slots
-        tables_d.copy_(buf["tables"], non_blocking=True)                  # 2
-        lens_d.copy_(buf["lens"], non_blocking=True)
-        slots_d.copy_(buf["slots"], non_blocking=True)
-        buf["done"].record(stream)
-        if pairs:                                                          # 3
+        st = staging[i % 2]
+        st["done"].synchronize()            # the copy issued two steps ago is done
+        _, pairs = alloc.append_batch(seqs, ones, slots_out=st["slots"])    # 1
+        alloc.build_block_tables(seqs, mb, tables_out=st["tables"], lens_out=st["lens"])
+        packed_d.copy_(st["buf"], non_blocking=True)                        # 2
+        st["done"].record(stream)
+        if pairs:                                                            # 3
             src = torch.tensor([a for a, _ in pairs], dtype=torch.int32).to(dev)
             dst = torch.tensor([c for _, c in pairs], dtype=torch.int32).to(dev)
             pkv.copy_blocks(kc, vc, src, dst)
-        pkv.paged_kv_append(k_new[i], v_new[i], kc, vc, slots_d)          # 4
+        pkv.paged_kv_append(k_new[i], v_new[i], kc, vc, slots_d)            # 4
+        lens = st["lens"]
         mc = int(lens.max())
         e0, e1, e2 = ev[i]
         e0.record(stream)
         pkv.paged_attention_decode_partials(q[i], kc, vc, tables_d, lens_d, w.scale, mc,  # 5
                                             part, out, workspace)
         e1.record(stream)
-        pkv.paged_attention_decode_merge(lens_d, w.num_kv_heads, w.block_size, max_blocks, mc,
+        pkv.paged_attention_decode_merge(lens_d, w.num_kv_heads, w.block_size, mb, mc,
                                          part, out, workspace)
         e2.record(stream)
-        step_bytes.append(kv_bytes(w, lens))
+        step_bytes[i] = kv_bytes(w, lens)
+        step_ctx[i] = mc
 
     for i in range(args.warmup):
         step(i)
@@ -153,11 +173,94 @@ def gpu_run(args, w, torch, pkv, workloads):
     timed = range(args.warmup, total_steps)
     part_ms = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in timed])
     merge_ms = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in timed])
-    bytes_timed = np.array(step_bytes[args.warmup:], dtype=np.float64)
     if not torch.isfinite(out).all():
         raise RuntimeError("decode produced non-finite output")
-    return dict(wall=wall, part_ms=part_ms, merge_ms=merge_ms, bytes=bytes_timed, batch=b,
-                part=part, max_len=max_len)
+    res = dict(wall=wall, part_ms=part_ms, merge_ms=merge_ms, bytes=step_bytes[args.warmup:],
+               batch=b, part=part)
+    if w.chunk and not args.no_prefill:
+        res["prefill"] = prefill_run(w, p, alloc, kc, vc, torch, pkv, dev)
+    return res
+
+
+def prefill_run(w, p, alloc, kc, vc, torch, pkv, dev):
+    """One causal chunk of w.chunk rows per sequence after its decode steps:
+    append the chunk's K/V, then time the prefill call (HIP events on its
+    stream, mean of 10 launches after 2 untimed)."""
+    seqs = np.asarray(p.seqs, dtype=np.int64)
+    b, c = len(seqs), w.chunk
+    slots, pairs = alloc.append_batch(seqs, np.full(b, c, dtype=np.int32))
+    if pairs:
+        pkv.copy_blocks(kc, vc, torch.tensor([a for a, _ in pairs], dtype=torch.int32).to(dev),
+                        torch.tensor([d for _, d in pairs], dtype=torch.int32).to(dev))
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed + 7)
+    kv = (torch.randn((2, b * c, w.num_kv_heads, w.head_dim), generator=gen, device=dev)
+          * w.std).to(w.dtype)
+    pkv.paged_kv_append(kv[0], kv[1], kc, vc, torch.from_numpy(slots).to(dev))
+    del kv
+    mb = max(len(alloc.block_table(int(s))) for s in seqs)
+    th, lh = alloc.build_block_tables(seqs, mb)
+    tables = torch.from_numpy(th.copy()).to(dev)
+    lens = torch.from_numpy(lh.copy()).to(dev)
+    cu = torch.arange(0, (b + 1) * c, c, dtype=torch.int32, device=dev)
+    q = (torch.randn((b * c, w.num_heads, w.head_dim), generator=gen, device=dev)
+         * w.std).to(w.dtype)
+    out = torch.empty((b * c, w.num_heads, w.head_dim), dtype=torch.float32, device=dev)
+    # algorithmic flops: row i of a chunk at position n - c + i attends to
+    # n - c + i + 1 keys; 2 flops per multiply-add in QK^T and in PV
+    ctx = lh.astype(np.int64) - c
+    keys = int(np.sum(c * ctx + c * (c + 1) // 2))
+    flops = 4.0 * w.head_dim * w.num_heads * keys
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(2):
+        pkv.paged_attention_prefill(q, kc, vc, tables, lens, cu, w.scale, c, out=out)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    e0.record(stream)
+    for _ in range(reps):
+        pkv.paged_attention_prefill(q, kc, vc, tables, lens, cu, w.scale, c, out=out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    if not torch.isfinite(out).all():
+        raise RuntimeError("prefill produced non-finite output")
+    ms = e0.elapsed_time(e1) / reps
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {"kernel": "prefill_kernel", "rows": b * c, "chunk": c, "ms": round(ms, 4),
+            "rows_per_s": round(b * c / (ms * 1e-3), 1),
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
+                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+                         "flops_per_launch": flops}}
+
+
+def copy_calibration(torch, pkv):
+    """Copy 2 GiB of K/V blocks (1 GiB per cache) with pkv_copy_blocks: a
+    plain copy of known size whose HBM counters give the scale between
+    rocprofv3's FETCH_SIZE/WRITE_SIZE and bytes moved."""
+    dev = torch.device("cuda:0")
+    hkv, bs, d = 8, 16, 128
+    block_bytes = hkv * bs * d * 2
+    pairs = (1 << 30) // block_bytes
+    kc = torch.zeros((2 * pairs, hkv, bs, d), dtype=torch.bfloat16, device=dev)
+    vc = torch.zeros_like(kc)
+    src = torch.arange(pairs, dtype=torch.int32, device=dev)
+    dst = src + pairs
+    for _ in range(3):
+        pkv.copy_blocks(kc, vc, src[:min(pairs, 65535)], dst[:min(pairs, 65535)])
+    torch.cuda.synchronize()
+    per_launch = min(pairs, 65535)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        pkv.copy_blocks(kc, vc, src[:per_launch], dst[:per_launch])
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 5
+    moved = 2 * per_launch * block_bytes
+    print(json.dumps({"calibration": "copy_blocks_kernel", "read_bytes_per_launch": moved,
+                      "write_bytes_per_launch": moved, "ms": round(ms, 4),
+                      "gbps_read_plus_write": round(2 * moved / (ms * 1e-3) / 1e9, 1)}),
+          flush=True)
 
 
 def cpu_baseline(w, workloads):
@@ -202,29 +305,34 @@ def cpu_baseline(w, workloads):
         paged_decode(q, kc, vc, np.array(tables), lens, w.scale, w.block_size)
         reps += 1
         el = time.perf_counter() - t0
-        if el > 10.0 or reps >= 50:
+        if el > 10.0 and reps >= 3:
             break
     per = el / reps
     gbps = kv_bytes(w, np.array(lens)) / per / 1e9
     return {"value": round(gbps, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
             "tokens_per_s": round(len(seqs) / per, 2),
             "sample": f"{len(seqs)} of {w.num_seqs} sequences (context lens "
-                      f"{[int(x) for x in lens]}), float64 numpy gather-then-attend, "
-                      f"{reps} repetitions, {el:.1f} s; host has "
+                      f"{[int(x) for x in lens]}), one decode step each, float64 numpy "
+                      f"gather-then-attend, {reps} repetitions in {el:.1f} s; host has "
                       f"{len(os.sched_getaffinity(0))} cores available"}
 
 
 def traffic_from_profiles(w, kernel_src):
-    """HBM bytes per launch from the committed PMC summary, when it was
-    taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"decode_partition_{w.name}_pmc.json")
+    """HBM bytes per launch of the decode partition kernel from the committed
+    counter summary (profiles/decode_partition_<workload>_traffic.md), when
+    it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"decode_partition_{w.name}_traffic.md")
     if not os.path.exists(path):
         return None
-    rec = json.load(open(path))
+    text = open(path).read()
+    fields = dict(re.findall(r"^- (\w+): (\S+)$", text, flags=re.M))
     digest = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
-    if rec.get("kernel_source_sha256") != digest:
+    if fields.get("kernel_source_sha256") != digest:
         return None
-    return rec.get("hbm_bytes_per_launch")
+    try:
+        return int(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def main():
@@ -237,9 +345,10 @@ def main():
     import paged_kv_cache_420_amd as pkv
     import workloads
 
+    if args.copy_calibration:
+        copy_calibration(torch, pkv)
+        return
     w = workloads.get(args.workload)
-    if w.chunk:
-        w = workloads.scaled(w, chunk=0)
     r = gpu_run(args, w, torch, pkv, workloads)
     ms_step = r["wall"] / args.steps * 1e3
     mean_bytes = float(r["bytes"].mean())
@@ -258,12 +367,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {torch.bfloat16: "bf16", torch.float16: "fp16", torch.float32: "fp32"}[w.dtype],
+        "dtype": DTYPE_NAMES[str(w.dtype)],
         "data": "synthetic",
         "config": {"workload": w.name, "num_seqs": w.num_seqs, "num_heads": w.num_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                    "block_size": w.block_size, "context_lens": w.lens,
-                   "shared_prefix": w.prefix, "partition_size": r["part"] or 512},
+                   "shared_prefix": w.prefix, "partition_size": r["part"]},
         "hbm_peak_frac": round(value / HBM_PEAK_GBPS, 4),
         "tokens_per_s": round(r["batch"] / (ms_step * 1e-3), 1),
         "kv_bytes_per_step": int(mean_bytes),
@@ -273,8 +382,10 @@ def main():
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic_from_profiles(w, src)},
-        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(w, workloads),
     }
+    if "prefill" in r:
+        line["prefill"] = r["prefill"]
+    line["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(w, workloads)
     print(json.dumps(line), flush=True)
 
 

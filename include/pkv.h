@@ -202,6 +202,15 @@ int32_t pkv_copy_blocks(void* key_cache, void* value_cache,
                         int32_t num_kv_heads, int32_t block_size,
                         int32_t head_dim, int32_t dtype, void* stream);
 
+/* The split-K partition (tokens) pkv_paged_attention_decode uses for these
+ * sizes: partition_size itself when it is non-zero and valid, else the
+ * automatic choice -- the longest of 1024, 512, 256, 128 tokens that still
+ * gives num_seqs * num_kv_heads * ceil(max_context_len / partition) >= 2048
+ * workgroups (128 if none does) -- raised to block_size if shorter. */
+int32_t pkv_paged_attention_decode_partition_size(
+    int32_t num_seqs, int32_t num_kv_heads, int32_t block_size,
+    int32_t max_context_len, int32_t partition_size, int32_t* resolved);
+
 /* Workspace needed by pkv_paged_attention_decode for these sizes, in
  * bytes (0 when no sequence needs more than one partition).  Pass the same
  * partition_size as to the decode call (0 = automatic: the choice depends

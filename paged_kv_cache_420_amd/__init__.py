@@ -23,7 +23,8 @@ __all__ = [
     "PkvError", "InvalidArgument", "OutOfBlocks", "NoSuchSequence",
     "SequenceExists", "BufferTooSmall", "HipError", "Unsupported",
     "BlockAllocator", "paged_kv_append", "copy_blocks",
-    "paged_attention_decode_workspace_size", "paged_attention_decode",
+    "paged_attention_decode_workspace_size", "paged_attention_decode_partition_size",
+    "paged_attention_decode",
     "paged_attention_decode_partials", "paged_attention_decode_merge",
     "paged_attention_prefill", "library_path", "version",
 ]
@@ -92,6 +93,7 @@ _SIGNATURES = {
     "pkv_build_block_tables": (_I32, [_P, _PI64, _I32, _I32, _PI32, _PI32]),
     "pkv_paged_kv_append": (_I32, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P]),
     "pkv_copy_blocks": (_I32, [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P]),
+    "pkv_paged_attention_decode_partition_size": (_I32, [_I32, _I32, _I32, _I32, _I32, _PI32]),
     "pkv_paged_attention_decode_workspace_size": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32,
                                                          ctypes.POINTER(ctypes.c_size_t)]),
     "pkv_paged_attention_decode": (_I32, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
@@ -190,14 +192,22 @@ class BlockAllocator:
                                    ctypes.byref(dst), ctypes.byref(cnt)))
         return slots[:n], ([(src.value, dst.value)] if cnt.value else [])
 
-    def append_batch(self, seqs, counts):
-        """All-or-nothing append; returns (slots int32 [sum counts], cow pairs)."""
+    def append_batch(self, seqs, counts, slots_out=None):
+        """All-or-nothing append; returns (slots int32 [sum counts], cow pairs).
+        ``slots_out``: optional contiguous int32 array to write the slots into
+        (a view of it is returned)."""
         seqs = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64))
         counts = np.ascontiguousarray(np.asarray(counts, dtype=np.int32))
         if seqs.shape != counts.shape:
             raise InvalidArgument("seqs and counts differ in length")
         total = int(counts.astype(np.int64).sum())
-        slots = np.empty(max(total, 1), dtype=np.int32)
+        if slots_out is None:
+            slots = np.empty(max(total, 1), dtype=np.int32)
+        else:
+            slots = slots_out
+            if (slots.dtype != np.int32 or slots.ndim != 1 or not slots.flags.c_contiguous
+                    or slots.shape[0] < total):
+                raise InvalidArgument("slots_out must be a contiguous int32 array of sum(counts)")
         cap = max(len(seqs), 1)
         src = np.empty(cap, dtype=np.int32)
         dst = np.empty(cap, dtype=np.int32)
@@ -239,12 +249,22 @@ class BlockAllocator:
         _check(_lib.pkv_allocator_snapshot(self._h, _i32p(free), ctypes.byref(nf), _i32p(ref)))
         return free[:nf.value].tolist(), ref.tolist()
 
-    def build_block_tables(self, seqs, max_blocks):
-        """Host int32 arrays (block_tables [B, max_blocks] -1 padded, context_lens [B])."""
+    def build_block_tables(self, seqs, max_blocks, tables_out=None, lens_out=None):
+        """Host int32 arrays (block_tables [B, max_blocks] -1 padded, context_lens [B]).
+        ``tables_out``/``lens_out``: optional contiguous int32 arrays of those
+        shapes to fill instead (e.g. views of a pinned staging buffer)."""
         seqs = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64))
         b = len(seqs)
-        tables = np.empty((max(b, 1), max(max_blocks, 1)), dtype=np.int32)
-        lens = np.empty(max(b, 1), dtype=np.int32)
+        if tables_out is None or lens_out is None:
+            tables = np.empty((max(b, 1), max(max_blocks, 1)), dtype=np.int32)
+            lens = np.empty(max(b, 1), dtype=np.int32)
+        else:
+            tables, lens = tables_out, lens_out
+            if (tables.dtype != np.int32 or tables.shape != (b, max_blocks)
+                    or not tables.flags.c_contiguous or lens.dtype != np.int32
+                    or lens.shape != (b,) or not lens.flags.c_contiguous):
+                raise InvalidArgument("tables_out/lens_out must be contiguous int32 "
+                                      "[B, max_blocks] and [B]")
         _check(_lib.pkv_build_block_tables(self._h, seqs.ctypes.data_as(_PI64), b, max_blocks,
                                            _i32p(tables), _i32p(lens)))
         return tables[:b, :max_blocks], lens[:b]
@@ -314,6 +334,16 @@ def copy_blocks(key_cache, value_cache, src, dst):
     _check(_lib.pkv_copy_blocks(key_cache.data_ptr(), value_cache.data_ptr(), src.data_ptr(),
                                 dst.data_ptr(), src.shape[0], nb, hkv, bs, d,
                                 _dtype_code(key_cache), _stream(key_cache)))
+
+
+def paged_attention_decode_partition_size(num_seqs, num_kv_heads, block_size, max_context_len,
+                                          partition_size=0):
+    """Split-K partition (tokens) the decode call uses for these sizes."""
+    out = _I32()
+    _check(_lib.pkv_paged_attention_decode_partition_size(num_seqs, num_kv_heads, block_size,
+                                                          max_context_len, partition_size,
+                                                          ctypes.byref(out)))
+    return out.value
 
 
 def paged_attention_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim,

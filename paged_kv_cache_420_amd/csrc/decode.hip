@@ -580,6 +580,20 @@ size_t workspace_bytes(int B, int Hq, int D, int max_parts) {
 
 using namespace pkv;
 
+extern "C" int32_t pkv_paged_attention_decode_partition_size(
+    int32_t num_seqs, int32_t num_kv_heads, int32_t block_size,
+    int32_t max_context_len, int32_t partition_size, int32_t* resolved) {
+  if (!resolved) return fail(PKV_ERR_INVALID, "resolved is NULL");
+  if (num_seqs < 0 || num_kv_heads <= 0 || block_size <= 0 || max_context_len < 0)
+    return fail(PKV_ERR_INVALID, "invalid sizes");
+  int32_t part = 0;
+  int32_t st = resolve_partition(partition_size, block_size, num_seqs, num_kv_heads,
+                                 max_context_len, &part);
+  if (st != PKV_OK) return st;
+  *resolved = part;
+  return ok();
+}
+
 extern "C" int32_t pkv_paged_attention_decode_workspace_size(
     int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
     int32_t max_context_len, int32_t partition_size, size_t* bytes) {

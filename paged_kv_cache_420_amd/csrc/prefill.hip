@@ -64,12 +64,18 @@ struct Half<PKV_BF16> {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
   }
-  // p = hi + lo with both halves representable (round to nearest even).
-  __device__ static void split(float p, uint32_t& hi, uint32_t& lo) {
-    const __bf16 h = static_cast<__bf16>(p);
-    const __bf16 l = static_cast<__bf16>(p - static_cast<float>(h));
-    hi = __builtin_bit_cast(uint16_t, h);
-    lo = __builtin_bit_cast(uint16_t, l);
+  // Two weights p0, p1 as packed hi and lo pairs with p = hi + lo: hi is p
+  // truncated to bfloat16 (its top 16 bits), lo = p - hi (exact in float32,
+  // at most 16 significant bits) rounded to bfloat16.  hi + lo carries p to
+  // about 2^-16 relative.
+  __device__ static void split2(float p0, float p1, uint32_t& hi, uint32_t& lo) {
+    const uint32_t b0 = __float_as_uint(p0), b1 = __float_as_uint(p1);
+    hi = (b0 >> 16) | (b1 & 0xffff0000u);
+    const float l0 = p0 - __uint_as_float(b0 & 0xffff0000u);
+    const float l1 = p1 - __uint_as_float(b1 & 0xffff0000u);
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{l0, l1}, bf16x2));
   }
 };
 
@@ -79,30 +85,44 @@ struct Half<PKV_F16> {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
   }
-  __device__ static void split(float p, uint32_t& hi, uint32_t& lo) {
-    const _Float16 h = static_cast<_Float16>(p);
-    const _Float16 l = static_cast<_Float16>(p - static_cast<float>(h));
-    hi = __builtin_bit_cast(uint16_t, h);
-    lo = __builtin_bit_cast(uint16_t, l);
+  // hi = p rounded to float16, lo = p - hi rounded to float16.
+  __device__ static void split2(float p0, float p1, uint32_t& hi, uint32_t& lo) {
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    const f16x2 h = __builtin_convertvector(f32x2{p0, p1}, f16x2);
+    const f16x2 l = __builtin_convertvector(
+        f32x2{p0 - static_cast<float>(h.x), p1 - static_cast<float>(h.y)}, f16x2);
+    hi = __builtin_bit_cast(uint32_t, h);
+    lo = __builtin_bit_cast(uint32_t, l);
   }
 };
 
 __device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
 
-// Column of V^T (in LDS) that holds key k of a 64-key tile.  Write k as
-// 32 s + 16 t + 4 g + r (s: 32-key MFMA step, t: which 16-key S^T tile of
-// the step, g: lane group, r: accumulator register).  The lanes of group g
-// hold, for step s, the keys with t in {0,1} and r in 0..3 -- eight keys
-// that must sit in consecutive columns for one 16-byte A-operand read.
-__device__ __forceinline__ int vt_col(int k) {
-  const int s = k >> 5, t = (k >> 4) & 1, g = (k >> 2) & 3, r = k & 3;
-  return 32 * s + 8 * g + 4 * t + r;
-}
+// Lazy rescaling threshold (log2 units): the running max of a row is only
+// raised -- and the accumulators rescaled -- when a tile's max exceeds it by
+// more than this, so weights stay below 2^8 and the rescale is rare.
+constexpr float kRescaleSlack = 8.0f;
 
 // Grid: x = query head (permuted so that heads of one KV group share an
 // XCD when num_heads % 8 == 0), y = 128-row tile of the chunk, z = sequence.
+// Register use is capped for two workgroups per CU (two waves per SIMD):
+// one workgroup's MFMA work then covers the other's barrier and load waits
+// (measured 1.5x over one wave per SIMD at 304 registers).
+//
+// K/V tile layout in LDS (two buffers, so one barrier per tile):
+//   K   [64 keys][128 dims] row-major, rows padded to 272 bytes;
+//   V^T [128 dims][64 keys], rows padded to 144 bytes, keys permuted so that
+//       the 8 keys one lane group feeds to a PV MFMA step are 16 contiguous
+//       bytes: key 32 s + 16 t + 4 g + r sits in 16-byte chunk 4 s + g at
+//       position 4 t + r.
+// Gather: waves 0-1 fetch V, waves 2-3 fetch K, eight 16-byte loads per
+// thread.  A V thread takes the eight keys of one chunk at one 8-dim piece
+// and transposes them in registers into eight 16-byte V^T row segments; a
+// K thread takes eight consecutive keys at one piece.  Lane assignments make
+// every 16 consecutive lanes' LDS stores cover all 64 banks once.
 template <int DT>
-__global__ __launch_bounds__(kThreads) void prefill_kernel(
+__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
     const uint16_t* __restrict__ query, const uint16_t* __restrict__ key_cache,
     const uint16_t* __restrict__ value_cache, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ context_lens, const int32_t* __restrict__ cu_query_lens,
@@ -110,8 +130,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
     int32_t num_blocks, int32_t total_q, int32_t max_q, float scale_log2,
     float* __restrict__ out) {
   using H = Half<DT>;
-  __shared__ __attribute__((aligned(16))) uint8_t s_k[kLdsK];
-  __shared__ __attribute__((aligned(16))) uint8_t s_vt[kLdsV];
+  __shared__ __attribute__((aligned(16))) uint8_t s_k[2][kLdsK];
+  __shared__ __attribute__((aligned(16))) uint8_t s_vt[2][kLdsV];
 
   const int xcd_slice = num_heads >> 3;
   const int h = (num_heads & 7) == 0
@@ -154,7 +174,11 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
   const int grp = lane >> 4;  // lane group: 8-element k slice, 4-row output slice
 
   // Q^T as the B operand of S^T = K Q^T: lane holds row (16 qg + col), head
-  // dims 32 ks + 8 grp .. + 7.  Rows past the chunk are zero.
+  // dims 32 ks + 8 grp .. + 7.  Rows past the chunk are zero.  A negative
+  // scale is applied as an exact sign flip of q, so the softmax below can
+  // take maxima of the raw scores and fold |scale| into one FMA.
+  const uint32_t qsign = scale_log2 < 0.f ? 0x80008000u : 0u;
+  const float sl2 = fabsf(scale_log2);
   u32x4 qf[2][kD / 32];
 #pragma unroll
   for (int qg = 0; qg < 2; ++qg) {
@@ -163,68 +187,92 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
     for (int ks = 0; ks < kD / 32; ++ks) {
       if (i < c) {
         qf[qg][ks] = *reinterpret_cast<const u32x4*>(
-            query + (int64_t(q0 + i) * num_heads + h) * kD + 32 * ks + 8 * grp);
+                         query + (int64_t(q0 + i) * num_heads + h) * kD + 32 * ks + 8 * grp) ^
+                     qsign;
       } else {
         qf[qg][ks] = u32x4{0, 0, 0, 0};
       }
     }
   }
 
-  // ---- tile gather: thread = (16-byte piece pc of a row, key quad kq) -----
-  const int pc = tid & 15;
-  const int kq = tid >> 4;  // keys 4 kq .. 4 kq + 3 of the tile
+  // ---- tile gather ----------------------------------------------------------
+  const bool v_role = tid < 128;
+  const int gt = tid & 127;
+  // V role: chunk ck = (s, g) of the V^T row, piece pc (dims 8 pc .. + 7);
+  // its keys are quad A = 32 s + 4 g + 0..3 and quad B = quad A + 16.
+  // K role: piece pc, keys 8 ko .. 8 ko + 7.
+  const int ck = gt & 7, vpc = gt >> 3;
+  const int kpc = gt & 15, ko = gt >> 4;
   const int64_t tile_elems = int64_t(bs) * kD;
   const int64_t blk_elems = tile_elems * num_kv_heads;
   const int32_t* table = block_tables + int64_t(b) * max_blocks;
+  const uint16_t* vbase = value_cache + int64_t(kvh) * tile_elems + 8 * vpc;
+  const uint16_t* kbase = key_cache + int64_t(kvh) * tile_elems + 8 * kpc;
   bool bad_blk = false;
-  u32x4 kr[4], vr[4];
+  u32x4 g8[8];  // the eight staged 16-byte pieces
 
+  // element offset of `key`'s row at this thread's piece; flags bad ids
+  auto row_of = [&](int key) -> int64_t {
+    int id = table[key >> log2_bs];
+    if (id < 0 || id >= num_blocks) {
+      bad_blk = true;
+      id = 0;
+    }
+    return int64_t(id) * blk_elems + int64_t(key & (bs - 1)) * kD;
+  };
+
+  // Loads are unconditional: a quad/octet past kv_end is clamped to the
+  // last needed one (always a valid row of a checked block), and the keys
+  // past kv_end are zeroed when the last, partial tile is stored.
   auto load_tile = [&](int j) {
-    const int key = j * kKTile + 4 * kq;  // 4 | bs: the quad is in one block
-    if (key < kv_end) {
-      int id = table[key >> log2_bs];
-      if (id < 0 || id >= num_blocks) {
-        bad_blk = true;
-        id = 0;
-      }
-      const int64_t base = int64_t(id) * blk_elems + int64_t(kvh) * tile_elems +
-                           int64_t(key & (bs - 1)) * kD + 8 * pc;
+    const int key0 = j * kKTile;
+    if (v_role) {
+      const int ka = key0 + 32 * (ck >> 2) + 4 * (ck & 3);  // quad A
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        // rows past kv_end inside the quad are zeroed at the LDS store
-        kr[jj] = *reinterpret_cast<const u32x4*>(key_cache + base + jj * kD);
-        vr[jj] = *reinterpret_cast<const u32x4*>(value_cache + base + jj * kD);
+      for (int qd = 0; qd < 2; ++qd) {
+        const int kq = min(ka + 16 * qd, kv_end - 1) & ~3;  // 4 | bs: quad in one block
+        const uint16_t* src = vbase + row_of(kq);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) g8[4 * qd + r] = *reinterpret_cast<const u32x4*>(src + r * kD);
       }
     } else {
+      const int k8 = min(key0 + 8 * ko, kv_end - 1) & ~7;  // 8 | bs: octet in one block
+      const uint16_t* src = kbase + row_of(k8);
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        kr[jj] = u32x4{0, 0, 0, 0};
-        vr[jj] = u32x4{0, 0, 0, 0};
-      }
+      for (int r = 0; r < 8; ++r) g8[r] = *reinterpret_cast<const u32x4*>(src + r * kD);
     }
   };
 
-  auto store_tile = [&](int j) {
-    const int key = j * kKTile + 4 * kq;
+  auto store_tile = [&](int buf, int j) {
+    const int key0 = j * kKTile;
+    if (key0 + kKTile > kv_end) {  // last tile: zero the keys past the range
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      if (key + jj >= kv_end) {
-        kr[jj] = u32x4{0, 0, 0, 0};
-        vr[jj] = u32x4{0, 0, 0, 0};
+      for (int r = 0; r < 8; ++r) {
+        const int key = v_role ? key0 + 32 * (ck >> 2) + 4 * (ck & 3) + 16 * (r >> 2) + (r & 3)
+                               : key0 + 8 * ko + r;
+        if (key >= kv_end) g8[r] = u32x4{0, 0, 0, 0};
       }
-      *reinterpret_cast<u32x4*>(s_k + (4 * kq + jj) * kKRow + 16 * pc) = kr[jj];
     }
-    // V^T: element e of the piece is head dim 8 pc + e; the quad's four keys
-    // go to four consecutive columns (one 8-byte store per head dim).
-    const int colb = 2 * vt_col(4 * kq);
+    if (v_role) {
+      // g8[k] holds dims 8 vpc .. + 7 of key k of the chunk (k = 4 t + r);
+      // V^T row 8 vpc + e gets, at chunk ck, the eight keys' element e.
+      uint8_t* dst = s_vt[buf] + (8 * vpc) * kVtRow + 16 * ck;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int w = e >> 1;
-      const int sh = (e & 1) * 16;
-      const uint32_t a0 = (vr[0][w] >> sh) & 0xffffu, a1 = (vr[1][w] >> sh) & 0xffffu;
-      const uint32_t a2 = (vr[2][w] >> sh) & 0xffffu, a3 = (vr[3][w] >> sh) & 0xffffu;
-      *reinterpret_cast<u32x2*>(s_vt + (8 * pc + e) * kVtRow + colb) =
-          u32x2{a0 | (a1 << 16), a2 | (a3 << 16)};
+      for (int e = 0; e < 8; ++e) {
+        const int w = e >> 1;
+        u32x4 row;
+#pragma unroll
+        for (int k2 = 0; k2 < 4; ++k2) {
+          const uint32_t a = g8[2 * k2][w], bb = g8[2 * k2 + 1][w];
+          row[k2] = (e & 1) ? ((a >> 16) | (bb & 0xffff0000u))
+                            : ((a & 0xffffu) | (bb << 16));
+        }
+        *reinterpret_cast<u32x4*>(dst + e * kVtRow) = row;
+      }
+    } else {
+      uint8_t* dst = s_k[buf] + (8 * ko) * kKRow + 16 * kpc;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) *reinterpret_cast<u32x4*>(dst + r * kKRow) = g8[r];
     }
   };
 
@@ -234,11 +282,13 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
   for (int qg = 0; qg < 2; ++qg)
 #pragma unroll
     for (int dt = 0; dt < kD / 16; ++dt) o[qg][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[2] = {-INFINITY, -INFINITY};
+  float m_run[2] = {-INFINITY, -INFINITY};  // log2 units, scale applied
   float l_run[2] = {0.f, 0.f};
 
-  auto compute_tile = [&](int j) {
+  auto compute_tile = [&](int buf, int j) {
     const int key0 = j * kKTile;
+    const uint8_t* sk = s_k[buf];
+    const uint8_t* svt = s_vt[buf];
     // S^T tiles: kt = 16-key slice, one per (row group, slice)
     f32x4 s[2][4];
 #pragma unroll
@@ -250,56 +300,87 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
         const u32x4 a = *reinterpret_cast<const u32x4*>(
-            s_k + (16 * kt + col) * kKRow + 64 * ks + 16 * grp);
+            sk + (16 * kt + col) * kKRow + 64 * ks + 16 * grp);
 #pragma unroll
         for (int qg = 0; qg < 2; ++qg) s[qg][kt] = H::mma(a, qf[qg][ks], s[qg][kt]);
       }
     }
 
-    const bool need_mask = key0 + kKTile - 1 > pos_first;
+    // causal limit: only tiles reaching past this wave's first row mask.
+    // Key 16 kt + 4 grp + r of the tile is visible to row 16 qg + col iff
+    // 16 kt + r <= lim[qg].
+    const bool diag = key0 + kKTile - 1 > pos_first;
+    int lim[2];
+#pragma unroll
+    for (int qg = 0; qg < 2; ++qg) lim[qg] = pos_first + 16 * qg + col - key0 - 4 * grp;
+    if (diag) {
+#pragma unroll
+      for (int qg = 0; qg < 2; ++qg)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (16 * kt + r > lim[qg]) s[qg][kt][r] = -INFINITY;
+    }
+
     uint32_t phi[2][2][4], plo[2][2][4];  // [qg][step][word]
+    float mts[2];
+    bool grow = false;
 #pragma unroll
     for (int qg = 0; qg < 2; ++qg) {
-      const int pq = pos_first + 16 * qg + col;  // this lane's row position
-      float x[16];
       float mt = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = key0 + 16 * kt + 4 * grp + r;
-          float v = s[qg][kt][r] * scale_log2;
-          if (need_mask && key > pq) v = -INFINITY;
-          x[4 * kt + r] = v;
-          mt = fmaxf(mt, v);
-        }
+        mt = fmaxf(mt, fmaxf(fmaxf(s[qg][kt][0], s[qg][kt][1]),
+                             fmaxf(s[qg][kt][2], s[qg][kt][3])));
       mt = fmaxf(mt, __shfl_xor(mt, 16));
       mt = fmaxf(mt, __shfl_xor(mt, 32));
-      // every row has key 0, so m_run is finite after the first tile
-      const float m_new = fmaxf(m_run[qg], mt);
-      const float alpha = __builtin_amdgcn_exp2f(m_run[qg] - m_new);
-      m_run[qg] = m_new;
+      mts[qg] = mt == -INFINITY ? -INFINITY : mt * sl2;  // no -inf * 0
+      grow |= mts[qg] > m_run[qg] + kRescaleSlack;
+    }
+    // a row's max only moves up when it outgrows the slack; every row has
+    // key 0, so the first tile always sets it
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+      for (int qg = 0; qg < 2; ++qg) {
+        const bool up = mts[qg] > m_run[qg] + kRescaleSlack;
+        const float m_new = up ? mts[qg] : m_run[qg];
+        const float alpha = __builtin_amdgcn_exp2f(m_run[qg] - m_new);
+        m_run[qg] = m_new;
+        l_run[qg] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < kD / 16; ++dt) o[qg][dt] *= alpha;
+      }
+    }
+#pragma unroll
+    for (int qg = 0; qg < 2; ++qg) {
+      const float nm = -m_run[qg];
+      float x[16];
       float sum = 0.f;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        x[e] = __builtin_amdgcn_exp2f(x[e] - m_new);
-        sum += x[e];
-      }
-      l_run[qg] = l_run[qg] * alpha + sum;
+      for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int dt = 0; dt < kD / 16; ++dt) o[qg][dt] *= alpha;
+        for (int r = 0; r < 4; ++r)
+          x[4 * kt + r] = __builtin_amdgcn_exp2f(fmaf(s[qg][kt][r], sl2, nm));
+      if (diag) {  // masked weights are exactly 0, whatever the scale
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (16 * kt + r > lim[qg]) x[4 * kt + r] = 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sum += x[e];
+      l_run[qg] += sum;
       // B operand of step st: element e = 4 t + r is key 32 st + 16 t + 4 grp + r,
       // i.e. S^T slice kt = 2 st + t, register r.
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          uint32_t h0, l0, h1, l1;
           const int e0 = 2 * w;
-          H::split(x[4 * (2 * st + (e0 >> 2)) + (e0 & 3)], h0, l0);
-          H::split(x[4 * (2 * st + ((e0 + 1) >> 2)) + ((e0 + 1) & 3)], h1, l1);
-          phi[qg][st][w] = h0 | (h1 << 16);
-          plo[qg][st][w] = l0 | (l1 << 16);
+          H::split2(x[4 * (2 * st + (e0 >> 2)) + (e0 & 3)],
+                    x[4 * (2 * st + (e0 >> 2)) + (e0 & 3) + 1], phi[qg][st][w], plo[qg][st][w]);
         }
     }
 
@@ -308,7 +389,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
 #pragma unroll
       for (int dt = 0; dt < kD / 16; ++dt) {
         const u32x4 a = *reinterpret_cast<const u32x4*>(
-            s_vt + (16 * dt + col) * kVtRow + 64 * st + 16 * grp);
+            svt + (16 * dt + col) * kVtRow + 64 * st + 16 * grp);
 #pragma unroll
         for (int qg = 0; qg < 2; ++qg) {
           const u32x4 bh = {phi[qg][st][0], phi[qg][st][1], phi[qg][st][2], phi[qg][st][3]};
@@ -320,13 +401,17 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
     }
   };
 
+  // tile j lives in LDS buffer j % 2; tile j + 1's loads are in flight while
+  // tile j is computed, then stored into the other buffer (last read two
+  // barriers ago)
   load_tile(0);
+  store_tile(0, 0);
+  __syncthreads();
   for (int j = 0; j < ntiles; ++j) {
-    __syncthreads();  // every wave is done reading the previous tile
-    store_tile(j);
+    if (j + 1 < ntiles) load_tile(j + 1);
+    if (wrows > 0 && j * kKTile <= pos_last) compute_tile(j & 1, j);
+    if (j + 1 < ntiles) store_tile((j + 1) & 1, j + 1);
     __syncthreads();
-    if (j + 1 < ntiles) load_tile(j + 1);  // in flight during the MFMA work
-    if (wrows > 0 && j * kKTile <= pos_last) compute_tile(j);
   }
   bad_blk = __syncthreads_or(bad_blk);
 
