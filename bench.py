@@ -6,15 +6,17 @@ through every stage of the path:
   1. host allocator: one new slot per sequence (batch append, all or
      nothing; copy-on-write pairs if a shared block is hit), written with
      the block tables and lengths into one pinned staging buffer;
-  2. that buffer to the device in one asynchronous copy;
+  2. tables and lengths to the device in one asynchronous copy;
   3. block copies for copy-on-write pairs (none unless blocks are shared);
-  4. paged_kv_append of the step's new K/V rows;
-  5. paged_attention_decode: split-K partition kernel, then the merge.
+  4. paged_attention_decode_append: the split-K decode kernel, which first
+     stores each sequence's new K/V row at its newest position (the slot
+     the allocator returned), then the log-sum-exp merge kernel.
 The cache is resident in HBM before timing starts.  ``value`` is the KV
 bytes the decode reads per step (sum over sequences of context_len * Hkv *
 head_dim * 2 * element size) divided by the wall time of a whole step.
-``roofline`` reports the partition kernel alone, timed with HIP events on
-the stream it runs on; its ``traffic`` comes from the committed rocprofv3
+``roofline`` reports the decode partition kernel alone, timed with HIP
+events on the stream it runs on; its ``traffic`` comes from the committed
+rocprofv3
 counter summary of the same kernel source, when there is one.
 ``cpu_baseline`` times the float64 CPU oracle on a small sample of the same
 workload (reported only).  For the shared-prefix workload the line also
@@ -115,52 +117,50 @@ def gpu_run(args, w, torch, pkv, workloads):
                                                          w.head_dim, max_len, part)
     workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
 
-    # one staging buffer per step parity: [tables b*mb | lens b | slots b]
+    # Per step parity, a pinned staging buffer [tables b*mb | lens b | slots b];
+    # tables and lengths go to one device buffer with one copy on the
+    # kernels' stream (a copy on a stream of its own costs more: the
+    # cross-queue wait measured ~21 us per step against ~10 us in-stream).
+    # The slots stay on the host (the fused append derives them from the
+    # tables).
     words = b * mb + 2 * b
-    packed_d = torch.empty(words, dtype=torch.int32, device=dev)
-    tables_d = packed_d[:b * mb].view(b, mb)
-    lens_d = packed_d[b * mb:b * mb + b]
-    slots_d = packed_d[b * mb + b:]
-    staging = []
+    head = b * mb + b
+    stream = torch.cuda.current_stream(dev)
+    packed_d = torch.empty(head, dtype=torch.int32, device=dev)
+    tables_d, lens_d = packed_d[:b * mb].view(b, mb), packed_d[b * mb:]
+    slot = []
     for _ in range(2):
         buf = torch.empty(words, dtype=torch.int32, pin_memory=True)
         arr = buf.numpy()
-        staging.append(dict(buf=buf, tables=arr[:b * mb].reshape(b, mb),
-                            lens=arr[b * mb:b * mb + b], slots=arr[b * mb + b:],
-                            done=torch.cuda.Event()))
-    for st in staging:
-        st["done"].record()
-    ones = np.ones(b, dtype=np.int32)
-    stream = torch.cuda.current_stream(dev)
+        tables_h, lens_h, slots_h = arr[:b * mb].reshape(b, mb), arr[b * mb:head], arr[head:]
+        slot.append(dict(buf=buf, head=buf[:head], lens=lens_h, uploaded=torch.cuda.Event(),
+                         append=alloc.prepared_append_tables(seqs, np.ones(b, dtype=np.int32), mb,
+                                                             slots_h, tables_h, lens_h)))
+        slot[-1]["uploaded"].record(stream)
+    launch = pkv.DecodeLauncher(kc, vc, w.num_heads, b, mb, max_len, part, out, workspace)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(total_steps)]
     step_bytes = np.zeros(total_steps, dtype=np.float64)
-    step_ctx = np.zeros(total_steps, dtype=np.int64)
 
     def step(i):
-        st = staging[i % 2]
-        st["done"].synchronize()            # the copy issued two steps ago is done
-        _, pairs = alloc.append_batch(seqs, ones, slots_out=st["slots"])    # 1
-        alloc.build_block_tables(seqs, mb, tables_out=st["tables"], lens_out=st["lens"])
-        packed_d.copy_(st["buf"], non_blocking=True)                        # 2
-        st["done"].record(stream)
+        st = slot[i % 2]
+        st["uploaded"].synchronize()        # its upload two steps ago has finished
+        pairs = st["append"]()                                               # 1
+        packed_d.copy_(st["head"], non_blocking=True)                        # 2
+        st["uploaded"].record(stream)
         if pairs:                                                            # 3
             src = torch.tensor([a for a, _ in pairs], dtype=torch.int32).to(dev)
             dst = torch.tensor([c for _, c in pairs], dtype=torch.int32).to(dev)
             pkv.copy_blocks(kc, vc, src, dst)
-        pkv.paged_kv_append(k_new[i], v_new[i], kc, vc, slots_d)            # 4
         lens = st["lens"]
         mc = int(lens.max())
         e0, e1, e2 = ev[i]
         e0.record(stream)
-        pkv.paged_attention_decode_partials(q[i], kc, vc, tables_d, lens_d, w.scale, mc,  # 5
-                                            part, out, workspace)
+        launch.partials(q[i], tables_d, lens_d, mc, w.scale, k_new[i], v_new[i])  # 4
         e1.record(stream)
-        pkv.paged_attention_decode_merge(lens_d, w.num_kv_heads, w.block_size, mb, mc,
-                                         part, out, workspace)
+        launch.merge(lens_d, mc)
         e2.record(stream)
         step_bytes[i] = kv_bytes(w, lens)
-        step_ctx[i] = mc
 
     for i in range(args.warmup):
         step(i)
@@ -171,11 +171,11 @@ def gpu_run(args, w, torch, pkv, workloads):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     timed = range(args.warmup, total_steps)
-    part_ms = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in timed])
+    kernel_ms = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in timed])
     merge_ms = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in timed])
     if not torch.isfinite(out).all():
         raise RuntimeError("decode produced non-finite output")
-    res = dict(wall=wall, part_ms=part_ms, merge_ms=merge_ms, bytes=step_bytes[args.warmup:],
+    res = dict(wall=wall, kernel_ms=kernel_ms, merge_ms=merge_ms, bytes=step_bytes[args.warmup:],
                batch=b, part=part)
     if w.chunk and not args.no_prefill:
         res["prefill"] = prefill_run(w, p, alloc, kc, vc, torch, pkv, dev)
@@ -353,8 +353,8 @@ def main():
     ms_step = r["wall"] / args.steps * 1e3
     mean_bytes = float(r["bytes"].mean())
     value = mean_bytes / (ms_step * 1e-3) / 1e9
-    part_ms = float(r["part_ms"].mean())
-    achieved = mean_bytes / (part_ms * 1e-3) / 1e9
+    kernel_ms = float(r["kernel_ms"].mean())
+    achieved = mean_bytes / (kernel_ms * 1e-3) / 1e9
     src = os.path.join(ROOT, "paged_kv_cache_420_amd", "csrc", "decode.hip")
     line = {
         "metric": METRIC,
@@ -376,9 +376,9 @@ def main():
         "hbm_peak_frac": round(value / HBM_PEAK_GBPS, 4),
         "tokens_per_s": round(r["batch"] / (ms_step * 1e-3), 1),
         "kv_bytes_per_step": int(mean_bytes),
-        "decode_partition_us": round(part_ms * 1e3, 2),
+        "decode_partition_us": round(kernel_ms * 1e3, 2),
         "decode_merge_us": round(float(r["merge_ms"].mean()) * 1e3, 2),
-        "roofline": {"bound": "hbm", "kernel": "decode_partition_kernel",
+        "roofline": {"bound": "hbm", "kernel": "decode_partition_kernel (append fused)",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic_from_profiles(w, src)},

@@ -145,6 +145,21 @@ int32_t pkv_append_batch(pkv_allocator* alloc, const int64_t* seqs,
                          int32_t* cow_src, int32_t* cow_dst, int32_t cow_cap,
                          int32_t* n_cow);
 
+/* pkv_append_batch, then the batch's updated tables and lengths written as
+ * by pkv_build_block_tables (one call per decode step: the host images of
+ * the device arrays the attention calls read).  All or nothing: a table
+ * that would outgrow max_blocks fails with PKV_ERR_BUFFER_TOO_SMALL before
+ * any state changes.
+ *   block_tables  [num_seqs][max_blocks] host int32, -1 past each table
+ *   context_lens  [num_seqs] host int32 */
+int32_t pkv_append_batch_tables(pkv_allocator* alloc, const int64_t* seqs,
+                                const int32_t* counts, int32_t num_seqs,
+                                int32_t* slots_out, int64_t slots_cap,
+                                int32_t* cow_src, int32_t* cow_dst,
+                                int32_t cow_cap, int32_t* n_cow,
+                                int32_t max_blocks, int32_t* block_tables,
+                                int32_t* context_lens);
+
 /* Queries (host outputs). */
 int32_t pkv_seq_len(const pkv_allocator* alloc, int64_t seq, int32_t* len);
 /* Copies the table into out[cap]; *n = its length (checked against cap). */
@@ -211,10 +226,12 @@ int32_t pkv_paged_attention_decode_partition_size(
     int32_t num_seqs, int32_t num_kv_heads, int32_t block_size,
     int32_t max_context_len, int32_t partition_size, int32_t* resolved);
 
-/* Workspace needed by pkv_paged_attention_decode for these sizes, in
- * bytes (0 when no sequence needs more than one partition).  Pass the same
- * partition_size as to the decode call (0 = automatic: the choice depends
- * on num_seqs, num_kv_heads and max_context_len). */
+/* Workspace needed by pkv_paged_attention_decode(_append) for these sizes,
+ * in bytes (0 when no sequence can span two partitions): the split-K
+ * partials, num_seqs * num_heads * partitions * (head_dim + 2) floats.
+ * Pass the same partition_size as to the decode call (0 = automatic: the
+ * choice depends on num_seqs, num_kv_heads and max_context_len).  Its
+ * contents on entry do not matter. */
 int32_t pkv_paged_attention_decode_workspace_size(
     int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
     int32_t head_dim, int32_t max_context_len, int32_t partition_size,
@@ -232,11 +249,16 @@ int32_t pkv_paged_attention_decode_workspace_size(
  *                  max_blocks_per_seq * block_size, or whose used table
  *                  entries fall outside [0, num_blocks), gets NaN rows
  *   partition_size tokens per split-K partition: 0 = automatic, else a
- *                  multiple of block_size, at least 64, at most 1024
+ *                  multiple of 64 in [64, 1024] (raised to block_size)
  *   out            [num_seqs][num_heads][head_dim] float32
  *   workspace      device buffer of at least the size reported by
  *                  pkv_paged_attention_decode_workspace_size (may be NULL
- *                  when that size is 0)
+ *                  when that size is 0).  Calls that share a workspace must
+ *                  not run concurrently.
+ * Two launches on `stream`: the split-K partition kernel (sequences that
+ * fit one partition get their final rows directly), then the log-sum-exp
+ * merge of the longer ones (skipped when no sequence can span two
+ * partitions).
  * Supported: head_dim in {64, 128}; num_heads / num_kv_heads in
  * {1, 2, 4, 8}; block_size a power of two in [8, 256]; the scale is any
  * finite float.  Row h reads KV head h / (num_heads / num_kv_heads). */
@@ -249,15 +271,53 @@ int32_t pkv_paged_attention_decode(
     int32_t partition_size, float* out, void* workspace,
     size_t workspace_bytes, int32_t dtype, void* stream);
 
-/* The two stages of pkv_paged_attention_decode, for callers that schedule
- * or time them separately (same arguments, same semantics):
+/* One decode step with the append fused into the decode kernel: store this
+ * step's K/V row of every sequence at its newest position, then decode
+ * exactly as pkv_paged_attention_decode (explainer, serving section: each
+ * new token adds one K and one V vector, then attends over every cached
+ * token, its own included).  Copy-on-write copies reported by the
+ * allocator for this step must have been enqueued before.
+ *   key, value     [num_seqs][num_kv_heads][head_dim], cache dtype: the new
+ *                  rows; sequence b's row goes to position
+ *                  context_lens[b] - 1, whose slot is
+ *                  block_tables[b][(n-1) / block_size] * block_size +
+ *                  (n-1) % block_size -- the slot the allocator returned
+ *                  for that token (article §2.1)
+ *   context_lens   counts the new token; sequences with length 0 or
+ *                  inconsistent entries get no store (their rows as in
+ *                  pkv_paged_attention_decode)
+ * The result, caches included, is bit for bit that of pkv_paged_kv_append
+ * with those slots followed by pkv_paged_attention_decode. */
+int32_t pkv_paged_attention_decode_append(
+    const void* query, const void* key, const void* value, void* key_cache,
+    void* value_cache, const int32_t* block_tables, const int32_t* context_lens,
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+    int32_t max_context_len, float scale, int32_t partition_size, float* out,
+    void* workspace, size_t workspace_bytes, int32_t dtype, void* stream);
+
+/* The first stage of pkv_paged_attention_decode_append (the partition
+ * kernel with the fused store); follow it with
+ * pkv_paged_attention_decode_merge on the same stream, as for _partials
+ * below.  Same arguments as pkv_paged_attention_decode_append. */
+int32_t pkv_paged_attention_decode_append_partials(
+    const void* query, const void* key, const void* value, void* key_cache,
+    void* value_cache, const int32_t* block_tables, const int32_t* context_lens,
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+    int32_t max_context_len, float scale, int32_t partition_size, float* out,
+    void* workspace, size_t workspace_bytes, int32_t dtype, void* stream);
+
+/* pkv_paged_attention_decode as two launches, for callers that schedule or
+ * time the stages separately (same arguments, same semantics, same
+ * workspace):
  *   _partials launches the split-K partition kernel: sequences that fit in
  *   one partition get their final rows in `out`; longer ones leave
  *   per-partition (max, sum, unnormalised output) in `workspace`.
  *   _merge launches the log-sum-exp merge of those partials into `out`
  *   (nothing to do when no sequence spans two partitions).
- * Calling _partials then _merge on one stream, with identical sizes,
- * partition_size and buffers, is exactly pkv_paged_attention_decode. */
+ * _partials then _merge on one stream gives bit for bit the output of
+ * pkv_paged_attention_decode. */
 int32_t pkv_paged_attention_decode_partials(
     const void* query, const void* key_cache, const void* value_cache,
     const int32_t* block_tables, const int32_t* context_lens,

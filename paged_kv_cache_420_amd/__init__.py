@@ -22,9 +22,10 @@ import torch
 __all__ = [
     "PkvError", "InvalidArgument", "OutOfBlocks", "NoSuchSequence",
     "SequenceExists", "BufferTooSmall", "HipError", "Unsupported",
-    "BlockAllocator", "paged_kv_append", "copy_blocks",
+    "BlockAllocator", "DecodeLauncher", "paged_kv_append", "copy_blocks",
     "paged_attention_decode_workspace_size", "paged_attention_decode_partition_size",
-    "paged_attention_decode",
+    "paged_attention_decode", "paged_attention_decode_append",
+    "paged_attention_decode_append_partials",
     "paged_attention_decode_partials", "paged_attention_decode_merge",
     "paged_attention_prefill", "library_path", "version",
 ]
@@ -76,28 +77,36 @@ _PI64 = ctypes.POINTER(ctypes.c_int64)
 _SIGNATURES = {
     "pkv_last_error": (ctypes.c_char_p, []),
     "pkv_version": (ctypes.c_char_p, []),
-    "pkv_allocator_create": (_I32, [_I32, _I32, _PI32, ctypes.POINTER(_P)]),
+    "pkv_allocator_create": (_I32, [_I32, _I32, _P, ctypes.POINTER(_P)]),
     "pkv_allocator_destroy": (None, [_P]),
     "pkv_seq_add": (_I32, [_P, _I64]),
     "pkv_seq_free": (_I32, [_P, _I64]),
     "pkv_seq_fork": (_I32, [_P, _I64, _I64]),
-    "pkv_seq_append": (_I32, [_P, _I64, _I32, _PI32, _PI32, _PI32, _PI32]),
-    "pkv_append_batch": (_I32, [_P, _PI64, _PI32, _I32, _PI32, _I64, _PI32, _PI32, _I32, _PI32]),
-    "pkv_seq_len": (_I32, [_P, _I64, _PI32]),
-    "pkv_seq_block_table": (_I32, [_P, _I64, _PI32, _I32, _PI32]),
-    "pkv_num_free_blocks": (_I32, [_P, _PI32]),
-    "pkv_num_blocks": (_I32, [_P, _PI32]),
-    "pkv_block_size": (_I32, [_P, _PI32]),
-    "pkv_block_refcount": (_I32, [_P, _I32, _PI32]),
-    "pkv_allocator_snapshot": (_I32, [_P, _PI32, _PI32, _PI32]),
-    "pkv_build_block_tables": (_I32, [_P, _PI64, _I32, _I32, _PI32, _PI32]),
+    "pkv_seq_append": (_I32, [_P, _I64, _I32, _P, _P, _P, _P]),
+    "pkv_append_batch": (_I32, [_P, _P, _P, _I32, _P, _I64, _P, _P, _I32, _P]),
+    "pkv_append_batch_tables": (_I32, [_P, _P, _P, _I32, _P, _I64, _P, _P, _I32, _P,
+                                       _I32, _P, _P]),
+    "pkv_seq_len": (_I32, [_P, _I64, _P]),
+    "pkv_seq_block_table": (_I32, [_P, _I64, _P, _I32, _P]),
+    "pkv_num_free_blocks": (_I32, [_P, _P]),
+    "pkv_num_blocks": (_I32, [_P, _P]),
+    "pkv_block_size": (_I32, [_P, _P]),
+    "pkv_block_refcount": (_I32, [_P, _I32, _P]),
+    "pkv_allocator_snapshot": (_I32, [_P, _P, _P, _P]),
+    "pkv_build_block_tables": (_I32, [_P, _P, _I32, _I32, _P, _P]),
     "pkv_paged_kv_append": (_I32, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P]),
     "pkv_copy_blocks": (_I32, [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P]),
-    "pkv_paged_attention_decode_partition_size": (_I32, [_I32, _I32, _I32, _I32, _I32, _PI32]),
+    "pkv_paged_attention_decode_partition_size": (_I32, [_I32, _I32, _I32, _I32, _I32, _P]),
     "pkv_paged_attention_decode_workspace_size": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32,
                                                          ctypes.POINTER(ctypes.c_size_t)]),
     "pkv_paged_attention_decode": (_I32, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                                           ctypes.c_float, _I32, _P, _P, ctypes.c_size_t, _I32, _P]),
+    "pkv_paged_attention_decode_append": (_I32, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
+                                                 _I32, _I32, _I32, ctypes.c_float, _I32, _P, _P,
+                                                 ctypes.c_size_t, _I32, _P]),
+    "pkv_paged_attention_decode_append_partials": (_I32, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32,
+                                                          _I32, _I32, _I32, _I32, _I32, ctypes.c_float,
+                                                          _I32, _P, _P, ctypes.c_size_t, _I32, _P]),
     "pkv_paged_attention_decode_partials": (_I32, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                                                    _I32, ctypes.c_float, _I32, _P, _P, ctypes.c_size_t, _I32, _P]),
     "pkv_paged_attention_decode_merge": (_I32, [_P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P,
@@ -138,7 +147,7 @@ def _check(status):
 
 
 def _i32p(arr):
-    return arr.ctypes.data_as(_PI32)
+    return arr.ctypes.data
 
 
 # ---------------------------------------------------------------------------
@@ -164,6 +173,7 @@ class BlockAllocator:
                                          _i32p(order) if order is not None else None,
                                          ctypes.byref(handle)))
         self._h = handle
+        self._cow = None
         self.num_blocks = num_blocks
         self.block_size = block_size
 
@@ -212,10 +222,73 @@ class BlockAllocator:
         src = np.empty(cap, dtype=np.int32)
         dst = np.empty(cap, dtype=np.int32)
         cnt = _I32()
-        _check(_lib.pkv_append_batch(self._h, seqs.ctypes.data_as(_PI64), _i32p(counts), len(seqs),
+        _check(_lib.pkv_append_batch(self._h, seqs.ctypes.data, _i32p(counts), len(seqs),
                                      _i32p(slots), total, _i32p(src), _i32p(dst), len(seqs),
                                      ctypes.byref(cnt)))
         return slots[:total], list(zip(src[:cnt.value].tolist(), dst[:cnt.value].tolist()))
+
+    def append_batch_tables(self, seqs, counts, max_blocks, slots_out=None, tables_out=None,
+                            lens_out=None):
+        """append_batch, then the batch's updated tables [B, max_blocks] and
+        lengths [B] (pkv_append_batch_tables): all in one call, all or
+        nothing.  Outputs may be given as contiguous int32 arrays (e.g. views
+        of a pinned staging buffer).  Returns (slots, cow pairs, tables, lens)."""
+        seqs = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64))
+        counts = np.ascontiguousarray(np.asarray(counts, dtype=np.int32))
+        b = len(seqs)
+        if counts.shape != seqs.shape:
+            raise InvalidArgument("seqs and counts differ in length")
+        total = int(counts.sum(dtype=np.int64))
+
+        def out(arr, shape):
+            if arr is None:
+                return np.empty(shape, dtype=np.int32)
+            if arr.dtype != np.int32 or arr.shape != shape or not arr.flags.c_contiguous:
+                raise InvalidArgument(f"output must be a contiguous int32 array of shape {shape}")
+            return arr
+
+        slots = out(slots_out, (total,))
+        tables = out(tables_out, (b, max_blocks))
+        lens = out(lens_out, (b,))
+        cap = max(b, 1)
+        if self._cow is None or len(self._cow[0]) < cap:
+            self._cow = (np.empty(cap, dtype=np.int32), np.empty(cap, dtype=np.int32))
+        src, dst = self._cow
+        cnt = _I32()
+        _check(_lib.pkv_append_batch_tables(
+            self._h, seqs.ctypes.data, counts.ctypes.data, b,
+            slots.ctypes.data, total, src.ctypes.data,
+            dst.ctypes.data, b, ctypes.byref(cnt), max_blocks,
+            tables.ctypes.data, lens.ctypes.data))
+        pairs = list(zip(src[:cnt.value].tolist(), dst[:cnt.value].tolist()))
+        return slots, pairs, tables, lens
+
+    def prepared_append_tables(self, seqs, counts, max_blocks, slots_out, tables_out, lens_out):
+        """append_batch_tables with every argument marshalled once, for a
+        loop that appends the same counts to the same sequences into the
+        same (e.g. pinned staging) arrays each step.  Returns a function
+        that makes the call and returns the copy-on-write pairs."""
+        seqs = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64))
+        counts = np.ascontiguousarray(np.asarray(counts, dtype=np.int32))
+        b = len(seqs)
+        total = int(counts.sum(dtype=np.int64))
+        for arr, shape in ((slots_out, (total,)), (tables_out, (b, max_blocks)), (lens_out, (b,))):
+            if arr.dtype != np.int32 or arr.shape != shape or not arr.flags.c_contiguous:
+                raise InvalidArgument(f"output must be a contiguous int32 array of shape {shape}")
+        src = np.empty(max(b, 1), dtype=np.int32)
+        dst = np.empty(max(b, 1), dtype=np.int32)
+        cnt = _I32()
+        keep = (seqs, counts, slots_out, tables_out, lens_out, src, dst, cnt)
+        args = (self._h, seqs.ctypes.data, counts.ctypes.data, b, slots_out.ctypes.data, total,
+                src.ctypes.data, dst.ctypes.data, b, ctypes.byref(cnt), max_blocks,
+                tables_out.ctypes.data, lens_out.ctypes.data)
+        fn = _lib.pkv_append_batch_tables
+
+        def call(_keep=keep):
+            _check(fn(*args))
+            k = cnt.value
+            return list(zip(src[:k].tolist(), dst[:k].tolist())) if k else []
+        return call
 
     def seq_len(self, seq):
         out = _I32()
@@ -265,7 +338,7 @@ class BlockAllocator:
                     or lens.shape != (b,) or not lens.flags.c_contiguous):
                 raise InvalidArgument("tables_out/lens_out must be contiguous int32 "
                                       "[B, max_blocks] and [B]")
-        _check(_lib.pkv_build_block_tables(self._h, seqs.ctypes.data_as(_PI64), b, max_blocks,
+        _check(_lib.pkv_build_block_tables(self._h, seqs.ctypes.data, b, max_blocks,
                                            _i32p(tables), _i32p(lens)))
         return tables[:b, :max_blocks], lens[:b]
 
@@ -398,6 +471,123 @@ def paged_attention_decode(query, key_cache, value_cache, block_tables, context_
         int(max_context_len), float(scale), int(partition_size), out.data_ptr(), ws_ptr, ws_bytes,
         _dtype_code(key_cache), _stream(query)))
     return out
+
+
+def _decode_append(fn, query, key, value, key_cache, value_cache, block_tables, context_lens,
+                   scale, max_context_len, partition_size, out, workspace):
+    (nb, hkv, bs, d, b, hq), out, workspace, ws_ptr, ws_bytes = _decode_args(
+        query, key_cache, value_cache, block_tables, context_lens, max_context_len,
+        partition_size, out, workspace)
+    _dev(key, "key", dtype=key_cache.dtype, ndim=3)
+    _dev(value, "value", dtype=key_cache.dtype, ndim=3)
+    if tuple(key.shape) != (b, hkv, d) or value.shape != key.shape:
+        raise InvalidArgument("key/value must be [B, num_kv_heads, head_dim]")
+    _check(fn(query.data_ptr(), key.data_ptr(), value.data_ptr(), key_cache.data_ptr(),
+              value_cache.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(), b, hq,
+              hkv, d, bs, block_tables.shape[1], nb, int(max_context_len), float(scale),
+              int(partition_size), out.data_ptr(), ws_ptr, ws_bytes, _dtype_code(key_cache),
+              _stream(query)))
+    return out
+
+
+def paged_attention_decode_append(query, key, value, key_cache, value_cache, block_tables,
+                                  context_lens, scale, max_context_len, partition_size=0,
+                                  out=None, workspace=None):
+    """One decode step with the append fused into the decode kernel
+    (pkv_paged_attention_decode_append): store key/value [B, Hkv, D] at each
+    sequence's newest position (context_lens[b] - 1, counted in
+    context_lens), then decode.  Returns out [B, Hq, D] float32."""
+    return _decode_append(_lib.pkv_paged_attention_decode_append, query, key, value, key_cache,
+                          value_cache, block_tables, context_lens, scale, max_context_len,
+                          partition_size, out, workspace)
+
+
+def paged_attention_decode_append_partials(query, key, value, key_cache, value_cache,
+                                           block_tables, context_lens, scale, max_context_len,
+                                           partition_size, out, workspace):
+    """First stage of paged_attention_decode_append
+    (pkv_paged_attention_decode_append_partials); pass the same ``out`` and
+    ``workspace`` to paged_attention_decode_merge."""
+    return _decode_append(_lib.pkv_paged_attention_decode_append_partials, query, key, value,
+                          key_cache, value_cache, block_tables, context_lens, scale,
+                          max_context_len, partition_size, out, workspace)
+
+
+class DecodeLauncher:
+    """Paged decode launches with the fixed arguments marshalled once: a
+    serving loop's hot path costs one ctypes call per launch.
+
+    The caches, output, workspace and sizes are checked when the launcher
+    is made; each launch checks only the shapes and dtypes of the per-step
+    tensors (query, new K/V rows, tables, lengths) and that its
+    max_context_len is within the bound the workspace was sized for.  The
+    library checks everything else, as for the plain functions.
+    ``partials`` (with ``key``/``value``: the append fused in) and ``merge``
+    are the two stages of paged_attention_decode(_append)."""
+
+    def __init__(self, key_cache, value_cache, num_heads, num_seqs, max_blocks,
+                 max_context_len, partition_size, out, workspace, stream=None):
+        nb, hkv, bs, d = _cache_dims(key_cache, value_cache)
+        _dev(out, "out", dtype=torch.float32, ndim=3)
+        if tuple(out.shape) != (num_seqs, num_heads, d):
+            raise InvalidArgument("out must be [num_seqs, num_heads, head_dim]")
+        need = paged_attention_decode_workspace_size(num_seqs, num_heads, hkv, d,
+                                                     int(max_context_len), partition_size)
+        ws_ptr, ws_bytes = None, 0
+        if workspace is not None:
+            _dev(workspace, "workspace")
+            ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+        if ws_bytes < need:
+            raise BufferTooSmall(f"workspace needs {need} bytes")
+        self.part = paged_attention_decode_partition_size(num_seqs, hkv, bs, int(max_context_len),
+                                                          partition_size)
+        self._keep = (key_cache, value_cache, out, workspace)
+        self._dtype = key_cache.dtype
+        self._q_shape = (num_seqs, num_heads, d)
+        self._kv_shape = (num_seqs, hkv, d)
+        self._t_shape = (num_seqs, max_blocks)
+        self._max_ctx = int(max_context_len)
+        self._stream = ctypes.c_void_p((torch.cuda.current_stream(key_cache.device)
+                                        if stream is None else stream).cuda_stream)
+        self._dims = (num_seqs, num_heads, hkv, d, bs, max_blocks, nb)
+        self._kc, self._vc, self._out = key_cache.data_ptr(), value_cache.data_ptr(), out.data_ptr()
+        self._ws = (ws_ptr, ws_bytes)
+        self._code = _dtype_code(key_cache)
+
+    def _check_step(self, t, shape, dtype, name):
+        if t.shape != shape or t.dtype != dtype or not t.is_contiguous():
+            raise InvalidArgument(f"{name} must be a contiguous {dtype} tensor of shape {shape}")
+        return t.data_ptr()
+
+    def partials(self, query, block_tables, context_lens, max_context_len, scale, key=None,
+                 value=None):
+        if max_context_len > self._max_ctx:
+            raise InvalidArgument("max_context_len above the launcher's bound")
+        q = self._check_step(query, self._q_shape, self._dtype, "query")
+        t = self._check_step(block_tables, self._t_shape, torch.int32, "block_tables")
+        l_ = self._check_step(context_lens, self._t_shape[:1], torch.int32, "context_lens")
+        b, hq, hkv, d, bs, mb, nb = self._dims
+        if key is None:
+            _check(_lib.pkv_paged_attention_decode_partials(
+                q, self._kc, self._vc, t, l_, b, hq, hkv, d, bs, mb, nb, int(max_context_len),
+                float(scale), self.part, self._out, self._ws[0], self._ws[1], self._code,
+                self._stream))
+        else:
+            k = self._check_step(key, self._kv_shape, self._dtype, "key")
+            v = self._check_step(value, self._kv_shape, self._dtype, "value")
+            _check(_lib.pkv_paged_attention_decode_append_partials(
+                q, k, v, self._kc, self._vc, t, l_, b, hq, hkv, d, bs, mb, nb,
+                int(max_context_len), float(scale), self.part, self._out, self._ws[0],
+                self._ws[1], self._code, self._stream))
+
+    def merge(self, context_lens, max_context_len):
+        if max_context_len > self._max_ctx:
+            raise InvalidArgument("max_context_len above the launcher's bound")
+        l_ = self._check_step(context_lens, self._t_shape[:1], torch.int32, "context_lens")
+        b, hq, hkv, d, bs, mb, nb = self._dims
+        _check(_lib.pkv_paged_attention_decode_merge(
+            l_, b, hq, hkv, d, bs, mb, int(max_context_len), self.part, self._out, self._ws[0],
+            self._ws[1], self._stream))
 
 
 def paged_attention_decode_partials(query, key_cache, value_cache, block_tables, context_lens,

@@ -1,7 +1,8 @@
 // Host block allocator (see allocator.h for the contract and sources).
 #include "allocator.h"
 
-#include <unordered_set>
+#include <algorithm>
+#include <utility>
 
 #include "common.h"
 
@@ -113,40 +114,62 @@ int32_t BlockAllocator::append_batch(const int64_t* seqs,
                                      const int32_t* counts, int32_t num_seqs,
                                      int32_t* slots, int64_t slots_cap,
                                      CowPair* cow, int32_t cow_cap,
-                                     int32_t* n_cow) {
+                                     int32_t* n_cow, int32_t max_blocks,
+                                     int32_t* tables, int32_t* lens) {
   if (num_seqs < 0) return fail(PKV_ERR_INVALID, "negative batch size");
-  // Validate everything, and count the blocks the whole batch needs in
-  // batch order: a copy-on-write of one sequence lowers the count of a
-  // block other members of the batch may still share.
-  std::unordered_set<int64_t> seen;
+  // One lookup per sequence; scratch reused across calls (one decode step
+  // of a large batch should cost microseconds, not allocations).
+  thread_local std::vector<Seq*> ptr;
+  thread_local std::vector<int64_t> ids;
+  thread_local std::vector<std::pair<int32_t, int32_t>> dropped;  // block, refs given up
+  ptr.resize(num_seqs);
+  ids.assign(seqs, seqs + num_seqs);
   for (int32_t i = 0; i < num_seqs; ++i) {
-    if (!has(seqs[i]))
+    auto it = seqs_.find(seqs[i]);
+    if (it == seqs_.end())
       return fail(PKV_ERR_NO_SUCH_SEQ, "no sequence %lld",
-                  static_cast<long long>(seqs[i]));
-    if (!seen.insert(seqs[i]).second)
-      return fail(PKV_ERR_INVALID, "sequence %lld appears twice in a batch",
                   static_cast<long long>(seqs[i]));
     if (counts[i] < 0)
       return fail(PKV_ERR_INVALID, "negative token count %d", counts[i]);
+    ptr[i] = &it->second;
   }
-  std::unordered_map<int32_t, int32_t> dropped;  // block -> refs given up
+  std::sort(ids.begin(), ids.end());
+  for (int32_t i = 1; i < num_seqs; ++i)
+    if (ids[i] == ids[i - 1])
+      return fail(PKV_ERR_INVALID, "sequence %lld appears twice in a batch",
+                  static_cast<long long>(ids[i]));
+  // Count the blocks the whole batch needs in batch order: a copy-on-write
+  // of one sequence lowers the count of a block other members may share.
+  dropped.clear();
   int64_t total_slots = 0, need = 0;
   int32_t cows = 0;
   for (int32_t i = 0; i < num_seqs; ++i) {
-    const Seq& s = seqs_.at(seqs[i]);
+    const Seq& s = *ptr[i];
     int32_t last_ref = 0;
     if (!s.table.empty()) {
-      int32_t last = s.table.back();
-      auto d = dropped.find(last);
-      last_ref = ref_[last] - (d == dropped.end() ? 0 : d->second);
+      const int32_t last = s.table.back();
+      last_ref = ref_[last];
+      for (const auto& d : dropped)
+        if (d.first == last) last_ref -= d.second;
     }
     bool c = false;
     need += blocks_needed(s, counts[i], last_ref, &c);
     if (c) {
-      ++dropped[s.table.back()];
+      bool found = false;
+      for (auto& d : dropped)
+        if (d.first == s.table.back()) {
+          ++d.second;
+          found = true;
+        }
+      if (!found) dropped.emplace_back(s.table.back(), 1);
       ++cows;
     }
     total_slots += counts[i];
+    if (tables &&
+        cdiv(int64_t(s.len) + counts[i], block_size_) > int64_t(max_blocks))
+      return fail(PKV_ERR_BUFFER_TOO_SMALL,
+                  "sequence %lld would hold more than max_blocks %d blocks",
+                  static_cast<long long>(seqs[i]), max_blocks);
   }
   if (total_slots > slots_cap)
     return fail(PKV_ERR_BUFFER_TOO_SMALL, "slots buffer holds %lld, need %lld",
@@ -161,11 +184,21 @@ int32_t BlockAllocator::append_batch(const int64_t* seqs,
   std::vector<CowPair> pairs;
   int64_t off = 0;
   for (int32_t i = 0; i < num_seqs; ++i) {
-    grow(seqs_.at(seqs[i]), counts[i], slots + off, &pairs);
+    grow(*ptr[i], counts[i], slots + off, &pairs);
     off += counts[i];
   }
   for (size_t k = 0; k < pairs.size(); ++k) cow[k] = pairs[k];
   *n_cow = static_cast<int32_t>(pairs.size());
+  if (tables) {
+    for (int32_t i = 0; i < num_seqs; ++i) {
+      const Seq& s = *ptr[i];
+      int32_t* row = tables + int64_t(i) * max_blocks;
+      const int32_t nb = static_cast<int32_t>(s.table.size());
+      std::copy(s.table.begin(), s.table.end(), row);
+      std::fill(row + nb, row + max_blocks, -1);
+      if (lens) lens[i] = s.len;
+    }
+  }
   return ok();
 }
 

@@ -49,9 +49,14 @@ class BlockAllocator {
   int32_t append(int64_t seq, int32_t n, int32_t* slots,
                  std::vector<CowPair>* cow);
   // All-or-nothing over the batch; capacities checked before any change.
+  // With `tables` (and `lens`), the batch's updated block tables are then
+  // written as rows of max_blocks entries (-1 past each table's end) and
+  // its lengths; a table longer than max_blocks fails up front.
   int32_t append_batch(const int64_t* seqs, const int32_t* counts,
                        int32_t num_seqs, int32_t* slots, int64_t slots_cap,
-                       CowPair* cow, int32_t cow_cap, int32_t* n_cow);
+                       CowPair* cow, int32_t cow_cap, int32_t* n_cow,
+                       int32_t max_blocks = 0, int32_t* tables = nullptr,
+                       int32_t* lens = nullptr);
 
  private:
   struct Seq {

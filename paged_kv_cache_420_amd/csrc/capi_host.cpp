@@ -138,6 +138,38 @@ int32_t pkv_append_batch(pkv_allocator* alloc, const int64_t* seqs,
   return PKV_OK;
 }
 
+int32_t pkv_append_batch_tables(pkv_allocator* alloc, const int64_t* seqs,
+                                const int32_t* counts, int32_t num_seqs,
+                                int32_t* slots_out, int64_t slots_cap,
+                                int32_t* cow_src, int32_t* cow_dst,
+                                int32_t cow_cap, int32_t* n_cow,
+                                int32_t max_blocks, int32_t* block_tables,
+                                int32_t* context_lens) {
+  PKV_REQUIRE(alloc, "allocator is NULL");
+  PKV_REQUIRE(num_seqs == 0 || (seqs && counts), "seqs/counts are NULL");
+  PKV_REQUIRE(slots_cap == 0 || slots_out, "slots_out is NULL");
+  PKV_REQUIRE(cow_cap == 0 || (cow_src && cow_dst), "cow outputs are NULL");
+  PKV_REQUIRE(n_cow, "n_cow is NULL");
+  PKV_REQUIRE(cow_cap >= 0 && slots_cap >= 0 && max_blocks >= 0, "negative capacity");
+  PKV_REQUIRE(num_seqs == 0 || max_blocks == 0 || block_tables, "block_tables is NULL");
+  PKV_REQUIRE(num_seqs == 0 || context_lens, "context_lens is NULL");
+  thread_local std::vector<pkv::CowPair> pairs;
+  pairs.resize(cow_cap > 0 ? cow_cap : 0);
+  int32_t got = 0;
+  thread_local int32_t dummy_row = 0;
+  int32_t st = alloc->impl.append_batch(seqs, counts, num_seqs, slots_out, slots_cap,
+                                        pairs.data(), cow_cap, &got, max_blocks,
+                                        block_tables ? block_tables : &dummy_row,
+                                        context_lens);
+  if (st != PKV_OK) return st;
+  for (int32_t i = 0; i < got; ++i) {
+    cow_src[i] = pairs[i].src;
+    cow_dst[i] = pairs[i].dst;
+  }
+  *n_cow = got;
+  return PKV_OK;
+}
+
 int32_t pkv_seq_len(const pkv_allocator* alloc, int64_t seq, int32_t* len) {
   PKV_REQUIRE(alloc && len, "NULL argument");
   if (!alloc->impl.has(seq))

@@ -226,20 +226,32 @@ __device__ __forceinline__ void issue_chunk(uint4 (&buf)[U], const uint8_t* base
   }
 }
 
+// Everything a decode launch needs, passed by value as the kernel argument.
+struct DecodeParams {
+  const uint8_t* query;        // [B][Hq][D]
+  const uint8_t* key_cache;    // [NB][Hkv][BS][D]
+  const uint8_t* value_cache;
+  const int32_t* block_tables; // [B][max_blocks]
+  const int32_t* context_lens; // [B]
+  const uint8_t* key_new;      // [B][Hkv][D] or null: fused append
+  const uint8_t* value_new;
+  float* out;                  // [B][Hq][D]
+  float* ws_acc;               // [B][Hq][max_parts][D]  (split-K partials)
+  float* ws_ml;                // [B][Hq][max_parts][2]
+  int32_t num_kv_heads, log2_bs, max_blocks, num_blocks, max_ctx, part, max_parts;
+  float scale_log2;
+};
+
 // Dynamic LDS: [scores: max(part*G, kWaves*G*D) floats][block ids][m/l].
 template <int DT, int D, int G, int U>
-__global__ __launch_bounds__(kThreads) void decode_partition_kernel(
-    const uint8_t* __restrict__ query, const uint8_t* __restrict__ key_cache,
-    const uint8_t* __restrict__ value_cache,
-    const int32_t* __restrict__ block_tables,
-    const int32_t* __restrict__ context_lens, int32_t num_kv_heads,
-    int32_t log2_bs, int32_t max_blocks, int32_t num_blocks,
-    int32_t max_ctx, int32_t part, int32_t max_parts, float scale_log2,
-    float* __restrict__ out, float* __restrict__ ws_acc,
-    float* __restrict__ ws_ml) {
+__global__ __launch_bounds__(kThreads) void decode_partition_kernel(const DecodeParams prm) {
   using C = Cfg<DT, D, G, U>;
   using E = Elem<DT>;
   extern __shared__ float smem[];
+  const int32_t num_kv_heads = prm.num_kv_heads, log2_bs = prm.log2_bs;
+  const int32_t max_blocks = prm.max_blocks, num_blocks = prm.num_blocks;
+  const int32_t part = prm.part, max_parts = prm.max_parts;
+  const float scale_log2 = prm.scale_log2;
 
   // Grid (kv head, sequence, partition), kv head fastest: workgroups go to
   // the 8 XCDs round-robin by linear id, so consecutive ids must carry
@@ -256,13 +268,13 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(
   const int bs = 1 << log2_bs;
   const int num_heads = num_kv_heads * G;
 
-  const int n = context_lens[b];
+  const int n = prm.context_lens[b];
   const bool bad_len =
-      n < 0 || n > max_ctx || int64_t(n) > int64_t(max_blocks) * bs;
+      n < 0 || n > prm.max_ctx || int64_t(n) > int64_t(max_blocks) * bs;
   const int nparts = bad_len ? 1 : max(1, cdiv(n, part));
   if (p_idx >= nparts) return;
 
-  float* out_row = out + (int64_t(b) * num_heads + int64_t(kvh) * G) * D;
+  float* out_row = prm.out + (int64_t(b) * num_heads + int64_t(kvh) * G) * D;
   if (bad_len || n == 0) {
     const float fill = bad_len ? __builtin_nanf("") : 0.0f;
     for (int i = tid; i < G * D; i += kThreads) out_row[i] = fill;
@@ -277,7 +289,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(
   const int p0 = p_idx * part;
   const int ntok = min(part, n - p0);
   const int nblk = (ntok + bs - 1) >> log2_bs;
-  const int32_t* table = block_tables + int64_t(b) * max_blocks + (p0 >> log2_bs);
+  const int32_t* table = prm.block_tables + int64_t(b) * max_blocks + (p0 >> log2_bs);
   bool bad_blk = false;
   for (int i = tid; i < nblk; i += kThreads) {
     int id = table[i];
@@ -286,6 +298,32 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(
       id = 0;
     }
     s_blk[i] = id;
+  }
+
+  const int64_t tile_bytes = int64_t(bs) * C::kRow;           // one (block, head) tile
+  const int64_t blk_stride = tile_bytes * num_kv_heads;
+
+  // Fused append: the partition holding the newest position n - 1 stores
+  // this step's K/V row for its kv head there before reading the cache
+  // (the same bytes a separate slot-mapped append would write).  Only this
+  // workgroup reads those two rows in this launch, and the barrier below
+  // orders its stores before its own loads (workgroup scope: the stores
+  // reach this XCD's L2, the loads miss the L1, which starts every launch
+  // empty).  No device-scope fence is needed -- on this GPU one writes back
+  // the XCD's whole L2.
+  if (prm.key_new != nullptr && p_idx == nparts - 1) {
+    const int pos = n - 1 - p0;  // within the partition
+    int id = table[pos >> log2_bs];
+    if (id >= 0 && id < num_blocks && tid < 2 * C::kLpt) {
+      const bool is_v = tid >= C::kLpt;
+      const int piece = tid - (is_v ? C::kLpt : 0);
+      const int64_t src = (int64_t(b) * num_kv_heads + kvh) * C::kRow + piece * 16;
+      const int64_t dst = int64_t(id) * blk_stride + int64_t(kvh) * tile_bytes +
+                          int64_t(pos & (bs - 1)) * C::kRow + piece * 16;
+      const uint8_t* from = is_v ? prm.value_new : prm.key_new;
+      uint8_t* to = const_cast<uint8_t*>(is_v ? prm.value_cache : prm.key_cache);
+      *reinterpret_cast<uint4*>(to + dst) = *reinterpret_cast<const uint4*>(from + src);
+    }
   }
   bad_blk = __syncthreads_or(bad_blk);
 
@@ -296,12 +334,10 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(
 #pragma unroll
   for (int g = 0; g < G; ++g)
     q[g] = *reinterpret_cast<const uint4*>(
-        query + ((int64_t(b) * num_heads + int64_t(kvh) * G + g) * C::kRow) + dl * 16);
+        prm.query + ((int64_t(b) * num_heads + int64_t(kvh) * G + g) * C::kRow) + dl * 16);
 
-  const int64_t tile_bytes = int64_t(bs) * C::kRow;           // one (block, head) tile
-  const int64_t blk_stride = tile_bytes * num_kv_heads;
-  const uint8_t* kbase = key_cache + int64_t(kvh) * tile_bytes + dl * 16;
-  const uint8_t* vbase = value_cache + int64_t(kvh) * tile_bytes + dl * 16;
+  const uint8_t* kbase = prm.key_cache + int64_t(kvh) * tile_bytes + dl * 16;
+  const uint8_t* vbase = prm.value_cache + int64_t(kvh) * tile_bytes + dl * 16;
   const int nchunks = cdiv(ntok, C::kChunkTok);
   // This wave's chunks are wave, wave + kWaves, ...: nj of them.  The walk
   // over them keeps the next chunk's loads in flight while one is computed,
@@ -445,10 +481,10 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(
       out_row[i] = bad_blk ? nan : a / l;
     } else {
       const int64_t row = (int64_t(b) * num_heads + int64_t(kvh) * G + g) * max_parts + p_idx;
-      ws_acc[row * D + (i - g * D)] = bad_blk ? nan : a;
+      prm.ws_acc[row * D + (i - g * D)] = bad_blk ? nan : a;
       if (i - g * D == 0) {
-        ws_ml[row * 2] = bad_blk ? nan : m;
-        ws_ml[row * 2 + 1] = bad_blk ? nan : l;
+        prm.ws_ml[row * 2] = bad_blk ? nan : m;
+        prm.ws_ml[row * 2 + 1] = bad_blk ? nan : l;
       }
     }
   }
@@ -525,51 +561,43 @@ int32_t resolve_partition(int32_t partition_size, int32_t block_size,
 }
 
 template <int DT, int D, int G>
-hipError_t launch_decode(const void* q, const void* kc, const void* vc,
-                         const int32_t* tables, const int32_t* lens, int B,
-                         int Hkv, int log2_bs, int max_blocks, int num_blocks,
-                         int max_ctx, int part, int max_parts, float scale_log2,
-                         float* out, float* ws_acc, float* ws_ml,
-                         hipStream_t stream) {
-  const int score_floats = std::max(part * G, kWaves * G * D);
-  const size_t lds = size_t(score_floats) * 4 + size_t(part >> 3) * 4 +
+hipError_t launch_decode(const DecodeParams& prm, int B, hipStream_t stream) {
+  const int score_floats = std::max(prm.part * G, kWaves * G * D);
+  const size_t lds = size_t(score_floats) * 4 + size_t(prm.part >> 3) * 4 +
                      size_t(2 * kWaves * G) * 4;
   hipLaunchKernelGGL((decode_partition_kernel<DT, D, G, kUnitsPerChunk>),
-                     dim3(Hkv, B, max_parts), dim3(kThreads), lds, stream,
-                     static_cast<const uint8_t*>(q), static_cast<const uint8_t*>(kc),
-                     static_cast<const uint8_t*>(vc), tables, lens, Hkv, log2_bs,
-                     max_blocks, num_blocks, max_ctx, part, max_parts, scale_log2,
-                     out, ws_acc, ws_ml);
+                     dim3(prm.num_kv_heads, B, prm.max_parts), dim3(kThreads), lds, stream, prm);
   return hipGetLastError();
 }
 
 template <int DT, int D>
-hipError_t dispatch_group(int G, const void* q, const void* kc, const void* vc,
-                          const int32_t* tables, const int32_t* lens, int B,
-                          int Hkv, int log2_bs, int max_blocks, int num_blocks,
-                          int max_ctx, int part, int max_parts, float sl2,
-                          float* out, float* wa, float* wm, hipStream_t s) {
+hipError_t dispatch_group(int G, const DecodeParams& prm, int B, hipStream_t s) {
   switch (G) {
-    case 1: return launch_decode<DT, D, 1>(q, kc, vc, tables, lens, B, Hkv, log2_bs, max_blocks, num_blocks, max_ctx, part, max_parts, sl2, out, wa, wm, s);
-    case 2: return launch_decode<DT, D, 2>(q, kc, vc, tables, lens, B, Hkv, log2_bs, max_blocks, num_blocks, max_ctx, part, max_parts, sl2, out, wa, wm, s);
-    case 4: return launch_decode<DT, D, 4>(q, kc, vc, tables, lens, B, Hkv, log2_bs, max_blocks, num_blocks, max_ctx, part, max_parts, sl2, out, wa, wm, s);
-    case 8: return launch_decode<DT, D, 8>(q, kc, vc, tables, lens, B, Hkv, log2_bs, max_blocks, num_blocks, max_ctx, part, max_parts, sl2, out, wa, wm, s);
+    case 1: return launch_decode<DT, D, 1>(prm, B, s);
+    case 2: return launch_decode<DT, D, 2>(prm, B, s);
+    case 4: return launch_decode<DT, D, 4>(prm, B, s);
+    case 8: return launch_decode<DT, D, 8>(prm, B, s);
   }
   return hipErrorInvalidValue;
 }
 
-template <int DT>
-hipError_t dispatch_dim(int D, int G, const void* q, const void* kc,
-                        const void* vc, const int32_t* tables,
-                        const int32_t* lens, int B, int Hkv, int log2_bs,
-                        int max_blocks, int num_blocks, int max_ctx, int part,
-                        int max_parts, float sl2, float* out, float* wa,
-                        float* wm, hipStream_t s) {
-  if (D == 64)
-    return dispatch_group<DT, 64>(G, q, kc, vc, tables, lens, B, Hkv, log2_bs, max_blocks, num_blocks, max_ctx, part, max_parts, sl2, out, wa, wm, s);
-  return dispatch_group<DT, 128>(G, q, kc, vc, tables, lens, B, Hkv, log2_bs, max_blocks, num_blocks, max_ctx, part, max_parts, sl2, out, wa, wm, s);
+hipError_t dispatch_decode(int32_t dtype, int D, int G, const DecodeParams& prm, int B,
+                           hipStream_t s) {
+  switch (dtype) {
+    case PKV_BF16:
+      return D == 64 ? dispatch_group<PKV_BF16, 64>(G, prm, B, s)
+                     : dispatch_group<PKV_BF16, 128>(G, prm, B, s);
+    case PKV_F16:
+      return D == 64 ? dispatch_group<PKV_F16, 64>(G, prm, B, s)
+                     : dispatch_group<PKV_F16, 128>(G, prm, B, s);
+    default:
+      return D == 64 ? dispatch_group<PKV_F32, 64>(G, prm, B, s)
+                     : dispatch_group<PKV_F32, 128>(G, prm, B, s);
+  }
 }
 
+// Workspace (only when some sequence may span two partitions):
+//   [acc: B * Hq * max_parts * D floats][(m, l): B * Hq * max_parts * 2 floats]
 size_t workspace_bytes(int B, int Hq, int D, int max_parts) {
   if (max_parts <= 1) return 0;
   return size_t(B) * Hq * max_parts * (size_t(D) + 2) * sizeof(float);
@@ -640,7 +668,6 @@ int32_t prepare_decode(const void* query, const void* key_cache,
   if (num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0)
     return fail(PKV_ERR_INVALID, "num_heads %d must be a positive multiple of num_kv_heads %d",
                 num_heads, num_kv_heads);
-  if (num_kv_heads > 65535) return fail(PKV_ERR_UNSUPPORTED, "too many kv heads");
   a->G = num_heads / num_kv_heads;
   if (a->G != 1 && a->G != 2 && a->G != 4 && a->G != 8)
     return fail(PKV_ERR_UNSUPPORTED, "heads per kv head must be 1, 2, 4 or 8 (got %d)", a->G);
@@ -672,9 +699,10 @@ int32_t prepare_decode(const void* query, const void* key_cache,
                 workspace ? workspace_bytes_given : size_t(0));
   if (need > 0 && !aligned16(workspace))
     return fail(PKV_ERR_INVALID, "workspace must be 16-byte aligned");
-  a->ws_acc = need ? static_cast<float*>(workspace) : nullptr;
-  a->ws_ml = need ? a->ws_acc + size_t(num_seqs) * num_heads * a->max_parts * head_dim
-                  : nullptr;
+  if (need > 0) {
+    a->ws_acc = static_cast<float*>(workspace);
+    a->ws_ml = a->ws_acc + size_t(num_seqs) * num_heads * a->max_parts * head_dim;
+  }
   a->log2_bs = 0;
   while ((1 << a->log2_bs) < block_size) ++a->log2_bs;
   return PKV_OK;
@@ -691,6 +719,65 @@ hipError_t launch_merge(const int32_t* lens, int B, int Hq, int log2_bs,
   return hipGetLastError();
 }
 
+// The partition kernel (with the fused append when key_new/value_new are
+// given), then -- when `merge` is set and some sequence can span two
+// partitions -- the log-sum-exp merge.  The merge is a launch of its own:
+// partitions of one sequence run on different XCDs, whose L2s are only
+// made coherent with each other at a kernel boundary (a device-scope fence
+// per workgroup writes back the whole L2 and costs more than the launch).
+int32_t run_decode(const void* query, const void* key_new, const void* value_new,
+                   const void* key_cache, const void* value_cache,
+                   const int32_t* block_tables, const int32_t* context_lens,
+                   int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                   int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                   int32_t num_blocks, int32_t max_context_len, float scale,
+                   int32_t partition_size, float* out, void* workspace,
+                   size_t workspace_bytes_given, int32_t dtype, void* stream, bool merge) {
+  DecodeArgs a;
+  int32_t st = prepare_decode(query, key_cache, value_cache, block_tables, context_lens,
+                              num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                              max_blocks_per_seq, num_blocks, max_context_len, scale,
+                              partition_size, out, workspace, workspace_bytes_given, dtype,
+                              true, &a);
+  if (st != PKV_OK) return st;
+  if (key_new || value_new) {
+    if (!key_new || !value_new) return fail(PKV_ERR_INVALID, "key and value must both be given");
+    if (!aligned16(key_new) || !aligned16(value_new))
+      return fail(PKV_ERR_INVALID, "key and value must be 16-byte aligned");
+  }
+  if (num_seqs == 0) return ok();
+  DecodeParams prm{};
+  prm.query = static_cast<const uint8_t*>(query);
+  prm.key_cache = static_cast<const uint8_t*>(key_cache);
+  prm.value_cache = static_cast<const uint8_t*>(value_cache);
+  prm.block_tables = block_tables;
+  prm.context_lens = context_lens;
+  prm.key_new = static_cast<const uint8_t*>(key_new);
+  prm.value_new = static_cast<const uint8_t*>(value_new);
+  prm.out = out;
+  prm.ws_acc = a.ws_acc;
+  prm.ws_ml = a.ws_ml;
+  prm.num_kv_heads = num_kv_heads;
+  prm.log2_bs = a.log2_bs;
+  prm.max_blocks = max_blocks_per_seq;
+  prm.num_blocks = num_blocks;
+  prm.max_ctx = max_context_len;
+  prm.part = a.part;
+  prm.max_parts = a.max_parts;
+  prm.scale_log2 = scale * kLog2e;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = dispatch_decode(dtype, head_dim, a.G, prm, num_seqs, s);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  if (!merge || a.max_parts <= 1) return ok();
+  e = head_dim == 64
+      ? launch_merge<64>(context_lens, num_seqs, num_heads, a.log2_bs, max_blocks_per_seq,
+                         max_context_len, a.part, a.max_parts, a.ws_acc, a.ws_ml, out, s)
+      : launch_merge<128>(context_lens, num_seqs, num_heads, a.log2_bs, max_blocks_per_seq,
+                          max_context_len, a.part, a.max_parts, a.ws_acc, a.ws_ml, out, s);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "decode merge launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 }  // namespace
 }  // namespace pkv
 
@@ -702,30 +789,10 @@ extern "C" int32_t pkv_paged_attention_decode_partials(
     int32_t num_blocks, int32_t max_context_len, float scale,
     int32_t partition_size, float* out, void* workspace,
     size_t workspace_bytes_given, int32_t dtype, void* stream) {
-  DecodeArgs a;
-  int32_t st = prepare_decode(query, key_cache, value_cache, block_tables, context_lens,
-                              num_seqs, num_heads, num_kv_heads, head_dim, block_size,
-                              max_blocks_per_seq, num_blocks, max_context_len, scale,
-                              partition_size, out, workspace, workspace_bytes_given, dtype,
-                              true, &a);
-  if (st != PKV_OK) return st;
-  if (num_seqs == 0) return ok();
-  const float sl2 = scale * kLog2e;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e;
-  switch (dtype) {
-    case PKV_BF16:
-      e = dispatch_dim<PKV_BF16>(head_dim, a.G, query, key_cache, value_cache, block_tables, context_lens, num_seqs, num_kv_heads, a.log2_bs, max_blocks_per_seq, num_blocks, max_context_len, a.part, a.max_parts, sl2, out, a.ws_acc, a.ws_ml, s);
-      break;
-    case PKV_F16:
-      e = dispatch_dim<PKV_F16>(head_dim, a.G, query, key_cache, value_cache, block_tables, context_lens, num_seqs, num_kv_heads, a.log2_bs, max_blocks_per_seq, num_blocks, max_context_len, a.part, a.max_parts, sl2, out, a.ws_acc, a.ws_ml, s);
-      break;
-    default:
-      e = dispatch_dim<PKV_F32>(head_dim, a.G, query, key_cache, value_cache, block_tables, context_lens, num_seqs, num_kv_heads, a.log2_bs, max_blocks_per_seq, num_blocks, max_context_len, a.part, a.max_parts, sl2, out, a.ws_acc, a.ws_ml, s);
-      break;
-  }
-  if (e != hipSuccess) return fail(PKV_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
-  return ok();
+  return run_decode(query, nullptr, nullptr, key_cache, value_cache, block_tables,
+                    context_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                    max_blocks_per_seq, num_blocks, max_context_len, scale, partition_size,
+                    out, workspace, workspace_bytes_given, dtype, stream, false);
 }
 
 extern "C" int32_t pkv_paged_attention_decode_merge(
@@ -759,13 +826,38 @@ extern "C" int32_t pkv_paged_attention_decode(
     int32_t num_blocks, int32_t max_context_len, float scale,
     int32_t partition_size, float* out, void* workspace,
     size_t workspace_bytes_given, int32_t dtype, void* stream) {
-  int32_t st = pkv_paged_attention_decode_partials(
-      query, key_cache, value_cache, block_tables, context_lens, num_seqs, num_heads,
-      num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, max_context_len,
-      scale, partition_size, out, workspace, workspace_bytes_given, dtype, stream);
-  if (st != PKV_OK) return st;
-  return pkv_paged_attention_decode_merge(context_lens, num_seqs, num_heads, num_kv_heads,
-                                          head_dim, block_size, max_blocks_per_seq,
-                                          max_context_len, partition_size, out, workspace,
-                                          workspace_bytes_given, stream);
+  return run_decode(query, nullptr, nullptr, key_cache, value_cache, block_tables,
+                    context_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                    max_blocks_per_seq, num_blocks, max_context_len, scale, partition_size,
+                    out, workspace, workspace_bytes_given, dtype, stream, true);
+}
+
+extern "C" int32_t pkv_paged_attention_decode_append(
+    const void* query, const void* key, const void* value, void* key_cache,
+    void* value_cache, const int32_t* block_tables, const int32_t* context_lens,
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+    int32_t max_context_len, float scale, int32_t partition_size, float* out,
+    void* workspace, size_t workspace_bytes_given, int32_t dtype, void* stream) {
+  if (num_seqs > 0 && (!key || !value))
+    return fail(PKV_ERR_INVALID, "NULL pointer argument");
+  return run_decode(query, key, value, key_cache, value_cache, block_tables, context_lens,
+                    num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                    max_blocks_per_seq, num_blocks, max_context_len, scale, partition_size,
+                    out, workspace, workspace_bytes_given, dtype, stream, true);
+}
+
+extern "C" int32_t pkv_paged_attention_decode_append_partials(
+    const void* query, const void* key, const void* value, void* key_cache,
+    void* value_cache, const int32_t* block_tables, const int32_t* context_lens,
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+    int32_t max_context_len, float scale, int32_t partition_size, float* out,
+    void* workspace, size_t workspace_bytes_given, int32_t dtype, void* stream) {
+  if (num_seqs > 0 && (!key || !value))
+    return fail(PKV_ERR_INVALID, "NULL pointer argument");
+  return run_decode(query, key, value, key_cache, value_cache, block_tables, context_lens,
+                    num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                    max_blocks_per_seq, num_blocks, max_context_len, scale, partition_size,
+                    out, workspace, workspace_bytes_given, dtype, stream, false);
 }

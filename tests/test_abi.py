@@ -63,10 +63,18 @@ def test_device_calls_reject_bad_arguments_before_launch():
     assert lib.pkv_paged_attention_decode_workspace_size(64, 32, 32, 128, 2000, 0,
                                                          ctypes.byref(ws)) == 0
     assert ws.value == 64 * 32 * 2 * (128 + 2) * 4
+    # GQA: partials per query head
+    assert lib.pkv_paged_attention_decode_workspace_size(256, 64, 8, 128, 8192, 512,
+                                                         ctypes.byref(ws)) == 0
+    assert ws.value == 256 * 64 * 16 * (128 + 2) * 4
     # decode: NULL pointers with otherwise valid sizes
     assert lib.pkv_paged_attention_decode(null, null, null, null, null, 2, 4, 4, 128, 16, 8, 64,
                                           100, 1.0, 0, null, null, 0, 2, null) == 1
     assert b"NULL" in lib.pkv_last_error()
+    # fused decode + append: NULL new rows with a non-empty batch
+    assert lib.pkv_paged_attention_decode_append(null, null, null, null, null, null, null, 2, 4, 4,
+                                                 128, 16, 8, 64, 100, 1.0, 0, null, null, 0, 2,
+                                                 null) == 1
     # empty batches are no-ops
     assert lib.pkv_paged_kv_append(null, null, null, null, null, 0, 1, 64, 16, 4, 2, null) == 0
     assert lib.pkv_paged_attention_decode(null, null, null, null, null, 0, 4, 4, 128, 16, 8, 64,
@@ -137,7 +145,7 @@ def test_hand_worked_trace_through_the_c_abi():
 
 
 ops = st.lists(
-    st.tuples(st.sampled_from(["add", "append", "fork", "free", "batch"]),
+    st.tuples(st.sampled_from(["add", "append", "fork", "free", "batch", "batch_tables"]),
               st.integers(0, 5), st.integers(0, 5), st.integers(0, 23)),
     min_size=1, max_size=80)
 
@@ -162,6 +170,25 @@ def test_native_allocator_matches_reference_bit_for_bit(seq_ops, block_size, num
                 elif op == "append":
                     slots, pairs = a.append(s, n)
                     return ("ok", list(slots), [tuple(p) for p in pairs])
+                elif op == "batch_tables":
+                    # append + the batch's tables in one call; max_blocks is
+                    # small enough to overflow now and then (all or nothing)
+                    batch = sorted({s, t})
+                    counts = [(n + 5 * i) % 9 for i in range(len(batch))]
+                    mb = 1 + n % 6
+                    if is_ref:
+                        for q in batch:
+                            a.length(q)  # KeyError for an unknown sequence
+                        if any(-(-(a.length(q) + c) // block_size) > mb
+                               for q, c in zip(batch, counts)):
+                            return ("too_small",)
+                        slots, pairs = a.append_batch(batch, counts)
+                        tables, lens = a.build_tables(batch, mb)
+                    else:
+                        slots, pairs, tables, lens = a.append_batch_tables(batch, counts, mb)
+                    return ("ok", list(slots), [tuple(p) for p in pairs],
+                            np.asarray(tables, dtype=np.int32).reshape(len(batch), mb).tolist(),
+                            [int(x) for x in lens])
                 else:
                     batch = sorted({s, t, (s + 2) % 6})
                     counts = [(n + 3 * i) % 7 for i in range(len(batch))]
@@ -170,6 +197,8 @@ def test_native_allocator_matches_reference_bit_for_bit(seq_ops, block_size, num
                 return ("ok",)
             except (RefOutOfBlocks, pkv.OutOfBlocks):
                 return ("out_of_blocks",)
+            except pkv.BufferTooSmall:
+                return ("too_small",)
             except (KeyError, pkv.NoSuchSequence):
                 return ("no_such_seq",)
             except (ValueError, pkv.SequenceExists, pkv.InvalidArgument):
@@ -200,3 +229,38 @@ def test_shared_prefix_workload_builds_identically():
     s_r, c_r = ref.append_batch(p.seqs, [w.chunk] * len(p.seqs))
     s_n, c_n = nat.append_batch(p.seqs, [w.chunk] * len(p.seqs))
     assert list(s_r) == s_n.tolist() and c_r == c_n
+
+
+def test_prepared_append_tables_repeats_the_call():
+    """The marshalled-once variant used by serving loops writes the same
+    slots, tables and lengths as the plain call, step after step, into the
+    arrays it was given."""
+    order = list(range(40))[::-1]
+    a = pkv.BlockAllocator(40, 4, order)
+    b = pkv.BlockAllocator(40, 4, order)
+    for x in (a, b):
+        for q in (7, 8):
+            x.add(q)
+        x.append(7, 5)
+        x.fork(7, 9)  # shares 7's partly filled last block: copy-on-write below
+    seqs, counts, mb = [7, 8, 9], [1, 2, 1], 8
+    slots = np.empty(4, dtype=np.int32)
+    tables = np.empty((3, mb), dtype=np.int32)
+    lens = np.empty(3, dtype=np.int32)
+    step = a.prepared_append_tables(seqs, counts, mb, slots, tables, lens)
+    for _ in range(6):
+        pairs = step()
+        s2, p2, t2, l2 = b.append_batch_tables(seqs, counts, mb)
+        assert pairs == p2
+        assert slots.tolist() == s2.tolist()
+        assert np.array_equal(tables, t2) and lens.tolist() == l2.tolist()
+    assert a.snapshot() == b.snapshot()
+    # a table would outgrow max_blocks: the failing call changes nothing
+    while True:
+        before = (a.snapshot(), [a.block_table(q) for q in seqs], [a.seq_len(q) for q in seqs])
+        try:
+            step()
+        except pkv.BufferTooSmall:
+            break
+    assert before == (a.snapshot(), [a.block_table(q) for q in seqs],
+                      [a.seq_len(q) for q in seqs])

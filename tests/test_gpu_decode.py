@@ -188,3 +188,182 @@ def test_full_size_sampled_against_oracle(name):
     log(name, "sampled max abs err", worst, "over", len(pick), "sequences")
     assert worst <= TOL[w.dtype]
     assert np.isfinite(got).all()
+
+
+# ---------------------------------------------------------------------------
+# one-call decode vs its two stages; decode with the append fused in
+# ---------------------------------------------------------------------------
+
+MULTI = {
+    "bf16_part64": (workloads.scaled(workloads.get("llama7b_bf16"), num_seqs=6, num_heads=4,
+                                     num_kv_heads=4, lens="uniform:1,900"), 64),
+    "gqa8_part128": (workloads.scaled(workloads.get("gqa_bf16"), num_seqs=5, num_heads=16,
+                                      num_kv_heads=2, lens="uniform:100,1500"), 128),
+    "fp32_d64_part256": (workloads.scaled(workloads.get("tiny_fp32"), num_seqs=5, num_blocks=0,
+                                          lens="uniform:1,1300"), 256),
+}
+
+
+@pytest.mark.parametrize("name", list(MULTI))
+def test_one_call_is_bitwise_its_two_stages(name):
+    w, part = MULTI[name]
+    log("case", name)
+    p = workloads.plan(w)
+    g = GpuState(w, p)
+    tables, lens, _, lh = g.tables()
+    q, _ = decode_queries(w, p.seqs)
+    q = q.to(DEV)
+    mc = int(lh.max())
+    one = pkv.paged_attention_decode(q, g.kc, g.vc, tables, lens, w.scale, mc, partition_size=part)
+    need = pkv.paged_attention_decode_workspace_size(len(p.seqs), w.num_heads, w.num_kv_heads,
+                                                     w.head_dim, mc, part)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    two = torch.empty_like(one)
+    pkv.paged_attention_decode_partials(q, g.kc, g.vc, tables, lens, w.scale, mc, part, two, ws)
+    pkv.paged_attention_decode_merge(lens, w.num_kv_heads, w.block_size, tables.shape[1], mc, part,
+                                     two, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(one, two)
+
+
+def test_workspace_contents_never_matter():
+    # garbage, a previous call's partials or a previous shape's partials
+    w, part = MULTI["bf16_part64"]
+    p = workloads.plan(w)
+    g = GpuState(w, p)
+    tables, lens, _, lh = g.tables()
+    q, _ = decode_queries(w, p.seqs)
+    q = q.to(DEV)
+    mc = int(lh.max())
+    ref = pkv.paged_attention_decode(q, g.kc, g.vc, tables, lens, w.scale, mc, partition_size=part)
+    need = pkv.paged_attention_decode_workspace_size(len(p.seqs), w.num_heads, w.num_kv_heads,
+                                                     w.head_dim, mc, part)
+    ws = torch.full((need + 4096,), 0xFF, dtype=torch.uint8, device=DEV)
+    for fill in (0xFF, 0x00, 0x5A):
+        ws.fill_(fill)
+        for _ in range(3):
+            got = pkv.paged_attention_decode(q, g.kc, g.vc, tables, lens, w.scale, mc,
+                                             partition_size=part, workspace=ws)
+            assert torch.equal(got, ref)
+    # a smaller batch through the same workspace, then the full one again
+    small = pkv.paged_attention_decode(q[:2].contiguous(), g.kc, g.vc, tables[:2].contiguous(),
+                                       lens[:2].contiguous(), w.scale, mc, partition_size=part,
+                                       workspace=ws)
+    assert torch.equal(small, ref[:2])
+    got = pkv.paged_attention_decode(q, g.kc, g.vc, tables, lens, w.scale, mc,
+                                     partition_size=part, workspace=ws)
+    assert torch.equal(got, ref)
+    # random garbage
+    ws.copy_(torch.randint(0, 256, ws.shape, dtype=torch.uint8, device=DEV))
+    got = pkv.paged_attention_decode(q, g.kc, g.vc, tables, lens, w.scale, mc,
+                                     partition_size=part, workspace=ws)
+    assert torch.equal(got, ref)
+
+
+APPEND = {
+    "bf16_auto": (workloads.scaled(workloads.get("llama7b_bf16"), num_seqs=7, num_heads=4,
+                                   num_kv_heads=4, lens="uniform:0,1500"), 0),
+    "bf16_part64": (MULTI["bf16_part64"][0], 64),
+    "gqa8_part128": (MULTI["gqa8_part128"][0], 128),
+    "fp16_bs32": (workloads.scaled(workloads.get("llama13b_fp16"), num_seqs=6, num_heads=2,
+                                   num_kv_heads=2, lens="uniform:0,700"), 0),
+    "fp32_d64_bs8": (workloads.scaled(workloads.get("tiny_fp32"), num_seqs=4, num_blocks=0,
+                                      block_size=8, lens="uniform:0,300"), 64),
+}
+
+
+@pytest.mark.parametrize("name", list(APPEND))
+def test_decode_append_is_append_then_decode(name):
+    """Fused append == pkv_paged_kv_append at the allocator's slots followed by
+    pkv_paged_attention_decode: pools and outputs bit for bit, and the
+    output within tolerance of the oracle after the oracle's append."""
+    w, part = APPEND[name]
+    log("case", name)
+    p = workloads.plan(w)
+    a = GpuState(w, p)
+    b = GpuState(w, p)
+    o = OracleState(w, p)
+    seqs = p.seqs
+    slots_a, pairs_a = a.alloc.append_batch(seqs, np.ones(len(seqs), dtype=np.int32))
+    slots_b, pairs_b = b.alloc.append_batch(seqs, np.ones(len(seqs), dtype=np.int32))
+    slots_o, pairs_o = o.alloc.append_batch(seqs, [1] * len(seqs))
+    assert not pairs_a and not pairs_b and not pairs_o
+    assert slots_a.tolist() == slots_b.tolist() == list(slots_o)
+    k, v = workloads.kv_rows(w, len(p.ops), len(seqs))  # [B, Hkv, D]
+    kt, vt = workloads.to_dtype(k, w.dtype), workloads.to_dtype(v, w.dtype)
+    q, q64 = decode_queries(w, seqs)
+    q = q.to(DEV)
+    # a: two calls
+    pkv.paged_kv_append(kt.to(DEV), vt.to(DEV), a.kc, a.vc, torch.from_numpy(slots_a).to(DEV))
+    ta, la, _, lh = a.tables()
+    mc = int(lh.max())
+    out_a = pkv.paged_attention_decode(q, a.kc, a.vc, ta, la, w.scale, mc, partition_size=part)
+    # b: one launch
+    tb, lb, _, _ = b.tables()
+    out_b = pkv.paged_attention_decode_append(q, kt.to(DEV), vt.to(DEV), b.kc, b.vc, tb, lb,
+                                              w.scale, mc, partition_size=part)
+    # c: the fused call's two stages
+    c = GpuState(w, p)
+    c.alloc.append_batch(seqs, np.ones(len(seqs), dtype=np.int32))
+    tc, lc, _, _ = c.tables()
+    need = pkv.paged_attention_decode_workspace_size(len(seqs), w.num_heads, w.num_kv_heads,
+                                                     w.head_dim, mc, part)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=DEV)
+    out_c = torch.empty_like(out_b)
+    pkv.paged_attention_decode_append_partials(q, kt.to(DEV), vt.to(DEV), c.kc, c.vc, tc, lc,
+                                               w.scale, mc, part, out_c, ws)
+    pkv.paged_attention_decode_merge(lc, w.num_kv_heads, w.block_size, tc.shape[1], mc, part,
+                                     out_c, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out_a, out_b) and torch.equal(out_b, out_c)
+    for x in (b, c):
+        assert torch.equal(a.kc.view(torch.uint8), x.kc.view(torch.uint8))
+        assert torch.equal(a.vc.view(torch.uint8), x.vc.view(torch.uint8))
+    # oracle
+    from oracle import kv_append as o_append
+    o_append(o.kc, o.vc, workloads.as_f64(kt), workloads.as_f64(vt), slots_o, w.block_size)
+    tables, lens = o.tables()
+    want = paged_decode(q64, o.kc, o.vc, tables, lens, w.scale, w.block_size)
+    err = max_abs_err(out_b.cpu().numpy(), want)
+    log(name, "max abs err", err)
+    assert err <= TOL[w.dtype]
+
+
+def test_launcher_is_the_plain_calls():
+    """DecodeLauncher (arguments marshalled once) launches exactly what
+    paged_attention_decode(_append) launch: bitwise equal outputs."""
+    w, part = APPEND["gqa8_part128"]
+    p = workloads.plan(w)
+    a, b = GpuState(w, p), GpuState(w, p)
+    seqs = p.seqs
+    for x in (a, b):
+        x.alloc.append_batch(seqs, np.ones(len(seqs), dtype=np.int32))
+    k, v = workloads.kv_rows(w, len(p.ops), len(seqs))
+    kt = workloads.to_dtype(k, w.dtype).to(DEV)
+    vt = workloads.to_dtype(v, w.dtype).to(DEV)
+    q, _ = decode_queries(w, seqs)
+    q = q.to(DEV)
+    ta, la, _, lh = a.tables()
+    tb, lb, _, _ = b.tables()
+    mc = int(lh.max())
+    want = pkv.paged_attention_decode_append(q, kt, vt, a.kc, a.vc, ta, la, w.scale, mc,
+                                             partition_size=part)
+    need = pkv.paged_attention_decode_workspace_size(len(seqs), w.num_heads, w.num_kv_heads,
+                                                     w.head_dim, mc + 50, part)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(want)
+    launch = pkv.DecodeLauncher(b.kc, b.vc, w.num_heads, len(seqs), tb.shape[1], mc + 50, part,
+                                out, ws)
+    launch.partials(q, tb, lb, mc, w.scale, kt, vt)
+    launch.merge(lb, mc)
+    torch.cuda.synchronize()
+    assert torch.equal(out, want)
+    assert torch.equal(a.kc.view(torch.uint8), b.kc.view(torch.uint8))
+    # a decode without the append through the same launcher
+    plain = pkv.paged_attention_decode(q, a.kc, a.vc, ta, la, w.scale, mc, partition_size=part)
+    launch.partials(q, tb, lb, mc, w.scale)
+    launch.merge(lb, mc)
+    torch.cuda.synchronize()
+    assert torch.equal(out, plain)
+    with pytest.raises(pkv.InvalidArgument):
+        launch.partials(q, tb, lb, mc + 51, w.scale)
