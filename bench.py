@@ -4,13 +4,15 @@
 A step is one decode step of one attention layer over the whole batch,
 through every stage of the path:
   1. host allocator: one new slot per sequence (batch append, all or
-     nothing; copy-on-write pairs if a shared block is hit), written with
-     the block tables and lengths into one pinned staging buffer;
-  2. tables and lengths to the device in one asynchronous copy;
+     nothing; copy-on-write pairs if a shared block is hit), reporting the
+     lengths and the block-table entries the appends set;
+  2. those go to the device by value, in the kernel arguments of the
+     decode launches (the block table itself stays on the device);
   3. block copies for copy-on-write pairs (none unless blocks are shared);
-  4. paged_attention_decode_append: the split-K decode kernel, which first
-     stores each sequence's new K/V row at its newest position (the slot
-     the allocator returned), then the log-sum-exp merge kernel.
+  4. paged_attention_decode_step: the split-K decode kernel, which applies
+     the table changes, stores each sequence's new K/V row at its newest
+     position (the slot the allocator returned) and attends, then the
+     log-sum-exp merge kernel.
 The cache is resident in HBM before timing starts.  ``value`` is the KV
 bytes the decode reads per step (sum over sequences of context_len * Hkv *
 head_dim * 2 * element size) divided by the wall time of a whole step.
@@ -117,50 +119,39 @@ def gpu_run(args, w, torch, pkv, workloads):
                                                          w.head_dim, max_len, part)
     workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
 
-    # Per step parity, a pinned staging buffer [tables b*mb | lens b | slots b];
-    # tables and lengths go to one device buffer with one copy on the
-    # kernels' stream (a copy on a stream of its own costs more: the
-    # cross-queue wait measured ~21 us per step against ~10 us in-stream).
-    # The slots stay on the host (the fused append derives them from the
-    # tables).
-    words = b * mb + 2 * b
-    head = b * mb + b
+    # The block table lives on the device across steps.  Each step's
+    # lengths and the table entries its appends set travel by value in the
+    # kernel arguments (pkv_paged_attention_decode_step): nothing is copied
+    # to the device on the step's path.  Host arrays are reused every step:
+    # their contents are copied into the launch when it is enqueued.
     stream = torch.cuda.current_stream(dev)
-    packed_d = torch.empty(head, dtype=torch.int32, device=dev)
-    tables_d, lens_d = packed_d[:b * mb].view(b, mb), packed_d[b * mb:]
-    slot = []
-    for _ in range(2):
-        buf = torch.empty(words, dtype=torch.int32, pin_memory=True)
-        arr = buf.numpy()
-        tables_h, lens_h, slots_h = arr[:b * mb].reshape(b, mb), arr[b * mb:head], arr[head:]
-        slot.append(dict(buf=buf, head=buf[:head], lens=lens_h, uploaded=torch.cuda.Event(),
-                         append=alloc.prepared_append_tables(seqs, np.ones(b, dtype=np.int32), mb,
-                                                             slots_h, tables_h, lens_h)))
-        slot[-1]["uploaded"].record(stream)
+    th, _ = alloc.build_block_tables(seqs, mb)
+    tables_d = torch.from_numpy(th.copy()).to(dev)
+    slots_h = np.empty(b, dtype=np.int32)
+    lens_h = np.empty(b, dtype=np.int32)
+    changes_h = np.empty((b + 1, 3), dtype=np.int32)
+    append = alloc.prepared_append_changes(seqs, np.ones(b, dtype=np.int32), slots_h, lens_h,
+                                           changes_h)
     launch = pkv.DecodeLauncher(kc, vc, w.num_heads, b, mb, max_len, part, out, workspace)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(total_steps)]
     step_bytes = np.zeros(total_steps, dtype=np.float64)
 
     def step(i):
-        st = slot[i % 2]
-        st["uploaded"].synchronize()        # its upload two steps ago has finished
-        pairs = st["append"]()                                               # 1
-        packed_d.copy_(st["head"], non_blocking=True)                        # 2
-        st["uploaded"].record(stream)
+        pairs, n_changes = append()                                          # 1, 2
         if pairs:                                                            # 3
             src = torch.tensor([a for a, _ in pairs], dtype=torch.int32).to(dev)
             dst = torch.tensor([c for _, c in pairs], dtype=torch.int32).to(dev)
             pkv.copy_blocks(kc, vc, src, dst)
-        lens = st["lens"]
-        mc = int(lens.max())
+        mc = int(lens_h.max())
         e0, e1, e2 = ev[i]
         e0.record(stream)
-        launch.partials(q[i], tables_d, lens_d, mc, w.scale, k_new[i], v_new[i])  # 4
+        launch.step_partials(q[i], tables_d, lens_h, changes_h, n_changes, mc, w.scale,  # 4
+                             k_new[i], v_new[i])
         e1.record(stream)
-        launch.merge(lens_d, mc)
+        launch.step_merge(lens_h, mc)
         e2.record(stream)
-        step_bytes[i] = kv_bytes(w, lens)
+        step_bytes[i] = kv_bytes(w, lens_h)
 
     for i in range(args.warmup):
         step(i)

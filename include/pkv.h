@@ -160,6 +160,22 @@ int32_t pkv_append_batch_tables(pkv_allocator* alloc, const int64_t* seqs,
                                 int32_t max_blocks, int32_t* block_tables,
                                 int32_t* context_lens);
 
+/* pkv_append_batch, reporting instead of full tables the block-table
+ * entries the batch sets -- each a triple (row of the batch, logical block
+ * index, physical block): a fresh block, or the copy-on-write replacement
+ * of a sequence's last entry -- and the batch's lengths after the append.
+ * This is the per-step metadata the step decode calls take.
+ *   context_lens [num_seqs] host int32 (out)
+ *   changes      [changes_cap][3] host int32 (out), *n_changes triples;
+ *                the capacity is checked before any state changes */
+int32_t pkv_append_batch_changes(pkv_allocator* alloc, const int64_t* seqs,
+                                 const int32_t* counts, int32_t num_seqs,
+                                 int32_t* slots_out, int64_t slots_cap,
+                                 int32_t* cow_src, int32_t* cow_dst,
+                                 int32_t cow_cap, int32_t* n_cow,
+                                 int32_t* context_lens, int32_t* changes,
+                                 int32_t changes_cap, int32_t* n_changes);
+
 /* Queries (host outputs). */
 int32_t pkv_seq_len(const pkv_allocator* alloc, int64_t seq, int32_t* len);
 /* Copies the table into out[cap]; *n = its length (checked against cap). */
@@ -307,6 +323,50 @@ int32_t pkv_paged_attention_decode_append_partials(
     int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
     int32_t max_context_len, float scale, int32_t partition_size, float* out,
     void* workspace, size_t workspace_bytes, int32_t dtype, void* stream);
+
+/* One decode step with its per-step metadata passed by value in the
+ * kernel arguments, so nothing is copied to the device on the step's
+ * critical path (a serving loop's decode step).  Equivalent to: apply the
+ * table changes to block_tables, then pkv_paged_attention_decode_append
+ * (or pkv_paged_attention_decode when key and value are NULL) with these
+ * lengths.
+ *   block_tables   device [num_seqs][max_blocks_per_seq], kept by the
+ *                  caller across steps and updated in place: the kernels
+ *                  apply `changes` while reading it and store them
+ *   context_lens   HOST [num_seqs] int32, lengths including the new token
+ *   changes        HOST [num_changes][3] int32 (row, logical block index,
+ *                  physical block): the entries this step's appends set,
+ *                  as reported by pkv_append_batch_changes
+ *   key, value     [num_seqs][num_kv_heads][head_dim] new rows, or both
+ *                  NULL for no append
+ * Limits (kernel-argument space): num_seqs <= 256, num_changes <= 256
+ * (PKV_ERR_UNSUPPORTED beyond).  Other arguments, semantics and errors as
+ * pkv_paged_attention_decode_append. */
+int32_t pkv_paged_attention_decode_step(
+    const void* query, const void* key, const void* value, void* key_cache,
+    void* value_cache, int32_t* block_tables, const int32_t* context_lens,
+    const int32_t* changes, int32_t num_changes, int32_t num_seqs,
+    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+    int32_t max_context_len, float scale, int32_t partition_size, float* out,
+    void* workspace, size_t workspace_bytes, int32_t dtype, void* stream);
+
+/* The two stages of pkv_paged_attention_decode_step (same arguments; the
+ * merge needs only the host lengths). */
+int32_t pkv_paged_attention_decode_step_partials(
+    const void* query, const void* key, const void* value, void* key_cache,
+    void* value_cache, int32_t* block_tables, const int32_t* context_lens,
+    const int32_t* changes, int32_t num_changes, int32_t num_seqs,
+    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+    int32_t max_context_len, float scale, int32_t partition_size, float* out,
+    void* workspace, size_t workspace_bytes, int32_t dtype, void* stream);
+int32_t pkv_paged_attention_decode_step_merge(
+    const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t max_blocks_per_seq, int32_t max_context_len,
+    int32_t partition_size, float* out, void* workspace,
+    size_t workspace_bytes, void* stream);
 
 /* pkv_paged_attention_decode as two launches, for callers that schedule or
  * time the stages separately (same arguments, same semantics, same

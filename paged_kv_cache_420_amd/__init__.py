@@ -25,7 +25,7 @@ __all__ = [
     "BlockAllocator", "DecodeLauncher", "paged_kv_append", "copy_blocks",
     "paged_attention_decode_workspace_size", "paged_attention_decode_partition_size",
     "paged_attention_decode", "paged_attention_decode_append",
-    "paged_attention_decode_append_partials",
+    "paged_attention_decode_append_partials", "paged_attention_decode_step",
     "paged_attention_decode_partials", "paged_attention_decode_merge",
     "paged_attention_prefill", "library_path", "version",
 ]
@@ -86,6 +86,17 @@ _SIGNATURES = {
     "pkv_append_batch": (_I32, [_P, _P, _P, _I32, _P, _I64, _P, _P, _I32, _P]),
     "pkv_append_batch_tables": (_I32, [_P, _P, _P, _I32, _P, _I64, _P, _P, _I32, _P,
                                        _I32, _P, _P]),
+    "pkv_append_batch_changes": (_I32, [_P, _P, _P, _I32, _P, _I64, _P, _P, _I32, _P, _P, _P, _I32,
+                                        _P]),
+    "pkv_paged_attention_decode_step": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32,
+                                               _I32, _I32, _I32, _I32, _I32, ctypes.c_float, _I32,
+                                               _P, _P, ctypes.c_size_t, _I32, _P]),
+    "pkv_paged_attention_decode_step_partials": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32,
+                                                        _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                                                        ctypes.c_float, _I32, _P, _P,
+                                                        ctypes.c_size_t, _I32, _P]),
+    "pkv_paged_attention_decode_step_merge": (_I32, [_P, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                                                     _I32, _P, _P, ctypes.c_size_t, _P]),
     "pkv_seq_len": (_I32, [_P, _I64, _P]),
     "pkv_seq_block_table": (_I32, [_P, _I64, _P, _I32, _P]),
     "pkv_num_free_blocks": (_I32, [_P, _P]),
@@ -290,6 +301,60 @@ class BlockAllocator:
             return list(zip(src[:k].tolist(), dst[:k].tolist())) if k else []
         return call
 
+    def append_batch_changes(self, seqs, counts):
+        """append_batch, reporting the table entries it set and the lengths
+        (pkv_append_batch_changes).  Returns (slots, cow pairs, lens [B],
+        changes [n, 3] int32 rows of (batch row, logical block, block))."""
+        seqs = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64))
+        counts = np.ascontiguousarray(np.asarray(counts, dtype=np.int32))
+        b = len(seqs)
+        if counts.shape != seqs.shape:
+            raise InvalidArgument("seqs and counts differ in length")
+        total = int(counts.sum(dtype=np.int64))
+        cap = int(np.sum(-(-counts.astype(np.int64) // self.block_size))) + b + 1
+        slots = np.empty(max(total, 1), dtype=np.int32)
+        lens = np.empty(max(b, 1), dtype=np.int32)
+        changes = np.empty((cap, 3), dtype=np.int32)
+        src = np.empty(max(b, 1), dtype=np.int32)
+        dst = np.empty(max(b, 1), dtype=np.int32)
+        ncow, nch = _I32(), _I32()
+        _check(_lib.pkv_append_batch_changes(
+            self._h, seqs.ctypes.data, counts.ctypes.data, b, slots.ctypes.data, total,
+            src.ctypes.data, dst.ctypes.data, b, ctypes.byref(ncow), lens.ctypes.data,
+            changes.ctypes.data, cap, ctypes.byref(nch)))
+        pairs = list(zip(src[:ncow.value].tolist(), dst[:ncow.value].tolist()))
+        return slots[:total], pairs, lens[:b], changes[:nch.value]
+
+    def prepared_append_changes(self, seqs, counts, slots_out, lens_out, changes_out):
+        """append_batch_changes with every argument marshalled once, into
+        the given contiguous int32 arrays (changes_out [cap, 3]).  Returns a
+        function that makes the call and returns (cow pairs, number of
+        changes)."""
+        seqs = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64))
+        counts = np.ascontiguousarray(np.asarray(counts, dtype=np.int32))
+        b = len(seqs)
+        total = int(counts.sum(dtype=np.int64))
+        for arr, nd in ((slots_out, 1), (lens_out, 1), (changes_out, 2)):
+            if arr.dtype != np.int32 or arr.ndim != nd or not arr.flags.c_contiguous:
+                raise InvalidArgument("outputs must be contiguous int32 arrays")
+        if slots_out.shape[0] < total or lens_out.shape[0] < b or changes_out.shape[1] != 3:
+            raise InvalidArgument("output arrays too small")
+        src = np.empty(max(b, 1), dtype=np.int32)
+        dst = np.empty(max(b, 1), dtype=np.int32)
+        ncow, nch = _I32(), _I32()
+        keep = (seqs, counts, slots_out, lens_out, changes_out, src, dst, ncow, nch)
+        args = (self._h, seqs.ctypes.data, counts.ctypes.data, b, slots_out.ctypes.data, total,
+                src.ctypes.data, dst.ctypes.data, b, ctypes.byref(ncow), lens_out.ctypes.data,
+                changes_out.ctypes.data, changes_out.shape[0], ctypes.byref(nch))
+        fn = _lib.pkv_append_batch_changes
+
+        def call(_keep=keep):
+            _check(fn(*args))
+            k = ncow.value
+            pairs = list(zip(src[:k].tolist(), dst[:k].tolist())) if k else []
+            return pairs, nch.value
+        return call
+
     def seq_len(self, seq):
         out = _I32()
         _check(_lib.pkv_seq_len(self._h, seq, ctypes.byref(out)))
@@ -434,10 +499,13 @@ def _decode_args(query, key_cache, value_cache, block_tables, context_lens, max_
     nb, hkv, bs, d = _cache_dims(key_cache, value_cache)
     _dev(query, "query", dtype=key_cache.dtype, ndim=3)
     _dev(block_tables, "block_tables", dtype=torch.int32, ndim=2)
-    _dev(context_lens, "context_lens", dtype=torch.int32, ndim=1)
     b, hq, dq = query.shape
-    if dq != d or block_tables.shape[0] != b or context_lens.shape[0] != b:
-        raise InvalidArgument("query, block_tables and context_lens disagree on shape")
+    if context_lens is not None:  # None: host lengths, checked by the caller
+        _dev(context_lens, "context_lens", dtype=torch.int32, ndim=1)
+        if context_lens.shape[0] != b:
+            raise InvalidArgument("query and context_lens disagree on shape")
+    if dq != d or block_tables.shape[0] != b:
+        raise InvalidArgument("query and block_tables disagree on shape")
     if out is None:
         out = torch.empty((b, hq, d), dtype=torch.float32, device=query.device)
     _dev(out, "out", dtype=torch.float32, ndim=3)
@@ -580,6 +648,34 @@ class DecodeLauncher:
                 int(max_context_len), float(scale), self.part, self._out, self._ws[0],
                 self._ws[1], self._code, self._stream))
 
+    def step_partials(self, query, block_tables, lens, changes, num_changes, max_context_len,
+                      scale, key=None, value=None):
+        """First stage of pkv_paged_attention_decode_step: host lengths
+        ``lens`` and table changes ``changes[:num_changes]`` (contiguous
+        int32 numpy arrays) go by value in the kernel arguments."""
+        if max_context_len > self._max_ctx:
+            raise InvalidArgument("max_context_len above the launcher's bound")
+        q = self._check_step(query, self._q_shape, self._dtype, "query")
+        t = self._check_step(block_tables, self._t_shape, torch.int32, "block_tables")
+        b, hq, hkv, d, bs, mb, nb = self._dims
+        k = v = None
+        if key is not None:
+            k = self._check_step(key, self._kv_shape, self._dtype, "key")
+            v = self._check_step(value, self._kv_shape, self._dtype, "value")
+        _check(_lib.pkv_paged_attention_decode_step_partials(
+            q, k, v, self._kc, self._vc, t, lens.ctypes.data, changes.ctypes.data,
+            int(num_changes), b, hq, hkv, d, bs, mb, nb, int(max_context_len), float(scale),
+            self.part, self._out, self._ws[0], self._ws[1], self._code, self._stream))
+
+    def step_merge(self, lens, max_context_len):
+        """Second stage of pkv_paged_attention_decode_step (host lengths)."""
+        if max_context_len > self._max_ctx:
+            raise InvalidArgument("max_context_len above the launcher's bound")
+        b, hq, hkv, d, bs, mb, nb = self._dims
+        _check(_lib.pkv_paged_attention_decode_step_merge(
+            lens.ctypes.data, b, hq, hkv, d, bs, mb, int(max_context_len), self.part, self._out,
+            self._ws[0], self._ws[1], self._stream))
+
     def merge(self, context_lens, max_context_len):
         if max_context_len > self._max_ctx:
             raise InvalidArgument("max_context_len above the launcher's bound")
@@ -588,6 +684,39 @@ class DecodeLauncher:
         _check(_lib.pkv_paged_attention_decode_merge(
             l_, b, hq, hkv, d, bs, mb, int(max_context_len), self.part, self._out, self._ws[0],
             self._ws[1], self._stream))
+
+
+def paged_attention_decode_step(query, key, value, key_cache, value_cache, block_tables,
+                                context_lens, changes, scale, max_context_len, partition_size=0,
+                                out=None, workspace=None):
+    """Decode step with host metadata by value (pkv_paged_attention_decode_step).
+
+    block_tables: device int32 [B, max_blocks], updated in place with
+    ``changes``; context_lens: host int32 [B] (numpy); changes: host int32
+    [n, 3] (batch row, logical block, block), e.g. from
+    BlockAllocator.append_batch_changes; key/value: new rows [B, Hkv, D] or
+    None.  Returns out [B, Hq, D] float32."""
+    (nb, hkv, bs, d, b, hq), out, workspace, ws_ptr, ws_bytes = _decode_args(
+        query, key_cache, value_cache, block_tables, None, max_context_len, partition_size, out,
+        workspace)
+    lens = np.ascontiguousarray(np.asarray(context_lens, dtype=np.int32))
+    changes = np.ascontiguousarray(np.asarray(changes, dtype=np.int32).reshape(-1, 3))
+    if lens.shape != (b,):
+        raise InvalidArgument("context_lens must hold one length per sequence")
+    kp = vp = None
+    if key is not None or value is not None:
+        _dev(key, "key", dtype=key_cache.dtype, ndim=3)
+        _dev(value, "value", dtype=key_cache.dtype, ndim=3)
+        if tuple(key.shape) != (b, hkv, d) or value.shape != key.shape:
+            raise InvalidArgument("key/value must be [B, num_kv_heads, head_dim]")
+        kp, vp = key.data_ptr(), value.data_ptr()
+    _check(_lib.pkv_paged_attention_decode_step(
+        query.data_ptr(), kp, vp, key_cache.data_ptr(), value_cache.data_ptr(),
+        block_tables.data_ptr(), lens.ctypes.data, changes.ctypes.data, changes.shape[0], b, hq,
+        hkv, d, bs, block_tables.shape[1], nb, int(max_context_len), float(scale),
+        int(partition_size), out.data_ptr(), ws_ptr, ws_bytes, _dtype_code(key_cache),
+        _stream(query)))
+    return out
 
 
 def paged_attention_decode_partials(query, key_cache, value_cache, block_tables, context_lens,

@@ -74,7 +74,8 @@ int64_t BlockAllocator::blocks_needed(const Seq& s, int32_t n,
 }
 
 void BlockAllocator::grow(Seq& s, int32_t n, int32_t* slots,
-                          std::vector<CowPair>* cow) {
+                          std::vector<CowPair>* cow,
+                          std::vector<TableChange>* changes, int32_t row) {
   bool do_cow = false;
   if (n > 0 && s.len % block_size_ != 0) do_cow = ref_[s.table.back()] > 1;
   if (do_cow) {
@@ -83,10 +84,17 @@ void BlockAllocator::grow(Seq& s, int32_t n, int32_t* slots,
     --ref_[old];
     s.table.back() = fresh;
     cow->push_back({old, fresh});
+    if (changes)
+      changes->push_back({row, static_cast<int32_t>(s.table.size()) - 1, fresh});
   }
   for (int32_t i = 0; i < n; ++i) {
     int32_t p = s.len + i;
-    if (p % block_size_ == 0) s.table.push_back(pop());
+    if (p % block_size_ == 0) {
+      s.table.push_back(pop());
+      if (changes)
+        changes->push_back(
+            {row, static_cast<int32_t>(s.table.size()) - 1, s.table.back()});
+    }
     slots[i] = s.table[p / block_size_] * block_size_ + p % block_size_;
   }
   s.len += n;
@@ -115,7 +123,9 @@ int32_t BlockAllocator::append_batch(const int64_t* seqs,
                                      int32_t* slots, int64_t slots_cap,
                                      CowPair* cow, int32_t cow_cap,
                                      int32_t* n_cow, int32_t max_blocks,
-                                     int32_t* tables, int32_t* lens) {
+                                     int32_t* tables, int32_t* lens,
+                                     TableChange* changes, int32_t changes_cap,
+                                     int32_t* n_changes) {
   if (num_seqs < 0) return fail(PKV_ERR_INVALID, "negative batch size");
   // One lookup per sequence; scratch reused across calls (one decode step
   // of a large batch should cost microseconds, not allocations).
@@ -178,17 +188,29 @@ int32_t BlockAllocator::append_batch(const int64_t* seqs,
   if (cows > cow_cap)
     return fail(PKV_ERR_BUFFER_TOO_SMALL, "cow buffer holds %d, need %d",
                 cow_cap, cows);
+  if (changes && need > changes_cap)
+    return fail(PKV_ERR_BUFFER_TOO_SMALL, "changes buffer holds %d, need %lld",
+                changes_cap, static_cast<long long>(need));
   if (need > num_free())
     return fail(PKV_ERR_OUT_OF_BLOCKS, "batch needs %lld blocks, %d free",
                 static_cast<long long>(need), num_free());
-  std::vector<CowPair> pairs;
+  thread_local std::vector<CowPair> pairs;
+  thread_local std::vector<TableChange> set;
+  pairs.clear();
+  set.clear();
   int64_t off = 0;
   for (int32_t i = 0; i < num_seqs; ++i) {
-    grow(*ptr[i], counts[i], slots + off, &pairs);
+    grow(*ptr[i], counts[i], slots + off, &pairs, changes ? &set : nullptr, i);
     off += counts[i];
   }
   for (size_t k = 0; k < pairs.size(); ++k) cow[k] = pairs[k];
   *n_cow = static_cast<int32_t>(pairs.size());
+  if (changes) {
+    for (size_t k = 0; k < set.size(); ++k) changes[k] = set[k];
+    *n_changes = static_cast<int32_t>(set.size());
+    if (lens)
+      for (int32_t i = 0; i < num_seqs; ++i) lens[i] = ptr[i]->len;
+  }
   if (tables) {
     for (int32_t i = 0; i < num_seqs; ++i) {
       const Seq& s = *ptr[i];

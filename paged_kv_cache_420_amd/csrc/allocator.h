@@ -21,6 +21,15 @@ struct CowPair {
   int32_t dst;
 };
 
+// One block-table entry an append set: row of the batch, logical block
+// index, physical block (a fresh block, or the copy-on-write replacement of
+// the last entry).
+struct TableChange {
+  int32_t row;
+  int32_t index;
+  int32_t block;
+};
+
 class BlockAllocator {
  public:
   // `order` lists every block once; order[0] is handed out first.
@@ -52,11 +61,14 @@ class BlockAllocator {
   // With `tables` (and `lens`), the batch's updated block tables are then
   // written as rows of max_blocks entries (-1 past each table's end) and
   // its lengths; a table longer than max_blocks fails up front.
+  // With `changes`, every table entry the batch sets is reported instead
+  // (capacity changes_cap, checked up front), plus the lengths in `lens`.
   int32_t append_batch(const int64_t* seqs, const int32_t* counts,
                        int32_t num_seqs, int32_t* slots, int64_t slots_cap,
                        CowPair* cow, int32_t cow_cap, int32_t* n_cow,
                        int32_t max_blocks = 0, int32_t* tables = nullptr,
-                       int32_t* lens = nullptr);
+                       int32_t* lens = nullptr, TableChange* changes = nullptr,
+                       int32_t changes_cap = 0, int32_t* n_changes = nullptr);
 
  private:
   struct Seq {
@@ -67,7 +79,8 @@ class BlockAllocator {
   // of its last block; sets *cow when a copy-on-write happens first.
   int64_t blocks_needed(const Seq& s, int32_t n, int32_t last_ref,
                         bool* cow) const;
-  void grow(Seq& s, int32_t n, int32_t* slots, std::vector<CowPair>* cow);
+  void grow(Seq& s, int32_t n, int32_t* slots, std::vector<CowPair>* cow,
+            std::vector<TableChange>* changes = nullptr, int32_t row = 0);
   int32_t pop();
 
   int32_t num_blocks_;

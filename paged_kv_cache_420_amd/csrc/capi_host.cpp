@@ -170,6 +170,36 @@ int32_t pkv_append_batch_tables(pkv_allocator* alloc, const int64_t* seqs,
   return PKV_OK;
 }
 
+int32_t pkv_append_batch_changes(pkv_allocator* alloc, const int64_t* seqs,
+                                 const int32_t* counts, int32_t num_seqs,
+                                 int32_t* slots_out, int64_t slots_cap,
+                                 int32_t* cow_src, int32_t* cow_dst,
+                                 int32_t cow_cap, int32_t* n_cow,
+                                 int32_t* context_lens, int32_t* changes,
+                                 int32_t changes_cap, int32_t* n_changes) {
+  PKV_REQUIRE(alloc, "allocator is NULL");
+  PKV_REQUIRE(num_seqs == 0 || (seqs && counts && context_lens), "NULL argument");
+  PKV_REQUIRE(slots_cap == 0 || slots_out, "slots_out is NULL");
+  PKV_REQUIRE(cow_cap == 0 || (cow_src && cow_dst), "cow outputs are NULL");
+  PKV_REQUIRE(n_cow && n_changes, "count outputs are NULL");
+  PKV_REQUIRE(changes_cap == 0 || changes, "changes is NULL");
+  PKV_REQUIRE(cow_cap >= 0 && slots_cap >= 0 && changes_cap >= 0, "negative capacity");
+  thread_local std::vector<pkv::CowPair> pairs;
+  pairs.resize(cow_cap > 0 ? cow_cap : 0);
+  static_assert(sizeof(pkv::TableChange) == 3 * sizeof(int32_t), "packed triples");
+  int32_t got = 0;
+  int32_t st = alloc->impl.append_batch(
+      seqs, counts, num_seqs, slots_out, slots_cap, pairs.data(), cow_cap, &got, 0, nullptr,
+      context_lens, reinterpret_cast<pkv::TableChange*>(changes), changes_cap, n_changes);
+  if (st != PKV_OK) return st;
+  for (int32_t i = 0; i < got; ++i) {
+    cow_src[i] = pairs[i].src;
+    cow_dst[i] = pairs[i].dst;
+  }
+  *n_cow = got;
+  return PKV_OK;
+}
+
 int32_t pkv_seq_len(const pkv_allocator* alloc, int64_t seq, int32_t* len) {
   PKV_REQUIRE(alloc && len, "NULL argument");
   if (!alloc->impl.has(seq))

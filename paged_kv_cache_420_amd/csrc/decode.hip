@@ -232,6 +232,7 @@ struct DecodeParams {
   const uint8_t* key_cache;    // [NB][Hkv][BS][D]
   const uint8_t* value_cache;
   const int32_t* block_tables; // [B][max_blocks]
+  int32_t* block_tables_rw;    // the same array, written by step launches
   const int32_t* context_lens; // [B]
   const uint8_t* key_new;      // [B][Hkv][D] or null: fused append
   const uint8_t* value_new;
@@ -242,9 +243,34 @@ struct DecodeParams {
   float scale_log2;
 };
 
+// Where a launch gets each sequence's length and which table entries it
+// must see changed.  DeviceMeta: lengths from the device array, tables as
+// they are in device memory.  StepMeta: per-step metadata passed by value
+// in the kernel arguments (no host-to-device copy on the step's critical
+// path) -- the lengths, and the table entries this step's appends set,
+// which the kernels apply while staging block ids and persist to the
+// device table for later launches.
+constexpr int kStepMaxSeqs = 256;
+constexpr int kStepMaxChanges = 256;
+
+struct DeviceMeta {
+  static constexpr bool kHost = false;
+  __device__ int len(const DecodeParams& prm, int b) const { return prm.context_lens[b]; }
+};
+
+struct StepMeta {
+  static constexpr bool kHost = true;
+  int32_t lens[kStepMaxSeqs];
+  int32_t change_key[kStepMaxChanges];    // logical block index << 8 | row
+  int32_t change_block[kStepMaxChanges];  // physical block
+  int32_t num_changes;
+  __device__ int len(const DecodeParams&, int b) const { return lens[b]; }
+};
+
 // Dynamic LDS: [scores: max(part*G, kWaves*G*D) floats][block ids][m/l].
-template <int DT, int D, int G, int U>
-__global__ __launch_bounds__(kThreads) void decode_partition_kernel(const DecodeParams prm) {
+template <int DT, int D, int G, int U, class Meta>
+__global__ __launch_bounds__(kThreads) void decode_partition_kernel(const DecodeParams prm,
+                                                                    const Meta meta) {
   using C = Cfg<DT, D, G, U>;
   using E = Elem<DT>;
   extern __shared__ float smem[];
@@ -268,7 +294,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(const Decode
   const int bs = 1 << log2_bs;
   const int num_heads = num_kv_heads * G;
 
-  const int n = prm.context_lens[b];
+  const int n = meta.len(prm, b);
   const bool bad_len =
       n < 0 || n > prm.max_ctx || int64_t(n) > int64_t(max_blocks) * bs;
   const int nparts = bad_len ? 1 : max(1, cdiv(n, part));
@@ -290,15 +316,31 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(const Decode
   const int ntok = min(part, n - p0);
   const int nblk = (ntok + bs - 1) >> log2_bs;
   const int32_t* table = prm.block_tables + int64_t(b) * max_blocks + (p0 >> log2_bs);
+  for (int i = tid; i < nblk; i += kThreads) s_blk[i] = table[i];
+  if constexpr (Meta::kHost) {
+    // this step's table changes for this sequence and partition: staged,
+    // and persisted once (by the kv-head-0 workgroup of the partition)
+    __syncthreads();
+    const int j0 = p0 >> log2_bs;
+    for (int t = tid; t < meta.num_changes; t += kThreads) {
+      const int key = meta.change_key[t];
+      const int j = (key >> 8) - j0;
+      if ((key & 255) == b && j >= 0 && j < nblk) {
+        s_blk[j] = meta.change_block[t];
+        if (kvh == 0) prm.block_tables_rw[int64_t(b) * max_blocks + j0 + j] = meta.change_block[t];
+      }
+    }
+  }
+  __syncthreads();
   bool bad_blk = false;
   for (int i = tid; i < nblk; i += kThreads) {
-    int id = table[i];
+    const int id = s_blk[i];
     if (id < 0 || id >= num_blocks) {
       bad_blk = true;
-      id = 0;
+      s_blk[i] = 0;
     }
-    s_blk[i] = id;
   }
+  bad_blk = __syncthreads_or(bad_blk);
 
   const int64_t tile_bytes = int64_t(bs) * C::kRow;           // one (block, head) tile
   const int64_t blk_stride = tile_bytes * num_kv_heads;
@@ -306,15 +348,15 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(const Decode
   // Fused append: the partition holding the newest position n - 1 stores
   // this step's K/V row for its kv head there before reading the cache
   // (the same bytes a separate slot-mapped append would write).  Only this
-  // workgroup reads those two rows in this launch, and the barrier below
-  // orders its stores before its own loads (workgroup scope: the stores
-  // reach this XCD's L2, the loads miss the L1, which starts every launch
-  // empty).  No device-scope fence is needed -- on this GPU one writes back
-  // the XCD's whole L2.
+  // workgroup reads those two rows in this launch, and the barrier orders
+  // its stores before its own loads (workgroup scope: the stores reach this
+  // XCD's L2, the loads miss the L1, which starts every launch empty).  No
+  // device-scope fence is needed -- on this GPU one writes back the XCD's
+  // whole L2.
   if (prm.key_new != nullptr && p_idx == nparts - 1) {
     const int pos = n - 1 - p0;  // within the partition
-    int id = table[pos >> log2_bs];
-    if (id >= 0 && id < num_blocks && tid < 2 * C::kLpt) {
+    if (tid < 2 * C::kLpt && !bad_blk) {
+      const int id = s_blk[pos >> log2_bs];
       const bool is_v = tid >= C::kLpt;
       const int piece = tid - (is_v ? C::kLpt : 0);
       const int64_t src = (int64_t(b) * num_kv_heads + kvh) * C::kRow + piece * 16;
@@ -324,8 +366,8 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(const Decode
       uint8_t* to = const_cast<uint8_t*>(is_v ? prm.value_cache : prm.key_cache);
       *reinterpret_cast<uint4*>(to + dst) = *reinterpret_cast<const uint4*>(from + src);
     }
+    __syncthreads();
   }
-  bad_blk = __syncthreads_or(bad_blk);
 
   // q slices of the G heads: lane covers bytes (lane % LPT) * 16 of the row.
   const int dl = lane % C::kLpt;
@@ -493,15 +535,17 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(const Decode
 // Merge the partitions of one (sequence, head): with per-partition max m_p
 // (log2 units), sum l_p and unnormalised acc_p,
 //   out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p,  M = max_p m_p.
-template <int D>
+template <int D, class Meta>
 __global__ __launch_bounds__(64) void decode_reduce_kernel(
-    const int32_t* __restrict__ context_lens, int32_t num_heads,
-    int32_t log2_bs, int32_t max_blocks, int32_t max_ctx, int32_t part,
-    int32_t max_parts, const float* __restrict__ ws_acc,
-    const float* __restrict__ ws_ml, float* __restrict__ out) {
+    const DecodeParams prm, const Meta meta, int32_t num_heads) {
+  const int32_t log2_bs = prm.log2_bs, max_blocks = prm.max_blocks, max_ctx = prm.max_ctx;
+  const int32_t part = prm.part, max_parts = prm.max_parts;
+  const float* __restrict__ ws_acc = prm.ws_acc;
+  const float* __restrict__ ws_ml = prm.ws_ml;
+  float* __restrict__ out = prm.out;
   const int h = blockIdx.x;
   const int b = blockIdx.y;
-  const int n = context_lens[b];
+  const int n = meta.len(prm, b);
   const bool bad_len = n < 0 || n > max_ctx ||
                        int64_t(n) > (int64_t(max_blocks) << log2_bs);
   if (bad_len) return;
@@ -560,40 +604,55 @@ int32_t resolve_partition(int32_t partition_size, int32_t block_size,
   return PKV_OK;
 }
 
-template <int DT, int D, int G>
-hipError_t launch_decode(const DecodeParams& prm, int B, hipStream_t stream) {
+template <int DT, int D, int G, class Meta>
+hipError_t launch_decode(const DecodeParams& prm, const Meta& meta, int B, hipStream_t stream) {
   const int score_floats = std::max(prm.part * G, kWaves * G * D);
   const size_t lds = size_t(score_floats) * 4 + size_t(prm.part >> 3) * 4 +
                      size_t(2 * kWaves * G) * 4;
-  hipLaunchKernelGGL((decode_partition_kernel<DT, D, G, kUnitsPerChunk>),
-                     dim3(prm.num_kv_heads, B, prm.max_parts), dim3(kThreads), lds, stream, prm);
+  hipLaunchKernelGGL((decode_partition_kernel<DT, D, G, kUnitsPerChunk, Meta>),
+                     dim3(prm.num_kv_heads, B, prm.max_parts), dim3(kThreads), lds, stream, prm,
+                     meta);
   return hipGetLastError();
 }
 
-template <int DT, int D>
-hipError_t dispatch_group(int G, const DecodeParams& prm, int B, hipStream_t s) {
+template <int DT, int D, class Meta>
+hipError_t dispatch_group(int G, const DecodeParams& prm, const Meta& meta, int B,
+                          hipStream_t s) {
   switch (G) {
-    case 1: return launch_decode<DT, D, 1>(prm, B, s);
-    case 2: return launch_decode<DT, D, 2>(prm, B, s);
-    case 4: return launch_decode<DT, D, 4>(prm, B, s);
-    case 8: return launch_decode<DT, D, 8>(prm, B, s);
+    case 1: return launch_decode<DT, D, 1>(prm, meta, B, s);
+    case 2: return launch_decode<DT, D, 2>(prm, meta, B, s);
+    case 4: return launch_decode<DT, D, 4>(prm, meta, B, s);
+    case 8: return launch_decode<DT, D, 8>(prm, meta, B, s);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t dispatch_decode(int32_t dtype, int D, int G, const DecodeParams& prm, int B,
-                           hipStream_t s) {
+template <class Meta>
+hipError_t dispatch_decode(int32_t dtype, int D, int G, const DecodeParams& prm,
+                           const Meta& meta, int B, hipStream_t s) {
   switch (dtype) {
     case PKV_BF16:
-      return D == 64 ? dispatch_group<PKV_BF16, 64>(G, prm, B, s)
-                     : dispatch_group<PKV_BF16, 128>(G, prm, B, s);
+      return D == 64 ? dispatch_group<PKV_BF16, 64>(G, prm, meta, B, s)
+                     : dispatch_group<PKV_BF16, 128>(G, prm, meta, B, s);
     case PKV_F16:
-      return D == 64 ? dispatch_group<PKV_F16, 64>(G, prm, B, s)
-                     : dispatch_group<PKV_F16, 128>(G, prm, B, s);
+      return D == 64 ? dispatch_group<PKV_F16, 64>(G, prm, meta, B, s)
+                     : dispatch_group<PKV_F16, 128>(G, prm, meta, B, s);
     default:
-      return D == 64 ? dispatch_group<PKV_F32, 64>(G, prm, B, s)
-                     : dispatch_group<PKV_F32, 128>(G, prm, B, s);
+      return D == 64 ? dispatch_group<PKV_F32, 64>(G, prm, meta, B, s)
+                     : dispatch_group<PKV_F32, 128>(G, prm, meta, B, s);
   }
+}
+
+template <class Meta>
+hipError_t launch_merge(const DecodeParams& prm, const Meta& meta, int B, int Hq, int D,
+                        hipStream_t s) {
+  if (D == 64)
+    hipLaunchKernelGGL((decode_reduce_kernel<64, Meta>), dim3(Hq, B), dim3(64), 0, s, prm, meta,
+                       Hq);
+  else
+    hipLaunchKernelGGL((decode_reduce_kernel<128, Meta>), dim3(Hq, B), dim3(64), 0, s, prm,
+                       meta, Hq);
+  return hipGetLastError();
 }
 
 // Workspace (only when some sequence may span two partitions):
@@ -708,23 +767,14 @@ int32_t prepare_decode(const void* query, const void* key_cache,
   return PKV_OK;
 }
 
-template <int D>
-hipError_t launch_merge(const int32_t* lens, int B, int Hq, int log2_bs,
-                        int max_blocks, int max_ctx, int part, int max_parts,
-                        const float* ws_acc, const float* ws_ml, float* out,
-                        hipStream_t s) {
-  hipLaunchKernelGGL((decode_reduce_kernel<D>), dim3(Hq, B), dim3(64), 0, s, lens,
-                     Hq, log2_bs, max_blocks, max_ctx, part, max_parts, ws_acc,
-                     ws_ml, out);
-  return hipGetLastError();
-}
-
 // The partition kernel (with the fused append when key_new/value_new are
 // given), then -- when `merge` is set and some sequence can span two
 // partitions -- the log-sum-exp merge.  The merge is a launch of its own:
 // partitions of one sequence run on different XCDs, whose L2s are only
 // made coherent with each other at a kernel boundary (a device-scope fence
 // per workgroup writes back the whole L2 and costs more than the launch).
+// `step` (may be null): lengths and table changes by value, for the step
+// calls; context_lens is then unused.
 int32_t run_decode(const void* query, const void* key_new, const void* value_new,
                    const void* key_cache, const void* value_cache,
                    const int32_t* block_tables, const int32_t* context_lens,
@@ -732,13 +782,15 @@ int32_t run_decode(const void* query, const void* key_new, const void* value_new
                    int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
                    int32_t num_blocks, int32_t max_context_len, float scale,
                    int32_t partition_size, float* out, void* workspace,
-                   size_t workspace_bytes_given, int32_t dtype, void* stream, bool merge) {
+                   size_t workspace_bytes_given, int32_t dtype, void* stream, bool partials,
+                   bool merge, const StepMeta* step) {
   DecodeArgs a;
-  int32_t st = prepare_decode(query, key_cache, value_cache, block_tables, context_lens,
+  const int32_t* lens_check = step ? reinterpret_cast<const int32_t*>(step->lens) : context_lens;
+  int32_t st = prepare_decode(query, key_cache, value_cache, block_tables, lens_check,
                               num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                               max_blocks_per_seq, num_blocks, max_context_len, scale,
                               partition_size, out, workspace, workspace_bytes_given, dtype,
-                              true, &a);
+                              partials, &a);
   if (st != PKV_OK) return st;
   if (key_new || value_new) {
     if (!key_new || !value_new) return fail(PKV_ERR_INVALID, "key and value must both be given");
@@ -751,6 +803,7 @@ int32_t run_decode(const void* query, const void* key_new, const void* value_new
   prm.key_cache = static_cast<const uint8_t*>(key_cache);
   prm.value_cache = static_cast<const uint8_t*>(value_cache);
   prm.block_tables = block_tables;
+  prm.block_tables_rw = const_cast<int32_t*>(block_tables);
   prm.context_lens = context_lens;
   prm.key_new = static_cast<const uint8_t*>(key_new);
   prm.value_new = static_cast<const uint8_t*>(value_new);
@@ -766,16 +819,42 @@ int32_t run_decode(const void* query, const void* key_new, const void* value_new
   prm.max_parts = a.max_parts;
   prm.scale_log2 = scale * kLog2e;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = dispatch_decode(dtype, head_dim, a.G, prm, num_seqs, s);
-  if (e != hipSuccess) return fail(PKV_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  hipError_t e = hipSuccess;
+  if (partials) {
+    e = step ? dispatch_decode(dtype, head_dim, a.G, prm, *step, num_seqs, s)
+             : dispatch_decode(dtype, head_dim, a.G, prm, DeviceMeta{}, num_seqs, s);
+    if (e != hipSuccess) return fail(PKV_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  }
   if (!merge || a.max_parts <= 1) return ok();
-  e = head_dim == 64
-      ? launch_merge<64>(context_lens, num_seqs, num_heads, a.log2_bs, max_blocks_per_seq,
-                         max_context_len, a.part, a.max_parts, a.ws_acc, a.ws_ml, out, s)
-      : launch_merge<128>(context_lens, num_seqs, num_heads, a.log2_bs, max_blocks_per_seq,
-                          max_context_len, a.part, a.max_parts, a.ws_acc, a.ws_ml, out, s);
+  e = step ? launch_merge(prm, *step, num_seqs, num_heads, head_dim, s)
+           : launch_merge(prm, DeviceMeta{}, num_seqs, num_heads, head_dim, s);
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "decode merge launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+// Packs a step's host metadata (checked against the kernel-argument limits).
+int32_t pack_step(const int32_t* context_lens, const int32_t* changes, int32_t num_changes,
+                  int32_t num_seqs, int32_t max_blocks_per_seq, StepMeta* m) {
+  if (num_seqs > kStepMaxSeqs)
+    return fail(PKV_ERR_UNSUPPORTED, "step calls take at most %d sequences (got %d)",
+                kStepMaxSeqs, num_seqs);
+  if (num_changes < 0 || num_changes > kStepMaxChanges)
+    return fail(PKV_ERR_UNSUPPORTED, "step calls take at most %d table changes (got %d)",
+                kStepMaxChanges, num_changes);
+  if (num_seqs > 0 && !context_lens) return fail(PKV_ERR_INVALID, "context_lens is NULL");
+  if (num_changes > 0 && !changes) return fail(PKV_ERR_INVALID, "changes is NULL");
+  for (int32_t i = 0; i < num_seqs; ++i) m->lens[i] = context_lens[i];
+  for (int32_t i = 0; i < num_changes; ++i) {
+    const int32_t row = changes[3 * i], idx = changes[3 * i + 1];
+    if (row < 0 || row >= num_seqs || idx < 0 || idx >= max_blocks_per_seq ||
+        idx >= (1 << 23))
+      return fail(PKV_ERR_INVALID, "table change %d (row %d, index %d) out of range", i, row,
+                  idx);
+    m->change_key[i] = (idx << 8) | row;
+    m->change_block[i] = changes[3 * i + 2];
+  }
+  m->num_changes = num_changes;
+  return PKV_OK;
 }
 
 }  // namespace
@@ -792,7 +871,7 @@ extern "C" int32_t pkv_paged_attention_decode_partials(
   return run_decode(query, nullptr, nullptr, key_cache, value_cache, block_tables,
                     context_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                     max_blocks_per_seq, num_blocks, max_context_len, scale, partition_size,
-                    out, workspace, workspace_bytes_given, dtype, stream, false);
+                    out, workspace, workspace_bytes_given, dtype, stream, true, false, nullptr);
 }
 
 extern "C" int32_t pkv_paged_attention_decode_merge(
@@ -801,21 +880,10 @@ extern "C" int32_t pkv_paged_attention_decode_merge(
     int32_t max_blocks_per_seq, int32_t max_context_len,
     int32_t partition_size, float* out, void* workspace,
     size_t workspace_bytes_given, void* stream) {
-  DecodeArgs a;
-  int32_t st = prepare_decode(nullptr, nullptr, nullptr, nullptr, context_lens, num_seqs,
-                              num_heads, num_kv_heads, head_dim, block_size,
-                              max_blocks_per_seq, 1, max_context_len, 1.0f, partition_size,
-                              out, workspace, workspace_bytes_given, PKV_F32, false, &a);
-  if (st != PKV_OK) return st;
-  if (num_seqs == 0 || a.max_parts <= 1) return ok();
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = head_dim == 64
-      ? launch_merge<64>(context_lens, num_seqs, num_heads, a.log2_bs, max_blocks_per_seq,
-                         max_context_len, a.part, a.max_parts, a.ws_acc, a.ws_ml, out, s)
-      : launch_merge<128>(context_lens, num_seqs, num_heads, a.log2_bs, max_blocks_per_seq,
-                          max_context_len, a.part, a.max_parts, a.ws_acc, a.ws_ml, out, s);
-  if (e != hipSuccess) return fail(PKV_ERR_HIP, "decode merge launch: %s", hipGetErrorString(e));
-  return ok();
+  return run_decode(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, context_lens, num_seqs,
+                    num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, 1,
+                    max_context_len, 1.0f, partition_size, out, workspace,
+                    workspace_bytes_given, PKV_F32, stream, false, true, nullptr);
 }
 
 extern "C" int32_t pkv_paged_attention_decode(
@@ -829,7 +897,7 @@ extern "C" int32_t pkv_paged_attention_decode(
   return run_decode(query, nullptr, nullptr, key_cache, value_cache, block_tables,
                     context_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                     max_blocks_per_seq, num_blocks, max_context_len, scale, partition_size,
-                    out, workspace, workspace_bytes_given, dtype, stream, true);
+                    out, workspace, workspace_bytes_given, dtype, stream, true, true, nullptr);
 }
 
 extern "C" int32_t pkv_paged_attention_decode_append(
@@ -844,7 +912,7 @@ extern "C" int32_t pkv_paged_attention_decode_append(
   return run_decode(query, key, value, key_cache, value_cache, block_tables, context_lens,
                     num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                     max_blocks_per_seq, num_blocks, max_context_len, scale, partition_size,
-                    out, workspace, workspace_bytes_given, dtype, stream, true);
+                    out, workspace, workspace_bytes_given, dtype, stream, true, true, nullptr);
 }
 
 extern "C" int32_t pkv_paged_attention_decode_append_partials(
@@ -859,5 +927,66 @@ extern "C" int32_t pkv_paged_attention_decode_append_partials(
   return run_decode(query, key, value, key_cache, value_cache, block_tables, context_lens,
                     num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                     max_blocks_per_seq, num_blocks, max_context_len, scale, partition_size,
-                    out, workspace, workspace_bytes_given, dtype, stream, false);
+                    out, workspace, workspace_bytes_given, dtype, stream, true, false, nullptr);
+}
+
+namespace {
+int32_t step_call(const void* query, const void* key, const void* value, void* key_cache,
+                  void* value_cache, int32_t* block_tables, const int32_t* context_lens,
+                  const int32_t* changes, int32_t num_changes, int32_t num_seqs,
+                  int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                  int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+                  int32_t max_context_len, float scale, int32_t partition_size, float* out,
+                  void* workspace, size_t workspace_bytes_given, int32_t dtype, void* stream,
+                  bool partials, bool merge) {
+  StepMeta m;
+  int32_t st = pack_step(context_lens, changes, num_changes, num_seqs, max_blocks_per_seq, &m);
+  if (st != PKV_OK) return st;
+  return run_decode(query, key, value, key_cache, value_cache, block_tables, nullptr, num_seqs,
+                    num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                    num_blocks, max_context_len, scale, partition_size, out, workspace,
+                    workspace_bytes_given, dtype, stream, partials, merge, &m);
+}
+}  // namespace
+
+extern "C" int32_t pkv_paged_attention_decode_step(
+    const void* query, const void* key, const void* value, void* key_cache,
+    void* value_cache, int32_t* block_tables, const int32_t* context_lens,
+    const int32_t* changes, int32_t num_changes, int32_t num_seqs, int32_t num_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+    int32_t num_blocks, int32_t max_context_len, float scale, int32_t partition_size,
+    float* out, void* workspace, size_t workspace_bytes_given, int32_t dtype, void* stream) {
+  return step_call(query, key, value, key_cache, value_cache, block_tables, context_lens,
+                   changes, num_changes, num_seqs, num_heads, num_kv_heads, head_dim,
+                   block_size, max_blocks_per_seq, num_blocks, max_context_len, scale,
+                   partition_size, out, workspace, workspace_bytes_given, dtype, stream, true,
+                   true);
+}
+
+extern "C" int32_t pkv_paged_attention_decode_step_partials(
+    const void* query, const void* key, const void* value, void* key_cache,
+    void* value_cache, int32_t* block_tables, const int32_t* context_lens,
+    const int32_t* changes, int32_t num_changes, int32_t num_seqs, int32_t num_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+    int32_t num_blocks, int32_t max_context_len, float scale, int32_t partition_size,
+    float* out, void* workspace, size_t workspace_bytes_given, int32_t dtype, void* stream) {
+  return step_call(query, key, value, key_cache, value_cache, block_tables, context_lens,
+                   changes, num_changes, num_seqs, num_heads, num_kv_heads, head_dim,
+                   block_size, max_blocks_per_seq, num_blocks, max_context_len, scale,
+                   partition_size, out, workspace, workspace_bytes_given, dtype, stream, true,
+                   false);
+}
+
+extern "C" int32_t pkv_paged_attention_decode_step_merge(
+    const int32_t* context_lens, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq, int32_t max_context_len,
+    int32_t partition_size, float* out, void* workspace, size_t workspace_bytes_given,
+    void* stream) {
+  StepMeta m;
+  int32_t st = pack_step(context_lens, nullptr, 0, num_seqs, max_blocks_per_seq, &m);
+  if (st != PKV_OK) return st;
+  return run_decode(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, num_seqs,
+                    num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, 1,
+                    max_context_len, 1.0f, partition_size, out, workspace,
+                    workspace_bytes_given, PKV_F32, stream, false, true, &m);
 }

@@ -104,6 +104,18 @@ def test_allocator_reports_errors():
         a.build_block_tables([5], 0) if a.append(5, 1) else None
 
 
+def _live(a):
+    """Sequence ids the native allocator holds (ids 0..5 in the op tests)."""
+    out = set()
+    for q in range(6):
+        try:
+            a.seq_len(q)
+            out.add(q)
+        except pkv.NoSuchSequence:
+            pass
+    return out
+
+
 def _state(a, seqs):
     if isinstance(a, RefAllocator):
         free, ref, tables = a.snapshot()
@@ -145,7 +157,8 @@ def test_hand_worked_trace_through_the_c_abi():
 
 
 ops = st.lists(
-    st.tuples(st.sampled_from(["add", "append", "fork", "free", "batch", "batch_tables"]),
+    st.tuples(st.sampled_from(["add", "append", "fork", "free", "batch", "batch_tables",
+                               "batch_changes"]),
               st.integers(0, 5), st.integers(0, 5), st.integers(0, 23)),
     min_size=1, max_size=80)
 
@@ -170,6 +183,26 @@ def test_native_allocator_matches_reference_bit_for_bit(seq_ops, block_size, num
                 elif op == "append":
                     slots, pairs = a.append(s, n)
                     return ("ok", list(slots), [tuple(p) for p in pairs])
+                elif op == "batch_changes":
+                    # the reported entries turn the old tables into the new ones
+                    batch = sorted({s, t, (s + 3) % 6})
+                    counts = [(n + 2 * i) % 8 for i in range(len(batch))]
+                    if is_ref:
+                        slots, pairs = a.append_batch(batch, counts)
+                        lens = [a.length(q) for q in batch]
+                        tables = [a.table(q) for q in batch]
+                    else:
+                        before = [a.block_table(q) if q in _live(a) else None for q in batch]
+                        slots, pairs, lens, changes = a.append_batch_changes(batch, counts)
+                        tables = [list(tb) for tb in before]
+                        for row, idx, blk in changes.tolist():
+                            if idx == len(tables[row]):
+                                tables[row].append(blk)
+                            else:
+                                tables[row][idx] = blk
+                        assert tables == [a.block_table(q) for q in batch]
+                    return ("ok", list(slots), [tuple(p) for p in pairs], [int(x) for x in lens],
+                            [list(tb) for tb in tables])
                 elif op == "batch_tables":
                     # append + the batch's tables in one call; max_blocks is
                     # small enough to overflow now and then (all or nothing)

@@ -367,3 +367,75 @@ def test_launcher_is_the_plain_calls():
     assert torch.equal(out, plain)
     with pytest.raises(pkv.InvalidArgument):
         launch.partials(q, tb, lb, mc + 51, w.scale)
+
+
+STEP = {
+    # 40-token prefix forked into every sequence: not block aligned, so the
+    # first append of a sequence with no suffix yet copies the shared last
+    # block during the steps (a table change that replaces an entry); 20
+    # steps cross block boundaries
+    "bf16_shared_cow": workloads.scaled(workloads.get("shared_prefix_bf16"), num_seqs=6,
+                                        num_heads=4, num_kv_heads=4, prefix=40,
+                                        lens="fixed:0,0,5,100,0,37", chunk=0),
+    "gqa8_fp16_bs32": workloads.scaled(workloads.get("llama13b_fp16"), num_seqs=5, num_heads=16,
+                                       num_kv_heads=2, lens="uniform:0,900"),
+}
+
+
+@pytest.mark.parametrize("name", list(STEP))
+def test_step_call_is_full_upload_decode(name):
+    """pkv_paged_attention_decode_step (lengths and table changes by value,
+    a device table kept across steps) == pkv_paged_attention_decode_append
+    with freshly uploaded tables, bit for bit: outputs, caches and, at the
+    end, the device table itself."""
+    w = STEP[name]
+    log("case", name)
+    p = workloads.plan(w)
+    a, b = GpuState(w, p), GpuState(w, p)
+    seqs = p.seqs
+    steps, part = 20, 64
+    mb = max(len(a.alloc.block_table(s)) for s in seqs) + steps // w.block_size + 2
+    th, _ = b.alloc.build_block_tables(seqs, mb)
+    dev_tables = torch.from_numpy(th.copy()).to(DEV)   # b's table, kept on the device
+    ones = np.ones(len(seqs), dtype=np.int32)
+    for i in range(steps):
+        k, v = workloads.kv_rows(w, len(p.ops) + i, len(seqs))
+        kt = workloads.to_dtype(k, w.dtype).to(DEV)
+        vt = workloads.to_dtype(v, w.dtype).to(DEV)
+        q = workloads.to_dtype(workloads.normal([w.seed, 9, i], (len(seqs), w.num_heads,
+                                                                  w.head_dim), w.std),
+                               w.dtype).to(DEV)
+        _, pa = a.alloc.append_batch(seqs, ones)
+        _, pb, lens, changes = b.alloc.append_batch_changes(seqs, ones)
+        assert pa == pb
+        for x, pairs in ((a, pa), (b, pb)):
+            if pairs:
+                x._copy(pairs)
+        ta, la, _, lh = a.tables(seqs)
+        ta = torch.nn.functional.pad(ta, (0, mb - ta.shape[1]), value=-1).contiguous()
+        mc = int(lh.max())
+        want = pkv.paged_attention_decode_append(q, kt, vt, a.kc, a.vc, ta, la, w.scale, mc,
+                                                 partition_size=part)
+        got = pkv.paged_attention_decode_step(q, kt, vt, b.kc, b.vc, dev_tables, lens, changes,
+                                              w.scale, mc, partition_size=part)
+        torch.cuda.synchronize()
+        assert lens.tolist() == lh.tolist()
+        assert torch.equal(got, want), f"step {i}"
+    assert torch.equal(a.kc.view(torch.uint8), b.kc.view(torch.uint8))
+    assert torch.equal(a.vc.view(torch.uint8), b.vc.view(torch.uint8))
+    th, _ = b.alloc.build_block_tables(seqs, mb)
+    assert np.array_equal(dev_tables.cpu().numpy(), th)
+
+
+def test_step_call_limits():
+    w = STEP["bf16_shared_cow"]
+    kc = torch.zeros((8, 4, 16, 128), dtype=torch.bfloat16, device=DEV)
+    q = torch.zeros((300, 4, 128), dtype=torch.bfloat16, device=DEV)
+    t = torch.zeros((300, 2), dtype=torch.int32, device=DEV)
+    lens = np.ones(300, dtype=np.int32)
+    with pytest.raises(pkv.Unsupported):
+        pkv.paged_attention_decode_step(q, None, None, kc, kc, t, lens, np.zeros((0, 3)),
+                                        w.scale, 1)
+    with pytest.raises(pkv.InvalidArgument):  # change row outside the batch
+        pkv.paged_attention_decode_step(q[:2].contiguous(), None, None, kc, kc, t[:2].contiguous(),
+                                        lens[:2], np.array([[5, 0, 1]]), w.scale, 1)
