@@ -323,7 +323,6 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
             if (16 * kt + r > lim[qg]) s[qg][kt][r] = -INFINITY;
     }
 
-    uint32_t phi[2][2][4], plo[2][2][4];  // [qg][step][word]
     float mts[2];
     bool grow = false;
 #pragma unroll
@@ -352,48 +351,40 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
         for (int dt = 0; dt < kD / 16; ++dt) o[qg][dt] *= alpha;
       }
     }
-#pragma unroll
-    for (int qg = 0; qg < 2; ++qg) {
-      const float nm = -m_run[qg];
-      float x[16];
-      float sum = 0.f;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          x[4 * kt + r] = __builtin_amdgcn_exp2f(fmaf(s[qg][kt][r], sl2, nm));
-      if (diag) {  // masked weights are exactly 0, whatever the scale
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (16 * kt + r > lim[qg]) x[4 * kt + r] = 0.f;
-      }
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sum += x[e];
-      l_run[qg] += sum;
-      // B operand of step st: element e = 4 t + r is key 32 st + 16 t + 4 grp + r,
-      // i.e. S^T slice kt = 2 st + t, register r.
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const int e0 = 2 * w;
-          H::split2(x[4 * (2 * st + (e0 >> 2)) + (e0 & 3)],
-                    x[4 * (2 * st + (e0 >> 2)) + (e0 & 3) + 1], phi[qg][st][w], plo[qg][st][w]);
-        }
-    }
-
+    // P and O^T += V^T P^T one 32-key step at a time: the exp and split of
+    // step 1 (VALU) then issue while step 0's MFMAs execute, and step 1's
+    // MFMAs overlap the next tile's LDS stores; V^T operands stay shared
+    // by both row groups.
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
+      uint32_t phi[2][4], plo[2][4];  // [qg][word]
+#pragma unroll
+      for (int qg = 0; qg < 2; ++qg) {
+        const float nm = -m_run[qg];
+        float x[8];  // element e = 4 t + r: key 32 st + 16 t + 4 grp + r (slice 2 st + t)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          x[e] = __builtin_amdgcn_exp2f(fmaf(s[qg][2 * st + (e >> 2)][e & 3], sl2, nm));
+        if (diag) {  // masked weights are exactly 0, whatever the scale
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (16 * (2 * st + (e >> 2)) + (e & 3) > lim[qg]) x[e] = 0.f;
+        }
+        float sum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sum += x[e];
+        l_run[qg] += sum;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) H::split2(x[2 * w], x[2 * w + 1], phi[qg][w], plo[qg][w]);
+      }
 #pragma unroll
       for (int dt = 0; dt < kD / 16; ++dt) {
         const u32x4 a = *reinterpret_cast<const u32x4*>(
             svt + (16 * dt + col) * kVtRow + 64 * st + 16 * grp);
 #pragma unroll
         for (int qg = 0; qg < 2; ++qg) {
-          const u32x4 bh = {phi[qg][st][0], phi[qg][st][1], phi[qg][st][2], phi[qg][st][3]};
-          const u32x4 bl = {plo[qg][st][0], plo[qg][st][1], plo[qg][st][2], plo[qg][st][3]};
+          const u32x4 bh = {phi[qg][0], phi[qg][1], phi[qg][2], phi[qg][3]};
+          const u32x4 bl = {plo[qg][0], plo[qg][1], plo[qg][2], plo[qg][3]};
           o[qg][dt] = H::mma(a, bh, o[qg][dt]);
           o[qg][dt] = H::mma(a, bl, o[qg][dt]);
         }
