@@ -16,6 +16,9 @@ through every stage of the path:
 The cache is resident in HBM before timing starts.  ``value`` is the KV
 bytes the decode reads per step (sum over sequences of context_len * Hkv *
 head_dim * 2 * element size) divided by the wall time of a whole step.
+With a shared prefix those logical bytes exceed what HBM delivers (the
+prefix is read once per sequence but served from the caches); the roofline
+then uses the unique bytes (prefix counted once).
 ``roofline`` reports the decode partition kernel alone, timed with HIP
 events on the stream it runs on; its ``traffic`` comes from the committed
 rocprofv3
@@ -63,11 +66,23 @@ def parse():
                     help="skip the chunked-prefill leg of the shared-prefix workload")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time pkv_copy_blocks over a known byte count and exit")
+    ap.add_argument("--block-size-sweep", action="store_true",
+                    help="decode GB/s and slot utilisation at block sizes 8..256, shuffled vs "
+                         "identity (contiguous) block placement; one JSON line each")
     return ap.parse_args()
 
 
 def kv_bytes(w, lens):
     return int(np.sum(lens, dtype=np.int64)) * w.num_kv_heads * w.head_dim * 2 * w.elem_bytes
+
+
+def kv_bytes_unique(w, lens):
+    """KV bytes with a shared prefix counted once (what a step must fetch
+    from HBM at least); equal to kv_bytes when nothing is shared."""
+    if not w.prefix:
+        return kv_bytes(w, lens)
+    tokens = int(np.sum(np.asarray(lens, dtype=np.int64) - w.prefix)) + w.prefix
+    return tokens * w.num_kv_heads * w.head_dim * 2 * w.elem_bytes
 
 
 def setup(w, pkv, workloads, torch, dev):
@@ -136,6 +151,7 @@ def gpu_run(args, w, torch, pkv, workloads):
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(total_steps)]
     step_bytes = np.zeros(total_steps, dtype=np.float64)
+    step_unique = np.zeros(total_steps, dtype=np.float64)
 
     def step(i):
         pairs, n_changes = append()                                          # 1, 2
@@ -152,6 +168,7 @@ def gpu_run(args, w, torch, pkv, workloads):
         launch.step_merge(lens_h, mc)
         e2.record(stream)
         step_bytes[i] = kv_bytes(w, lens_h)
+        step_unique[i] = kv_bytes_unique(w, lens_h)
 
     for i in range(args.warmup):
         step(i)
@@ -167,6 +184,7 @@ def gpu_run(args, w, torch, pkv, workloads):
     if not torch.isfinite(out).all():
         raise RuntimeError("decode produced non-finite output")
     res = dict(wall=wall, kernel_ms=kernel_ms, merge_ms=merge_ms, bytes=step_bytes[args.warmup:],
+               unique_bytes=step_unique[args.warmup:],
                batch=b, part=part)
     if w.chunk and not args.no_prefill:
         res["prefill"] = prefill_run(w, p, alloc, kc, vc, torch, pkv, dev)
@@ -254,6 +272,75 @@ def copy_calibration(torch, pkv):
           flush=True)
 
 
+def block_size_sweep(args, torch, pkv, workloads):
+    """Paging overhead and the pages' block-size advice (blocks of 16-32
+    tokens recommended; large blocks waste memory): the headline batch at
+    each block size, with its blocks either scattered by the seeded
+    permutation or placed in order (each sequence's blocks contiguous -- the
+    layout of a contiguous per-request cache).  Reports decode GB/s (mean
+    of 20 timed calls after 5, HIP events around partials + merge) and slot
+    utilisation = cached tokens / allocated slots, next to a reservation of
+    the longest context for every sequence."""
+    import dataclasses
+    dev = torch.device("cuda:0")
+    base = workloads.get("llama7b_bf16")
+    reserve = int(base.lens.split(",")[-1])  # the longest request the length law allows
+    for bs in (8, 16, 32, 64, 128, 256):
+        w = workloads.scaled(base, block_size=bs)
+        for layout in ("shuffled", "identity"):
+            p = workloads.plan(w)
+            if layout == "identity":
+                p = dataclasses.replace(p, free_order=np.arange(p.num_blocks, dtype=np.int32))
+            shape = (p.num_blocks, w.num_kv_heads, bs, w.head_dim)
+            kc = torch.zeros(shape, dtype=w.dtype, device=dev)
+            vc = torch.zeros(shape, dtype=w.dtype, device=dev)
+            alloc = pkv.BlockAllocator(p.num_blocks, bs, p.free_order)
+            gen = torch.Generator(device=dev)
+            gen.manual_seed(w.seed)
+
+            def on_append(i, seq, n, slots):
+                kv = (torch.randn((2, n, w.num_kv_heads, w.head_dim), generator=gen, device=dev)
+                      ).to(w.dtype)
+                pkv.paged_kv_append(kv[0], kv[1], kc, vc, torch.from_numpy(slots).to(dev))
+
+            workloads.run_schedule(p.ops, alloc, on_append)
+            seqs = np.asarray(p.seqs, dtype=np.int64)
+            mb = max(len(alloc.block_table(int(s))) for s in seqs)
+            th, lh = alloc.build_block_tables(seqs, mb)
+            tables = torch.from_numpy(th.copy()).to(dev)
+            lens = torch.from_numpy(lh.copy()).to(dev)
+            mc = int(lh.max())
+            q = torch.randn((len(seqs), w.num_heads, w.head_dim), generator=gen,
+                            device=dev).to(w.dtype)
+            out = torch.empty((len(seqs), w.num_heads, w.head_dim), dtype=torch.float32, device=dev)
+            part = pkv.paged_attention_decode_partition_size(len(seqs), w.num_kv_heads, bs, mc, 0)
+            need = pkv.paged_attention_decode_workspace_size(len(seqs), w.num_heads,
+                                                             w.num_kv_heads, w.head_dim, mc, part)
+            ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+            for _ in range(5):
+                pkv.paged_attention_decode(q, kc, vc, tables, lens, w.scale, mc, part, out, ws)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(20):
+                pkv.paged_attention_decode(q, kc, vc, tables, lens, w.scale, mc, part, out, ws)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / 20
+            nbytes = kv_bytes(w, lh)
+            used = int(lh.sum())
+            allocated = int(sum(-(-int(n) // bs) * bs for n in lh))
+            print(json.dumps({
+                "sweep": "block_size", "workload": w.name, "block_size": bs, "layout": layout,
+                "partition_size": part, "decode_us": round(ms * 1e3, 2),
+                "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                "hbm_peak_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                "slot_utilisation": round(used / allocated, 4),
+                "max_length_reservation_utilisation": round(used / (len(lh) * reserve), 4)}),
+                flush=True)
+            del kc, vc, alloc
+            torch.cuda.empty_cache()
+
+
 def cpu_baseline(w, workloads):
     """The float64 oracle on a sample of the workload's sequences."""
     import threadpoolctl
@@ -339,13 +426,18 @@ def main():
     if args.copy_calibration:
         copy_calibration(torch, pkv)
         return
+    if args.block_size_sweep:
+        block_size_sweep(args, torch, pkv, workloads)
+        return
     w = workloads.get(args.workload)
     r = gpu_run(args, w, torch, pkv, workloads)
     ms_step = r["wall"] / args.steps * 1e3
     mean_bytes = float(r["bytes"].mean())
     value = mean_bytes / (ms_step * 1e-3) / 1e9
     kernel_ms = float(r["kernel_ms"].mean())
-    achieved = mean_bytes / (kernel_ms * 1e-3) / 1e9
+    # roofline on the bytes HBM must deliver: a shared prefix counts once
+    unique_bytes = float(r["unique_bytes"].mean())
+    achieved = unique_bytes / (kernel_ms * 1e-3) / 1e9
     src = os.path.join(ROOT, "paged_kv_cache_420_amd", "csrc", "decode.hip")
     line = {
         "metric": METRIC,
@@ -367,6 +459,7 @@ def main():
         "hbm_peak_frac": round(value / HBM_PEAK_GBPS, 4),
         "tokens_per_s": round(r["batch"] / (ms_step * 1e-3), 1),
         "kv_bytes_per_step": int(mean_bytes),
+        "kv_bytes_per_step_unique": int(unique_bytes),
         "decode_partition_us": round(kernel_ms * 1e3, 2),
         "decode_merge_us": round(float(r["merge_ms"].mean()) * 1e3, 2),
         "roofline": {"bound": "hbm", "kernel": "decode_partition_kernel (append fused)",
