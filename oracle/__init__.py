@@ -30,6 +30,7 @@ Modules:
   attention  -- gather, decode, chunked prefill (float64)
   kvstore    -- slot-mapping append and block copy on host arrays
   allocator  -- the reference block allocator (pure Python)
+  fp8        -- E4M3 codes for an 8-bit cache: value table, quantise, dequantise
 
 Parity status: every function here is pinned by tests/test_oracle*.py against
 closed forms, hand-worked fixtures under tests/golden/, brute force on tiny
@@ -39,6 +40,7 @@ inputs, and torch's own scaled_dot_product_attention in float64 on the CPU.
 from .attention import gather_kv, paged_decode, paged_prefill, dense_attention
 from .kvstore import kv_append, copy_blocks, slot_of
 from .allocator import RefAllocator, OutOfBlocks
+from . import fp8
 
 __all__ = [
     "gather_kv",
@@ -50,4 +52,5 @@ __all__ = [
     "slot_of",
     "RefAllocator",
     "OutOfBlocks",
+    "fp8",
 ]
