@@ -68,7 +68,12 @@ typedef enum pkv_status {
 typedef enum pkv_dtype {
   PKV_F32 = 0,
   PKV_F16 = 1,
-  PKV_BF16 = 2
+  PKV_BF16 = 2,
+  /* 8-bit cache codes (OCP E4M3: bias 7, no infinities, 448 the largest
+   * finite value) with one float32 scale per cache: a code c stands for
+   * value(c) * scale.  Only the byte-moving calls (pkv_paged_kv_append,
+   * pkv_copy_blocks) and the *_fp8 calls take it. */
+  PKV_FP8_E4M3 = 3
 } pkv_dtype;
 
 /* Description of the last failure on the calling thread ("" if none). */
@@ -233,6 +238,28 @@ int32_t pkv_copy_blocks(void* key_cache, void* value_cache,
                         int32_t num_kv_heads, int32_t block_size,
                         int32_t head_dim, int32_t dtype, void* stream);
 
+/* Quantising append for an 8-bit (PKV_FP8_E4M3) cache.  The pages name
+ * low-bit KV storage only as a direction (KV-cache article, §4.2 fixes list
+ * and §5 future directions); the format is the OCP 8-bit floating point
+ * specification's E4M3.  Same slot mapping as pkv_paged_kv_append, but
+ * each element x of key (value) is stored as the E4M3 code nearest to
+ * x / k_scale (x / v_scale): one correctly rounded float32 division, then
+ * round to nearest with ties to the even code, magnitudes above 448
+ * saturating to 448.
+ *   key, value      [num_tokens][num_kv_heads][head_dim], src_dtype
+ *                   (PKV_F32, PKV_F16 or PKV_BF16), finite values
+ *   key_cache, value_cache   one byte per element, layout above
+ *   k_scale, v_scale         positive finite float32
+ * head_dim must be a multiple of 16; pointers 16-byte aligned. */
+int32_t pkv_paged_kv_append_fp8(const void* key, const void* value,
+                                void* key_cache, void* value_cache,
+                                const int32_t* slot_mapping,
+                                int32_t num_tokens, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size,
+                                int32_t num_blocks, float k_scale,
+                                float v_scale, int32_t src_dtype,
+                                void* stream);
+
 /* The split-K partition (tokens) pkv_paged_attention_decode uses for these
  * sizes: partition_size itself when it is non-zero and valid, else the
  * automatic choice -- the longest of 1024, 512, 256, 128 tokens that still
@@ -392,6 +419,38 @@ int32_t pkv_paged_attention_decode_merge(
     int32_t max_blocks_per_seq, int32_t max_context_len,
     int32_t partition_size, float* out, void* workspace,
     size_t workspace_bytes, void* stream);
+
+/* pkv_paged_attention_decode over an 8-bit (PKV_FP8_E4M3) cache written by
+ * pkv_paged_kv_append_fp8 (KV-cache article §5: paging combined with
+ * quantisation).  Same arguments, layout, partitions, workspace and error
+ * behaviour as pkv_paged_attention_decode, except:
+ *   query          [num_seqs][num_heads][head_dim], query_dtype (PKV_BF16
+ *                  or PKV_F16)
+ *   key_cache, value_cache   one E4M3 code per element
+ *   k_scale, v_scale         the caches' scales: element (t, d) of K is
+ *                  value(code) * k_scale, of V value(code) * v_scale
+ * One more limit than the 16-bit call: block_size * head_dim >= 1024 (a
+ * head_dim of 64 needs blocks of at least 16 tokens).
+ * The result is attention over those dequantised values (each code widens
+ * exactly to the query's 16-bit type; float32 accumulation), so it agrees
+ * with the 16-bit path on the same values.  _partials is the first stage
+ * only; pkv_paged_attention_decode_merge completes it. */
+int32_t pkv_paged_attention_decode_fp8(
+    const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, const int32_t* context_lens,
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+    int32_t num_blocks, int32_t max_context_len, float scale, float k_scale,
+    float v_scale, int32_t partition_size, float* out, void* workspace,
+    size_t workspace_bytes, int32_t query_dtype, void* stream);
+int32_t pkv_paged_attention_decode_fp8_partials(
+    const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, const int32_t* context_lens,
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+    int32_t num_blocks, int32_t max_context_len, float scale, float k_scale,
+    float v_scale, int32_t partition_size, float* out, void* workspace,
+    size_t workspace_bytes, int32_t query_dtype, void* stream);
 
 /* Causal chunked prefill against the same paged cache (article §4.1/§4.2:
  * long prompts in chunks; §2.1: the same block-table gather and softmax).

@@ -67,33 +67,26 @@ def float_to_e4m3(y):
 
     `y` is converted to float32 first; the comparison itself is exact in
     float64 (every float32 and every midpoint of two codes is a float64).
+    For each |y| the two neighbouring code values lo <= |y| < hi are found
+    in the ascending table; the nearer wins, an exact tie goes to the code
+    whose mantissa (code bit 0) is even.
     """
     y = np.asarray(y, dtype=np.float32)
     flat = y.reshape(-1).astype(np.float64)
     codes, vals = _positive_codes()
-    out = np.empty(flat.shape, dtype=np.uint8)
-    for i, v in enumerate(flat):
-        if np.isnan(v):
-            out[i] = 0xFF if np.signbit(v) else 0x7F
-            continue
-        sign = 0x80 if np.signbit(v) else 0x00
-        a = abs(v)
-        if a >= E4M3_MAX:
-            out[i] = sign | 0x7E
-            continue
-        # vals[j - 1] <= a < vals[j]
-        j = int(np.searchsorted(vals, a, side="right"))
-        lo, hi = j - 1, j
-        d_lo = a - vals[lo]
-        d_hi = vals[hi] - a
-        if d_lo < d_hi:
-            pick = lo
-        elif d_hi < d_lo:
-            pick = hi
-        else:  # exact tie: the even mantissa (code bit 0 clear)
-            pick = lo if codes[lo] % 2 == 0 else hi
-        out[i] = sign | int(codes[pick])
-    return out.reshape(y.shape)
+    a = np.abs(flat)
+    nan = np.isnan(flat)
+    sign = np.where(np.signbit(flat), 0x80, 0x00).astype(np.int64)
+    j = np.clip(np.searchsorted(vals, np.where(nan, 0.0, a), side="right"), 1, len(vals) - 1)
+    lo, hi = j - 1, j
+    d_lo = a - vals[lo]
+    d_hi = vals[hi] - a
+    pick = np.where(d_lo < d_hi, lo,
+                    np.where(d_hi < d_lo, hi, np.where(codes[lo] % 2 == 0, lo, hi)))
+    out = codes[pick]
+    out = np.where(a >= E4M3_MAX, 0x7E, out)
+    out = np.where(nan, 0x7F, out) | sign
+    return out.astype(np.uint8).reshape(y.shape)
 
 
 def quantize(x, scale):

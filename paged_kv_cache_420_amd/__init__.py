@@ -10,7 +10,8 @@ no fallback: importing this package fails if libpkv.so has not been built
 (python paged_kv_cache_420_amd/_build.py).
 
 Cache layout (K and V alike): [num_blocks, num_kv_heads, block_size, head_dim],
-a tensor of the cache dtype (float32, float16 or bfloat16) on the GPU.
+a tensor of the cache dtype (float32, float16 or bfloat16) on the GPU, or of
+8-bit E4M3 codes (uint8 or float8_e4m3fn) for the *_fp8 calls.
 """
 
 import ctypes
@@ -27,7 +28,8 @@ __all__ = [
     "paged_attention_decode", "paged_attention_decode_append",
     "paged_attention_decode_append_partials", "paged_attention_decode_step",
     "paged_attention_decode_partials", "paged_attention_decode_merge",
-    "paged_attention_prefill", "library_path", "version",
+    "paged_attention_prefill", "paged_kv_append_fp8", "paged_attention_decode_fp8",
+    "paged_attention_decode_fp8_partials", "library_path", "version",
 ]
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
@@ -122,6 +124,16 @@ _SIGNATURES = {
                                                    _I32, ctypes.c_float, _I32, _P, _P, ctypes.c_size_t, _I32, _P]),
     "pkv_paged_attention_decode_merge": (_I32, [_P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P,
                                                 ctypes.c_size_t, _P]),
+    "pkv_paged_kv_append_fp8": (_I32, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
+                                       ctypes.c_float, ctypes.c_float, _I32, _P]),
+    "pkv_paged_attention_decode_fp8": (_I32, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
+                                              _I32, _I32, ctypes.c_float, ctypes.c_float,
+                                              ctypes.c_float, _I32, _P, _P, ctypes.c_size_t, _I32,
+                                              _P]),
+    "pkv_paged_attention_decode_fp8_partials": (_I32, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32,
+                                                       _I32, _I32, _I32, _I32, ctypes.c_float,
+                                                       ctypes.c_float, ctypes.c_float, _I32, _P,
+                                                       _P, ctypes.c_size_t, _I32, _P]),
     "pkv_paged_attention_prefill": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                                            _I32, ctypes.c_float, _P, _I32, _P]),
 }
@@ -413,9 +425,15 @@ class BlockAllocator:
 # ---------------------------------------------------------------------------
 
 _DTYPES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+# 8-bit caches hold E4M3 codes; a uint8 tensor or torch's float8_e4m3fn
+# (the same bytes) is accepted.
+_FP8_CODE = 3
+_FP8_TYPES = (torch.uint8, torch.float8_e4m3fn)
 
 
 def _dtype_code(t):
+    if t.dtype in _FP8_TYPES:
+        return _FP8_CODE
     try:
         return _DTYPES[t.dtype]
     except KeyError:
@@ -495,9 +513,16 @@ def paged_attention_decode_workspace_size(num_seqs, num_heads, num_kv_heads, hea
 
 
 def _decode_args(query, key_cache, value_cache, block_tables, context_lens, max_context_len,
-                 partition_size, out, workspace):
+                 partition_size, out, workspace, fp8=False):
     nb, hkv, bs, d = _cache_dims(key_cache, value_cache)
-    _dev(query, "query", dtype=key_cache.dtype, ndim=3)
+    if fp8:
+        if key_cache.dtype not in _FP8_TYPES:
+            raise InvalidArgument("an 8-bit cache must be uint8 or float8_e4m3fn")
+        _dev(query, "query", ndim=3)
+        if query.dtype not in (torch.bfloat16, torch.float16):
+            raise InvalidArgument("the query of an 8-bit cache must be bfloat16 or float16")
+    else:
+        _dev(query, "query", dtype=key_cache.dtype, ndim=3)
     _dev(block_tables, "block_tables", dtype=torch.int32, ndim=2)
     b, hq, dq = query.shape
     if context_lens is not None:  # None: host lengths, checked by the caller
@@ -732,6 +757,59 @@ def paged_attention_decode_partials(query, key_cache, value_cache, block_tables,
         int(max_context_len), float(scale), int(partition_size), out.data_ptr(), ws_ptr, ws_bytes,
         _dtype_code(key_cache), _stream(query)))
     return out
+
+
+def paged_kv_append_fp8(key, value, key_cache, value_cache, slot_mapping, k_scale, v_scale):
+    """Quantising scatter of key/value [T, Hkv, D] (float32/float16/bfloat16)
+    into 8-bit E4M3 caches (uint8 or float8_e4m3fn) at slot_mapping [T]:
+    code = nearest E4M3 to x / scale.  pkv_paged_kv_append_fp8."""
+    nb, hkv, bs, d = _cache_dims(key_cache, value_cache)
+    if key_cache.dtype not in _FP8_TYPES:
+        raise InvalidArgument("the caches must be uint8 or float8_e4m3fn")
+    _dev(key, "key", ndim=3)
+    _dev(value, "value", dtype=key.dtype, ndim=3)
+    _dev(slot_mapping, "slot_mapping", dtype=torch.int32, ndim=1)
+    t = key.shape[0]
+    if key.shape != (t, hkv, d) or value.shape != key.shape or slot_mapping.shape[0] != t:
+        raise InvalidArgument("key/value must be [T, num_kv_heads, head_dim] with T slots")
+    _check(_lib.pkv_paged_kv_append_fp8(key.data_ptr(), value.data_ptr(), key_cache.data_ptr(),
+                                        value_cache.data_ptr(), slot_mapping.data_ptr(), t, hkv,
+                                        d, bs, nb, float(k_scale), float(v_scale),
+                                        _dtype_code(key), _stream(key_cache)))
+
+
+def _decode_fp8(fn, query, key_cache, value_cache, block_tables, context_lens, scale, k_scale,
+                v_scale, max_context_len, partition_size, out, workspace):
+    (nb, hkv, bs, d, b, hq), out, workspace, ws_ptr, ws_bytes = _decode_args(
+        query, key_cache, value_cache, block_tables, context_lens, max_context_len,
+        partition_size, out, workspace, fp8=True)
+    _check(fn(query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+              block_tables.data_ptr(), context_lens.data_ptr(), b, hq, hkv, d, bs,
+              block_tables.shape[1], nb, int(max_context_len), float(scale), float(k_scale),
+              float(v_scale), int(partition_size), out.data_ptr(), ws_ptr, ws_bytes,
+              _dtype_code(query), _stream(query)))
+    return out
+
+
+def paged_attention_decode_fp8(query, key_cache, value_cache, block_tables, context_lens, scale,
+                               k_scale, v_scale, max_context_len, partition_size=0, out=None,
+                               workspace=None):
+    """Decode over 8-bit E4M3 caches (pkv_paged_attention_decode_fp8): as
+    paged_attention_decode with K = code value * k_scale, V = code value *
+    v_scale; query bfloat16 or float16; returns out [B, Hq, D] float32."""
+    return _decode_fp8(_lib.pkv_paged_attention_decode_fp8, query, key_cache, value_cache,
+                       block_tables, context_lens, scale, k_scale, v_scale, max_context_len,
+                       partition_size, out, workspace)
+
+
+def paged_attention_decode_fp8_partials(query, key_cache, value_cache, block_tables,
+                                        context_lens, scale, k_scale, v_scale, max_context_len,
+                                        partition_size, out, workspace):
+    """First stage of paged_attention_decode_fp8; paged_attention_decode_merge
+    with the same ``out``/``workspace`` completes it."""
+    return _decode_fp8(_lib.pkv_paged_attention_decode_fp8_partials, query, key_cache,
+                       value_cache, block_tables, context_lens, scale, k_scale, v_scale,
+                       max_context_len, partition_size, out, workspace)
 
 
 def paged_attention_decode_merge(context_lens, num_kv_heads, block_size, max_blocks_per_seq,

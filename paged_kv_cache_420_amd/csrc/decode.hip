@@ -51,6 +51,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 // ---- element traits: packed dot product of a 16-byte q slice with a
 // ---- 16-byte K slice, and widening of a 16-byte V slice to floats.
@@ -61,6 +62,12 @@ template <>
 struct Elem<PKV_BF16> {
   static constexpr int kBytes = 2;
   static constexpr int kPerLane = 8;
+  static constexpr int kQBytes = 2;      // bytes per query element
+  static constexpr bool kQuantised = false;
+  using Q = uint4;                          // a lane's slice of one q row
+  __device__ static Q load_q(const uint8_t* slice) {
+    return *reinterpret_cast<const uint4*>(slice);
+  }
   __device__ static float dot(const uint4& q, const uint4& k, float acc) {
     acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.x),
                                           __builtin_bit_cast(bf16x2_t, k.x), acc, false);
@@ -86,6 +93,12 @@ template <>
 struct Elem<PKV_F16> {
   static constexpr int kBytes = 2;
   static constexpr int kPerLane = 8;
+  static constexpr int kQBytes = 2;      // bytes per query element
+  static constexpr bool kQuantised = false;
+  using Q = uint4;                          // a lane's slice of one q row
+  __device__ static Q load_q(const uint8_t* slice) {
+    return *reinterpret_cast<const uint4*>(slice);
+  }
   __device__ static float dot(const uint4& q, const uint4& k, float acc) {
     acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, q.x),
                                  __builtin_bit_cast(f16x2_t, k.x), acc, false);
@@ -112,6 +125,12 @@ template <>
 struct Elem<PKV_F32> {
   static constexpr int kBytes = 4;
   static constexpr int kPerLane = 4;
+  static constexpr int kQBytes = 4;      // bytes per query element
+  static constexpr bool kQuantised = false;
+  using Q = uint4;                          // a lane's slice of one q row
+  __device__ static Q load_q(const uint8_t* slice) {
+    return *reinterpret_cast<const uint4*>(slice);
+  }
   __device__ static float dot(const uint4& q, const uint4& k, float acc) {
     acc = fmaf(__uint_as_float(q.x), __uint_as_float(k.x), acc);
     acc = fmaf(__uint_as_float(q.y), __uint_as_float(k.y), acc);
@@ -126,6 +145,79 @@ struct Elem<PKV_F32> {
     f[3] = __uint_as_float(v.w);
   }
 };
+
+// ---- 8-bit (E4M3) cache read with a 16-bit query.  A lane's 16-byte slice
+// ---- holds 16 codes; each code widens exactly to bf16 / f16 (3 mantissa
+// ---- bits, exponents 2^-9 .. 2^8) and to float32 in one conversion per
+// ---- pair, so the dot products and the weighted sums see the stored values
+// ---- unchanged; the caches' scales are applied outside the loops.
+constexpr int kFp8QBf16 = 100;  // template ids, not ABI values
+constexpr int kFp8QF16 = 101;
+
+struct Slice32 {
+  uint4 lo, hi;  // 16 query elements of 2 bytes
+};
+
+template <class Half>
+struct ElemFp8 {
+  static constexpr int kBytes = 1;
+  static constexpr int kPerLane = 16;
+  static constexpr int kQBytes = 2;
+  static constexpr bool kQuantised = true;
+  using Q = Slice32;
+  __device__ static Q load_q(const uint8_t* slice) {
+    return Q{reinterpret_cast<const uint4*>(slice)[0], reinterpret_cast<const uint4*>(slice)[1]};
+  }
+  __device__ static float dot(const Q& q, const uint4& k, float acc) {
+    const uint32_t kw[4] = {k.x, k.y, k.z, k.w};
+    const uint32_t qw[8] = {q.lo.x, q.lo.y, q.lo.z, q.lo.w, q.hi.x, q.hi.y, q.hi.z, q.hi.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc = Half::dot2(qw[2 * i], Half::widen_pair(kw[i], false), acc);
+      acc = Half::dot2(qw[2 * i + 1], Half::widen_pair(kw[i], true), acc);
+    }
+    return acc;
+  }
+  __device__ static void widen(const uint4& v, float (&f)[16]) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], false);
+      const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], true);
+      f[4 * i] = a.x;
+      f[4 * i + 1] = a.y;
+      f[4 * i + 2] = b.x;
+      f[4 * i + 3] = b.y;
+    }
+  }
+};
+
+// Codes 0, 1 (hi = false) or 2, 3 (hi = true) of a word as a 16-bit pair,
+// and the packed dot product with a pair of query elements.
+struct HalfBf16 {
+  __device__ static bf16x2_t widen_pair(uint32_t w, bool hi) {
+    return hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
+              : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  }
+  __device__ static float dot2(uint32_t q, bf16x2_t k, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q), k, acc, false);
+  }
+};
+
+struct HalfF16 {
+  __device__ static f16x2_t widen_pair(uint32_t w, bool hi) {
+    return hi ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true)
+              : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+  }
+  __device__ static float dot2(uint32_t q, f16x2_t k, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, q), k, acc, false);
+  }
+};
+
+template <>
+struct Elem<kFp8QBf16> : ElemFp8<HalfBf16> {};
+template <>
+struct Elem<kFp8QF16> : ElemFp8<HalfF16> {};
 
 // ---- cross-lane exchange for butterfly steps.  Steps run from the highest
 // ---- lane bit to the lowest; within a row of 16 lanes the DPP mirror
@@ -240,7 +332,8 @@ struct DecodeParams {
   float* ws_acc;               // [B][Hq][max_parts][D]  (split-K partials)
   float* ws_ml;                // [B][Hq][max_parts][2]
   int32_t num_kv_heads, log2_bs, max_blocks, num_blocks, max_ctx, part, max_parts;
-  float scale_log2;
+  float scale_log2;            // scale * log2(e), times the K scale of an 8-bit cache
+  float v_scale;               // V scale of an 8-bit cache (unused otherwise)
 };
 
 // Where a launch gets each sequence's length and which table entries it
@@ -353,7 +446,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(const Decode
   // XCD's L2, the loads miss the L1, which starts every launch empty).  No
   // device-scope fence is needed -- on this GPU one writes back the XCD's
   // whole L2.
-  if (prm.key_new != nullptr && p_idx == nparts - 1) {
+  if (!E::kQuantised && prm.key_new != nullptr && p_idx == nparts - 1) {
     const int pos = n - 1 - p0;  // within the partition
     if (tid < 2 * C::kLpt && !bad_blk) {
       const int id = s_blk[pos >> log2_bs];
@@ -372,11 +465,12 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(const Decode
   // q slices of the G heads: lane covers bytes (lane % LPT) * 16 of the row.
   const int dl = lane % C::kLpt;
   const int tok_in_unit = lane / C::kLpt;
-  uint4 q[G];
+  typename E::Q q[G];
 #pragma unroll
   for (int g = 0; g < G; ++g)
-    q[g] = *reinterpret_cast<const uint4*>(
-        prm.query + ((int64_t(b) * num_heads + int64_t(kvh) * G + g) * C::kRow) + dl * 16);
+    q[g] = E::load_q(prm.query +
+                     (int64_t(b) * num_heads + int64_t(kvh) * G + g) * (D * E::kQBytes) +
+                     dl * (C::kEpl * E::kQBytes));
 
   const uint8_t* kbase = prm.key_cache + int64_t(kvh) * tile_bytes + dl * 16;
   const uint8_t* vbase = prm.value_cache + int64_t(kvh) * tile_bytes + dl * 16;
@@ -519,6 +613,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(const Decode
     float m = s_red[g];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) m = fmaxf(m, s_red[w * G + g]);
+    if constexpr (E::kQuantised) a *= prm.v_scale;
     if (nparts == 1) {
       out_row[i] = bad_blk ? nan : a / l;
     } else {
@@ -637,6 +732,17 @@ hipError_t dispatch_decode(int32_t dtype, int D, int G, const DecodeParams& prm,
     case PKV_F16:
       return D == 64 ? dispatch_group<PKV_F16, 64>(G, prm, meta, B, s)
                      : dispatch_group<PKV_F16, 128>(G, prm, meta, B, s);
+    case kFp8QBf16:
+    case kFp8QF16:
+      if constexpr (Meta::kHost) {
+        return hipErrorInvalidValue;  // 8-bit caches have no step form
+      } else if (dtype == kFp8QBf16) {
+        return D == 64 ? dispatch_group<kFp8QBf16, 64>(G, prm, meta, B, s)
+                       : dispatch_group<kFp8QBf16, 128>(G, prm, meta, B, s);
+      } else {
+        return D == 64 ? dispatch_group<kFp8QF16, 64>(G, prm, meta, B, s)
+                       : dispatch_group<kFp8QF16, 128>(G, prm, meta, B, s);
+      }
     default:
       return D == 64 ? dispatch_group<PKV_F32, 64>(G, prm, meta, B, s)
                      : dispatch_group<PKV_F32, 128>(G, prm, meta, B, s);
@@ -721,7 +827,14 @@ int32_t prepare_decode(const void* query, const void* key_cache,
                        int32_t partition_size, float* out, void* workspace,
                        size_t workspace_bytes_given, int32_t dtype,
                        bool need_inputs, DecodeArgs* a) {
-  if (dtype_bytes(dtype) == 0) return fail(PKV_ERR_INVALID, "unknown dtype %d", dtype);
+  if (dtype == kFp8QBf16 || dtype == kFp8QF16) {
+    // 8-bit cache, 16-bit query: checked by the *_fp8 entry points
+  } else if (dtype == PKV_FP8_E4M3) {
+    return fail(PKV_ERR_INVALID,
+                "8-bit caches are read by pkv_paged_attention_decode_fp8 (with a 16-bit query)");
+  } else if (dtype_bytes(dtype) == 0) {
+    return fail(PKV_ERR_INVALID, "unknown dtype %d", dtype);
+  }
   if (num_seqs < 0) return fail(PKV_ERR_INVALID, "negative num_seqs");
   if (num_seqs > 65535) return fail(PKV_ERR_UNSUPPORTED, "at most 65535 sequences per call");
   if (num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0)
@@ -734,6 +847,13 @@ int32_t prepare_decode(const void* query, const void* key_cache,
     return fail(PKV_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", head_dim);
   if (!is_pow2(block_size) || block_size < 8 || block_size > 256)
     return fail(PKV_ERR_UNSUPPORTED, "block_size must be a power of two in [8, 256]");
+  // a wavefront's 16-byte loads cover 1 KiB of one (block, kv-head) tile:
+  // the tile must hold at least that much
+  const int cache_elem = (dtype == kFp8QBf16 || dtype == kFp8QF16) ? 1 : dtype_bytes(dtype);
+  if (need_inputs && int64_t(block_size) * head_dim * cache_elem < 1024)
+    return fail(PKV_ERR_UNSUPPORTED,
+                "block_size * head_dim * element size must be at least 1024 bytes (got %d x %d x %d)",
+                block_size, head_dim, cache_elem);
   if (max_blocks_per_seq <= 0 || num_blocks <= 0 || max_context_len < 0)
     return fail(PKV_ERR_INVALID, "invalid table/pool sizes");
   if (int64_t(num_blocks) * block_size >= (int64_t(1) << 31))
@@ -783,7 +903,8 @@ int32_t run_decode(const void* query, const void* key_new, const void* value_new
                    int32_t num_blocks, int32_t max_context_len, float scale,
                    int32_t partition_size, float* out, void* workspace,
                    size_t workspace_bytes_given, int32_t dtype, void* stream, bool partials,
-                   bool merge, const StepMeta* step) {
+                   bool merge, const StepMeta* step, float k_scale = 1.0f,
+                   float v_scale = 1.0f) {
   DecodeArgs a;
   const int32_t* lens_check = step ? reinterpret_cast<const int32_t*>(step->lens) : context_lens;
   int32_t st = prepare_decode(query, key_cache, value_cache, block_tables, lens_check,
@@ -817,7 +938,8 @@ int32_t run_decode(const void* query, const void* key_new, const void* value_new
   prm.max_ctx = max_context_len;
   prm.part = a.part;
   prm.max_parts = a.max_parts;
-  prm.scale_log2 = scale * kLog2e;
+  prm.scale_log2 = k_scale == 1.0f ? scale * kLog2e : (scale * k_scale) * kLog2e;
+  prm.v_scale = v_scale;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
   if (partials) {
@@ -989,4 +1111,52 @@ extern "C" int32_t pkv_paged_attention_decode_step_merge(
                     num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, 1,
                     max_context_len, 1.0f, partition_size, out, workspace,
                     workspace_bytes_given, PKV_F32, stream, false, true, &m);
+}
+
+namespace {
+int32_t fp8_call(const void* query, const void* key_cache, const void* value_cache,
+                 const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                 int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                 int32_t max_blocks_per_seq, int32_t num_blocks, int32_t max_context_len,
+                 float scale, float k_scale, float v_scale, int32_t partition_size, float* out,
+                 void* workspace, size_t workspace_bytes_given, int32_t query_dtype,
+                 void* stream, bool merge) {
+  if (query_dtype != PKV_BF16 && query_dtype != PKV_F16)
+    return fail(PKV_ERR_INVALID, "query_dtype %d must be BF16 or F16 for an 8-bit cache",
+                query_dtype);
+  if (!(std::isfinite(k_scale) && k_scale > 0.0f && std::isfinite(v_scale) && v_scale > 0.0f))
+    return fail(PKV_ERR_INVALID, "k_scale and v_scale must be positive and finite");
+  return run_decode(query, nullptr, nullptr, key_cache, value_cache, block_tables,
+                    context_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                    max_blocks_per_seq, num_blocks, max_context_len, scale, partition_size,
+                    out, workspace, workspace_bytes_given,
+                    query_dtype == PKV_BF16 ? kFp8QBf16 : kFp8QF16, stream, true, merge,
+                    nullptr, k_scale, v_scale);
+}
+}  // namespace
+
+extern "C" int32_t pkv_paged_attention_decode_fp8(
+    const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t max_blocks_per_seq, int32_t num_blocks, int32_t max_context_len, float scale,
+    float k_scale, float v_scale, int32_t partition_size, float* out, void* workspace,
+    size_t workspace_bytes_given, int32_t query_dtype, void* stream) {
+  return fp8_call(query, key_cache, value_cache, block_tables, context_lens, num_seqs,
+                  num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                  num_blocks, max_context_len, scale, k_scale, v_scale, partition_size, out,
+                  workspace, workspace_bytes_given, query_dtype, stream, true);
+}
+
+extern "C" int32_t pkv_paged_attention_decode_fp8_partials(
+    const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t max_blocks_per_seq, int32_t num_blocks, int32_t max_context_len, float scale,
+    float k_scale, float v_scale, int32_t partition_size, float* out, void* workspace,
+    size_t workspace_bytes_given, int32_t query_dtype, void* stream) {
+  return fp8_call(query, key_cache, value_cache, block_tables, context_lens, num_seqs,
+                  num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                  num_blocks, max_context_len, scale, k_scale, v_scale, partition_size, out,
+                  workspace, workspace_bytes_given, query_dtype, stream, false);
 }

@@ -14,6 +14,8 @@
 // same row, so a wavefront reads and writes whole 1 KiB spans.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
+
 #include "common.h"
 
 namespace pkv {
@@ -42,6 +44,115 @@ __global__ __launch_bounds__(256) void append_kernel(
                     pieces_per_row + piece;
   key_cache[dst] = key[i];
   value_cache[dst] = value[i];
+}
+
+// Quantising append into an 8-bit (E4M3) cache.  One lane per 16 elements
+// of a (token, kv-head) row: it reads them from K and from V in the source
+// type, divides each by the cache's scale (float32, correctly rounded),
+// clamps to the largest finite code value, and converts pairs with the
+// hardware conversion (round to nearest, ties to even); the 16 codes are
+// one 16-byte store.  The clamp first makes the conversion saturating,
+// as the stored format requires: a value above 448 rounds to 448 either
+// way, and a NaN passes the clamp and stays NaN.
+template <int SRC>
+struct Src16;
+
+template <>
+struct Src16<PKV_F32> {
+  static constexpr int kBytes = 64;
+  __device__ static void load(const uint8_t* p, float (&f)[16]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint4 w = reinterpret_cast<const uint4*>(p)[j];
+      f[4 * j] = __uint_as_float(w.x);
+      f[4 * j + 1] = __uint_as_float(w.y);
+      f[4 * j + 2] = __uint_as_float(w.z);
+      f[4 * j + 3] = __uint_as_float(w.w);
+    }
+  }
+};
+
+template <>
+struct Src16<PKV_BF16> {
+  static constexpr int kBytes = 32;
+  __device__ static void load(const uint8_t* p, float (&f)[16]) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint4 w = reinterpret_cast<const uint4*>(p)[j];
+      const uint32_t x[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f[8 * j + 2 * i] = __uint_as_float(x[i] << 16);
+        f[8 * j + 2 * i + 1] = __uint_as_float(x[i] & 0xffff0000u);
+      }
+    }
+  }
+};
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+template <>
+struct Src16<PKV_F16> {
+  static constexpr int kBytes = 32;
+  __device__ static void load(const uint8_t* p, float (&f)[16]) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint4 w = reinterpret_cast<const uint4*>(p)[j];
+      const uint32_t x[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const half2_t h = __builtin_bit_cast(half2_t, x[i]);
+        f[8 * j + 2 * i] = float(h.x);
+        f[8 * j + 2 * i + 1] = float(h.y);
+      }
+    }
+  }
+};
+
+constexpr float kE4m3Max = 448.0f;
+
+__device__ __forceinline__ float to_code_range(float x, float scale) {
+  const float y = x / scale;
+  return y > kE4m3Max ? kE4m3Max : (y < -kE4m3Max ? -kE4m3Max : y);
+}
+
+__device__ __forceinline__ uint4 quantize16(const float (&f)[16], float scale) {
+  uint32_t w[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    // bytes 0, 1 from the low-word conversion, bytes 2, 3 from the high
+    const uint32_t lo = __builtin_amdgcn_cvt_pk_fp8_f32(
+        to_code_range(f[4 * j], scale), to_code_range(f[4 * j + 1], scale), 0, false);
+    w[j] = __builtin_amdgcn_cvt_pk_fp8_f32(to_code_range(f[4 * j + 2], scale),
+                                           to_code_range(f[4 * j + 3], scale), lo, true);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+template <int SRC>
+__global__ __launch_bounds__(256) void append_fp8_kernel(
+    const uint8_t* __restrict__ key, const uint8_t* __restrict__ value,
+    uint4* __restrict__ key_cache, uint4* __restrict__ value_cache,
+    const int32_t* __restrict__ slots, int64_t total_pieces,
+    int32_t pieces_per_row, int32_t num_kv_heads, int32_t block_size,
+    int64_t num_slots, float k_scale, float v_scale) {
+  int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= total_pieces) return;
+  int64_t row = i / pieces_per_row;
+  int32_t piece = int32_t(i - row * pieces_per_row);
+  int64_t token = row / num_kv_heads;
+  int32_t head = int32_t(row - token * num_kv_heads);
+  int32_t slot = slots[token];
+  if (slot < 0 || slot >= num_slots) return;
+  int32_t blk = slot / block_size;
+  int32_t off = slot - blk * block_size;
+  int64_t dst = ((int64_t(blk) * num_kv_heads + head) * block_size + off) *
+                    pieces_per_row + piece;
+  float f[16];
+  Src16<SRC>::load(key + i * Src16<SRC>::kBytes, f);
+  key_cache[dst] = quantize16(f, k_scale);
+  Src16<SRC>::load(value + i * Src16<SRC>::kBytes, f);
+  value_cache[dst] = quantize16(f, v_scale);
 }
 
 // grid.y = pair; each lane copies 16-byte pieces of one block, strided.
@@ -152,5 +263,55 @@ extern "C" int32_t pkv_copy_blocks(void* key_cache, void* value_cache,
   hipError_t e = hipGetLastError();
   if (e != hipSuccess)
     return fail(PKV_ERR_HIP, "copy_blocks launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+extern "C" int32_t pkv_paged_kv_append_fp8(
+    const void* key, const void* value, void* key_cache, void* value_cache,
+    const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t num_blocks, float k_scale,
+    float v_scale, int32_t src_dtype, void* stream) {
+  if (src_dtype != PKV_F32 && src_dtype != PKV_F16 && src_dtype != PKV_BF16)
+    return fail(PKV_ERR_INVALID, "src_dtype %d must be F32, F16 or BF16", src_dtype);
+  int32_t st = check_cache_args(num_kv_heads, head_dim, block_size, num_blocks,
+                                PKV_FP8_E4M3);
+  if (st != PKV_OK) return st;
+  if (!(std::isfinite(k_scale) && k_scale > 0.0f && std::isfinite(v_scale) &&
+        v_scale > 0.0f))
+    return fail(PKV_ERR_INVALID, "k_scale and v_scale must be positive and finite");
+  if (num_tokens < 0)
+    return fail(PKV_ERR_INVALID, "negative num_tokens %d", num_tokens);
+  if (num_tokens == 0) return ok();
+  if (!key || !value || !key_cache || !value_cache || !slot_mapping)
+    return fail(PKV_ERR_INVALID, "NULL pointer argument");
+  if (!aligned16(key) || !aligned16(value) || !aligned16(key_cache) ||
+      !aligned16(value_cache))
+    return fail(PKV_ERR_INVALID, "K/V buffers must be 16-byte aligned");
+  const int32_t pieces = head_dim / 16;
+  const int64_t total = int64_t(num_tokens) * num_kv_heads * pieces;
+  const int64_t blocks = (total + 255) / 256;
+  if (blocks >= (int64_t(1) << 31))
+    return fail(PKV_ERR_INVALID, "append too large for one launch");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const auto* k = static_cast<const uint8_t*>(key);
+  const auto* v = static_cast<const uint8_t*>(value);
+  auto* kc = static_cast<uint4*>(key_cache);
+  auto* vc = static_cast<uint4*>(value_cache);
+  const int64_t num_slots = int64_t(num_blocks) * block_size;
+  if (src_dtype == PKV_F32)
+    hipLaunchKernelGGL(append_fp8_kernel<PKV_F32>, dim3(unsigned(blocks)), dim3(256), 0, s, k, v,
+                       kc, vc, slot_mapping, total, pieces, num_kv_heads, block_size, num_slots,
+                       k_scale, v_scale);
+  else if (src_dtype == PKV_F16)
+    hipLaunchKernelGGL(append_fp8_kernel<PKV_F16>, dim3(unsigned(blocks)), dim3(256), 0, s, k, v,
+                       kc, vc, slot_mapping, total, pieces, num_kv_heads, block_size, num_slots,
+                       k_scale, v_scale);
+  else
+    hipLaunchKernelGGL(append_fp8_kernel<PKV_BF16>, dim3(unsigned(blocks)), dim3(256), 0, s, k,
+                       v, kc, vc, slot_mapping, total, pieces, num_kv_heads, block_size,
+                       num_slots, k_scale, v_scale);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return fail(PKV_ERR_HIP, "fp8 append launch: %s", hipGetErrorString(e));
   return ok();
 }

@@ -12,7 +12,7 @@ import torch
 
 import paged_kv_cache_420_amd as pkv
 import workloads
-from oracle import RefAllocator, copy_blocks as o_copy, kv_append as o_append
+from oracle import RefAllocator, copy_blocks as o_copy, fp8, kv_append as o_append
 
 DEV = "cuda:0"
 TOL = {torch.float32: 1e-5, torch.float16: 2e-3, torch.bfloat16: 2e-3}
@@ -26,12 +26,15 @@ class GpuState:
     def __init__(self, w, p, ops=None, nan_fill=True):
         self.w, self.p = w, p
         shape = (p.num_blocks, w.num_kv_heads, w.block_size, w.head_dim)
-        fill = float("nan") if nan_fill else 0.0
-        self.kc = torch.full(shape, fill, dtype=w.dtype, device=DEV)
-        self.vc = torch.full(shape, fill, dtype=w.dtype, device=DEV)
+        self.kc, self.vc = self._caches(shape, nan_fill)
         self.alloc = pkv.BlockAllocator(p.num_blocks, w.block_size, p.free_order)
         self.slot_log = []
         self.run(p.ops if ops is None else ops)
+
+    def _caches(self, shape, nan_fill):
+        fill = float("nan") if nan_fill else 0.0
+        return (torch.full(shape, fill, dtype=self.w.dtype, device=DEV),
+                torch.full(shape, fill, dtype=self.w.dtype, device=DEV))
 
     def _copy(self, pairs):
         src = torch.tensor([a for a, _ in pairs], dtype=torch.int32, device=DEV)
@@ -58,6 +61,29 @@ class GpuState:
         t, l = self.alloc.build_block_tables(seqs, maxb)
         return (torch.from_numpy(t.copy()).to(DEV), torch.from_numpy(l.copy()).to(DEV),
                 t, l)
+
+
+class GpuStateFp8(GpuState):
+    """8-bit E4M3 caches (uint8, unwritten bytes = the NaN code 0x7F) filled
+    by the quantising append from the workload's values in its dtype."""
+
+    def __init__(self, w, p, k_scale, v_scale, ops=None):
+        self.k_scale, self.v_scale = k_scale, v_scale
+        super().__init__(w, p, ops)
+
+    def _caches(self, shape, nan_fill):
+        return (torch.full(shape, 0x7F, dtype=torch.uint8, device=DEV),
+                torch.full(shape, 0x7F, dtype=torch.uint8, device=DEV))
+
+    def _append(self, i, seq, n, slots):
+        self.slot_log.append((seq, slots.tolist()))
+        if n == 0:
+            return
+        k, v = workloads.kv_rows(self.w, i, n)
+        pkv.paged_kv_append_fp8(workloads.to_dtype(k, self.w.dtype).to(DEV),
+                                workloads.to_dtype(v, self.w.dtype).to(DEV),
+                                self.kc, self.vc, torch.from_numpy(slots).to(DEV),
+                                self.k_scale, self.v_scale)
 
 
 class OracleState:
@@ -131,3 +157,41 @@ def max_abs_err(got, want):
     got = np.asarray(got, dtype=np.float64)
     assert np.isfinite(got).all(), "non-finite output"
     return float(np.max(np.abs(got - want))) if got.size else 0.0
+
+
+class OracleStateFp8(OracleState):
+    """Oracle side of GpuStateFp8: code pools (uint8, 0x7F where unwritten)
+    written with oracle.fp8.quantize of the same values; ``kc``/``vc`` are
+    the float64 dequantised pools (NaN where unwritten)."""
+
+    def __init__(self, w, p, k_scale, v_scale, ops=None):
+        self.k_scale, self.v_scale = k_scale, v_scale
+        shape = (p.num_blocks, w.num_kv_heads, w.block_size, w.head_dim)
+        self.kcodes = np.full(shape, 0x7F, dtype=np.uint8)
+        self.vcodes = np.full(shape, 0x7F, dtype=np.uint8)
+        super().__init__(w, p, ops)
+
+    def _copy(self, pairs):
+        o_copy(self.kcodes, self.vcodes, [a for a, _ in pairs], [b for _, b in pairs])
+
+    def _append(self, i, seq, n, slots):
+        self.slot_log.append((seq, list(slots)))
+        if n == 0:
+            return
+        k, v = workloads.kv_rows(self.w, i, n)
+        kq = fp8.quantize(workloads.as_f64(workloads.to_dtype(k, self.w.dtype)), self.k_scale)
+        vq = fp8.quantize(workloads.as_f64(workloads.to_dtype(v, self.w.dtype)), self.v_scale)
+        o_append(self.kcodes, self.vcodes, kq, vq, slots, self.w.block_size)
+
+    def run(self, ops, first_index=0):
+        super().run(ops, first_index)
+        self.kc = fp8.dequantize(self.kcodes, self.k_scale)
+        self.vc = fp8.dequantize(self.vcodes, self.v_scale)
+
+
+def logical_kv_fp8(w, segments, k_scale, v_scale):
+    """Float64 dequantised logical K, V of one sequence: the generator's
+    values in the workload dtype, quantised by the oracle."""
+    k, v = logical_kv(w, segments)
+    return (fp8.dequantize(fp8.quantize(k, k_scale), k_scale),
+            fp8.dequantize(fp8.quantize(v, v_scale), v_scale))

@@ -75,7 +75,35 @@ def test_device_calls_reject_bad_arguments_before_launch():
     assert lib.pkv_paged_attention_decode_append(null, null, null, null, null, null, null, 2, 4, 4,
                                                  128, 16, 8, 64, 100, 1.0, 0, null, null, 0, 2,
                                                  null) == 1
+    # 8-bit caches: only through the *_fp8 calls, with a 16-bit query and
+    # positive finite scales
+    assert lib.pkv_paged_attention_decode(null, null, null, null, null, 2, 4, 4, 128, 16, 8, 64,
+                                          100, 1.0, 0, null, null, 0, 3, null) == 1
+    assert b"fp8" in lib.pkv_last_error()
+    assert lib.pkv_paged_attention_decode_fp8(null, null, null, null, null, 2, 4, 4, 128, 16, 8,
+                                              64, 100, 1.0, 0.5, 0.5, 0, null, null, 0, 0,
+                                              null) == 1
+    assert lib.pkv_paged_attention_decode_fp8(null, null, null, null, null, 2, 4, 4, 128, 16, 8,
+                                              64, 100, 1.0, 0.0, 0.5, 0, null, null, 0, 2,
+                                              null) == 1
+    assert lib.pkv_paged_attention_decode_fp8_partials(null, null, null, null, null, 2, 6, 2,
+                                                       128, 16, 8, 64, 100, 1.0, 0.5, 0.5, 0,
+                                                       null, null, 0, 2, null) == 7
+    # head_dim 64 codes in 8-token blocks: tiles under 1 KiB
+    assert lib.pkv_paged_attention_decode_fp8(null, null, null, null, null, 2, 4, 4, 64, 8, 8,
+                                              64, 100, 1.0, 0.5, 0.5, 0, null, null, 0, 2,
+                                              null) == 7
+    assert lib.pkv_paged_kv_append_fp8(null, null, null, null, null, 1, 1, 64, 16, 4, 1.0, 1.0,
+                                       3, null) == 1
+    assert lib.pkv_paged_kv_append_fp8(null, null, null, null, null, 1, 1, 64, 16, 4, -1.0, 1.0,
+                                       2, null) == 1
+    assert lib.pkv_paged_kv_append_fp8(null, null, null, null, null, 1, 1, 24, 16, 4, 1.0, 1.0,
+                                       2, null) == 1          # 24 codes: not 16-byte rows
+    assert lib.pkv_paged_attention_prefill(null, null, null, null, null, null, 1, 4, 4, 128, 16,
+                                           8, 64, 1, 1, 1.0, null, 3, null) == 7
     # empty batches are no-ops
+    assert lib.pkv_paged_kv_append_fp8(null, null, null, null, null, 0, 1, 64, 16, 4, 1.0, 1.0,
+                                       2, null) == 0
     assert lib.pkv_paged_kv_append(null, null, null, null, null, 0, 1, 64, 16, 4, 2, null) == 0
     assert lib.pkv_paged_attention_decode(null, null, null, null, null, 0, 4, 4, 128, 16, 8, 64,
                                           100, 1.0, 0, null, null, 0, 2, null) == 0
