@@ -31,6 +31,8 @@ timed the same way, against the bf16 matrix-core peak.
 Usage: python bench.py [--steps K] [--warmup W] [--workload NAME]
        python bench.py --copy-calibration   (block copy of a known size,
                                              the scale for HBM counters)
+       python bench.py --block-size-sweep   (paging overhead, block sizes)
+       python bench.py --fp8 [--workload NAME]  (8-bit cache vs 16-bit)
 """
 
 import argparse
@@ -66,6 +68,9 @@ def parse():
                     help="skip the chunked-prefill leg of the shared-prefix workload")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time pkv_copy_blocks over a known byte count and exit")
+    ap.add_argument("--fp8", action="store_true",
+                    help="8-bit (E4M3) cache leg: quantising append builds the workload's "
+                         "cache, then decode over it is timed next to the 16-bit cache")
     ap.add_argument("--block-size-sweep", action="store_true",
                     help="decode GB/s and slot utilisation at block sizes 8..256, shuffled vs "
                          "identity (contiguous) block placement; one JSON line each")
@@ -341,6 +346,101 @@ def block_size_sweep(args, torch, pkv, workloads):
             torch.cuda.empty_cache()
 
 
+def fp8_leg(args, torch, pkv, workloads):
+    """Decode over an 8-bit (E4M3) cache of the workload's batch, built by
+    the quantising append with the workload's per-tensor scales, next to
+    the same batch in its 16-bit dtype.  Each is timed as partials + merge
+    on a fixed cache state (HIP events on the stream, mean over the timed
+    calls after the warm-up); bytes are the KV bytes each cache holds for
+    the batch (1 byte per element for the 8-bit cache)."""
+    dev = torch.device("cuda:0")
+    w = workloads.get(args.workload)
+    ks, vs = workloads.FP8_SCALES
+    res = {}
+    for kind in ("fp8_e4m3", DTYPE_NAMES[str(w.dtype)]):
+        p = workloads.plan(w)
+        shape = (p.num_blocks, w.num_kv_heads, w.block_size, w.head_dim)
+        cdt = torch.uint8 if kind == "fp8_e4m3" else w.dtype
+        kc = torch.zeros(shape, dtype=cdt, device=dev)
+        vc = torch.zeros(shape, dtype=cdt, device=dev)
+        alloc = pkv.BlockAllocator(p.num_blocks, w.block_size, p.free_order)
+
+        def on_copy(pairs):
+            src = torch.tensor([a for a, _ in pairs], dtype=torch.int32, device=dev)
+            dst = torch.tensor([b for _, b in pairs], dtype=torch.int32, device=dev)
+            pkv.copy_blocks(kc, vc, src, dst)
+
+        def on_append(i, seq, n, slots):
+            k, v = workloads.kv_rows(w, i, n)
+            k = workloads.to_dtype(k, w.dtype).to(dev)
+            v = workloads.to_dtype(v, w.dtype).to(dev)
+            sl = torch.from_numpy(slots).to(dev)
+            if kind == "fp8_e4m3":
+                pkv.paged_kv_append_fp8(k, v, kc, vc, sl, ks, vs)
+            else:
+                pkv.paged_kv_append(k, v, kc, vc, sl)
+
+        workloads.run_schedule(p.ops, alloc, on_append, on_copy)
+        seqs = np.asarray(p.seqs, dtype=np.int64)
+        mb = max(len(alloc.block_table(int(s))) for s in seqs)
+        th, lh = alloc.build_block_tables(seqs, mb)
+        tables = torch.from_numpy(th.copy()).to(dev)
+        lens = torch.from_numpy(lh.copy()).to(dev)
+        mc = int(lh.max())
+        b = len(seqs)
+        q = workloads.to_dtype(np.stack([workloads.decode_query(w, s) for s in p.seqs]),
+                               w.dtype).to(dev)
+        out = torch.empty((b, w.num_heads, w.head_dim), dtype=torch.float32, device=dev)
+        part = pkv.paged_attention_decode_partition_size(b, w.num_kv_heads, w.block_size, mc,
+                                                         w.partition_size)
+        need = pkv.paged_attention_decode_workspace_size(b, w.num_heads, w.num_kv_heads,
+                                                         w.head_dim, mc, part)
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+
+        def partials():
+            if kind == "fp8_e4m3":
+                pkv.paged_attention_decode_fp8_partials(q, kc, vc, tables, lens, w.scale, ks, vs,
+                                                        mc, part, out, ws)
+            else:
+                pkv.paged_attention_decode_partials(q, kc, vc, tables, lens, w.scale, mc, part,
+                                                    out, ws)
+
+        def merge():
+            pkv.paged_attention_decode_merge(lens, w.num_kv_heads, w.block_size, mb, mc, part,
+                                             out, ws)
+
+        stream = torch.cuda.current_stream(dev)
+        n = args.warmup + args.steps
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+        for i in range(n):
+            ev[i][0].record(stream)
+            partials()
+            ev[i][1].record(stream)
+            merge()
+            ev[i][2].record(stream)
+        torch.cuda.synchronize()
+        if not torch.isfinite(out).all():
+            raise RuntimeError("decode produced non-finite output")
+        timed = range(args.warmup, n)
+        kern = float(np.mean([ev[i][0].elapsed_time(ev[i][1]) for i in timed]))
+        both = float(np.mean([ev[i][0].elapsed_time(ev[i][2]) for i in timed]))
+        elem = 1 if kind == "fp8_e4m3" else w.elem_bytes
+        nbytes = int(np.sum(lh, dtype=np.int64)) * w.num_kv_heads * w.head_dim * 2 * elem
+        res[kind] = {"kv_bytes": nbytes, "partition_size": part,
+                     "decode_partition_us": round(kern * 1e3, 2),
+                     "decode_us": round(both * 1e3, 2),
+                     "kernel_gbps": round(nbytes / (kern * 1e-3) / 1e9, 1),
+                     "kernel_hbm_peak_frac": round(nbytes / (kern * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                     "tokens_per_s": round(b / (both * 1e-3), 1)}
+        del kc, vc, alloc
+        torch.cuda.empty_cache()
+    k8, k16 = res["fp8_e4m3"], res[DTYPE_NAMES[str(w.dtype)]]
+    print(json.dumps({"leg": "fp8_kv_cache", "workload": w.name, "k_scale": ks, "v_scale": vs,
+                      "steps": args.steps, "warmup": args.warmup, "caches": res,
+                      "decode_speedup_vs_16bit": round(k16["decode_us"] / k8["decode_us"], 3)}),
+          flush=True)
+
+
 def cpu_baseline(w, workloads):
     """The float64 oracle on a sample of the workload's sequences."""
     import threadpoolctl
@@ -428,6 +528,9 @@ def main():
         return
     if args.block_size_sweep:
         block_size_sweep(args, torch, pkv, workloads)
+        return
+    if args.fp8:
+        fp8_leg(args, torch, pkv, workloads)
         return
     w = workloads.get(args.workload)
     r = gpu_run(args, w, torch, pkv, workloads)

@@ -551,16 +551,19 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(const Decode
 #pragma unroll
     for (int e = 0; e < C::kEpl; ++e) acc[g][e] = 0.0f;
 
+  // Rows past the partition's last token are zeroed as raw bits (four
+  // selects per 16-byte slice, whatever the element type) before they are
+  // widened, so stale or NaN cache contents contribute exactly nothing.
   auto pv = [&](const uint4 (&vv)[U], int c) {
     const int t0 = c * C::kChunkTok;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int t = t0 + u * C::kTpl + tok_in_unit;
       const bool live = t < ntok;
+      const uint4 raw = make_uint4(live ? vv[u].x : 0u, live ? vv[u].y : 0u,
+                                   live ? vv[u].z : 0u, live ? vv[u].w : 0u);
       float f[C::kEpl];
-      E::widen(vv[u], f);
-#pragma unroll
-      for (int e = 0; e < C::kEpl; ++e) f[e] = live ? f[e] : 0.0f;
+      E::widen(raw, f);
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         const float p = s_score[t * G + g];
