@@ -207,6 +207,104 @@ int32_t pkv_build_block_tables(const pkv_allocator* alloc,
                                int32_t* context_lens);
 
 /* ======================================================================
+ * Continuous-batching scheduler (host)
+ *
+ * Requests join and leave the running batch at every step, and a finished
+ * request's blocks return to the pool at once for a waiting one ("vLLM 初探"
+ * tutorial §1.3 and §1.5; explainer, continuous-batching section); prompts
+ * are prefilled in chunks (KV-cache article §4.1/§4.2) and the running set
+ * is capped (article §3.2, max_num_seqs).  The pages give the mechanism
+ * only; the policy below is this library's, and a host model of it is
+ * checked against it step by step.
+ *
+ * A request has a prompt of P tokens and O decode steps.  Its cache holds
+ * prefilled + generated tokens; it is finished after its O-th decode row.
+ * pkv_scheduler_step, in order:
+ *   1. retire: every running request with O decode rows done is freed
+ *      (pkv_seq_free order) and reported as finished;
+ *   2. admit: while the waiting queue is not empty and fewer than
+ *      max_num_seqs run, its head joins the running set (at its end) if
+ *        paged (reserve_tokens == 0): free blocks >=
+ *          ceil(min(P, chunk_size) / block_size) + running requests;
+ *        reservation model (reserve_tokens > 0): (running + 1) *
+ *          ceil(reserve_tokens / block_size) <= num_blocks -- every
+ *          request holds room for its longest case, as a contiguous
+ *          per-request cache would;
+ *      else admission stops (first come, first served);
+ *   3. decode rows, oldest running request first, one token each for every
+ *      request whose prompt is done, while the step's token budget
+ *      (max_num_batched_tokens) lasts.  If the append needs more blocks
+ *      than are free, the youngest running request without a row in this
+ *      step is preempted -- its blocks freed, its generated tokens added to
+ *      its prompt, its progress reset -- and put back at the head of the
+ *      queue, until the append fits or the request itself was preempted;
+ *   4. prefill chunks, oldest first: min(P - prefilled, chunk_size,
+ *      budget left) tokens; if they do not fit, younger requests without a
+ *      row are preempted as above; if that is not enough the chunk and all
+ *      later ones wait.
+ * Rows are reported decode rows first, then prefill chunks, each with its
+ * request id, query length (1 for decode rows), context length after the
+ * step's appends, and block table; `slots` holds the rows' new slots in
+ * row order (the slot mapping for pkv_paged_kv_append).  The requests
+ * never share blocks, so no copy-on-write arises.
+ * ====================================================================== */
+
+typedef struct pkv_scheduler pkv_scheduler;
+
+/* num_blocks x block_size pool; init_free_order as for
+ * pkv_allocator_create (NULL = 0..num_blocks-1); max_num_seqs running
+ * requests at most; max_num_batched_tokens rows per step; chunk_size prompt
+ * tokens per prefill chunk; reserve_tokens 0 for paged admission, else the
+ * per-request reservation of the reservation model. */
+int32_t pkv_scheduler_create(int32_t num_blocks, int32_t block_size,
+                             const int32_t* init_free_order,
+                             int32_t max_num_seqs,
+                             int32_t max_num_batched_tokens,
+                             int32_t chunk_size, int32_t reserve_tokens,
+                             pkv_scheduler** out);
+void pkv_scheduler_destroy(pkv_scheduler* sched);
+
+/* Queue a request (prompt_len >= 1, output_len >= 1 decode steps).
+ * INVALID if it could never fit the pool (or the reservation); SEQ_EXISTS
+ * if the id is waiting or running. */
+int32_t pkv_scheduler_add_request(pkv_scheduler* sched, int64_t id,
+                                  int32_t prompt_len, int32_t output_len);
+
+/* Columns the block_tables of the next step need (the longest table any
+ * queued or running request can reach). */
+int32_t pkv_scheduler_max_blocks(const pkv_scheduler* sched, int32_t* out);
+
+/* One step (policy above).  Caller-owned host arrays:
+ *   seq_ids, query_lens, context_lens   [max_rows]   (max_rows >= max_num_seqs)
+ *   slots                               [max_tokens] (>= max_num_batched_tokens)
+ *   block_tables                        [max_rows][max_blocks], -1 padded
+ *                                       (max_blocks >= pkv_scheduler_max_blocks)
+ * Returns the row counts: rows [0, num_decode) are decode rows, the rest
+ * prefill chunks; num_tokens = sum of query_lens.  BUFFER_TOO_SMALL (state
+ * unchanged) if a capacity is short. */
+int32_t pkv_scheduler_step(pkv_scheduler* sched, int32_t max_rows,
+                           int32_t max_tokens, int32_t max_blocks,
+                           int64_t* seq_ids, int32_t* query_lens,
+                           int32_t* context_lens, int32_t* slots,
+                           int32_t* block_tables, int32_t* num_decode,
+                           int32_t* num_rows, int32_t* num_tokens);
+
+/* Requests the last step retired (finished) and preempted, in the order it
+ * did so.  The counts are always written; BUFFER_TOO_SMALL if a capacity
+ * is short. */
+int32_t pkv_scheduler_last_events(const pkv_scheduler* sched,
+                                  int64_t* finished, int32_t finished_cap,
+                                  int32_t* num_finished, int64_t* preempted,
+                                  int32_t preempted_cap,
+                                  int32_t* num_preempted);
+
+/* out[9]: steps, running, waiting, finished (total), preemptions (total),
+ * cached tokens of the running requests, slots their blocks hold, slots
+ * reserved for them (reservation model; else = the slots held), free
+ * blocks. */
+int32_t pkv_scheduler_stats(const pkv_scheduler* sched, int64_t* out);
+
+/* ======================================================================
  * Device calls (gfx950 HIP kernels)
  * ====================================================================== */
 

@@ -23,7 +23,7 @@ import torch
 __all__ = [
     "PkvError", "InvalidArgument", "OutOfBlocks", "NoSuchSequence",
     "SequenceExists", "BufferTooSmall", "HipError", "Unsupported",
-    "BlockAllocator", "DecodeLauncher", "paged_kv_append", "copy_blocks",
+    "BlockAllocator", "Scheduler", "StepPlan", "DecodeLauncher", "paged_kv_append", "copy_blocks",
     "paged_attention_decode_workspace_size", "paged_attention_decode_partition_size",
     "paged_attention_decode", "paged_attention_decode_append",
     "paged_attention_decode_append_partials", "paged_attention_decode_step",
@@ -134,6 +134,13 @@ _SIGNATURES = {
                                                        _I32, _I32, _I32, _I32, ctypes.c_float,
                                                        ctypes.c_float, ctypes.c_float, _I32, _P,
                                                        _P, ctypes.c_size_t, _I32, _P]),
+    "pkv_scheduler_create": (_I32, [_I32, _I32, _P, _I32, _I32, _I32, _I32, ctypes.POINTER(_P)]),
+    "pkv_scheduler_destroy": (None, [_P]),
+    "pkv_scheduler_add_request": (_I32, [_P, _I64, _I32, _I32]),
+    "pkv_scheduler_max_blocks": (_I32, [_P, _P]),
+    "pkv_scheduler_step": (_I32, [_P, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "pkv_scheduler_last_events": (_I32, [_P, _P, _I32, _P, _P, _I32, _P]),
+    "pkv_scheduler_stats": (_I32, [_P, _P]),
     "pkv_paged_attention_prefill": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                                            _I32, ctypes.c_float, _P, _I32, _P]),
 }
@@ -418,6 +425,108 @@ class BlockAllocator:
         _check(_lib.pkv_build_block_tables(self._h, seqs.ctypes.data, b, max_blocks,
                                            _i32p(tables), _i32p(lens)))
         return tables[:b, :max_blocks], lens[:b]
+
+
+class StepPlan:
+    """One scheduler step: rows [0, num_decode) are decode rows, the rest
+    prefill chunks.  Arrays are views of the scheduler's buffers, valid until
+    its next step."""
+
+    def __init__(self, seq_ids, query_lens, context_lens, slots, block_tables, num_decode,
+                 finished, preempted):
+        self.seq_ids = seq_ids
+        self.query_lens = query_lens
+        self.context_lens = context_lens
+        self.slots = slots
+        self.block_tables = block_tables
+        self.num_decode = num_decode
+        self.finished = finished
+        self.preempted = preempted
+
+    @property
+    def num_rows(self):
+        return len(self.seq_ids)
+
+    @property
+    def num_prefill(self):
+        return self.num_rows - self.num_decode
+
+    @property
+    def num_tokens(self):
+        return len(self.slots)
+
+
+_STAT_NAMES = ("steps", "running", "waiting", "finished", "preemptions", "cached_tokens",
+               "allocated_slots", "reserved_slots", "free_blocks")
+
+
+class Scheduler:
+    """Continuous-batching step scheduler (pkv_scheduler_*; policy in pkv.h)."""
+
+    def __init__(self, num_blocks, block_size, max_num_seqs, max_num_batched_tokens, chunk_size,
+                 reserve_tokens=0, init_free_order=None):
+        self._h = _P()
+        order = None
+        if init_free_order is not None:
+            order = np.ascontiguousarray(init_free_order, dtype=np.int32)
+            if order.shape != (num_blocks,):
+                raise InvalidArgument("init_free_order must hold num_blocks entries")
+        _check(_lib.pkv_scheduler_create(num_blocks, block_size,
+                                         None if order is None else order.ctypes.data,
+                                         max_num_seqs, max_num_batched_tokens, chunk_size,
+                                         reserve_tokens, ctypes.byref(self._h)))
+        self.max_num_seqs = max_num_seqs
+        self.max_num_batched_tokens = max_num_batched_tokens
+        self._ids = np.empty(max_num_seqs, dtype=np.int64)
+        self._qlen = np.empty(max_num_seqs, dtype=np.int32)
+        self._ctx = np.empty(max_num_seqs, dtype=np.int32)
+        self._slots = np.empty(max_num_batched_tokens, dtype=np.int32)
+        self._fin = np.empty(max_num_seqs, dtype=np.int64)
+        self._pre = np.empty(max_num_seqs, dtype=np.int64)
+        self._tables = np.empty(0, dtype=np.int32)
+        self._counts = np.empty(3, dtype=np.int32)
+        self._stats = np.empty(9, dtype=np.int64)
+
+    def close(self):
+        if getattr(self, "_h", None) and _lib is not None:
+            _lib.pkv_scheduler_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def add_request(self, rid, prompt_len, output_len):
+        _check(_lib.pkv_scheduler_add_request(self._h, int(rid), int(prompt_len),
+                                              int(output_len)))
+
+    def max_blocks(self):
+        out = _I32()
+        _check(_lib.pkv_scheduler_max_blocks(self._h, ctypes.byref(out)))
+        return out.value
+
+    def step(self, max_blocks=None):
+        """Run one step; returns a StepPlan (block_tables [rows, max_blocks])."""
+        mb = self.max_blocks() if max_blocks is None else int(max_blocks)
+        if self._tables.size < self.max_num_seqs * mb:
+            self._tables = np.empty(self.max_num_seqs * mb, dtype=np.int32)
+        c = self._counts
+        _check(_lib.pkv_scheduler_step(self._h, self.max_num_seqs, self.max_num_batched_tokens, mb,
+                                       self._ids.ctypes.data, self._qlen.ctypes.data,
+                                       self._ctx.ctypes.data, self._slots.ctypes.data,
+                                       self._tables.ctypes.data, c[0:].ctypes.data,
+                                       c[1:].ctypes.data, c[2:].ctypes.data))
+        nd, nr, nt = int(c[0]), int(c[1]), int(c[2])
+        nf, npre = _I32(), _I32()
+        _check(_lib.pkv_scheduler_last_events(self._h, self._fin.ctypes.data, len(self._fin),
+                                              ctypes.byref(nf), self._pre.ctypes.data,
+                                              len(self._pre), ctypes.byref(npre)))
+        tables = self._tables[:self.max_num_seqs * mb].reshape(self.max_num_seqs, mb)[:nr]
+        return StepPlan(self._ids[:nr], self._qlen[:nr], self._ctx[:nr], self._slots[:nt], tables,
+                        nd, self._fin[:nf.value].tolist(), self._pre[:npre.value].tolist())
+
+    def stats(self):
+        _check(_lib.pkv_scheduler_stats(self._h, self._stats.ctypes.data))
+        return dict(zip(_STAT_NAMES, (int(x) for x in self._stats)))
 
 
 # ---------------------------------------------------------------------------

@@ -100,6 +100,14 @@ void BlockAllocator::grow(Seq& s, int32_t n, int32_t* slots,
   s.len += n;
 }
 
+int64_t BlockAllocator::blocks_for_append(int64_t seq, int32_t n) const {
+  auto it = seqs_.find(seq);
+  if (it == seqs_.end()) return -1;
+  const Seq& s = it->second;
+  bool c = false;
+  return blocks_needed(s, n, s.table.empty() ? 0 : ref_[s.table.back()], &c);
+}
+
 int32_t BlockAllocator::append(int64_t seq, int32_t n, int32_t* slots,
                                std::vector<CowPair>* cow) {
   auto it = seqs_.find(seq);

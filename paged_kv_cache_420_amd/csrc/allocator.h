@@ -50,6 +50,10 @@ class BlockAllocator {
   void free_stack(int32_t* out) const;
   const std::vector<int32_t>& refcounts() const { return ref_; }
 
+  // Blocks an append of n tokens to `seq` would take (fresh blocks plus a
+  // copy-on-write block), without changing anything; -1 if no such seq.
+  int64_t blocks_for_append(int64_t seq, int32_t n) const;
+
   // Each returns a pkv_status; on failure nothing has changed.
   int32_t add(int64_t seq);
   int32_t release(int64_t seq);

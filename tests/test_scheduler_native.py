@@ -1,0 +1,112 @@
+"""The native continuous-batching scheduler (pkv_scheduler_*) against the
+reference scheduler, step for step and bit for bit: rows, context lengths,
+block tables, slots, finished and preempted requests, statistics.  CPU
+only: the scheduler is host code."""
+
+import json
+import os
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+from conftest import GOLDEN
+
+import paged_kv_cache_420_amd as pkv
+from oracle.scheduler import RefScheduler
+
+
+def _compare_step(nat, ref):
+    plan = nat.step()
+    want = ref.step()
+    rows = [(int(plan.seq_ids[i]), int(plan.query_lens[i]), int(plan.context_lens[i]),
+             [int(x) for x in plan.block_tables[i] if x >= 0]) for i in range(plan.num_rows)]
+    assert rows == [(r[0], r[1], r[2], list(r[3])) for r in want["rows"]]
+    assert plan.num_decode == want["num_decode"]
+    assert [int(x) for x in plan.slots] == want["slots"]
+    assert plan.finished == want["finished"]
+    assert plan.preempted == want["preempted"]
+    # -1 padding past each table's end
+    for i in range(plan.num_rows):
+        t = plan.block_tables[i]
+        n = len(rows[i][3])
+        assert (t[n:] == -1).all()
+    assert nat.stats() == ref.stats()
+
+
+def _pair(nb, bs, seqs, budget, chunk, reserve, order=None):
+    nat = pkv.Scheduler(nb, bs, seqs, budget, chunk, reserve, order)
+    ref = RefScheduler(nb, bs, seqs, budget, chunk, reserve, order)
+    return nat, ref
+
+
+def test_golden_traces_through_the_c_abi():
+    with open(os.path.join(GOLDEN, "scheduler_traces.json")) as f:
+        traces = json.load(f)["traces"]
+    for t in traces:
+        c = t["config"]
+        nat = pkv.Scheduler(c["num_blocks"], c["block_size"], c["max_num_seqs"],
+                            c["max_num_batched_tokens"], c["chunk_size"], c["reserve_tokens"])
+        ids = {name: 100 + i for i, (name, _, _) in enumerate(t["requests"])}
+        names = {v: k for k, v in ids.items()}
+        for name, p, o in t["requests"]:
+            nat.add_request(ids[name], p, o)
+        for want in t["steps"]:
+            plan = nat.step()
+            rows = [[names[int(plan.seq_ids[i])], int(plan.query_lens[i]),
+                     int(plan.context_lens[i]),
+                     [int(x) for x in plan.block_tables[i] if x >= 0]]
+                    for i in range(plan.num_rows)]
+            assert rows == want["rows"], want["why"]
+            assert plan.num_decode == want["num_decode"]
+            assert [int(x) for x in plan.slots] == want["slots"], want["why"]
+            assert [names[x] for x in plan.finished] == want["finished"]
+            assert [names[x] for x in plan.preempted] == want["preempted"]
+        nat.close()
+
+
+@settings(max_examples=80, deadline=None)
+@given(reqs=st.lists(st.tuples(st.integers(1, 40), st.integers(1, 30)), min_size=1,
+                     max_size=14),
+       bs=st.sampled_from([1, 2, 4, 8, 16]), seqs=st.integers(1, 6), budget=st.integers(1, 30),
+       chunk=st.integers(1, 20), spare=st.integers(0, 16), reserve_on=st.booleans(),
+       arrivals=st.lists(st.integers(0, 3), min_size=14, max_size=14), data=st.data())
+def test_native_matches_reference_step_for_step(reqs, bs, seqs, budget, chunk, spare,
+                                                reserve_on, arrivals, data):
+    reserve = max(p + o for p, o in reqs) if reserve_on else 0
+    need = max(-(-(p + o) // bs) for p, o in reqs)
+    nb = need + spare
+    order = np.array(data.draw(st.permutations(list(range(nb)))), dtype=np.int32)
+    nat, ref = _pair(nb, bs, seqs, budget, chunk, reserve, order)
+    # requests arrive over the first steps, a few at a time
+    pending = [(i, p, o) for i, (p, o) in enumerate(reqs)]
+    step = 0
+    while pending or ref.running or ref.waiting:
+        k = arrivals[step % len(arrivals)] if step < 20 else len(pending)
+        for rid, p, o in pending[:k]:
+            nat.add_request(rid, p, o)
+            ref.add_request(rid, p, o)
+        pending = pending[k:]
+        _compare_step(nat, ref)
+        step += 1
+        assert step < 5000
+    assert nat.stats()["finished"] == len(reqs)
+    nat.close()
+
+
+def test_native_rejects_bad_requests_and_buffers():
+    s = pkv.Scheduler(4, 4, 2, 8, 4, reserve_tokens=10)
+    with pytest.raises(pkv.InvalidArgument):
+        s.add_request(0, 8, 3)
+    s.add_request(1, 2, 2)
+    with pytest.raises(pkv.SequenceExists):
+        s.add_request(1, 2, 2)
+    with pytest.raises(pkv.BufferTooSmall):
+        s.step(max_blocks=0)
+    assert s.stats()["steps"] == 0                # nothing happened
+    assert s.step().num_rows == 1
+    with pytest.raises(pkv.InvalidArgument):
+        pkv.Scheduler(4, 4, 0, 8, 4)
+    t = pkv.Scheduler(2, 4, 2, 8, 4)
+    with pytest.raises(pkv.InvalidArgument):
+        t.add_request(0, 6, 3)
