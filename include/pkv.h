@@ -224,8 +224,9 @@ int32_t pkv_build_block_tables(const pkv_allocator* alloc,
  *      (pkv_seq_free order) and reported as finished;
  *   2. admit: while the waiting queue is not empty and fewer than
  *      max_num_seqs run, its head joins the running set (at its end) if
- *        paged (reserve_tokens == 0): free blocks >=
- *          ceil(min(P, chunk_size) / block_size) + running requests;
+ *        paged (reserve_tokens == 0): free blocks >= ceil(P / block_size)
+ *          + the blocks the running requests' unfinished prompts still
+ *          need + one per running request;
  *        reservation model (reserve_tokens > 0): (running + 1) *
  *          ceil(reserve_tokens / block_size) <= num_blocks -- every
  *          request holds room for its longest case, as a contiguous

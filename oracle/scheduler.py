@@ -21,7 +21,8 @@ which the native scheduler must reproduce step for step):
 * Each step: (1) retire every running request with O decode rows done
   (release its blocks); (2) admit from the head of the FIFO queue while
   fewer than max_num_seqs run and, for paged admission, the free blocks
-  cover the first chunk's blocks plus one block per running request, or,
+  cover the request's whole prompt, the prompt blocks the running requests
+  have yet to take, and one block per running request, or,
   for the reservation model, while (running + 1) reservations of
   ceil(reserve_tokens / block_size) blocks fit the pool; (3) give every
   request whose prompt is done one decode row, oldest first, while the
@@ -89,8 +90,14 @@ class RefScheduler:
             return False
         if self.reserve:
             return (len(self.running) + 1) * _cdiv(self.reserve, self.block_size) <= self.num_blocks
-        first = _cdiv(min(r.prompt, self.chunk), self.block_size)
-        return self.alloc.num_free() >= first + len(self.running)
+        # the prompt's blocks, the prompt blocks running requests have yet
+        # to take, one block per running request
+        pending = 0
+        for x in self.running:
+            if x.prefilled < x.prompt:
+                pending += _cdiv(x.prompt, self.block_size) - len(self.alloc.tables[x.id])
+        need = _cdiv(r.prompt, self.block_size) + pending + len(self.running)
+        return self.alloc.num_free() >= need
 
     def _preempt_youngest(self, candidates, has_row, preempted):
         """Preempt the youngest request in `candidates` (a list of running

@@ -44,10 +44,14 @@ bool Scheduler::admissible(const Request& r) const {
   if (run >= cfg_.max_num_seqs) return false;
   if (cfg_.reserve_tokens > 0)
     return int64_t(run + 1) * reserve_blocks() <= cfg_.num_blocks;
-  // blocks for the first chunk, plus one per running request (what their
+  // blocks for its whole prompt, plus the prompt blocks the running
+  // requests still have to take, plus one per running request (what their
   // next decode rows may take)
-  const int64_t first = cdiv(std::min(r.prompt, cfg_.chunk_size), cfg_.block_size);
-  return alloc_.num_free() >= first + run;
+  int64_t need = cdiv(r.prompt, cfg_.block_size) + run;
+  for (const Request& x : running_)
+    if (x.prefilled < x.prompt)
+      need += cdiv(x.prompt, cfg_.block_size) - int64_t(alloc_.table(x.id).size());
+  return alloc_.num_free() >= need;
 }
 
 int32_t Scheduler::preempt_youngest(int32_t min_index) {

@@ -191,3 +191,69 @@ def run_schedule(ops, alloc, on_append=None, on_copy=None, first_index=0):
                 on_append(i, op[1], op[2], slots)
         else:
             raise ValueError(op)
+
+
+# ---------------------------------------------------------------------------
+# Continuous-batching traces
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class ServingTrace:
+    """Requests of a continuous-batching run, all queued at the start (an
+    offline batch), with the layer shape their attention runs at."""
+    name: str
+    num_requests: int
+    prompt: str                 # length law of prompts (as Workload.lens)
+    output: str                 # length law of decode steps per request
+    num_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    dtype: torch.dtype
+    num_blocks: int
+    max_num_seqs: int
+    max_num_batched_tokens: int
+    chunk_size: int
+    seed: int
+    std: float = 1.0
+
+    @property
+    def scale(self):
+        return 1.0 / math.sqrt(self.head_dim)
+
+
+# The LLaMA-7B-shaped layer under a request mix in the pages' terms: prompts
+# of 100-2000 tokens (the KV-cache article's 100- vs 2000-token requests),
+# replies mostly short but up to 2000 tokens (the explainer's reserve of
+# 2000 with 50 used; the 13B batch's geometric law, mean 600, clipped to
+# [10, 2000]); 512-token prompt chunks and a 4096-token step budget (the
+# article's chunked prefill); at most 256 running requests; a pool of 16384
+# blocks of 16 tokens (4.3 GB of bf16 K and V for one layer).
+SERVING = {
+    "serve_llama7b": ServingTrace("serve_llama7b", 1024, "uniform:100,2000",
+                                  "geometric:600,10,2000", 32, 32, 128, 16, torch.bfloat16,
+                                  16384, 256, 4096, 512, 4206),
+}
+
+
+def serving_requests(t):
+    """(id, prompt, output) of every request, drawn from default_rng(seed):
+    prompt lengths first, then output lengths."""
+    rng = np.random.default_rng(t.seed)
+    pw = Workload("p", t.num_requests, 1, 1, 1, 1, t.dtype, 1.0, 0, t.prompt)
+    ow = Workload("o", t.num_requests, 1, 1, 1, 1, t.dtype, 1.0, 0, t.output)
+    prompts = draw_lengths(pw, rng)
+    outputs = draw_lengths(ow, rng)
+    return [(i, int(p), int(o)) for i, (p, o) in enumerate(zip(prompts, outputs))]
+
+
+def serving_token_kv(t, rid, pos):
+    """K and V row of request ``rid`` at position ``pos``: float32 [Hkv, D]
+    each, from default_rng([seed, 1, rid, pos])."""
+    both = normal([t.seed, 1, rid, pos], (2, t.num_kv_heads, t.head_dim), t.std)
+    return both[0], both[1]
+
+
+def serving_query(t, rid, pos):
+    """Query row of request ``rid`` at position ``pos``: float32 [Hq, D]."""
+    return normal([t.seed, 2, rid, pos], (t.num_heads, t.head_dim), t.std)
