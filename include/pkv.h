@@ -206,6 +206,44 @@ int32_t pkv_build_block_tables(const pkv_allocator* alloc,
                                int32_t max_blocks, int32_t* block_tables,
                                int32_t* context_lens);
 
+/* ---- Swap space: a host tier of blocks ------------------------------
+ * The KV-cache article's §4.2 answers running out of device memory with
+ * swap space in host memory, and its §5 names a page pool spanning GPU and
+ * CPU memory.  Here a second pool of num_host_blocks blocks (its own LIFO
+ * free stack, block 0 on top, no sharing) holds swapped-out sequences:
+ *   swap_out(seq): every block of the table, in logical order, gets a host
+ *     block (pairs device -> host reported); the device blocks are then
+ *     released as pkv_seq_free releases them (a shared block stays with
+ *     its other holders); the sequence keeps its length, its table now
+ *     names host blocks, and it cannot grow, fork or appear in a device
+ *     call until swap_in.  OUT_OF_BLOCKS (nothing changed) if the host
+ *     tier lacks blocks.
+ *   swap_in(seq): every host block, in logical order, gets a fresh device
+ *     block (pairs host -> device reported; the host blocks are pushed
+ *     back in that order).  OUT_OF_BLOCKS (nothing changed) if the device
+ *     pool lacks blocks.
+ *   pkv_seq_free of a swapped sequence returns its host blocks.
+ * The caller moves the data with pkv_swap_blocks using the reported pairs
+ * (swap-out copies before the device blocks are reused; swap-in copies
+ * before the sequence is read). */
+int32_t pkv_allocator_set_host_pool(pkv_allocator* alloc,
+                                    int32_t num_host_blocks);
+int32_t pkv_num_free_host_blocks(const pkv_allocator* alloc, int32_t* n);
+int32_t pkv_seq_is_swapped(const pkv_allocator* alloc, int64_t seq,
+                           int32_t* swapped);
+/* pairs in device_blocks[i] -> host_blocks[i], i < *n (cap >= table length,
+ * else BUFFER_TOO_SMALL with nothing changed) */
+int32_t pkv_seq_swap_out(pkv_allocator* alloc, int64_t seq,
+                         int32_t* device_blocks, int32_t* host_blocks,
+                         int32_t cap, int32_t* n);
+/* pairs in host_blocks[i] -> device_blocks[i] */
+int32_t pkv_seq_swap_in(pkv_allocator* alloc, int64_t seq,
+                        int32_t* host_blocks, int32_t* device_blocks,
+                        int32_t cap, int32_t* n);
+/* host_free_stack[num_host_blocks]: free host blocks, top first. */
+int32_t pkv_allocator_host_snapshot(const pkv_allocator* alloc,
+                                    int32_t* host_free_stack, int32_t* n_free);
+
 /* ======================================================================
  * Continuous-batching scheduler (host)
  *
@@ -358,6 +396,23 @@ int32_t pkv_paged_kv_append_fp8(const void* key, const void* value,
                                 int32_t num_blocks, float k_scale,
                                 float v_scale, int32_t src_dtype,
                                 void* stream);
+
+/* Whole-block copies between two pools of the same block layout -- the
+ * data side of swapping (KV-cache article §4.2, swap space): for each i,
+ * block dst_blocks[i] of the destination caches := block src_blocks[i] of
+ * the source caches, K and V.  Either side may be device memory or pinned
+ * host memory (hipHostMalloc, torch pin_memory); copies are enqueued on
+ * `stream` (runs of consecutive pairs as one copy) and asynchronous with
+ * respect to the host, so the host pool must stay alive and unchanged
+ * until the stream reaches them.  src_blocks/dst_blocks are HOST arrays,
+ * checked against the pool sizes; block_bytes = num_kv_heads *
+ * block_size * head_dim * element size. */
+int32_t pkv_swap_blocks(const void* src_key_cache, const void* src_value_cache,
+                        void* dst_key_cache, void* dst_value_cache,
+                        const int32_t* src_blocks, const int32_t* dst_blocks,
+                        int32_t num_pairs, int32_t src_num_blocks,
+                        int32_t dst_num_blocks, int64_t block_bytes,
+                        void* stream);
 
 /* The split-K partition (tokens) pkv_paged_attention_decode uses for these
  * sizes: partition_size itself when it is non-zero and valid, else the

@@ -33,6 +33,20 @@ Readings (the pages fix none of these):
   block whose count reaches zero is pushed on the free stack.
 * a call that would need more blocks than are free fails and changes nothing;
   a batch append is all-or-nothing over the whole batch.
+
+Swap space (KV-cache article §4.2: host memory as swap space when device
+memory runs out; §5: a page pool spanning GPU and CPU memory).  Readings:
+* a second pool of host blocks with its own stack (block 0 popped first);
+  host blocks are never shared.
+* ``swap_out(seq)``: for each block of the table in logical order a host
+  block is popped, the pair (device, host) reported, and the device block
+  released as ``free`` releases it; the table then lists the host blocks
+  and the sequence is marked swapped.  ``swap_in(seq)``: for each host
+  block in logical order a device block is popped (count 1), the pair
+  (host, device) reported and the host block pushed back.  Each fails
+  with nothing changed if its target pool lacks blocks.
+* a swapped sequence cannot grow, fork or be packed into device tables;
+  ``free`` pushes its host blocks back in logical order.
 """
 
 
@@ -58,6 +72,9 @@ class RefAllocator:
         self.ref = [0] * num_blocks
         self.tables = {}
         self.lens = {}
+        self.swapped = set()
+        self._host_free = []
+        self.num_host_blocks = 0
 
     # -- queries --------------------------------------------------------
     def num_free(self):
@@ -87,6 +104,8 @@ class RefAllocator:
     def fork(self, parent, child):
         if parent not in self.tables:
             raise KeyError(parent)
+        if parent in self.swapped:
+            raise ValueError("sequence is swapped out")
         if child in self.tables:
             raise ValueError("child sequence already exists")
         self.tables[child] = list(self.tables[parent])
@@ -97,11 +116,66 @@ class RefAllocator:
     def free(self, seq):
         if seq not in self.tables:
             raise KeyError(seq)
-        for b in self.tables.pop(seq):
+        if seq in self.swapped:
+            self._host_free += self.tables.pop(seq)
+            self.swapped.discard(seq)
+        else:
+            for b in self.tables.pop(seq):
+                self.ref[b] -= 1
+                if self.ref[b] == 0:
+                    self._free.append(b)
+        del self.lens[seq]
+
+    # -- swap space -------------------------------------------------------
+    def set_host_pool(self, num_host_blocks):
+        if num_host_blocks < 0:
+            raise ValueError("negative host pool")
+        if self.swapped:
+            raise ValueError("the host pool is in use")
+        self.num_host_blocks = num_host_blocks
+        self._host_free = list(reversed(range(num_host_blocks)))
+
+    def host_free_stack(self):
+        return list(reversed(self._host_free))
+
+    def swap_out(self, seq):
+        if seq not in self.tables:
+            raise KeyError(seq)
+        if seq in self.swapped:
+            raise ValueError("already swapped out")
+        table = self.tables[seq]
+        if len(table) > len(self._host_free):
+            raise OutOfBlocks(seq)
+        pairs, host = [], []
+        for b in table:
+            h = self._host_free.pop()
+            pairs.append((b, h))
+            host.append(h)
             self.ref[b] -= 1
             if self.ref[b] == 0:
                 self._free.append(b)
-        del self.lens[seq]
+        self.tables[seq] = host
+        self.swapped.add(seq)
+        return pairs
+
+    def swap_in(self, seq):
+        if seq not in self.tables:
+            raise KeyError(seq)
+        if seq not in self.swapped:
+            raise ValueError("not swapped out")
+        table = self.tables[seq]
+        if len(table) > len(self._free):
+            raise OutOfBlocks(seq)
+        pairs, dev = [], []
+        for h in table:
+            b = self._free.pop()
+            self.ref[b] = 1
+            pairs.append((h, b))
+            dev.append(b)
+            self._host_free.append(h)
+        self.tables[seq] = dev
+        self.swapped.discard(seq)
+        return pairs
 
     # -- growth -------------------------------------------------------------
     def _needs(self, seq, n):
@@ -117,6 +191,8 @@ class RefAllocator:
             raise KeyError(seq)
         if n < 0:
             raise ValueError("negative token count")
+        if seq in self.swapped:
+            raise ValueError("sequence is swapped out")
         fresh, cow = self._needs(seq, n)
         if fresh + int(cow) > len(self._free):
             raise OutOfBlocks(seq)
@@ -153,6 +229,8 @@ class RefAllocator:
                 raise KeyError(s)
             if c < 0:
                 raise ValueError("negative token count")
+            if s in self.swapped:
+                raise ValueError("sequence is swapped out")
         saved = (list(self._free), list(self.ref),
                  {s: list(t) for s, t in self.tables.items()}, dict(self.lens))
         slots, pairs = [], []
@@ -172,6 +250,8 @@ class RefAllocator:
         rows, lens = [], []
         for s in seqs:
             t = self.tables[s]
+            if s in self.swapped:
+                raise ValueError("sequence is swapped out")
             if len(t) > max_blocks:
                 raise ValueError("max_blocks too small")
             rows.append(t + [-1] * (max_blocks - len(t)))

@@ -29,7 +29,7 @@ __all__ = [
     "paged_attention_decode_append_partials", "paged_attention_decode_step",
     "paged_attention_decode_partials", "paged_attention_decode_merge",
     "paged_attention_prefill", "paged_kv_append_fp8", "paged_attention_decode_fp8",
-    "paged_attention_decode_fp8_partials", "library_path", "version",
+    "paged_attention_decode_fp8_partials", "swap_blocks", "library_path", "version",
 ]
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
@@ -106,6 +106,13 @@ _SIGNATURES = {
     "pkv_block_size": (_I32, [_P, _P]),
     "pkv_block_refcount": (_I32, [_P, _I32, _P]),
     "pkv_allocator_snapshot": (_I32, [_P, _P, _P, _P]),
+    "pkv_allocator_set_host_pool": (_I32, [_P, _I32]),
+    "pkv_num_free_host_blocks": (_I32, [_P, _P]),
+    "pkv_seq_is_swapped": (_I32, [_P, _I64, _P]),
+    "pkv_seq_swap_out": (_I32, [_P, _I64, _P, _P, _I32, _P]),
+    "pkv_seq_swap_in": (_I32, [_P, _I64, _P, _P, _I32, _P]),
+    "pkv_allocator_host_snapshot": (_I32, [_P, _P, _P]),
+    "pkv_swap_blocks": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _P]),
     "pkv_build_block_tables": (_I32, [_P, _P, _I32, _I32, _P, _P]),
     "pkv_paged_kv_append": (_I32, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P]),
     "pkv_copy_blocks": (_I32, [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P]),
@@ -406,6 +413,44 @@ class BlockAllocator:
         _check(_lib.pkv_allocator_snapshot(self._h, _i32p(free), ctypes.byref(nf), _i32p(ref)))
         return free[:nf.value].tolist(), ref.tolist()
 
+    # -- swap space (pkv_allocator_set_host_pool, pkv_seq_swap_out/in) -----
+    def set_host_pool(self, num_host_blocks):
+        _check(_lib.pkv_allocator_set_host_pool(self._h, int(num_host_blocks)))
+        self.num_host_blocks = int(num_host_blocks)
+
+    def num_free_host(self):
+        out = _I32()
+        _check(_lib.pkv_num_free_host_blocks(self._h, ctypes.byref(out)))
+        return out.value
+
+    def is_swapped(self, seq):
+        out = _I32()
+        _check(_lib.pkv_seq_is_swapped(self._h, int(seq), ctypes.byref(out)))
+        return bool(out.value)
+
+    def _swap(self, fn, seq):
+        cap = max(1, self.num_blocks, getattr(self, "num_host_blocks", 0))
+        a = np.empty(cap, dtype=np.int32)
+        b = np.empty(cap, dtype=np.int32)
+        n = _I32()
+        _check(fn(self._h, int(seq), _i32p(a), _i32p(b), cap, ctypes.byref(n)))
+        return np.stack([a[:n.value], b[:n.value]], axis=1)
+
+    def swap_out(self, seq):
+        """Move seq to the host tier; returns int32 pairs [n, 2] (device, host)."""
+        return self._swap(_lib.pkv_seq_swap_out, seq)
+
+    def swap_in(self, seq):
+        """Back to device blocks; returns int32 pairs [n, 2] (host, device)."""
+        return self._swap(_lib.pkv_seq_swap_in, seq)
+
+    def host_snapshot(self):
+        """Free host blocks, top of the stack first."""
+        out = np.empty(max(1, getattr(self, "num_host_blocks", 0)), dtype=np.int32)
+        n = _I32()
+        _check(_lib.pkv_allocator_host_snapshot(self._h, _i32p(out), ctypes.byref(n)))
+        return out[:n.value].tolist()
+
     def build_block_tables(self, seqs, max_blocks, tables_out=None, lens_out=None):
         """Host int32 arrays (block_tables [B, max_blocks] -1 padded, context_lens [B]).
         ``tables_out``/``lens_out``: optional contiguous int32 arrays of those
@@ -599,6 +644,36 @@ def copy_blocks(key_cache, value_cache, src, dst):
     _check(_lib.pkv_copy_blocks(key_cache.data_ptr(), value_cache.data_ptr(), src.data_ptr(),
                                 dst.data_ptr(), src.shape[0], nb, hkv, bs, d,
                                 _dtype_code(key_cache), _stream(key_cache)))
+
+
+def swap_blocks(src_key_cache, src_value_cache, dst_key_cache, dst_value_cache, src_blocks,
+                dst_blocks):
+    """Block dst_blocks[i] of the destination caches := block src_blocks[i]
+    of the source caches (pkv_swap_blocks).  Caches of one shape per side
+    ([blocks, Hkv, block_size, D], same dtype), each on the GPU or in pinned
+    host memory; block ids are host arrays.  Enqueued on the current
+    stream of the GPU side."""
+    for t, name in ((src_key_cache, "src_key_cache"), (src_value_cache, "src_value_cache"),
+                    (dst_key_cache, "dst_key_cache"), (dst_value_cache, "dst_value_cache")):
+        if not isinstance(t, torch.Tensor) or t.dim() != 4 or not t.is_contiguous():
+            raise InvalidArgument(f"{name} must be a contiguous 4-d tensor")
+        if not t.is_cuda and not t.is_pinned():
+            raise InvalidArgument(f"{name} must be on the GPU or in pinned host memory")
+    if src_key_cache.shape[1:] != dst_key_cache.shape[1:] or \
+            src_key_cache.dtype != dst_key_cache.dtype or \
+            src_value_cache.shape != src_key_cache.shape or \
+            dst_value_cache.shape != dst_key_cache.shape:
+        raise InvalidArgument("source and destination pools differ in block layout")
+    src = np.ascontiguousarray(src_blocks, dtype=np.int32).reshape(-1)
+    dst = np.ascontiguousarray(dst_blocks, dtype=np.int32).reshape(-1)
+    if src.shape != dst.shape:
+        raise InvalidArgument("src_blocks and dst_blocks differ in length")
+    gpu = dst_key_cache if dst_key_cache.is_cuda else src_key_cache
+    block_bytes = src_key_cache[0].numel() * src_key_cache.element_size()
+    _check(_lib.pkv_swap_blocks(src_key_cache.data_ptr(), src_value_cache.data_ptr(),
+                                dst_key_cache.data_ptr(), dst_value_cache.data_ptr(), _i32p(src),
+                                _i32p(dst), len(src), src_key_cache.shape[0],
+                                dst_key_cache.shape[0], block_bytes, _stream(gpu)))
 
 
 def paged_attention_decode_partition_size(num_seqs, num_kv_heads, block_size, max_context_len,

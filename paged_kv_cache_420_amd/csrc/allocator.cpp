@@ -45,9 +45,76 @@ int32_t BlockAllocator::release(int64_t seq) {
     return fail(PKV_ERR_NO_SUCH_SEQ, "no sequence %lld",
                 static_cast<long long>(seq));
   // Logical order: a block reaching zero goes on top of the free stack.
-  for (int32_t b : it->second.table)
-    if (--ref_[b] == 0) free_.push_back(b);
+  if (it->second.swapped) {
+    for (int32_t h : it->second.table) {
+      host_ref_[h] = 0;
+      host_free_.push_back(h);
+    }
+  } else {
+    for (int32_t b : it->second.table)
+      if (--ref_[b] == 0) free_.push_back(b);
+  }
   seqs_.erase(it);
+  return ok();
+}
+
+int32_t BlockAllocator::set_host_pool(int32_t num_host_blocks) {
+  if (num_host_blocks < 0) return fail(PKV_ERR_INVALID, "negative host pool size");
+  for (const auto& kv : seqs_)
+    if (kv.second.swapped)
+      return fail(PKV_ERR_INVALID, "sequences are swapped out; the host pool is in use");
+  host_ref_.assign(num_host_blocks, 0);
+  host_free_.clear();
+  for (int32_t h = num_host_blocks - 1; h >= 0; --h) host_free_.push_back(h);
+  return ok();
+}
+
+void BlockAllocator::host_free_stack(int32_t* out) const {
+  int32_t i = 0;
+  for (auto it = host_free_.rbegin(); it != host_free_.rend(); ++it) out[i++] = *it;
+}
+
+int32_t BlockAllocator::swap_out(int64_t seq, std::vector<CowPair>* pairs) {
+  auto it = seqs_.find(seq);
+  if (it == seqs_.end())
+    return fail(PKV_ERR_NO_SUCH_SEQ, "no sequence %lld", static_cast<long long>(seq));
+  Seq& s = it->second;
+  if (s.swapped)
+    return fail(PKV_ERR_INVALID, "sequence %lld is already swapped out",
+                static_cast<long long>(seq));
+  if (s.table.size() > host_free_.size())
+    return fail(PKV_ERR_OUT_OF_BLOCKS, "need %zu host blocks, %zu free", s.table.size(),
+                host_free_.size());
+  for (int32_t& b : s.table) {
+    const int32_t h = host_free_.back();
+    host_free_.pop_back();
+    host_ref_[h] = 1;
+    pairs->push_back({b, h});
+    if (--ref_[b] == 0) free_.push_back(b);
+    b = h;
+  }
+  s.swapped = true;
+  return ok();
+}
+
+int32_t BlockAllocator::swap_in(int64_t seq, std::vector<CowPair>* pairs) {
+  auto it = seqs_.find(seq);
+  if (it == seqs_.end())
+    return fail(PKV_ERR_NO_SUCH_SEQ, "no sequence %lld", static_cast<long long>(seq));
+  Seq& s = it->second;
+  if (!s.swapped)
+    return fail(PKV_ERR_INVALID, "sequence %lld is not swapped out",
+                static_cast<long long>(seq));
+  if (int64_t(s.table.size()) > num_free())
+    return fail(PKV_ERR_OUT_OF_BLOCKS, "need %zu blocks, %d free", s.table.size(), num_free());
+  for (int32_t& h : s.table) {
+    const int32_t b = pop();
+    pairs->push_back({h, b});
+    host_ref_[h] = 0;
+    host_free_.push_back(h);
+    h = b;
+  }
+  s.swapped = false;
   return ok();
 }
 
@@ -59,6 +126,8 @@ int32_t BlockAllocator::fork(int64_t parent, int64_t child) {
   if (has(child))
     return fail(PKV_ERR_SEQ_EXISTS, "child sequence %lld already exists",
                 static_cast<long long>(child));
+  if (it->second.swapped)
+    return fail(PKV_ERR_INVALID, "sequence %lld is swapped out", static_cast<long long>(parent));
   Seq copy = it->second;
   for (int32_t b : copy.table) ++ref_[b];
   seqs_.emplace(child, std::move(copy));
@@ -104,6 +173,7 @@ int64_t BlockAllocator::blocks_for_append(int64_t seq, int32_t n) const {
   auto it = seqs_.find(seq);
   if (it == seqs_.end()) return -1;
   const Seq& s = it->second;
+  if (s.swapped) return -1;
   bool c = false;
   return blocks_needed(s, n, s.table.empty() ? 0 : ref_[s.table.back()], &c);
 }
@@ -116,6 +186,8 @@ int32_t BlockAllocator::append(int64_t seq, int32_t n, int32_t* slots,
                 static_cast<long long>(seq));
   if (n < 0) return fail(PKV_ERR_INVALID, "negative token count %d", n);
   Seq& s = it->second;
+  if (s.swapped)
+    return fail(PKV_ERR_INVALID, "sequence %lld is swapped out", static_cast<long long>(seq));
   bool c = false;
   int32_t last_ref = s.table.empty() ? 0 : ref_[s.table.back()];
   int64_t need = blocks_needed(s, n, last_ref, &c);
@@ -149,6 +221,9 @@ int32_t BlockAllocator::append_batch(const int64_t* seqs,
                   static_cast<long long>(seqs[i]));
     if (counts[i] < 0)
       return fail(PKV_ERR_INVALID, "negative token count %d", counts[i]);
+    if (it->second.swapped)
+      return fail(PKV_ERR_INVALID, "sequence %lld is swapped out",
+                  static_cast<long long>(seqs[i]));
     ptr[i] = &it->second;
   }
   std::sort(ids.begin(), ids.end());

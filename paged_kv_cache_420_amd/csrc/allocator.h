@@ -67,6 +67,23 @@ class BlockAllocator {
   // its lengths; a table longer than max_blocks fails up front.
   // With `changes`, every table entry the batch sets is reported instead
   // (capacity changes_cap, checked up front), plus the lengths in `lens`.
+  // Host tier (swap space): num_host_blocks blocks in a second pool with
+  // its own free stack (0 on top).  A swapped-out sequence keeps its
+  // length and a table of host blocks; it cannot grow, fork or be read by
+  // the device calls until it is swapped back in.
+  int32_t set_host_pool(int32_t num_host_blocks);
+  int32_t num_host_blocks() const { return static_cast<int32_t>(host_ref_.size()); }
+  int32_t num_free_host() const { return static_cast<int32_t>(host_free_.size()); }
+  bool swapped(int64_t seq) const {
+    auto it = seqs_.find(seq);
+    return it != seqs_.end() && it->second.swapped;
+  }
+  void host_free_stack(int32_t* out) const;
+  // Moves every block of `seq` to the host tier: pairs (device block, host
+  // block) in logical order; device blocks are released as by release().
+  int32_t swap_out(int64_t seq, std::vector<CowPair>* pairs);
+  // Back to fresh device blocks: pairs (host block, device block).
+  int32_t swap_in(int64_t seq, std::vector<CowPair>* pairs);
   int32_t append_batch(const int64_t* seqs, const int32_t* counts,
                        int32_t num_seqs, int32_t* slots, int64_t slots_cap,
                        CowPair* cow, int32_t cow_cap, int32_t* n_cow,
@@ -76,8 +93,9 @@ class BlockAllocator {
 
  private:
   struct Seq {
-    std::vector<int32_t> table;
+    std::vector<int32_t> table;  // device blocks, or host blocks when swapped
     int32_t len = 0;
+    bool swapped = false;
   };
   // Blocks `seq` needs to grow by n, given `last_ref` as the current count
   // of its last block; sets *cow when a copy-on-write happens first.
@@ -91,6 +109,8 @@ class BlockAllocator {
   int32_t block_size_;
   std::vector<int32_t> free_;  // stack; top is free_.back()
   std::vector<int32_t> ref_;
+  std::vector<int32_t> host_free_;  // stack; top is host_free_.back()
+  std::vector<char> host_ref_;      // 1 while a swapped sequence holds it
   std::unordered_map<int64_t, Seq> seqs_;
 };
 

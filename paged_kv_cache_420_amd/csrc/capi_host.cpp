@@ -96,6 +96,65 @@ int32_t pkv_seq_fork(pkv_allocator* alloc, int64_t parent, int64_t child) {
   return alloc->impl.fork(parent, child);
 }
 
+int32_t pkv_allocator_set_host_pool(pkv_allocator* alloc, int32_t num_host_blocks) {
+  PKV_REQUIRE(alloc, "allocator is NULL");
+  return alloc->impl.set_host_pool(num_host_blocks);
+}
+
+int32_t pkv_num_free_host_blocks(const pkv_allocator* alloc, int32_t* out) {
+  PKV_REQUIRE(alloc && out, "NULL argument");
+  *out = alloc->impl.num_free_host();
+  return ok();
+}
+
+int32_t pkv_seq_is_swapped(const pkv_allocator* alloc, int64_t seq, int32_t* out) {
+  PKV_REQUIRE(alloc && out, "NULL argument");
+  if (!alloc->impl.has(seq))
+    return fail(PKV_ERR_NO_SUCH_SEQ, "no sequence %lld", static_cast<long long>(seq));
+  *out = alloc->impl.swapped(seq) ? 1 : 0;
+  return ok();
+}
+
+static int32_t swap_call(pkv_allocator* alloc, int64_t seq, int32_t* src_blocks,
+                         int32_t* dst_blocks, int32_t cap, int32_t* n, bool out) {
+  PKV_REQUIRE(alloc && n, "NULL argument");
+  if (!alloc->impl.has(seq))
+    return fail(PKV_ERR_NO_SUCH_SEQ, "no sequence %lld", static_cast<long long>(seq));
+  const size_t need = alloc->impl.table(seq).size();
+  if (int64_t(need) > cap)
+    return fail(PKV_ERR_BUFFER_TOO_SMALL, "sequence holds %zu blocks, capacity %d", need, cap);
+  PKV_REQUIRE(need == 0 || (src_blocks && dst_blocks), "NULL argument");
+  thread_local std::vector<pkv::CowPair> pairs;
+  pairs.clear();
+  int32_t st = out ? alloc->impl.swap_out(seq, &pairs) : alloc->impl.swap_in(seq, &pairs);
+  if (st != PKV_OK) return st;
+  for (size_t i = 0; i < pairs.size(); ++i) {
+    src_blocks[i] = pairs[i].src;
+    dst_blocks[i] = pairs[i].dst;
+  }
+  *n = static_cast<int32_t>(pairs.size());
+  return ok();
+}
+
+int32_t pkv_seq_swap_out(pkv_allocator* alloc, int64_t seq, int32_t* device_blocks,
+                         int32_t* host_blocks, int32_t cap, int32_t* n) {
+  return swap_call(alloc, seq, device_blocks, host_blocks, cap, n, true);
+}
+
+int32_t pkv_seq_swap_in(pkv_allocator* alloc, int64_t seq, int32_t* host_blocks,
+                        int32_t* device_blocks, int32_t cap, int32_t* n) {
+  return swap_call(alloc, seq, host_blocks, device_blocks, cap, n, false);
+}
+
+int32_t pkv_allocator_host_snapshot(const pkv_allocator* alloc, int32_t* host_free_stack,
+                                    int32_t* n_free) {
+  PKV_REQUIRE(alloc && n_free, "NULL argument");
+  *n_free = alloc->impl.num_free_host();
+  PKV_REQUIRE(*n_free == 0 || host_free_stack, "host_free_stack is NULL");
+  alloc->impl.host_free_stack(host_free_stack);
+  return ok();
+}
+
 int32_t pkv_seq_append(pkv_allocator* alloc, int64_t seq, int32_t n,
                        int32_t* slots_out, int32_t* cow_src,
                        int32_t* cow_dst, int32_t* n_cow) {
@@ -275,6 +334,9 @@ int32_t pkv_build_block_tables(const pkv_allocator* alloc,
   for (int32_t i = 0; i < num_seqs; ++i) {
     if (!alloc->impl.has(seqs[i]))
       return fail(PKV_ERR_NO_SUCH_SEQ, "no sequence %lld",
+                  static_cast<long long>(seqs[i]));
+    if (alloc->impl.swapped(seqs[i]))
+      return fail(PKV_ERR_INVALID, "sequence %lld is swapped out",
                   static_cast<long long>(seqs[i]));
     if (static_cast<int64_t>(alloc->impl.table(seqs[i]).size()) > max_blocks)
       return fail(PKV_ERR_BUFFER_TOO_SMALL,

@@ -315,3 +315,42 @@ extern "C" int32_t pkv_paged_kv_append_fp8(
     return fail(PKV_ERR_HIP, "fp8 append launch: %s", hipGetErrorString(e));
   return ok();
 }
+
+extern "C" int32_t pkv_swap_blocks(const void* src_key_cache, const void* src_value_cache,
+                                   void* dst_key_cache, void* dst_value_cache,
+                                   const int32_t* src_blocks, const int32_t* dst_blocks,
+                                   int32_t num_pairs, int32_t src_num_blocks,
+                                   int32_t dst_num_blocks, int64_t block_bytes, void* stream) {
+  if (num_pairs < 0) return fail(PKV_ERR_INVALID, "negative num_pairs %d", num_pairs);
+  if (num_pairs == 0) return ok();
+  if (!src_key_cache || !src_value_cache || !dst_key_cache || !dst_value_cache ||
+      !src_blocks || !dst_blocks)
+    return fail(PKV_ERR_INVALID, "NULL pointer argument");
+  if (block_bytes <= 0 || src_num_blocks <= 0 || dst_num_blocks <= 0)
+    return fail(PKV_ERR_INVALID, "sizes must be positive");
+  for (int32_t i = 0; i < num_pairs; ++i)
+    if (src_blocks[i] < 0 || src_blocks[i] >= src_num_blocks || dst_blocks[i] < 0 ||
+        dst_blocks[i] >= dst_num_blocks)
+      return fail(PKV_ERR_INVALID, "pair %d (%d -> %d) outside the pools", i, src_blocks[i],
+                  dst_blocks[i]);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const auto* sk = static_cast<const uint8_t*>(src_key_cache);
+  const auto* sv = static_cast<const uint8_t*>(src_value_cache);
+  auto* dk = static_cast<uint8_t*>(dst_key_cache);
+  auto* dv = static_cast<uint8_t*>(dst_value_cache);
+  // runs of pairs consecutive on both sides move as one copy
+  for (int32_t i = 0; i < num_pairs;) {
+    int32_t j = i + 1;
+    while (j < num_pairs && src_blocks[j] == src_blocks[j - 1] + 1 &&
+           dst_blocks[j] == dst_blocks[j - 1] + 1)
+      ++j;
+    const int64_t off_s = int64_t(src_blocks[i]) * block_bytes;
+    const int64_t off_d = int64_t(dst_blocks[i]) * block_bytes;
+    const size_t bytes = size_t(j - i) * size_t(block_bytes);
+    hipError_t e = hipMemcpyAsync(dk + off_d, sk + off_s, bytes, hipMemcpyDefault, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(dv + off_d, sv + off_s, bytes, hipMemcpyDefault, s);
+    if (e != hipSuccess) return fail(PKV_ERR_HIP, "swap copy: %s", hipGetErrorString(e));
+    i = j;
+  }
+  return ok();
+}

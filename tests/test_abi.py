@@ -147,15 +147,18 @@ def _live(a):
 def _state(a, seqs):
     if isinstance(a, RefAllocator):
         free, ref, tables = a.snapshot()
-        return free, ref, {s: tables[s] for s in seqs if s in tables}
+        return (free, ref, {s: tables[s] for s in seqs if s in tables},
+                sorted(q for q in a.swapped if q in seqs), a.host_free_stack())
     free, ref = a.snapshot()
-    tables = {}
+    tables, swapped = {}, []
     for s in seqs:
         try:
             tables[s] = (a.block_table(s), a.seq_len(s))
+            if a.is_swapped(s):
+                swapped.append(s)
         except pkv.NoSuchSequence:
             pass
-    return free, ref, tables
+    return free, ref, tables, swapped, a.host_snapshot()
 
 
 def test_hand_worked_trace_through_the_c_abi():
@@ -186,18 +189,22 @@ def test_hand_worked_trace_through_the_c_abi():
 
 ops = st.lists(
     st.tuples(st.sampled_from(["add", "append", "fork", "free", "batch", "batch_tables",
-                               "batch_changes"]),
+                               "batch_changes", "swap_out", "swap_in"]),
               st.integers(0, 5), st.integers(0, 5), st.integers(0, 23)),
     min_size=1, max_size=80)
 
 
 @settings(max_examples=300, deadline=None)
-@given(ops, st.integers(1, 8), st.integers(1, 24), st.randoms(use_true_random=False))
-def test_native_allocator_matches_reference_bit_for_bit(seq_ops, block_size, num_blocks, rnd):
+@given(ops, st.integers(1, 8), st.integers(1, 24), st.integers(0, 16),
+       st.randoms(use_true_random=False))
+def test_native_allocator_matches_reference_bit_for_bit(seq_ops, block_size, num_blocks,
+                                                        host_blocks, rnd):
     order = list(range(num_blocks))
     rnd.shuffle(order)
     ref = RefAllocator(num_blocks, block_size, order)
     nat = pkv.BlockAllocator(num_blocks, block_size, order)
+    ref.set_host_pool(host_blocks)
+    nat.set_host_pool(host_blocks)
     ids = range(6)
     for op, s, t, n in seq_ops:
         def apply(a, is_ref):
@@ -211,6 +218,9 @@ def test_native_allocator_matches_reference_bit_for_bit(seq_ops, block_size, num
                 elif op == "append":
                     slots, pairs = a.append(s, n)
                     return ("ok", list(slots), [tuple(p) for p in pairs])
+                elif op in ("swap_out", "swap_in"):
+                    pairs = getattr(a, op)(s)
+                    return ("ok", [tuple(int(x) for x in p) for p in pairs])
                 elif op == "batch_changes":
                     # the reported entries turn the old tables into the new ones
                     batch = sorted({s, t, (s + 3) % 6})
@@ -238,8 +248,10 @@ def test_native_allocator_matches_reference_bit_for_bit(seq_ops, block_size, num
                     counts = [(n + 5 * i) % 9 for i in range(len(batch))]
                     mb = 1 + n % 6
                     if is_ref:
-                        for q in batch:
-                            a.length(q)  # KeyError for an unknown sequence
+                        for q in batch:  # each sequence in batch order:
+                            a.length(q)  # KeyError for an unknown one,
+                            if q in a.swapped:  # then swapped out
+                                raise ValueError("swapped out")
                         if any(-(-(a.length(q) + c) // block_size) > mb
                                for q, c in zip(batch, counts)):
                             return ("too_small",)
@@ -268,8 +280,9 @@ def test_native_allocator_matches_reference_bit_for_bit(seq_ops, block_size, num
         r2 = apply(nat, False)
         assert r1 == r2, (op, s, t, n)
         assert _state(ref, ids) == _state(nat, ids)
-    tables_r, lens_r = ref.build_tables([i for i in ids if i in ref.tables], 30)
-    tables_n, lens_n = nat.build_block_tables([i for i in ids if i in ref.tables], 30)
+    live = [i for i in ids if i in ref.tables and i not in ref.swapped]
+    tables_r, lens_r = ref.build_tables(live, 30)
+    tables_n, lens_n = nat.build_block_tables(live, 30)
     assert np.array_equal(np.array(tables_r, dtype=np.int32).reshape(tables_n.shape), tables_n)
     assert list(lens_r) == lens_n.tolist()
     nat.close()
@@ -325,3 +338,26 @@ def test_prepared_append_tables_repeats_the_call():
             break
     assert before == (a.snapshot(), [a.block_table(q) for q in seqs],
                       [a.seq_len(q) for q in seqs])
+
+
+def test_swap_walkthrough_through_the_c_abi():
+    """The hand-worked swap walkthrough of the oracle tests, natively."""
+    from test_oracle_allocator import _swap_walkthrough
+    a = pkv.BlockAllocator(4, 2)
+    ids = {"A": 1, "B": 2}
+
+    class Named:  # the walkthrough names sequences by letter
+        def __getattr__(self, name):
+            f = getattr(a, name)
+            return lambda *args: f(*[ids.get(x, x) if isinstance(x, str) else x for x in args])
+
+        def set_host_pool(self, n):
+            a.set_host_pool(n)
+
+    _swap_walkthrough(Named())
+    free, ref = a.snapshot()
+    assert free == [1, 0] and ref == [0, 0, 1, 1]
+    assert a.block_table(1) == [2, 3] and a.seq_len(1) == 3
+    assert a.host_snapshot() == [1, 0, 2]
+    assert not a.is_swapped(1)
+    a.close()

@@ -84,3 +84,59 @@ def test_copy_blocks_is_exact_and_skips_bad_pairs():
     from oracle import copy_blocks
     copy_blocks(ko, vo, [1, 4], [0, 5])
     assert np.array_equal(kc.cpu().numpy(), ko) and np.array_equal(vc.cpu().numpy(), vo)
+
+
+@pytest.mark.parametrize("dtype_name", ["llama7b_small", "llama13b_small"])
+def test_swap_out_and_in_restores_every_byte(dtype_name):
+    """Swap a sequence to a pinned host pool, let another sequence reuse its
+    device blocks, swap it back into other blocks: the host pool holds the
+    oracle's values for the swapped blocks, and decode of the sequence is
+    bitwise what it was before (fixed partition size, so the result does
+    not depend on the batch)."""
+    w = SMALL[dtype_name]
+    p = workloads.plan(w)
+    g = GpuState(w, p)
+    o = OracleState(w, p)
+    host_blocks = 64
+    a = g.alloc
+    a.set_host_pool(host_blocks)
+    shape = (host_blocks, w.num_kv_heads, w.block_size, w.head_dim)
+    hk = torch.full(shape, float("nan"), dtype=w.dtype).pin_memory()
+    hv = torch.full(shape, float("nan"), dtype=w.dtype).pin_memory()
+    victim = int(np.argmax(p.lens))              # the longest sequence
+    seq = p.seqs[victim]
+    q = torch.from_numpy(np.stack([workloads.decode_query(w, s) for s in p.seqs])).to(w.dtype)
+    qd = q.to(DEV)
+
+    def decode_one(s, row):
+        t, l = a.build_block_tables([s], 64)
+        out = pkv.paged_attention_decode(qd[row:row + 1].contiguous(), g.kc, g.vc,
+                                         torch.from_numpy(t.copy()).to(DEV),
+                                         torch.from_numpy(l.copy()).to(DEV), w.scale,
+                                         int(l[0]), partition_size=128)
+        return out.cpu()
+
+    before = decode_one(seq, victim)
+    dev_table = a.block_table(seq)
+    pairs = a.swap_out(seq)
+    assert [int(x) for x in pairs[:, 0]] == dev_table and a.is_swapped(seq)
+    pkv.swap_blocks(g.kc, g.vc, hk, hv, pairs[:, 0], pairs[:, 1])
+    torch.cuda.synchronize()
+    # the host pool holds exactly the oracle's blocks
+    for d, h in pairs.tolist():
+        assert np.array_equal(hk[h].to(torch.float64).numpy(), o.kc[d], equal_nan=True)
+        assert np.array_equal(hv[h].to(torch.float64).numpy(), o.vc[d], equal_nan=True)
+    # another sequence takes the freed blocks and overwrites them
+    a.add(999)
+    n_new = len(dev_table) * w.block_size
+    slots, _ = a.append(999, n_new)
+    junk = torch.full((n_new, w.num_kv_heads, w.head_dim), 7.0, dtype=w.dtype, device=DEV)
+    pkv.paged_kv_append(junk, junk, g.kc, g.vc, torch.from_numpy(slots).to(DEV))
+    assert set(a.block_table(999)) & set(dev_table)
+    back = a.swap_in(seq)
+    assert [int(x) for x in back[:, 0]] == [int(x) for x in pairs[:, 1]]
+    assert not set(int(x) for x in back[:, 1]) & set(a.block_table(999))
+    pkv.swap_blocks(hk, hv, g.kc, g.vc, back[:, 0], back[:, 1])
+    after = decode_one(seq, victim)
+    assert torch.equal(before, after)
+    log(dtype_name, "swapped", len(pairs), "blocks; decode bitwise equal")

@@ -189,3 +189,50 @@ def test_random_ops_keep_invariants(seq_ops, block_size, num_blocks, rnd):
         except (OutOfBlocks, KeyError, ValueError):
             assert a.snapshot() == before
         check_invariants(a)
+
+
+def _swap_walkthrough(a):
+    """Worked by hand (device pool 4 blocks, block 0 first; block size 2;
+    host pool 3 blocks, host block 0 first): a sequence shared by a fork is
+    swapped out and back while its sibling grows."""
+    a.set_host_pool(3)
+    a.add("A")
+    slots, _ = a.append("A", 3)
+    assert list(slots) == [0, 1, 2]                      # blocks 0, 1
+    a.fork("A", "B")                                     # both hold [0, 1]
+    assert [tuple(int(x) for x in p) for p in a.swap_out("A")] == [(0, 0), (1, 1)]
+    # A's host blocks 0, 1; device blocks stay with B (counts back to 1)
+    slots, pairs = a.append("B", 1)
+    assert list(slots) == [3] and len(pairs) == 0         # no longer shared: no copy
+    assert [tuple(int(x) for x in p) for p in a.swap_in("A")] == [(0, 2), (1, 3)]
+    a.free("B")                                          # pushes 0 then 1
+
+
+def test_swap_walkthrough_worked_by_hand():
+    a = RefAllocator(4, 2)
+    _swap_walkthrough(a)
+    free, ref, tables = a.snapshot()
+    assert free == [1, 0] and ref == [0, 0, 1, 1]
+    assert tables == {"A": ([2, 3], 3)}
+    assert a.host_free_stack() == [1, 0, 2]
+
+
+def test_swapped_sequence_is_frozen_and_frees_host_blocks():
+    a = RefAllocator(6, 2)
+    a.set_host_pool(2)
+    a.add(1)
+    a.append(1, 4)                                       # blocks 0, 1
+    a.add(3)
+    a.append(3, 5)                                       # blocks 2, 3, 4
+    before = a.snapshot()
+    with pytest.raises(OutOfBlocks):
+        a.swap_out(3)                                    # 3 blocks, host pool of 2
+    assert a.snapshot() == before and a.host_free_stack() == [0, 1]
+    a.swap_out(1)
+    assert a.free_stack() == [1, 0, 5]
+    for bad in (lambda: a.append(1, 1), lambda: a.fork(1, 9), lambda: a.build_tables([1], 4),
+                lambda: a.append_batch([1], [1]), lambda: a.swap_out(1)):
+        with pytest.raises(ValueError):
+            bad()
+    a.free(1)
+    assert a.host_free_stack() == [1, 0] and 1 not in a.tables
