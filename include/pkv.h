@@ -274,9 +274,15 @@ int32_t pkv_allocator_host_snapshot(const pkv_allocator* alloc,
  *      request whose prompt is done, while the step's token budget
  *      (max_num_batched_tokens) lasts.  If the append needs more blocks
  *      than are free, the youngest running request without a row in this
- *      step is preempted -- its blocks freed, its generated tokens added to
- *      its prompt, its progress reset -- and put back at the head of the
- *      queue, until the append fits or the request itself was preempted;
+ *      step is preempted and put back at the head of the queue, until the
+ *      append fits or the request itself was preempted.  Preemption swaps
+ *      the request's blocks to the host tier when it has room for them
+ *      (progress kept; KV-cache article §4.2, swap space), else recomputes
+ *      (blocks freed, generated tokens added to the prompt, progress
+ *      reset).  A swapped request at the head of the queue is admitted
+ *      when the free blocks cover its blocks + the running requests'
+ *      unfinished prompt blocks + one per running request, and swapped
+ *      back in;
  *   4. prefill chunks, oldest first: min(P - prefilled, chunk_size,
  *      budget left) tokens; if they do not fit, younger requests without a
  *      row are preempted as above; if that is not enough the chunk and all
@@ -294,13 +300,14 @@ typedef struct pkv_scheduler pkv_scheduler;
  * pkv_allocator_create (NULL = 0..num_blocks-1); max_num_seqs running
  * requests at most; max_num_batched_tokens rows per step; chunk_size prompt
  * tokens per prefill chunk; reserve_tokens 0 for paged admission, else the
- * per-request reservation of the reservation model. */
+ * per-request reservation of the reservation model; host_blocks the swap
+ * space (host tier blocks; 0: preemption always recomputes). */
 int32_t pkv_scheduler_create(int32_t num_blocks, int32_t block_size,
                              const int32_t* init_free_order,
                              int32_t max_num_seqs,
                              int32_t max_num_batched_tokens,
                              int32_t chunk_size, int32_t reserve_tokens,
-                             pkv_scheduler** out);
+                             int32_t host_blocks, pkv_scheduler** out);
 void pkv_scheduler_destroy(pkv_scheduler* sched);
 
 /* Queue a request (prompt_len >= 1, output_len >= 1 decode steps).
@@ -337,10 +344,24 @@ int32_t pkv_scheduler_last_events(const pkv_scheduler* sched,
                                   int32_t preempted_cap,
                                   int32_t* num_preempted);
 
-/* out[9]: steps, running, waiting, finished (total), preemptions (total),
+/* Block moves of the last step, for pkv_swap_blocks: swap-ins (host block
+ * in_host[i] -> device block in_device[i], made at admission) and
+ * swap-outs (device out_device[i] -> host out_host[i], made by
+ * preemption).  Run the swap-in copies, then the swap-out copies, before
+ * the step's append and attention: a swap-out's device blocks may be
+ * written by this step's appends, and a host block a swap-in released
+ * may be taken by a swap-out of the same step.  Counts are always
+ * written; BUFFER_TOO_SMALL if a capacity is short. */
+int32_t pkv_scheduler_last_swaps(const pkv_scheduler* sched, int32_t* in_host,
+                                 int32_t* in_device, int32_t in_cap,
+                                 int32_t* num_in, int32_t* out_device,
+                                 int32_t* out_host, int32_t out_cap,
+                                 int32_t* num_out);
+
+/* out[11]: steps, running, waiting, finished (total), preemptions (total),
  * cached tokens of the running requests, slots their blocks hold, slots
  * reserved for them (reservation model; else = the slots held), free
- * blocks. */
+ * blocks, swap-outs (total), swap-ins (total). */
 int32_t pkv_scheduler_stats(const pkv_scheduler* sched, int64_t* out);
 
 /* ======================================================================

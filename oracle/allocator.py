@@ -135,6 +135,9 @@ class RefAllocator:
         self.num_host_blocks = num_host_blocks
         self._host_free = list(reversed(range(num_host_blocks)))
 
+    def num_free_host(self):
+        return len(self._host_free)
+
     def host_free_stack(self):
         return list(reversed(self._host_free))
 

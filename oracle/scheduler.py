@@ -35,6 +35,12 @@ which the native scheduler must reproduce step for step):
   still does not fit, prefill stops for this step.
 * Rows are reported decode rows first, then chunks: (id, query length,
   context length after the step, block table), plus the slots in row order.
+* With a host tier (KV-cache article §4.2: swap space in host memory), a
+  preempted request whose blocks fit the tier's free blocks is swapped out
+  instead (its progress kept; pairs device -> host reported); when such a
+  request heads the queue it is admitted if the free blocks cover its own
+  blocks plus the running requests' pending prompt blocks plus one per
+  running request, and swapped back in (pairs host -> device).
 
 Parity pins: tests/test_oracle_scheduler.py replays hand-worked traces
 (tests/golden/scheduler_traces.json) and checks invariants (budget, cap,
@@ -57,12 +63,17 @@ class _Req:
         self.id, self.prompt, self.output = rid, prompt, output
         self.prefilled = 0
         self.generated = 0
+        self.swapped = False
 
 
 class RefScheduler:
     def __init__(self, num_blocks, block_size, max_num_seqs, max_num_batched_tokens, chunk_size,
-                 reserve_tokens=0, init_order=None):
+                 reserve_tokens=0, init_order=None, host_blocks=0):
         self.alloc = RefAllocator(num_blocks, block_size, init_order)
+        self.alloc.set_host_pool(host_blocks)
+        self.host_blocks = host_blocks
+        self.total_swapped_out = 0
+        self.total_swapped_in = 0
         self.num_blocks, self.block_size = num_blocks, block_size
         self.max_num_seqs = max_num_seqs
         self.budget = max_num_batched_tokens
@@ -96,20 +107,26 @@ class RefScheduler:
         for x in self.running:
             if x.prefilled < x.prompt:
                 pending += _cdiv(x.prompt, self.block_size) - len(self.alloc.tables[x.id])
-        need = _cdiv(r.prompt, self.block_size) + pending + len(self.running)
+        own = len(self.alloc.tables[r.id]) if r.swapped else _cdiv(r.prompt, self.block_size)
+        need = own + pending + len(self.running)
         return self.alloc.num_free() >= need
 
-    def _preempt_youngest(self, candidates, has_row, preempted):
+    def _preempt_youngest(self, candidates, has_row, preempted, swap_out):
         """Preempt the youngest request in `candidates` (a list of running
         requests, oldest first) without a row this step; return it or None."""
         for r in reversed(candidates):
             if r.id in has_row:
                 continue
-            self.alloc.free(r.id)
+            if self.host_blocks and len(self.alloc.tables[r.id]) <= self.alloc.num_free_host():
+                swap_out += self.alloc.swap_out(r.id)
+                r.swapped = True
+                self.total_swapped_out += 1
+            else:
+                self.alloc.free(r.id)
+                r.prompt += r.generated
+                r.output -= r.generated
+                r.prefilled = r.generated = 0
             self.running.remove(r)
-            r.prompt += r.generated
-            r.output -= r.generated
-            r.prefilled = r.generated = 0
             self.waiting.appendleft(r)
             preempted.append(r.id)
             self.total_preempted += 1
@@ -120,7 +137,7 @@ class RefScheduler:
         """Returns a dict: rows [(id, qlen, ctx, table)], num_decode, slots,
         finished, preempted."""
         self.steps += 1
-        finished, preempted = [], []
+        finished, preempted, swap_in, swap_out = [], [], [], []
         # 1. retire
         for r in list(self.running):
             if r.generated == r.output:
@@ -131,7 +148,12 @@ class RefScheduler:
         # 2. admit
         while self.waiting and self._admissible(self.waiting[0]):
             r = self.waiting.popleft()
-            self.alloc.add(r.id)
+            if r.swapped:
+                swap_in += self.alloc.swap_in(r.id)
+                r.swapped = False
+                self.total_swapped_in += 1
+            else:
+                self.alloc.add(r.id)
             self.running.append(r)
         budget = self.budget
         rows, slots, has_row = [], [], set()
@@ -147,7 +169,8 @@ class RefScheduler:
                     got, _ = self.alloc.append(r.id, 1)
                 except OutOfBlocks:
                     idx = self.running.index(r)
-                    victim = self._preempt_youngest(self.running[idx:], has_row, preempted)
+                    victim = self._preempt_youngest(self.running[idx:], has_row, preempted,
+                                                    swap_out)
                     if victim is r:
                         break
             if got is None:
@@ -171,7 +194,8 @@ class RefScheduler:
                     got, _ = self.alloc.append(r.id, c)
                 except OutOfBlocks:
                     idx = self.running.index(r)
-                    if self._preempt_youngest(self.running[idx + 1:], has_row, preempted) is None:
+                    if self._preempt_youngest(self.running[idx + 1:], has_row, preempted,
+                                              swap_out) is None:
                         break
             if got is None:
                 break
@@ -181,7 +205,7 @@ class RefScheduler:
             has_row.add(r.id)
             budget -= c
         return {"rows": rows, "num_decode": num_decode, "slots": slots, "finished": finished,
-                "preempted": preempted}
+                "preempted": preempted, "swap_in": swap_in, "swap_out": swap_out}
 
     def stats(self):
         bs = self.block_size
@@ -191,4 +215,5 @@ class RefScheduler:
         return {"steps": self.steps, "running": len(self.running), "waiting": len(self.waiting),
                 "finished": self.total_finished, "preemptions": self.total_preempted,
                 "cached_tokens": cached, "allocated_slots": held, "reserved_slots": reserved,
-                "free_blocks": self.alloc.num_free()}
+                "free_blocks": self.alloc.num_free(), "swapped_out": self.total_swapped_out,
+                "swapped_in": self.total_swapped_in}

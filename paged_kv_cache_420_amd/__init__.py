@@ -141,7 +141,9 @@ _SIGNATURES = {
                                                        _I32, _I32, _I32, _I32, ctypes.c_float,
                                                        ctypes.c_float, ctypes.c_float, _I32, _P,
                                                        _P, ctypes.c_size_t, _I32, _P]),
-    "pkv_scheduler_create": (_I32, [_I32, _I32, _P, _I32, _I32, _I32, _I32, ctypes.POINTER(_P)]),
+    "pkv_scheduler_create": (_I32, [_I32, _I32, _P, _I32, _I32, _I32, _I32, _I32,
+                                    ctypes.POINTER(_P)]),
+    "pkv_scheduler_last_swaps": (_I32, [_P, _P, _P, _I32, _P, _P, _P, _I32, _P]),
     "pkv_scheduler_destroy": (None, [_P]),
     "pkv_scheduler_add_request": (_I32, [_P, _I64, _I32, _I32]),
     "pkv_scheduler_max_blocks": (_I32, [_P, _P]),
@@ -478,7 +480,7 @@ class StepPlan:
     its next step."""
 
     def __init__(self, seq_ids, query_lens, context_lens, slots, block_tables, num_decode,
-                 finished, preempted):
+                 finished, preempted, swap_in=None, swap_out=None):
         self.seq_ids = seq_ids
         self.query_lens = query_lens
         self.context_lens = context_lens
@@ -487,6 +489,9 @@ class StepPlan:
         self.num_decode = num_decode
         self.finished = finished
         self.preempted = preempted
+        # int32 [n, 2]: (host, device) block pairs to copy in, (device, host) out
+        self.swap_in = np.zeros((0, 2), np.int32) if swap_in is None else swap_in
+        self.swap_out = np.zeros((0, 2), np.int32) if swap_out is None else swap_out
 
     @property
     def num_rows(self):
@@ -502,14 +507,14 @@ class StepPlan:
 
 
 _STAT_NAMES = ("steps", "running", "waiting", "finished", "preemptions", "cached_tokens",
-               "allocated_slots", "reserved_slots", "free_blocks")
+               "allocated_slots", "reserved_slots", "free_blocks", "swapped_out", "swapped_in")
 
 
 class Scheduler:
     """Continuous-batching step scheduler (pkv_scheduler_*; policy in pkv.h)."""
 
     def __init__(self, num_blocks, block_size, max_num_seqs, max_num_batched_tokens, chunk_size,
-                 reserve_tokens=0, init_free_order=None):
+                 reserve_tokens=0, init_free_order=None, host_blocks=0):
         self._h = _P()
         order = None
         if init_free_order is not None:
@@ -519,7 +524,10 @@ class Scheduler:
         _check(_lib.pkv_scheduler_create(num_blocks, block_size,
                                          None if order is None else order.ctypes.data,
                                          max_num_seqs, max_num_batched_tokens, chunk_size,
-                                         reserve_tokens, ctypes.byref(self._h)))
+                                         reserve_tokens, host_blocks, ctypes.byref(self._h)))
+        self.num_blocks, self.host_blocks = num_blocks, host_blocks
+        cap = max(1, num_blocks, host_blocks)
+        self._swaps = [np.empty(cap, dtype=np.int32) for _ in range(4)]
         self.max_num_seqs = max_num_seqs
         self.max_num_batched_tokens = max_num_batched_tokens
         self._ids = np.empty(max_num_seqs, dtype=np.int64)
@@ -530,7 +538,7 @@ class Scheduler:
         self._pre = np.empty(max_num_seqs, dtype=np.int64)
         self._tables = np.empty(0, dtype=np.int32)
         self._counts = np.empty(3, dtype=np.int32)
-        self._stats = np.empty(9, dtype=np.int64)
+        self._stats = np.empty(11, dtype=np.int64)
 
     def close(self):
         if getattr(self, "_h", None) and _lib is not None:
@@ -566,8 +574,16 @@ class Scheduler:
                                               ctypes.byref(nf), self._pre.ctypes.data,
                                               len(self._pre), ctypes.byref(npre)))
         tables = self._tables[:self.max_num_seqs * mb].reshape(self.max_num_seqs, mb)[:nr]
+        ih, idv, od, oh = self._swaps
+        ni, no = _I32(), _I32()
+        _check(_lib.pkv_scheduler_last_swaps(self._h, ih.ctypes.data, idv.ctypes.data, len(ih),
+                                             ctypes.byref(ni), od.ctypes.data, oh.ctypes.data,
+                                             len(od), ctypes.byref(no)))
+        swap_in = np.stack([ih[:ni.value], idv[:ni.value]], axis=1)
+        swap_out = np.stack([od[:no.value], oh[:no.value]], axis=1)
         return StepPlan(self._ids[:nr], self._qlen[:nr], self._ctx[:nr], self._slots[:nt], tables,
-                        nd, self._fin[:nf.value].tolist(), self._pre[:npre.value].tolist())
+                        nd, self._fin[:nf.value].tolist(), self._pre[:npre.value].tolist(),
+                        swap_in, swap_out)
 
     def stats(self):
         _check(_lib.pkv_scheduler_stats(self._h, self._stats.ctypes.data))

@@ -18,16 +18,18 @@ extern "C" {
 int32_t pkv_scheduler_create(int32_t num_blocks, int32_t block_size,
                              const int32_t* init_free_order, int32_t max_num_seqs,
                              int32_t max_num_batched_tokens, int32_t chunk_size,
-                             int32_t reserve_tokens, pkv_scheduler** out) {
+                             int32_t reserve_tokens, int32_t host_blocks,
+                             pkv_scheduler** out) {
   if (!out) return fail(PKV_ERR_INVALID, "out is NULL");
   *out = nullptr;
   if (num_blocks <= 0 || block_size <= 0 || max_num_seqs <= 0 || max_num_batched_tokens <= 0 ||
-      chunk_size <= 0 || reserve_tokens < 0)
+      chunk_size <= 0 || reserve_tokens < 0 || host_blocks < 0)
     return fail(PKV_ERR_INVALID,
                 "sizes must be positive (num_blocks %d, block_size %d, max_num_seqs %d, "
-                "max_num_batched_tokens %d, chunk_size %d) and reserve_tokens >= 0 (%d)",
+                "max_num_batched_tokens %d, chunk_size %d), reserve_tokens (%d) and "
+                "host_blocks (%d) >= 0",
                 num_blocks, block_size, max_num_seqs, max_num_batched_tokens, chunk_size,
-                reserve_tokens);
+                reserve_tokens, host_blocks);
   if (int64_t(num_blocks) * block_size >= (int64_t(1) << 31))
     return fail(PKV_ERR_INVALID, "num_blocks * block_size must be below 2^31");
   std::vector<int32_t> order(num_blocks);
@@ -45,7 +47,7 @@ int32_t pkv_scheduler_create(int32_t num_blocks, int32_t block_size,
     for (int32_t i = 0; i < num_blocks; ++i) order[i] = i;
   }
   pkv::SchedulerConfig cfg{num_blocks, block_size, max_num_seqs, max_num_batched_tokens,
-                           chunk_size, reserve_tokens};
+                           chunk_size, reserve_tokens, host_blocks};
   auto* s = new (std::nothrow) pkv_scheduler{pkv::Scheduler(cfg, order)};
   if (!s) return fail(PKV_ERR_INVALID, "out of host memory");
   *out = s;
@@ -119,6 +121,30 @@ int32_t pkv_scheduler_last_events(const pkv_scheduler* s, int64_t* finished,
   return ok();
 }
 
+int32_t pkv_scheduler_last_swaps(const pkv_scheduler* s, int32_t* in_host, int32_t* in_device,
+                                 int32_t in_cap, int32_t* num_in, int32_t* out_device,
+                                 int32_t* out_host, int32_t out_cap, int32_t* num_out) {
+  if (!s || !num_in || !num_out) return fail(PKV_ERR_INVALID, "NULL argument");
+  const auto& a = s->impl.swap_in_pairs();
+  const auto& b = s->impl.swap_out_pairs();
+  *num_in = static_cast<int32_t>(a.size());
+  *num_out = static_cast<int32_t>(b.size());
+  if (int64_t(a.size()) > in_cap || int64_t(b.size()) > out_cap)
+    return fail(PKV_ERR_BUFFER_TOO_SMALL, "%zu swap-in and %zu swap-out pairs", a.size(),
+                b.size());
+  if ((!a.empty() && (!in_host || !in_device)) || (!b.empty() && (!out_device || !out_host)))
+    return fail(PKV_ERR_INVALID, "NULL argument");
+  for (size_t i = 0; i < a.size(); ++i) {
+    in_host[i] = a[i].src;
+    in_device[i] = a[i].dst;
+  }
+  for (size_t i = 0; i < b.size(); ++i) {
+    out_device[i] = b[i].src;
+    out_host[i] = b[i].dst;
+  }
+  return ok();
+}
+
 int32_t pkv_scheduler_stats(const pkv_scheduler* s, int64_t* out) {
   if (!s || !out) return fail(PKV_ERR_INVALID, "NULL argument");
   const pkv::Scheduler& k = s->impl;
@@ -131,6 +157,8 @@ int32_t pkv_scheduler_stats(const pkv_scheduler* s, int64_t* out) {
   out[6] = k.allocated_slots();
   out[7] = k.reserved_slots();
   out[8] = k.allocator().num_free();
+  out[9] = k.total_swapped_out();
+  out[10] = k.total_swapped_in();
   return ok();
 }
 

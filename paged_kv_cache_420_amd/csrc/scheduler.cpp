@@ -13,7 +13,9 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 }  // namespace
 
 Scheduler::Scheduler(const SchedulerConfig& cfg, const std::vector<int32_t>& order)
-    : cfg_(cfg), alloc_(cfg.num_blocks, cfg.block_size, order) {}
+    : cfg_(cfg), alloc_(cfg.num_blocks, cfg.block_size, order) {
+  alloc_.set_host_pool(cfg.host_blocks);
+}
 
 int32_t Scheduler::reserve_blocks() const {
   return static_cast<int32_t>(cdiv(cfg_.reserve_tokens, cfg_.block_size));
@@ -47,7 +49,9 @@ bool Scheduler::admissible(const Request& r) const {
   // blocks for its whole prompt, plus the prompt blocks the running
   // requests still have to take, plus one per running request (what their
   // next decode rows may take)
-  int64_t need = cdiv(r.prompt, cfg_.block_size) + run;
+  // (a swapped-out request needs its blocks back instead of its prompt's)
+  int64_t need = (r.swapped ? int64_t(alloc_.table(r.id).size())
+                            : cdiv(r.prompt, cfg_.block_size)) + run;
   for (const Request& x : running_)
     if (x.prefilled < x.prompt)
       need += cdiv(x.prompt, cfg_.block_size) - int64_t(alloc_.table(x.id).size());
@@ -58,12 +62,19 @@ int32_t Scheduler::preempt_youngest(int32_t min_index) {
   for (int32_t j = running() - 1; j >= min_index; --j) {
     if (has_row_[j]) continue;
     Request v = running_[j];
-    alloc_.release(v.id);
-    // recompute: the tokens it generated become part of what it prefills
-    v.prompt += v.generated;
-    v.output -= v.generated;
-    v.prefilled = 0;
-    v.generated = 0;
+    if (cfg_.host_blocks > 0 &&
+        int64_t(alloc_.table(v.id).size()) <= alloc_.num_free_host()) {
+      alloc_.swap_out(v.id, &swap_out_);
+      v.swapped = true;
+      ++total_swap_out_;
+    } else {
+      alloc_.release(v.id);
+      // recompute: the tokens it generated become part of what it prefills
+      v.prompt += v.generated;
+      v.output -= v.generated;
+      v.prefilled = 0;
+      v.generated = 0;
+    }
     running_.erase(running_.begin() + j);
     has_row_.erase(has_row_.begin() + j);
     waiting_.push_front(v);
@@ -88,6 +99,8 @@ void Scheduler::step() {
   slots_.clear();
   finished_.clear();
   preempted_.clear();
+  swap_in_.clear();
+  swap_out_.clear();
   num_decode_ = 0;
   ++steps_;
 
@@ -110,7 +123,13 @@ void Scheduler::step() {
   while (!waiting_.empty() && admissible(waiting_.front())) {
     Request r = waiting_.front();
     waiting_.pop_front();
-    alloc_.add(r.id);
+    if (r.swapped) {
+      alloc_.swap_in(r.id, &swap_in_);
+      r.swapped = false;
+      ++total_swap_in_;
+    } else {
+      alloc_.add(r.id);
+    }
     running_.push_back(r);
   }
   has_row_.assign(running_.size(), false);

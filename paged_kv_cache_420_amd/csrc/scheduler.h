@@ -27,6 +27,7 @@ struct SchedulerConfig {
   int32_t max_num_batched_tokens;
   int32_t chunk_size;
   int32_t reserve_tokens;  // 0: admit on free blocks; > 0: reservation model
+  int32_t host_blocks;     // swap space for preempted requests (0: recompute only)
 };
 
 struct Request {
@@ -35,6 +36,7 @@ struct Request {
   int32_t output;     // decode steps still to run before the request finishes
   int32_t prefilled = 0;
   int32_t generated = 0;
+  bool swapped = false;  // its blocks are in the host tier
 };
 
 // One scheduled row: a decode row (1 token) or a prefill chunk.
@@ -66,6 +68,12 @@ class Scheduler {
   const std::vector<int32_t>& slots() const { return slots_; }
   const std::vector<int64_t>& finished() const { return finished_; }
   const std::vector<int64_t>& preempted() const { return preempted_; }
+  // This step's block moves: host -> device (swap-ins at admission) and
+  // device -> host (swap-outs of preempted requests).
+  const std::vector<CowPair>& swap_in_pairs() const { return swap_in_; }
+  const std::vector<CowPair>& swap_out_pairs() const { return swap_out_; }
+  int64_t total_swapped_out() const { return total_swap_out_; }
+  int64_t total_swapped_in() const { return total_swap_in_; }
 
   int32_t running() const { return static_cast<int32_t>(running_.size()); }
   int32_t waiting() const { return static_cast<int32_t>(waiting_.size()); }
@@ -79,10 +87,12 @@ class Scheduler {
  private:
   int32_t reserve_blocks() const;
   bool admissible(const Request& r) const;
-  // Frees the youngest running request that has no row in this step
-  // (recompute: its generated tokens join its prompt) and puts it at the
-  // front of the waiting queue; returns its index in running_ or -1.
-  int32_t preempt_youngest(int32_t planned_upto);
+  // Preempts the youngest running request at index >= min_index that has
+  // no row in this step -- to the host tier if it has room (progress
+  // kept), else by recompute (blocks freed, its generated tokens join its
+  // prompt) -- and puts it at the front of the waiting queue; returns its
+  // index in running_ or -1.
+  int32_t preempt_youngest(int32_t min_index);
 
   SchedulerConfig cfg_;
   BlockAllocator alloc_;
@@ -93,6 +103,8 @@ class Scheduler {
   std::vector<int32_t> slots_;
   std::vector<int64_t> finished_, preempted_;
   std::vector<CowPair> cow_;       // stays empty: requests never share blocks
+  std::vector<CowPair> swap_in_, swap_out_;
+  int64_t total_swap_out_ = 0, total_swap_in_ = 0;
   int32_t num_decode_ = 0;
   int64_t total_finished_ = 0, total_preempted_ = 0, steps_ = 0;
 };

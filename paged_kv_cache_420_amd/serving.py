@@ -5,6 +5,9 @@ Each step ("vLLM 初探" tutorial §1.3; explainer, continuous-batching
 section; KV-cache article §4.1/§4.2 for the chunks):
   1. the native scheduler (pkv_scheduler_step) retires, admits and plans
      decode rows and prompt chunks, updating the block allocator;
+  1b. blocks it swapped in or out (preemption into a host tier; KV-cache
+     article §4.2, swap space) are copied: swap-ins first, then swap-outs,
+     both before anything of this step writes the pool;
   2. the plan's slot mapping, block tables, lengths and chunk offsets go to
      the device in one copy from pinned host memory;
   3. pkv_paged_kv_append stores every row's new K/V through the slots;
@@ -18,16 +21,19 @@ import numpy as np
 import torch
 
 from . import (Scheduler, paged_attention_decode, paged_attention_decode_workspace_size,
-               paged_attention_prefill, paged_kv_append)
+               paged_attention_prefill, paged_kv_append, swap_blocks)
 
 
 class ServingDriver:
     def __init__(self, scheduler, key_cache, value_cache, num_heads, scale, max_request_tokens,
-                 partition_size=0):
+                 partition_size=0, host_key_cache=None, host_value_cache=None):
         if not isinstance(scheduler, Scheduler):
             raise TypeError("scheduler must be a paged_kv_cache_420_amd.Scheduler")
         self.sched = scheduler
         self.kc, self.vc = key_cache, value_cache
+        self.hk, self.hv = host_key_cache, host_value_cache
+        if scheduler.host_blocks and (self.hk is None or self.hk.shape[0] < scheduler.host_blocks):
+            raise ValueError("a scheduler with a host tier needs pinned host caches that hold it")
         nb, self.num_kv_heads, self.block_size, self.head_dim = key_cache.shape
         self.num_heads = num_heads
         self.scale = scale
@@ -58,6 +64,11 @@ class ServingDriver:
         D], prefill outputs [prefill tokens, Hq, D]); the outputs are views of
         buffers reused by the next step."""
         plan = self.sched.step(self.max_blocks)
+        if len(plan.swap_in):
+            swap_blocks(self.hk, self.hv, self.kc, self.vc, plan.swap_in[:, 0], plan.swap_in[:, 1])
+        if len(plan.swap_out):
+            swap_blocks(self.kc, self.vc, self.hk, self.hv, plan.swap_out[:, 0],
+                        plan.swap_out[:, 1])
         if plan.num_rows == 0:
             return plan, None, None
         nd, nr, nt = plan.num_decode, plan.num_rows, plan.num_tokens

@@ -5,8 +5,9 @@ kernels (append, decode, chunked prefill).  Every token's K/V and every
 query row are drawn from per-(request, position) streams, so the oracle
 rebuilds each request's logical K/V and checks every output row of every
 step: decode rows against attention over the whole context, prompt rows
-causally.  The pool is small enough that requests are preempted and
-recomputed, which the test checks happened.  Tolerance 2e-3 (bf16 cache,
+causally.  The pool is small enough that a request is preempted --
+recomputed, or swapped to a pinned host pool and back -- which the test
+checks happened.  Tolerance 2e-3 (bf16 cache,
 float32 accumulation).
 """
 
@@ -78,20 +79,29 @@ class Tokens:
         return np.stack([r[2] for r in rows]), np.stack([r[3] for r in rows])
 
 
-def test_serving_trace_matches_oracle_every_step():
+@pytest.mark.parametrize("host_blocks", [0, 24])
+def test_serving_trace_matches_oracle_every_step(host_blocks):
+    """host_blocks 0: preemption recomputes; 24: it swaps to a pinned host
+    pool and back, and the outputs must not notice."""
     t = SMALL
     reqs = workloads.serving_requests(t)
     max_tokens = max(p + o for _, p, o in reqs)
     rng = np.random.default_rng(t.seed)
     order = rng.permutation(t.num_blocks).astype(np.int32)
     sched = pkv.Scheduler(t.num_blocks, t.block_size, t.max_num_seqs, t.max_num_batched_tokens,
-                          t.chunk_size, 0, order)
+                          t.chunk_size, 0, order, host_blocks=host_blocks)
     for rid, p, o in reqs:
         sched.add_request(rid, p, o)
     shape = (t.num_blocks, t.num_kv_heads, t.block_size, t.head_dim)
     kc = torch.full(shape, float("nan"), dtype=t.dtype, device=DEV)
     vc = torch.full(shape, float("nan"), dtype=t.dtype, device=DEV)
-    drv = ServingDriver(sched, kc, vc, t.num_heads, t.scale, max_tokens)
+    hk = hv = None
+    if host_blocks:
+        hshape = (host_blocks,) + shape[1:]
+        hk = torch.full(hshape, float("nan"), dtype=t.dtype).pin_memory()
+        hv = torch.full(hshape, float("nan"), dtype=t.dtype).pin_memory()
+    drv = ServingDriver(sched, kc, vc, t.num_heads, t.scale, max_tokens,
+                        host_key_cache=hk, host_value_cache=hv)
     tok = Tokens(t)
     worst, steps, rows_checked = 0.0, 0, 0
     while True:
@@ -123,5 +133,7 @@ def test_serving_trace_matches_oracle_every_step():
     st = sched.stats()
     log("steps", steps, "rows checked", rows_checked, "max abs err", worst, "stats", st)
     assert st["finished"] == len(reqs)
-    assert st["preemptions"] > 0          # the recompute path ran
+    assert st["preemptions"] > 0          # the preemption path ran
+    if host_blocks:
+        assert st["swapped_out"] == st["preemptions"] and st["swapped_in"] > 0
     assert worst <= TOL

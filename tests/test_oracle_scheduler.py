@@ -27,7 +27,8 @@ def _traces():
 
 def _build(cfg, requests):
     s = RefScheduler(cfg["num_blocks"], cfg["block_size"], cfg["max_num_seqs"],
-                     cfg["max_num_batched_tokens"], cfg["chunk_size"], cfg["reserve_tokens"])
+                     cfg["max_num_batched_tokens"], cfg["chunk_size"], cfg["reserve_tokens"],
+                     host_blocks=cfg["host_blocks"])
     for name, p, o in requests:
         s.add_request(name, p, o)
     return s
@@ -44,6 +45,9 @@ def test_hand_worked_traces(trace):
         assert got["slots"] == want["slots"], (k, want["why"])
         assert got["finished"] == want["finished"], k
         assert got["preempted"] == want["preempted"], k
+        if "swap_in" in want:
+            assert [list(p) for p in got["swap_in"]] == want["swap_in"], (k, want["why"])
+            assert [list(p) for p in got["swap_out"]] == want["swap_out"], (k, want["why"])
     assert s.stats()["finished"] == len(trace["requests"])
     assert s.alloc.num_free() == trace["config"]["num_blocks"]
 
@@ -67,7 +71,8 @@ def run_to_end(s, requests, max_steps=100000):
         assert all(1 <= r[1] <= s.chunk for r in rows[st_["num_decode"]:])
         assert len(set(st_["slots"])) == len(st_["slots"])          # distinct slots
         for rid in st_["preempted"]:
-            tokens[rid] = 0                                         # recomputed later
+            if rid not in s.alloc.swapped:
+                tokens[rid] = 0                                     # recomputed later
         k = 0
         for rid, q, ctx, table in rows:
             new = st_["slots"][k:k + q]
@@ -80,8 +85,10 @@ def run_to_end(s, requests, max_steps=100000):
         for rid in st_["finished"]:
             assert tokens[rid] == total[rid]                        # all its tokens
             assert rid not in s.alloc.tables                        # freed at once
-        held = sum(len(t) for t in s.alloc.tables.values())
+        held = sum(len(t) for q, t in s.alloc.tables.items() if q not in s.alloc.swapped)
         assert held + s.alloc.num_free() == s.num_blocks
+        in_host = sum(len(s.alloc.tables[q]) for q in s.alloc.swapped)
+        assert in_host + s.alloc.num_free_host() == s.alloc.num_host_blocks
         if not s.running and not s.waiting:
             return out
     raise AssertionError("trace did not drain")
@@ -90,15 +97,15 @@ def run_to_end(s, requests, max_steps=100000):
 traces = st.lists(st.tuples(st.integers(1, 40), st.integers(1, 30)), min_size=1, max_size=12)
 
 
-@settings(max_examples=60, deadline=None)
+@settings(max_examples=80, deadline=None)
 @given(reqs=traces, bs=st.sampled_from([1, 2, 4, 8]), seqs=st.integers(1, 5),
        budget=st.integers(1, 24), chunk=st.integers(1, 16), spare=st.integers(0, 12),
-       data=st.data())
-def test_random_traces_keep_the_invariants(reqs, bs, seqs, budget, chunk, spare, data):
+       host=st.sampled_from([0, 0, 4, 16, 64]), data=st.data())
+def test_random_traces_keep_the_invariants(reqs, bs, seqs, budget, chunk, spare, host, data):
     need = max(-(-(p + o) // bs) for p, o in reqs)
     nb = need + spare
     order = data.draw(st.permutations(list(range(nb))))
-    s = RefScheduler(nb, bs, seqs, budget, chunk, 0, order)
+    s = RefScheduler(nb, bs, seqs, budget, chunk, 0, order, host_blocks=host)
     requests = [(i, p, o) for i, (p, o) in enumerate(reqs)]
     for rid, p, o in requests:
         s.add_request(rid, p, o)

@@ -26,6 +26,8 @@ def _compare_step(nat, ref):
     assert [int(x) for x in plan.slots] == want["slots"]
     assert plan.finished == want["finished"]
     assert plan.preempted == want["preempted"]
+    assert plan.swap_in.tolist() == [list(p) for p in want["swap_in"]]
+    assert plan.swap_out.tolist() == [list(p) for p in want["swap_out"]]
     # -1 padding past each table's end
     for i in range(plan.num_rows):
         t = plan.block_tables[i]
@@ -34,9 +36,9 @@ def _compare_step(nat, ref):
     assert nat.stats() == ref.stats()
 
 
-def _pair(nb, bs, seqs, budget, chunk, reserve, order=None):
-    nat = pkv.Scheduler(nb, bs, seqs, budget, chunk, reserve, order)
-    ref = RefScheduler(nb, bs, seqs, budget, chunk, reserve, order)
+def _pair(nb, bs, seqs, budget, chunk, reserve, order=None, host=0):
+    nat = pkv.Scheduler(nb, bs, seqs, budget, chunk, reserve, order, host_blocks=host)
+    ref = RefScheduler(nb, bs, seqs, budget, chunk, reserve, order, host_blocks=host)
     return nat, ref
 
 
@@ -46,7 +48,8 @@ def test_golden_traces_through_the_c_abi():
     for t in traces:
         c = t["config"]
         nat = pkv.Scheduler(c["num_blocks"], c["block_size"], c["max_num_seqs"],
-                            c["max_num_batched_tokens"], c["chunk_size"], c["reserve_tokens"])
+                            c["max_num_batched_tokens"], c["chunk_size"], c["reserve_tokens"],
+                            host_blocks=c["host_blocks"])
         ids = {name: 100 + i for i, (name, _, _) in enumerate(t["requests"])}
         names = {v: k for k, v in ids.items()}
         for name, p, o in t["requests"]:
@@ -62,6 +65,9 @@ def test_golden_traces_through_the_c_abi():
             assert [int(x) for x in plan.slots] == want["slots"], want["why"]
             assert [names[x] for x in plan.finished] == want["finished"]
             assert [names[x] for x in plan.preempted] == want["preempted"]
+            if "swap_in" in want:
+                assert plan.swap_in.tolist() == want["swap_in"], want["why"]
+                assert plan.swap_out.tolist() == want["swap_out"], want["why"]
         nat.close()
 
 
@@ -70,14 +76,15 @@ def test_golden_traces_through_the_c_abi():
                      max_size=14),
        bs=st.sampled_from([1, 2, 4, 8, 16]), seqs=st.integers(1, 6), budget=st.integers(1, 30),
        chunk=st.integers(1, 20), spare=st.integers(0, 16), reserve_on=st.booleans(),
+       host=st.sampled_from([0, 0, 3, 16, 64]),
        arrivals=st.lists(st.integers(0, 3), min_size=14, max_size=14), data=st.data())
 def test_native_matches_reference_step_for_step(reqs, bs, seqs, budget, chunk, spare,
-                                                reserve_on, arrivals, data):
+                                                reserve_on, host, arrivals, data):
     reserve = max(p + o for p, o in reqs) if reserve_on else 0
     need = max(-(-(p + o) // bs) for p, o in reqs)
     nb = need + spare
     order = np.array(data.draw(st.permutations(list(range(nb)))), dtype=np.int32)
-    nat, ref = _pair(nb, bs, seqs, budget, chunk, reserve, order)
+    nat, ref = _pair(nb, bs, seqs, budget, chunk, reserve, order, host)
     # requests arrive over the first steps, a few at a time
     pending = [(i, p, o) for i, (p, o) in enumerate(reqs)]
     step = 0
