@@ -437,9 +437,10 @@ int32_t pkv_swap_blocks(const void* src_key_cache, const void* src_value_cache,
 
 /* The split-K partition (tokens) pkv_paged_attention_decode uses for these
  * sizes: partition_size itself when it is non-zero and valid, else the
- * automatic choice -- the longest of 1024, 512, 256, 128 tokens that still
- * gives num_seqs * num_kv_heads * ceil(max_context_len / partition) >= 2048
- * workgroups (128 if none does) -- raised to block_size if shorter. */
+ * automatic choice -- the longest of 2048 (only when max_context_len <=
+ * 4096), 1024, 512, 256, 128 tokens that still gives num_seqs *
+ * num_kv_heads * ceil(max_context_len / partition) >= 2048 workgroups (128
+ * if none does) -- raised to block_size if shorter. */
 int32_t pkv_paged_attention_decode_partition_size(
     int32_t num_seqs, int32_t num_kv_heads, int32_t block_size,
     int32_t max_context_len, int32_t partition_size, int32_t* resolved);
@@ -467,7 +468,7 @@ int32_t pkv_paged_attention_decode_workspace_size(
  *                  max_blocks_per_seq * block_size, or whose used table
  *                  entries fall outside [0, num_blocks), gets NaN rows
  *   partition_size tokens per split-K partition: 0 = automatic, else a
- *                  multiple of 64 in [64, 1024] (raised to block_size)
+ *                  multiple of 64 in [64, 2048] (raised to block_size)
  *   out            [num_seqs][num_heads][head_dim] float32
  *   workspace      device buffer of at least the size reported by
  *                  pkv_paged_attention_decode_workspace_size (may be NULL

@@ -62,6 +62,9 @@ def test_device_calls_reject_bad_arguments_before_launch():
     assert ws.value == 1 * 8 * (4096 // 128) * (128 + 2) * 4
     assert lib.pkv_paged_attention_decode_workspace_size(64, 32, 32, 128, 2000, 0,
                                                          ctypes.byref(ws)) == 0
+    assert ws.value == 0                     # one 2048-token partition
+    assert lib.pkv_paged_attention_decode_workspace_size(64, 32, 32, 128, 4000, 0,
+                                                         ctypes.byref(ws)) == 0
     assert ws.value == 64 * 32 * 2 * (128 + 2) * 4
     # GQA: partials per query head
     assert lib.pkv_paged_attention_decode_workspace_size(256, 64, 8, 128, 8192, 512,
