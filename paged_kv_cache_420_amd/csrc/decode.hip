@@ -976,7 +976,8 @@ int32_t run_decode(const void* query, const void* key_new, const void* value_new
 
 // Packs a step's host metadata (checked against the kernel-argument limits).
 int32_t pack_step(const int32_t* context_lens, const int32_t* changes, int32_t num_changes,
-                  int32_t num_seqs, int32_t max_blocks_per_seq, StepMeta* m) {
+                  int32_t num_seqs, int32_t num_kv_heads, int32_t max_blocks_per_seq,
+                  StepMeta* m) {
   if (num_seqs > kStepMaxSeqs)
     return fail(PKV_ERR_UNSUPPORTED, "step calls take at most %d sequences (got %d)",
                 kStepMaxSeqs, num_seqs);
@@ -986,13 +987,24 @@ int32_t pack_step(const int32_t* context_lens, const int32_t* changes, int32_t n
   if (num_seqs > 0 && !context_lens) return fail(PKV_ERR_INVALID, "context_lens is NULL");
   if (num_changes > 0 && !changes) return fail(PKV_ERR_INVALID, "changes is NULL");
   for (int32_t i = 0; i < num_seqs; ++i) m->lens[i] = context_lens[i];
-  // longest first (stable): a rough longest-processing-time order for the
-  // workgroup dispatcher
+  // Longest first (stable), so long partitions start first; then, within
+  // each round of R = 256 / num_kv_heads sequences -- the sequences whose
+  // workgroups one pass of the dispatcher spreads over all 256 CUs -- every
+  // other round reversed ("snake"), so the CUs that get a round's longest
+  // sequence get the next round's shortest and the CUs' loads even out
+  // when the whole grid is resident at once (7B-shaped batch: partition
+  // kernel 1% faster than plain longest-first).
   int32_t idx[kStepMaxSeqs];
   for (int32_t i = 0; i < num_seqs; ++i) idx[i] = i;
   std::stable_sort(idx, idx + num_seqs,
                    [&](int32_t a, int32_t b) { return context_lens[a] > context_lens[b]; });
-  for (int32_t i = 0; i < num_seqs; ++i) m->order[i] = static_cast<uint8_t>(idx[i]);
+  const int32_t R = std::max(1, 256 / std::max(1, num_kv_heads));
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    const int32_t k = i / R, j = i % R;
+    int32_t src = k % 2 == 0 ? i : k * R + (R - 1 - j);
+    if (src >= num_seqs) src = i;  // a short last round keeps its order
+    m->order[i] = static_cast<uint8_t>(idx[src]);
+  }
   for (int32_t i = 0; i < num_changes; ++i) {
     const int32_t row = changes[3 * i], idx = changes[3 * i + 1];
     if (row < 0 || row >= num_seqs || idx < 0 || idx >= max_blocks_per_seq ||
@@ -1089,7 +1101,8 @@ int32_t step_call(const void* query, const void* key, const void* value, void* k
                   void* workspace, size_t workspace_bytes_given, int32_t dtype, void* stream,
                   bool partials, bool merge) {
   StepMeta m;
-  int32_t st = pack_step(context_lens, changes, num_changes, num_seqs, max_blocks_per_seq, &m);
+  int32_t st = pack_step(context_lens, changes, num_changes, num_seqs, num_kv_heads,
+                         max_blocks_per_seq, &m);
   if (st != PKV_OK) return st;
   return run_decode(query, key, value, key_cache, value_cache, block_tables, nullptr, num_seqs,
                     num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
@@ -1132,7 +1145,8 @@ extern "C" int32_t pkv_paged_attention_decode_step_merge(
     int32_t partition_size, float* out, void* workspace, size_t workspace_bytes_given,
     void* stream) {
   StepMeta m;
-  int32_t st = pack_step(context_lens, nullptr, 0, num_seqs, max_blocks_per_seq, &m);
+  int32_t st = pack_step(context_lens, nullptr, 0, num_seqs, num_kv_heads, max_blocks_per_seq,
+                         &m);
   if (st != PKV_OK) return st;
   return run_decode(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, num_seqs,
                     num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, 1,
