@@ -365,10 +365,19 @@ struct StepMeta {
   __device__ int seq(int y) const { return order[y]; }
 };
 
+// Workgroups per CU the compiler must fit: 16-bit caches with 8 query heads
+// per kv head (the GQA layer) take 4 (128 VGPRs, 4 waves per SIMD; 20
+// bytes per lane spill) instead of the 3 their 130 VGPRs would allow: 2%
+// faster, the kernel being close to VALU-bound.  Others fit 8 unforced.
+template <int DT, int G>
+constexpr int decode_min_blocks() {
+  return (G >= 8 && Elem<DT>::kBytes == 2) ? 4 : 1;
+}
+
 // Dynamic LDS: [scores: max(part*G, kWaves*G*D) floats][block ids][m/l].
 template <int DT, int D, int G, int U, class Meta>
-__global__ __launch_bounds__(kThreads) void decode_partition_kernel(const DecodeParams prm,
-                                                                    const Meta meta) {
+__global__ __launch_bounds__(kThreads, (decode_min_blocks<DT, G>())) void decode_partition_kernel(
+    const DecodeParams prm, const Meta meta) {
   using C = Cfg<DT, D, G, U>;
   using E = Elem<DT>;
   extern __shared__ float smem[];
