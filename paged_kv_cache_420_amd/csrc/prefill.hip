@@ -21,10 +21,16 @@
 //     for a 32-key step are given consecutive columns of V^T in LDS.  So the
 //     online softmax (running max, rescale, sum) needs only two cross-lane
 //     steps per row and P never leaves registers;
-//   * P is fed to the MFMA as hi + lo halves in the cache's 16-bit type
-//     (hi = round(p), lo = round(p - hi)), which keeps the weights exact to
-//     about 16 bits: a single 16-bit P would put rows with a few dominant
-//     keys past a 2e-3 tolerance.  Accumulation and softmax are float32.
+//   * the PV product runs in float16 whatever the cache's 16-bit type: P is
+//     rounded to float16 once (11 significant bits: a weight's relative
+//     error is at most 2^-12, so an output row moves by at most 2^-12 of
+//     its largest |v|; bfloat16's 8 bits would move rows with a few
+//     dominant keys past a 2e-3 tolerance), and a bfloat16 V tile is
+//     widened to float16 as it is staged in LDS -- exact for every
+//     |v| >= 2^-14 (8 significant bits fit in 11), rounded below that (an
+//     error under 2^-25), and limited to |v| <= 65504 as a float16 cache
+//     would be.  QK^T stays in the cache type; accumulation and softmax
+//     are float32.
 // Keys past the causal limit are excluded by select (-inf before exp), and
 // keys past the needed range are zero-filled in LDS, so stale or NaN cache
 // contents never reach an output.
@@ -54,7 +60,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-// 16-bit element type of the cache: the MFMA and the hi/lo split of P.
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// 16-bit element type of the cache: the QK^T MFMA, and how a staged V word
+// (two elements) becomes two float16 values.
 template <int DT>
 struct Half;
 
@@ -64,18 +74,9 @@ struct Half<PKV_BF16> {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
   }
-  // Two weights p0, p1 as packed hi and lo pairs with p = hi + lo: hi is p
-  // truncated to bfloat16 (its top 16 bits), lo = p - hi (exact in float32,
-  // at most 16 significant bits) rounded to bfloat16.  hi + lo carries p to
-  // about 2^-16 relative.
-  __device__ static void split2(float p0, float p1, uint32_t& hi, uint32_t& lo) {
-    const uint32_t b0 = __float_as_uint(p0), b1 = __float_as_uint(p1);
-    hi = (b0 >> 16) | (b1 & 0xffff0000u);
-    const float l0 = p0 - __uint_as_float(b0 & 0xffff0000u);
-    const float l1 = p1 - __uint_as_float(b1 & 0xffff0000u);
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    typedef float f32x2 __attribute__((ext_vector_type(2)));
-    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{l0, l1}, bf16x2));
+  __device__ static uint32_t to_f16x2(uint32_t w) {
+    const f32x2 f = {__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u)};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
   }
 };
 
@@ -85,17 +86,17 @@ struct Half<PKV_F16> {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
   }
-  // hi = p rounded to float16, lo = p - hi rounded to float16.
-  __device__ static void split2(float p0, float p1, uint32_t& hi, uint32_t& lo) {
-    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-    typedef float f32x2 __attribute__((ext_vector_type(2)));
-    const f16x2 h = __builtin_convertvector(f32x2{p0, p1}, f16x2);
-    const f16x2 l = __builtin_convertvector(
-        f32x2{p0 - static_cast<float>(h.x), p1 - static_cast<float>(h.y)}, f16x2);
-    hi = __builtin_bit_cast(uint32_t, h);
-    lo = __builtin_bit_cast(uint32_t, l);
-  }
+  __device__ static uint32_t to_f16x2(uint32_t w) { return w; }
 };
+
+// O^T += V^T P^T in float16, and two weights as a float16 pair.
+__device__ __forceinline__ f32x4 mma_f16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ uint32_t weights_f16x2(float p0, float p1) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{p0, p1}, f16x2));
+}
 
 __device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
 
@@ -254,6 +255,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
       }
     }
     if (v_role) {
+      // V is staged as float16 (the PV product's type)
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) g8[r][w] = H::to_f16x2(g8[r][w]);
       // g8[k] holds dims 8 vpc .. + 7 of key k of the chunk (k = 4 t + r);
       // V^T row 8 vpc + e gets, at chunk ck, the eight keys' element e.
       uint8_t* dst = s_vt[buf] + (8 * vpc) * kVtRow + 16 * ck;
@@ -351,13 +357,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
         for (int dt = 0; dt < kD / 16; ++dt) o[qg][dt] *= alpha;
       }
     }
-    // P and O^T += V^T P^T one 32-key step at a time: the exp and split of
-    // step 1 (VALU) then issue while step 0's MFMAs execute, and step 1's
+    // P and O^T += V^T P^T one 32-key step at a time: the exp and rounding
+    // of step 1 (VALU) then issue while step 0's MFMAs execute, and step 1's
     // MFMAs overlap the next tile's LDS stores; V^T operands stay shared
     // by both row groups.
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
-      uint32_t phi[2][4], plo[2][4];  // [qg][word]
+      uint32_t pw[2][4];  // [qg][word]: float16 weight pairs
 #pragma unroll
       for (int qg = 0; qg < 2; ++qg) {
         const float nm = -m_run[qg];
@@ -375,7 +381,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
         for (int e = 0; e < 8; ++e) sum += x[e];
         l_run[qg] += sum;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) H::split2(x[2 * w], x[2 * w + 1], phi[qg][w], plo[qg][w]);
+        for (int w = 0; w < 4; ++w) pw[qg][w] = weights_f16x2(x[2 * w], x[2 * w + 1]);
       }
 #pragma unroll
       for (int dt = 0; dt < kD / 16; ++dt) {
@@ -383,10 +389,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
             svt + (16 * dt + col) * kVtRow + 64 * st + 16 * grp);
 #pragma unroll
         for (int qg = 0; qg < 2; ++qg) {
-          const u32x4 bh = {phi[qg][0], phi[qg][1], phi[qg][2], phi[qg][3]};
-          const u32x4 bl = {plo[qg][0], plo[qg][1], plo[qg][2], plo[qg][3]};
-          o[qg][dt] = H::mma(a, bh, o[qg][dt]);
-          o[qg][dt] = H::mma(a, bl, o[qg][dt]);
+          const u32x4 bp = {pw[qg][0], pw[qg][1], pw[qg][2], pw[qg][3]};
+          o[qg][dt] = mma_f16(a, bp, o[qg][dt]);
         }
       }
     }
