@@ -49,9 +49,9 @@ constexpr int kD = 128;               // head dim served by this kernel
 constexpr int kQTile = 32 * kWaves;   // query rows per workgroup
 constexpr int kKTile = 64;            // keys per K/V tile
 constexpr int kKRow = kD * 2 + 16;    // LDS bytes per K row (16 B pad)
-constexpr int kVtRow = kKTile * 2 + 16;  // LDS bytes per V^T row (16 B pad)
+constexpr int kVRow = kD * 2 + 32;    // LDS bytes per V row (32 B pad)
 constexpr int kLdsK = kKTile * kKRow;
-constexpr int kLdsV = kD * kVtRow;
+constexpr int kLdsV = kKTile * kVRow;
 constexpr float kLog2e = 1.4426950408889634f;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -59,6 +59,18 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// LDS transpose read (gfx950): every lane reads 8 bytes; within each group
+// of 16 lanes, treating lane j's four 16-bit elements as row j of a 16 x 4
+// matrix D, lane i receives D[4 k + i / 4][i % 4] for k = 0..3 (checked by
+// an in-bounds probe on the GPU).
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint8_t* p) {
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)(const __attribute__((address_space(3))) uint8_t*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -111,17 +123,15 @@ constexpr float kRescaleSlack = 8.0f;
 // one workgroup's MFMA work then covers the other's barrier and load waits
 // (measured 1.5x over one wave per SIMD at 304 registers).
 //
-// K/V tile layout in LDS (two buffers, so one barrier per tile):
-//   K   [64 keys][128 dims] row-major, rows padded to 272 bytes;
-//   V^T [128 dims][64 keys], rows padded to 144 bytes, keys permuted so that
-//       the 8 keys one lane group feeds to a PV MFMA step are 16 contiguous
-//       bytes: key 32 s + 16 t + 4 g + r sits in 16-byte chunk 4 s + g at
-//       position 4 t + r.
-// Gather: waves 0-1 fetch V, waves 2-3 fetch K, eight 16-byte loads per
-// thread.  A V thread takes the eight keys of one chunk at one 8-dim piece
-// and transposes them in registers into eight 16-byte V^T row segments; a
-// K thread takes eight consecutive keys at one piece.  Lane assignments make
-// every 16 consecutive lanes' LDS stores cover all 64 banks once.
+// K/V tile layout in LDS (two buffers, so one barrier per tile): both
+// row-major [64 keys][128 dims], K rows padded to 272 bytes and V rows to
+// 288 (float16 V), so that neither the 16-byte K reads of 16 rows nor the
+// 8-byte transpose reads of 4 V rows by a 16-lane group share a bank.
+// Gather: every thread moves four 16-byte pieces of K and four of V (key
+// 16 i + tid / 16, piece tid % 16), 16 consecutive lanes covering one
+// contiguous row.  The PV product's V^T operand comes out of the row-major
+// V tile through the LDS transpose read, so V needs no transposition in
+// registers.
 template <int DT>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
     const uint16_t* __restrict__ query, const uint16_t* __restrict__ key_cache,
@@ -132,7 +142,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
     float* __restrict__ out) {
   using H = Half<DT>;
   __shared__ __attribute__((aligned(16))) uint8_t s_k[2][kLdsK];
-  __shared__ __attribute__((aligned(16))) uint8_t s_vt[2][kLdsV];
+  __shared__ __attribute__((aligned(16))) uint8_t s_v[2][kLdsV];
 
   const int xcd_slice = num_heads >> 3;
   const int h = (num_heads & 7) == 0
@@ -197,22 +207,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
   }
 
   // ---- tile gather ----------------------------------------------------------
-  const bool v_role = tid < 128;
-  const int gt = tid & 127;
-  // V role: chunk ck = (s, g) of the V^T row, piece pc (dims 8 pc .. + 7);
-  // its keys are quad A = 32 s + 4 g + 0..3 and quad B = quad A + 16.
-  // K role: piece pc, keys 8 ko .. 8 ko + 7.
-  const int ck = gt & 7, vpc = gt >> 3;
-  const int kpc = gt & 15, ko = gt >> 4;
+  // piece i of this thread: key 16 i + pk of the tile, dims 8 pd .. + 7
+  const int pk = tid >> 4, pd = tid & 15;
   const int64_t tile_elems = int64_t(bs) * kD;
   const int64_t blk_elems = tile_elems * num_kv_heads;
   const int32_t* table = block_tables + int64_t(b) * max_blocks;
-  const uint16_t* vbase = value_cache + int64_t(kvh) * tile_elems + 8 * vpc;
-  const uint16_t* kbase = key_cache + int64_t(kvh) * tile_elems + 8 * kpc;
+  const int64_t head_off = int64_t(kvh) * tile_elems + 8 * pd;
   bool bad_blk = false;
-  u32x4 g8[8];  // the eight staged 16-byte pieces
+  u32x4 gk[4], gv[4];  // the staged 16-byte pieces
 
-  // element offset of `key`'s row at this thread's piece; flags bad ids
+  // element offset of `key`'s row; flags bad ids
   auto row_of = [&](int key) -> int64_t {
     int id = table[key >> log2_bs];
     if (id < 0 || id >= num_blocks) {
@@ -222,25 +226,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
     return int64_t(id) * blk_elems + int64_t(key & (bs - 1)) * kD;
   };
 
-  // Loads are unconditional: a quad/octet past kv_end is clamped to the
-  // last needed one (always a valid row of a checked block), and the keys
-  // past kv_end are zeroed when the last, partial tile is stored.
+  // Loads are unconditional: a key past kv_end is clamped to the last
+  // needed one (a valid row of a checked block), and the keys past kv_end
+  // are zeroed when the last, partial tile is stored.
   auto load_tile = [&](int j) {
     const int key0 = j * kKTile;
-    if (v_role) {
-      const int ka = key0 + 32 * (ck >> 2) + 4 * (ck & 3);  // quad A
 #pragma unroll
-      for (int qd = 0; qd < 2; ++qd) {
-        const int kq = min(ka + 16 * qd, kv_end - 1) & ~3;  // 4 | bs: quad in one block
-        const uint16_t* src = vbase + row_of(kq);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) g8[4 * qd + r] = *reinterpret_cast<const u32x4*>(src + r * kD);
-      }
-    } else {
-      const int k8 = min(key0 + 8 * ko, kv_end - 1) & ~7;  // 8 | bs: octet in one block
-      const uint16_t* src = kbase + row_of(k8);
-#pragma unroll
-      for (int r = 0; r < 8; ++r) g8[r] = *reinterpret_cast<const u32x4*>(src + r * kD);
+    for (int i = 0; i < 4; ++i) {
+      const int64_t off = row_of(min(key0 + 16 * i + pk, kv_end - 1)) + head_off;
+      gk[i] = *reinterpret_cast<const u32x4*>(key_cache + off);
+      gv[i] = *reinterpret_cast<const u32x4*>(value_cache + off);
     }
   };
 
@@ -248,37 +243,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
     const int key0 = j * kKTile;
     if (key0 + kKTile > kv_end) {  // last tile: zero the keys past the range
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int key = v_role ? key0 + 32 * (ck >> 2) + 4 * (ck & 3) + 16 * (r >> 2) + (r & 3)
-                               : key0 + 8 * ko + r;
-        if (key >= kv_end) g8[r] = u32x4{0, 0, 0, 0};
-      }
+      for (int i = 0; i < 4; ++i)
+        if (key0 + 16 * i + pk >= kv_end) gk[i] = gv[i] = u32x4{0, 0, 0, 0};
     }
-    if (v_role) {
-      // V is staged as float16 (the PV product's type)
 #pragma unroll
-      for (int r = 0; r < 8; ++r)
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<u32x4*>(s_k[buf] + (16 * i + pk) * kKRow + 16 * pd) = gk[i];
+      u32x4 v = gv[i];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) g8[r][w] = H::to_f16x2(g8[r][w]);
-      // g8[k] holds dims 8 vpc .. + 7 of key k of the chunk (k = 4 t + r);
-      // V^T row 8 vpc + e gets, at chunk ck, the eight keys' element e.
-      uint8_t* dst = s_vt[buf] + (8 * vpc) * kVtRow + 16 * ck;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int w = e >> 1;
-        u32x4 row;
-#pragma unroll
-        for (int k2 = 0; k2 < 4; ++k2) {
-          const uint32_t a = g8[2 * k2][w], bb = g8[2 * k2 + 1][w];
-          row[k2] = (e & 1) ? ((a >> 16) | (bb & 0xffff0000u))
-                            : ((a & 0xffffu) | (bb << 16));
-        }
-        *reinterpret_cast<u32x4*>(dst + e * kVtRow) = row;
-      }
-    } else {
-      uint8_t* dst = s_k[buf] + (8 * ko) * kKRow + 16 * kpc;
-#pragma unroll
-      for (int r = 0; r < 8; ++r) *reinterpret_cast<u32x4*>(dst + r * kKRow) = g8[r];
+      for (int w = 0; w < 4; ++w) v[w] = H::to_f16x2(v[w]);  // V as float16
+      *reinterpret_cast<u32x4*>(s_v[buf] + (16 * i + pk) * kVRow + 16 * pd) = v;
     }
   };
 
@@ -294,7 +268,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
   auto compute_tile = [&](int buf, int j) {
     const int key0 = j * kKTile;
     const uint8_t* sk = s_k[buf];
-    const uint8_t* svt = s_vt[buf];
+    const uint8_t* sv = s_v[buf];
     // S^T tiles: kt = 16-key slice, one per (row group, slice)
     f32x4 s[2][4];
 #pragma unroll
@@ -385,8 +359,15 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
       }
 #pragma unroll
       for (int dt = 0; dt < kD / 16; ++dt) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(
-            svt + (16 * dt + col) * kVtRow + 64 * st + 16 * grp);
+        // V^T operand: element e = 4 t + k of lane (grp, col) is dim 16 dt +
+        // col of key 32 st + 16 t + 4 grp + k -- the keys this lane's P
+        // elements hold.  Transpose read t: lane (grp, col) reads key
+        // 32 st + 16 t + 4 grp + col / 4, dims 16 dt + 4 (col % 4) .. + 3.
+        const uint8_t* vrow = sv + (32 * st + 4 * grp + (col >> 2)) * kVRow +
+                              (16 * dt + 4 * (col & 3)) * 2;
+        const u32x2 v0 = lds_read_tr16(vrow);
+        const u32x2 v1 = lds_read_tr16(vrow + 16 * kVRow);
+        const u32x4 a = {v0.x, v0.y, v1.x, v1.y};
 #pragma unroll
         for (int qg = 0; qg < 2; ++qg) {
           const u32x4 bp = {pw[qg][0], pw[qg][1], pw[qg][2], pw[qg][3]};
