@@ -228,12 +228,27 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
 
   // Loads are unconditional: a key past kv_end is clamped to the last
   // needed one (a valid row of a checked block), and the keys past kv_end
-  // are zeroed when the last, partial tile is stored.
+  // are zeroed when the last, partial tile is stored.  With blocks of 16
+  // tokens or more, the 16 keys of a piece group (16-aligned) share one
+  // block, so its id is one scalar load per group and tile.
+  const bool wide_blocks = log2_bs >= 4;
   auto load_tile = [&](int j) {
     const int key0 = j * kKTile;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int64_t off = row_of(min(key0 + 16 * i + pk, kv_end - 1)) + head_off;
+      const int key = min(key0 + 16 * i + pk, kv_end - 1);
+      int64_t off;
+      if (wide_blocks) {
+        const int gkey = min(key0 + 16 * i, kv_end - 1);  // uniform
+        int id = table[gkey >> log2_bs];
+        if (id < 0 || id >= num_blocks) {
+          bad_blk = true;
+          id = 0;
+        }
+        off = int64_t(id) * blk_elems + int64_t(key & (bs - 1)) * kD + head_off;
+      } else {
+        off = row_of(key) + head_off;
+      }
       gk[i] = *reinterpret_cast<const u32x4*>(key_cache + off);
       gv[i] = *reinterpret_cast<const u32x4*>(value_cache + off);
     }
@@ -263,7 +278,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
 #pragma unroll
     for (int dt = 0; dt < kD / 16; ++dt) o[qg][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run[2] = {-INFINITY, -INFINITY};  // log2 units, scale applied
-  float l_run[2] = {0.f, 0.f};
+  // Row sums of the float16 weights, on the matrix cores: a ones row in the
+  // A operand (dim 0 of a 16-dim tile) against P^T puts each query row's
+  // sum in output row 0, i.e. element 0 of lanes 0..15 (lane = query row).
+  f32x4 l_acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  const uint32_t one_w = col == 0 ? 0x3C003C00u : 0u;  // float16 1.0 pairs
+  const u32x4 ones = {one_w, one_w, one_w, one_w};
 
   auto compute_tile = [&](int buf, int j) {
     const int key0 = j * kKTile;
@@ -326,7 +346,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
         const float m_new = up ? mts[qg] : m_run[qg];
         const float alpha = __builtin_amdgcn_exp2f(m_run[qg] - m_new);
         m_run[qg] = m_new;
-        l_run[qg] *= alpha;
+        l_acc[qg] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < kD / 16; ++dt) o[qg][dt] *= alpha;
       }
@@ -350,10 +370,6 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
           for (int e = 0; e < 8; ++e)
             if (16 * (2 * st + (e >> 2)) + (e & 3) > lim[qg]) x[e] = 0.f;
         }
-        float sum = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sum += x[e];
-        l_run[qg] += sum;
 #pragma unroll
         for (int w = 0; w < 4; ++w) pw[qg][w] = weights_f16x2(x[2 * w], x[2 * w + 1]);
       }
@@ -373,6 +389,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
           const u32x4 bp = {pw[qg][0], pw[qg][1], pw[qg][2], pw[qg][3]};
           o[qg][dt] = mma_f16(a, bp, o[qg][dt]);
         }
+      }
+#pragma unroll
+      for (int qg = 0; qg < 2; ++qg) {
+        const u32x4 bp = {pw[qg][0], pw[qg][1], pw[qg][2], pw[qg][3]};
+        l_acc[qg] = mma_f16(ones, bp, l_acc[qg]);
       }
     }
   };
@@ -395,9 +416,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
   // ---- 16 dt + 4 grp .. + 3 ------------------------------------------------
 #pragma unroll
   for (int qg = 0; qg < 2; ++qg) {
-    float l = l_run[qg];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    const float l = __shfl(l_acc[qg][0], col);  // row sum from lane col
     const int i = r0 + 32 * wave + 16 * qg + col;
     if (i >= c) continue;
     const float inv = bad_blk ? __builtin_nanf("") : 1.0f / l;
