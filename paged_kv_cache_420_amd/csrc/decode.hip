@@ -219,10 +219,11 @@ struct Elem<kFp8QBf16> : ElemFp8<HalfBf16> {};
 template <>
 struct Elem<kFp8QF16> : ElemFp8<HalfF16> {};
 
-// ---- cross-lane exchange for butterfly steps.  Steps run from the highest
-// ---- lane bit to the lowest; within a row of 16 lanes the DPP mirror
-// ---- patterns flip exactly the bit being reduced while keeping the higher
-// ---- ones, which is all a butterfly step needs.
+// ---- cross-lane exchange for the reduction over the lanes of a token row.
+// ---- Lane bit M's partner: quad_perm for bits 1 and 2 and row_ror:8 for
+// ---- bit 8 flip exactly that bit; row_half_mirror for bit 4 flips bits 4,
+// ---- 2 and 1 together (lane l <-> 7 - l in each half row), which the
+// ---- register layout of the score reduction allows for.
 template <int M>
 __device__ __forceinline__ float lane_swap(float x) {
   int v = __float_as_int(x);
@@ -233,23 +234,57 @@ __device__ __forceinline__ float lane_swap(float x) {
   } else if constexpr (M == 4) {
     v = __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);  // row_half_mirror
   } else if constexpr (M == 8) {
-    v = __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);  // row_mirror
+    v = __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false);  // row_ror:8
   } else {
     v = __shfl_xor(v, M);
   }
   return __int_as_float(v);
 }
 
-// Transposed butterfly over the lane bits M, M/2, ..., 1 of `n` values per
-// lane.  While a lane holds more than one value, each step keeps one half
-// (chosen by the lane's bit M) and adds the partner's copy of that half, so
-// the partial sums end up distributed; once one value is left, the
-// remaining steps are plain butterflies.  Afterwards value i of a lane is
-// original value ((lane & (2M-1)) >> plain_steps) * n_left + i.
-template <int M, int N>
-__device__ __forceinline__ void transpose_reduce(float* v, int lane) {
+// ---- Score reduction.  A lane holds N = U*G partial dot products, slot
+// ---- s = g*U + u (head-major), each over its share of a token row; the
+// ---- row's lanes differ in the bits M = kLpt/2 ... 1, reduced from the top.
+// ---- While a lane holds more than one value a step halves them (a
+// ---- transposed butterfly): each lane keeps one half and adds its
+// ---- partner's copy of that half.  The top steps split heads (the upper
+// ---- half of the slots is heads G/2.. at the first step, and so on); for
+// ---- those a lane always keeps its lower half and sends its upper one,
+// ---- which is right because every lane's q registers were loaded with
+// ---- its heads XOR-permuted (head_perm below) so that the partner's upper
+// ---- half holds the same heads as the lane's lower half -- one DPP add per
+// ---- pair and no selects.  The remaining steps split units and pick the
+// ---- half with the lane's bit (two selects and an add per pair); once one
+// ---- value is left, the steps are plain butterflies.
+
+// Bit of lane `lane` that flips the heads of the step over lane bit M.
+// Bit 4's partner also flips bits 2 and 1, so theirs are taken relative to
+// bit 4, which keeps them unchanged across that step.
+template <int M>
+__device__ __forceinline__ int perm_bit(int lane) {
+  const int b = (lane & M) ? 1 : 0;
+  if constexpr (M >= 4) return b;
+  else return b ^ ((lane & 4) ? 1 : 0);
+}
+
+// XOR mask applied to the head index of the lane's q registers: the sum of
+// the head masks (G/2, G/4, ...) of the head-splitting steps it takes part
+// in, each taken when the lane's bit for that step is set.
+template <int kLpt, int G, int M = kLpt / 2, int Mask = G / 2>
+__device__ __forceinline__ int head_perm(int lane) {
+  if constexpr (M >= 1 && Mask >= 1)
+    return (perm_bit<M>(lane) ? Mask : 0) + head_perm<kLpt, G, M / 2, Mask / 2>(lane);
+  else
+    return 0;
+}
+
+template <int M, int N, int HeadSteps>
+__device__ __forceinline__ void reduce_scores(float* v, int lane) {
   if constexpr (M >= 1) {
-    if constexpr (N > 1) {
+    if constexpr (N > 1 && HeadSteps > 0) {
+#pragma unroll
+      for (int i = 0; i < N / 2; ++i) v[i] += lane_swap<M>(v[i + N / 2]);
+      reduce_scores<M / 2, N / 2, HeadSteps - 1>(v, lane);
+    } else if constexpr (N > 1) {
       const bool hi = (lane & M) != 0;
 #pragma unroll
       for (int i = 0; i < N / 2; ++i) {
@@ -257,11 +292,59 @@ __device__ __forceinline__ void transpose_reduce(float* v, int lane) {
         float send = hi ? v[i] : v[i + N / 2];
         v[i] = keep + lane_swap<M>(send);
       }
-      transpose_reduce<M / 2, N / 2>(v, lane);
+      reduce_scores<M / 2, N / 2, 0>(v, lane);
     } else {
       v[0] += lane_swap<M>(v[0]);
-      transpose_reduce<M / 2, 1>(v, lane);
+      reduce_scores<M / 2, 1, 0>(v, lane);
     }
+  }
+}
+
+// Slot offset of a lane's value 0 after reduce_scores: the upper halves it
+// kept at the select steps.
+template <int M, int N, int HeadSteps>
+__device__ __forceinline__ int reduced_slot(int lane) {
+  if constexpr (M >= 1 && N > 1) {
+    if constexpr (HeadSteps > 0)
+      return reduced_slot<M / 2, N / 2, HeadSteps - 1>(lane);
+    else
+      return ((lane & M) ? N / 2 : 0) + reduced_slot<M / 2, N / 2, 0>(lane);
+  } else {
+    return 0;
+  }
+}
+
+// ---- Combine of the weighted sums over the token rows of a wave: the lanes
+// ---- of one d-slice differ in the bits kLpt ... 32.  Transposed as well:
+// ---- at bits 32 and 16 the swap instructions exchange the upper half of
+// ---- one register with the lower half of another (v_permlane32_swap: the
+// ---- upper 32 lanes of the first operand with the lower 32 of the second;
+// ---- v_permlane16_swap: the odd rows of the first with the even rows of
+// ---- the second), so one swap and one add leave lanes with the bit clear
+// ---- holding the sum of value i and lanes with it set that of value
+// ---- i + N/2.  Below bit 16 a select-and-shuffle step does the same.
+template <int M, int Lo, int N>
+__device__ __forceinline__ void combine_rows(float* v, int lane) {
+  if constexpr (M >= Lo) {
+    static_assert(N > 1, "every step must leave a value per lane");
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+      if constexpr (M == 32 || M == 16) {
+        const auto r = M == 32 ? __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]),
+                                                                  __float_as_uint(v[i + N / 2]),
+                                                                  false, false)
+                               : __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]),
+                                                                  __float_as_uint(v[i + N / 2]),
+                                                                  false, false);
+        v[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+      } else {
+        const bool hi = (lane & M) != 0;
+        const float keep = hi ? v[i + N / 2] : v[i];
+        const float send = hi ? v[i] : v[i + N / 2];
+        v[i] = keep + (M == 8 ? lane_swap<8>(send) : __shfl_xor(send, M));
+      }
+    }
+    combine_rows<M / 2, Lo, N / 2>(v, lane);
   }
 }
 
@@ -287,20 +370,24 @@ struct Cfg {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // Units of the chunk number `c` of one wavefront, as 16-byte loads: unit u
-// covers tokens c*kChunkTok + u*kTpl .. + kTpl-1 of the partition, lane
-// `tok` of them at byte offset `base` within the row.  Units past the last
-// block of the partition re-read its last block (always a valid block id)
-// so every load is in bounds and the issue is branch-free; the values they
-// bring are masked out by the callers.  The loads are non-temporal: a
-// decode step reads each cached token once, so K/V should stream past the
-// caches rather than evict what is reused (measured: +4-6% on batches with
-// private caches, -7% where a 16 MB shared prefix was being served from the
+// covers tokens c*kChunkTok + u*kTpl .. + kTpl-1 of the partition; a lane
+// reads at byte offset `lane_off` = (its token within the unit) * row bytes
+// + (its 16-byte piece of the row).  A unit never straddles two blocks (a tile holds at least
+// the 1 KiB a unit reads), so the unit's address is uniform -- `tiles`, the
+// kv head's tile in block 0, plus block and row offsets, all scalar -- and
+// each lane adds its constant 32-bit offset.  Units past the last block of
+// the partition re-read its last block (always a valid block id) so every
+// load is in bounds and the issue is branch-free; the values they bring
+// are masked out by the callers.  The loads are non-temporal: a decode step
+// reads each cached token once, so K/V should stream past the caches
+// rather than evict what is reused (measured: +4-6% on batches with private
+// caches, -7% where a 16 MB shared prefix was being served from the
 // caches).
 template <class C, int U>
-__device__ __forceinline__ void issue_chunk(uint4 (&buf)[U], const uint8_t* base,
+__device__ __forceinline__ void issue_chunk(uint4 (&buf)[U], const uint8_t* tiles,
                                             const int* s_blk, int c, int nblk,
                                             int log2_bs, int64_t blk_stride,
-                                            int tok_in_unit) {
+                                            uint32_t lane_off) {
   const int bs_mask = (1 << log2_bs) - 1;
   int blk[U];
 #pragma unroll
@@ -311,9 +398,8 @@ __device__ __forceinline__ void issue_chunk(uint4 (&buf)[U], const uint8_t* base
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int tu = c * C::kChunkTok + u * C::kTpl;
-    const int row = (tu & bs_mask) + tok_in_unit;
-    const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-        base + int64_t(blk[u]) * blk_stride + int64_t(row) * C::kRow));
+    const uint8_t* unit = tiles + (int64_t(blk[u]) * blk_stride + (tu & bs_mask) * C::kRow);
+    const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(unit + lane_off));
     buf[u] = make_uint4(t.x, t.y, t.z, t.w);
   }
 }
@@ -476,18 +562,22 @@ __global__ __launch_bounds__(kThreads, (decode_min_blocks<DT, G>())) void decode
     __syncthreads();
   }
 
-  // q slices of the G heads: lane covers bytes (lane % LPT) * 16 of the row.
+  // q slices of the G heads: lane covers bytes (lane % LPT) * 16 of the row;
+  // register g holds head g ^ hperm (the score reduction's layout).
   const int dl = lane % C::kLpt;
   const int tok_in_unit = lane / C::kLpt;
+  const int hperm = head_perm<C::kLpt, G>(lane);
   typename E::Q q[G];
 #pragma unroll
   for (int g = 0; g < G; ++g)
     q[g] = E::load_q(prm.query +
-                     (int64_t(b) * num_heads + int64_t(kvh) * G + g) * (D * E::kQBytes) +
+                     (int64_t(b) * num_heads + int64_t(kvh) * G + (g ^ hperm)) *
+                         (D * E::kQBytes) +
                      dl * (C::kEpl * E::kQBytes));
 
-  const uint8_t* kbase = prm.key_cache + int64_t(kvh) * tile_bytes + dl * 16;
-  const uint8_t* vbase = prm.value_cache + int64_t(kvh) * tile_bytes + dl * 16;
+  const uint8_t* kbase = prm.key_cache + int64_t(kvh) * tile_bytes;
+  const uint8_t* vbase = prm.value_cache + int64_t(kvh) * tile_bytes;
+  const uint32_t lane_off = uint32_t(tok_in_unit * C::kRow + dl * 16);
   const int nchunks = cdiv(ntok, C::kChunkTok);
   // This wave's chunks are wave, wave + kWaves, ...: nj of them.  The walk
   // over them keeps the next chunk's loads in flight while one is computed,
@@ -499,20 +589,25 @@ __global__ __launch_bounds__(kThreads, (decode_min_blocks<DT, G>())) void decode
   auto my_chunk = [&](int j) { return wave + min(j, nj - 1) * kWaves; };
 
   // ---- QK pass ------------------------------------------------------------
+  // After the reduction a lane's value i is slot slot0 + i: head
+  // (slot / U) ^ hperm of unit slot % U.  Lanes that a final plain
+  // butterfly left with a copy of a partner's sums do not store.
+  constexpr int kHeadSteps = ilog2(G) < ilog2(C::kLpt) ? ilog2(G) : ilog2(C::kLpt);
+  const int slot0 = reduced_slot<C::kLpt / 2, C::kNv, kHeadSteps>(lane);
+  const bool score_writer = (dl & ((1 << C::kPlainLog) - 1)) == 0;
   auto qk = [&](const uint4 (&k)[U], int c) {
     const int t0 = c * C::kChunkTok;  // relative to p0
     float v[C::kNv];
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int g = 0; g < G; ++g)
 #pragma unroll
-      for (int g = 0; g < G; ++g) v[u * G + g] = E::dot(q[g], k[u], 0.0f);
-    transpose_reduce<C::kLpt / 2, C::kNv>(v, lane);
-    const int sub = lane & (C::kLpt - 1);
-    if ((sub & ((1 << C::kPlainLog) - 1)) == 0) {
+      for (int u = 0; u < U; ++u) v[g * U + u] = E::dot(q[g], k[u], 0.0f);
+    reduce_scores<C::kLpt / 2, C::kNv, kHeadSteps>(v, lane);
+    if (score_writer) {
 #pragma unroll
       for (int i = 0; i < C::kLeft; ++i) {
-        const int idx = (sub >> C::kPlainLog) * C::kLeft + i;
-        const int u = idx / G, g = idx - (idx / G) * G;
+        const int slot = slot0 + i;
+        const int u = slot % U, g = (slot / U) ^ hperm;
         const int t = t0 + u * C::kTpl + tok_in_unit;
         s_score[t * G + g] = t < ntok ? v[i] * scale_log2 : -INFINITY;
       }
@@ -521,13 +616,13 @@ __global__ __launch_bounds__(kThreads, (decode_min_blocks<DT, G>())) void decode
   {
     uint4 ka[U], kb[U];
     if (nj > 0) {
-      issue_chunk<C, U>(ka, kbase, s_blk, my_chunk(0), nblk, log2_bs, blk_stride, tok_in_unit);
+      issue_chunk<C, U>(ka, kbase, s_blk, my_chunk(0), nblk, log2_bs, blk_stride, lane_off);
       for (int j = 0; j < nj; j += 2) {
         issue_chunk<C, U>(kb, kbase, s_blk, my_chunk(j + 1), nblk, log2_bs, blk_stride,
-                          tok_in_unit);
+                          lane_off);
         qk(ka, my_chunk(j));
         issue_chunk<C, U>(ka, kbase, s_blk, my_chunk(j + 2), nblk, log2_bs, blk_stride,
-                          tok_in_unit);
+                          lane_off);
         if (j + 1 < nj) qk(kb, my_chunk(j + 1));
       }
     }
@@ -589,32 +684,34 @@ __global__ __launch_bounds__(kThreads, (decode_min_blocks<DT, G>())) void decode
   {
     uint4 va[U], vb[U];
     if (nj > 0) {
-      issue_chunk<C, U>(va, vbase, s_blk, my_chunk(0), nblk, log2_bs, blk_stride, tok_in_unit);
+      issue_chunk<C, U>(va, vbase, s_blk, my_chunk(0), nblk, log2_bs, blk_stride, lane_off);
       for (int j = 0; j < nj; j += 2) {
         issue_chunk<C, U>(vb, vbase, s_blk, my_chunk(j + 1), nblk, log2_bs, blk_stride,
-                          tok_in_unit);
+                          lane_off);
         pv(va, my_chunk(j));
         issue_chunk<C, U>(va, vbase, s_blk, my_chunk(j + 2), nblk, log2_bs, blk_stride,
-                          tok_in_unit);
+                          lane_off);
         if (j + 1 < nj) pv(vb, my_chunk(j + 1));
       }
     }
   }
 
   // ---- combine token rows within the wave, then the waves ----------------
+  // Each lane ends with kOut of the G * kEpl sums of its d-slice: flat index
+  // j = g * kEpl + e from out0 on.
+  constexpr int kOut = G * D / 64;
+  float* flat = &acc[0][0];
+  combine_rows<32, C::kLpt, G * C::kEpl>(flat, lane);
+  int out0 = 0;
 #pragma unroll
-  for (int m = C::kLpt; m < 64; m <<= 1)
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int e = 0; e < C::kEpl; ++e) acc[g][e] += __shfl_xor(acc[g][e], m);
+  for (int m = 32, h = G * C::kEpl / 2; m >= C::kLpt; m >>= 1, h >>= 1)
+    if (lane & m) out0 += h;
   __syncthreads();  // everyone is done reading weights from s_score
-  if (lane < C::kLpt) {
 #pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int e = 0; e < C::kEpl; ++e)
-        s_score[(wave * G + g) * D + lane * C::kEpl + e] = acc[g][e];
+  for (int i = 0; i < kOut; ++i) {
+    const int j = out0 + i;
+    const int g = j / C::kEpl, e = j % C::kEpl;
+    s_score[(wave * G + g) * D + dl * C::kEpl + e] = flat[i];
   }
   __syncthreads();
 
