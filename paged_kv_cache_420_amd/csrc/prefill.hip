@@ -112,6 +112,10 @@ __device__ __forceinline__ uint32_t weights_f16x2(float p0, float p1) {
 
 __device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
 
+__device__ __forceinline__ float fmax_nan(float a, float b) {
+  return __builtin_elementwise_maximum(a, b);
+}
+
 // Lazy rescaling threshold (log2 units): the running max of a row is only
 // raised -- and the accumulators rescaled -- when a tile's max exceeds it by
 // more than this, so weights stay below 2^8 and the rescale is rare.
@@ -212,45 +216,32 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
   const int64_t tile_elems = int64_t(bs) * kD;
   const int64_t blk_elems = tile_elems * num_kv_heads;
   const int32_t* table = block_tables + int64_t(b) * max_blocks;
-  const int64_t head_off = int64_t(kvh) * tile_elems + 8 * pd;
+  const uint16_t* k_head = key_cache + int64_t(kvh) * tile_elems;
+  const uint16_t* v_head = value_cache + int64_t(kvh) * tile_elems;
+  const uint32_t lane_elems = uint32_t(pk * kD + 8 * pd);  // within a 16-key group
   bool bad_blk = false;
   u32x4 gk[4], gv[4];  // the staged 16-byte pieces
 
-  // element offset of `key`'s row; flags bad ids
-  auto row_of = [&](int key) -> int64_t {
-    int id = table[key >> log2_bs];
-    if (id < 0 || id >= num_blocks) {
-      bad_blk = true;
-      id = 0;
-    }
-    return int64_t(id) * blk_elems + int64_t(key & (bs - 1)) * kD;
-  };
-
-  // Loads are unconditional: a key past kv_end is clamped to the last
-  // needed one (a valid row of a checked block), and the keys past kv_end
-  // are zeroed when the last, partial tile is stored.  With blocks of 16
-  // tokens or more, the 16 keys of a piece group (16-aligned) share one
-  // block, so its id is one scalar load per group and tile.
-  const bool wide_blocks = log2_bs >= 4;
+  // Loads are unconditional and in bounds.  Blocks hold 16 tokens or more,
+  // so the 16 keys of a piece group (16-aligned) share one block: its id is
+  // one uniform load per group and tile, and the group's address is a
+  // uniform base plus the lane's constant offset.  A group past kv_end
+  // re-reads the 16-aligned group holding key kv_end - 1 (a valid row range
+  // of a checked block); keys past kv_end, whatever they read, are zeroed
+  // when the last, partial tile is stored.
   auto load_tile = [&](int j) {
     const int key0 = j * kKTile;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int key = min(key0 + 16 * i + pk, kv_end - 1);
-      int64_t off;
-      if (wide_blocks) {
-        const int gkey = min(key0 + 16 * i, kv_end - 1);  // uniform
-        int id = table[gkey >> log2_bs];
-        if (id < 0 || id >= num_blocks) {
-          bad_blk = true;
-          id = 0;
-        }
-        off = int64_t(id) * blk_elems + int64_t(key & (bs - 1)) * kD + head_off;
-      } else {
-        off = row_of(key) + head_off;
+      const int gkey = min(key0 + 16 * i, kv_end - 1);  // uniform
+      int id = __builtin_amdgcn_readfirstlane(table[gkey >> log2_bs]);
+      if (id < 0 || id >= num_blocks) {
+        bad_blk = true;
+        id = 0;
       }
-      gk[i] = *reinterpret_cast<const u32x4*>(key_cache + off);
-      gv[i] = *reinterpret_cast<const u32x4*>(value_cache + off);
+      const int64_t group = int64_t(id) * blk_elems + int64_t(gkey & (bs - 1) & ~15) * kD;
+      gk[i] = *reinterpret_cast<const u32x4*>(k_head + group + lane_elems);
+      gv[i] = *reinterpret_cast<const u32x4*>(v_head + group + lane_elems);
     }
   };
 
@@ -327,13 +318,23 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
     bool grow = false;
 #pragma unroll
     for (int qg = 0; qg < 2; ++qg) {
+      // NaN-propagating maximum (v_maximum3_f32): unlike fmaxf it needs no
+      // quieting pass over the matrix-core results first; a NaN score
+      // makes the row NaN either way
       float mt = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
-        mt = fmaxf(mt, fmaxf(fmaxf(s[qg][kt][0], s[qg][kt][1]),
-                             fmaxf(s[qg][kt][2], s[qg][kt][3])));
-      mt = fmaxf(mt, __shfl_xor(mt, 16));
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
+        mt = fmax_nan(mt, fmax_nan(fmax_nan(s[qg][kt][0], s[qg][kt][1]),
+                                   fmax_nan(s[qg][kt][2], s[qg][kt][3])));
+      // across the four lane groups (lane bits 16 and 32): each swap gives
+      // both halves of a pair of rows, so the max of the two results is
+      // the butterfly step
+      const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mt), __float_as_uint(mt),
+                                                        false, false);
+      mt = fmax_nan(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+      const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt),
+                                                        false, false);
+      mt = fmax_nan(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
       mts[qg] = mt == -INFINITY ? -INFINITY : mt * sl2;  // no -inf * 0
       grow |= mts[qg] > m_run[qg] + kRescaleSlack;
     }
