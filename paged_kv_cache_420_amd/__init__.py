@@ -217,7 +217,8 @@ class BlockAllocator:
         self.block_size = block_size
 
     def close(self):
-        if getattr(self, "_h", None):
+        # at interpreter shutdown the module globals may already be gone
+        if getattr(self, "_h", None) and _lib is not None:
             _lib.pkv_allocator_destroy(self._h)
             self._h = None
 
