@@ -79,6 +79,33 @@ def test_decode_matches_oracle(name):
     assert err <= TOL[w.dtype]
 
 
+# Every (cache type, head_dim, query heads per kv head) the decode kernels
+# are compiled for: the score reduction and the combine across a wave's
+# token rows change shape with the lanes per row (4 .. 32) and with G, so
+# each instantiation meets the oracle at least once.  Partitions of 128
+# tokens with lengths up to 400 cover one- and multi-partition rows.
+SWEEP = [(dt, d, g) for dt in (torch.bfloat16, torch.float16, torch.float32)
+         for d in (64, 128) for g in (1, 2, 4, 8)]
+
+
+@pytest.mark.parametrize("dt,d,grp", SWEEP,
+                         ids=[f"{str(dt)[6:]}-d{d}-g{g}" for dt, d, g in SWEEP])
+def test_every_instantiation_matches_oracle(dt, d, grp):
+    w = workloads.scaled(workloads.get("llama7b_bf16"), num_seqs=3, num_kv_heads=2,
+                         num_heads=2 * grp, head_dim=d, dtype=dt, lens="uniform:1,400",
+                         seed=4300 + d + grp)
+    log("case", w)
+    p = workloads.plan(w)
+    g = GpuState(w, p)
+    o = OracleState(w, p)
+    got, q64 = run_decode(g, w, partition_size=128)
+    tables, lens = o.tables()
+    want = paged_decode(q64, o.kc, o.vc, tables, lens, w.scale, w.block_size)
+    err = max_abs_err(got, want)
+    log("max abs err", err)
+    assert err <= TOL[w.dtype]
+
+
 @pytest.mark.parametrize("part", [64, 128, 256, 1024])
 def test_partition_size_only_changes_rounding(part):
     w = SMALL["llama7b_small"]

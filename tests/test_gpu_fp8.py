@@ -113,6 +113,32 @@ def test_fp8_decode_matches_oracle(name):
     assert err <= TOL_FP8
 
 
+FP8_SWEEP = [(qt, d, g) for qt in (torch.bfloat16, torch.float16) for d in (64, 128)
+             for g in (1, 2, 4, 8)]
+
+
+@pytest.mark.parametrize("qt,d,grp", FP8_SWEEP,
+                         ids=[f"{str(qt)[6:]}q-d{d}-g{g}" for qt, d, g in FP8_SWEEP])
+def test_fp8_every_instantiation_matches_oracle(qt, d, grp):
+    """Every (query type, head_dim, G) the 8-bit decode kernel is compiled
+    for (4 or 8 lanes per token row), against the oracle over the
+    dequantised cache; partitions of 128 tokens cover the merge."""
+    w = workloads.scaled(workloads.get("llama7b_bf16"), num_seqs=3, num_kv_heads=2,
+                         num_heads=2 * grp, head_dim=d, dtype=qt, lens="uniform:1,400",
+                         seed=4400 + d + grp)
+    ks, vs = 0.013, 0.011
+    log("case", w, ks, vs)
+    p = workloads.plan(w)
+    g = GpuStateFp8(w, p, ks, vs)
+    o = OracleStateFp8(w, p, ks, vs)
+    got, q64 = run_fp8(g, w, ks, vs, 128)
+    tables, lens = o.tables()
+    want = paged_decode(q64, o.kc, o.vc, tables, lens, w.scale, w.block_size)
+    err = max_abs_err(got, want)
+    log("max abs err", err)
+    assert err <= TOL_FP8
+
+
 def test_fp8_one_call_is_bitwise_its_two_stages():
     w, ks, vs, _ = DECODE_CASES["llama7b_part64"]
     p = workloads.plan(w)
