@@ -22,12 +22,13 @@ then uses the unique bytes (prefix counted once).
 ``roofline`` reports the decode partition kernel alone, timed with HIP
 events on the stream it runs on (every fourth timed step, so the events'
 own cost stays out of the step time); its ``traffic`` comes from the committed
-rocprofv3
-counter summary of the same kernel source, when there is one.
+rocprofv3 counter summary of the same kernel source, when there is one.
 ``cpu_baseline`` times the float64 CPU oracle on a small sample of the same
-workload (reported only).  For the shared-prefix workload the line also
-carries ``prefill``: one causal 512-row chunked prefill per sequence,
-timed the same way, against the bf16 matrix-core peak.
+workload (reported only; the host's CPU model and core count go into its
+``sample``).  For the shared-prefix workload the line also carries
+``prefill``: one causal 512-row chunked prefill per sequence, timed the
+same way, against the bf16 matrix-core peak; its oracle timing (one
+sequence's chunk) is ``cpu_baseline.prefill``.
 
 Usage: python bench.py [--steps K] [--warmup W] [--workload NAME]
        python bench.py --copy-calibration   (block copy of a known size,
@@ -533,10 +534,23 @@ def serve_leg(args, torch, pkv, workloads):
         flush=True)
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, workloads):
-    """The float64 oracle on a sample of the workload's sequences."""
+    """The float64 oracle on a sample of the workload's sequences; for a
+    workload with a prefill chunk, also the oracle's causal prefill of one
+    sequence's chunk."""
     import threadpoolctl
-    from oracle import RefAllocator, copy_blocks, kv_append, paged_decode
+    from oracle import RefAllocator, copy_blocks, kv_append, paged_decode, paged_prefill
 
     sample = min(6, w.num_seqs)
     p = workloads.plan(w)
@@ -548,7 +562,7 @@ def cpu_baseline(w, workloads):
         return op[1] in keep or op[1] == workloads.PREFIX_SEQ
 
     need = sum(-(-int(n) // w.block_size) for n in p.lens[:sample]) + \
-        -(-w.prefix // w.block_size) + 4
+        -(-w.prefix // w.block_size) + -(-w.chunk // w.block_size) + 5
     ref = RefAllocator(need, w.block_size)
     shape = (need, w.num_kv_heads, w.block_size, w.head_dim)
     kc, vc = np.full(shape, np.nan), np.full(shape, np.nan)
@@ -579,12 +593,39 @@ def cpu_baseline(w, workloads):
             break
     per = el / reps
     gbps = kv_bytes(w, np.array(lens)) / per / 1e9
-    return {"value": round(gbps, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "tokens_per_s": round(len(seqs) / per, 2),
-            "sample": f"{len(seqs)} of {w.num_seqs} sequences (context lens "
-                      f"{[int(x) for x in lens]}), one decode step each, float64 numpy "
-                      f"gather-then-attend, {reps} repetitions in {el:.1f} s; host has "
-                      f"{len(os.sched_getaffinity(0))} cores available"}
+    host = f"host: {cpu_model()}, {len(os.sched_getaffinity(0))} cores available"
+    res = {"value": round(gbps, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+           "tokens_per_s": round(len(seqs) / per, 2),
+           "sample": f"{len(seqs)} of {w.num_seqs} sequences (context lens "
+                     f"{[int(x) for x in lens]}), one decode step each, float64 numpy "
+                     f"gather-then-attend, {reps} repetitions in {el:.1f} s; {host}"}
+    if w.chunk:
+        # one sequence's chunk: seeded rows appended after its context
+        s0, c = seqs[0], w.chunk
+        slots, pairs = ref.append(s0, c)
+        if pairs:
+            copy_blocks(kc, vc, [a for a, _ in pairs], [d for _, d in pairs])
+        kv = workloads.normal([w.seed, 9, 0], (2, c, w.num_kv_heads, w.head_dim), w.std)
+        kv_append(kc, vc, workloads.as_f64(workloads.to_dtype(kv[0], w.dtype)),
+                  workloads.as_f64(workloads.to_dtype(kv[1], w.dtype)), slots, w.block_size)
+        qr = workloads.as_f64(workloads.to_dtype(
+            workloads.normal([w.seed, 9, 1], (c, w.num_heads, w.head_dim), w.std), w.dtype))
+        t1, l1 = ref.build_tables([s0], len(ref.tables[s0]))
+        n = int(l1[0])
+        flops = 4.0 * w.head_dim * w.num_heads * (c * (n - c) + c * (c + 1) // 2)
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            paged_prefill(qr, kc, vc, np.array(t1), l1, [0, c], w.scale, w.block_size)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el > 5.0 and reps >= 2:
+                break
+        per = el / reps
+        res["prefill"] = {"value": round(flops / per / 1e9, 3), "unit": "GFLOP/s",
+                          "rows_per_s": round(c / per, 1),
+                          "sample": f"one sequence's {c}-row causal chunk at context {n}, "
+                                    f"float64 numpy, {reps} repetitions in {el:.1f} s"}
+    return res
 
 
 def traffic_from_profiles(w, kernel_src):
