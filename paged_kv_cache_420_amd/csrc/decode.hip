@@ -12,9 +12,10 @@
 // loads in flight, block ids staged in LDS, and scores/weights in LDS.
 //
 // Work split (split-K): one workgroup of 4 wavefronts per (kv head,
-// sequence, partition of `part` tokens), kv head fastest in the grid.  It serves all G = Hq / Hkv query heads
-// that read this kv head, so each K/V tile is fetched from HBM once per
-// group (GQA reuse).  Within the workgroup:
+// sequence, partition of `part` tokens), kv head fastest in the grid.  It
+// serves all G = Hq / Hkv query heads that read this kv head, so each K/V
+// tile is fetched from HBM once per group (GQA reuse).  Within the
+// workgroup:
 //   1. block ids of the partition -> LDS (range-checked);
 //   2. QK pass: a "unit" is one 16-byte load per lane = 1 KiB per wavefront,
 //      covering TPL consecutive tokens of one (block, kv-head) tile (LPT
@@ -27,12 +28,12 @@
 //   4. PV pass: same unit walk over V; each lane scales its slice of V by
 //      the weight of its token and accumulates G x EPL floats;
 //   5. lanes of different token rows and the 4 wavefronts are summed
-//      (shuffles, then LDS) and the partition's result is written either
+//      (lane swaps, then LDS) and the partition's result is written either
 //      as the final row (one partition) or as (acc, max, sum) partials that
 //      decode_reduce_kernel merges with a log-sum-exp.
-// Memory-bound for G <= 8 (1..8 flop per KV byte against a ~20 flop/B VALU
-// ridge), so no matrix cores: the loads and the reduction cost are what
-// matter.  Tokens past the context are excluded by select, never by
+// 1..8 flop per KV byte against a ~10 flop/B ridge for non-packed fp32 FMAs:
+// memory-bound for MHA and close to VALU-bound at G = 8, so no matrix
+// cores: the loads and the VALU work per byte are what matter.  Tokens past the context are excluded by select, never by
 // multiplying with zero, so stale or NaN cache contents never leak.
 #include <hip/hip_runtime.h>
 
