@@ -467,7 +467,8 @@ __global__ __launch_bounds__(kThreads, (decode_min_blocks<DT, G>())) void decode
     const DecodeParams prm, const Meta meta) {
   using C = Cfg<DT, D, G, U>;
   using E = Elem<DT>;
-  extern __shared__ float smem[];
+  // 16-byte aligned, so a token row of G weights is read with 16-byte loads
+  extern __shared__ __attribute__((aligned(16))) float smem[];
   const int32_t num_kv_heads = prm.num_kv_heads, log2_bs = prm.log2_bs;
   const int32_t max_blocks = prm.max_blocks, num_blocks = prm.num_blocks;
   const int32_t part = prm.part, max_parts = prm.max_parts;
