@@ -453,9 +453,10 @@ struct StepMeta {
 };
 
 // Workgroups per CU the compiler must fit: 16-bit caches with 8 query heads
-// per kv head (the GQA layer) take 4 (128 VGPRs, 4 waves per SIMD; 20
-// bytes per lane spill) instead of the 3 their 130 VGPRs would allow: 2%
-// faster, the kernel being close to VALU-bound.  Others fit 8 unforced.
+// per kv head (the GQA layer) are held to 4 (at most 128 VGPRs, 4 waves per
+// SIMD), which the kernel, close to VALU-bound, needs more than registers;
+// they fit in 114-117 VGPRs with no spill, so the bound is a guard.  Others
+// fit 8 unforced.
 template <int DT, int G>
 constexpr int decode_min_blocks() {
   return (G >= 8 && Elem<DT>::kBytes == 2) ? 4 : 1;
