@@ -7,12 +7,12 @@
 // n_b - 1; row i attends to positions 0 .. n_b - c_b + i, gathered through
 // the block table.
 //
-// Unlike decode this is a dense contraction (128 query rows share every
+// Unlike decode this is a dense contraction (256 query rows share every
 // K/V tile), so both products run on MFMA (v_mfma_f32_16x16x32_{bf16,f16}):
-//   * one workgroup = 4 wavefronts = 128 query rows of one query head of one
+//   * one workgroup = 8 wavefronts = 256 query rows of one query head of one
 //     sequence; each wavefront owns 32 rows (two 16-row groups);
 //   * K/V are walked in tiles of 64 keys.  The workgroup gathers a tile
-//     through the block table into LDS -- K row-major, V transposed -- while
+//     through the block table into LDS -- K and V row-major -- while
 //     the previous tile is being computed (the next tile's global loads are
 //     in flight during the MFMA work);
 //   * S^T = K Q^T (16 keys x 16 rows per MFMA): the accumulator layout puts
@@ -43,7 +43,7 @@
 namespace pkv {
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kD = 128;               // head dim served by this kernel
 constexpr int kQTile = 32 * kWaves;   // query rows per workgroup
@@ -122,22 +122,25 @@ __device__ __forceinline__ float fmax_nan(float a, float b) {
 constexpr float kRescaleSlack = 8.0f;
 
 // Grid: x = query head (permuted so that heads of one KV group share an
-// XCD when num_heads % 8 == 0), y = 128-row tile of the chunk, z = sequence.
-// Register use is capped for two workgroups per CU (two waves per SIMD):
-// one workgroup's MFMA work then covers the other's barrier and load waits
-// (measured 1.5x over one wave per SIMD at 304 registers).
+// XCD when num_heads % 8 == 0), y = 256-row tile of the chunk, z = sequence.
+// Register use is capped for two waves per SIMD (one eight-wave workgroup
+// per CU): one wave's MFMA work then covers the other's waits (measured
+// 1.5x over one wave per SIMD at 304 registers).  Eight waves rather than
+// two four-wave workgroups share each tile's gather -- its global loads,
+// the float16 widening of V and the LDS stores -- and halve the L2 re-reads
+// of K/V: 4.8% faster.
 //
 // K/V tile layout in LDS (two buffers, so one barrier per tile): both
 // row-major [64 keys][128 dims], K rows padded to 272 bytes and V rows to
 // 288 (float16 V), so that neither the 16-byte K reads of 16 rows nor the
 // 8-byte transpose reads of 4 V rows by a 16-lane group share a bank.
-// Gather: every thread moves four 16-byte pieces of K and four of V (key
-// 16 i + tid / 16, piece tid % 16), 16 consecutive lanes covering one
-// contiguous row.  The PV product's V^T operand comes out of the row-major
+// Gather: every thread moves two 16-byte pieces of K and two of V (key
+// 32 i + tid / 16, piece tid % 16), 16 consecutive lanes covering one
+// contiguous row; a wave's four rows lie in one 16-key group.  The PV product's V^T operand comes out of the row-major
 // V tile through the LDS transpose read, so V needs no transposition in
 // registers.
 template <int DT>
-__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
+__global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
     const uint16_t* __restrict__ query, const uint16_t* __restrict__ key_cache,
     const uint16_t* __restrict__ value_cache, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ context_lens, const int32_t* __restrict__ cu_query_lens,
@@ -212,15 +215,18 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
 
   // ---- tile gather ----------------------------------------------------------
   // piece i of this thread: key 16 i + pk of the tile, dims 8 pd .. + 7
+  // pieces per thread and tile; a piece row within its 16-key group
+  constexpr int kPieces = kKTile * 16 / kThreads;
+  constexpr int kPieceStride = kThreads / 16;  // keys between a thread's pieces
   const int pk = tid >> 4, pd = tid & 15;
   const int64_t tile_elems = int64_t(bs) * kD;
   const int64_t blk_elems = tile_elems * num_kv_heads;
   const int32_t* table = block_tables + int64_t(b) * max_blocks;
   const uint16_t* k_head = key_cache + int64_t(kvh) * tile_elems;
   const uint16_t* v_head = value_cache + int64_t(kvh) * tile_elems;
-  const uint32_t lane_elems = uint32_t(pk * kD + 8 * pd);  // within a 16-key group
+  const uint32_t lane_elems = uint32_t((pk & 15) * kD + 8 * pd);  // within a 16-key group
   bool bad_blk = false;
-  u32x4 gk[4], gv[4];  // the staged 16-byte pieces
+  u32x4 gk[kPieces], gv[kPieces];  // the staged 16-byte pieces
 
   // Loads are unconditional and in bounds.  Blocks hold 16 tokens or more,
   // so the 16 keys of a piece group (16-aligned) share one block: its id is
@@ -232,8 +238,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
   auto load_tile = [&](int j) {
     const int key0 = j * kKTile;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int gkey = min(key0 + 16 * i, kv_end - 1);  // uniform
+    for (int i = 0; i < kPieces; ++i) {
+      const int gkey = min(key0 + kPieceStride * i + 16 * (pk >> 4), kv_end - 1);  // uniform
       int id = __builtin_amdgcn_readfirstlane(table[gkey >> log2_bs]);
       if (id < 0 || id >= num_blocks) {
         bad_blk = true;
@@ -249,16 +255,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
     const int key0 = j * kKTile;
     if (key0 + kKTile > kv_end) {  // last tile: zero the keys past the range
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (key0 + 16 * i + pk >= kv_end) gk[i] = gv[i] = u32x4{0, 0, 0, 0};
+      for (int i = 0; i < kPieces; ++i)
+        if (key0 + kPieceStride * i + pk >= kv_end) gk[i] = gv[i] = u32x4{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<u32x4*>(s_k[buf] + (16 * i + pk) * kKRow + 16 * pd) = gk[i];
+    for (int i = 0; i < kPieces; ++i) {
+      *reinterpret_cast<u32x4*>(s_k[buf] + (kPieceStride * i + pk) * kKRow + 16 * pd) = gk[i];
       u32x4 v = gv[i];
 #pragma unroll
       for (int w = 0; w < 4; ++w) v[w] = H::to_f16x2(v[w]);  // V as float16
-      *reinterpret_cast<u32x4*>(s_v[buf] + (16 * i + pk) * kVRow + 16 * pd) = v;
+      *reinterpret_cast<u32x4*>(s_v[buf] + (kPieceStride * i + pk) * kVRow + 16 * pd) = v;
     }
   };
 
