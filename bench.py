@@ -160,7 +160,12 @@ def gpu_run(args, w, torch, pkv, workloads):
     changes_h = np.empty((b + 1, 3), dtype=np.int32)
     append = alloc.prepared_append_changes(seqs, np.ones(b, dtype=np.int32), slots_h, lens_h,
                                            changes_h)
-    launch = pkv.DecodeLauncher(kc, vc, w.num_heads, b, mb, max_len, part, out, workspace)
+    # blocks held by several sequences (refcount > 1, a forked prefix) are
+    # read once per sequence: the decode then loads K/V with the default
+    # cache policy instead of streaming them (PKV_DECODE_SHARED_BLOCKS)
+    shared = any(r > 1 for r in alloc.snapshot()[1])
+    launch = pkv.DecodeLauncher(kc, vc, w.num_heads, b, mb, max_len, part, out, workspace,
+                                shared_blocks=shared)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(total_steps)]
     # HIP events bracket the kernels of every fourth timed step: each record
@@ -205,7 +210,7 @@ def gpu_run(args, w, torch, pkv, workloads):
         raise RuntimeError("decode produced non-finite output")
     res = dict(wall=wall, kernel_ms=kernel_ms, merge_ms=merge_ms, bytes=step_bytes[args.warmup:],
                unique_bytes=step_unique[args.warmup:],
-               batch=b, part=part)
+               batch=b, part=part, shared=shared)
     if w.chunk and not args.no_prefill:
         res["prefill"] = prefill_run(w, p, alloc, kc, vc, torch, pkv, dev)
     return res
@@ -694,7 +699,8 @@ def main():
         "config": {"workload": w.name, "num_seqs": w.num_seqs, "num_heads": w.num_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                    "block_size": w.block_size, "context_lens": w.lens,
-                   "shared_prefix": w.prefix, "partition_size": r["part"]},
+                   "shared_prefix": w.prefix, "partition_size": r["part"],
+                   "kv_loads": "cached (shared blocks)" if r["shared"] else "non-temporal"},
         "hbm_peak_frac": round(value / HBM_PEAK_GBPS, 4),
         "tokens_per_s": round(r["batch"] / (ms_step * 1e-3), 1),
         "kv_bytes_per_step": int(mean_bytes),

@@ -76,6 +76,18 @@ typedef enum pkv_dtype {
   PKV_FP8_E4M3 = 3
 } pkv_dtype;
 
+/* Load-policy hint for the decode calls, OR'd into their dtype (or
+ * query_dtype) argument; it never changes a result, only how the cache is
+ * read.  Blocks may be shared by several sequences (explainer, section on
+ * memory sharing: forked requests map the same physical blocks; tutorial
+ * §1.4).  Without the hint, K/V are read with non-temporal loads, which
+ * suit a batch whose sequences each own their blocks: every cached token is
+ * read once per step.  With it, K/V are read with the default cache policy,
+ * so a block that several sequences of the batch share is fetched from HBM
+ * once and served from the caches for the others.  The allocator's
+ * refcounts (pkv_block_refcount > 1) tell the caller when to set it. */
+enum { PKV_DECODE_SHARED_BLOCKS = 0x100 };
+
 /* Description of the last failure on the calling thread ("" if none). */
 const char* pkv_last_error(void);
 

@@ -602,6 +602,16 @@ _FP8_CODE = 3
 _FP8_TYPES = (torch.uint8, torch.float8_e4m3fn)
 
 
+# pkv.h PKV_DECODE_SHARED_BLOCKS: OR'd into a decode call's dtype when
+# blocks are shared by several sequences of the batch (cached K/V loads
+# instead of streaming ones; results are unchanged)
+DECODE_SHARED_BLOCKS = 0x100
+
+
+def _decode_code(t, shared_blocks):
+    return _dtype_code(t) | (DECODE_SHARED_BLOCKS if shared_blocks else 0)
+
+
 def _dtype_code(t):
     if t.dtype in _FP8_TYPES:
         return _FP8_CODE
@@ -749,12 +759,15 @@ def _decode_args(query, key_cache, value_cache, block_tables, context_lens, max_
 
 
 def paged_attention_decode(query, key_cache, value_cache, block_tables, context_lens, scale,
-                           max_context_len, partition_size=0, out=None, workspace=None):
+                           max_context_len, partition_size=0, out=None, workspace=None,
+                           shared_blocks=False):
     """Decode attention (pkv_paged_attention_decode).
 
     query [B, Hq, D] (cache dtype); block_tables [B, max_blocks] int32;
     context_lens [B] int32; returns out [B, Hq, D] float32.
     ``max_context_len`` is a host-side bound on context_lens (sizes the grid).
+    ``shared_blocks``: some blocks are shared by several sequences of the
+    batch (PKV_DECODE_SHARED_BLOCKS; same result, cached loads).
     """
     (nb, hkv, bs, d, b, hq), out, workspace, ws_ptr, ws_bytes = _decode_args(
         query, key_cache, value_cache, block_tables, context_lens, max_context_len,
@@ -763,7 +776,7 @@ def paged_attention_decode(query, key_cache, value_cache, block_tables, context_
         query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(), block_tables.data_ptr(),
         context_lens.data_ptr(), b, hq, hkv, d, bs, block_tables.shape[1], nb,
         int(max_context_len), float(scale), int(partition_size), out.data_ptr(), ws_ptr, ws_bytes,
-        _dtype_code(key_cache), _stream(query)))
+        _decode_code(key_cache, shared_blocks), _stream(query)))
     return out
 
 
@@ -817,10 +830,12 @@ class DecodeLauncher:
     max_context_len is within the bound the workspace was sized for.  The
     library checks everything else, as for the plain functions.
     ``partials`` (with ``key``/``value``: the append fused in) and ``merge``
-    are the two stages of paged_attention_decode(_append)."""
+    are the two stages of paged_attention_decode(_append).  ``shared_blocks``
+    sets PKV_DECODE_SHARED_BLOCKS on every launch."""
 
     def __init__(self, key_cache, value_cache, num_heads, num_seqs, max_blocks,
-                 max_context_len, partition_size, out, workspace, stream=None):
+                 max_context_len, partition_size, out, workspace, stream=None,
+                 shared_blocks=False):
         nb, hkv, bs, d = _cache_dims(key_cache, value_cache)
         _dev(out, "out", dtype=torch.float32, ndim=3)
         if tuple(out.shape) != (num_seqs, num_heads, d):
@@ -846,7 +861,7 @@ class DecodeLauncher:
         self._dims = (num_seqs, num_heads, hkv, d, bs, max_blocks, nb)
         self._kc, self._vc, self._out = key_cache.data_ptr(), value_cache.data_ptr(), out.data_ptr()
         self._ws = (ws_ptr, ws_bytes)
-        self._code = _dtype_code(key_cache)
+        self._code = _decode_code(key_cache, shared_blocks)
 
     def _check_step(self, t, shape, dtype, name):
         if t.shape != shape or t.dtype != dtype or not t.is_contiguous():
@@ -914,7 +929,7 @@ class DecodeLauncher:
 
 def paged_attention_decode_step(query, key, value, key_cache, value_cache, block_tables,
                                 context_lens, changes, scale, max_context_len, partition_size=0,
-                                out=None, workspace=None):
+                                out=None, workspace=None, shared_blocks=False):
     """Decode step with host metadata by value (pkv_paged_attention_decode_step).
 
     block_tables: device int32 [B, max_blocks], updated in place with
@@ -940,8 +955,8 @@ def paged_attention_decode_step(query, key, value, key_cache, value_cache, block
         query.data_ptr(), kp, vp, key_cache.data_ptr(), value_cache.data_ptr(),
         block_tables.data_ptr(), lens.ctypes.data, changes.ctypes.data, changes.shape[0], b, hq,
         hkv, d, bs, block_tables.shape[1], nb, int(max_context_len), float(scale),
-        int(partition_size), out.data_ptr(), ws_ptr, ws_bytes, _dtype_code(key_cache),
-        _stream(query)))
+        int(partition_size), out.data_ptr(), ws_ptr, ws_bytes,
+        _decode_code(key_cache, shared_blocks), _stream(query)))
     return out
 
 
@@ -980,7 +995,7 @@ def paged_kv_append_fp8(key, value, key_cache, value_cache, slot_mapping, k_scal
 
 
 def _decode_fp8(fn, query, key_cache, value_cache, block_tables, context_lens, scale, k_scale,
-                v_scale, max_context_len, partition_size, out, workspace):
+                v_scale, max_context_len, partition_size, out, workspace, shared_blocks=False):
     (nb, hkv, bs, d, b, hq), out, workspace, ws_ptr, ws_bytes = _decode_args(
         query, key_cache, value_cache, block_tables, context_lens, max_context_len,
         partition_size, out, workspace, fp8=True)
@@ -988,19 +1003,19 @@ def _decode_fp8(fn, query, key_cache, value_cache, block_tables, context_lens, s
               block_tables.data_ptr(), context_lens.data_ptr(), b, hq, hkv, d, bs,
               block_tables.shape[1], nb, int(max_context_len), float(scale), float(k_scale),
               float(v_scale), int(partition_size), out.data_ptr(), ws_ptr, ws_bytes,
-              _dtype_code(query), _stream(query)))
+              _decode_code(query, shared_blocks), _stream(query)))
     return out
 
 
 def paged_attention_decode_fp8(query, key_cache, value_cache, block_tables, context_lens, scale,
                                k_scale, v_scale, max_context_len, partition_size=0, out=None,
-                               workspace=None):
+                               workspace=None, shared_blocks=False):
     """Decode over 8-bit E4M3 caches (pkv_paged_attention_decode_fp8): as
     paged_attention_decode with K = code value * k_scale, V = code value *
     v_scale; query bfloat16 or float16; returns out [B, Hq, D] float32."""
     return _decode_fp8(_lib.pkv_paged_attention_decode_fp8, query, key_cache, value_cache,
                        block_tables, context_lens, scale, k_scale, v_scale, max_context_len,
-                       partition_size, out, workspace)
+                       partition_size, out, workspace, shared_blocks)
 
 
 def paged_attention_decode_fp8_partials(query, key_cache, value_cache, block_tables,

@@ -379,12 +379,15 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 // each lane adds its constant 32-bit offset.  Units past the last block of
 // the partition re-read its last block (always a valid block id) so every
 // load is in bounds and the issue is branch-free; the values they bring
-// are masked out by the callers.  The loads are non-temporal: a decode step
-// reads each cached token once, so K/V should stream past the caches
-// rather than evict what is reused (measured: +4-6% on batches with private
-// caches, -7% where a 16 MB shared prefix was being served from the
-// caches).
-template <class C, int U>
+// are masked out by the callers.  kStream selects non-temporal loads: when
+// every sequence owns its blocks, a decode step reads each cached token
+// once, so K/V should stream past the caches rather than evict what is
+// reused (+4-8% on batches with private caches).  When blocks are shared
+// by several sequences of the batch (a forked prefix), each shared block
+// is read once per sequence and the caches serve all reads after the
+// first, so the loads keep the default policy (14% faster on 256
+// sequences sharing a 1024-token prefix).
+template <class C, int U, bool kStream>
 __device__ __forceinline__ void issue_chunk(uint4 (&buf)[U], const uint8_t* tiles,
                                             const int* s_blk, int c, int nblk,
                                             int log2_bs, int64_t blk_stride,
@@ -400,7 +403,10 @@ __device__ __forceinline__ void issue_chunk(uint4 (&buf)[U], const uint8_t* tile
   for (int u = 0; u < U; ++u) {
     const int tu = c * C::kChunkTok + u * C::kTpl;
     const uint8_t* unit = tiles + (int64_t(blk[u]) * blk_stride + (tu & bs_mask) * C::kRow);
-    const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(unit + lane_off));
+    const u32x4* at = reinterpret_cast<const u32x4*>(unit + lane_off);
+    u32x4 t;
+    if constexpr (kStream) t = __builtin_nontemporal_load(at);
+    else t = *at;
     buf[u] = make_uint4(t.x, t.y, t.z, t.w);
   }
 }
@@ -421,6 +427,7 @@ struct DecodeParams {
   int32_t num_kv_heads, log2_bs, max_blocks, num_blocks, max_ctx, part, max_parts;
   float scale_log2;            // scale * log2(e), times the K scale of an 8-bit cache
   float v_scale;               // V scale of an 8-bit cache (unused otherwise)
+  int32_t shared_blocks;       // nonzero: launch the cached-load kernel (shared blocks)
 };
 
 // Where a launch gets each sequence's length and which table entries it
@@ -463,7 +470,8 @@ constexpr int decode_min_blocks() {
 }
 
 // Dynamic LDS: [scores: max(part*G, kWaves*G*D) floats][block ids][m/l].
-template <int DT, int D, int G, int U, class Meta>
+// kStream: non-temporal K/V loads (blocks private to their sequences).
+template <int DT, int D, int G, int U, class Meta, bool kStream>
 __global__ __launch_bounds__(kThreads, (decode_min_blocks<DT, G>())) void decode_partition_kernel(
     const DecodeParams prm, const Meta meta) {
   using C = Cfg<DT, D, G, U>;
@@ -619,13 +627,14 @@ __global__ __launch_bounds__(kThreads, (decode_min_blocks<DT, G>())) void decode
   {
     uint4 ka[U], kb[U];
     if (nj > 0) {
-      issue_chunk<C, U>(ka, kbase, s_blk, my_chunk(0), nblk, log2_bs, blk_stride, lane_off);
+      issue_chunk<C, U, kStream>(ka, kbase, s_blk, my_chunk(0), nblk, log2_bs, blk_stride,
+                                 lane_off);
       for (int j = 0; j < nj; j += 2) {
-        issue_chunk<C, U>(kb, kbase, s_blk, my_chunk(j + 1), nblk, log2_bs, blk_stride,
-                          lane_off);
+        issue_chunk<C, U, kStream>(kb, kbase, s_blk, my_chunk(j + 1), nblk, log2_bs,
+                                   blk_stride, lane_off);
         qk(ka, my_chunk(j));
-        issue_chunk<C, U>(ka, kbase, s_blk, my_chunk(j + 2), nblk, log2_bs, blk_stride,
-                          lane_off);
+        issue_chunk<C, U, kStream>(ka, kbase, s_blk, my_chunk(j + 2), nblk, log2_bs,
+                                   blk_stride, lane_off);
         if (j + 1 < nj) qk(kb, my_chunk(j + 1));
       }
     }
@@ -687,13 +696,14 @@ __global__ __launch_bounds__(kThreads, (decode_min_blocks<DT, G>())) void decode
   {
     uint4 va[U], vb[U];
     if (nj > 0) {
-      issue_chunk<C, U>(va, vbase, s_blk, my_chunk(0), nblk, log2_bs, blk_stride, lane_off);
+      issue_chunk<C, U, kStream>(va, vbase, s_blk, my_chunk(0), nblk, log2_bs, blk_stride,
+                                 lane_off);
       for (int j = 0; j < nj; j += 2) {
-        issue_chunk<C, U>(vb, vbase, s_blk, my_chunk(j + 1), nblk, log2_bs, blk_stride,
-                          lane_off);
+        issue_chunk<C, U, kStream>(vb, vbase, s_blk, my_chunk(j + 1), nblk, log2_bs,
+                                   blk_stride, lane_off);
         pv(va, my_chunk(j));
-        issue_chunk<C, U>(va, vbase, s_blk, my_chunk(j + 2), nblk, log2_bs, blk_stride,
-                          lane_off);
+        issue_chunk<C, U, kStream>(va, vbase, s_blk, my_chunk(j + 2), nblk, log2_bs,
+                                   blk_stride, lane_off);
         if (j + 1 < nj) pv(vb, my_chunk(j + 1));
       }
     }
@@ -826,9 +836,13 @@ hipError_t launch_decode(const DecodeParams& prm, const Meta& meta, int B, hipSt
   const size_t lds = size_t(score_floats) * 4 + size_t(prm.part >> 3) * 4 +
                      size_t(2 * kWaves * G) * 4;
   if (lds > 160 * 1024) return hipErrorInvalidValue;  // beyond one CU's LDS
-  hipLaunchKernelGGL((decode_partition_kernel<DT, D, G, kUnitsPerChunk, Meta>),
-                     dim3(prm.num_kv_heads, B, prm.max_parts), dim3(kThreads), lds, stream, prm,
-                     meta);
+  const dim3 grid(prm.num_kv_heads, B, prm.max_parts);
+  if (prm.shared_blocks)
+    hipLaunchKernelGGL((decode_partition_kernel<DT, D, G, kUnitsPerChunk, Meta, false>), grid,
+                       dim3(kThreads), lds, stream, prm, meta);
+  else
+    hipLaunchKernelGGL((decode_partition_kernel<DT, D, G, kUnitsPerChunk, Meta, true>), grid,
+                       dim3(kThreads), lds, stream, prm, meta);
   return hipGetLastError();
 }
 
@@ -1027,6 +1041,8 @@ int32_t run_decode(const void* query, const void* key_new, const void* value_new
                    size_t workspace_bytes_given, int32_t dtype, void* stream, bool partials,
                    bool merge, const StepMeta* step, float k_scale = 1.0f,
                    float v_scale = 1.0f) {
+  const bool shared_blocks = (dtype & PKV_DECODE_SHARED_BLOCKS) != 0;
+  dtype &= ~int32_t(PKV_DECODE_SHARED_BLOCKS);
   DecodeArgs a;
   const int32_t* lens_check = step ? reinterpret_cast<const int32_t*>(step->lens) : context_lens;
   int32_t st = prepare_decode(query, key_cache, value_cache, block_tables, lens_check,
@@ -1062,6 +1078,7 @@ int32_t run_decode(const void* query, const void* key_new, const void* value_new
   prm.max_parts = a.max_parts;
   prm.scale_log2 = k_scale == 1.0f ? scale * kLog2e : (scale * k_scale) * kLog2e;
   prm.v_scale = v_scale;
+  prm.shared_blocks = shared_blocks ? 1 : 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
   if (partials) {
@@ -1271,6 +1288,8 @@ int32_t fp8_call(const void* query, const void* key_cache, const void* value_cac
                  float scale, float k_scale, float v_scale, int32_t partition_size, float* out,
                  void* workspace, size_t workspace_bytes_given, int32_t query_dtype,
                  void* stream, bool merge) {
+  const int32_t hint = query_dtype & int32_t(PKV_DECODE_SHARED_BLOCKS);
+  query_dtype &= ~int32_t(PKV_DECODE_SHARED_BLOCKS);
   if (query_dtype != PKV_BF16 && query_dtype != PKV_F16)
     return fail(PKV_ERR_INVALID, "query_dtype %d must be BF16 or F16 for an 8-bit cache",
                 query_dtype);
@@ -1280,7 +1299,7 @@ int32_t fp8_call(const void* query, const void* key_cache, const void* value_cac
                     context_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                     max_blocks_per_seq, num_blocks, max_context_len, scale, partition_size,
                     out, workspace, workspace_bytes_given,
-                    query_dtype == PKV_BF16 ? kFp8QBf16 : kFp8QF16, stream, true, merge,
+                    (query_dtype == PKV_BF16 ? kFp8QBf16 : kFp8QF16) | hint, stream, true, merge,
                     nullptr, k_scale, v_scale);
 }
 }  // namespace

@@ -466,3 +466,77 @@ def test_step_call_limits():
     with pytest.raises(pkv.InvalidArgument):  # change row outside the batch
         pkv.paged_attention_decode_step(q[:2].contiguous(), None, None, kc, kc, t[:2].contiguous(),
                                         lens[:2], np.array([[5, 0, 1]]), w.scale, 1)
+
+
+HINT = ["tiny_fp32_long", "llama13b_small", "gqa_small", "gqa4_d64_bs8", "shared_prefix_small"]
+
+
+@pytest.mark.parametrize("name", HINT)
+def test_shared_blocks_hint_changes_no_bit(name):
+    """PKV_DECODE_SHARED_BLOCKS launches the cached-load kernel; it must
+    give exactly the output of the streaming-load kernel (the same
+    arithmetic), in one call and split into partials + merge."""
+    w = SMALL[name]
+    log("case", name)
+    g = GpuState(w, workloads.plan(w))
+    tables, lens, _, lens_h = g.tables()
+    q, _ = decode_queries(w, g.p.seqs)
+    q = q.to(DEV)
+    mc = int(lens_h.max())
+    for part in (64, 0):
+        want = pkv.paged_attention_decode(q, g.kc, g.vc, tables, lens, w.scale, mc,
+                                          partition_size=part)
+        got = pkv.paged_attention_decode(q, g.kc, g.vc, tables, lens, w.scale, mc,
+                                         partition_size=part, shared_blocks=True)
+        torch.cuda.synchronize()
+        assert torch.equal(got, want), part
+
+
+def test_shared_blocks_hint_step_and_launcher():
+    """The hint on the step call and on a DecodeLauncher: bitwise the
+    unhinted calls, steps with copy-on-write included."""
+    w = STEP["bf16_shared_cow"]
+    p = workloads.plan(w)
+    a, b = GpuState(w, p), GpuState(w, p)
+    seqs = p.seqs
+    steps, part = 6, 64
+    mb = max(len(a.alloc.block_table(s)) for s in seqs) + steps // w.block_size + 2
+    dev = []
+    for x in (a, b):
+        th, _ = x.alloc.build_block_tables(seqs, mb)
+        dev.append(torch.from_numpy(th.copy()).to(DEV))
+    ones = np.ones(len(seqs), dtype=np.int32)
+    for i in range(steps):
+        k, v = workloads.kv_rows(w, len(p.ops) + i, len(seqs))
+        kt = workloads.to_dtype(k, w.dtype).to(DEV)
+        vt = workloads.to_dtype(v, w.dtype).to(DEV)
+        q = workloads.to_dtype(workloads.normal([w.seed, 9, i], (len(seqs), w.num_heads,
+                                                                  w.head_dim), w.std),
+                               w.dtype).to(DEV)
+        outs = []
+        for x, t, hint in ((a, dev[0], False), (b, dev[1], True)):
+            _, pairs, lens, changes = x.alloc.append_batch_changes(seqs, ones)
+            if pairs:
+                x._copy(pairs)
+            outs.append(pkv.paged_attention_decode_step(
+                q, kt, vt, x.kc, x.vc, t, lens, changes, w.scale, int(lens.max()),
+                partition_size=part, shared_blocks=hint))
+        torch.cuda.synchronize()
+        assert torch.equal(outs[0], outs[1]), f"step {i}"
+    tables, lens, _, lh = b.tables(seqs)
+    tables = torch.nn.functional.pad(tables, (0, mb - tables.shape[1]), value=-1).contiguous()
+    mc = int(lh.max())
+    q, _ = decode_queries(w, seqs)
+    q = q.to(DEV)
+    want = pkv.paged_attention_decode(q, b.kc, b.vc, tables, lens, w.scale, mc,
+                                      partition_size=part)
+    need = pkv.paged_attention_decode_workspace_size(len(seqs), w.num_heads, w.num_kv_heads,
+                                                     w.head_dim, mc, part)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(want)
+    launch = pkv.DecodeLauncher(b.kc, b.vc, w.num_heads, len(seqs), mb, mc, part, out, ws,
+                                shared_blocks=True)
+    launch.partials(q, tables, lens, mc, w.scale)
+    launch.merge(lens, mc)
+    torch.cuda.synchronize()
+    assert torch.equal(out, want)

@@ -236,3 +236,19 @@ def test_fp8_rejects_bad_arguments():
     with pytest.raises(pkv.InvalidArgument):
         # a 16-bit call on 8-bit caches
         pkv.paged_attention_decode(q.to(DEV), g.kc, g.vc, tables, lens, w.scale, 20)
+
+
+def test_fp8_shared_blocks_hint_changes_no_bit():
+    w, ks, vs, _ = DECODE_CASES["llama7b_part64"]
+    p = workloads.plan(w)
+    g = GpuStateFp8(w, p, ks, vs)
+    tables, lens, _, lh = g.tables()
+    q, _ = decode_queries(w, p.seqs)
+    qd = q.to(DEV)
+    mc = int(lh.max())
+    want = pkv.paged_attention_decode_fp8(qd, g.kc, g.vc, tables, lens, w.scale, ks, vs, mc,
+                                          partition_size=64)
+    got = pkv.paged_attention_decode_fp8(qd, g.kc, g.vc, tables, lens, w.scale, ks, vs, mc,
+                                         partition_size=64, shared_blocks=True)
+    torch.cuda.synchronize()
+    assert torch.equal(got, want)
