@@ -216,6 +216,48 @@ def test_full_size_sampled_against_oracle(name):
     assert worst <= TOL[w.dtype]
     assert np.isfinite(got).all()
 
+    # Then the step path bench.py times, at the same size: batch append with
+    # table changes, the step call with each sequence's new K/V row stored
+    # by the kernel, the library's partition size (the grid order that goes
+    # with it) and the shared-blocks hint when blocks are shared.  Two
+    # steps; the second is checked on the same sampled sequences.
+    seqs = p.seqs
+    nb = len(seqs)
+    mb = th.shape[1] + 2
+    t0, _ = g.alloc.build_block_tables(seqs, mb)
+    dev_tables = torch.from_numpy(t0.copy()).to(DEV)
+    shared = any(r > 1 for r in g.alloc.snapshot()[1])
+    ones = np.ones(nb, dtype=np.int32)
+    new_k, new_v = [], []
+    for i in range(2):
+        k, v = workloads.kv_rows(w, len(p.ops) + i, nb)
+        kt, vt = workloads.to_dtype(k, w.dtype), workloads.to_dtype(v, w.dtype)
+        new_k.append(workloads.as_f64(kt))
+        new_v.append(workloads.as_f64(vt))
+        qt = workloads.to_dtype(workloads.normal([w.seed, 11, i], (nb, w.num_heads, w.head_dim),
+                                                 w.std), w.dtype)
+        _, pairs, step_lens, changes = g.alloc.append_batch_changes(seqs, ones)
+        if pairs:
+            g._copy(pairs)
+        out = pkv.paged_attention_decode_step(qt.to(DEV), kt.to(DEV), vt.to(DEV), g.kc, g.vc,
+                                              dev_tables, step_lens, changes, w.scale,
+                                              int(step_lens.max()),
+                                              partition_size=w.partition_size,
+                                              shared_blocks=shared)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    q64 = workloads.as_f64(qt)
+    worst = 0.0
+    for b in pick:
+        k, v = logical_kv(w, segs[p.seqs[b]])
+        k = np.concatenate([k] + [x[b][None] for x in new_k])
+        v = np.concatenate([v] + [x[b][None] for x in new_v])
+        want = dense_attention(q64[b][None], k, v, w.scale)[0]
+        worst = max(worst, max_abs_err(got[b], want))
+    log(name, "step path sampled max abs err", worst, "shared hint", shared)
+    assert worst <= TOL[w.dtype]
+    assert np.isfinite(got).all()
+
 
 # ---------------------------------------------------------------------------
 # one-call decode vs its two stages; decode with the append fused in
@@ -409,18 +451,28 @@ STEP = {
 }
 
 
-@pytest.mark.parametrize("name", list(STEP))
-def test_step_call_is_full_upload_decode(name):
+# (workload, steps, partition): 64-token partitions keep the grid
+# partition-major; 1024-token ones over contexts up to 3000 take the grid
+# that dispatches a sequence's partitions together
+STEP_RUNS = {"bf16_shared_cow": ("bf16_shared_cow", 20, 64),
+             "gqa8_fp16_bs32": ("gqa8_fp16_bs32", 20, 64),
+             "bf16_long_part1024": ("bf16_long", 4, 1024)}
+STEP["bf16_long"] = workloads.scaled(workloads.get("llama7b_bf16"), num_seqs=7, num_heads=4,
+                                     num_kv_heads=2, lens="uniform:1,3000")
+
+
+@pytest.mark.parametrize("run", list(STEP_RUNS))
+def test_step_call_is_full_upload_decode(run):
     """pkv_paged_attention_decode_step (lengths and table changes by value,
     a device table kept across steps) == pkv_paged_attention_decode_append
     with freshly uploaded tables, bit for bit: outputs, caches and, at the
     end, the device table itself."""
+    name, steps, part = STEP_RUNS[run]
     w = STEP[name]
-    log("case", name)
+    log("case", name, steps, part)
     p = workloads.plan(w)
     a, b = GpuState(w, p), GpuState(w, p)
     seqs = p.seqs
-    steps, part = 20, 64
     mb = max(len(a.alloc.block_table(s)) for s in seqs) + steps // w.block_size + 2
     th, _ = b.alloc.build_block_tables(seqs, mb)
     dev_tables = torch.from_numpy(th.copy()).to(DEV)   # b's table, kept on the device
