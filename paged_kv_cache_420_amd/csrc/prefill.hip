@@ -239,7 +239,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
     const int key0 = j * kKTile;
 #pragma unroll
     for (int i = 0; i < kPieces; ++i) {
-      const int gkey = min(key0 + kPieceStride * i + 16 * (pk >> 4), kv_end - 1);  // uniform
+      // the piece's 16-key group, 16 (pk >> 4) = 16 (tid >> 8), is the same
+      // for all lanes of a wave: taken from the wave index it is a scalar,
+      // so the table read and the group's address are scalar work
+      const int gkey = min(key0 + kPieceStride * i + 16 * (wave >> 2), kv_end - 1);
       int id = __builtin_amdgcn_readfirstlane(table[gkey >> log2_bs]);
       if (id < 0 || id >= num_blocks) {
         bad_blk = true;
