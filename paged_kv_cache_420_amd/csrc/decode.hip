@@ -609,13 +609,57 @@ __global__ __launch_bounds__(kThreads, (decode_min_blocks<DT, G>())) void decode
   const uint32_t lane_off = uint32_t(tok_in_unit * C::kRow + dl * 16);
   const int nchunks = cdiv(ntok, C::kChunkTok);
   // This wave's chunks are wave, wave + kWaves, ...: nj of them.  The walk
-  // over them keeps the next chunk's loads in flight while one is computed,
-  // in two register buffers (no copies between them).  The prefetch is
-  // issued unconditionally -- past the end it re-reads the wave's last
-  // chunk, an L2 hit -- so the wait before each compute covers exactly the
-  // buffer it reads.
+  // over them (walk() below) keeps the next chunk's loads in flight while
+  // one is computed, in two register buffers (no copies between them).  Its
+  // loop runs while two more chunks exist, so every load it issues is
+  // needed and one chunk's loads are outstanding at the loop head; the last
+  // one or two chunks are computed after it.  The wait before each compute
+  // then covers exactly the buffer it reads, and no load re-reads a chunk
+  // (with streaming loads such a re-read would come from HBM again).
   const int nj = wave < nchunks ? (nchunks - 1 - wave) / kWaves + 1 : 0;
-  auto my_chunk = [&](int j) { return wave + min(j, nj - 1) * kWaves; };
+  auto my_chunk = [&](int j) { return wave + j * kWaves; };
+  // 8-bit caches at G = 8 and head_dim 128 hold 128 accumulator floats per
+  // lane: there the peeled tail's second copy of the compute costs spills,
+  // and the walk keeps one loop whose prefetch past the end re-reads the
+  // wave's last chunk instead (192 VGPRs, two waves per SIMD).
+  constexpr bool kPeeled = !(E::kQuantised && G >= 8 && D >= 128);
+  auto walk = [&](const uint8_t* base, auto&& compute) {
+    if (nj == 0) return;
+    uint4 a[U], b[U];
+    if constexpr (!kPeeled) {
+      auto clamped = [&](int j) { return my_chunk(min(j, nj - 1)); };
+      issue_chunk<C, U, kStream>(a, base, s_blk, clamped(0), nblk, log2_bs, blk_stride,
+                                 lane_off);
+      for (int j = 0; j < nj; j += 2) {
+        issue_chunk<C, U, kStream>(b, base, s_blk, clamped(j + 1), nblk, log2_bs, blk_stride,
+                                   lane_off);
+        compute(a, clamped(j));
+        issue_chunk<C, U, kStream>(a, base, s_blk, clamped(j + 2), nblk, log2_bs, blk_stride,
+                                   lane_off);
+        if (j + 1 < nj) compute(b, clamped(j + 1));
+      }
+      return;
+    }
+    issue_chunk<C, U, kStream>(a, base, s_blk, my_chunk(0), nblk, log2_bs, blk_stride,
+                               lane_off);
+    int j = 0;
+    for (; j + 2 < nj; j += 2) {
+      issue_chunk<C, U, kStream>(b, base, s_blk, my_chunk(j + 1), nblk, log2_bs, blk_stride,
+                                 lane_off);
+      compute(a, my_chunk(j));
+      issue_chunk<C, U, kStream>(a, base, s_blk, my_chunk(j + 2), nblk, log2_bs, blk_stride,
+                                 lane_off);
+      compute(b, my_chunk(j + 1));
+    }
+    if (j + 1 < nj) {
+      issue_chunk<C, U, kStream>(b, base, s_blk, my_chunk(j + 1), nblk, log2_bs, blk_stride,
+                                 lane_off);
+      compute(a, my_chunk(j));
+      compute(b, my_chunk(j + 1));
+    } else {
+      compute(a, my_chunk(j));
+    }
+  };
 
   // ---- QK pass ------------------------------------------------------------
   // After the reduction a lane's value i is slot slot0 + i: head
@@ -642,21 +686,7 @@ __global__ __launch_bounds__(kThreads, (decode_min_blocks<DT, G>())) void decode
       }
     }
   };
-  {
-    uint4 ka[U], kb[U];
-    if (nj > 0) {
-      issue_chunk<C, U, kStream>(ka, kbase, s_blk, my_chunk(0), nblk, log2_bs, blk_stride,
-                                 lane_off);
-      for (int j = 0; j < nj; j += 2) {
-        issue_chunk<C, U, kStream>(kb, kbase, s_blk, my_chunk(j + 1), nblk, log2_bs,
-                                   blk_stride, lane_off);
-        qk(ka, my_chunk(j));
-        issue_chunk<C, U, kStream>(ka, kbase, s_blk, my_chunk(j + 2), nblk, log2_bs,
-                                   blk_stride, lane_off);
-        if (j + 1 < nj) qk(kb, my_chunk(j + 1));
-      }
-    }
-  }
+  walk(kbase, qk);
   __syncthreads();
 
   // ---- softmax over the partition (entries e = t * G + g; a thread only
@@ -711,21 +741,7 @@ __global__ __launch_bounds__(kThreads, (decode_min_blocks<DT, G>())) void decode
       }
     }
   };
-  {
-    uint4 va[U], vb[U];
-    if (nj > 0) {
-      issue_chunk<C, U, kStream>(va, vbase, s_blk, my_chunk(0), nblk, log2_bs, blk_stride,
-                                 lane_off);
-      for (int j = 0; j < nj; j += 2) {
-        issue_chunk<C, U, kStream>(vb, vbase, s_blk, my_chunk(j + 1), nblk, log2_bs,
-                                   blk_stride, lane_off);
-        pv(va, my_chunk(j));
-        issue_chunk<C, U, kStream>(va, vbase, s_blk, my_chunk(j + 2), nblk, log2_bs,
-                                   blk_stride, lane_off);
-        if (j + 1 < nj) pv(vb, my_chunk(j + 1));
-      }
-    }
-  }
+  walk(vbase, pv);
 
   // ---- combine token rows within the wave, then the waves ----------------
   // Each lane ends with kOut of the G * kEpl sums of its d-slice: flat index
