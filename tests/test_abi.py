@@ -112,6 +112,39 @@ def test_device_calls_reject_bad_arguments_before_launch():
                                           100, 1.0, 0, null, null, 0, 2, null) == 0
 
 
+def test_shared_blocks_hint_is_checked_like_the_dtype_it_rides_on():
+    """PKV_DECODE_SHARED_BLOCKS (0x100) is taken off a decode call's dtype
+    before the dtype and everything else are checked; calls that move bytes
+    (append, block copies) do not take it."""
+    lib = pkv._lib
+    null = None
+    hint = pkv.DECODE_SHARED_BLOCKS
+    assert hint == 0x100
+    # a valid dtype with the hint: the remaining checks still run
+    assert lib.pkv_paged_attention_decode(null, null, null, null, null, 2, 4, 4, 128, 16, 8, 64,
+                                          100, 1.0, 0, null, null, 0, 2 | hint, null) == 1
+    assert b"NULL" in lib.pkv_last_error()
+    assert lib.pkv_paged_attention_decode(null, null, null, null, null, 2, 6, 2, 128, 16, 8, 64,
+                                          100, 1.0, 0, null, null, 0, 2 | hint, null) == 7
+    assert lib.pkv_paged_attention_decode(null, null, null, null, null, 0, 4, 4, 128, 16, 8, 64,
+                                          100, 1.0, 0, null, null, 0, 2 | hint, null) == 0
+    # an unknown dtype stays unknown with the hint
+    assert lib.pkv_paged_attention_decode(null, null, null, null, null, 2, 4, 4, 128, 16, 8, 64,
+                                          100, 1.0, 0, null, null, 0, 9 | hint, null) == 1
+    assert b"dtype" in lib.pkv_last_error()
+    # 8-bit decode: the hint rides on the query dtype
+    assert lib.pkv_paged_attention_decode_fp8(null, null, null, null, null, 2, 4, 4, 128, 16, 8,
+                                              64, 100, 1.0, 0.5, 0.5, 0, null, null, 0,
+                                              0 | hint, null) == 1
+    assert lib.pkv_paged_attention_decode_fp8(null, null, null, null, null, 2, 4, 4, 128, 16, 8,
+                                              64, 100, 1.0, 0.5, 0.5, 0, null, null, 0,
+                                              2 | hint, null) == 1
+    assert b"NULL" in lib.pkv_last_error()
+    # the byte-moving calls reject it as an unknown dtype
+    assert lib.pkv_paged_kv_append(null, null, null, null, null, 1, 1, 64, 16, 4, 2 | hint,
+                                   null) == 1
+
+
 def test_allocator_reports_errors():
     with pytest.raises(pkv.InvalidArgument):
         pkv.BlockAllocator(4, 2, [0, 1, 1, 2])
