@@ -448,6 +448,8 @@ struct DeviceMeta {
     b = blockIdx.y;
     p = blockIdx.z;
   }
+  // merge grid (query head, sequence)
+  __device__ int merge_seq(int y) const { return y; }
 };
 
 struct StepMeta {
@@ -465,6 +467,9 @@ struct StepMeta {
   int32_t parts_per_rank;
   uint8_t order[kStepMaxSeqs];
   __device__ int len(const DecodeParams&, int b) const { return lens[b]; }
+  // merge grid (query head, rank): the launch covers only the ranks up to
+  // the last sequence that spans two partitions
+  __device__ int merge_seq(int y) const { return order[y]; }
   __device__ void work(int& b, int& p) const {
     if (parts_per_rank > 0) {
       const int y = blockIdx.y;
@@ -800,7 +805,7 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(
   const float* __restrict__ ws_ml = prm.ws_ml;
   float* __restrict__ out = prm.out;
   const int h = blockIdx.x;
-  const int b = blockIdx.y;
+  const int b = meta.merge_seq(blockIdx.y);
   const int n = meta.len(prm, b);
   const bool bad_len = n < 0 || n > max_ctx ||
                        int64_t(n) > (int64_t(max_blocks) << log2_bs);
@@ -1139,14 +1144,19 @@ int32_t run_decode(const void* query, const void* key_new, const void* value_new
     if (e != hipSuccess) return fail(PKV_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   }
   if (!merge || a.max_parts <= 1) return ok();
+  int32_t merge_rows = num_seqs;
   if (step) {
-    // the step's lengths are known here: when every sequence fits one
-    // partition the partition kernel wrote the final rows and no merge runs
-    bool multi = false;
-    for (int32_t i = 0; i < num_seqs && !multi; ++i) multi = step->lens[i] > a.part;
-    if (!multi) return ok();
+    // the step's lengths are known here: the merge covers the ranks of the
+    // work order up to the last sequence that spans two partitions (the
+    // order is longest first, so these are the leading ranks); when every
+    // sequence fits one partition the partition kernel wrote the final
+    // rows and no merge runs
+    merge_rows = 0;
+    for (int32_t i = 0; i < num_seqs; ++i)
+      if (step->lens[step->order[i]] > a.part) merge_rows = i + 1;
+    if (merge_rows == 0) return ok();
   }
-  e = step ? launch_merge(prm, *step, num_seqs, num_heads, head_dim, s)
+  e = step ? launch_merge(prm, *step, merge_rows, num_heads, head_dim, s)
            : launch_merge(prm, DeviceMeta{}, num_seqs, num_heads, head_dim, s);
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "decode merge launch: %s", hipGetErrorString(e));
   return ok();

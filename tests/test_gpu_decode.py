@@ -592,3 +592,44 @@ def test_shared_blocks_hint_step_and_launcher():
     launch.merge(lens, mc)
     torch.cuda.synchronize()
     assert torch.equal(out, want)
+
+
+@pytest.mark.parametrize("part", [64, 1024])
+def test_step_two_stages_are_the_one_call(part):
+    """DecodeLauncher.step_partials + step_merge (the two launches bench.py
+    times) == pkv_paged_attention_decode_step in one call, bit for bit, over
+    steps where some sequences span several partitions and others one (the
+    merge covers the leading ranks of the longest-first order only)."""
+    w = STEP["bf16_long"]
+    p = workloads.plan(w)
+    a, b = GpuState(w, p), GpuState(w, p)
+    seqs = p.seqs
+    nb, steps = len(seqs), 3
+    mb = max(len(a.alloc.block_table(s)) for s in seqs) + 2
+    mc_bound = max(a.alloc.seq_len(s) for s in seqs) + steps
+    dev = []
+    for x in (a, b):
+        th, _ = x.alloc.build_block_tables(seqs, mb)
+        dev.append(torch.from_numpy(th.copy()).to(DEV))
+    need = pkv.paged_attention_decode_workspace_size(nb, w.num_heads, w.num_kv_heads, w.head_dim,
+                                                     mc_bound, part)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=DEV)
+    out = torch.empty((nb, w.num_heads, w.head_dim), dtype=torch.float32, device=DEV)
+    launch = pkv.DecodeLauncher(b.kc, b.vc, w.num_heads, nb, mb, mc_bound, part, out, ws)
+    ones = np.ones(nb, dtype=np.int32)
+    for i in range(steps):
+        k, v = workloads.kv_rows(w, len(p.ops) + i, nb)
+        kt = workloads.to_dtype(k, w.dtype).to(DEV)
+        vt = workloads.to_dtype(v, w.dtype).to(DEV)
+        q = workloads.to_dtype(workloads.normal([w.seed, 13, i], (nb, w.num_heads, w.head_dim),
+                                                w.std), w.dtype).to(DEV)
+        _, _, la, ca = a.alloc.append_batch_changes(seqs, ones)
+        _, _, lb, cb = b.alloc.append_batch_changes(seqs, ones)
+        mc = int(la.max())
+        want = pkv.paged_attention_decode_step(q, kt, vt, a.kc, a.vc, dev[0], la, ca, w.scale, mc,
+                                               partition_size=part)
+        launch.step_partials(q, dev[1], lb, cb, len(cb), mc, w.scale, kt, vt)
+        launch.step_merge(lb, mc)
+        torch.cuda.synchronize()
+        assert (la > part).any() and (la <= part).any() or part == 64
+        assert torch.equal(out, want), f"step {i}"
