@@ -23,14 +23,14 @@ from oracle import dense_attention, paged_decode
 pytestmark = pytest.mark.gpu
 
 
-def run_decode(g, w, seqs=None, partition_size=None, max_ctx=None):
+def run_decode(g, w, seqs=None, partition_size=None, max_ctx=None, shared_blocks=False):
     seqs = g.p.seqs if seqs is None else seqs
     tables, lens, _, lens_h = g.tables(seqs)
     q, q64 = decode_queries(w, seqs)
     mc = int(lens_h.max()) if max_ctx is None else max_ctx
     part = w.partition_size if partition_size is None else partition_size
     out = pkv.paged_attention_decode(q.to(DEV), g.kc, g.vc, tables, lens, w.scale, mc,
-                                     partition_size=part)
+                                     partition_size=part, shared_blocks=shared_blocks)
     torch.cuda.synchronize()
     return out.cpu().numpy(), q64
 
@@ -104,6 +104,9 @@ def test_every_instantiation_matches_oracle(dt, d, grp):
     err = max_abs_err(got, want)
     log("max abs err", err)
     assert err <= TOL[w.dtype]
+    # the cached-load instantiation (shared-blocks hint): the same bits
+    hinted, _ = run_decode(g, w, partition_size=128, shared_blocks=True)
+    assert np.array_equal(hinted, got)
 
 
 @pytest.mark.parametrize("part", [64, 128, 256, 1024])
@@ -633,3 +636,43 @@ def test_step_two_stages_are_the_one_call(part):
         torch.cuda.synchronize()
         assert (la > part).any() and (la <= part).any() or part == 64
         assert torch.equal(out, want), f"step {i}"
+
+
+@pytest.mark.parametrize("dt,d,grp", SWEEP,
+                         ids=[f"{str(dt)[6:]}-d{d}-g{g}" for dt, d, g in SWEEP])
+def test_step_every_instantiation_is_full_upload_decode(dt, d, grp):
+    """Every step-form instantiation (lengths and table changes by value),
+    streaming and cached loads alternating by step, against the decode with
+    the append fused and freshly uploaded tables: the same bits, with
+    128-token partitions so that the merge runs."""
+    w = workloads.scaled(workloads.get("llama7b_bf16"), num_seqs=3, num_kv_heads=2,
+                         num_heads=2 * grp, head_dim=d, dtype=dt, lens="uniform:1,400",
+                         seed=4500 + d + grp)
+    log("case", w)
+    p = workloads.plan(w)
+    a, b = GpuState(w, p), GpuState(w, p)
+    seqs = p.seqs
+    steps, part = 4, 128
+    mb = max(len(a.alloc.block_table(s)) for s in seqs) + 2
+    th, _ = b.alloc.build_block_tables(seqs, mb)
+    dev_tables = torch.from_numpy(th.copy()).to(DEV)
+    ones = np.ones(len(seqs), dtype=np.int32)
+    for i in range(steps):
+        k, v = workloads.kv_rows(w, len(p.ops) + i, len(seqs))
+        kt = workloads.to_dtype(k, w.dtype).to(DEV)
+        vt = workloads.to_dtype(v, w.dtype).to(DEV)
+        q = workloads.to_dtype(workloads.normal([w.seed, 9, i], (len(seqs), w.num_heads,
+                                                                  w.head_dim), w.std),
+                               w.dtype).to(DEV)
+        a.alloc.append_batch(seqs, ones)
+        _, _, lens, changes = b.alloc.append_batch_changes(seqs, ones)
+        ta, la, _, lh = a.tables(seqs)
+        ta = torch.nn.functional.pad(ta, (0, mb - ta.shape[1]), value=-1).contiguous()
+        mc = int(lh.max())
+        want = pkv.paged_attention_decode_append(q, kt, vt, a.kc, a.vc, ta, la, w.scale, mc,
+                                                 partition_size=part)
+        got = pkv.paged_attention_decode_step(q, kt, vt, b.kc, b.vc, dev_tables, lens, changes,
+                                              w.scale, mc, partition_size=part,
+                                              shared_blocks=bool(i % 2))
+        torch.cuda.synchronize()
+        assert torch.equal(got, want), f"step {i}"

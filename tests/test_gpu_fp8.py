@@ -88,12 +88,13 @@ DECODE_CASES = {
 }
 
 
-def run_fp8(g, w, ks, vs, part, seqs=None):
+def run_fp8(g, w, ks, vs, part, seqs=None, shared_blocks=False):
     seqs = g.p.seqs if seqs is None else seqs
     tables, lens, _, lens_h = g.tables(seqs)
     q, q64 = decode_queries(w, seqs)
     out = pkv.paged_attention_decode_fp8(q.to(DEV), g.kc, g.vc, tables, lens, w.scale, ks, vs,
-                                         int(lens_h.max()), partition_size=part)
+                                         int(lens_h.max()), partition_size=part,
+                                         shared_blocks=shared_blocks)
     torch.cuda.synchronize()
     return out.cpu().numpy(), q64
 
@@ -137,6 +138,9 @@ def test_fp8_every_instantiation_matches_oracle(qt, d, grp):
     err = max_abs_err(got, want)
     log("max abs err", err)
     assert err <= TOL_FP8
+    # the cached-load instantiation (shared-blocks hint): the same bits
+    hinted, _ = run_fp8(g, w, ks, vs, 128, shared_blocks=True)
+    assert np.array_equal(hinted, got)
 
 
 def test_fp8_one_call_is_bitwise_its_two_stages():
