@@ -640,6 +640,51 @@ int32_t pkv_paged_attention_decode_fp8_partials(
     float v_scale, int32_t partition_size, float* out, void* workspace,
     size_t workspace_bytes, int32_t query_dtype, void* stream);
 
+/* Decode attention for a batch whose sequences all begin with the same
+ * prefix_len tokens: forked from one parent, they share its blocks
+ * (explainer, section on memory sharing: parallel samples and shared
+ * prompts map the same physical blocks; tutorial §1.4).  The result is
+ * pkv_paged_attention_decode's (article §2.1: softmax(scale q K^T) V over
+ * each sequence's whole context), computed in three launches:
+ *   1. every sequence's query against the shared prefix, as one dense
+ *      contraction per query head ([num_seqs x 128] by [128 x prefix_len])
+ *      on the matrix cores (the chunked-prefill kernel without the causal
+ *      limit), leaving unnormalised partials;
+ *   2. each sequence's private suffix, tokens [prefix_len, context_len),
+ *      by the split-K decode kernel, as partials;
+ *   3. the log-sum-exp merge of both.
+ * The prefix's K/V is read once per query head instead of once per
+ * sequence.
+ *   query, caches, block_tables, context_lens, sizes, scale, out, dtype:
+ *                  as pkv_paged_attention_decode; dtype PKV_F16 or
+ *                  PKV_BF16 (the matrix-core path), head_dim 128; the
+ *                  PKV_DECODE_SHARED_BLOCKS hint applies to the suffix loads
+ *   prefix_len     tokens shared by every sequence, a positive multiple of
+ *                  block_size, at most max_context_len.  The caller
+ *                  guarantees that tokens [0, prefix_len) hold the same K/V
+ *                  in every sequence (a fork, or copies of one); they are
+ *                  read through row 0 of block_tables.  A sequence whose
+ *                  device length is below prefix_len gets a NaN row.
+ *   partition_size split-K partition of the suffixes (0 = automatic)
+ *   workspace      float32 partials, at least the bytes
+ *                  pkv_paged_attention_decode_shared_prefix_workspace_size
+ *                  gives; always needed (the prefix's partial has a slot)
+ * The prefix part rounds the softmax weights to float16 for its product
+ * with V, as the chunked prefill does (relative error of a weight at most
+ * 2^-12); a bfloat16 V is widened to float16 (|v| <= 65504). */
+int32_t pkv_paged_attention_decode_shared_prefix_workspace_size(
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t max_context_len,
+    int32_t prefix_len, int32_t partition_size, size_t* bytes);
+int32_t pkv_paged_attention_decode_shared_prefix(
+    const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, const int32_t* context_lens,
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+    int32_t num_blocks, int32_t max_context_len, int32_t prefix_len,
+    float scale, int32_t partition_size, float* out, void* workspace,
+    size_t workspace_bytes, int32_t dtype, void* stream);
+
 /* Causal chunked prefill against the same paged cache (article §4.1/§4.2:
  * long prompts in chunks; §2.1: the same block-table gather and softmax).
  * The chunk's K/V must already be appended.

@@ -141,6 +141,12 @@ _SIGNATURES = {
                                                        _I32, _I32, _I32, _I32, ctypes.c_float,
                                                        ctypes.c_float, ctypes.c_float, _I32, _P,
                                                        _P, ctypes.c_size_t, _I32, _P]),
+    "pkv_paged_attention_decode_shared_prefix_workspace_size": (
+        _I32, [_I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, ctypes.POINTER(ctypes.c_size_t)]),
+    "pkv_paged_attention_decode_shared_prefix": (_I32, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32,
+                                                        _I32, _I32, _I32, _I32, _I32,
+                                                        ctypes.c_float, _I32, _P, _P,
+                                                        ctypes.c_size_t, _I32, _P]),
     "pkv_scheduler_create": (_I32, [_I32, _I32, _P, _I32, _I32, _I32, _I32, _I32,
                                     ctypes.POINTER(_P)]),
     "pkv_scheduler_last_swaps": (_I32, [_P, _P, _P, _I32, _P, _P, _P, _I32, _P]),
@@ -1026,6 +1032,53 @@ def paged_attention_decode_fp8_partials(query, key_cache, value_cache, block_tab
     return _decode_fp8(_lib.pkv_paged_attention_decode_fp8_partials, query, key_cache,
                        value_cache, block_tables, context_lens, scale, k_scale, v_scale,
                        max_context_len, partition_size, out, workspace)
+
+
+def paged_attention_decode_shared_prefix_workspace_size(num_seqs, num_heads, num_kv_heads,
+                                                        head_dim, block_size, max_context_len,
+                                                        prefix_len, partition_size=0):
+    """Workspace bytes of paged_attention_decode_shared_prefix
+    (pkv_paged_attention_decode_shared_prefix_workspace_size)."""
+    out = ctypes.c_size_t()
+    _check(_lib.pkv_paged_attention_decode_shared_prefix_workspace_size(
+        int(num_seqs), int(num_heads), int(num_kv_heads), int(head_dim), int(block_size),
+        int(max_context_len), int(prefix_len), int(partition_size), ctypes.byref(out)))
+    return out.value
+
+
+def paged_attention_decode_shared_prefix(query, key_cache, value_cache, block_tables,
+                                         context_lens, prefix_len, scale, max_context_len,
+                                         partition_size=0, out=None, workspace=None,
+                                         shared_blocks=False):
+    """Decode for a batch whose sequences share their first ``prefix_len``
+    tokens (pkv_paged_attention_decode_shared_prefix): the prefix part as
+    one matrix-core contraction per head, the private suffixes by the split-K
+    decode kernel, then the merge.  Same arguments and result as
+    paged_attention_decode, plus ``prefix_len`` (a multiple of the block
+    size; the prefix is read through row 0 of ``block_tables``).
+    ``shared_blocks`` applies the load hint to the suffix reads."""
+    nb, hkv, bs, d = _cache_dims(key_cache, value_cache)
+    _dev(query, "query", dtype=key_cache.dtype, ndim=3)
+    _dev(block_tables, "block_tables", dtype=torch.int32, ndim=2)
+    _dev(context_lens, "context_lens", dtype=torch.int32, ndim=1)
+    b, hq, _ = query.shape
+    if query.shape[2] != d or block_tables.shape[0] != b or context_lens.shape[0] != b:
+        raise InvalidArgument("query [B, Hq, D], block_tables [B, max_blocks], context_lens [B]")
+    if out is None:
+        out = torch.empty((b, hq, d), dtype=torch.float32, device=query.device)
+    _dev(out, "out", dtype=torch.float32, ndim=3)
+    need = paged_attention_decode_shared_prefix_workspace_size(
+        b, hq, hkv, d, bs, int(max_context_len), int(prefix_len), partition_size)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=query.device)
+    _dev(workspace, "workspace")
+    _check(_lib.pkv_paged_attention_decode_shared_prefix(
+        query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(), block_tables.data_ptr(),
+        context_lens.data_ptr(), b, hq, hkv, d, bs, block_tables.shape[1], nb,
+        int(max_context_len), int(prefix_len), float(scale), int(partition_size),
+        out.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        _decode_code(key_cache, shared_blocks), _stream(query)))
+    return out
 
 
 def paged_attention_decode_merge(context_lens, num_kv_heads, block_size, max_blocks_per_seq,

@@ -32,4 +32,14 @@ inline bool aligned16(const void* p) {
   return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
 }
 
+// prefill.hip: the shared-prefix partials of
+// pkv_paged_attention_decode_shared_prefix (arguments checked by the
+// caller; returns the launch's hipError_t).
+int launch_prefix_partials(int32_t dtype, const void* query, const void* key_cache,
+                           const void* value_cache, const int32_t* block_tables, int32_t rows,
+                           int32_t num_heads, int32_t num_kv_heads, int32_t block_size,
+                           int32_t max_blocks_per_seq, int32_t num_blocks, int32_t prefix_len,
+                           float scale, float* ws_acc, float* ws_ml, int32_t slots,
+                           void* stream);
+
 }  // namespace pkv

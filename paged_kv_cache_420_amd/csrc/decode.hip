@@ -428,6 +428,10 @@ struct DecodeParams {
   float scale_log2;            // scale * log2(e), times the K scale of an 8-bit cache
   float v_scale;               // V scale of an 8-bit cache (unused otherwise)
   int32_t shared_blocks;       // nonzero: launch the cached-load kernel (shared blocks)
+  // Suffix mode (shared-prefix decode): the launch covers tokens [start,
+  // len) of every sequence and writes its partitions as partials from slot
+  // slot_base on (slot 0 holds the prefix's partial).  0, 0 otherwise.
+  int32_t start, slot_base;
 };
 
 // Where a launch gets each sequence's length and which table entries it
@@ -522,9 +526,11 @@ __global__ __launch_bounds__(kThreads, (decode_min_blocks<DT, G>())) void decode
   const int num_heads = num_kv_heads * G;
 
   const int n = meta.len(prm, b);
+  const int start = prm.start, slot_base = prm.slot_base;
   const bool bad_len =
-      n < 0 || n > prm.max_ctx || int64_t(n) > int64_t(max_blocks) * bs;
-  const int nparts = bad_len ? 1 : max(1, cdiv(n, part));
+      n < start || n > prm.max_ctx || int64_t(n) > int64_t(max_blocks) * bs;
+  // in suffix mode a sequence with no token past the prefix has no partition
+  const int nparts = bad_len ? 1 : slot_base > 0 ? cdiv(n - start, part) : max(1, cdiv(n, part));
   if (p_idx >= nparts) return;
 
   float* out_row = prm.out + (int64_t(b) * num_heads + int64_t(kvh) * G) * D;
@@ -539,7 +545,7 @@ __global__ __launch_bounds__(kThreads, (decode_min_blocks<DT, G>())) void decode
   int* s_blk = reinterpret_cast<int*>(smem + score_floats);
   float* s_red = reinterpret_cast<float*>(s_blk + (part >> 3));  // [2][kWaves][G]
 
-  const int p0 = p_idx * part;
+  const int p0 = start + p_idx * part;
   const int ntok = min(part, n - p0);
   const int nblk = (ntok + bs - 1) >> log2_bs;
   const int32_t* table = prm.block_tables + int64_t(b) * max_blocks + (p0 >> log2_bs);
@@ -780,10 +786,11 @@ __global__ __launch_bounds__(kThreads, (decode_min_blocks<DT, G>())) void decode
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) m = fmaxf(m, s_red[w * G + g]);
     if constexpr (E::kQuantised) a *= prm.v_scale;
-    if (nparts == 1) {
+    if (nparts == 1 && slot_base == 0) {
       out_row[i] = bad_blk ? nan : a / l;
     } else {
-      const int64_t row = (int64_t(b) * num_heads + int64_t(kvh) * G + g) * max_parts + p_idx;
+      const int64_t row =
+          (int64_t(b) * num_heads + int64_t(kvh) * G + g) * max_parts + slot_base + p_idx;
       prm.ws_acc[row * D + (i - g * D)] = bad_blk ? nan : a;
       if (i - g * D == 0) {
         prm.ws_ml[row * 2] = bad_blk ? nan : m;
@@ -807,11 +814,12 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(
   const int h = blockIdx.x;
   const int b = meta.merge_seq(blockIdx.y);
   const int n = meta.len(prm, b);
-  const bool bad_len = n < 0 || n > max_ctx ||
+  const bool bad_len = n < prm.start || n > max_ctx ||
                        int64_t(n) > (int64_t(max_blocks) << log2_bs);
   if (bad_len) return;
-  const int nparts = cdiv(n, part);
-  if (nparts <= 1) return;
+  // suffix mode: slot 0 is the shared prefix's partial, then the suffix's
+  const int nparts = prm.slot_base + cdiv(n - prm.start, part);
+  if (nparts <= 1 && prm.slot_base == 0) return;
   const int64_t row0 = (int64_t(b) * num_heads + h) * max_parts;
   float big = -INFINITY;
   bool any_nan = false;
@@ -1390,4 +1398,131 @@ extern "C" int32_t pkv_paged_attention_decode_fp8_partials(
                   num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                   num_blocks, max_context_len, scale, k_scale, v_scale, partition_size, out,
                   workspace, workspace_bytes_given, query_dtype, stream, false);
+}
+
+// ---- decode with a prefix shared by every sequence of the batch ----------
+
+namespace {
+int32_t shared_prefix_geometry(int32_t num_seqs, int32_t num_kv_heads, int32_t block_size,
+                               int32_t max_context_len, int32_t prefix_len,
+                               int32_t partition_size, int32_t* part, int32_t* slots) {
+  if (!is_pow2(block_size) || block_size < 16 || block_size > 256)
+    return fail(PKV_ERR_UNSUPPORTED, "block_size must be a power of two in [16, 256]");
+  if (prefix_len <= 0 || prefix_len % block_size != 0)
+    return fail(PKV_ERR_INVALID, "prefix_len %d must be a positive multiple of block_size %d",
+                prefix_len, block_size);
+  if (prefix_len > max_context_len)
+    return fail(PKV_ERR_INVALID, "prefix_len %d exceeds max_context_len %d", prefix_len,
+                max_context_len);
+  const int32_t suffix = max_context_len - prefix_len;
+  int32_t st = resolve_partition(partition_size, block_size, num_seqs, num_kv_heads,
+                                 std::max(1, suffix), part);
+  if (st != PKV_OK) return st;
+  *slots = 1 + (suffix + *part - 1) / *part;
+  if (*slots > 65535) return fail(PKV_ERR_UNSUPPORTED, "context too long");
+  return PKV_OK;
+}
+}  // namespace
+
+extern "C" int32_t pkv_paged_attention_decode_shared_prefix_workspace_size(
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int32_t max_context_len, int32_t prefix_len, int32_t partition_size,
+    size_t* bytes) {
+  if (!bytes) return fail(PKV_ERR_INVALID, "NULL pointer argument");
+  if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0)
+    return fail(PKV_ERR_INVALID, "invalid sizes");
+  int32_t part = 0, slots = 0;
+  int32_t st = shared_prefix_geometry(num_seqs, num_kv_heads, block_size, max_context_len,
+                                      prefix_len, partition_size, &part, &slots);
+  if (st != PKV_OK) return st;
+  *bytes = size_t(num_seqs) * num_heads * slots * (size_t(head_dim) + 2) * sizeof(float);
+  return ok();
+}
+
+extern "C" int32_t pkv_paged_attention_decode_shared_prefix(
+    const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t max_blocks_per_seq, int32_t num_blocks, int32_t max_context_len,
+    int32_t prefix_len, float scale, int32_t partition_size, float* out, void* workspace,
+    size_t workspace_bytes_given, int32_t dtype, void* stream) {
+  const bool shared_blocks = (dtype & PKV_DECODE_SHARED_BLOCKS) != 0;
+  dtype &= ~int32_t(PKV_DECODE_SHARED_BLOCKS);
+  if (dtype != PKV_BF16 && dtype != PKV_F16) {
+    if (dtype_bytes(dtype) == 0) return fail(PKV_ERR_INVALID, "unknown dtype %d", dtype);
+    return fail(PKV_ERR_UNSUPPORTED, "shared-prefix decode needs a float16 or bfloat16 cache");
+  }
+  if (num_seqs < 0) return fail(PKV_ERR_INVALID, "negative num_seqs");
+  if (num_seqs > 65535) return fail(PKV_ERR_UNSUPPORTED, "at most 65535 sequences per call");
+  if (num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID, "num_heads %d must be a positive multiple of num_kv_heads %d",
+                num_heads, num_kv_heads);
+  const int32_t G = num_heads / num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(PKV_ERR_UNSUPPORTED, "heads per kv head must be 1, 2, 4 or 8 (got %d)", G);
+  if (head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "shared-prefix decode supports head_dim 128 (got %d)",
+                head_dim);
+  if (max_blocks_per_seq <= 0 || num_blocks <= 0 || max_context_len < 0)
+    return fail(PKV_ERR_INVALID, "invalid table/pool sizes");
+  if (int64_t(num_blocks) * block_size >= (int64_t(1) << 31))
+    return fail(PKV_ERR_INVALID, "num_blocks * block_size must be below 2^31");
+  if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID, "scale must be finite");
+  int32_t part = 0, slots = 0;
+  int32_t st = shared_prefix_geometry(num_seqs, num_kv_heads, block_size, max_context_len,
+                                      prefix_len, partition_size, &part, &slots);
+  if (st != PKV_OK) return st;
+  if (int64_t(prefix_len) > int64_t(max_blocks_per_seq) * block_size)
+    return fail(PKV_ERR_INVALID, "prefix_len %d exceeds the block table's capacity", prefix_len);
+  if (num_seqs == 0) return ok();
+  if (!query || !key_cache || !value_cache || !block_tables || !context_lens || !out)
+    return fail(PKV_ERR_INVALID, "NULL pointer argument");
+  if (!aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache) || !aligned16(out))
+    return fail(PKV_ERR_INVALID, "query, caches and out must be 16-byte aligned");
+  const size_t need = size_t(num_seqs) * num_heads * slots * (size_t(head_dim) + 2) * sizeof(float);
+  if (!workspace || workspace_bytes_given < need)
+    return fail(PKV_ERR_BUFFER_TOO_SMALL, "workspace needs %zu bytes, got %zu", need,
+                workspace ? workspace_bytes_given : size_t(0));
+  if (!aligned16(workspace)) return fail(PKV_ERR_INVALID, "workspace must be 16-byte aligned");
+  float* ws_acc = static_cast<float*>(workspace);
+  float* ws_ml = ws_acc + size_t(num_seqs) * num_heads * slots * head_dim;
+
+  // 1. every query against the shared prefix, on the matrix cores
+  hipError_t e = static_cast<hipError_t>(launch_prefix_partials(
+      dtype, query, key_cache, value_cache, block_tables, num_seqs, num_heads, num_kv_heads,
+      block_size, max_blocks_per_seq, num_blocks, prefix_len, scale, ws_acc, ws_ml, slots,
+      stream));
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "prefix launch: %s", hipGetErrorString(e));
+
+  // 2. each sequence's private suffix, split-K, partials from slot 1 on
+  DecodeParams prm{};
+  prm.query = static_cast<const uint8_t*>(query);
+  prm.key_cache = static_cast<const uint8_t*>(key_cache);
+  prm.value_cache = static_cast<const uint8_t*>(value_cache);
+  prm.block_tables = block_tables;
+  prm.block_tables_rw = const_cast<int32_t*>(block_tables);
+  prm.context_lens = context_lens;
+  prm.out = out;
+  prm.ws_acc = ws_acc;
+  prm.ws_ml = ws_ml;
+  prm.num_kv_heads = num_kv_heads;
+  while ((1 << prm.log2_bs) < block_size) ++prm.log2_bs;
+  prm.max_blocks = max_blocks_per_seq;
+  prm.num_blocks = num_blocks;
+  prm.max_ctx = max_context_len;
+  prm.part = part;
+  prm.max_parts = slots;
+  prm.scale_log2 = scale * kLog2e;
+  prm.v_scale = 1.0f;
+  prm.shared_blocks = shared_blocks ? 1 : 0;
+  prm.start = prefix_len;
+  prm.slot_base = 1;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  e = dispatch_decode(dtype, head_dim, G, prm, DeviceMeta{}, num_seqs, s);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+
+  // 3. log-sum-exp merge of the prefix and suffix partials
+  e = launch_merge(prm, DeviceMeta{}, num_seqs, num_heads, head_dim, s);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "decode merge launch: %s", hipGetErrorString(e));
+  return ok();
 }

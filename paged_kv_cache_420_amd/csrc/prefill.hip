@@ -139,14 +139,29 @@ constexpr float kRescaleSlack = 8.0f;
 // contiguous row; a wave's four rows lie in one 16-key group.  The PV product's V^T operand comes out of the row-major
 // V tile through the LDS transpose read, so V needs no transposition in
 // registers.
-template <int DT>
+// Shared-prefix mode (kPrefix): the rows are the decode queries of a batch
+// whose sequences all begin with the same prefix_len tokens (reached
+// through row 0 of the block table).  Every row attends to the whole
+// prefix -- no causal limit -- and the result is left unnormalised, as a
+// split-K partial in slot 0 of the decode workspace ([rows][heads][slots]
+// of head_dim floats, and [rows][heads][slots][2] of (max, sum) in log2
+// units), for the decode merge to combine with the private suffixes.
+struct PrefixArgs {
+  float* ws_acc;
+  float* ws_ml;
+  int32_t rows;        // decode queries (one per sequence)
+  int32_t prefix_len;  // tokens, a multiple of the block size
+  int32_t slots;       // partials per (row, head) in the workspace
+};
+
+template <int DT, bool kPrefix>
 __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
     const uint16_t* __restrict__ query, const uint16_t* __restrict__ key_cache,
     const uint16_t* __restrict__ value_cache, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ context_lens, const int32_t* __restrict__ cu_query_lens,
     int32_t num_heads, int32_t group, int32_t log2_bs, int32_t max_blocks,
     int32_t num_blocks, int32_t total_q, int32_t max_q, float scale_log2,
-    float* __restrict__ out) {
+    float* __restrict__ out, const PrefixArgs pfx) {
   using H = Half<DT>;
   __shared__ __attribute__((aligned(16))) uint8_t s_k[2][kLdsK];
   __shared__ __attribute__((aligned(16))) uint8_t s_v[2][kLdsV];
@@ -164,15 +179,29 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
   const int num_kv_heads = num_heads / group;
   const int bs = 1 << log2_bs;
 
-  const int q0 = cu_query_lens[b], q1 = cu_query_lens[b + 1];
+  const int q0 = kPrefix ? 0 : cu_query_lens[b];
+  const int q1 = kPrefix ? pfx.rows : cu_query_lens[b + 1];
   if (q0 < 0 || q1 < q0 || q1 > total_q) return;  // rows unknown: nothing written
   const int c = q1 - q0;
   const int r0 = qt * kQTile;
   if (r0 >= c) return;
-  const int n = context_lens[b];
+  const int n = kPrefix ? pfx.prefix_len : context_lens[b];
   const int rows_here = min(kQTile, c - r0);
 
-  const bool bad_len = c > n || c > max_q || int64_t(n) > (int64_t(max_blocks) << log2_bs);
+  const bool bad_len = kPrefix ? int64_t(n) > (int64_t(max_blocks) << log2_bs)
+                               : c > n || c > max_q ||
+                                     int64_t(n) > (int64_t(max_blocks) << log2_bs);
+  if constexpr (kPrefix) {
+    if (bad_len) {  // rows NaN through their prefix partials
+      const float nan = __builtin_nanf("");
+      for (int i = tid; i < rows_here * kD; i += kThreads) {
+        const int64_t row = (int64_t(r0 + i / kD) * num_heads + h) * pfx.slots;
+        pfx.ws_acc[row * kD + (i % kD)] = nan;
+        if (i % kD == 0) pfx.ws_ml[row * 2] = pfx.ws_ml[row * 2 + 1] = nan;
+      }
+      return;
+    }
+  }
   if (bad_len) {
     const float nan = __builtin_nanf("");
     for (int i = tid; i < rows_here * kD; i += kThreads)
@@ -181,13 +210,15 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
   }
 
   const int pos_base = n - c;                    // position of chunk row 0
-  const int kv_end = pos_base + r0 + rows_here;  // keys [0, kv_end) are needed
+  // keys [0, kv_end) are needed (the whole prefix in shared-prefix mode)
+  const int kv_end = kPrefix ? n : pos_base + r0 + rows_here;
   const int ntiles = cdiv(kv_end, kKTile);
 
   // ---- this wavefront's rows ------------------------------------------------
   const int wrows = max(0, min(32, rows_here - 32 * wave));
   const int pos_first = pos_base + r0 + 32 * wave;  // position of its row 0
-  const int pos_last = pos_first + wrows - 1;
+  // last key any of its rows sees
+  const int pos_last = kPrefix ? n - 1 : pos_first + wrows - 1;
   const int col = lane & 15;  // query row within a 16-row group / key within 16
   const int grp = lane >> 4;  // lane group: 8-element k slice, 4-row output slice
 
@@ -308,11 +339,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
 
     // causal limit: only tiles reaching past this wave's first row mask.
     // Key 16 kt + 4 grp + r of the tile is visible to row 16 qg + col iff
-    // 16 kt + r <= lim[qg].
-    const bool diag = key0 + kKTile - 1 > pos_first;
+    // 16 kt + r <= lim[qg].  Shared-prefix mode: every row sees keys up to
+    // n - 1, so only the tile holding the prefix's end masks.
+    const bool diag = kPrefix ? key0 + kKTile > n : key0 + kKTile - 1 > pos_first;
     int lim[2];
 #pragma unroll
-    for (int qg = 0; qg < 2; ++qg) lim[qg] = pos_first + 16 * qg + col - key0 - 4 * grp;
+    for (int qg = 0; qg < 2; ++qg)
+      lim[qg] = kPrefix ? n - 1 - key0 - 4 * grp : pos_first + 16 * qg + col - key0 - 4 * grp;
     if (diag) {
 #pragma unroll
       for (int qg = 0; qg < 2; ++qg)
@@ -429,6 +462,22 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
     const float l = __shfl(l_acc[qg][0], col);  // row sum from lane col
     const int i = r0 + 32 * wave + 16 * qg + col;
     if (i >= c) continue;
+    if constexpr (kPrefix) {
+      // unnormalised partial in slot 0, with the row's running max (log2
+      // units, the scale applied) and its sum
+      const float nan = __builtin_nanf("");
+      const int64_t prow = (int64_t(i) * num_heads + h) * pfx.slots;
+      float* acc = pfx.ws_acc + prow * kD;
+#pragma unroll
+      for (int dt = 0; dt < kD / 16; ++dt)
+        *reinterpret_cast<f32x4*>(acc + 16 * dt + 4 * grp) =
+            bad_blk ? f32x4{nan, nan, nan, nan} : o[qg][dt];
+      if (grp == 0) {
+        pfx.ws_ml[prow * 2] = bad_blk ? nan : m_run[qg];
+        pfx.ws_ml[prow * 2 + 1] = bad_blk ? nan : l;
+      }
+      continue;
+    }
     const float inv = bad_blk ? __builtin_nanf("") : 1.0f / l;
     float* row = out + (int64_t(q0 + i) * num_heads + h) * kD;
 #pragma unroll
@@ -483,19 +532,51 @@ extern "C" int32_t pkv_paged_attention_prefill(
   const dim3 grid(num_heads, unsigned(tiles), num_seqs);
   const int group = num_heads / num_kv_heads;
   if (dtype == PKV_BF16) {
-    hipLaunchKernelGGL(prefill_kernel<PKV_BF16>, grid, dim3(kThreads), 0, s,
+    hipLaunchKernelGGL((prefill_kernel<PKV_BF16, false>), grid, dim3(kThreads), 0, s,
                        static_cast<const uint16_t*>(query), static_cast<const uint16_t*>(key_cache),
                        static_cast<const uint16_t*>(value_cache), block_tables, context_lens,
                        cu_query_lens, num_heads, group, log2_bs, max_blocks_per_seq, num_blocks,
-                       total_query_rows, max_query_len, sl2, out);
+                       total_query_rows, max_query_len, sl2, out, PrefixArgs{});
   } else {
-    hipLaunchKernelGGL(prefill_kernel<PKV_F16>, grid, dim3(kThreads), 0, s,
+    hipLaunchKernelGGL((prefill_kernel<PKV_F16, false>), grid, dim3(kThreads), 0, s,
                        static_cast<const uint16_t*>(query), static_cast<const uint16_t*>(key_cache),
                        static_cast<const uint16_t*>(value_cache), block_tables, context_lens,
                        cu_query_lens, num_heads, group, log2_bs, max_blocks_per_seq, num_blocks,
-                       total_query_rows, max_query_len, sl2, out);
+                       total_query_rows, max_query_len, sl2, out, PrefixArgs{});
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+// The shared-prefix part of pkv_paged_attention_decode_shared_prefix: the
+// prefill kernel in shared-prefix mode over `rows` decode queries
+// ([rows][num_heads][128]), the prefix reached through row 0 of
+// block_tables, partials into slot 0 of the decode workspace.  Arguments
+// are checked by the caller.
+int pkv::launch_prefix_partials(int32_t dtype, const void* query, const void* key_cache,
+                                const void* value_cache, const int32_t* block_tables,
+                                int32_t rows, int32_t num_heads, int32_t num_kv_heads,
+                                int32_t block_size, int32_t max_blocks_per_seq,
+                                int32_t num_blocks, int32_t prefix_len, float scale,
+                                float* ws_acc, float* ws_ml, int32_t slots, void* stream) {
+  int log2_bs = 0;
+  while ((1 << log2_bs) < block_size) ++log2_bs;
+  const PrefixArgs pfx{ws_acc, ws_ml, rows, prefix_len, slots};
+  const dim3 grid(num_heads, unsigned((rows + kQTile - 1) / kQTile), 1);
+  const int group = num_heads / num_kv_heads;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const auto* q = static_cast<const uint16_t*>(query);
+  const auto* kc = static_cast<const uint16_t*>(key_cache);
+  const auto* vc = static_cast<const uint16_t*>(value_cache);
+  const float sl2 = scale * kLog2e;
+  if (dtype == PKV_BF16)
+    hipLaunchKernelGGL((prefill_kernel<PKV_BF16, true>), grid, dim3(kThreads), 0, s, q, kc, vc,
+                       block_tables, nullptr, nullptr, num_heads, group, log2_bs,
+                       max_blocks_per_seq, num_blocks, rows, rows, sl2, nullptr, pfx);
+  else
+    hipLaunchKernelGGL((prefill_kernel<PKV_F16, true>), grid, dim3(kThreads), 0, s, q, kc, vc,
+                       block_tables, nullptr, nullptr, num_heads, group, log2_bs,
+                       max_blocks_per_seq, num_blocks, rows, rows, sl2, nullptr, pfx);
+  return static_cast<int>(hipGetLastError());
 }

@@ -676,3 +676,101 @@ def test_step_every_instantiation_is_full_upload_decode(dt, d, grp):
                                               shared_blocks=bool(i % 2))
         torch.cuda.synchronize()
         assert torch.equal(got, want), f"step {i}"
+
+
+# ---------------------------------------------------------------------------
+# decode with a prefix shared by every sequence (matrix-core prefix part,
+# split-K suffixes, merge)
+# ---------------------------------------------------------------------------
+
+SHARED = {
+    "bf16_mha_bs16": workloads.scaled(workloads.get("shared_prefix_bf16"), num_seqs=6,
+                                      num_heads=4, num_kv_heads=4, prefix=64,
+                                      lens="uniform:0,300", chunk=0),
+    "f16_gqa8_bs32": workloads.scaled(workloads.get("shared_prefix_bf16"), num_seqs=5,
+                                      num_heads=16, num_kv_heads=2, block_size=32, prefix=96,
+                                      dtype=torch.float16, lens="uniform:1,500", chunk=0),
+    "bf16_gqa2_long_prefix": workloads.scaled(workloads.get("shared_prefix_bf16"), num_seqs=4,
+                                              num_heads=4, num_kv_heads=2, prefix=400 - 400 % 16,
+                                              lens="uniform:0,200", chunk=0),
+}
+
+
+@pytest.mark.parametrize("name", list(SHARED))
+@pytest.mark.parametrize("part", [64, 0])
+def test_shared_prefix_decode_matches_oracle(name, part):
+    """pkv_paged_attention_decode_shared_prefix against the oracle's paged
+    decode over the same NaN-poisoned pool: the prefix part (float16 weights
+    on the matrix cores) and the suffix partials merged; sequences with no
+    suffix token included."""
+    w = SHARED[name]
+    log("case", name, part)
+    p = workloads.plan(w)
+    g = GpuState(w, p)
+    o = OracleState(w, p)
+    tables, lens, _, lh = g.tables()
+    q, q64 = decode_queries(w, p.seqs)
+    mc = int(lh.max())
+    need = pkv.paged_attention_decode_shared_prefix_workspace_size(
+        len(p.seqs), w.num_heads, w.num_kv_heads, w.head_dim, w.block_size, mc, w.prefix, part)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=DEV)   # NaN garbage
+    got = pkv.paged_attention_decode_shared_prefix(q.to(DEV), g.kc, g.vc, tables, lens, w.prefix,
+                                                   w.scale, mc, partition_size=part,
+                                                   workspace=ws)
+    torch.cuda.synchronize()
+    ot, ol = o.tables()
+    want = paged_decode(q64, o.kc, o.vc, ot, ol, w.scale, w.block_size)
+    err = max_abs_err(got.cpu().numpy(), want)
+    log(name, "max abs err", err)
+    assert err <= TOL[w.dtype]
+    # the suffix load hint changes no bit
+    hinted = pkv.paged_attention_decode_shared_prefix(q.to(DEV), g.kc, g.vc, tables, lens,
+                                                      w.prefix, w.scale, mc, partition_size=part,
+                                                      shared_blocks=True)
+    torch.cuda.synchronize()
+    assert torch.equal(hinted, got)
+
+
+def test_shared_prefix_decode_rows_below_the_prefix_are_nan():
+    w = SHARED["bf16_mha_bs16"]
+    p = workloads.plan(w)
+    g = GpuState(w, p)
+    tables, lens, _, lh = g.tables()
+    q, q64 = decode_queries(w, p.seqs)
+    bad = lens.clone()
+    bad[1] = w.prefix - 1                      # shorter than the shared prefix
+    mc = int(lh.max())
+    got = pkv.paged_attention_decode_shared_prefix(q.to(DEV), g.kc, g.vc, tables, bad, w.prefix,
+                                                   w.scale, mc).cpu().numpy()
+    assert np.isnan(got[1]).all()
+    ok_rows = [i for i in range(len(p.seqs)) if i != 1]
+    assert np.isfinite(got[ok_rows]).all()
+    with pytest.raises(pkv.InvalidArgument):   # not a multiple of the block size
+        pkv.paged_attention_decode_shared_prefix(q.to(DEV), g.kc, g.vc, tables, lens,
+                                                 w.prefix - 8, w.scale, mc)
+
+
+def test_shared_prefix_decode_full_size_sampled():
+    """The shared-prefix batch at full size (256 sequences, 1024-token
+    prefix): sampled sequences against oracle attention over the logical
+    K/V drawn again from the generator."""
+    w = workloads.scaled(workloads.get("shared_prefix_bf16"), chunk=0)
+    p = workloads.plan(w)
+    g = GpuState(w, p)
+    tables, lens, _, lh = g.tables()
+    q, q64 = decode_queries(w, p.seqs)
+    mc = int(lh.max())
+    got = pkv.paged_attention_decode_shared_prefix(q.to(DEV), g.kc, g.vc, tables, lens, w.prefix,
+                                                   w.scale, mc).cpu().numpy()
+    segs = logical_segments(p.ops)
+    rng = np.random.default_rng(11)
+    pick = sorted(set(rng.choice(len(p.seqs), size=8, replace=False).tolist())
+                  | {int(np.argmax(lh)), int(np.argmin(lh))})
+    worst = 0.0
+    for b in pick:
+        k, v = logical_kv(w, segs[p.seqs[b]])
+        want = dense_attention(q64[b][None], k, v, w.scale)[0]
+        worst = max(worst, max_abs_err(got[b], want))
+    log("shared-prefix decode, full size: sampled max abs err", worst)
+    assert worst <= TOL[w.dtype]
+    assert np.isfinite(got).all()
