@@ -211,9 +211,70 @@ def gpu_run(args, w, torch, pkv, workloads):
     res = dict(wall=wall, kernel_ms=kernel_ms, merge_ms=merge_ms, bytes=step_bytes[args.warmup:],
                unique_bytes=step_unique[args.warmup:],
                batch=b, part=part, shared=shared)
+    if w.prefix:
+        res["decode_shared_prefix"] = shared_prefix_decode_run(w, p, alloc, kc, vc, torch, pkv,
+                                                               dev)
     if w.chunk and not args.no_prefill:
         res["prefill"] = prefill_run(w, p, alloc, kc, vc, torch, pkv, dev)
     return res
+
+
+def shared_prefix_decode_run(w, p, alloc, kc, vc, torch, pkv, dev):
+    """On the cache state after the decode steps: the plain split-K decode
+    (partials + merge, shared-blocks hint) against the shared-prefix decode
+    (prefix on the matrix cores, suffixes split-K, merge), HIP events on
+    their stream, mean of 10 launches after 2 untimed."""
+    seqs = np.asarray(p.seqs, dtype=np.int64)
+    b = len(seqs)
+    mb = max(len(alloc.block_table(int(s))) for s in seqs)
+    th, lh = alloc.build_block_tables(seqs, mb)
+    tables = torch.from_numpy(th.copy()).to(dev)
+    lens = torch.from_numpy(lh.copy()).to(dev)
+    mc = int(lh.max())
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed + 5)
+    q = (torch.randn((b, w.num_heads, w.head_dim), generator=gen, device=dev) * w.std).to(w.dtype)
+    out_a = torch.empty((b, w.num_heads, w.head_dim), dtype=torch.float32, device=dev)
+    out_b = torch.empty_like(out_a)
+    ws_a = torch.empty(max(pkv.paged_attention_decode_workspace_size(
+        b, w.num_heads, w.num_kv_heads, w.head_dim, mc, 0), 16), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(max(pkv.paged_attention_decode_shared_prefix_workspace_size(
+        b, w.num_heads, w.num_kv_heads, w.head_dim, w.block_size, mc, w.prefix), 16),
+        dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def plain():
+        pkv.paged_attention_decode(q, kc, vc, tables, lens, w.scale, mc, out=out_a,
+                                   workspace=ws_a, shared_blocks=True)
+
+    def cascade():
+        pkv.paged_attention_decode_shared_prefix(q, kc, vc, tables, lens, w.prefix, w.scale, mc,
+                                                 out=out_b, workspace=ws_b)
+
+    times = {}
+    for name, fn in (("split_k", plain), ("shared_prefix", cascade)):
+        for _ in range(2):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(10):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times[name] = e0.elapsed_time(e1) / 10
+    diff = float((out_a - out_b).abs().max())
+    if not (diff <= 2e-3):
+        raise RuntimeError(f"shared-prefix decode differs from split-K decode by {diff}")
+    unique = kv_bytes_unique(w, lh)
+    us = times["shared_prefix"] * 1e3
+    return {"call": "pkv_paged_attention_decode_shared_prefix", "prefix_len": w.prefix,
+            "us": round(us, 2), "split_k_us": round(times["split_k"] * 1e3, 2),
+            "speedup": round(times["split_k"] / times["shared_prefix"], 3),
+            "unique_kv_bytes": int(unique),
+            "unique_gbps": round(unique / (us * 1e-6) / 1e9, 1),
+            "unique_hbm_peak_frac": round(unique / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            "tokens_per_s": round(b / (us * 1e-6), 1),
+            "max_abs_diff_vs_split_k": diff}
 
 
 def prefill_run(w, p, alloc, kc, vc, torch, pkv, dev):
@@ -713,6 +774,8 @@ def main():
                      "traffic": traffic_from_profiles(w, src),
                      "launches_timed": int(len(r["kernel_ms"]))},
     }
+    if "decode_shared_prefix" in r:
+        line["decode_shared_prefix"] = r["decode_shared_prefix"]
     if "prefill" in r:
         line["prefill"] = r["prefill"]
     line["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(w, workloads)
