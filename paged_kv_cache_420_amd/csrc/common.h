@@ -39,7 +39,11 @@ int launch_prefix_partials(int32_t dtype, const void* query, const void* key_cac
                            const void* value_cache, const int32_t* block_tables, int32_t rows,
                            int32_t num_heads, int32_t num_kv_heads, int32_t block_size,
                            int32_t max_blocks_per_seq, int32_t num_blocks, int32_t prefix_len,
-                           float scale, float* ws_acc, float* ws_ml, int32_t slots,
-                           void* stream);
+                           int32_t splits, int32_t split_keys, float scale, float* ws_acc,
+                           float* ws_ml, int32_t slots, void* stream);
+
+// Rows per workgroup of the prefill kernel (the shared-prefix split count
+// is chosen from the grid it gives).
+constexpr int kPrefillRowsPerGroup = 256;
 
 }  // namespace pkv

@@ -1403,9 +1403,13 @@ extern "C" int32_t pkv_paged_attention_decode_fp8_partials(
 // ---- decode with a prefix shared by every sequence of the batch ----------
 
 namespace {
-int32_t shared_prefix_geometry(int32_t num_seqs, int32_t num_kv_heads, int32_t block_size,
-                               int32_t max_context_len, int32_t prefix_len,
-                               int32_t partition_size, int32_t* part, int32_t* slots) {
+// The prefix is split into key ranges of a multiple of 64 keys so that the
+// prefix launch has a workgroup per CU (256) or more; each range is a
+// partial slot (0 .. splits - 1), the suffix partitions follow.
+int32_t shared_prefix_geometry(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                               int32_t block_size, int32_t max_context_len, int32_t prefix_len,
+                               int32_t partition_size, int32_t* part, int32_t* splits,
+                               int32_t* split_keys, int32_t* slots) {
   if (!is_pow2(block_size) || block_size < 16 || block_size > 256)
     return fail(PKV_ERR_UNSUPPORTED, "block_size must be a power of two in [16, 256]");
   if (prefix_len <= 0 || prefix_len % block_size != 0)
@@ -1418,7 +1422,14 @@ int32_t shared_prefix_geometry(int32_t num_seqs, int32_t num_kv_heads, int32_t b
   int32_t st = resolve_partition(partition_size, block_size, num_seqs, num_kv_heads,
                                  std::max(1, suffix), part);
   if (st != PKV_OK) return st;
-  *slots = 1 + (suffix + *part - 1) / *part;
+  const int64_t groups = int64_t(num_heads) *
+                        ((int64_t(num_seqs) + kPrefillRowsPerGroup - 1) / kPrefillRowsPerGroup);
+  const int32_t tiles = (prefix_len + 63) / 64;
+  const int32_t want = int32_t(std::min<int64_t>(tiles, std::max<int64_t>(1, (256 + groups - 1) /
+                                                                                std::max<int64_t>(groups, 1))));
+  *split_keys = ((tiles + want - 1) / want) * 64;
+  *splits = (prefix_len + *split_keys - 1) / *split_keys;
+  *slots = *splits + (suffix + *part - 1) / *part;
   if (*slots > 65535) return fail(PKV_ERR_UNSUPPORTED, "context too long");
   return PKV_OK;
 }
@@ -1431,9 +1442,10 @@ extern "C" int32_t pkv_paged_attention_decode_shared_prefix_workspace_size(
   if (!bytes) return fail(PKV_ERR_INVALID, "NULL pointer argument");
   if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0)
     return fail(PKV_ERR_INVALID, "invalid sizes");
-  int32_t part = 0, slots = 0;
-  int32_t st = shared_prefix_geometry(num_seqs, num_kv_heads, block_size, max_context_len,
-                                      prefix_len, partition_size, &part, &slots);
+  int32_t part = 0, splits = 0, split_keys = 0, slots = 0;
+  int32_t st = shared_prefix_geometry(num_seqs, num_heads, num_kv_heads, block_size,
+                                      max_context_len, prefix_len, partition_size, &part,
+                                      &splits, &split_keys, &slots);
   if (st != PKV_OK) return st;
   *bytes = size_t(num_seqs) * num_heads * slots * (size_t(head_dim) + 2) * sizeof(float);
   return ok();
@@ -1468,9 +1480,10 @@ extern "C" int32_t pkv_paged_attention_decode_shared_prefix(
   if (int64_t(num_blocks) * block_size >= (int64_t(1) << 31))
     return fail(PKV_ERR_INVALID, "num_blocks * block_size must be below 2^31");
   if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID, "scale must be finite");
-  int32_t part = 0, slots = 0;
-  int32_t st = shared_prefix_geometry(num_seqs, num_kv_heads, block_size, max_context_len,
-                                      prefix_len, partition_size, &part, &slots);
+  int32_t part = 0, splits = 0, split_keys = 0, slots = 0;
+  int32_t st = shared_prefix_geometry(num_seqs, num_heads, num_kv_heads, block_size,
+                                      max_context_len, prefix_len, partition_size, &part,
+                                      &splits, &split_keys, &slots);
   if (st != PKV_OK) return st;
   if (int64_t(prefix_len) > int64_t(max_blocks_per_seq) * block_size)
     return fail(PKV_ERR_INVALID, "prefix_len %d exceeds the block table's capacity", prefix_len);
@@ -1490,11 +1503,11 @@ extern "C" int32_t pkv_paged_attention_decode_shared_prefix(
   // 1. every query against the shared prefix, on the matrix cores
   hipError_t e = static_cast<hipError_t>(launch_prefix_partials(
       dtype, query, key_cache, value_cache, block_tables, num_seqs, num_heads, num_kv_heads,
-      block_size, max_blocks_per_seq, num_blocks, prefix_len, scale, ws_acc, ws_ml, slots,
-      stream));
+      block_size, max_blocks_per_seq, num_blocks, prefix_len, splits, split_keys, scale, ws_acc,
+      ws_ml, slots, stream));
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "prefix launch: %s", hipGetErrorString(e));
 
-  // 2. each sequence's private suffix, split-K, partials from slot 1 on
+  // 2. each sequence's private suffix, split-K, partials after the prefix's
   DecodeParams prm{};
   prm.query = static_cast<const uint8_t*>(query);
   prm.key_cache = static_cast<const uint8_t*>(key_cache);
@@ -1516,7 +1529,7 @@ extern "C" int32_t pkv_paged_attention_decode_shared_prefix(
   prm.v_scale = 1.0f;
   prm.shared_blocks = shared_blocks ? 1 : 0;
   prm.start = prefix_len;
-  prm.slot_base = 1;
+  prm.slot_base = splits;
   hipStream_t s = static_cast<hipStream_t>(stream);
   e = dispatch_decode(dtype, head_dim, G, prm, DeviceMeta{}, num_seqs, s);
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "decode launch: %s", hipGetErrorString(e));

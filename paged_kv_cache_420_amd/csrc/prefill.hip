@@ -47,6 +47,7 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kD = 128;               // head dim served by this kernel
 constexpr int kQTile = 32 * kWaves;   // query rows per workgroup
+static_assert(kQTile == kPrefillRowsPerGroup, "rows per workgroup");
 constexpr int kKTile = 64;            // keys per K/V tile
 constexpr int kKRow = kD * 2 + 16;    // LDS bytes per K row (16 B pad)
 constexpr int kVRow = kD * 2 + 32;    // LDS bytes per V row (32 B pad)
@@ -152,6 +153,9 @@ struct PrefixArgs {
   int32_t rows;        // decode queries (one per sequence)
   int32_t prefix_len;  // tokens, a multiple of the block size
   int32_t slots;       // partials per (row, head) in the workspace
+  int32_t split_keys;  // keys per split of the prefix (a multiple of 64):
+                       // split z = blockIdx.z takes keys [z, z + 1) *
+                       // split_keys and writes slot z
 };
 
 template <int DT, bool kPrefix>
@@ -171,7 +175,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
                     ? (blockIdx.x & 7) * xcd_slice + (blockIdx.x >> 3)
                     : blockIdx.x;
   const int qt = blockIdx.y;
-  const int b = blockIdx.z;
+  const int b = kPrefix ? 0 : blockIdx.z;
+  const int split = kPrefix ? blockIdx.z : 0;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -195,7 +200,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
     if (bad_len) {  // rows NaN through their prefix partials
       const float nan = __builtin_nanf("");
       for (int i = tid; i < rows_here * kD; i += kThreads) {
-        const int64_t row = (int64_t(r0 + i / kD) * num_heads + h) * pfx.slots;
+        const int64_t row = (int64_t(r0 + i / kD) * num_heads + h) * pfx.slots + split;
         pfx.ws_acc[row * kD + (i % kD)] = nan;
         if (i % kD == 0) pfx.ws_ml[row * 2] = pfx.ws_ml[row * 2 + 1] = nan;
       }
@@ -211,14 +216,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
 
   const int pos_base = n - c;                    // position of chunk row 0
   // keys [0, kv_end) are needed (the whole prefix in shared-prefix mode)
-  const int kv_end = kPrefix ? n : pos_base + r0 + rows_here;
+  const int kv_begin = kPrefix ? split * pfx.split_keys : 0;
+  const int kv_end = kPrefix ? min(n, kv_begin + pfx.split_keys) : pos_base + r0 + rows_here;
+  const int tile0 = kv_begin / kKTile;  // kv_begin is a multiple of the tile
   const int ntiles = cdiv(kv_end, kKTile);
 
   // ---- this wavefront's rows ------------------------------------------------
   const int wrows = max(0, min(32, rows_here - 32 * wave));
   const int pos_first = pos_base + r0 + 32 * wave;  // position of its row 0
   // last key any of its rows sees
-  const int pos_last = kPrefix ? n - 1 : pos_first + wrows - 1;
+  const int pos_last = kPrefix ? kv_end - 1 : pos_first + wrows - 1;
   const int col = lane & 15;  // query row within a 16-row group / key within 16
   const int grp = lane >> 4;  // lane group: 8-element k slice, 4-row output slice
 
@@ -341,11 +348,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
     // Key 16 kt + 4 grp + r of the tile is visible to row 16 qg + col iff
     // 16 kt + r <= lim[qg].  Shared-prefix mode: every row sees keys up to
     // n - 1, so only the tile holding the prefix's end masks.
-    const bool diag = kPrefix ? key0 + kKTile > n : key0 + kKTile - 1 > pos_first;
+    const bool diag = kPrefix ? key0 + kKTile > kv_end : key0 + kKTile - 1 > pos_first;
     int lim[2];
 #pragma unroll
     for (int qg = 0; qg < 2; ++qg)
-      lim[qg] = kPrefix ? n - 1 - key0 - 4 * grp : pos_first + 16 * qg + col - key0 - 4 * grp;
+      lim[qg] = kPrefix ? kv_end - 1 - key0 - 4 * grp
+                        : pos_first + 16 * qg + col - key0 - 4 * grp;
     if (diag) {
 #pragma unroll
       for (int qg = 0; qg < 2; ++qg)
@@ -441,16 +449,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
     }
   };
 
-  // tile j lives in LDS buffer j % 2; tile j + 1's loads are in flight while
-  // tile j is computed, then stored into the other buffer (last read two
-  // barriers ago)
-  load_tile(0);
-  store_tile(0, 0);
+  // tile j lives in LDS buffer (j - tile0) % 2; tile j + 1's loads are in
+  // flight while tile j is computed, then stored into the other buffer
+  // (last read two barriers ago)
+  load_tile(tile0);
+  store_tile(0, tile0);
   __syncthreads();
-  for (int j = 0; j < ntiles; ++j) {
+  for (int j = tile0; j < ntiles; ++j) {
     if (j + 1 < ntiles) load_tile(j + 1);
-    if (wrows > 0 && j * kKTile <= pos_last) compute_tile(j & 1, j);
-    if (j + 1 < ntiles) store_tile((j + 1) & 1, j + 1);
+    if (wrows > 0 && j * kKTile <= pos_last) compute_tile((j - tile0) & 1, j);
+    if (j + 1 < ntiles) store_tile((j + 1 - tile0) & 1, j + 1);
     __syncthreads();
   }
   bad_blk = __syncthreads_or(bad_blk);
@@ -466,7 +474,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
       // unnormalised partial in slot 0, with the row's running max (log2
       // units, the scale applied) and its sum
       const float nan = __builtin_nanf("");
-      const int64_t prow = (int64_t(i) * num_heads + h) * pfx.slots;
+      const int64_t prow = (int64_t(i) * num_heads + h) * pfx.slots + split;
       float* acc = pfx.ws_acc + prow * kD;
 #pragma unroll
       for (int dt = 0; dt < kD / 16; ++dt)
@@ -552,18 +560,20 @@ extern "C" int32_t pkv_paged_attention_prefill(
 // The shared-prefix part of pkv_paged_attention_decode_shared_prefix: the
 // prefill kernel in shared-prefix mode over `rows` decode queries
 // ([rows][num_heads][128]), the prefix reached through row 0 of
-// block_tables, partials into slot 0 of the decode workspace.  Arguments
+// block_tables and split into `splits` key ranges of `split_keys` keys,
+// partials into slots 0 .. splits - 1 of the decode workspace.  Arguments
 // are checked by the caller.
 int pkv::launch_prefix_partials(int32_t dtype, const void* query, const void* key_cache,
                                 const void* value_cache, const int32_t* block_tables,
                                 int32_t rows, int32_t num_heads, int32_t num_kv_heads,
                                 int32_t block_size, int32_t max_blocks_per_seq,
-                                int32_t num_blocks, int32_t prefix_len, float scale,
-                                float* ws_acc, float* ws_ml, int32_t slots, void* stream) {
+                                int32_t num_blocks, int32_t prefix_len, int32_t splits,
+                                int32_t split_keys, float scale, float* ws_acc, float* ws_ml,
+                                int32_t slots, void* stream) {
   int log2_bs = 0;
   while ((1 << log2_bs) < block_size) ++log2_bs;
-  const PrefixArgs pfx{ws_acc, ws_ml, rows, prefix_len, slots};
-  const dim3 grid(num_heads, unsigned((rows + kQTile - 1) / kQTile), 1);
+  const PrefixArgs pfx{ws_acc, ws_ml, rows, prefix_len, slots, split_keys};
+  const dim3 grid(num_heads, unsigned((rows + kQTile - 1) / kQTile), unsigned(splits));
   const int group = num_heads / num_kv_heads;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const auto* q = static_cast<const uint16_t*>(query);
