@@ -397,3 +397,45 @@ def test_swap_walkthrough_through_the_c_abi():
     assert a.host_snapshot() == [1, 0, 2]
     assert not a.is_swapped(1)
     a.close()
+
+
+def test_shared_prefix_decode_checks_its_arguments_before_launch():
+    lib = pkv._lib
+    null = None
+    ws = ctypes.c_size_t()
+    # shared-prefix batch geometry: 256 sequences, 32 heads, prefix 1024 in
+    # blocks of 16, contexts up to 3000: 8 prefix ranges of 128 keys (a
+    # workgroup per CU) + one 2048-token suffix partition; up to 3100, two
+    assert lib.pkv_paged_attention_decode_shared_prefix_workspace_size(
+        256, 32, 32, 128, 16, 3000, 1024, 0, ctypes.byref(ws)) == 0
+    assert ws.value == 256 * 32 * (8 + 1) * (128 + 2) * 4
+    assert lib.pkv_paged_attention_decode_shared_prefix_workspace_size(
+        256, 32, 32, 128, 16, 3100, 1024, 0, ctypes.byref(ws)) == 0
+    assert ws.value == 256 * 32 * (8 + 2) * (128 + 2) * 4
+    # one 64-key range when the prefix is one tile
+    assert lib.pkv_paged_attention_decode_shared_prefix_workspace_size(
+        4, 4, 4, 128, 16, 300, 64, 64, ctypes.byref(ws)) == 0
+    assert ws.value == 4 * 4 * (1 + 4) * (128 + 2) * 4
+    # prefix not a multiple of the block size, longer than the contexts
+    assert lib.pkv_paged_attention_decode_shared_prefix_workspace_size(
+        4, 4, 4, 128, 16, 300, 72, 0, ctypes.byref(ws)) == 1
+    assert lib.pkv_paged_attention_decode_shared_prefix_workspace_size(
+        4, 4, 4, 128, 16, 300, 320, 0, ctypes.byref(ws)) == 1
+    args = (null, null, null, null, null)
+    # float32 caches and head_dim 64 are not served by the matrix-core part
+    assert lib.pkv_paged_attention_decode_shared_prefix(*args, 4, 4, 4, 128, 16, 32, 64, 300,
+                                                        64, 1.0, 0, null, null, 0, 0,
+                                                        null) == 7
+    assert lib.pkv_paged_attention_decode_shared_prefix(*args, 4, 4, 4, 64, 16, 32, 64, 300,
+                                                        64, 1.0, 0, null, null, 0, 2,
+                                                        null) == 7
+    # the hint is taken off the dtype; then the NULL pointers are caught
+    assert lib.pkv_paged_attention_decode_shared_prefix(*args, 4, 4, 4, 128, 16, 32, 64, 300,
+                                                        64, 1.0, 0, null, null, 0,
+                                                        2 | pkv.DECODE_SHARED_BLOCKS,
+                                                        null) == 1
+    assert b"NULL" in lib.pkv_last_error()
+    # empty batch: nothing to do
+    assert lib.pkv_paged_attention_decode_shared_prefix(*args, 0, 4, 4, 128, 16, 32, 64, 300,
+                                                        64, 1.0, 0, null, null, 0, 2,
+                                                        null) == 0
