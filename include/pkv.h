@@ -492,7 +492,9 @@ int32_t pkv_paged_attention_decode_workspace_size(
  * partitions).
  * Supported: head_dim in {64, 128}; num_heads / num_kv_heads in
  * {1, 2, 4, 8}; block_size a power of two in [8, 256]; the scale is any
- * finite float.  Row h reads KV head h / (num_heads / num_kv_heads). */
+ * finite float.  Row h reads KV head h / (num_heads / num_kv_heads).
+ * dtype is the cache's (PKV_F32, PKV_F16, PKV_BF16), optionally OR'd with
+ * PKV_DECODE_SHARED_BLOCKS; the same holds for every decode call below. */
 int32_t pkv_paged_attention_decode(
     const void* query, const void* key_cache, const void* value_cache,
     const int32_t* block_tables, const int32_t* context_lens,
