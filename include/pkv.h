@@ -687,6 +687,27 @@ int32_t pkv_paged_attention_decode_shared_prefix(
     float scale, int32_t partition_size, float* out, void* workspace,
     size_t workspace_bytes, int32_t dtype, void* stream);
 
+/* The step form of pkv_paged_attention_decode_shared_prefix for serving
+ * loops, as pkv_paged_attention_decode_step is of the plain decode: host
+ * lengths (after this step's appends) and this step's table changes go by
+ * value in the kernel arguments, the suffix kernel applies the changes to
+ * the device table and stores each sequence's new K/V row (key, value
+ * [num_seqs][num_kv_heads][head_dim], or both NULL) at its newest position
+ * before reading (explainer, serving section).  Same limits as
+ * pkv_paged_attention_decode_step (at most 256 sequences and 256 changes);
+ * the prefix's blocks, read through row 0 of block_tables, are full
+ * blocks and never change.  Equal, bit for bit, to the append followed by
+ * pkv_paged_attention_decode_shared_prefix on the updated tables. */
+int32_t pkv_paged_attention_decode_shared_prefix_step(
+    const void* query, const void* key, const void* value, void* key_cache,
+    void* value_cache, int32_t* block_tables, const int32_t* context_lens,
+    const int32_t* changes, int32_t num_changes, int32_t num_seqs,
+    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+    int32_t max_context_len, int32_t prefix_len, float scale,
+    int32_t partition_size, float* out, void* workspace,
+    size_t workspace_bytes, int32_t dtype, void* stream);
+
 /* Causal chunked prefill against the same paged cache (article §4.1/§4.2:
  * long prompts in chunks; §2.1: the same block-table gather and softmax).
  * The chunk's K/V must already be appended.

@@ -147,6 +147,9 @@ _SIGNATURES = {
                                                         _I32, _I32, _I32, _I32, _I32,
                                                         ctypes.c_float, _I32, _P, _P,
                                                         ctypes.c_size_t, _I32, _P]),
+    "pkv_paged_attention_decode_shared_prefix_step": (
+        _I32, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+               _I32, _I32, ctypes.c_float, _I32, _P, _P, ctypes.c_size_t, _I32, _P]),
     "pkv_scheduler_create": (_I32, [_I32, _I32, _P, _I32, _I32, _I32, _I32, _I32,
                                     ctypes.POINTER(_P)]),
     "pkv_scheduler_last_swaps": (_I32, [_P, _P, _P, _I32, _P, _P, _P, _I32, _P]),
@@ -1078,6 +1081,48 @@ def paged_attention_decode_shared_prefix(query, key_cache, value_cache, block_ta
         int(max_context_len), int(prefix_len), float(scale), int(partition_size),
         out.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
         _decode_code(key_cache, shared_blocks), _stream(query)))
+    return out
+
+
+def paged_attention_decode_shared_prefix_step(query, key, value, key_cache, value_cache,
+                                              block_tables, context_lens, changes, prefix_len,
+                                              scale, max_context_len, partition_size=0, out=None,
+                                              workspace=None, shared_blocks=False):
+    """Step form of paged_attention_decode_shared_prefix
+    (pkv_paged_attention_decode_shared_prefix_step): block_tables is the
+    device table kept across steps (updated in place with ``changes``);
+    context_lens host int32 [B] and changes host int32 [n, 3] as for
+    paged_attention_decode_step; key/value the step's new rows or None."""
+    nb, hkv, bs, d = _cache_dims(key_cache, value_cache)
+    _dev(query, "query", dtype=key_cache.dtype, ndim=3)
+    _dev(block_tables, "block_tables", dtype=torch.int32, ndim=2)
+    b, hq, _ = query.shape
+    lens = np.ascontiguousarray(np.asarray(context_lens, dtype=np.int32))
+    changes = np.ascontiguousarray(np.asarray(changes, dtype=np.int32).reshape(-1, 3))
+    if lens.shape != (b,) or query.shape[2] != d or block_tables.shape[0] != b:
+        raise InvalidArgument("query [B, Hq, D], block_tables [B, max_blocks], context_lens [B]")
+    kp = vp = None
+    if key is not None or value is not None:
+        _dev(key, "key", dtype=key_cache.dtype, ndim=3)
+        _dev(value, "value", dtype=key_cache.dtype, ndim=3)
+        if tuple(key.shape) != (b, hkv, d) or value.shape != key.shape:
+            raise InvalidArgument("key/value must be [B, num_kv_heads, head_dim]")
+        kp, vp = key.data_ptr(), value.data_ptr()
+    if out is None:
+        out = torch.empty((b, hq, d), dtype=torch.float32, device=query.device)
+    _dev(out, "out", dtype=torch.float32, ndim=3)
+    need = paged_attention_decode_shared_prefix_workspace_size(
+        b, hq, hkv, d, bs, int(max_context_len), int(prefix_len), partition_size)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=query.device)
+    _dev(workspace, "workspace")
+    _check(_lib.pkv_paged_attention_decode_shared_prefix_step(
+        query.data_ptr(), kp, vp, key_cache.data_ptr(), value_cache.data_ptr(),
+        block_tables.data_ptr(), lens.ctypes.data, changes.ctypes.data, changes.shape[0], b, hq,
+        hkv, d, bs, block_tables.shape[1], nb, int(max_context_len), int(prefix_len), float(scale),
+        int(partition_size), out.data_ptr(), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _decode_code(key_cache, shared_blocks),
+        _stream(query)))
     return out
 
 

@@ -1451,13 +1451,18 @@ extern "C" int32_t pkv_paged_attention_decode_shared_prefix_workspace_size(
   return ok();
 }
 
-extern "C" int32_t pkv_paged_attention_decode_shared_prefix(
-    const void* query, const void* key_cache, const void* value_cache,
-    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
-    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-    int32_t max_blocks_per_seq, int32_t num_blocks, int32_t max_context_len,
-    int32_t prefix_len, float scale, int32_t partition_size, float* out, void* workspace,
-    size_t workspace_bytes_given, int32_t dtype, void* stream) {
+namespace {
+// The shared-prefix call, with the lengths from the device (step == null)
+// or by value with this step's table changes and new K/V rows (step form).
+int32_t shared_prefix_call(const void* query, const void* key_new, const void* value_new,
+                           const void* key_cache, const void* value_cache,
+                           const int32_t* block_tables, const int32_t* context_lens,
+                           int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                           int32_t num_blocks, int32_t max_context_len, int32_t prefix_len,
+                           float scale, int32_t partition_size, float* out, void* workspace,
+                           size_t workspace_bytes_given, int32_t dtype, void* stream,
+                           const StepMeta* step) {
   const bool shared_blocks = (dtype & PKV_DECODE_SHARED_BLOCKS) != 0;
   dtype &= ~int32_t(PKV_DECODE_SHARED_BLOCKS);
   if (dtype != PKV_BF16 && dtype != PKV_F16) {
@@ -1488,10 +1493,15 @@ extern "C" int32_t pkv_paged_attention_decode_shared_prefix(
   if (int64_t(prefix_len) > int64_t(max_blocks_per_seq) * block_size)
     return fail(PKV_ERR_INVALID, "prefix_len %d exceeds the block table's capacity", prefix_len);
   if (num_seqs == 0) return ok();
-  if (!query || !key_cache || !value_cache || !block_tables || !context_lens || !out)
+  if (!query || !key_cache || !value_cache || !block_tables || (!step && !context_lens) || !out)
     return fail(PKV_ERR_INVALID, "NULL pointer argument");
   if (!aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache) || !aligned16(out))
     return fail(PKV_ERR_INVALID, "query, caches and out must be 16-byte aligned");
+  if (key_new || value_new) {
+    if (!key_new || !value_new) return fail(PKV_ERR_INVALID, "key and value must both be given");
+    if (!aligned16(key_new) || !aligned16(value_new))
+      return fail(PKV_ERR_INVALID, "key and value must be 16-byte aligned");
+  }
   const size_t need = size_t(num_seqs) * num_heads * slots * (size_t(head_dim) + 2) * sizeof(float);
   if (!workspace || workspace_bytes_given < need)
     return fail(PKV_ERR_BUFFER_TOO_SMALL, "workspace needs %zu bytes, got %zu", need,
@@ -1515,6 +1525,8 @@ extern "C" int32_t pkv_paged_attention_decode_shared_prefix(
   prm.block_tables = block_tables;
   prm.block_tables_rw = const_cast<int32_t*>(block_tables);
   prm.context_lens = context_lens;
+  prm.key_new = static_cast<const uint8_t*>(key_new);
+  prm.value_new = static_cast<const uint8_t*>(value_new);
   prm.out = out;
   prm.ws_acc = ws_acc;
   prm.ws_ml = ws_ml;
@@ -1531,11 +1543,47 @@ extern "C" int32_t pkv_paged_attention_decode_shared_prefix(
   prm.start = prefix_len;
   prm.slot_base = splits;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  e = dispatch_decode(dtype, head_dim, G, prm, DeviceMeta{}, num_seqs, s);
+  e = step ? dispatch_decode(dtype, head_dim, G, prm, *step, num_seqs, s)
+           : dispatch_decode(dtype, head_dim, G, prm, DeviceMeta{}, num_seqs, s);
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
 
-  // 3. log-sum-exp merge of the prefix and suffix partials
-  e = launch_merge(prm, DeviceMeta{}, num_seqs, num_heads, head_dim, s);
+  // 3. log-sum-exp merge of the prefix and suffix partials (every row)
+  e = step ? launch_merge(prm, *step, num_seqs, num_heads, head_dim, s)
+           : launch_merge(prm, DeviceMeta{}, num_seqs, num_heads, head_dim, s);
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "decode merge launch: %s", hipGetErrorString(e));
   return ok();
+}
+}  // namespace
+
+extern "C" int32_t pkv_paged_attention_decode_shared_prefix(
+    const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t max_blocks_per_seq, int32_t num_blocks, int32_t max_context_len,
+    int32_t prefix_len, float scale, int32_t partition_size, float* out, void* workspace,
+    size_t workspace_bytes_given, int32_t dtype, void* stream) {
+  return shared_prefix_call(query, nullptr, nullptr, key_cache, value_cache, block_tables,
+                            context_lens, num_seqs, num_heads, num_kv_heads, head_dim,
+                            block_size, max_blocks_per_seq, num_blocks, max_context_len,
+                            prefix_len, scale, partition_size, out, workspace,
+                            workspace_bytes_given, dtype, stream, nullptr);
+}
+
+extern "C" int32_t pkv_paged_attention_decode_shared_prefix_step(
+    const void* query, const void* key, const void* value, void* key_cache,
+    void* value_cache, int32_t* block_tables, const int32_t* context_lens,
+    const int32_t* changes, int32_t num_changes, int32_t num_seqs, int32_t num_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+    int32_t num_blocks, int32_t max_context_len, int32_t prefix_len, float scale,
+    int32_t partition_size, float* out, void* workspace, size_t workspace_bytes_given,
+    int32_t dtype, void* stream) {
+  StepMeta m;
+  int32_t st = pack_step(context_lens, changes, num_changes, num_seqs, num_kv_heads,
+                         max_blocks_per_seq, &m);
+  if (st != PKV_OK) return st;
+  return shared_prefix_call(query, key, value, key_cache, value_cache, block_tables, nullptr,
+                            num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                            max_blocks_per_seq, num_blocks, max_context_len, prefix_len, scale,
+                            partition_size, out, workspace, workspace_bytes_given, dtype, stream,
+                            &m);
 }

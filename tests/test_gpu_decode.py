@@ -774,3 +774,48 @@ def test_shared_prefix_decode_full_size_sampled():
     log("shared-prefix decode, full size: sampled max abs err", worst)
     assert worst <= TOL[w.dtype]
     assert np.isfinite(got).all()
+
+
+@pytest.mark.parametrize("part", [64, 1024])
+def test_shared_prefix_step_is_append_then_shared_prefix_call(part):
+    """pkv_paged_attention_decode_shared_prefix_step (host lengths and
+    table changes by value, the new rows stored by the suffix kernel, a
+    device table kept across steps) == the append followed by the plain
+    shared-prefix call on freshly uploaded tables, bit for bit, over steps
+    that open new blocks; 1024-token partitions take the grid that
+    dispatches a sequence's partitions together."""
+    w = workloads.scaled(workloads.get("shared_prefix_bf16"), num_seqs=5, num_heads=8,
+                         num_kv_heads=4, prefix=128, lens="uniform:0,1500", chunk=0)
+    p = workloads.plan(w)
+    a, b = GpuState(w, p), GpuState(w, p)
+    seqs = p.seqs
+    steps = 20
+    mb = max(len(a.alloc.block_table(s)) for s in seqs) + steps // w.block_size + 2
+    th, _ = b.alloc.build_block_tables(seqs, mb)
+    dev_tables = torch.from_numpy(th.copy()).to(DEV)
+    ones = np.ones(len(seqs), dtype=np.int32)
+    for i in range(steps):
+        k, v = workloads.kv_rows(w, len(p.ops) + i, len(seqs))
+        kt = workloads.to_dtype(k, w.dtype).to(DEV)
+        vt = workloads.to_dtype(v, w.dtype).to(DEV)
+        q = workloads.to_dtype(workloads.normal([w.seed, 17, i], (len(seqs), w.num_heads,
+                                                                   w.head_dim), w.std),
+                               w.dtype).to(DEV)
+        slots, pa = a.alloc.append_batch(seqs, ones)
+        _, pb, lens, changes = b.alloc.append_batch_changes(seqs, ones)
+        assert not pa and not pb                 # the prefix is block aligned: no copies
+        pkv.paged_kv_append(kt, vt, a.kc, a.vc, torch.from_numpy(slots).to(DEV))
+        ta, la, _, lh = a.tables(seqs)
+        ta = torch.nn.functional.pad(ta, (0, mb - ta.shape[1]), value=-1).contiguous()
+        mc = int(lh.max())
+        want = pkv.paged_attention_decode_shared_prefix(q, a.kc, a.vc, ta, la, w.prefix, w.scale,
+                                                        mc, partition_size=part)
+        got = pkv.paged_attention_decode_shared_prefix_step(q, kt, vt, b.kc, b.vc, dev_tables,
+                                                            lens, changes, w.prefix, w.scale,
+                                                            mc, partition_size=part)
+        torch.cuda.synchronize()
+        assert torch.equal(got, want), f"step {i}"
+    assert torch.equal(a.kc.view(torch.uint8), b.kc.view(torch.uint8))
+    assert torch.equal(a.vc.view(torch.uint8), b.vc.view(torch.uint8))
+    th, _ = b.alloc.build_block_tables(seqs, mb)
+    assert np.array_equal(dev_tables.cpu().numpy(), th)
