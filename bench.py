@@ -12,23 +12,29 @@ through every stage of the path:
   4. paged_attention_decode_step: the split-K decode kernel, which applies
      the table changes, stores each sequence's new K/V row at its newest
      position (the slot the allocator returned) and attends, then the
-     log-sum-exp merge kernel.
+     log-sum-exp merge kernel.  A batch forked from one prefix (the
+     shared-prefix workload) steps through
+     paged_attention_decode_shared_prefix_step instead: every query against
+     the prefix on the matrix cores, the suffixes by the split-K kernel
+     (append fused), one merge.
 The cache is resident in HBM before timing starts.  ``value`` is the KV
 bytes the decode reads per step (sum over sequences of context_len * Hkv *
 head_dim * 2 * element size) divided by the wall time of a whole step.
 With a shared prefix those logical bytes exceed what HBM delivers (the
-prefix is read once per sequence but served from the caches); the roofline
-then uses the unique bytes (prefix counted once).
-``roofline`` reports the decode partition kernel alone, timed with HIP
+prefix is the same K/V for every sequence); the roofline then uses the
+unique bytes (prefix counted once).
+``roofline`` reports the decode partition kernel alone (with a shared
+prefix: the three launches of the shared-prefix call), timed with HIP
 events on the stream it runs on (every fourth timed step, so the events'
 own cost stays out of the step time); its ``traffic`` comes from the committed
 rocprofv3 counter summary of the same kernel source, when there is one.
 ``cpu_baseline`` times the float64 CPU oracle on a small sample of the same
 workload (reported only; the host's CPU model and core count go into its
 ``sample``).  For the shared-prefix workload the line also carries
-``prefill``: one causal 512-row chunked prefill per sequence, timed the
-same way, against the bf16 matrix-core peak; its oracle timing (one
-sequence's chunk) is ``cpu_baseline.prefill``.
+``decode_shared_prefix`` (the shared-prefix call against the split-K call
+on the same cache state) and ``prefill``: one causal 512-row chunked
+prefill per sequence, timed the same way, against the bf16 matrix-core
+peak; its oracle timing (one sequence's chunk) is ``cpu_baseline.prefill``.
 
 Usage: python bench.py [--steps K] [--warmup W] [--workload NAME]
        python bench.py --copy-calibration   (block copy of a known size,
@@ -166,6 +172,14 @@ def gpu_run(args, w, torch, pkv, workloads):
     shared = any(r > 1 for r in alloc.snapshot()[1])
     launch = pkv.DecodeLauncher(kc, vc, w.num_heads, b, mb, max_len, part, out, workspace,
                                 shared_blocks=shared)
+    # a batch forked from one prefix steps through the shared-prefix call
+    # instead: the prefix on the matrix cores, the suffixes split-K (the
+    # append fused), one merge
+    ws_sp = None
+    if w.prefix:
+        ws_sp = torch.empty(max(pkv.paged_attention_decode_shared_prefix_workspace_size(
+            b, w.num_heads, w.num_kv_heads, w.head_dim, w.block_size, max_len, w.prefix), 16),
+            dtype=torch.uint8, device=dev)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(total_steps)]
     # HIP events bracket the kernels of every fourth timed step: each record
@@ -185,11 +199,18 @@ def gpu_run(args, w, torch, pkv, workloads):
         timed_here = i in sampled
         if timed_here:
             ev[i][0].record(stream)
-        launch.step_partials(q[i], tables_d, lens_h, changes_h, n_changes, mc, w.scale,  # 4
-                             k_new[i], v_new[i])
-        if timed_here:
-            ev[i][1].record(stream)
-        launch.step_merge(lens_h, mc)
+        if w.prefix:                                                         # 4
+            pkv.paged_attention_decode_shared_prefix_step(
+                q[i], k_new[i], v_new[i], kc, vc, tables_d, lens_h, changes_h[:n_changes],
+                w.prefix, w.scale, mc, out=out, workspace=ws_sp)
+            if timed_here:
+                ev[i][1].record(stream)
+        else:
+            launch.step_partials(q[i], tables_d, lens_h, changes_h, n_changes, mc, w.scale,  # 4
+                                 k_new[i], v_new[i])
+            if timed_here:
+                ev[i][1].record(stream)
+            launch.step_merge(lens_h, mc)
         if timed_here:
             ev[i][2].record(stream)
         step_bytes[i] = kv_bytes(w, lens_h)
@@ -761,14 +782,19 @@ def main():
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                    "block_size": w.block_size, "context_lens": w.lens,
                    "shared_prefix": w.prefix, "partition_size": r["part"],
-                   "kv_loads": "cached (shared blocks)" if r["shared"] else "non-temporal"},
+                   "kv_loads": ("prefix: matrix-core contraction; suffixes: non-temporal"
+                                if w.prefix else
+                                "cached (shared blocks)" if r["shared"] else "non-temporal")},
         "hbm_peak_frac": round(value / HBM_PEAK_GBPS, 4),
         "tokens_per_s": round(r["batch"] / (ms_step * 1e-3), 1),
         "kv_bytes_per_step": int(mean_bytes),
         "kv_bytes_per_step_unique": int(unique_bytes),
         "decode_partition_us": round(kernel_ms * 1e3, 2),
         "decode_merge_us": round(float(r["merge_ms"].mean()) * 1e3, 2),
-        "roofline": {"bound": "hbm", "kernel": "decode_partition_kernel (append fused)",
+        "roofline": {"bound": "hbm",
+                     "kernel": ("shared-prefix decode step: prefix_kernel on the matrix cores + "
+                                "decode_partition_kernel over the suffixes (append fused) + merge"
+                                if w.prefix else "decode_partition_kernel (append fused)"),
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic_from_profiles(w, src),
