@@ -48,6 +48,9 @@ def test_hand_worked_traces(trace):
         if "swap_in" in want:
             assert [list(p) for p in got["swap_in"]] == want["swap_in"], (k, want["why"])
             assert [list(p) for p in got["swap_out"]] == want["swap_out"], (k, want["why"])
+        # the counters behind the reported slot utilisation (cached tokens
+        # over allocated or reserved slots), worked by hand per step
+        assert s.stats() == want["stats"], (k, want["why"])
     assert s.stats()["finished"] == len(trace["requests"])
     assert s.alloc.num_free() == trace["config"]["num_blocks"]
 

@@ -68,6 +68,7 @@ def test_golden_traces_through_the_c_abi():
             if "swap_in" in want:
                 assert plan.swap_in.tolist() == want["swap_in"], want["why"]
                 assert plan.swap_out.tolist() == want["swap_out"], want["why"]
+            assert nat.stats() == want["stats"], want["why"]
         nat.close()
 
 
