@@ -556,9 +556,13 @@ int32_t pkv_paged_attention_decode_append_partials(
  *                  as reported by pkv_append_batch_changes
  *   key, value     [num_seqs][num_kv_heads][head_dim] new rows, or both
  *                  NULL for no append
- * Limits (kernel-argument space): num_seqs <= 256, num_changes <= 256
- * (PKV_ERR_UNSUPPORTED beyond).  Other arguments, semantics and errors as
- * pkv_paged_attention_decode_append. */
+ * The metadata rides in kernel arguments: one launch of each kernel serves
+ * 256 sequences of the work order (longest first), so a larger batch takes
+ * ceil(num_seqs / 256) launches of each.  Limits: num_seqs <= 65535; the
+ * changes of the sequences one launch serves at most 256
+ * (PKV_ERR_UNSUPPORTED beyond) -- a step of one token per sequence makes
+ * at most one change per sequence, always within it.  Other arguments,
+ * semantics and errors as pkv_paged_attention_decode_append. */
 int32_t pkv_paged_attention_decode_step(
     const void* query, const void* key, const void* value, void* key_cache,
     void* value_cache, int32_t* block_tables, const int32_t* context_lens,
@@ -662,11 +666,12 @@ int32_t pkv_paged_attention_decode_fp8_partials(
  *                  PKV_BF16 (the matrix-core path), head_dim 128; the
  *                  PKV_DECODE_SHARED_BLOCKS hint applies to the suffix loads
  *   prefix_len     tokens shared by every sequence, a positive multiple of
- *                  block_size, at most max_context_len.  The caller
- *                  guarantees that tokens [0, prefix_len) hold the same K/V
- *                  in every sequence (a fork, or copies of one); they are
- *                  read through row 0 of block_tables.  A sequence whose
- *                  device length is below prefix_len gets a NaN row.
+ *                  block_size, at most max_context_len.  The prefix is
+ *                  read once, through row 0 of block_tables; every other
+ *                  row must name the same blocks for it (a fork shares
+ *                  them): a sequence whose first prefix_len / block_size
+ *                  table entries differ from row 0's, or whose device
+ *                  length is below prefix_len, gets a NaN row.
  *   partition_size split-K partition of the suffixes (0 = automatic)
  *   workspace      float32 partials, at least the bytes
  *                  pkv_paged_attention_decode_shared_prefix_workspace_size
@@ -693,11 +698,13 @@ int32_t pkv_paged_attention_decode_shared_prefix(
  * value in the kernel arguments, the suffix kernel applies the changes to
  * the device table and stores each sequence's new K/V row (key, value
  * [num_seqs][num_kv_heads][head_dim], or both NULL) at its newest position
- * before reading (explainer, serving section).  Same limits as
- * pkv_paged_attention_decode_step (at most 256 sequences and 256 changes);
- * the prefix's blocks, read through row 0 of block_tables, are full
- * blocks and never change.  Equal, bit for bit, to the append followed by
- * pkv_paged_attention_decode_shared_prefix on the updated tables. */
+ * before reading (explainer, serving section).  Launches and limits as
+ * pkv_paged_attention_decode_step.  The prefix's blocks are full blocks
+ * and never change: with key and value given every length must exceed
+ * prefix_len (the new row lands past the prefix), and every change must
+ * name a logical block past the prefix of a sequence longer than it
+ * (PKV_ERR_INVALID otherwise).  Equal, bit for bit, to the append followed
+ * by pkv_paged_attention_decode_shared_prefix on the updated tables. */
 int32_t pkv_paged_attention_decode_shared_prefix_step(
     const void* query, const void* key, const void* value, void* key_cache,
     void* value_cache, int32_t* block_tables, const int32_t* context_lens,

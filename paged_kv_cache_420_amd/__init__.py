@@ -877,6 +877,22 @@ class DecodeLauncher:
             raise InvalidArgument(f"{name} must be a contiguous {dtype} tensor of shape {shape}")
         return t.data_ptr()
 
+    def _host_lens(self, lens):
+        b = self._dims[0]
+        if not (isinstance(lens, np.ndarray) and lens.dtype == np.int32 and lens.shape == (b,)
+                and lens.flags.c_contiguous):
+            raise InvalidArgument(f"lens must be a contiguous int32 numpy array of shape ({b},)")
+        return lens.ctypes.data
+
+    @staticmethod
+    def _host_changes(changes, num_changes):
+        if not (isinstance(changes, np.ndarray) and changes.dtype == np.int32 and
+                changes.ndim == 2 and changes.shape[1] == 3 and changes.flags.c_contiguous):
+            raise InvalidArgument("changes must be a contiguous int32 numpy array of shape (n, 3)")
+        if not 0 <= int(num_changes) <= changes.shape[0]:
+            raise InvalidArgument("num_changes outside the changes array")
+        return changes.ctypes.data
+
     def partials(self, query, block_tables, context_lens, max_context_len, scale, key=None,
                  value=None):
         if max_context_len > self._max_ctx:
@@ -912,8 +928,10 @@ class DecodeLauncher:
         if key is not None:
             k = self._check_step(key, self._kv_shape, self._dtype, "key")
             v = self._check_step(value, self._kv_shape, self._dtype, "value")
+        lp = self._host_lens(lens)
+        cp = self._host_changes(changes, num_changes)
         _check(_lib.pkv_paged_attention_decode_step_partials(
-            q, k, v, self._kc, self._vc, t, lens.ctypes.data, changes.ctypes.data,
+            q, k, v, self._kc, self._vc, t, lp, cp,
             int(num_changes), b, hq, hkv, d, bs, mb, nb, int(max_context_len), float(scale),
             self.part, self._out, self._ws[0], self._ws[1], self._code, self._stream))
 
@@ -923,8 +941,8 @@ class DecodeLauncher:
             raise InvalidArgument("max_context_len above the launcher's bound")
         b, hq, hkv, d, bs, mb, nb = self._dims
         _check(_lib.pkv_paged_attention_decode_step_merge(
-            lens.ctypes.data, b, hq, hkv, d, bs, mb, int(max_context_len), self.part, self._out,
-            self._ws[0], self._ws[1], self._stream))
+            self._host_lens(lens), b, hq, hkv, d, bs, mb, int(max_context_len), self.part,
+            self._out, self._ws[0], self._ws[1], self._stream))
 
     def merge(self, context_lens, max_context_len):
         if max_context_len > self._max_ctx:
@@ -1070,6 +1088,8 @@ def paged_attention_decode_shared_prefix(query, key_cache, value_cache, block_ta
     if out is None:
         out = torch.empty((b, hq, d), dtype=torch.float32, device=query.device)
     _dev(out, "out", dtype=torch.float32, ndim=3)
+    if tuple(out.shape) != (b, hq, d):
+        raise InvalidArgument("out must be [B, Hq, D]")
     need = paged_attention_decode_shared_prefix_workspace_size(
         b, hq, hkv, d, bs, int(max_context_len), int(prefix_len), partition_size)
     if workspace is None:
@@ -1111,6 +1131,8 @@ def paged_attention_decode_shared_prefix_step(query, key, value, key_cache, valu
     if out is None:
         out = torch.empty((b, hq, d), dtype=torch.float32, device=query.device)
     _dev(out, "out", dtype=torch.float32, ndim=3)
+    if tuple(out.shape) != (b, hq, d):
+        raise InvalidArgument("out must be [B, Hq, D]")
     need = paged_attention_decode_shared_prefix_workspace_size(
         b, hq, hkv, d, bs, int(max_context_len), int(prefix_len), partition_size)
     if workspace is None:

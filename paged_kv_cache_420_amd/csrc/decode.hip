@@ -39,6 +39,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <vector>
 
 #include "common.h"
 
@@ -425,6 +426,7 @@ struct DecodeParams {
   float* ws_acc;               // [B][Hq][max_parts][D]  (split-K partials)
   float* ws_ml;                // [B][Hq][max_parts][2]
   int32_t num_kv_heads, log2_bs, max_blocks, num_blocks, max_ctx, part, max_parts;
+  int32_t grid_parts;          // partitions per sequence in the grid (<= max_parts)
   float scale_log2;            // scale * log2(e), times the K scale of an 8-bit cache
   float v_scale;               // V scale of an 8-bit cache (unused otherwise)
   int32_t shared_blocks;       // nonzero: launch the cached-load kernel (shared blocks)
@@ -440,16 +442,18 @@ struct DecodeParams {
 // in the kernel arguments (no host-to-device copy on the step's critical
 // path) -- the lengths, and the table entries this step's appends set,
 // which the kernels apply while staging block ids and persist to the
-// device table for later launches.
-constexpr int kStepMaxSeqs = 256;
-constexpr int kStepMaxChanges = 256;
+// device table for later launches.  One launch carries the metadata of at
+// most kStepRanks sequences (kernel-argument space); a larger batch is
+// served by consecutive launches over consecutive ranks of its work order.
+constexpr int kStepRanks = 256;
+constexpr int kStepMaxChanges = 256;  // per launch
 
 struct DeviceMeta {
   static constexpr bool kHost = false;
-  __device__ int len(const DecodeParams& prm, int b) const { return prm.context_lens[b]; }
-  // grid (kv head, sequence, partition)
-  __device__ void work(int& b, int& p) const {
-    b = blockIdx.y;
+  __device__ int len(const DecodeParams& prm, int b, int) const { return prm.context_lens[b]; }
+  // grid (kv head, sequence, partition): the rank is the sequence
+  __device__ void work(int& b, int& p, int& rank) const {
+    b = rank = blockIdx.y;
     p = blockIdx.z;
   }
   // merge grid (query head, sequence)
@@ -458,31 +462,33 @@ struct DeviceMeta {
 
 struct StepMeta {
   static constexpr bool kHost = true;
-  int32_t lens[kStepMaxSeqs];
-  int32_t change_key[kStepMaxChanges];    // logical block index << 8 | row
-  int32_t change_block[kStepMaxChanges];  // physical block
+  // Work order: rank r of this launch serves batch row seq[r], longest
+  // first over the whole batch, so the longest partitions start first and
+  // the short ones fill the end of the launch.  With parts_per_rank > 0
+  // the grid is (kv head, rank * parts_per_rank + partition, 1): a
+  // sequence's partitions are dispatched together, at its rank, instead of
+  // every sequence's second partition after all first ones.  0: grid (kv
+  // head, rank, partition).
+  int32_t lens[kStepRanks];                // by rank
+  int32_t change_key[kStepMaxChanges];     // logical block index << 8 | rank
+  int32_t change_block[kStepMaxChanges];   // physical block
+  uint16_t seq[kStepRanks];
   int32_t num_changes;
-  // Work order: rank r serves sequence order[r], longest first, so the
-  // longest partitions start first and the short ones fill the end of the
-  // launch.  With parts_per_rank > 0 the grid is (kv head, rank *
-  // parts_per_rank + partition, 1): a sequence's partitions are dispatched
-  // together, at its rank, instead of every sequence's second partition
-  // after all first ones.  0: grid (kv head, rank, partition).
   int32_t parts_per_rank;
-  uint8_t order[kStepMaxSeqs];
-  __device__ int len(const DecodeParams&, int b) const { return lens[b]; }
+  __device__ int len(const DecodeParams&, int, int rank) const { return lens[rank]; }
   // merge grid (query head, rank): the launch covers only the ranks up to
   // the last sequence that spans two partitions
-  __device__ int merge_seq(int y) const { return order[y]; }
-  __device__ void work(int& b, int& p) const {
+  __device__ int merge_seq(int y) const { return seq[y]; }
+  __device__ void work(int& b, int& p, int& rank) const {
     if (parts_per_rank > 0) {
       const int y = blockIdx.y;
-      b = order[y / parts_per_rank];
+      rank = y / parts_per_rank;
       p = y % parts_per_rank;
     } else {
-      b = order[blockIdx.y];
+      rank = blockIdx.y;
       p = blockIdx.z;
     }
+    b = seq[rank];
   }
 };
 
@@ -517,20 +523,34 @@ __global__ __launch_bounds__(kThreads, (decode_min_blocks<DT, G>())) void decode
   // maximum), and putting them fastest would pile every sequence's first
   // partition onto the same XCDs.
   const int kvh = blockIdx.x;
-  int b, p_idx;
-  meta.work(b, p_idx);
+  int b, p_idx, rank;
+  meta.work(b, p_idx, rank);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int bs = 1 << log2_bs;
   const int num_heads = num_kv_heads * G;
 
-  const int n = meta.len(prm, b);
+  const int n = meta.len(prm, b, rank);
   const int start = prm.start, slot_base = prm.slot_base;
   const bool bad_len =
       n < start || n > prm.max_ctx || int64_t(n) > int64_t(max_blocks) * bs;
   // in suffix mode a sequence with no token past the prefix has no partition
   const int nparts = bad_len ? 1 : slot_base > 0 ? cdiv(n - start, part) : max(1, cdiv(n, part));
+  if (slot_base > 0 && p_idx == 0 && !bad_len) {
+    // Suffix mode: the shared prefix was read through row 0 of the table.
+    // A sequence whose own table does not name the same blocks for it is
+    // inconsistent input: its prefix partial's max becomes NaN, so the
+    // merge writes a NaN row (first partition of each kv head; the prefix
+    // launch that wrote the partial has completed).
+    const int32_t* own = prm.block_tables + int64_t(b) * max_blocks;
+    bool differs = false;
+    for (int i = int(threadIdx.x); i < (start >> log2_bs); i += kThreads)
+      differs |= own[i] != prm.block_tables[i];
+    if (__syncthreads_or(differs) && threadIdx.x < G)
+      prm.ws_ml[((int64_t(b) * num_kv_heads * G + int64_t(kvh) * G + threadIdx.x) *
+                     prm.max_parts) * 2] = __builtin_nanf("");
+  }
   if (p_idx >= nparts) return;
 
   float* out_row = prm.out + (int64_t(b) * num_heads + int64_t(kvh) * G) * D;
@@ -558,7 +578,7 @@ __global__ __launch_bounds__(kThreads, (decode_min_blocks<DT, G>())) void decode
     for (int t = tid; t < meta.num_changes; t += kThreads) {
       const int key = meta.change_key[t];
       const int j = (key >> 8) - j0;
-      if ((key & 255) == b && j >= 0 && j < nblk) {
+      if ((key & 255) == rank && j >= 0 && j < nblk) {
         s_blk[j] = meta.change_block[t];
         if (kvh == 0) prm.block_tables_rw[int64_t(b) * max_blocks + j0 + j] = meta.change_block[t];
       }
@@ -813,7 +833,7 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(
   float* __restrict__ out = prm.out;
   const int h = blockIdx.x;
   const int b = meta.merge_seq(blockIdx.y);
-  const int n = meta.len(prm, b);
+  const int n = meta.len(prm, b, blockIdx.y);
   const bool bad_len = n < prm.start || n > max_ctx ||
                        int64_t(n) > (int64_t(max_blocks) << log2_bs);
   if (bad_len) return;
@@ -883,7 +903,7 @@ hipError_t launch_decode(const DecodeParams& prm, const Meta& meta, int B, hipSt
   const size_t lds = size_t(score_floats) * 4 + size_t(prm.part >> 3) * 4 +
                      size_t(2 * kWaves * G) * 4;
   if (lds > 160 * 1024) return hipErrorInvalidValue;  // beyond one CU's LDS
-  dim3 grid(prm.num_kv_heads, B, prm.max_parts);
+  dim3 grid(prm.num_kv_heads, B, prm.grid_parts);
   Meta m = meta;
   if constexpr (Meta::kHost) {
     // A sequence's partitions consecutive in the grid (when the row count
@@ -896,10 +916,10 @@ hipError_t launch_decode(const DecodeParams& prm, const Meta& meta, int B, hipSt
     // with shared blocks every sequence's first partition reads the shared
     // prefix at once, while it is in the caches (2% faster).
     m.parts_per_rank = 0;
-    if (prm.max_parts > 1 && prm.part >= 1024 && !prm.shared_blocks &&
-        int64_t(B) * prm.max_parts <= 65535) {
-      m.parts_per_rank = prm.max_parts;
-      grid = dim3(prm.num_kv_heads, B * prm.max_parts, 1);
+    if (prm.grid_parts > 1 && prm.part >= 1024 && !prm.shared_blocks &&
+        int64_t(B) * prm.grid_parts <= 65535) {
+      m.parts_per_rank = prm.grid_parts;
+      grid = dim3(prm.num_kv_heads, B * prm.grid_parts, 1);
     }
   }
   if (prm.shared_blocks)
@@ -1009,6 +1029,23 @@ extern "C" int32_t pkv_paged_attention_decode_workspace_size(
 namespace pkv {
 namespace {
 
+// The launches of one step call (see make_step_plan).
+struct StepPlan {
+  std::vector<StepMeta> chunks;
+  const int32_t* host_lens = nullptr;  // [num_seqs], batch order
+  int32_t num_seqs = 0;
+  int32_t ranks(size_t c) const {
+    return std::min<int32_t>(kStepRanks, num_seqs - int32_t(c) * kStepRanks);
+  }
+  // ranks of launch c up to the last one whose length exceeds `part`
+  int32_t rows_above(size_t c, int32_t part) const {
+    int32_t rows = 0;
+    for (int32_t r = 0; r < ranks(c); ++r)
+      if (chunks[c].lens[r] > part) rows = r + 1;
+    return rows;
+  }
+};
+
 struct DecodeArgs {
   int32_t G = 0, part = 0, max_parts = 0, log2_bs = 0;
   float* ws_acc = nullptr;
@@ -1095,7 +1132,7 @@ int32_t prepare_decode(const void* query, const void* key_cache,
 // made coherent with each other at a kernel boundary (a device-scope fence
 // per workgroup writes back the whole L2 and costs more than the launch).
 // `step` (may be null): lengths and table changes by value, for the step
-// calls; context_lens is then unused.
+// calls, one launch per chunk of ranks; context_lens is then unused.
 int32_t run_decode(const void* query, const void* key_new, const void* value_new,
                    const void* key_cache, const void* value_cache,
                    const int32_t* block_tables, const int32_t* context_lens,
@@ -1104,12 +1141,13 @@ int32_t run_decode(const void* query, const void* key_new, const void* value_new
                    int32_t num_blocks, int32_t max_context_len, float scale,
                    int32_t partition_size, float* out, void* workspace,
                    size_t workspace_bytes_given, int32_t dtype, void* stream, bool partials,
-                   bool merge, const StepMeta* step, float k_scale = 1.0f,
+                   bool merge, const StepPlan* step, float k_scale = 1.0f,
                    float v_scale = 1.0f) {
   const bool shared_blocks = (dtype & PKV_DECODE_SHARED_BLOCKS) != 0;
   dtype &= ~int32_t(PKV_DECODE_SHARED_BLOCKS);
   DecodeArgs a;
-  const int32_t* lens_check = step ? reinterpret_cast<const int32_t*>(step->lens) : context_lens;
+  // the step calls' host lengths were checked when the plan was made
+  const int32_t* lens_check = step ? step->host_lens : context_lens;
   int32_t st = prepare_decode(query, key_cache, value_cache, block_tables, lens_check,
                               num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                               max_blocks_per_seq, num_blocks, max_context_len, scale,
@@ -1141,48 +1179,52 @@ int32_t run_decode(const void* query, const void* key_new, const void* value_new
   prm.max_ctx = max_context_len;
   prm.part = a.part;
   prm.max_parts = a.max_parts;
+  prm.grid_parts = a.max_parts;
   prm.scale_log2 = k_scale == 1.0f ? scale * kLog2e : (scale * k_scale) * kLog2e;
   prm.v_scale = v_scale;
   prm.shared_blocks = shared_blocks ? 1 : 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
   if (partials) {
-    e = step ? dispatch_decode(dtype, head_dim, a.G, prm, *step, num_seqs, s)
-             : dispatch_decode(dtype, head_dim, a.G, prm, DeviceMeta{}, num_seqs, s);
+    if (step) {
+      for (size_t c = 0; c < step->chunks.size() && e == hipSuccess; ++c)
+        e = dispatch_decode(dtype, head_dim, a.G, prm, step->chunks[c], step->ranks(c), s);
+    } else {
+      e = dispatch_decode(dtype, head_dim, a.G, prm, DeviceMeta{}, num_seqs, s);
+    }
     if (e != hipSuccess) return fail(PKV_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   }
   if (!merge || a.max_parts <= 1) return ok();
-  int32_t merge_rows = num_seqs;
   if (step) {
-    // the step's lengths are known here: the merge covers the ranks of the
-    // work order up to the last sequence that spans two partitions (the
+    // the step's lengths are known here: in each launch the merge covers
+    // the ranks up to the last sequence that spans two partitions (the
     // order is longest first, so these are the leading ranks); when every
     // sequence fits one partition the partition kernel wrote the final
     // rows and no merge runs
-    merge_rows = 0;
-    for (int32_t i = 0; i < num_seqs; ++i)
-      if (step->lens[step->order[i]] > a.part) merge_rows = i + 1;
-    if (merge_rows == 0) return ok();
+    for (size_t c = 0; c < step->chunks.size() && e == hipSuccess; ++c) {
+      const int32_t rows = step->rows_above(c, a.part);
+      if (rows > 0) e = launch_merge(prm, step->chunks[c], rows, num_heads, head_dim, s);
+    }
+  } else {
+    e = launch_merge(prm, DeviceMeta{}, num_seqs, num_heads, head_dim, s);
   }
-  e = step ? launch_merge(prm, *step, merge_rows, num_heads, head_dim, s)
-           : launch_merge(prm, DeviceMeta{}, num_seqs, num_heads, head_dim, s);
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "decode merge launch: %s", hipGetErrorString(e));
   return ok();
 }
 
-// Packs a step's host metadata (checked against the kernel-argument limits).
-int32_t pack_step(const int32_t* context_lens, const int32_t* changes, int32_t num_changes,
-                  int32_t num_seqs, int32_t num_kv_heads, int32_t max_blocks_per_seq,
-                  StepMeta* m) {
-  if (num_seqs > kStepMaxSeqs)
-    return fail(PKV_ERR_UNSUPPORTED, "step calls take at most %d sequences (got %d)",
-                kStepMaxSeqs, num_seqs);
-  if (num_changes < 0 || num_changes > kStepMaxChanges)
-    return fail(PKV_ERR_UNSUPPORTED, "step calls take at most %d table changes (got %d)",
-                kStepMaxChanges, num_changes);
+// Makes a step's launch metadata from its host lengths and table changes:
+// the work order over the whole batch, cut into launches of kStepRanks
+// ranks, each carrying its ranks' lengths and the changes of their rows
+// (at most kStepMaxChanges per launch).
+int32_t make_step_plan(const int32_t* context_lens, const int32_t* changes,
+                       int32_t num_changes, int32_t num_seqs, int32_t num_kv_heads,
+                       int32_t max_blocks_per_seq, StepPlan* plan) {
+  if (num_seqs > 65535)
+    return fail(PKV_ERR_UNSUPPORTED, "at most 65535 sequences per call (got %d)", num_seqs);
+  if (num_changes < 0) return fail(PKV_ERR_INVALID, "negative num_changes");
   if (num_seqs > 0 && !context_lens) return fail(PKV_ERR_INVALID, "context_lens is NULL");
   if (num_changes > 0 && !changes) return fail(PKV_ERR_INVALID, "changes is NULL");
-  for (int32_t i = 0; i < num_seqs; ++i) m->lens[i] = context_lens[i];
+  plan->host_lens = context_lens;
   // Longest first (stable), so long partitions start first; then, within
   // each round of R = 256 / num_kv_heads sequences -- the sequences whose
   // workgroups one pass of the dispatcher spreads over all 256 CUs -- every
@@ -1190,27 +1232,40 @@ int32_t pack_step(const int32_t* context_lens, const int32_t* changes, int32_t n
   // sequence get the next round's shortest and the CUs' loads even out
   // when the whole grid is resident at once (7B-shaped batch: partition
   // kernel 1% faster than plain longest-first).
-  int32_t idx[kStepMaxSeqs];
+  std::vector<int32_t> idx(num_seqs), order(num_seqs), rank_of(num_seqs);
   for (int32_t i = 0; i < num_seqs; ++i) idx[i] = i;
-  std::stable_sort(idx, idx + num_seqs,
+  std::stable_sort(idx.begin(), idx.end(),
                    [&](int32_t a, int32_t b) { return context_lens[a] > context_lens[b]; });
   const int32_t R = std::max(1, 256 / std::max(1, num_kv_heads));
   for (int32_t i = 0; i < num_seqs; ++i) {
     const int32_t k = i / R, j = i % R;
     int32_t src = k % 2 == 0 ? i : k * R + (R - 1 - j);
     if (src >= num_seqs) src = i;  // a short last round keeps its order
-    m->order[i] = static_cast<uint8_t>(idx[src]);
+    order[i] = idx[src];
+    rank_of[idx[src]] = i;
+  }
+  const int32_t nchunks = (num_seqs + kStepRanks - 1) / kStepRanks;
+  plan->num_seqs = num_seqs;
+  plan->chunks.assign(nchunks, StepMeta{});
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    StepMeta& m = plan->chunks[i / kStepRanks];
+    m.lens[i % kStepRanks] = context_lens[order[i]];
+    m.seq[i % kStepRanks] = static_cast<uint16_t>(order[i]);
   }
   for (int32_t i = 0; i < num_changes; ++i) {
-    const int32_t row = changes[3 * i], idx = changes[3 * i + 1];
-    if (row < 0 || row >= num_seqs || idx < 0 || idx >= max_blocks_per_seq ||
-        idx >= (1 << 23))
+    const int32_t row = changes[3 * i], blk = changes[3 * i + 1];
+    if (row < 0 || row >= num_seqs || blk < 0 || blk >= max_blocks_per_seq || blk >= (1 << 23))
       return fail(PKV_ERR_INVALID, "table change %d (row %d, index %d) out of range", i, row,
-                  idx);
-    m->change_key[i] = (idx << 8) | row;
-    m->change_block[i] = changes[3 * i + 2];
+                  blk);
+    StepMeta& m = plan->chunks[rank_of[row] / kStepRanks];
+    if (m.num_changes == kStepMaxChanges)
+      return fail(PKV_ERR_UNSUPPORTED,
+                  "step calls take at most %d table changes per %d sequences of the work order",
+                  kStepMaxChanges, kStepRanks);
+    m.change_key[m.num_changes] = (blk << 8) | (rank_of[row] % kStepRanks);
+    m.change_block[m.num_changes] = changes[3 * i + 2];
+    ++m.num_changes;
   }
-  m->num_changes = num_changes;
   return PKV_OK;
 }
 
@@ -1296,14 +1351,14 @@ int32_t step_call(const void* query, const void* key, const void* value, void* k
                   int32_t max_context_len, float scale, int32_t partition_size, float* out,
                   void* workspace, size_t workspace_bytes_given, int32_t dtype, void* stream,
                   bool partials, bool merge) {
-  StepMeta m;
-  int32_t st = pack_step(context_lens, changes, num_changes, num_seqs, num_kv_heads,
-                         max_blocks_per_seq, &m);
+  StepPlan plan;
+  int32_t st = make_step_plan(context_lens, changes, num_changes, num_seqs, num_kv_heads,
+                              max_blocks_per_seq, &plan);
   if (st != PKV_OK) return st;
   return run_decode(query, key, value, key_cache, value_cache, block_tables, nullptr, num_seqs,
                     num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                     num_blocks, max_context_len, scale, partition_size, out, workspace,
-                    workspace_bytes_given, dtype, stream, partials, merge, &m);
+                    workspace_bytes_given, dtype, stream, partials, merge, &plan);
 }
 }  // namespace
 
@@ -1340,14 +1395,14 @@ extern "C" int32_t pkv_paged_attention_decode_step_merge(
     int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq, int32_t max_context_len,
     int32_t partition_size, float* out, void* workspace, size_t workspace_bytes_given,
     void* stream) {
-  StepMeta m;
-  int32_t st = pack_step(context_lens, nullptr, 0, num_seqs, num_kv_heads, max_blocks_per_seq,
-                         &m);
+  StepPlan plan;
+  int32_t st = make_step_plan(context_lens, nullptr, 0, num_seqs, num_kv_heads,
+                              max_blocks_per_seq, &plan);
   if (st != PKV_OK) return st;
   return run_decode(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, num_seqs,
                     num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, 1,
                     max_context_len, 1.0f, partition_size, out, workspace,
-                    workspace_bytes_given, PKV_F32, stream, false, true, &m);
+                    workspace_bytes_given, PKV_F32, stream, false, true, &plan);
 }
 
 namespace {
@@ -1462,7 +1517,8 @@ int32_t shared_prefix_call(const void* query, const void* key_new, const void* v
                            int32_t num_blocks, int32_t max_context_len, int32_t prefix_len,
                            float scale, int32_t partition_size, float* out, void* workspace,
                            size_t workspace_bytes_given, int32_t dtype, void* stream,
-                           const StepMeta* step) {
+                           const StepPlan* step, const int32_t* changes = nullptr,
+                           int32_t num_changes = 0) {
   const bool shared_blocks = (dtype & PKV_DECODE_SHARED_BLOCKS) != 0;
   dtype &= ~int32_t(PKV_DECODE_SHARED_BLOCKS);
   if (dtype != PKV_BF16 && dtype != PKV_F16) {
@@ -1492,6 +1548,23 @@ int32_t shared_prefix_call(const void* query, const void* key_new, const void* v
   if (st != PKV_OK) return st;
   if (int64_t(prefix_len) > int64_t(max_blocks_per_seq) * block_size)
     return fail(PKV_ERR_INVALID, "prefix_len %d exceeds the block table's capacity", prefix_len);
+  if (step) {
+    // The step form stores each new row past the prefix and persists table
+    // changes from the suffix kernel: a new row inside the prefix, or a
+    // change to a prefix entry or to a row with no suffix token, would
+    // break the sharing or never reach the device table.
+    for (int32_t i = 0; i < num_seqs; ++i)
+      if (key_new && step->host_lens[i] <= prefix_len)
+        return fail(PKV_ERR_INVALID,
+                    "sequence %d: length %d leaves no suffix position for its new row", i,
+                    step->host_lens[i]);
+    for (int32_t i = 0; i < num_changes; ++i) {
+      const int32_t row = changes[3 * i], blk = changes[3 * i + 1];
+      if (int64_t(blk) * block_size < prefix_len || step->host_lens[row] <= prefix_len)
+        return fail(PKV_ERR_INVALID,
+                    "table change %d (row %d, index %d) touches the shared prefix", i, row, blk);
+    }
+  }
   if (num_seqs == 0) return ok();
   if (!query || !key_cache || !value_cache || !block_tables || (!step && !context_lens) || !out)
     return fail(PKV_ERR_INVALID, "NULL pointer argument");
@@ -1536,20 +1609,29 @@ int32_t shared_prefix_call(const void* query, const void* key_new, const void* v
   prm.num_blocks = num_blocks;
   prm.max_ctx = max_context_len;
   prm.part = part;
-  prm.max_parts = slots;
+  prm.max_parts = slots;                         // workspace slots per row
+  prm.grid_parts = std::max(1, slots - splits);  // suffix partitions
   prm.scale_log2 = scale * kLog2e;
   prm.v_scale = 1.0f;
   prm.shared_blocks = shared_blocks ? 1 : 0;
   prm.start = prefix_len;
   prm.slot_base = splits;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  e = step ? dispatch_decode(dtype, head_dim, G, prm, *step, num_seqs, s)
-           : dispatch_decode(dtype, head_dim, G, prm, DeviceMeta{}, num_seqs, s);
+  if (step) {
+    for (size_t c = 0; c < step->chunks.size() && e == hipSuccess; ++c)
+      e = dispatch_decode(dtype, head_dim, G, prm, step->chunks[c], step->ranks(c), s);
+  } else {
+    e = dispatch_decode(dtype, head_dim, G, prm, DeviceMeta{}, num_seqs, s);
+  }
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
 
   // 3. log-sum-exp merge of the prefix and suffix partials (every row)
-  e = step ? launch_merge(prm, *step, num_seqs, num_heads, head_dim, s)
-           : launch_merge(prm, DeviceMeta{}, num_seqs, num_heads, head_dim, s);
+  if (step) {
+    for (size_t c = 0; c < step->chunks.size() && e == hipSuccess; ++c)
+      e = launch_merge(prm, step->chunks[c], step->ranks(c), num_heads, head_dim, s);
+  } else {
+    e = launch_merge(prm, DeviceMeta{}, num_seqs, num_heads, head_dim, s);
+  }
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "decode merge launch: %s", hipGetErrorString(e));
   return ok();
 }
@@ -1577,13 +1659,13 @@ extern "C" int32_t pkv_paged_attention_decode_shared_prefix_step(
     int32_t num_blocks, int32_t max_context_len, int32_t prefix_len, float scale,
     int32_t partition_size, float* out, void* workspace, size_t workspace_bytes_given,
     int32_t dtype, void* stream) {
-  StepMeta m;
-  int32_t st = pack_step(context_lens, changes, num_changes, num_seqs, num_kv_heads,
-                         max_blocks_per_seq, &m);
+  StepPlan plan;
+  int32_t st = make_step_plan(context_lens, changes, num_changes, num_seqs, num_kv_heads,
+                              max_blocks_per_seq, &plan);
   if (st != PKV_OK) return st;
   return shared_prefix_call(query, key, value, key_cache, value_cache, block_tables, nullptr,
                             num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                             max_blocks_per_seq, num_blocks, max_context_len, prefix_len, scale,
                             partition_size, out, workspace, workspace_bytes_given, dtype, stream,
-                            &m);
+                            &plan, changes, num_changes);
 }

@@ -195,3 +195,45 @@ def logical_kv_fp8(w, segments, k_scale, v_scale):
     k, v = logical_kv(w, segments)
     return (fp8.dequantize(fp8.quantize(k, k_scale), k_scale),
             fp8.dequantize(fp8.quantize(v, v_scale), v_scale))
+
+
+# ---------------------------------------------------------------------------
+# Full-size coverage: the oracle over every sequence of a batch
+# ---------------------------------------------------------------------------
+
+def host_threads():
+    """Worker threads for the oracle on the host: the cores this process may
+    use, at most 16 (a GPU machine's share of its host)."""
+    import os
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+class LogicalKV:
+    """Float64 logical K/V of the sequences of a schedule, drawn again from
+    the generator; segments shared by several sequences (a forked prefix)
+    are drawn once and kept."""
+
+    def __init__(self, w, ops):
+        self.w = w
+        self.segs = logical_segments(ops)
+        count = {}
+        for segs in self.segs.values():
+            for s in segs:
+                count[s] = count.get(s, 0) + 1
+        self.shared = {s: logical_kv(w, [s]) for s, c in count.items() if c > 1}
+
+    def get(self, seq):
+        parts = [self.shared[s] if s in self.shared else logical_kv(self.w, [s])
+                 for s in self.segs[seq]]
+        shape = (0, self.w.num_kv_heads, self.w.head_dim)
+        if not parts:
+            return np.zeros(shape), np.zeros(shape)
+        return (np.concatenate([k for k, _ in parts]), np.concatenate([v for _, v in parts]))
+
+
+def parallel_map(fn, items):
+    """fn over items on host threads (numpy's generator fills, BLAS and
+    torch's casts run without the interpreter lock); results in order."""
+    import concurrent.futures as cf
+    with cf.ThreadPoolExecutor(host_threads()) as ex:
+        return list(ex.map(fn, items))

@@ -3,8 +3,8 @@
 Small cases run the whole oracle path (reference allocator, oracle append,
 oracle paged decode over a NaN-poisoned pool) and compare every output
 element.  Full-size workloads, in the launch configuration bench.py times,
-compare sampled sequences against oracle attention over the sequence's
-logical K/V drawn again from the generator.  Tolerances: 1e-5 max-abs for
+compare every sequence and head against oracle attention over the
+sequence's logical K/V drawn again from the generator.  Tolerances: 1e-5 max-abs for
 float32 caches, 2e-3 for float16/bfloat16 caches (float32 accumulation).
 """
 
@@ -16,8 +16,8 @@ import torch
 
 import paged_kv_cache_420_amd as pkv
 import workloads
-from cases import (DEV, TOL, GpuState, OracleState, decode_queries, log, logical_kv,
-                   logical_segments, max_abs_err)
+from cases import (DEV, TOL, GpuState, LogicalKV, OracleState, decode_queries, log,
+                   logical_kv, logical_segments, max_abs_err, parallel_map)
 from oracle import dense_attention, paged_decode
 
 pytestmark = pytest.mark.gpu
@@ -191,7 +191,15 @@ FULL = ["tiny_fp32", "llama7b_bf16", "llama13b_fp16", "gqa_bf16", "shared_prefix
 
 
 @pytest.mark.parametrize("name", FULL)
-def test_full_size_sampled_against_oracle(name):
+def test_full_size_every_sequence_against_oracle(name):
+    """Each workload at full size over a NaN-poisoned pool: every sequence
+    and every head of the plain decode call, and of the second of two
+    steps of the step call in the launch configuration bench.py times
+    (batch append with table changes, each new K/V row stored by the
+    kernel, the library's partition size and the grid order that goes with
+    it, the shared-blocks hint when blocks are shared), against oracle
+    attention over the sequence's logical K/V drawn again from the
+    generator (paging leaves the result unchanged)."""
     w = workloads.get(name)
     if w.chunk:
         w = workloads.scaled(w, chunk=0)  # decode state; prefill is its own test
@@ -206,24 +214,8 @@ def test_full_size_sampled_against_oracle(name):
     rt, rl = ref.build_tables(p.seqs, th.shape[1])
     assert np.array_equal(np.array(rt, dtype=np.int32), th) and list(rl) == lh.tolist()
     got, q64 = run_decode(g, w)
-    segs = logical_segments(p.ops)
-    rng = np.random.default_rng(7)
-    pick = sorted(set(rng.choice(len(p.seqs), size=min(8, len(p.seqs)), replace=False).tolist())
-                  | {int(np.argmax(lh)), int(np.argmin(lh))})
-    worst = 0.0
-    for b in pick:
-        k, v = logical_kv(w, segs[p.seqs[b]])
-        want = dense_attention(q64[b][None], k, v, w.scale)[0]
-        worst = max(worst, max_abs_err(got[b], want))
-    log(name, "sampled max abs err", worst, "over", len(pick), "sequences")
-    assert worst <= TOL[w.dtype]
-    assert np.isfinite(got).all()
 
-    # Then the step path bench.py times, at the same size: batch append with
-    # table changes, the step call with each sequence's new K/V row stored
-    # by the kernel, the library's partition size (the grid order that goes
-    # with it) and the shared-blocks hint when blocks are shared.  Two
-    # steps; the second is checked on the same sampled sequences.
+    # the step path, two steps
     seqs = p.seqs
     nb = len(seqs)
     mb = th.shape[1] + 2
@@ -248,18 +240,24 @@ def test_full_size_sampled_against_oracle(name):
                                               partition_size=w.partition_size,
                                               shared_blocks=shared)
     torch.cuda.synchronize()
-    got = out.cpu().numpy()
-    q64 = workloads.as_f64(qt)
-    worst = 0.0
-    for b in pick:
-        k, v = logical_kv(w, segs[p.seqs[b]])
+    got_step = out.cpu().numpy()
+    q64_step = workloads.as_f64(qt)
+
+    lkv = LogicalKV(w, p.ops)
+
+    def errors(b):
+        k, v = lkv.get(seqs[b])
+        plain = dense_attention(q64[b][None], k, v, w.scale)[0]
         k = np.concatenate([k] + [x[b][None] for x in new_k])
         v = np.concatenate([v] + [x[b][None] for x in new_v])
-        want = dense_attention(q64[b][None], k, v, w.scale)[0]
-        worst = max(worst, max_abs_err(got[b], want))
-    log(name, "step path sampled max abs err", worst, "shared hint", shared)
-    assert worst <= TOL[w.dtype]
-    assert np.isfinite(got).all()
+        step = dense_attention(q64_step[b][None], k, v, w.scale)[0]
+        return max_abs_err(got[b], plain), max_abs_err(got_step[b], step)
+
+    errs = np.array(parallel_map(errors, range(nb)))
+    log(name, "every sequence and head:", nb, "sequences; max abs err plain",
+        errs[:, 0].max(), "step", errs[:, 1].max(), "shared hint", shared)
+    assert errs[:, 0].max() <= TOL[w.dtype]
+    assert errs[:, 1].max() <= TOL[w.dtype]
 
 
 # ---------------------------------------------------------------------------
@@ -515,12 +513,143 @@ def test_step_call_limits():
     q = torch.zeros((300, 4, 128), dtype=torch.bfloat16, device=DEV)
     t = torch.zeros((300, 2), dtype=torch.int32, device=DEV)
     lens = np.ones(300, dtype=np.int32)
+    # 257 changes for rows served by the first launch (ranks 0..255)
+    many = np.array([[r, 0, 1] for r in range(200)] + [[r, 1, 1] for r in range(57)],
+                    dtype=np.int32)
     with pytest.raises(pkv.Unsupported):
-        pkv.paged_attention_decode_step(q, None, None, kc, kc, t, lens, np.zeros((0, 3)),
-                                        w.scale, 1)
+        pkv.paged_attention_decode_step(q, None, None, kc, kc, t, lens, many, w.scale, 1)
     with pytest.raises(pkv.InvalidArgument):  # change row outside the batch
         pkv.paged_attention_decode_step(q[:2].contiguous(), None, None, kc, kc, t[:2].contiguous(),
                                         lens[:2], np.array([[5, 0, 1]]), w.scale, 1)
+
+
+def test_step_call_past_256_sequences():
+    """512 sequences: the step call runs as launches of 256 ranks of the
+    longest-first order, each with its ranks' lengths and changes.  Over
+    three steps it equals the fused-append decode on freshly uploaded
+    tables bit for bit (outputs, caches, device table), and the last
+    step's every row meets the oracle."""
+    w = workloads.scaled(workloads.get("llama7b_bf16"), num_seqs=512, num_heads=4,
+                         num_kv_heads=2, lens="uniform:1,700", seed=4610)
+    p = workloads.plan(w)
+    a, b = GpuState(w, p), GpuState(w, p)
+    seqs = p.seqs
+    nb, steps, part = len(seqs), 3, 256
+    mb = max(len(a.alloc.block_table(s)) for s in seqs) + 2
+    th, _ = b.alloc.build_block_tables(seqs, mb)
+    dev_tables = torch.from_numpy(th.copy()).to(DEV)
+    ones = np.ones(nb, dtype=np.int32)
+    new_k, new_v = [], []
+    for i in range(steps):
+        k, v = workloads.kv_rows(w, len(p.ops) + i, nb)
+        kt, vt = workloads.to_dtype(k, w.dtype), workloads.to_dtype(v, w.dtype)
+        new_k.append(workloads.as_f64(kt))
+        new_v.append(workloads.as_f64(vt))
+        kt, vt = kt.to(DEV), vt.to(DEV)
+        qt = workloads.to_dtype(workloads.normal([w.seed, 9, i], (nb, w.num_heads, w.head_dim),
+                                                 w.std), w.dtype)
+        a.alloc.append_batch(seqs, ones)
+        _, _, lens, changes = b.alloc.append_batch_changes(seqs, ones)
+        ta, la, _, lh = a.tables(seqs)
+        ta = torch.nn.functional.pad(ta, (0, mb - ta.shape[1]), value=-1).contiguous()
+        mc = int(lh.max())
+        want = pkv.paged_attention_decode_append(qt.to(DEV), kt, vt, a.kc, a.vc, ta, la, w.scale,
+                                                 mc, partition_size=part)
+        got = pkv.paged_attention_decode_step(qt.to(DEV), kt, vt, b.kc, b.vc, dev_tables, lens,
+                                              changes, w.scale, mc, partition_size=part)
+        torch.cuda.synchronize()
+        assert torch.equal(got, want), f"step {i}"
+    assert torch.equal(a.kc.view(torch.uint8), b.kc.view(torch.uint8))
+    assert torch.equal(a.vc.view(torch.uint8), b.vc.view(torch.uint8))
+    th, _ = b.alloc.build_block_tables(seqs, mb)
+    assert np.array_equal(dev_tables.cpu().numpy(), th)
+    got = got.cpu().numpy()
+    q64 = workloads.as_f64(qt)
+    lkv = LogicalKV(w, p.ops)
+
+    def err(r):
+        k, v = lkv.get(seqs[r])
+        k = np.concatenate([k] + [x[r][None] for x in new_k])
+        v = np.concatenate([v] + [x[r][None] for x in new_v])
+        return max_abs_err(got[r], dense_attention(q64[r][None], k, v, w.scale)[0])
+
+    worst = max(parallel_map(err, range(nb)))
+    log("512-sequence step, every row: max abs err", worst)
+    assert worst <= TOL[w.dtype]
+
+
+def test_shared_prefix_step_past_256_sequences():
+    """The shared-prefix step form over 300 sequences (two launches of the
+    suffix kernel and of the merge): bitwise the append followed by the
+    plain shared-prefix call on freshly uploaded tables."""
+    w = workloads.scaled(workloads.get("shared_prefix_bf16"), num_seqs=300, num_heads=4,
+                         num_kv_heads=2, prefix=48, lens="uniform:1,400", chunk=0, seed=4611)
+    p = workloads.plan(w)
+    a, b = GpuState(w, p), GpuState(w, p)
+    seqs = p.seqs
+    nb, steps = len(seqs), 2
+    mb = max(len(a.alloc.block_table(s)) for s in seqs) + 2
+    th, _ = b.alloc.build_block_tables(seqs, mb)
+    dev_tables = torch.from_numpy(th.copy()).to(DEV)
+    ones = np.ones(nb, dtype=np.int32)
+    for i in range(steps):
+        k, v = workloads.kv_rows(w, len(p.ops) + i, nb)
+        kt = workloads.to_dtype(k, w.dtype).to(DEV)
+        vt = workloads.to_dtype(v, w.dtype).to(DEV)
+        q = workloads.to_dtype(workloads.normal([w.seed, 17, i], (nb, w.num_heads, w.head_dim),
+                                                w.std), w.dtype).to(DEV)
+        slots, pa = a.alloc.append_batch(seqs, ones)
+        _, pb, lens, changes = b.alloc.append_batch_changes(seqs, ones)
+        assert not pa and not pb
+        pkv.paged_kv_append(kt, vt, a.kc, a.vc, torch.from_numpy(slots).to(DEV))
+        ta, la, _, lh = a.tables(seqs)
+        ta = torch.nn.functional.pad(ta, (0, mb - ta.shape[1]), value=-1).contiguous()
+        mc = int(lh.max())
+        want = pkv.paged_attention_decode_shared_prefix(q, a.kc, a.vc, ta, la, w.prefix, w.scale,
+                                                        mc, partition_size=128)
+        got = pkv.paged_attention_decode_shared_prefix_step(q, kt, vt, b.kc, b.vc, dev_tables,
+                                                            lens, changes, w.prefix, w.scale,
+                                                            mc, partition_size=128)
+        torch.cuda.synchronize()
+        assert torch.equal(got, want), f"step {i}"
+    th, _ = b.alloc.build_block_tables(seqs, mb)
+    assert np.array_equal(dev_tables.cpu().numpy(), th)
+
+
+def test_launcher_step_rejects_bad_host_arrays():
+    """DecodeLauncher's step stages read host lengths and changes through
+    raw pointers: wrong dtype, shape or count is refused before the call."""
+    w, part = APPEND["gqa8_part128"]
+    p = workloads.plan(w)
+    g = GpuState(w, p)
+    seqs = p.seqs
+    nb = len(seqs)
+    tables, lens, _, lh = g.tables()
+    mc = int(lh.max())
+    need = pkv.paged_attention_decode_workspace_size(nb, w.num_heads, w.num_kv_heads,
+                                                     w.head_dim, mc, part)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=DEV)
+    out = torch.empty((nb, w.num_heads, w.head_dim), dtype=torch.float32, device=DEV)
+    launch = pkv.DecodeLauncher(g.kc, g.vc, w.num_heads, nb, tables.shape[1], mc, part, out, ws)
+    q, _ = decode_queries(w, seqs)
+    q = q.to(DEV)
+    good_l = lh.astype(np.int32).copy()
+    good_c = np.zeros((1, 3), dtype=np.int32)
+    for bad_l in (lh.astype(np.int64), good_l[:-1].copy(), good_l.tolist()):
+        with pytest.raises(pkv.InvalidArgument):
+            launch.step_partials(q, tables, bad_l, good_c, 0, mc, w.scale)
+        with pytest.raises(pkv.InvalidArgument):
+            launch.step_merge(bad_l, mc)
+    for bad_c, n in ((good_c.astype(np.int64), 0), (np.zeros((2, 2), dtype=np.int32), 0),
+                     (good_c, 2), (good_c, -1)):
+        with pytest.raises(pkv.InvalidArgument):
+            launch.step_partials(q, tables, good_l, bad_c, n, mc, w.scale)
+    launch.step_partials(q, tables, good_l, good_c, 0, mc, w.scale)
+    launch.step_merge(good_l, mc)
+    torch.cuda.synchronize()
+    want = pkv.paged_attention_decode(q, g.kc, g.vc, tables, lens, w.scale, mc,
+                                      partition_size=part)
+    assert torch.equal(out, want)
 
 
 HINT = ["tiny_fp32_long", "llama13b_small", "gqa_small", "gqa4_d64_bs8", "shared_prefix_small"]
@@ -750,30 +879,134 @@ def test_shared_prefix_decode_rows_below_the_prefix_are_nan():
                                                  w.prefix - 8, w.scale, mc)
 
 
-def test_shared_prefix_decode_full_size_sampled():
+def test_shared_prefix_decode_full_size_every_sequence():
     """The shared-prefix batch at full size (256 sequences, 1024-token
-    prefix): sampled sequences against oracle attention over the logical
-    K/V drawn again from the generator."""
+    prefix) over a NaN-poisoned pool: every sequence and head of the plain
+    shared-prefix call, and of the second of two steps of its step form as
+    bench.py times it (new rows stored by the suffix kernel, table changes
+    by value), against oracle attention over the logical K/V drawn again
+    from the generator."""
     w = workloads.scaled(workloads.get("shared_prefix_bf16"), chunk=0)
     p = workloads.plan(w)
     g = GpuState(w, p)
-    tables, lens, _, lh = g.tables()
+    tables, lens, th, lh = g.tables()
     q, q64 = decode_queries(w, p.seqs)
     mc = int(lh.max())
     got = pkv.paged_attention_decode_shared_prefix(q.to(DEV), g.kc, g.vc, tables, lens, w.prefix,
                                                    w.scale, mc).cpu().numpy()
-    segs = logical_segments(p.ops)
-    rng = np.random.default_rng(11)
-    pick = sorted(set(rng.choice(len(p.seqs), size=8, replace=False).tolist())
-                  | {int(np.argmax(lh)), int(np.argmin(lh))})
-    worst = 0.0
-    for b in pick:
-        k, v = logical_kv(w, segs[p.seqs[b]])
-        want = dense_attention(q64[b][None], k, v, w.scale)[0]
-        worst = max(worst, max_abs_err(got[b], want))
-    log("shared-prefix decode, full size: sampled max abs err", worst)
-    assert worst <= TOL[w.dtype]
-    assert np.isfinite(got).all()
+    seqs = p.seqs
+    nb = len(seqs)
+    steps = 2
+    mb = th.shape[1] + 2
+    t0, _ = g.alloc.build_block_tables(seqs, mb)
+    dev_tables = torch.from_numpy(t0.copy()).to(DEV)
+    max_len = mc + steps
+    ws = torch.empty(pkv.paged_attention_decode_shared_prefix_workspace_size(
+        nb, w.num_heads, w.num_kv_heads, w.head_dim, w.block_size, max_len, w.prefix),
+        dtype=torch.uint8, device=DEV)
+    out = torch.empty((nb, w.num_heads, w.head_dim), dtype=torch.float32, device=DEV)
+    ones = np.ones(nb, dtype=np.int32)
+    new_k, new_v = [], []
+    for i in range(steps):
+        k, v = workloads.kv_rows(w, len(p.ops) + i, nb)
+        kt, vt = workloads.to_dtype(k, w.dtype), workloads.to_dtype(v, w.dtype)
+        new_k.append(workloads.as_f64(kt))
+        new_v.append(workloads.as_f64(vt))
+        qt = workloads.to_dtype(workloads.normal([w.seed, 19, i], (nb, w.num_heads, w.head_dim),
+                                                 w.std), w.dtype)
+        _, pairs, step_lens, changes = g.alloc.append_batch_changes(seqs, ones)
+        assert not pairs
+        pkv.paged_attention_decode_shared_prefix_step(
+            qt.to(DEV), kt.to(DEV), vt.to(DEV), g.kc, g.vc, dev_tables, step_lens, changes,
+            w.prefix, w.scale, int(step_lens.max()), out=out, workspace=ws)
+    torch.cuda.synchronize()
+    got_step = out.cpu().numpy()
+    q64_step = workloads.as_f64(qt)
+    lkv = LogicalKV(w, p.ops)
+
+    def errors(b):
+        k, v = lkv.get(seqs[b])
+        plain = dense_attention(q64[b][None], k, v, w.scale)[0]
+        k = np.concatenate([k] + [x[b][None] for x in new_k])
+        v = np.concatenate([v] + [x[b][None] for x in new_v])
+        step = dense_attention(q64_step[b][None], k, v, w.scale)[0]
+        return max_abs_err(got[b], plain), max_abs_err(got_step[b], step)
+
+    errs = np.array(parallel_map(errors, range(nb)))
+    log("shared-prefix decode, full size, every sequence and head: max abs err plain",
+        errs[:, 0].max(), "step", errs[:, 1].max())
+    assert errs[:, 0].max() <= TOL[w.dtype]
+    assert errs[:, 1].max() <= TOL[w.dtype]
+
+
+def test_shared_prefix_table_mismatch_gives_nan_rows():
+    """The prefix is read through row 0 of the table; a sequence whose own
+    table names other blocks for it gets a NaN row (plain and step form),
+    whether or not it has suffix tokens; the other rows are unchanged."""
+    w = SHARED["bf16_mha_bs16"]
+    p = workloads.plan(w)
+    g = GpuState(w, p)
+    tables, lens, th, lh = g.tables()
+    q, _ = decode_queries(w, p.seqs)
+    q = q.to(DEV)
+    mc = int(lh.max())
+    want = pkv.paged_attention_decode_shared_prefix(q, g.kc, g.vc, tables, lens, w.prefix,
+                                                    w.scale, mc)
+    # rows other than 0 (row 0's table is the one the prefix is read through)
+    long_ = 1 + int(np.argmax(lh[1:]))
+    short = 1 if long_ != 1 else 2
+    bad = tables.clone()
+    bad[long_, 1] = bad[long_, 2]          # a prefix entry of a row with suffix tokens
+    bad_lens = lens.clone()
+    bad_lens[short] = w.prefix             # no suffix token: only the prefix partial
+    bad[short, 0] = int(th[long_, -1])
+    got = pkv.paged_attention_decode_shared_prefix(q, g.kc, g.vc, bad, bad_lens, w.prefix,
+                                                   w.scale, mc)
+    torch.cuda.synchronize()
+    got, want = got.cpu().numpy(), want.cpu().numpy()
+    assert np.isnan(got[long_]).all() and np.isnan(got[short]).all()
+    rest = [i for i in range(len(p.seqs)) if i not in (short, long_)]
+    assert np.array_equal(got[rest], want[rest])
+    # step form (no new rows; the same device table)
+    lens_h = lh.astype(np.int32).copy()
+    lens_h[short] = w.prefix
+    got = pkv.paged_attention_decode_shared_prefix_step(
+        q, None, None, g.kc, g.vc, bad, lens_h, np.zeros((0, 3), dtype=np.int32), w.prefix,
+        w.scale, mc).cpu().numpy()
+    assert np.isnan(got[long_]).all() and np.isnan(got[short]).all()
+    assert np.array_equal(got[rest], want[rest])
+
+
+def test_shared_prefix_step_rejects_prefix_writes():
+    w = SHARED["bf16_mha_bs16"]
+    p = workloads.plan(w)
+    g = GpuState(w, p)
+    tables, lens, th, lh = g.tables()
+    q, _ = decode_queries(w, p.seqs)
+    q = q.to(DEV)
+    nb = len(p.seqs)
+    kv = torch.zeros((nb, w.num_kv_heads, w.head_dim), dtype=w.dtype, device=DEV)
+    lens_h = lh.astype(np.int32).copy()
+    no_changes = np.zeros((0, 3), dtype=np.int32)
+    mc = int(lh.max())
+    short = lens_h.copy()
+    short[0] = w.prefix                    # the new row would land inside the prefix
+    with pytest.raises(pkv.InvalidArgument):
+        pkv.paged_attention_decode_shared_prefix_step(q, kv, kv, g.kc, g.vc, tables, short,
+                                                      no_changes, w.prefix, w.scale, mc)
+    with pytest.raises(pkv.InvalidArgument):  # a change to a prefix entry
+        pkv.paged_attention_decode_shared_prefix_step(
+            q, None, None, g.kc, g.vc, tables, lens_h, np.array([[1, 0, 3]], dtype=np.int32),
+            w.prefix, w.scale, mc)
+    with pytest.raises(pkv.InvalidArgument):  # out of the wrong shape
+        pkv.paged_attention_decode_shared_prefix(q, g.kc, g.vc, tables, lens, w.prefix, w.scale,
+                                                 mc, out=torch.empty((nb - 1, w.num_heads,
+                                                                      w.head_dim),
+                                                                     device=DEV))
+    with pytest.raises(pkv.InvalidArgument):
+        pkv.paged_attention_decode_shared_prefix_step(
+            q, None, None, g.kc, g.vc, tables, lens_h, no_changes, w.prefix, w.scale, mc,
+            out=torch.empty((nb, w.num_heads + 1, w.head_dim), device=DEV))
 
 
 @pytest.mark.parametrize("part", [64, 1024])
