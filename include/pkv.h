@@ -614,6 +614,28 @@ int32_t pkv_paged_attention_decode_merge(
     int32_t partition_size, float* out, void* workspace,
     size_t workspace_bytes, void* stream);
 
+/* pkv_paged_attention_decode for callers that cannot allocate device memory
+ * or pass a workspace (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same kernels, with the split-K
+ * partials kept in a fixed array of 64 MiB that the library holds on every
+ * GPU it runs on until the process ends.  The call allocates nothing.
+ * Arguments as pkv_paged_attention_decode without the workspace; sizes
+ * whose partials (pkv_paged_attention_decode_workspace_size) exceed 64 MiB
+ * are rejected with PKV_ERR_BUFFER_TOO_SMALL before anything is enqueued.
+ * Every call on one GPU uses that GPU's array (left holding the last call's
+ * partials; no call needs it cleared): calls that overlap on one GPU --
+ * on concurrent streams, or from several host threads -- race and must be
+ * ordered by the caller.  The device is the stream's (the current device
+ * for the null stream); the array's address there is looked up on the
+ * first call on that device. */
+int32_t pkv_paged_attention_decode_noalloc(
+    const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, const int32_t* context_lens,
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+    int32_t num_blocks, int32_t max_context_len, float scale,
+    int32_t partition_size, float* out, int32_t dtype, void* stream);
+
 /* pkv_paged_attention_decode over an 8-bit (PKV_FP8_E4M3) cache written by
  * pkv_paged_kv_append_fp8 (KV-cache article §5: paging combined with
  * quantisation).  Same arguments, layout, partitions, workspace and error

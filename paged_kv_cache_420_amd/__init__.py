@@ -131,6 +131,9 @@ _SIGNATURES = {
                                                    _I32, ctypes.c_float, _I32, _P, _P, ctypes.c_size_t, _I32, _P]),
     "pkv_paged_attention_decode_merge": (_I32, [_P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P,
                                                 ctypes.c_size_t, _P]),
+    "pkv_paged_attention_decode_noalloc": (_I32, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
+                                                  _I32, _I32, _I32, ctypes.c_float, _I32, _P, _I32,
+                                                  _P]),
     "pkv_paged_kv_append_fp8": (_I32, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
                                        ctypes.c_float, ctypes.c_float, _I32, _P]),
     "pkv_paged_attention_decode_fp8": (_I32, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
@@ -803,6 +806,31 @@ def _decode_append(fn, query, key, value, key_cache, value_cache, block_tables, 
               hkv, d, bs, block_tables.shape[1], nb, int(max_context_len), float(scale),
               int(partition_size), out.data_ptr(), ws_ptr, ws_bytes, _dtype_code(key_cache),
               _stream(query)))
+    return out
+
+
+def paged_attention_decode_noalloc(query, key_cache, value_cache, block_tables, context_lens,
+                                   scale, max_context_len, out, partition_size=0,
+                                   shared_blocks=False):
+    """paged_attention_decode with its split-K partials in the library's
+    fixed device array instead of a workspace (pkv_paged_attention_decode_noalloc):
+    the call allocates nothing, so ``out`` [B, Hq, D] float32 is required.
+    Calls on one GPU share the array and must not overlap."""
+    nb, hkv, bs, d = _cache_dims(key_cache, value_cache)
+    _dev(query, "query", dtype=key_cache.dtype, ndim=3)
+    _dev(block_tables, "block_tables", dtype=torch.int32, ndim=2)
+    _dev(context_lens, "context_lens", dtype=torch.int32, ndim=1)
+    b, hq, dq = query.shape
+    if dq != d or block_tables.shape[0] != b or context_lens.shape[0] != b:
+        raise InvalidArgument("query [B, Hq, D], block_tables [B, max_blocks], context_lens [B]")
+    _dev(out, "out", dtype=torch.float32, ndim=3)
+    if tuple(out.shape) != (b, hq, d):
+        raise InvalidArgument("out must be [B, Hq, D]")
+    _check(_lib.pkv_paged_attention_decode_noalloc(
+        query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(), block_tables.data_ptr(),
+        context_lens.data_ptr(), b, hq, hkv, d, bs, block_tables.shape[1], nb,
+        int(max_context_len), float(scale), int(partition_size), out.data_ptr(),
+        _decode_code(key_cache, shared_blocks), _stream(query)))
     return out
 
 

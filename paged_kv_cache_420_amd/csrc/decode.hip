@@ -39,6 +39,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <vector>
 
 #include "common.h"
@@ -1668,4 +1669,75 @@ extern "C" int32_t pkv_paged_attention_decode_shared_prefix_step(
                             max_blocks_per_seq, num_blocks, max_context_len, prefix_len, scale,
                             partition_size, out, workspace, workspace_bytes_given, dtype, stream,
                             &plan, changes, num_changes);
+}
+
+// ---- decode with no allocation at all: split-K partials in a fixed array --
+
+namespace {
+// The split-K partials of pkv_paged_attention_decode_noalloc.  Every GPU
+// the library runs on holds its own copy from the time the library's code
+// is loaded there until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in for the
+// device copy): the device address comes from hipGetSymbolAddress, per
+// device, below.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the device `stream` runs on, looked
+// up once per device with that device current.
+int32_t scratch_for_stream(hipStream_t stream, void** ptr) {
+  int dev = 0;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "stream device: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(PKV_ERR_UNSUPPORTED, "device %d beyond the %d this library serves", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int current = 0;
+    e = hipGetDevice(&current);
+    if (e == hipSuccess && current != dev) e = hipSetDevice(dev);
+    void* p = nullptr;
+    if (e == hipSuccess) e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (current != dev) {
+      const hipError_t back = hipSetDevice(current);
+      if (e == hipSuccess) e = back;
+    }
+    if (e != hipSuccess || !p)
+      return fail(PKV_ERR_HIP, "scratch address on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return PKV_OK;
+}
+}  // namespace
+
+extern "C" int32_t pkv_paged_attention_decode_noalloc(
+    const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t max_blocks_per_seq, int32_t num_blocks, int32_t max_context_len, float scale,
+    int32_t partition_size, float* out, int32_t dtype, void* stream) {
+  size_t need = 0;
+  int32_t st = pkv_paged_attention_decode_workspace_size(
+      num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, partition_size, &need);
+  if (st != PKV_OK) return st;
+  if (need > kScratchBytes)
+    return fail(PKV_ERR_BUFFER_TOO_SMALL,
+                "these sizes need %zu bytes of split-K partials, beyond the %zu bytes of the "
+                "library's fixed scratch array (use pkv_paged_attention_decode with a workspace)",
+                need, kScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    st = scratch_for_stream(static_cast<hipStream_t>(stream), &ws);
+    if (st != PKV_OK) return st;
+  }
+  return run_decode(query, nullptr, nullptr, key_cache, value_cache, block_tables, context_lens,
+                    num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                    num_blocks, max_context_len, scale, partition_size, out, ws,
+                    need > 0 ? kScratchBytes : 0, dtype, stream, true, true, nullptr);
 }
