@@ -24,10 +24,14 @@ With a shared prefix those logical bytes exceed what HBM delivers (the
 prefix is the same K/V for every sequence); the roofline then uses the
 unique bytes (prefix counted once).
 ``roofline`` reports the decode partition kernel alone (with a shared
-prefix: the three launches of the shared-prefix call), timed with HIP
-events on the stream it runs on (every fourth timed step, so the events'
-own cost stays out of the step time); its ``traffic`` comes from the committed
+prefix: the three launches of the shared-prefix call) on the cache state
+after the timed steps, 20 launches back to back between one pair of HIP
+events on the stream it runs on; its ``traffic`` comes from the committed
 rocprofv3 counter summary of the same kernel source, when there is one.
+``workloads`` carries the same figures for every other workload (20 steps
+after 5; their caches filled with values drawn on the device), and
+``stream_read`` the achievable HBM read rate: a plain read of 4 GiB with
+the decode kernel's load width and policy.
 ``cpu_baseline`` times the float64 CPU oracle on a small sample of the same
 workload (reported only; the host's CPU model and core count go into its
 ``sample``).  For the shared-prefix workload the line also carries
@@ -74,6 +78,8 @@ def parse():
                     help="split-K partition in tokens (default: the workload's, else automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (profiling runs)")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="time only --workload (no other workloads, no stream-read ceiling)")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the chunked-prefill leg of the shared-prefix workload")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -127,14 +133,46 @@ def setup(w, pkv, workloads, torch, dev):
     return p, kc, vc, alloc
 
 
-def gpu_run(args, w, torch, pkv, workloads):
+def fast_setup(w, pkv, workloads, torch, dev):
+    """The cache state of a timing-only leg: the workload's schedule through
+    the native allocator, with K/V values drawn on the device (torch's
+    generator, seeded) instead of the host generator the parity tests use."""
+    p = workloads.plan(w)
+    shape = (p.num_blocks, w.num_kv_heads, w.block_size, w.head_dim)
+    kc = torch.zeros(shape, dtype=w.dtype, device=dev)
+    vc = torch.zeros(shape, dtype=w.dtype, device=dev)
+    alloc = pkv.BlockAllocator(p.num_blocks, w.block_size, p.free_order)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed)
+
+    def on_copy(pairs):
+        src = torch.tensor([a for a, _ in pairs], dtype=torch.int32, device=dev)
+        dst = torch.tensor([b for _, b in pairs], dtype=torch.int32, device=dev)
+        pkv.copy_blocks(kc, vc, src, dst)
+
+    def on_append(i, seq, n, slots):
+        kv = (torch.randn((2, n, w.num_kv_heads, w.head_dim), generator=gen, device=dev)
+              * w.std).to(w.dtype)
+        pkv.paged_kv_append(kv[0], kv[1], kc, vc, torch.from_numpy(slots).to(dev))
+
+    workloads.run_schedule(p.ops, alloc, on_append, on_copy)
+    torch.cuda.synchronize()
+    return p, kc, vc, alloc
+
+
+def gpu_run(args, w, torch, pkv, workloads, steps=None, warmup=None, fast=False):
+    """``steps`` decode steps after ``warmup`` untimed ones (default: the
+    command line's), then the roofline kernel alone in a back-to-back loop
+    on the final cache state."""
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    steps = args.steps if steps is None else steps
+    warmup = args.warmup if warmup is None else warmup
     part_arg = w.partition_size if args.partition_size is None else args.partition_size
-    p, kc, vc, alloc = setup(w, pkv, workloads, torch, dev)
+    p, kc, vc, alloc = (fast_setup if fast else setup)(w, pkv, workloads, torch, dev)
     seqs = np.asarray(p.seqs, dtype=np.int64)
     b = len(seqs)
-    total_steps = args.warmup + args.steps
+    total_steps = warmup + steps
     max_len = int(max(alloc.seq_len(s) for s in p.seqs)) + total_steps
     mb = -(-max_len // w.block_size)
     part = pkv.paged_attention_decode_partition_size(b, w.num_kv_heads, w.block_size, max_len,
@@ -180,12 +218,6 @@ def gpu_run(args, w, torch, pkv, workloads):
         ws_sp = torch.empty(max(pkv.paged_attention_decode_shared_prefix_workspace_size(
             b, w.num_heads, w.num_kv_heads, w.head_dim, w.block_size, max_len, w.prefix), 16),
             dtype=torch.uint8, device=dev)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(total_steps)]
-    # HIP events bracket the kernels of every fourth timed step: each record
-    # is a packet on the stream that costs about 4 us, which recording on
-    # every step would add to the step time being measured
-    sampled = set(range(args.warmup, total_steps, 4))
     step_bytes = np.zeros(total_steps, dtype=np.float64)
     step_unique = np.zeros(total_steps, dtype=np.float64)
 
@@ -196,48 +228,96 @@ def gpu_run(args, w, torch, pkv, workloads):
             dst = torch.tensor([c for _, c in pairs], dtype=torch.int32).to(dev)
             pkv.copy_blocks(kc, vc, src, dst)
         mc = int(lens_h.max())
-        timed_here = i in sampled
-        if timed_here:
-            ev[i][0].record(stream)
         if w.prefix:                                                         # 4
             pkv.paged_attention_decode_shared_prefix_step(
                 q[i], k_new[i], v_new[i], kc, vc, tables_d, lens_h, changes_h[:n_changes],
                 w.prefix, w.scale, mc, out=out, workspace=ws_sp)
-            if timed_here:
-                ev[i][1].record(stream)
         else:
             launch.step_partials(q[i], tables_d, lens_h, changes_h, n_changes, mc, w.scale,  # 4
                                  k_new[i], v_new[i])
-            if timed_here:
-                ev[i][1].record(stream)
             launch.step_merge(lens_h, mc)
-        if timed_here:
-            ev[i][2].record(stream)
         step_bytes[i] = kv_bytes(w, lens_h)
         step_unique[i] = kv_bytes_unique(w, lens_h)
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.warmup, total_steps):
+    for i in range(warmup, total_steps):
         step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    timed = sorted(sampled)
-    kernel_ms = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in timed])
-    merge_ms = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in timed])
     if not torch.isfinite(out).all():
         raise RuntimeError("decode produced non-finite output")
-    res = dict(wall=wall, kernel_ms=kernel_ms, merge_ms=merge_ms, bytes=step_bytes[args.warmup:],
-               unique_bytes=step_unique[args.warmup:],
-               batch=b, part=part, shared=shared)
+
+    # The roofline kernel alone, on the final cache state: the step's
+    # partition kernel (no new rows, no table changes: the fused store of
+    # one row per sequence is left out) -- with a shared prefix, the whole
+    # shared-prefix call -- launched back to back between one pair of HIP
+    # events on its stream, so the events cost nothing per launch.  Then the
+    # merge alone the same way.
+    mc = int(lens_h.max())
+    no_changes = changes_h[:0]
+    if w.prefix:
+        def kernel():
+            pkv.paged_attention_decode_shared_prefix_step(
+                q[-1], None, None, kc, vc, tables_d, lens_h, no_changes, w.prefix, w.scale, mc,
+                out=out, workspace=ws_sp)
+        merge = None
+    else:
+        def kernel():
+            launch.step_partials(q[-1], tables_d, lens_h, changes_h, 0, mc, w.scale)
+
+        def merge():
+            launch.step_merge(lens_h, mc)
+    kernel_us = time_loop(torch, stream, kernel, 20) * 1e3
+    merge_us = time_loop(torch, stream, merge, 20) * 1e3 if merge else 0.0
+    res = dict(wall=wall, kernel_us=kernel_us, merge_us=merge_us,
+               kernel_bytes=float(kv_bytes(w, lens_h)),
+               kernel_unique_bytes=float(kv_bytes_unique(w, lens_h)),
+               bytes=step_bytes[warmup:], unique_bytes=step_unique[warmup:],
+               batch=b, part=part, shared=shared, steps=steps)
     if w.prefix:
         res["decode_shared_prefix"] = shared_prefix_decode_run(w, p, alloc, kc, vc, torch, pkv,
                                                                dev)
     if w.chunk and not args.no_prefill:
         res["prefill"] = prefill_run(w, p, alloc, kc, vc, torch, pkv, dev)
     return res
+
+
+def time_loop(torch, stream, fn, reps, warm=3):
+    """Mean milliseconds per call of ``fn`` over ``reps`` calls launched back
+    to back between one pair of HIP events on ``stream``."""
+    for _ in range(warm):
+        fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def stream_read_run(torch, pkv):
+    """The achievable HBM read rate: 4 GiB read once per launch with the
+    decode kernel's load width and policy (pkv_stream_read), mean of 10
+    back-to-back launches after 3."""
+    dev = torch.device("cuda:0")
+    nbytes = 4 << 30
+    buf = torch.ones(nbytes // 2, dtype=torch.bfloat16, device=dev)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    best = None
+    for wg in (2048, 4096, 8192):
+        ms = time_loop(torch, stream, lambda: pkv.stream_read(buf, wg, sink), 10)
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        if best is None or gbps > best["gbps"]:
+            best = {"bytes": nbytes, "workgroups": wg, "us": round(ms * 1e3, 2),
+                    "gbps": round(gbps, 1), "hbm_peak_frac": round(gbps / HBM_PEAK_GBPS, 4)}
+    del buf
+    torch.cuda.empty_cache()
+    return best
 
 
 def shared_prefix_decode_run(w, p, alloc, kc, vc, torch, pkv, dev):
@@ -757,22 +837,16 @@ def main():
         return
     w = workloads.get(args.workload)
     r = gpu_run(args, w, torch, pkv, workloads)
-    ms_step = r["wall"] / args.steps * 1e3
-    mean_bytes = float(r["bytes"].mean())
-    value = mean_bytes / (ms_step * 1e-3) / 1e9
-    kernel_ms = float(r["kernel_ms"].mean())
-    # roofline on the bytes HBM must deliver: a shared prefix counts once
-    unique_bytes = float(r["unique_bytes"].mean())
-    achieved = unique_bytes / (kernel_ms * 1e-3) / 1e9
+    leg = summarise(w, r)
     src = os.path.join(ROOT, "paged_kv_cache_420_amd", "csrc", "decode.hip")
     line = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": leg["gbps"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
+        "ms_per_step": leg["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -782,30 +856,78 @@ def main():
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                    "block_size": w.block_size, "context_lens": w.lens,
                    "shared_prefix": w.prefix, "partition_size": r["part"],
-                   "kv_loads": ("prefix: matrix-core contraction; suffixes: non-temporal"
-                                if w.prefix else
-                                "cached (shared blocks)" if r["shared"] else "non-temporal")},
-        "hbm_peak_frac": round(value / HBM_PEAK_GBPS, 4),
-        "tokens_per_s": round(r["batch"] / (ms_step * 1e-3), 1),
-        "kv_bytes_per_step": int(mean_bytes),
-        "kv_bytes_per_step_unique": int(unique_bytes),
-        "decode_partition_us": round(kernel_ms * 1e3, 2),
-        "decode_merge_us": round(float(r["merge_ms"].mean()) * 1e3, 2),
-        "roofline": {"bound": "hbm",
-                     "kernel": ("shared-prefix decode step: prefix_kernel on the matrix cores + "
-                                "decode_partition_kernel over the suffixes (append fused) + merge"
-                                if w.prefix else "decode_partition_kernel (append fused)"),
-                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                   "kv_loads": leg["kv_loads"]},
+        "hbm_peak_frac": leg["hbm_peak_frac"],
+        "tokens_per_s": leg["tokens_per_s"],
+        "kv_bytes_per_step": leg["kv_bytes_per_step"],
+        "kv_bytes_per_step_unique": leg["kv_bytes_per_step_unique"],
+        "decode_partition_us": leg["kernel_us"],
+        "decode_merge_us": leg["merge_us"],
+        "roofline": {"bound": "hbm", "kernel": leg["kernel"],
+                     "achieved": leg["kernel_gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": leg["kernel_hbm_peak_frac"],
                      "traffic": traffic_from_profiles(w, src),
-                     "launches_timed": int(len(r["kernel_ms"]))},
+                     "traffic_from": (f"profiles/decode_partition_{w.name}_traffic.md: "
+                                      "rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE of the same "
+                                      "kernel source, scaled by the block-copy calibration "
+                                      "(null when the source has changed since)"),
+                     "bytes_per_launch": leg["kernel_bytes"],
+                     "timing": "20 launches back to back between one pair of HIP events on "
+                               "the kernel's stream, on the cache state after the timed steps"},
     }
     if "decode_shared_prefix" in r:
         line["decode_shared_prefix"] = r["decode_shared_prefix"]
     if "prefill" in r:
         line["prefill"] = r["prefill"]
+    if not args.headline_only:
+        # the other workloads, each through the same step (cache values drawn
+        # on the device), and the achievable read rate
+        extra = {}
+        for name in workloads.WORKLOADS:
+            if name == w.name:
+                continue
+            wx = workloads.get(name)
+            rx = gpu_run(args, wx, torch, pkv, workloads, steps=20, warmup=5, fast=True)
+            extra[name] = summarise(wx, rx)
+            for key in ("decode_shared_prefix", "prefill"):
+                if key in rx:
+                    extra[name][key] = rx[key]
+            torch.cuda.empty_cache()
+        line["workloads"] = extra
+        sr = stream_read_run(torch, pkv)
+        sr["decode_kernel_frac_of_stream_read"] = round(leg["kernel_gbps"] / sr["gbps"], 4)
+        line["stream_read"] = sr
     line["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(w, workloads)
     print(json.dumps(line), flush=True)
+
+
+def summarise(w, r):
+    """Step rate and roofline figures of one gpu_run."""
+    ms_step = r["wall"] / r["steps"] * 1e3
+    mean_bytes = float(r["bytes"].mean())
+    unique = float(r["unique_bytes"].mean())
+    # roofline on the bytes HBM must deliver: a shared prefix counts once
+    kgbps = r["kernel_unique_bytes"] / (r["kernel_us"] * 1e-6) / 1e9
+    return {
+        "workload": w.name, "num_seqs": w.num_seqs, "partition_size": r["part"],
+        "ms_per_step": round(ms_step, 5),
+        "gbps": round(mean_bytes / (ms_step * 1e-3) / 1e9, 2),
+        "hbm_peak_frac": round(mean_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "unique_gbps": round(unique / (ms_step * 1e-3) / 1e9, 2),
+        "unique_hbm_peak_frac": round(unique / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "tokens_per_s": round(r["batch"] / (ms_step * 1e-3), 1),
+        "kv_bytes_per_step": int(mean_bytes), "kv_bytes_per_step_unique": int(unique),
+        "kernel": ("shared-prefix decode call: prefix on the matrix cores + "
+                   "decode_partition_kernel over the suffixes + merge"
+                   if w.prefix else "decode_partition_kernel (step form)"),
+        "kernel_us": round(r["kernel_us"], 2), "merge_us": round(r["merge_us"], 2),
+        "kernel_bytes": int(r["kernel_unique_bytes"]),
+        "kernel_gbps": round(kgbps, 2),
+        "kernel_hbm_peak_frac": round(kgbps / HBM_PEAK_GBPS, 4),
+        "kv_loads": ("prefix: matrix-core contraction; suffixes: non-temporal"
+                     if w.prefix else
+                     "cached (shared blocks)" if r["shared"] else "non-temporal"),
+    }
 
 
 if __name__ == "__main__":

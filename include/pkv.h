@@ -769,6 +769,21 @@ int32_t pkv_paged_attention_prefill(
     int32_t max_query_len, float scale, float* out, int32_t dtype,
     void* stream);
 
+/* ======================================================================
+ * Measurement
+ * ====================================================================== */
+
+/* Read `bytes` (a multiple of 16) of device memory at `buffer` once, with
+ * the 16-byte non-temporal loads the decode kernel uses for K/V, over
+ * `workgroups` workgroups of 256 threads: the achievable HBM read rate
+ * against which the decode kernel's bandwidth is read (the KV-cache
+ * article, §2.1, has the paged kernel hide the cost of gathering
+ * non-contiguous pages; a contiguous read of the same bytes is the bar).
+ * `sink` is a device word that the kernel may write (it keeps the loads
+ * from being dropped).  Asynchronous on `stream`. */
+int32_t pkv_stream_read(const void* buffer, int64_t bytes, int32_t workgroups,
+                        uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -131,6 +131,7 @@ _SIGNATURES = {
                                                    _I32, ctypes.c_float, _I32, _P, _P, ctypes.c_size_t, _I32, _P]),
     "pkv_paged_attention_decode_merge": (_I32, [_P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P,
                                                 ctypes.c_size_t, _P]),
+    "pkv_stream_read": (_I32, [_P, _I64, _I32, _P, _P]),
     "pkv_paged_attention_decode_noalloc": (_I32, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
                                                   _I32, _I32, _I32, ctypes.c_float, _I32, _P, _I32,
                                                   _P]),
@@ -807,6 +808,18 @@ def _decode_append(fn, query, key, value, key_cache, value_cache, block_tables, 
               int(partition_size), out.data_ptr(), ws_ptr, ws_bytes, _dtype_code(key_cache),
               _stream(query)))
     return out
+
+
+def stream_read(buffer, workgroups, sink):
+    """Read every byte of the device tensor ``buffer`` once (pkv_stream_read,
+    a measurement aid: the achievable HBM read rate); ``sink`` is a device
+    tensor of at least 4 bytes the kernel may write."""
+    _dev(buffer, "buffer")
+    _dev(sink, "sink")
+    if sink.numel() * sink.element_size() < 4:
+        raise InvalidArgument("sink must hold at least 4 bytes")
+    _check(_lib.pkv_stream_read(buffer.data_ptr(), buffer.numel() * buffer.element_size(),
+                                int(workgroups), sink.data_ptr(), _stream(buffer)))
 
 
 def paged_attention_decode_noalloc(query, key_cache, value_cache, block_tables, context_lens,
