@@ -90,6 +90,17 @@ struct Elem<PKV_BF16> {
       f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
     }
   }
+  // Element e of two token rows a and b as a float16 pair (a_e, b_e):
+  // widened to float32 (exact), then converted (exact for 2^-14 <= |v| <=
+  // 65504: 8 significant bits fit in 11).
+  __device__ static void pair_f16(const uint4& a, const uint4& b, uint32_t (&p)[8]) {
+    float fa[8], fb[8];
+    widen(a, fa);
+    widen(b, fb);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      p[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{fa[e], fb[e]}, f16x2_t));
+  }
 };
 
 template <>
@@ -120,6 +131,16 @@ struct Elem<PKV_F16> {
       f16x2_t h = __builtin_bit_cast(f16x2_t, w[i]);
       f[2 * i] = float(h.x);
       f[2 * i + 1] = float(h.y);
+    }
+  }
+  // Element e of two token rows a and b as a float16 pair (a_e, b_e): the
+  // halves regrouped, no conversion.
+  __device__ static void pair_f16(const uint4& a, const uint4& b, uint32_t (&p)[8]) {
+    const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[2 * i] = (wa[i] & 0xffffu) | (wb[i] << 16);
+      p[2 * i + 1] = (wa[i] >> 16) | (wb[i] & 0xffff0000u);
     }
   }
 };
@@ -411,6 +432,11 @@ __device__ __forceinline__ void issue_chunk(uint4 (&buf)[U], const uint8_t* tile
     else t = *at;
     buf[u] = make_uint4(t.x, t.y, t.z, t.w);
   }
+  // Keep the loads here, ahead of the computation on the previous chunk
+  // that follows: left to itself the scheduler sinks them (with their
+  // block-id reads and address arithmetic) into that computation, and a
+  // wave then has only one chunk in flight while it computes.
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // Everything a decode launch needs, passed by value as the kernel argument.
@@ -510,6 +536,13 @@ __global__ __launch_bounds__(kThreads, (decode_min_blocks<DT, G>())) void decode
     const DecodeParams prm, const Meta meta) {
   using C = Cfg<DT, D, G, U>;
   using E = Elem<DT>;
+  // With 8 query heads per kv head the kernel is bound by VALU issue rather
+  // than by HBM, and the weighted sum over V is most of it: there the
+  // weights are rounded to float16 (relative error at most 2^-11) and two
+  // tokens go through one packed float16 dot product per element and head
+  // (v_dot2_f32_f16, float32 accumulation) instead of two float32 FMAs.
+  // A bfloat16 V is widened to float16 exactly within +-65504.
+  constexpr bool kF16Pv = E::kBytes == 2 && !E::kQuantised && G >= 8 && U % 2 == 0;
   // 16-byte aligned, so a token row of G weights is read with 16-byte loads
   extern __shared__ __attribute__((aligned(16))) float smem[];
   const int32_t num_kv_heads = prm.num_kv_heads, log2_bs = prm.log2_bs;
@@ -655,41 +688,45 @@ __global__ __launch_bounds__(kThreads, (decode_min_blocks<DT, G>())) void decode
   // and the walk keeps one loop whose prefetch past the end re-reads the
   // wave's last chunk instead (192 VGPRs, two waves per SIMD).
   constexpr bool kPeeled = !(E::kQuantised && G >= 8 && D >= 128);
-  auto walk = [&](const uint8_t* base, auto&& compute) {
+  // The walk's two buffers; `first_issued`: the wave's first chunk is
+  // already in flight in `buf0` (the V pass has it loaded during the softmax).
+  uint4 buf0[U], buf1[U];
+  auto walk = [&](const uint8_t* base, auto&& compute, bool first_issued) {
     if (nj == 0) return;
-    uint4 a[U], b[U];
     if constexpr (!kPeeled) {
       auto clamped = [&](int j) { return my_chunk(min(j, nj - 1)); };
-      issue_chunk<C, U, kStream>(a, base, s_blk, clamped(0), nblk, log2_bs, blk_stride,
-                                 lane_off);
+      if (!first_issued)
+        issue_chunk<C, U, kStream>(buf0, base, s_blk, clamped(0), nblk, log2_bs, blk_stride,
+                                   lane_off);
       for (int j = 0; j < nj; j += 2) {
-        issue_chunk<C, U, kStream>(b, base, s_blk, clamped(j + 1), nblk, log2_bs, blk_stride,
+        issue_chunk<C, U, kStream>(buf1, base, s_blk, clamped(j + 1), nblk, log2_bs, blk_stride,
                                    lane_off);
-        compute(a, clamped(j));
-        issue_chunk<C, U, kStream>(a, base, s_blk, clamped(j + 2), nblk, log2_bs, blk_stride,
+        compute(buf0, clamped(j));
+        issue_chunk<C, U, kStream>(buf0, base, s_blk, clamped(j + 2), nblk, log2_bs, blk_stride,
                                    lane_off);
-        if (j + 1 < nj) compute(b, clamped(j + 1));
+        if (j + 1 < nj) compute(buf1, clamped(j + 1));
       }
       return;
     }
-    issue_chunk<C, U, kStream>(a, base, s_blk, my_chunk(0), nblk, log2_bs, blk_stride,
-                               lane_off);
+    if (!first_issued)
+      issue_chunk<C, U, kStream>(buf0, base, s_blk, my_chunk(0), nblk, log2_bs, blk_stride,
+                                 lane_off);
     int j = 0;
     for (; j + 2 < nj; j += 2) {
-      issue_chunk<C, U, kStream>(b, base, s_blk, my_chunk(j + 1), nblk, log2_bs, blk_stride,
+      issue_chunk<C, U, kStream>(buf1, base, s_blk, my_chunk(j + 1), nblk, log2_bs, blk_stride,
                                  lane_off);
-      compute(a, my_chunk(j));
-      issue_chunk<C, U, kStream>(a, base, s_blk, my_chunk(j + 2), nblk, log2_bs, blk_stride,
+      compute(buf0, my_chunk(j));
+      issue_chunk<C, U, kStream>(buf0, base, s_blk, my_chunk(j + 2), nblk, log2_bs, blk_stride,
                                  lane_off);
-      compute(b, my_chunk(j + 1));
+      compute(buf1, my_chunk(j + 1));
     }
     if (j + 1 < nj) {
-      issue_chunk<C, U, kStream>(b, base, s_blk, my_chunk(j + 1), nblk, log2_bs, blk_stride,
+      issue_chunk<C, U, kStream>(buf1, base, s_blk, my_chunk(j + 1), nblk, log2_bs, blk_stride,
                                  lane_off);
-      compute(a, my_chunk(j));
-      compute(b, my_chunk(j + 1));
+      compute(buf0, my_chunk(j));
+      compute(buf1, my_chunk(j + 1));
     } else {
-      compute(a, my_chunk(j));
+      compute(buf0, my_chunk(j));
     }
   };
 
@@ -718,7 +755,10 @@ __global__ __launch_bounds__(kThreads, (decode_min_blocks<DT, G>())) void decode
       }
     }
   };
-  walk(kbase, qk);
+  walk(kbase, qk, false);
+  // The V pass's first chunk goes out now, to arrive during the softmax.
+  if (nj > 0)
+    issue_chunk<C, U, kStream>(buf0, vbase, s_blk, my_chunk(0), nblk, log2_bs, blk_stride, lane_off);
   __syncthreads();
 
   // ---- softmax over the partition (entries e = t * G + g; a thread only
@@ -735,10 +775,40 @@ __global__ __launch_bounds__(kThreads, (decode_min_blocks<DT, G>())) void decode
 #pragma unroll
   for (int w = 1; w < kWaves; ++w) head_max = fmaxf(head_max, s_red[w * G + my_head]);
   float sum = 0.0f;
-  for (int e = tid; e < nent; e += kThreads) {
-    const float p = __builtin_amdgcn_exp2f(s_score[e] - head_max);
-    s_score[e] = p;
-    sum += p;
+  // float16 weights (kF16Pv): pair entry q = pi * G + g holds the weights
+  // of head g for the tokens ta, tb = ta + kTpl that a lane meets together
+  // in units u and u + 1 (pi = c * (U/2) * kTpl + (u/2) * kTpl + lane's
+  // token), as one float16 pair, written over the scores in place: ta >= pi,
+  // so a pass reads only at or above the words it writes, and the barrier
+  // in each round orders its reads before its writes, while later rounds
+  // read only above them.  The sum is taken over the rounded weights the
+  // product uses.
+  uint32_t* s_pw = reinterpret_cast<uint32_t*>(s_score);
+  if constexpr (kF16Pv) {
+    constexpr int kPairsPerChunk = (U / 2) * C::kTpl;
+    const int npe = nent / 2;
+    for (int base = 0; base < npe; base += kThreads) {
+      const int q = base + tid;
+      uint32_t word = 0;
+      if (q < npe) {
+        const int pi = q / G, g = q % G;
+        const int c = pi / kPairsPerChunk, r = pi % kPairsPerChunk;
+        const int ta = c * C::kChunkTok + (r / C::kTpl) * 2 * C::kTpl + r % C::kTpl;
+        const _Float16 pa = _Float16(__builtin_amdgcn_exp2f(s_score[ta * G + g] - head_max));
+        const _Float16 pb =
+            _Float16(__builtin_amdgcn_exp2f(s_score[(ta + C::kTpl) * G + g] - head_max));
+        sum += float(pa) + float(pb);
+        word = __builtin_bit_cast(uint32_t, f16x2_t{pa, pb});
+      }
+      __syncthreads();
+      if (q < npe) s_pw[q] = word;
+    }
+  } else {
+    for (int e = tid; e < nent; e += kThreads) {
+      const float p = __builtin_amdgcn_exp2f(s_score[e] - head_max);
+      s_score[e] = p;
+      sum += p;
+    }
   }
 #pragma unroll
   for (int m = G; m < 64; m <<= 1) sum += __shfl_xor(sum, m);
@@ -757,6 +827,31 @@ __global__ __launch_bounds__(kThreads, (decode_min_blocks<DT, G>())) void decode
   // widened, so stale or NaN cache contents contribute exactly nothing.
   auto pv = [&](const uint4 (&vv)[U], int c) {
     const int t0 = c * C::kChunkTok;
+    if constexpr (kF16Pv) {
+      // A lane's tokens of units u and u + 1 (kTpl apart) as float16
+      // pairs: one packed dot product per element and head covers both.
+#pragma unroll
+      for (int u = 0; u < U; u += 2) {
+        const int ta = t0 + u * C::kTpl + tok_in_unit, tb = ta + C::kTpl;
+        const bool la = ta < ntok, lb = tb < ntok;
+        const uint4 ra = make_uint4(la ? vv[u].x : 0u, la ? vv[u].y : 0u, la ? vv[u].z : 0u,
+                                    la ? vv[u].w : 0u);
+        const uint4 rb = make_uint4(lb ? vv[u + 1].x : 0u, lb ? vv[u + 1].y : 0u,
+                                    lb ? vv[u + 1].z : 0u, lb ? vv[u + 1].w : 0u);
+        uint32_t vp[C::kEpl];
+        E::pair_f16(ra, rb, vp);
+        const uint32_t* pw = s_pw + ((c * (U / 2) + u / 2) * C::kTpl + tok_in_unit) * G;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const f16x2_t w2 = __builtin_bit_cast(f16x2_t, pw[g]);
+#pragma unroll
+          for (int e = 0; e < C::kEpl; ++e)
+            acc[g][e] = __builtin_amdgcn_fdot2(w2, __builtin_bit_cast(f16x2_t, vp[e]), acc[g][e],
+                                               false);
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int t = t0 + u * C::kTpl + tok_in_unit;
@@ -773,7 +868,7 @@ __global__ __launch_bounds__(kThreads, (decode_min_blocks<DT, G>())) void decode
       }
     }
   };
-  walk(vbase, pv);
+  walk(vbase, pv, true);
 
   // ---- combine token rows within the wave, then the waves ----------------
   // Each lane ends with kOut of the G * kEpl sums of its d-slice: flat index
