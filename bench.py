@@ -16,7 +16,10 @@ through every stage of the path:
      shared-prefix workload) steps through
      paged_attention_decode_shared_prefix_step instead: every query against
      the prefix on the matrix cores, the suffixes by the split-K kernel
-     (append fused), one merge.
+     (append fused), one merge; a batch of several prefix groups (the
+     grouped-prefix workload) through
+     paged_attention_decode_grouped_prefix_step, the same three launches
+     with every group's prefix in the one matrix-core launch.
 The cache is resident in HBM before timing starts.  ``value`` is the KV
 bytes the decode reads per step (sum over sequences of context_len * Hkv *
 head_dim * 2 * element size) divided by the wall time of a whole step.
@@ -34,9 +37,10 @@ after 5; their caches filled with values drawn on the device), and
 the decode kernel's load width and policy.
 ``cpu_baseline`` times the float64 CPU oracle on a small sample of the same
 workload (reported only; the host's CPU model and core count go into its
-``sample``).  For the shared-prefix workload the line also carries
-``decode_shared_prefix`` (the shared-prefix call against the split-K call
-on the same cache state) and ``prefill``: one causal 512-row chunked
+``sample``).  For the prefix workloads the line also carries
+``decode_shared_prefix`` (the shared- or grouped-prefix call against the
+split-K call on the same cache state), and for the shared-prefix one
+``prefill``: one causal 512-row chunked
 prefill per sequence, timed the same way, against the bf16 matrix-core
 peak; its oracle timing (one sequence's chunk) is ``cpu_baseline.prefill``.
 
@@ -102,12 +106,51 @@ def kv_bytes(w, lens):
 
 
 def kv_bytes_unique(w, lens):
-    """KV bytes with a shared prefix counted once (what a step must fetch
+    """KV bytes with each shared prefix counted once (what a step must fetch
     from HBM at least); equal to kv_bytes when nothing is shared."""
-    if not w.prefix:
+    import workloads
+    layout = workloads.prefix_layout(w)
+    if not layout:
         return kv_bytes(w, lens)
-    tokens = int(np.sum(np.asarray(lens, dtype=np.int64) - w.prefix)) + w.prefix
+    starts, plens = layout
+    tokens = int(np.sum(np.asarray(lens, dtype=np.int64) - workloads.seq_prefixes(w)))
+    tokens += sum(n for g, n in enumerate(plens) if starts[g + 1] > starts[g])
     return tokens * w.num_kv_heads * w.head_dim * 2 * w.elem_bytes
+
+
+def prefix_ws_bytes(pkv, w, b, max_len):
+    """Workspace of the workload's prefix call (shared or grouped)."""
+    import workloads
+    if w.prefix:
+        return pkv.paged_attention_decode_shared_prefix_workspace_size(
+            b, w.num_heads, w.num_kv_heads, w.head_dim, w.block_size, max_len, w.prefix)
+    starts, plens = workloads.prefix_layout(w)
+    return pkv.paged_attention_decode_grouped_prefix_workspace_size(
+        b, w.num_heads, w.num_kv_heads, w.head_dim, w.block_size, max_len, starts, plens)
+
+
+def prefix_step(pkv, w, q, k, v, kc, vc, tables, lens, changes, mc, out, ws):
+    """One step of the workload's prefix call: the shared-prefix step for one
+    prefix, the grouped-prefix step for several groups."""
+    import workloads
+    if w.prefix:
+        return pkv.paged_attention_decode_shared_prefix_step(
+            q, k, v, kc, vc, tables, lens, changes, w.prefix, w.scale, mc, out=out, workspace=ws)
+    starts, plens = workloads.prefix_layout(w)
+    return pkv.paged_attention_decode_grouped_prefix_step(
+        q, k, v, kc, vc, tables, lens, changes, starts, plens, w.scale, mc, out=out,
+        workspace=ws)
+
+
+def prefix_call(pkv, w, q, kc, vc, tables, lens, mc, out, ws):
+    """The plain (device lengths) form of the workload's prefix call."""
+    import workloads
+    if w.prefix:
+        return pkv.paged_attention_decode_shared_prefix(q, kc, vc, tables, lens, w.prefix,
+                                                        w.scale, mc, out=out, workspace=ws)
+    starts, plens = workloads.prefix_layout(w)
+    return pkv.paged_attention_decode_grouped_prefix(q, kc, vc, tables, lens, starts, plens,
+                                                     w.scale, mc, out=out, workspace=ws)
 
 
 def setup(w, pkv, workloads, torch, dev):
@@ -210,14 +253,14 @@ def gpu_run(args, w, torch, pkv, workloads, steps=None, warmup=None, fast=False)
     shared = any(r > 1 for r in alloc.snapshot()[1])
     launch = pkv.DecodeLauncher(kc, vc, w.num_heads, b, mb, max_len, part, out, workspace,
                                 shared_blocks=shared)
-    # a batch forked from one prefix steps through the shared-prefix call
-    # instead: the prefix on the matrix cores, the suffixes split-K (the
-    # append fused), one merge
+    # a batch forked from one prefix, or made of prefix groups, steps through
+    # the shared- or grouped-prefix call instead: the prefixes on the matrix
+    # cores, the suffixes split-K (the append fused), one merge
     ws_sp = None
-    if w.prefix:
-        ws_sp = torch.empty(max(pkv.paged_attention_decode_shared_prefix_workspace_size(
-            b, w.num_heads, w.num_kv_heads, w.head_dim, w.block_size, max_len, w.prefix), 16),
-            dtype=torch.uint8, device=dev)
+    prefixed = workloads.prefix_layout(w) is not None
+    if prefixed:
+        ws_sp = torch.empty(max(prefix_ws_bytes(pkv, w, b, max_len), 16), dtype=torch.uint8,
+                            device=dev)
     step_bytes = np.zeros(total_steps, dtype=np.float64)
     step_unique = np.zeros(total_steps, dtype=np.float64)
 
@@ -228,10 +271,9 @@ def gpu_run(args, w, torch, pkv, workloads, steps=None, warmup=None, fast=False)
             dst = torch.tensor([c for _, c in pairs], dtype=torch.int32).to(dev)
             pkv.copy_blocks(kc, vc, src, dst)
         mc = int(lens_h.max())
-        if w.prefix:                                                         # 4
-            pkv.paged_attention_decode_shared_prefix_step(
-                q[i], k_new[i], v_new[i], kc, vc, tables_d, lens_h, changes_h[:n_changes],
-                w.prefix, w.scale, mc, out=out, workspace=ws_sp)
+        if prefixed:                                                         # 4
+            prefix_step(pkv, w, q[i], k_new[i], v_new[i], kc, vc, tables_d, lens_h,
+                        changes_h[:n_changes], mc, out, ws_sp)
         else:
             launch.step_partials(q[i], tables_d, lens_h, changes_h, n_changes, mc, w.scale,  # 4
                                  k_new[i], v_new[i])
@@ -258,11 +300,10 @@ def gpu_run(args, w, torch, pkv, workloads, steps=None, warmup=None, fast=False)
     # merge alone the same way.
     mc = int(lens_h.max())
     no_changes = changes_h[:0]
-    if w.prefix:
+    if prefixed:
         def kernel():
-            pkv.paged_attention_decode_shared_prefix_step(
-                q[-1], None, None, kc, vc, tables_d, lens_h, no_changes, w.prefix, w.scale, mc,
-                out=out, workspace=ws_sp)
+            prefix_step(pkv, w, q[-1], None, None, kc, vc, tables_d, lens_h, no_changes, mc, out,
+                        ws_sp)
         merge = None
     else:
         def kernel():
@@ -277,7 +318,7 @@ def gpu_run(args, w, torch, pkv, workloads, steps=None, warmup=None, fast=False)
                kernel_unique_bytes=float(kv_bytes_unique(w, lens_h)),
                bytes=step_bytes[warmup:], unique_bytes=step_unique[warmup:],
                batch=b, part=part, shared=shared, steps=steps)
-    if w.prefix:
+    if prefixed:
         res["decode_shared_prefix"] = shared_prefix_decode_run(w, p, alloc, kc, vc, torch, pkv,
                                                                dev)
     if w.chunk and not args.no_prefill:
@@ -339,9 +380,7 @@ def shared_prefix_decode_run(w, p, alloc, kc, vc, torch, pkv, dev):
     out_b = torch.empty_like(out_a)
     ws_a = torch.empty(max(pkv.paged_attention_decode_workspace_size(
         b, w.num_heads, w.num_kv_heads, w.head_dim, mc, 0), 16), dtype=torch.uint8, device=dev)
-    ws_b = torch.empty(max(pkv.paged_attention_decode_shared_prefix_workspace_size(
-        b, w.num_heads, w.num_kv_heads, w.head_dim, w.block_size, mc, w.prefix), 16),
-        dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(max(prefix_ws_bytes(pkv, w, b, mc), 16), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def plain():
@@ -349,8 +388,7 @@ def shared_prefix_decode_run(w, p, alloc, kc, vc, torch, pkv, dev):
                                    workspace=ws_a, shared_blocks=True)
 
     def cascade():
-        pkv.paged_attention_decode_shared_prefix(q, kc, vc, tables, lens, w.prefix, w.scale, mc,
-                                                 out=out_b, workspace=ws_b)
+        prefix_call(pkv, w, q, kc, vc, tables, lens, mc, out_b, ws_b)
 
     times = {}
     for name, fn in (("split_k", plain), ("shared_prefix", cascade)):
@@ -368,7 +406,11 @@ def shared_prefix_decode_run(w, p, alloc, kc, vc, torch, pkv, dev):
         raise RuntimeError(f"shared-prefix decode differs from split-K decode by {diff}")
     unique = kv_bytes_unique(w, lh)
     us = times["shared_prefix"] * 1e3
-    return {"call": "pkv_paged_attention_decode_shared_prefix", "prefix_len": w.prefix,
+    import workloads
+    starts, plens = workloads.prefix_layout(w)
+    return {"call": ("pkv_paged_attention_decode_shared_prefix" if w.prefix else
+                     "pkv_paged_attention_decode_grouped_prefix"),
+            "group_starts": starts, "prefix_lens": plens,
             "us": round(us, 2), "split_k_us": round(times["split_k"] * 1e3, 2),
             "speedup": round(times["split_k"] / times["shared_prefix"], 3),
             "unique_kv_bytes": int(unique),
@@ -726,10 +768,11 @@ def cpu_baseline(w, workloads):
     def wanted(op):
         if op[0] == "fork":
             return op[2] in keep
-        return op[1] in keep or op[1] == workloads.PREFIX_SEQ
+        return op[1] in keep or op[1] >= workloads.PREFIX_SEQ   # a prefix parent
 
-    need = sum(-(-int(n) // w.block_size) for n in p.lens[:sample]) + \
-        -(-w.prefix // w.block_size) + -(-w.chunk // w.block_size) + 5
+    prefixes = sum(-(-n // w.block_size) for n in (workloads.prefix_layout(w) or [[], []])[1])
+    need = sum(-(-int(n) // w.block_size) for n in p.lens[:sample]) + prefixes + \
+        -(-w.chunk // w.block_size) + 5
     ref = RefAllocator(need, w.block_size)
     shape = (need, w.num_kv_heads, w.block_size, w.head_dim)
     kc, vc = np.full(shape, np.nan), np.full(shape, np.nan)
@@ -855,7 +898,8 @@ def main():
         "config": {"workload": w.name, "num_seqs": w.num_seqs, "num_heads": w.num_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                    "block_size": w.block_size, "context_lens": w.lens,
-                   "shared_prefix": w.prefix, "partition_size": r["part"],
+                   "shared_prefix": w.prefix, "prefix_groups": list(w.prefix_groups),
+                   "partition_size": r["part"],
                    "kv_loads": leg["kv_loads"]},
         "hbm_peak_frac": leg["hbm_peak_frac"],
         "tokens_per_s": leg["tokens_per_s"],
@@ -919,13 +963,16 @@ def summarise(w, r):
         "kv_bytes_per_step": int(mean_bytes), "kv_bytes_per_step_unique": int(unique),
         "kernel": ("shared-prefix decode call: prefix on the matrix cores + "
                    "decode_partition_kernel over the suffixes + merge"
-                   if w.prefix else "decode_partition_kernel (step form)"),
+                   if w.prefix else
+                   "grouped-prefix decode call: every group's prefix on the matrix cores + "
+                   "decode_partition_kernel over the suffixes + merge"
+                   if w.prefix_groups else "decode_partition_kernel (step form)"),
         "kernel_us": round(r["kernel_us"], 2), "merge_us": round(r["merge_us"], 2),
         "kernel_bytes": int(r["kernel_unique_bytes"]),
         "kernel_gbps": round(kgbps, 2),
         "kernel_hbm_peak_frac": round(kgbps / HBM_PEAK_GBPS, 4),
         "kv_loads": ("prefix: matrix-core contraction; suffixes: non-temporal"
-                     if w.prefix else
+                     if w.prefix or w.prefix_groups else
                      "cached (shared blocks)" if r["shared"] else "non-temporal"),
     }
 

@@ -493,6 +493,11 @@ int32_t pkv_paged_attention_decode_workspace_size(
  * Supported: head_dim in {64, 128}; num_heads / num_kv_heads in
  * {1, 2, 4, 8}; block_size a power of two in [8, 256]; the scale is any
  * finite float.  Row h reads KV head h / (num_heads / num_kv_heads).
+ * With 8 query heads per KV head on a float16 or bfloat16 cache the
+ * softmax weights are rounded to float16 for the weighted sum over V
+ * (relative error 2^-11 per weight, float32 accumulation; the
+ * normaliser is the sum of the rounded weights) and a bfloat16 V is
+ * widened to float16, so such a V must stay within +-65504.
  * dtype is the cache's (PKV_F32, PKV_F16, PKV_BF16), optionally OR'd with
  * PKV_DECODE_SHARED_BLOCKS; the same holds for every decode call below. */
 int32_t pkv_paged_attention_decode(
@@ -695,9 +700,10 @@ int32_t pkv_paged_attention_decode_fp8_partials(
  *                  table entries differ from row 0's, or whose device
  *                  length is below prefix_len, gets a NaN row.
  *   partition_size split-K partition of the suffixes (0 = automatic)
- *   workspace      float32 partials, at least the bytes
+ *   workspace      per-row records and float32 partials, at least the bytes
  *                  pkv_paged_attention_decode_shared_prefix_workspace_size
  *                  gives; always needed (the prefix's partial has a slot)
+ * This is pkv_paged_attention_decode_grouped_prefix with one group.
  * The prefix part rounds the softmax weights to float16 for its product
  * with V, as the chunked prefill does (relative error of a weight at most
  * 2^-12); a bfloat16 V is widened to float16 (|v| <= 65504). */
@@ -736,6 +742,67 @@ int32_t pkv_paged_attention_decode_shared_prefix_step(
     int32_t max_context_len, int32_t prefix_len, float scale,
     int32_t partition_size, float* out, void* workspace,
     size_t workspace_bytes, int32_t dtype, void* stream);
+
+/* Decode attention for a batch made of prefix groups: consecutive rows
+ * forked from one parent, each group sharing its parent's first tokens
+ * (explainer, section on memory sharing: parallel samples of one prompt,
+ * and several prompts each with its own samples, map the shared blocks
+ * once; tutorial §1.4).  The generalisation of
+ * pkv_paged_attention_decode_shared_prefix to several groups, with the
+ * same result as pkv_paged_attention_decode on the same tables: every
+ * group's prefix on the matrix cores, read once per query head and group
+ * (one launch for all groups, key ranges of equal length), every suffix
+ * split-K, one merge.
+ *   num_groups     groups, 1 .. 128
+ *   group_starts   host int32 [num_groups + 1]: group g is rows
+ *                  group_starts[g] .. group_starts[g + 1] - 1; starts at 0,
+ *                  never decreases (empty groups are allowed), ends at
+ *                  num_seqs
+ *   prefix_lens    host int32 [num_groups]: tokens group g shares, 0 or a
+ *                  multiple of block_size, at most max_context_len and the
+ *                  table's capacity.  0: the group's rows share nothing and
+ *                  are decoded from token 0 by the suffix launch.  The
+ *                  prefix is read through the table of the group's first
+ *                  row; a row whose first prefix_lens[g] / block_size
+ *                  entries differ from it, or whose device length is below
+ *                  prefix_lens[g], gets a NaN row.
+ *   workspace      at least the bytes
+ *                  pkv_paged_attention_decode_grouped_prefix_workspace_size
+ *                  gives for the same groups
+ * Other arguments, limits, errors and the float16 rounding of the prefix
+ * weights as pkv_paged_attention_decode_shared_prefix. */
+int32_t pkv_paged_attention_decode_grouped_prefix_workspace_size(
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int32_t max_context_len, int32_t num_groups,
+    const int32_t* group_starts, const int32_t* prefix_lens, int32_t partition_size,
+    size_t* bytes);
+int32_t pkv_paged_attention_decode_grouped_prefix(
+    const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t max_blocks_per_seq, int32_t num_blocks, int32_t max_context_len,
+    int32_t num_groups, const int32_t* group_starts, const int32_t* prefix_lens, float scale,
+    int32_t partition_size, float* out, void* workspace, size_t workspace_bytes,
+    int32_t dtype, void* stream);
+
+/* The step form of pkv_paged_attention_decode_grouped_prefix, as
+ * pkv_paged_attention_decode_shared_prefix_step is of the one-group call:
+ * host lengths and this step's table changes by value, new K/V rows stored
+ * by the suffix kernel.  Work order longest suffix first.  In a group with
+ * a prefix, with key and value given every length must exceed the group's
+ * prefix, and a change must name a logical block past the prefix of a
+ * sequence longer than it (PKV_ERR_INVALID otherwise).  Equal, bit for bit,
+ * to the append followed by pkv_paged_attention_decode_grouped_prefix on
+ * the updated tables. */
+int32_t pkv_paged_attention_decode_grouped_prefix_step(
+    const void* query, const void* key, const void* value, void* key_cache,
+    void* value_cache, int32_t* block_tables, const int32_t* context_lens,
+    const int32_t* changes, int32_t num_changes, int32_t num_seqs, int32_t num_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+    int32_t num_blocks, int32_t max_context_len, int32_t num_groups,
+    const int32_t* group_starts, const int32_t* prefix_lens, float scale,
+    int32_t partition_size, float* out, void* workspace, size_t workspace_bytes,
+    int32_t dtype, void* stream);
 
 /* Causal chunked prefill against the same paged cache (article §4.1/§4.2:
  * long prompts in chunks; §2.1: the same block-table gather and softmax).

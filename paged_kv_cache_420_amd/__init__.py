@@ -29,7 +29,12 @@ __all__ = [
     "paged_attention_decode_append_partials", "paged_attention_decode_step",
     "paged_attention_decode_partials", "paged_attention_decode_merge",
     "paged_attention_prefill", "paged_kv_append_fp8", "paged_attention_decode_fp8",
-    "paged_attention_decode_fp8_partials", "swap_blocks", "library_path", "version",
+    "paged_attention_decode_fp8_partials", "paged_attention_decode_shared_prefix",
+    "paged_attention_decode_shared_prefix_step",
+    "paged_attention_decode_shared_prefix_workspace_size",
+    "paged_attention_decode_grouped_prefix", "paged_attention_decode_grouped_prefix_step",
+    "paged_attention_decode_grouped_prefix_workspace_size", "paged_attention_decode_noalloc",
+    "stream_read", "swap_blocks", "library_path", "version",
 ]
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
@@ -154,6 +159,15 @@ _SIGNATURES = {
     "pkv_paged_attention_decode_shared_prefix_step": (
         _I32, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                _I32, _I32, ctypes.c_float, _I32, _P, _P, ctypes.c_size_t, _I32, _P]),
+    "pkv_paged_attention_decode_grouped_prefix_workspace_size": (
+        _I32, [_I32, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _I32,
+               ctypes.POINTER(ctypes.c_size_t)]),
+    "pkv_paged_attention_decode_grouped_prefix": (
+        _I32, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P,
+               ctypes.c_float, _I32, _P, _P, ctypes.c_size_t, _I32, _P]),
+    "pkv_paged_attention_decode_grouped_prefix_step": (
+        _I32, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+               _I32, _I32, _P, _P, ctypes.c_float, _I32, _P, _P, ctypes.c_size_t, _I32, _P]),
     "pkv_scheduler_create": (_I32, [_I32, _I32, _P, _I32, _I32, _I32, _I32, _I32,
                                     ctypes.POINTER(_P)]),
     "pkv_scheduler_last_swaps": (_I32, [_P, _P, _P, _I32, _P, _P, _P, _I32, _P]),
@@ -1186,6 +1200,111 @@ def paged_attention_decode_shared_prefix_step(query, key, value, key_cache, valu
         int(partition_size), out.data_ptr(), workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), _decode_code(key_cache, shared_blocks),
         _stream(query)))
+    return out
+
+
+def _prefix_groups(group_starts, prefix_lens):
+    """Host int32 copies of a grouped-prefix call's group arrays."""
+    starts = np.ascontiguousarray(np.asarray(group_starts, dtype=np.int32).reshape(-1))
+    lens = np.ascontiguousarray(np.asarray(prefix_lens, dtype=np.int32).reshape(-1))
+    if starts.shape[0] != lens.shape[0] + 1 or lens.shape[0] == 0:
+        raise InvalidArgument("group_starts must have one entry more than prefix_lens (>= 1)")
+    return starts, lens
+
+
+def paged_attention_decode_grouped_prefix_workspace_size(num_seqs, num_heads, num_kv_heads,
+                                                         head_dim, block_size, max_context_len,
+                                                         group_starts, prefix_lens,
+                                                         partition_size=0):
+    """Workspace bytes of paged_attention_decode_grouped_prefix
+    (pkv_paged_attention_decode_grouped_prefix_workspace_size)."""
+    starts, lens = _prefix_groups(group_starts, prefix_lens)
+    out = ctypes.c_size_t()
+    _check(_lib.pkv_paged_attention_decode_grouped_prefix_workspace_size(
+        int(num_seqs), int(num_heads), int(num_kv_heads), int(head_dim), int(block_size),
+        int(max_context_len), lens.shape[0], starts.ctypes.data, lens.ctypes.data,
+        int(partition_size), ctypes.byref(out)))
+    return out.value
+
+
+def _grouped_args(query, key_cache, value_cache, block_tables, group_starts, prefix_lens,
+                  max_context_len, partition_size, out, workspace):
+    nb, hkv, bs, d = _cache_dims(key_cache, value_cache)
+    _dev(query, "query", dtype=key_cache.dtype, ndim=3)
+    _dev(block_tables, "block_tables", dtype=torch.int32, ndim=2)
+    b, hq, _ = query.shape
+    if query.shape[2] != d or block_tables.shape[0] != b:
+        raise InvalidArgument("query [B, Hq, D], block_tables [B, max_blocks]")
+    starts, lens = _prefix_groups(group_starts, prefix_lens)
+    if out is None:
+        out = torch.empty((b, hq, d), dtype=torch.float32, device=query.device)
+    _dev(out, "out", dtype=torch.float32, ndim=3)
+    if tuple(out.shape) != (b, hq, d):
+        raise InvalidArgument("out must be [B, Hq, D]")
+    need = paged_attention_decode_grouped_prefix_workspace_size(
+        b, hq, hkv, d, bs, int(max_context_len), starts, lens, partition_size)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=query.device)
+    _dev(workspace, "workspace")
+    return nb, hkv, bs, d, b, hq, starts, lens, out, workspace
+
+
+def paged_attention_decode_grouped_prefix(query, key_cache, value_cache, block_tables,
+                                          context_lens, group_starts, prefix_lens, scale,
+                                          max_context_len, partition_size=0, out=None,
+                                          workspace=None, shared_blocks=False):
+    """Decode for a batch of prefix groups
+    (pkv_paged_attention_decode_grouped_prefix): rows group_starts[g] ..
+    group_starts[g + 1] - 1 share their first prefix_lens[g] tokens (0: no
+    sharing), read through the table of the group's first row.  Same result
+    as paged_attention_decode on the same tables."""
+    nb, hkv, bs, d, b, hq, starts, lens, out, workspace = _grouped_args(
+        query, key_cache, value_cache, block_tables, group_starts, prefix_lens,
+        max_context_len, partition_size, out, workspace)
+    _dev(context_lens, "context_lens", dtype=torch.int32, ndim=1)
+    if context_lens.shape[0] != b:
+        raise InvalidArgument("context_lens must be [B]")
+    _check(_lib.pkv_paged_attention_decode_grouped_prefix(
+        query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(), block_tables.data_ptr(),
+        context_lens.data_ptr(), b, hq, hkv, d, bs, block_tables.shape[1], nb,
+        int(max_context_len), lens.shape[0], starts.ctypes.data, lens.ctypes.data, float(scale),
+        int(partition_size), out.data_ptr(), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _decode_code(key_cache, shared_blocks),
+        _stream(query)))
+    return out
+
+
+def paged_attention_decode_grouped_prefix_step(query, key, value, key_cache, value_cache,
+                                               block_tables, context_lens, changes, group_starts,
+                                               prefix_lens, scale, max_context_len,
+                                               partition_size=0, out=None, workspace=None,
+                                               shared_blocks=False):
+    """Step form of paged_attention_decode_grouped_prefix
+    (pkv_paged_attention_decode_grouped_prefix_step): block_tables is the
+    device table kept across steps (updated in place with ``changes``);
+    context_lens host int32 [B] and changes host int32 [n, 3] as for
+    paged_attention_decode_step; key/value the step's new rows or None."""
+    nb, hkv, bs, d, b, hq, starts, glens, out, workspace = _grouped_args(
+        query, key_cache, value_cache, block_tables, group_starts, prefix_lens,
+        max_context_len, partition_size, out, workspace)
+    lens = np.ascontiguousarray(np.asarray(context_lens, dtype=np.int32))
+    changes = np.ascontiguousarray(np.asarray(changes, dtype=np.int32).reshape(-1, 3))
+    if lens.shape != (b,):
+        raise InvalidArgument("context_lens must be host int32 [B]")
+    kp = vp = None
+    if key is not None or value is not None:
+        _dev(key, "key", dtype=key_cache.dtype, ndim=3)
+        _dev(value, "value", dtype=key_cache.dtype, ndim=3)
+        if tuple(key.shape) != (b, hkv, d) or value.shape != key.shape:
+            raise InvalidArgument("key/value must be [B, num_kv_heads, head_dim]")
+        kp, vp = key.data_ptr(), value.data_ptr()
+    _check(_lib.pkv_paged_attention_decode_grouped_prefix_step(
+        query.data_ptr(), kp, vp, key_cache.data_ptr(), value_cache.data_ptr(),
+        block_tables.data_ptr(), lens.ctypes.data, changes.ctypes.data, changes.shape[0], b, hq,
+        hkv, d, bs, block_tables.shape[1], nb, int(max_context_len), glens.shape[0],
+        starts.ctypes.data, glens.ctypes.data, float(scale), int(partition_size), out.data_ptr(),
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        _decode_code(key_cache, shared_blocks), _stream(query)))
     return out
 
 

@@ -32,15 +32,28 @@ inline bool aligned16(const void* p) {
   return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
 }
 
-// prefill.hip: the shared-prefix partials of
-// pkv_paged_attention_decode_shared_prefix (arguments checked by the
-// caller; returns the launch's hipError_t).
+// Prefix groups of one shared-prefix decode call: the batch's rows
+// [start[g], start[g + 1]) were forked from one parent and share its first
+// prefix_len[g] tokens (0: the group shares nothing).
+constexpr int kMaxPrefixGroups = 128;
+struct PrefixGroups {
+  int32_t count;
+  int32_t start[kMaxPrefixGroups + 1];
+  int32_t prefix_len[kMaxPrefixGroups];
+};
+
+// prefill.hip: the prefix partials of the shared-prefix decode (arguments
+// checked by the caller; returns the launch's hipError_t).  Every group's
+// prefix is split into key ranges of split_keys keys; range z of group g
+// goes to partial slot z of each of its rows.  The launch also writes each
+// row's record row_info[4 r .. 4 r + 3] = {prefix_len, first row of its
+// group, prefix slots, 0} for the suffix and merge launches.
 int launch_prefix_partials(int32_t dtype, const void* query, const void* key_cache,
-                           const void* value_cache, const int32_t* block_tables, int32_t rows,
-                           int32_t num_heads, int32_t num_kv_heads, int32_t block_size,
-                           int32_t max_blocks_per_seq, int32_t num_blocks, int32_t prefix_len,
-                           int32_t splits, int32_t split_keys, float scale, float* ws_acc,
-                           float* ws_ml, int32_t slots, void* stream);
+                           const void* value_cache, const int32_t* block_tables,
+                           const PrefixGroups& groups, int32_t num_heads, int32_t num_kv_heads,
+                           int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+                           int32_t split_keys, int32_t max_splits, float scale, float* ws_acc,
+                           float* ws_ml, int32_t* row_info, int32_t slots, void* stream);
 
 // Rows per workgroup of the prefill kernel (the shared-prefix split count
 // is chosen from the grid it gives).

@@ -457,10 +457,14 @@ struct DecodeParams {
   float scale_log2;            // scale * log2(e), times the K scale of an 8-bit cache
   float v_scale;               // V scale of an 8-bit cache (unused otherwise)
   int32_t shared_blocks;       // nonzero: launch the cached-load kernel (shared blocks)
-  // Suffix mode (shared-prefix decode): the launch covers tokens [start,
-  // len) of every sequence and writes its partitions as partials from slot
-  // slot_base on (slot 0 holds the prefix's partial).  0, 0 otherwise.
-  int32_t start, slot_base;
+  // Suffix mode (shared-prefix decode), when row_info is set: the launch
+  // covers tokens [start, len) of every sequence, start being the prefix
+  // length of its group (row_info[4 b]), and writes its partitions as
+  // partials from slot slot_base on (the slots before hold the prefix's
+  // partials: row_info[4 b + 2] of them).  row_info[4 b + 1] is the first
+  // row of the group, whose table reached the prefix.
+  const int32_t* row_info;
+  int32_t slot_base;
 };
 
 // Where a launch gets each sequence's length and which table entries it
@@ -566,21 +570,25 @@ __global__ __launch_bounds__(kThreads, (decode_min_blocks<DT, G>())) void decode
   const int num_heads = num_kv_heads * G;
 
   const int n = meta.len(prm, b, rank);
-  const int start = prm.start, slot_base = prm.slot_base;
+  const bool suffix = prm.row_info != nullptr;
+  const int slot_base = prm.slot_base;
+  const int start = suffix ? prm.row_info[4 * int64_t(b)] : 0;
   const bool bad_len =
       n < start || n > prm.max_ctx || int64_t(n) > int64_t(max_blocks) * bs;
   // in suffix mode a sequence with no token past the prefix has no partition
-  const int nparts = bad_len ? 1 : slot_base > 0 ? cdiv(n - start, part) : max(1, cdiv(n, part));
-  if (slot_base > 0 && p_idx == 0 && !bad_len) {
-    // Suffix mode: the shared prefix was read through row 0 of the table.
-    // A sequence whose own table does not name the same blocks for it is
-    // inconsistent input: its prefix partial's max becomes NaN, so the
-    // merge writes a NaN row (first partition of each kv head; the prefix
-    // launch that wrote the partial has completed).
+  const int nparts = bad_len ? 1 : suffix ? cdiv(n - start, part) : max(1, cdiv(n, part));
+  if (suffix && start > 0 && p_idx == 0 && !bad_len) {
+    // Suffix mode: the group's prefix was read through the table of its
+    // first row.  A sequence whose own table does not name the same blocks
+    // for it is inconsistent input: its first prefix partial's max becomes
+    // NaN, so the merge writes a NaN row (first partition of each kv head;
+    // the prefix launch that wrote the partial has completed).
     const int32_t* own = prm.block_tables + int64_t(b) * max_blocks;
+    const int32_t* first =
+        prm.block_tables + int64_t(prm.row_info[4 * int64_t(b) + 1]) * max_blocks;
     bool differs = false;
     for (int i = int(threadIdx.x); i < (start >> log2_bs); i += kThreads)
-      differs |= own[i] != prm.block_tables[i];
+      differs |= own[i] != first[i];
     if (__syncthreads_or(differs) && threadIdx.x < G)
       prm.ws_ml[((int64_t(b) * num_kv_heads * G + int64_t(kvh) * G + threadIdx.x) *
                      prm.max_parts) * 2] = __builtin_nanf("");
@@ -902,7 +910,7 @@ __global__ __launch_bounds__(kThreads, (decode_min_blocks<DT, G>())) void decode
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) m = fmaxf(m, s_red[w * G + g]);
     if constexpr (E::kQuantised) a *= prm.v_scale;
-    if (nparts == 1 && slot_base == 0) {
+    if (nparts == 1 && !suffix) {
       out_row[i] = bad_blk ? nan : a / l;
     } else {
       const int64_t row =
@@ -930,17 +938,28 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(
   const int h = blockIdx.x;
   const int b = meta.merge_seq(blockIdx.y);
   const int n = meta.len(prm, b, blockIdx.y);
-  const bool bad_len = n < prm.start || n > max_ctx ||
+  // suffix mode: the prefix's partials in slots [0, pslots), the suffix's
+  // from slot_base on
+  const bool suffix = prm.row_info != nullptr;
+  const int start = suffix ? prm.row_info[4 * int64_t(b)] : 0;
+  const int pslots = suffix ? prm.row_info[4 * int64_t(b) + 2] : 0;
+  const bool bad_len = n < start || n > max_ctx ||
                        int64_t(n) > (int64_t(max_blocks) << log2_bs);
   if (bad_len) return;
-  // suffix mode: slot 0 is the shared prefix's partial, then the suffix's
-  const int nparts = prm.slot_base + cdiv(n - prm.start, part);
-  if (nparts <= 1 && prm.slot_base == 0) return;
+  const int nparts = pslots + cdiv(n - start, part);
+  if (nparts <= 1 && !suffix) return;
+  float* o = out + (int64_t(b) * num_heads + h) * D;
+  if (nparts == 0) {  // a group with no prefix: an empty context
+#pragma unroll
+    for (int j = 0; j < D / 64; ++j) o[j * 64 + threadIdx.x] = 0.0f;
+    return;
+  }
   const int64_t row0 = (int64_t(b) * num_heads + h) * max_parts;
+  const int skip = prm.slot_base - pslots;  // slots between the two runs
   float big = -INFINITY;
   bool any_nan = false;
   for (int p = 0; p < nparts; ++p) {
-    const float m = ws_ml[(row0 + p) * 2];
+    const float m = ws_ml[(row0 + p + (p < pslots ? 0 : skip)) * 2];
     any_nan |= m != m;
     big = fmaxf(big, m);
   }
@@ -949,13 +968,13 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(
 #pragma unroll
   for (int j = 0; j < D / 64; ++j) num[j] = 0.0f;
   for (int p = 0; p < nparts; ++p) {
-    const float w = __builtin_amdgcn_exp2f(ws_ml[(row0 + p) * 2] - big);
-    den = fmaf(w, ws_ml[(row0 + p) * 2 + 1], den);
+    const int64_t slot = row0 + p + (p < pslots ? 0 : skip);
+    const float w = __builtin_amdgcn_exp2f(ws_ml[slot * 2] - big);
+    den = fmaf(w, ws_ml[slot * 2 + 1], den);
 #pragma unroll
     for (int j = 0; j < D / 64; ++j)
-      num[j] = fmaf(w, ws_acc[(row0 + p) * D + j * 64 + threadIdx.x], num[j]);
+      num[j] = fmaf(w, ws_acc[slot * D + j * 64 + threadIdx.x], num[j]);
   }
-  float* o = out + (int64_t(b) * num_heads + h) * D;
 #pragma unroll
   for (int j = 0; j < D / 64; ++j)
     o[j * 64 + threadIdx.x] = any_nan ? __builtin_nanf("") : num[j] / den;
@@ -1314,14 +1333,17 @@ int32_t run_decode(const void* query, const void* key_new, const void* value_new
 // (at most kStepMaxChanges per launch).
 int32_t make_step_plan(const int32_t* context_lens, const int32_t* changes,
                        int32_t num_changes, int32_t num_seqs, int32_t num_kv_heads,
-                       int32_t max_blocks_per_seq, StepPlan* plan) {
+                       int32_t max_blocks_per_seq, StepPlan* plan,
+                       const int32_t* skipped = nullptr) {
   if (num_seqs > 65535)
     return fail(PKV_ERR_UNSUPPORTED, "at most 65535 sequences per call (got %d)", num_seqs);
   if (num_changes < 0) return fail(PKV_ERR_INVALID, "negative num_changes");
   if (num_seqs > 0 && !context_lens) return fail(PKV_ERR_INVALID, "context_lens is NULL");
   if (num_changes > 0 && !changes) return fail(PKV_ERR_INVALID, "changes is NULL");
   plan->host_lens = context_lens;
-  // Longest first (stable), so long partitions start first; then, within
+  // Longest first (stable), so long partitions start first -- by the tokens
+  // the launch reads, the length less the shared prefix (skipped[i]) in a
+  // shared-prefix step; then, within
   // each round of R = 256 / num_kv_heads sequences -- the sequences whose
   // workgroups one pass of the dispatcher spreads over all 256 CUs -- every
   // other round reversed ("snake"), so the CUs that get a round's longest
@@ -1330,8 +1352,10 @@ int32_t make_step_plan(const int32_t* context_lens, const int32_t* changes,
   // kernel 1% faster than plain longest-first).
   std::vector<int32_t> idx(num_seqs), order(num_seqs), rank_of(num_seqs);
   for (int32_t i = 0; i < num_seqs; ++i) idx[i] = i;
-  std::stable_sort(idx.begin(), idx.end(),
-                   [&](int32_t a, int32_t b) { return context_lens[a] > context_lens[b]; });
+  auto work = [&](int32_t i) {
+    return int64_t(context_lens[i]) - (skipped ? skipped[i] : 0);
+  };
+  std::stable_sort(idx.begin(), idx.end(), [&](int32_t a, int32_t b) { return work(a) > work(b); });
   const int32_t R = std::max(1, 256 / std::max(1, num_kv_heads));
   for (int32_t i = 0; i < num_seqs; ++i) {
     const int32_t k = i / R, j = i % R;
@@ -1551,78 +1575,169 @@ extern "C" int32_t pkv_paged_attention_decode_fp8_partials(
                   workspace, workspace_bytes_given, query_dtype, stream, false);
 }
 
-// ---- decode with a prefix shared by every sequence of the batch ----------
+// ---- decode with prefixes shared by groups of sequences -------------------
 
 namespace {
-// The prefix is split into key ranges of a multiple of 64 keys so that the
-// prefix launch has a workgroup per CU (256) or more; each range is a
-// partial slot (0 .. splits - 1), the suffix partitions follow.
-int32_t shared_prefix_geometry(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
-                               int32_t block_size, int32_t max_context_len, int32_t prefix_len,
-                               int32_t partition_size, int32_t* part, int32_t* splits,
-                               int32_t* split_keys, int32_t* slots) {
+// Checks the host arrays describing the prefix groups and copies them into
+// `out`: group g is rows [group_starts[g], group_starts[g + 1]), sharing
+// prefix_lens[g] tokens (0, or a multiple of block_size up to
+// max_context_len).
+int32_t read_groups(int32_t num_seqs, int32_t num_groups, const int32_t* group_starts,
+                    const int32_t* prefix_lens, int32_t block_size, int32_t max_context_len,
+                    PrefixGroups* out) {
   if (!is_pow2(block_size) || block_size < 16 || block_size > 256)
     return fail(PKV_ERR_UNSUPPORTED, "block_size must be a power of two in [16, 256]");
-  if (prefix_len <= 0 || prefix_len % block_size != 0)
-    return fail(PKV_ERR_INVALID, "prefix_len %d must be a positive multiple of block_size %d",
-                prefix_len, block_size);
-  if (prefix_len > max_context_len)
-    return fail(PKV_ERR_INVALID, "prefix_len %d exceeds max_context_len %d", prefix_len,
-                max_context_len);
-  const int32_t suffix = max_context_len - prefix_len;
-  int32_t st = resolve_partition(partition_size, block_size, num_seqs, num_kv_heads,
-                                 std::max(1, suffix), part);
-  if (st != PKV_OK) return st;
-  const int64_t groups = int64_t(num_heads) *
-                        ((int64_t(num_seqs) + kPrefillRowsPerGroup - 1) / kPrefillRowsPerGroup);
-  const int32_t tiles = (prefix_len + 63) / 64;
-  const int32_t want = int32_t(std::min<int64_t>(tiles, std::max<int64_t>(1, (256 + groups - 1) /
-                                                                                std::max<int64_t>(groups, 1))));
-  *split_keys = ((tiles + want - 1) / want) * 64;
-  *splits = (prefix_len + *split_keys - 1) / *split_keys;
-  *slots = *splits + (suffix + *part - 1) / *part;
-  if (*slots > 65535) return fail(PKV_ERR_UNSUPPORTED, "context too long");
+  if (num_groups < 1) return fail(PKV_ERR_INVALID, "num_groups %d must be positive", num_groups);
+  if (num_groups > kMaxPrefixGroups)
+    return fail(PKV_ERR_UNSUPPORTED, "at most %d prefix groups per call (got %d)",
+                kMaxPrefixGroups, num_groups);
+  if (!group_starts || !prefix_lens) return fail(PKV_ERR_INVALID, "NULL group array");
+  if (group_starts[0] != 0 || group_starts[num_groups] != num_seqs)
+    return fail(PKV_ERR_INVALID, "group_starts must run from 0 to num_seqs %d", num_seqs);
+  out->count = num_groups;
+  for (int32_t g = 0; g <= num_groups; ++g) {
+    if (g > 0 && group_starts[g] < group_starts[g - 1])
+      return fail(PKV_ERR_INVALID, "group_starts must not decrease (group %d)", g - 1);
+    out->start[g] = group_starts[g];
+  }
+  for (int32_t g = 0; g < num_groups; ++g) {
+    const int32_t len = prefix_lens[g];
+    if (len < 0 || len % block_size != 0)
+      return fail(PKV_ERR_INVALID,
+                  "prefix_lens[%d] = %d must be a non-negative multiple of block_size %d", g,
+                  len, block_size);
+    if (len > max_context_len)
+      return fail(PKV_ERR_INVALID, "prefix_lens[%d] = %d exceeds max_context_len %d", g, len,
+                  max_context_len);
+    out->prefix_len[g] = len;
+  }
   return PKV_OK;
 }
-}  // namespace
 
-extern "C" int32_t pkv_paged_attention_decode_shared_prefix_workspace_size(
-    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
-    int32_t block_size, int32_t max_context_len, int32_t prefix_len, int32_t partition_size,
-    size_t* bytes) {
-  if (!bytes) return fail(PKV_ERR_INVALID, "NULL pointer argument");
-  if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0)
-    return fail(PKV_ERR_INVALID, "invalid sizes");
-  int32_t part = 0, splits = 0, split_keys = 0, slots = 0;
-  int32_t st = shared_prefix_geometry(num_seqs, num_heads, num_kv_heads, block_size,
-                                      max_context_len, prefix_len, partition_size, &part,
-                                      &splits, &split_keys, &slots);
+struct PrefixGeometry {
+  int32_t part = 0;        // suffix partition
+  int32_t split_keys = 0;  // keys per prefix split, a multiple of 64
+  int32_t max_splits = 0;  // splits of the longest prefix (slots before the suffix's)
+  int32_t slots = 0;       // partial slots per (row, head)
+};
+
+// Every prefix is split into key ranges of split_keys keys, the same for
+// all groups (so the prefix launch's workgroups carry similar work), long
+// enough that the launch has about a workgroup per CU (256) or more.  A
+// row's slots: its group's prefix splits, then (from max_splits on) its
+// suffix partitions.
+int32_t prefix_geometry(int32_t num_heads, int32_t num_kv_heads, int32_t block_size,
+                        int32_t max_context_len, const PrefixGroups& grp,
+                        int32_t partition_size, PrefixGeometry* geo) {
+  if (!is_pow2(block_size) || block_size < 16 || block_size > 256)
+    return fail(PKV_ERR_UNSUPPORTED, "block_size must be a power of two in [16, 256]");
+  int32_t min_prefix = max_context_len, max_prefix = 0;
+  int64_t tiles = 0;  // row tiles of groups with a prefix
+  for (int32_t g = 0; g < grp.count; ++g) {
+    const int32_t rows = grp.start[g + 1] - grp.start[g];
+    if (rows == 0) continue;
+    min_prefix = std::min(min_prefix, grp.prefix_len[g]);
+    max_prefix = std::max(max_prefix, grp.prefix_len[g]);
+    if (grp.prefix_len[g] > 0) tiles += (rows + kPrefillRowsPerGroup - 1) / kPrefillRowsPerGroup;
+  }
+  const int32_t num_seqs = grp.start[grp.count];
+  const int32_t suffix = max_context_len - std::min(min_prefix, max_prefix);
+  int32_t st = resolve_partition(partition_size, block_size, num_seqs, num_kv_heads,
+                                 std::max(1, suffix), &geo->part);
   if (st != PKV_OK) return st;
-  *bytes = size_t(num_seqs) * num_heads * slots * (size_t(head_dim) + 2) * sizeof(float);
+  if (max_prefix == 0) {
+    geo->split_keys = 64;
+    geo->max_splits = 0;
+  } else {
+    const int64_t pairs = int64_t(num_heads) * tiles;
+    const int32_t key_tiles = (max_prefix + 63) / 64;
+    const int32_t want = int32_t(std::min<int64_t>(key_tiles, std::max<int64_t>(1, (256 + pairs - 1) / pairs)));
+    geo->split_keys = ((key_tiles + want - 1) / want) * 64;
+    geo->max_splits = (max_prefix + geo->split_keys - 1) / geo->split_keys;
+  }
+  geo->slots = std::max(1, geo->max_splits + (suffix + geo->part - 1) / geo->part);
+  if (geo->slots > 65535) return fail(PKV_ERR_UNSUPPORTED, "context too long");
+  return PKV_OK;
+}
+
+// Workspace: [row records: num_seqs * 4 int32][acc: num_seqs * Hq * slots *
+// D floats][(m, l): num_seqs * Hq * slots * 2 floats].
+size_t prefix_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                              int32_t slots) {
+  return size_t(num_seqs) * 4 * sizeof(int32_t) +
+         size_t(num_seqs) * num_heads * slots * (size_t(head_dim) + 2) * sizeof(float);
+}
+
+int32_t grouped_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t block_size, int32_t max_context_len,
+                               int32_t num_groups, const int32_t* group_starts,
+                               const int32_t* prefix_lens, int32_t partition_size,
+                               size_t* bytes) {
+  if (!bytes) return fail(PKV_ERR_INVALID, "NULL pointer argument");
+  if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      max_context_len < 0)
+    return fail(PKV_ERR_INVALID, "invalid sizes");
+  PrefixGroups grp;
+  int32_t st = read_groups(num_seqs, num_groups, group_starts, prefix_lens, block_size,
+                           max_context_len, &grp);
+  if (st != PKV_OK) return st;
+  PrefixGeometry geo;
+  st = prefix_geometry(num_heads, num_kv_heads, block_size, max_context_len, grp,
+                       partition_size, &geo);
+  if (st != PKV_OK) return st;
+  *bytes = prefix_workspace_bytes(num_seqs, num_heads, head_dim, geo.slots);
   return ok();
 }
 
-namespace {
-// The shared-prefix call, with the lengths from the device (step == null)
+// Lengths and groups of a step call checked against the sharing: the step
+// stores each new row past its group's prefix and persists table changes
+// from the suffix kernel, so a new row inside a prefix, or a change to a
+// prefix entry or to a row with no suffix token, would break the sharing or
+// never reach the device table.
+int32_t check_step_against_groups(const PrefixGroups& grp, const int32_t* host_lens,
+                                  bool new_rows, const int32_t* changes, int32_t num_changes,
+                                  int32_t block_size, std::vector<int32_t>* row_prefix) {
+  const int32_t num_seqs = grp.start[grp.count];
+  row_prefix->assign(num_seqs, 0);
+  for (int32_t g = 0; g < grp.count; ++g)
+    for (int32_t r = grp.start[g]; r < grp.start[g + 1]; ++r) (*row_prefix)[r] = grp.prefix_len[g];
+  if (num_seqs > 0 && !host_lens) return fail(PKV_ERR_INVALID, "context_lens is NULL");
+  if (num_changes > 0 && !changes) return fail(PKV_ERR_INVALID, "changes is NULL");
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    const int32_t pre = (*row_prefix)[i];
+    if (new_rows && pre > 0 && host_lens[i] <= pre)
+      return fail(PKV_ERR_INVALID,
+                  "sequence %d: length %d leaves no suffix position for its new row", i,
+                  host_lens[i]);
+  }
+  for (int32_t i = 0; i < num_changes; ++i) {
+    const int32_t row = changes[3 * i], blk = changes[3 * i + 1];
+    if (row < 0 || row >= num_seqs) continue;  // the step plan reports it
+    const int32_t pre = (*row_prefix)[row];
+    if (pre > 0 && (int64_t(blk) * block_size < pre || host_lens[row] <= pre))
+      return fail(PKV_ERR_INVALID,
+                  "table change %d (row %d, index %d) touches a shared prefix", i, row, blk);
+  }
+  return PKV_OK;
+}
+
+// The shared-prefix decode, with the lengths from the device (step == null)
 // or by value with this step's table changes and new K/V rows (step form).
 int32_t shared_prefix_call(const void* query, const void* key_new, const void* value_new,
                            const void* key_cache, const void* value_cache,
                            const int32_t* block_tables, const int32_t* context_lens,
                            int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                            int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
-                           int32_t num_blocks, int32_t max_context_len, int32_t prefix_len,
+                           int32_t num_blocks, int32_t max_context_len, const PrefixGroups& grp,
                            float scale, int32_t partition_size, float* out, void* workspace,
                            size_t workspace_bytes_given, int32_t dtype, void* stream,
-                           const StepPlan* step, const int32_t* changes = nullptr,
-                           int32_t num_changes = 0) {
+                           const StepPlan* step) {
   const bool shared_blocks = (dtype & PKV_DECODE_SHARED_BLOCKS) != 0;
   dtype &= ~int32_t(PKV_DECODE_SHARED_BLOCKS);
   if (dtype != PKV_BF16 && dtype != PKV_F16) {
     if (dtype_bytes(dtype) == 0) return fail(PKV_ERR_INVALID, "unknown dtype %d", dtype);
     return fail(PKV_ERR_UNSUPPORTED, "shared-prefix decode needs a float16 or bfloat16 cache");
   }
-  if (num_seqs < 0) return fail(PKV_ERR_INVALID, "negative num_seqs");
-  if (num_seqs > 65535) return fail(PKV_ERR_UNSUPPORTED, "at most 65535 sequences per call");
   if (num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0)
     return fail(PKV_ERR_INVALID, "num_heads %d must be a positive multiple of num_kv_heads %d",
                 num_heads, num_kv_heads);
@@ -1637,30 +1752,14 @@ int32_t shared_prefix_call(const void* query, const void* key_new, const void* v
   if (int64_t(num_blocks) * block_size >= (int64_t(1) << 31))
     return fail(PKV_ERR_INVALID, "num_blocks * block_size must be below 2^31");
   if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID, "scale must be finite");
-  int32_t part = 0, splits = 0, split_keys = 0, slots = 0;
-  int32_t st = shared_prefix_geometry(num_seqs, num_heads, num_kv_heads, block_size,
-                                      max_context_len, prefix_len, partition_size, &part,
-                                      &splits, &split_keys, &slots);
+  PrefixGeometry geo;
+  int32_t st = prefix_geometry(num_heads, num_kv_heads, block_size, max_context_len, grp,
+                               partition_size, &geo);
   if (st != PKV_OK) return st;
-  if (int64_t(prefix_len) > int64_t(max_blocks_per_seq) * block_size)
-    return fail(PKV_ERR_INVALID, "prefix_len %d exceeds the block table's capacity", prefix_len);
-  if (step) {
-    // The step form stores each new row past the prefix and persists table
-    // changes from the suffix kernel: a new row inside the prefix, or a
-    // change to a prefix entry or to a row with no suffix token, would
-    // break the sharing or never reach the device table.
-    for (int32_t i = 0; i < num_seqs; ++i)
-      if (key_new && step->host_lens[i] <= prefix_len)
-        return fail(PKV_ERR_INVALID,
-                    "sequence %d: length %d leaves no suffix position for its new row", i,
-                    step->host_lens[i]);
-    for (int32_t i = 0; i < num_changes; ++i) {
-      const int32_t row = changes[3 * i], blk = changes[3 * i + 1];
-      if (int64_t(blk) * block_size < prefix_len || step->host_lens[row] <= prefix_len)
-        return fail(PKV_ERR_INVALID,
-                    "table change %d (row %d, index %d) touches the shared prefix", i, row, blk);
-    }
-  }
+  for (int32_t g = 0; g < grp.count; ++g)
+    if (int64_t(grp.prefix_len[g]) > int64_t(max_blocks_per_seq) * block_size)
+      return fail(PKV_ERR_INVALID, "prefix_lens[%d] = %d exceeds the block table's capacity", g,
+                  grp.prefix_len[g]);
   if (num_seqs == 0) return ok();
   if (!query || !key_cache || !value_cache || !block_tables || (!step && !context_lens) || !out)
     return fail(PKV_ERR_INVALID, "NULL pointer argument");
@@ -1671,19 +1770,21 @@ int32_t shared_prefix_call(const void* query, const void* key_new, const void* v
     if (!aligned16(key_new) || !aligned16(value_new))
       return fail(PKV_ERR_INVALID, "key and value must be 16-byte aligned");
   }
-  const size_t need = size_t(num_seqs) * num_heads * slots * (size_t(head_dim) + 2) * sizeof(float);
+  const size_t need = prefix_workspace_bytes(num_seqs, num_heads, head_dim, geo.slots);
   if (!workspace || workspace_bytes_given < need)
     return fail(PKV_ERR_BUFFER_TOO_SMALL, "workspace needs %zu bytes, got %zu", need,
                 workspace ? workspace_bytes_given : size_t(0));
   if (!aligned16(workspace)) return fail(PKV_ERR_INVALID, "workspace must be 16-byte aligned");
-  float* ws_acc = static_cast<float*>(workspace);
-  float* ws_ml = ws_acc + size_t(num_seqs) * num_heads * slots * head_dim;
+  int32_t* row_info = static_cast<int32_t*>(workspace);
+  float* ws_acc = reinterpret_cast<float*>(row_info + size_t(num_seqs) * 4);
+  float* ws_ml = ws_acc + size_t(num_seqs) * num_heads * geo.slots * head_dim;
 
-  // 1. every query against the shared prefix, on the matrix cores
+  // 1. every query against its group's prefix, on the matrix cores (also
+  // every row's record: prefix length, the group's first row, prefix slots)
   hipError_t e = static_cast<hipError_t>(launch_prefix_partials(
-      dtype, query, key_cache, value_cache, block_tables, num_seqs, num_heads, num_kv_heads,
-      block_size, max_blocks_per_seq, num_blocks, prefix_len, splits, split_keys, scale, ws_acc,
-      ws_ml, slots, stream));
+      dtype, query, key_cache, value_cache, block_tables, grp, num_heads, num_kv_heads,
+      block_size, max_blocks_per_seq, num_blocks, geo.split_keys, geo.max_splits, scale, ws_acc,
+      ws_ml, row_info, geo.slots, stream));
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "prefix launch: %s", hipGetErrorString(e));
 
   // 2. each sequence's private suffix, split-K, partials after the prefix's
@@ -1704,14 +1805,14 @@ int32_t shared_prefix_call(const void* query, const void* key_new, const void* v
   prm.max_blocks = max_blocks_per_seq;
   prm.num_blocks = num_blocks;
   prm.max_ctx = max_context_len;
-  prm.part = part;
-  prm.max_parts = slots;                         // workspace slots per row
-  prm.grid_parts = std::max(1, slots - splits);  // suffix partitions
+  prm.part = geo.part;
+  prm.max_parts = geo.slots;                                // workspace slots per row
+  prm.grid_parts = std::max(1, geo.slots - geo.max_splits);  // suffix partitions
   prm.scale_log2 = scale * kLog2e;
   prm.v_scale = 1.0f;
   prm.shared_blocks = shared_blocks ? 1 : 0;
-  prm.start = prefix_len;
-  prm.slot_base = splits;
+  prm.row_info = row_info;
+  prm.slot_base = geo.max_splits;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (step) {
     for (size_t c = 0; c < step->chunks.size() && e == hipSuccess; ++c)
@@ -1731,7 +1832,59 @@ int32_t shared_prefix_call(const void* query, const void* key_new, const void* v
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "decode merge launch: %s", hipGetErrorString(e));
   return ok();
 }
+
+int32_t grouped_call(const void* query, const void* key, const void* value,
+                     const void* key_cache, const void* value_cache, const int32_t* block_tables,
+                     const int32_t* context_lens, const int32_t* changes, int32_t num_changes,
+                     int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                     int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+                     int32_t max_context_len, int32_t num_groups, const int32_t* group_starts,
+                     const int32_t* prefix_lens, float scale, int32_t partition_size,
+                     float* out, void* workspace, size_t workspace_bytes_given, int32_t dtype,
+                     void* stream, bool step_form) {
+  if (num_seqs < 0) return fail(PKV_ERR_INVALID, "negative num_seqs");
+  if (num_seqs > 65535) return fail(PKV_ERR_UNSUPPORTED, "at most 65535 sequences per call");
+  if (!is_pow2(block_size) || block_size < 16 || block_size > 256)
+    return fail(PKV_ERR_UNSUPPORTED, "block_size must be a power of two in [16, 256]");
+  if (max_context_len < 0) return fail(PKV_ERR_INVALID, "negative max_context_len");
+  PrefixGroups grp;
+  int32_t st = read_groups(num_seqs, num_groups, group_starts, prefix_lens, block_size,
+                           max_context_len, &grp);
+  if (st != PKV_OK) return st;
+  if (!step_form)
+    return shared_prefix_call(query, nullptr, nullptr, key_cache, value_cache, block_tables,
+                              context_lens, num_seqs, num_heads, num_kv_heads, head_dim,
+                              block_size, max_blocks_per_seq, num_blocks, max_context_len, grp,
+                              scale, partition_size, out, workspace, workspace_bytes_given, dtype,
+                              stream, nullptr);
+  if (num_changes < 0) return fail(PKV_ERR_INVALID, "negative num_changes");
+  std::vector<int32_t> row_prefix;
+  st = check_step_against_groups(grp, context_lens, key != nullptr, changes, num_changes,
+                                 block_size, &row_prefix);
+  if (st != PKV_OK) return st;
+  StepPlan plan;
+  st = make_step_plan(context_lens, changes, num_changes, num_seqs, num_kv_heads,
+                      max_blocks_per_seq, &plan, row_prefix.data());
+  if (st != PKV_OK) return st;
+  return shared_prefix_call(query, key, value, key_cache, value_cache, block_tables, nullptr,
+                            num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                            max_blocks_per_seq, num_blocks, max_context_len, grp, scale,
+                            partition_size, out, workspace, workspace_bytes_given, dtype, stream,
+                            &plan);
+}
 }  // namespace
+
+extern "C" int32_t pkv_paged_attention_decode_shared_prefix_workspace_size(
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int32_t max_context_len, int32_t prefix_len, int32_t partition_size,
+    size_t* bytes) {
+  if (prefix_len <= 0)
+    return fail(PKV_ERR_INVALID, "prefix_len %d must be a positive multiple of block_size %d",
+                prefix_len, block_size);
+  const int32_t starts[2] = {0, num_seqs};
+  return grouped_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                                max_context_len, 1, starts, &prefix_len, partition_size, bytes);
+}
 
 extern "C" int32_t pkv_paged_attention_decode_shared_prefix(
     const void* query, const void* key_cache, const void* value_cache,
@@ -1740,11 +1893,15 @@ extern "C" int32_t pkv_paged_attention_decode_shared_prefix(
     int32_t max_blocks_per_seq, int32_t num_blocks, int32_t max_context_len,
     int32_t prefix_len, float scale, int32_t partition_size, float* out, void* workspace,
     size_t workspace_bytes_given, int32_t dtype, void* stream) {
-  return shared_prefix_call(query, nullptr, nullptr, key_cache, value_cache, block_tables,
-                            context_lens, num_seqs, num_heads, num_kv_heads, head_dim,
-                            block_size, max_blocks_per_seq, num_blocks, max_context_len,
-                            prefix_len, scale, partition_size, out, workspace,
-                            workspace_bytes_given, dtype, stream, nullptr);
+  if (prefix_len <= 0)
+    return fail(PKV_ERR_INVALID, "prefix_len %d must be a positive multiple of block_size %d",
+                prefix_len, block_size);
+  const int32_t starts[2] = {0, std::max(num_seqs, 0)};
+  return grouped_call(query, nullptr, nullptr, key_cache, value_cache, block_tables,
+                      context_lens, nullptr, 0, num_seqs, num_heads, num_kv_heads, head_dim,
+                      block_size, max_blocks_per_seq, num_blocks, max_context_len, 1, starts,
+                      &prefix_len, scale, partition_size, out, workspace, workspace_bytes_given,
+                      dtype, stream, false);
 }
 
 extern "C" int32_t pkv_paged_attention_decode_shared_prefix_step(
@@ -1755,15 +1912,56 @@ extern "C" int32_t pkv_paged_attention_decode_shared_prefix_step(
     int32_t num_blocks, int32_t max_context_len, int32_t prefix_len, float scale,
     int32_t partition_size, float* out, void* workspace, size_t workspace_bytes_given,
     int32_t dtype, void* stream) {
-  StepPlan plan;
-  int32_t st = make_step_plan(context_lens, changes, num_changes, num_seqs, num_kv_heads,
-                              max_blocks_per_seq, &plan);
-  if (st != PKV_OK) return st;
-  return shared_prefix_call(query, key, value, key_cache, value_cache, block_tables, nullptr,
-                            num_seqs, num_heads, num_kv_heads, head_dim, block_size,
-                            max_blocks_per_seq, num_blocks, max_context_len, prefix_len, scale,
-                            partition_size, out, workspace, workspace_bytes_given, dtype, stream,
-                            &plan, changes, num_changes);
+  if (prefix_len <= 0)
+    return fail(PKV_ERR_INVALID, "prefix_len %d must be a positive multiple of block_size %d",
+                prefix_len, block_size);
+  const int32_t starts[2] = {0, std::max(num_seqs, 0)};
+  return grouped_call(query, key, value, key_cache, value_cache, block_tables, context_lens,
+                      changes, num_changes, num_seqs, num_heads, num_kv_heads, head_dim,
+                      block_size, max_blocks_per_seq, num_blocks, max_context_len, 1, starts,
+                      &prefix_len, scale, partition_size, out, workspace, workspace_bytes_given,
+                      dtype, stream, true);
+}
+
+extern "C" int32_t pkv_paged_attention_decode_grouped_prefix_workspace_size(
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int32_t max_context_len, int32_t num_groups,
+    const int32_t* group_starts, const int32_t* prefix_lens, int32_t partition_size,
+    size_t* bytes) {
+  return grouped_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                                max_context_len, num_groups, group_starts, prefix_lens,
+                                partition_size, bytes);
+}
+
+extern "C" int32_t pkv_paged_attention_decode_grouped_prefix(
+    const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t max_blocks_per_seq, int32_t num_blocks, int32_t max_context_len,
+    int32_t num_groups, const int32_t* group_starts, const int32_t* prefix_lens, float scale,
+    int32_t partition_size, float* out, void* workspace, size_t workspace_bytes_given,
+    int32_t dtype, void* stream) {
+  return grouped_call(query, nullptr, nullptr, key_cache, value_cache, block_tables,
+                      context_lens, nullptr, 0, num_seqs, num_heads, num_kv_heads, head_dim,
+                      block_size, max_blocks_per_seq, num_blocks, max_context_len, num_groups,
+                      group_starts, prefix_lens, scale, partition_size, out, workspace,
+                      workspace_bytes_given, dtype, stream, false);
+}
+
+extern "C" int32_t pkv_paged_attention_decode_grouped_prefix_step(
+    const void* query, const void* key, const void* value, void* key_cache,
+    void* value_cache, int32_t* block_tables, const int32_t* context_lens,
+    const int32_t* changes, int32_t num_changes, int32_t num_seqs, int32_t num_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+    int32_t num_blocks, int32_t max_context_len, int32_t num_groups,
+    const int32_t* group_starts, const int32_t* prefix_lens, float scale,
+    int32_t partition_size, float* out, void* workspace, size_t workspace_bytes_given,
+    int32_t dtype, void* stream) {
+  return grouped_call(query, key, value, key_cache, value_cache, block_tables, context_lens,
+                      changes, num_changes, num_seqs, num_heads, num_kv_heads, head_dim,
+                      block_size, max_blocks_per_seq, num_blocks, max_context_len, num_groups,
+                      group_starts, prefix_lens, scale, partition_size, out, workspace,
+                      workspace_bytes_given, dtype, stream, true);
 }
 
 // ---- decode with no allocation at all: split-K partials in a fixed array --

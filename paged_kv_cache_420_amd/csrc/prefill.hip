@@ -36,6 +36,7 @@
 // contents never reach an output.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 
 #include "common.h"
@@ -141,21 +142,25 @@ constexpr float kRescaleSlack = 8.0f;
 // V tile through the LDS transpose read, so V needs no transposition in
 // registers.
 // Shared-prefix mode (kPrefix): the rows are the decode queries of a batch
-// whose sequences all begin with the same prefix_len tokens (reached
-// through row 0 of the block table).  Every row attends to the whole
-// prefix -- no causal limit -- and the result is left unnormalised, as a
-// split-K partial in slot 0 of the decode workspace ([rows][heads][slots]
-// of head_dim floats, and [rows][heads][slots][2] of (max, sum) in log2
-// units), for the decode merge to combine with the private suffixes.
+// made of prefix groups -- consecutive rows forked from one parent, whose
+// sequences all begin with the group's prefix_len tokens (reached through
+// the table of the group's first row).  Every row attends to its group's
+// whole prefix -- no causal limit -- and the result is left unnormalised,
+// as split-K partials in the first slots of the decode workspace
+// ([rows][heads][slots] of head_dim floats, and [rows][heads][slots][2] of
+// (max, sum) in log2 units), for the decode merge to combine with the
+// private suffixes.  A row tile (blockIdx.y) lies in one group.
 struct PrefixArgs {
   float* ws_acc;
   float* ws_ml;
-  int32_t rows;        // decode queries (one per sequence)
-  int32_t prefix_len;  // tokens, a multiple of the block size
+  int32_t* row_info;   // [rows][4]: prefix_len, first row of the group,
+                       // prefix slots, 0 (written by split 0 of head 0)
   int32_t slots;       // partials per (row, head) in the workspace
-  int32_t split_keys;  // keys per split of the prefix (a multiple of 64):
+  int32_t split_keys;  // keys per split of a prefix (a multiple of 64):
                        // split z = blockIdx.z takes keys [z, z + 1) *
-                       // split_keys and writes slot z
+                       // split_keys of its group's prefix and writes slot z
+  int32_t tile_base[kMaxPrefixGroups + 1];  // first row tile of each group
+  PrefixGroups groups;
 };
 
 template <int DT, bool kPrefix>
@@ -174,8 +179,20 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
   const int h = (num_heads & 7) == 0
                     ? (blockIdx.x & 7) * xcd_slice + (blockIdx.x >> 3)
                     : blockIdx.x;
-  const int qt = blockIdx.y;
-  const int b = kPrefix ? 0 : blockIdx.z;
+  // Shared-prefix mode: the row tile's group is the last g whose first
+  // tile is at or before blockIdx.y (groups with no rows have no tiles)
+  int g = 0;
+  if constexpr (kPrefix) {
+    int hi = pfx.groups.count - 1;
+    while (g < hi) {
+      const int mid = (g + hi + 1) >> 1;
+      if (pfx.tile_base[mid] <= int(blockIdx.y)) g = mid;
+      else hi = mid - 1;
+    }
+  }
+  const int qt = kPrefix ? int(blockIdx.y) - pfx.tile_base[g] : int(blockIdx.y);
+  // the group's first row reaches the prefix through its table
+  const int b = kPrefix ? pfx.groups.start[g] : blockIdx.z;
   const int split = kPrefix ? blockIdx.z : 0;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -184,14 +201,24 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
   const int num_kv_heads = num_heads / group;
   const int bs = 1 << log2_bs;
 
-  const int q0 = kPrefix ? 0 : cu_query_lens[b];
-  const int q1 = kPrefix ? pfx.rows : cu_query_lens[b + 1];
+  const int q0 = kPrefix ? pfx.groups.start[g] : cu_query_lens[b];
+  const int q1 = kPrefix ? pfx.groups.start[g + 1] : cu_query_lens[b + 1];
   if (q0 < 0 || q1 < q0 || q1 > total_q) return;  // rows unknown: nothing written
   const int c = q1 - q0;
   const int r0 = qt * kQTile;
   if (r0 >= c) return;
-  const int n = kPrefix ? pfx.prefix_len : context_lens[b];
+  const int n = kPrefix ? pfx.groups.prefix_len[g] : context_lens[b];
   const int rows_here = min(kQTile, c - r0);
+  if constexpr (kPrefix) {
+    // each row's record for the suffix and merge launches, then only the
+    // splits the group's prefix has do work (none for a group with no prefix)
+    const int prefix_splits = (n + pfx.split_keys - 1) / pfx.split_keys;
+    if (blockIdx.x == 0 && split == 0)
+      for (int i = tid; i < rows_here; i += kThreads)
+        *reinterpret_cast<int4*>(pfx.row_info + int64_t(q0 + r0 + i) * 4) =
+            make_int4(n, q0, prefix_splits, 0);
+    if (split >= prefix_splits) return;
+  }
 
   const bool bad_len = kPrefix ? int64_t(n) > (int64_t(max_blocks) << log2_bs)
                                : c > n || c > max_q ||
@@ -200,7 +227,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
     if (bad_len) {  // rows NaN through their prefix partials
       const float nan = __builtin_nanf("");
       for (int i = tid; i < rows_here * kD; i += kThreads) {
-        const int64_t row = (int64_t(r0 + i / kD) * num_heads + h) * pfx.slots + split;
+        const int64_t row = (int64_t(q0 + r0 + i / kD) * num_heads + h) * pfx.slots + split;
         pfx.ws_acc[row * kD + (i % kD)] = nan;
         if (i % kD == 0) pfx.ws_ml[row * 2] = pfx.ws_ml[row * 2 + 1] = nan;
       }
@@ -471,10 +498,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
     const int i = r0 + 32 * wave + 16 * qg + col;
     if (i >= c) continue;
     if constexpr (kPrefix) {
-      // unnormalised partial in slot 0, with the row's running max (log2
-      // units, the scale applied) and its sum
+      // unnormalised partial in the split's slot, with the row's running
+      // max (log2 units, the scale applied) and its sum
       const float nan = __builtin_nanf("");
-      const int64_t prow = (int64_t(i) * num_heads + h) * pfx.slots + split;
+      const int64_t prow = (int64_t(q0 + i) * num_heads + h) * pfx.slots + split;
       float* acc = pfx.ws_acc + prow * kD;
 #pragma unroll
       for (int dt = 0; dt < kD / 16; ++dt)
@@ -557,23 +584,36 @@ extern "C" int32_t pkv_paged_attention_prefill(
   return ok();
 }
 
-// The shared-prefix part of pkv_paged_attention_decode_shared_prefix: the
-// prefill kernel in shared-prefix mode over `rows` decode queries
-// ([rows][num_heads][128]), the prefix reached through row 0 of
-// block_tables and split into `splits` key ranges of `split_keys` keys,
-// partials into slots 0 .. splits - 1 of the decode workspace.  Arguments
-// are checked by the caller.
+// The prefix part of the shared-prefix decode: the prefill kernel in
+// shared-prefix mode over the decode queries ([rows][num_heads][128]) of
+// every group, grid (query head, row tiles of all groups, key ranges).
+// Arguments are checked by the caller.
 int pkv::launch_prefix_partials(int32_t dtype, const void* query, const void* key_cache,
                                 const void* value_cache, const int32_t* block_tables,
-                                int32_t rows, int32_t num_heads, int32_t num_kv_heads,
-                                int32_t block_size, int32_t max_blocks_per_seq,
-                                int32_t num_blocks, int32_t prefix_len, int32_t splits,
-                                int32_t split_keys, float scale, float* ws_acc, float* ws_ml,
-                                int32_t slots, void* stream) {
+                                const PrefixGroups& groups, int32_t num_heads,
+                                int32_t num_kv_heads, int32_t block_size,
+                                int32_t max_blocks_per_seq, int32_t num_blocks,
+                                int32_t split_keys, int32_t max_splits, float scale,
+                                float* ws_acc, float* ws_ml, int32_t* row_info, int32_t slots,
+                                void* stream) {
   int log2_bs = 0;
   while ((1 << log2_bs) < block_size) ++log2_bs;
-  const PrefixArgs pfx{ws_acc, ws_ml, rows, prefix_len, slots, split_keys};
-  const dim3 grid(num_heads, unsigned((rows + kQTile - 1) / kQTile), unsigned(splits));
+  PrefixArgs pfx{};
+  pfx.ws_acc = ws_acc;
+  pfx.ws_ml = ws_ml;
+  pfx.row_info = row_info;
+  pfx.slots = slots;
+  pfx.split_keys = split_keys;
+  pfx.groups = groups;
+  int tiles = 0;
+  for (int g = 0; g < groups.count; ++g) {
+    pfx.tile_base[g] = tiles;
+    tiles += (groups.start[g + 1] - groups.start[g] + kQTile - 1) / kQTile;
+  }
+  pfx.tile_base[groups.count] = tiles;
+  const int32_t rows = groups.start[groups.count];
+  if (tiles == 0) return static_cast<int>(hipSuccess);
+  const dim3 grid(num_heads, unsigned(tiles), unsigned(std::max(1, max_splits)));
   const int group = num_heads / num_kv_heads;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const auto* q = static_cast<const uint16_t*>(query);

@@ -406,16 +406,17 @@ def test_shared_prefix_decode_checks_its_arguments_before_launch():
     # shared-prefix batch geometry: 256 sequences, 32 heads, prefix 1024 in
     # blocks of 16, contexts up to 3000: 8 prefix ranges of 128 keys (a
     # workgroup per CU) + one 2048-token suffix partition; up to 3100, two
+    # (the workspace starts with a 16-byte record per sequence)
     assert lib.pkv_paged_attention_decode_shared_prefix_workspace_size(
         256, 32, 32, 128, 16, 3000, 1024, 0, ctypes.byref(ws)) == 0
-    assert ws.value == 256 * 32 * (8 + 1) * (128 + 2) * 4
+    assert ws.value == 256 * 16 + 256 * 32 * (8 + 1) * (128 + 2) * 4
     assert lib.pkv_paged_attention_decode_shared_prefix_workspace_size(
         256, 32, 32, 128, 16, 3100, 1024, 0, ctypes.byref(ws)) == 0
-    assert ws.value == 256 * 32 * (8 + 2) * (128 + 2) * 4
+    assert ws.value == 256 * 16 + 256 * 32 * (8 + 2) * (128 + 2) * 4
     # one 64-key range when the prefix is one tile
     assert lib.pkv_paged_attention_decode_shared_prefix_workspace_size(
         4, 4, 4, 128, 16, 300, 64, 64, ctypes.byref(ws)) == 0
-    assert ws.value == 4 * 4 * (1 + 4) * (128 + 2) * 4
+    assert ws.value == 4 * 16 + 4 * 4 * (1 + 4) * (128 + 2) * 4
     # prefix not a multiple of the block size, longer than the contexts
     assert lib.pkv_paged_attention_decode_shared_prefix_workspace_size(
         4, 4, 4, 128, 16, 300, 72, 0, ctypes.byref(ws)) == 1
@@ -439,3 +440,67 @@ def test_shared_prefix_decode_checks_its_arguments_before_launch():
     assert lib.pkv_paged_attention_decode_shared_prefix(*args, 0, 4, 4, 128, 16, 32, 64, 300,
                                                         64, 1.0, 0, null, null, 0, 2,
                                                         null) == 0
+
+
+def test_grouped_prefix_decode_checks_its_arguments_before_launch():
+    lib = pkv._lib
+    null = None
+    ws = ctypes.c_size_t()
+
+    def arr(xs):
+        return (ctypes.c_int32 * len(xs))(*xs)
+
+    # four groups of 64 of 256 sequences, prefixes 1024/512/1536/768,
+    # contexts up to 3600: four row tiles x 32 heads = 128 (head, tile)
+    # pairs, so 2 key ranges for the longest prefix (24 tiles of 64 keys ->
+    # ranges of 768 keys; every prefix needs at most 2); suffixes up to
+    # 3600 - 512 = 3088 tokens in 2048-token partitions: 2 + 2 slots
+    starts, plens = arr([0, 64, 128, 192, 256]), arr([1024, 512, 1536, 768])
+    assert lib.pkv_paged_attention_decode_grouped_prefix_workspace_size(
+        256, 32, 32, 128, 16, 3600, 4, starts, plens, 0, ctypes.byref(ws)) == 0
+    assert ws.value == 256 * 16 + 256 * 32 * (2 + 2) * (128 + 2) * 4
+    # no prefix anywhere: no prefix slot, suffixes from token 0
+    assert lib.pkv_paged_attention_decode_grouped_prefix_workspace_size(
+        8, 4, 4, 128, 16, 300, 2, arr([0, 3, 8]), arr([0, 0]), 64, ctypes.byref(ws)) == 0
+    assert ws.value == 8 * 16 + 8 * 4 * 5 * (128 + 2) * 4
+    # bad groups: no group, too many, not starting at 0, not ending at
+    # num_seqs, decreasing, a prefix off the block grid or past the contexts
+    assert lib.pkv_paged_attention_decode_grouped_prefix_workspace_size(
+        8, 4, 4, 128, 16, 300, 0, arr([0]), arr([0]), 0, ctypes.byref(ws)) == 1
+    assert lib.pkv_paged_attention_decode_grouped_prefix_workspace_size(
+        8, 4, 4, 128, 16, 300, 129, arr([0] * 129 + [8]), arr([0] * 129), 0,
+        ctypes.byref(ws)) == 7
+    for s_, p_ in (([1, 3, 8], [16, 32]), ([0, 3, 7], [16, 32]), ([0, 5, 3, 8], [16, 32, 0]),
+                   ([0, 3, 8], [24, 32]), ([0, 3, 8], [16, 320]), ([0, 3, 8], [-16, 32])):
+        assert lib.pkv_paged_attention_decode_grouped_prefix_workspace_size(
+            8, 4, 4, 128, 16, 300, len(p_), arr(s_), arr(p_), 0, ctypes.byref(ws)) == 1, (s_, p_)
+    assert lib.pkv_paged_attention_decode_grouped_prefix_workspace_size(
+        8, 4, 4, 128, 16, 300, 2, null, arr([0, 0]), 0, ctypes.byref(ws)) == 1
+    # block size 8 is not served by the matrix-core part
+    assert lib.pkv_paged_attention_decode_grouped_prefix_workspace_size(
+        8, 4, 4, 128, 8, 300, 2, arr([0, 3, 8]), arr([16, 32]), 0, ctypes.byref(ws)) == 7
+    args = (null, null, null, null, null)
+    g = (2, arr([0, 3, 8]), arr([16, 32]))
+    # float32 caches are not served; NULL pointers are caught; an empty
+    # batch does nothing
+    assert lib.pkv_paged_attention_decode_grouped_prefix(*args, 8, 4, 4, 128, 16, 32, 64, 300,
+                                                         *g, 1.0, 0, null, null, 0, 0,
+                                                         null) == 7
+    assert lib.pkv_paged_attention_decode_grouped_prefix(*args, 8, 4, 4, 128, 16, 32, 64, 300,
+                                                         *g, 1.0, 0, null, null, 0, 2,
+                                                         null) == 1
+    assert lib.pkv_paged_attention_decode_grouped_prefix(*args, 0, 4, 4, 128, 16, 32, 64, 300,
+                                                         1, arr([0, 0]), arr([16]), 1.0, 0, null,
+                                                         null, 0, 2, null) == 0
+    # step form: a new row inside a group's prefix, a change to a prefix
+    # entry, both rejected before any launch (NULL device pointers here)
+    lens = arr([20, 30, 40, 50, 60, 70, 80, 90])
+    kv = ctypes.c_void_p(16)   # never dereferenced: the host checks fail first
+    assert lib.pkv_paged_attention_decode_grouped_prefix_step(
+        null, kv, kv, null, null, null, arr([16] + [20] * 7), null, 0, 8, 4, 4, 128, 16, 32, 64,
+        300, *g, 1.0, 0, null, null, 0, 2, null) == 1
+    assert b"no suffix position" in lib.pkv_last_error()
+    assert lib.pkv_paged_attention_decode_grouped_prefix_step(
+        null, null, null, null, null, null, lens, arr([4, 1, 7]), 1, 8, 4, 4, 128, 16, 32, 64,
+        300, *g, 1.0, 0, null, null, 0, 2, null) == 1
+    assert b"shared prefix" in lib.pkv_last_error()

@@ -19,7 +19,9 @@ Recipe (per configuration, ``seed`` fixed):
   3. The schedule adds each sequence and appends its tokens in index order;
      the shared-prefix configuration first fills a 1024-token prefix
      sequence, forks every sequence from it, frees the prefix sequence,
-     then appends each private suffix.
+     then appends each private suffix.  The grouped-prefix configuration
+     does the same per group (consecutive sequences, equal group sizes, the
+     last group smaller), group by group, then appends every suffix.
   4. The K/V rows of append op number i come from
      default_rng([seed, 1, i]); queries of sequence b from
      default_rng([seed, 2, b]) (decode) or default_rng([seed, 3, b])
@@ -53,6 +55,7 @@ class Workload:
     partition_size: int = 0    # split-K partition for decode (0 = library default)
     prefix: int = 0            # shared prefix tokens (shared-prefix workload)
     chunk: int = 0             # chunked-prefill rows per sequence
+    prefix_groups: tuple = ()  # per-group prefix tokens (grouped-prefix workload)
 
     @property
     def scale(self):
@@ -74,6 +77,10 @@ WORKLOADS = {
                          "uniform:512,8192", partition_size=512),
     "shared_prefix_bf16": Workload("shared_prefix_bf16", 256, 32, 32, 128, 16, torch.bfloat16,
                                    1.0, 4205, "uniform:10,2000", prefix=1024, chunk=512),
+    # the shared-prefix batch as four prompts with 64 samples each
+    "grouped_prefix_bf16": Workload("grouped_prefix_bf16", 256, 32, 32, 128, 16,
+                                    torch.bfloat16, 1.0, 4207, "uniform:10,2000",
+                                    prefix_groups=(1024, 512, 1536, 768)),
 }
 
 
@@ -107,6 +114,31 @@ def draw_lengths(w, rng):
     raise ValueError(w.lens)
 
 
+def prefix_layout(w):
+    """(group_starts, prefix_lens) of the batch's prefix groups -- group g is
+    sequences group_starts[g] .. group_starts[g + 1] - 1, sharing their
+    first prefix_lens[g] tokens -- or None when nothing is shared."""
+    if w.prefix_groups:
+        n = len(w.prefix_groups)
+        size = -(-w.num_seqs // n)
+        starts = [min(g * size, w.num_seqs) for g in range(n)] + [w.num_seqs]
+        return starts, list(w.prefix_groups)
+    if w.prefix:
+        return [0, w.num_seqs], [w.prefix]
+    return None
+
+
+def seq_prefixes(w):
+    """Shared-prefix tokens of each sequence (int64 [num_seqs])."""
+    out = np.zeros(w.num_seqs, dtype=np.int64)
+    layout = prefix_layout(w)
+    if layout:
+        starts, lens = layout
+        for g, n in enumerate(lens):
+            out[starts[g]:starts[g + 1]] = n
+    return out
+
+
 @dataclasses.dataclass
 class Plan:
     workload: Workload
@@ -120,7 +152,7 @@ class Plan:
 def plan(w):
     rng = np.random.default_rng(w.seed)
     lens = draw_lengths(w, rng)
-    per_seq_final = lens + w.prefix + w.chunk
+    per_seq_final = lens + seq_prefixes(w) + w.chunk
     nb = w.num_blocks or 2 * int(sum(-(-int(n) // w.block_size) for n in per_seq_final))
     order = rng.permutation(nb).astype(np.int32)
     ops = []
@@ -129,6 +161,14 @@ def plan(w):
         ops += [("add", PREFIX_SEQ), ("append", PREFIX_SEQ, w.prefix)]
         ops += [("fork", PREFIX_SEQ, s) for s in seqs]
         ops += [("free", PREFIX_SEQ)]
+        ops += [("append", s, int(n)) for s, n in zip(seqs, lens)]
+    elif w.prefix_groups:
+        starts, plens = prefix_layout(w)
+        for g, n in enumerate(plens):
+            parent = PREFIX_SEQ + g
+            ops += [("add", parent)] + ([("append", parent, n)] if n else [])
+            ops += [("fork", parent, s) for s in seqs[starts[g]:starts[g + 1]]]
+            ops += [("free", parent)]
         ops += [("append", s, int(n)) for s, n in zip(seqs, lens)]
     else:
         for s, n in zip(seqs, lens):
