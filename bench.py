@@ -667,10 +667,12 @@ def fp8_leg(args, torch, pkv, workloads):
 
 def serve_leg(args, torch, pkv, workloads):
     """The serving trace (all requests queued at the start) run to the end
-    through the step driver, twice on the same pool: paged admission, and
-    the reservation model (every running request holds room for the
-    longest request the length laws allow, as a contiguous per-request
-    cache must).  Reports steps, wall time, generated and prompt tokens per
+    through the step driver on the same pool: paged admission, and the
+    reservation model (every running request holds room for the longest
+    request the length laws allow, as a contiguous per-request cache must);
+    paged admission once more with the decode rows' full tables uploaded
+    every step (the driver's decode="upload") instead of kept in
+    device-resident lanes and changed by value (decode="step").  Reports steps, wall time, generated and prompt tokens per
     second, the mean running set, and the mean over steps of slot
     utilisation (cached tokens / slots held by the running requests) next
     to reservation utilisation (cached tokens / slots reserved)."""
@@ -695,12 +697,13 @@ def serve_leg(args, torch, pkv, workloads):
 
     order = np.random.default_rng(t.seed).permutation(t.num_blocks).astype(np.int32)
     res = {}
-    for policy, rt in (("paged", 0), ("reservation", reserve)):
+    for policy, rt, mode in (("paged", 0, "step"), ("reservation", reserve, "step"),
+                             ("paged_upload", 0, "upload")):
         sched = pkv.Scheduler(t.num_blocks, t.block_size, t.max_num_seqs,
                               t.max_num_batched_tokens, t.chunk_size, rt, order)
         for rid, p, o in reqs:
             sched.add_request(rid, p, o)
-        drv = ServingDriver(sched, kc, vc, t.num_heads, t.scale, reserve)
+        drv = ServingDriver(sched, kc, vc, t.num_heads, t.scale, reserve, decode=mode)
         util, rutil, running, dec_rows, pre_tok = [], [], [], 0, 0
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -720,7 +723,7 @@ def serve_leg(args, torch, pkv, workloads):
         st = sched.stats()
         if st["finished"] != len(reqs):
             raise RuntimeError(f"{policy}: {st['finished']} of {len(reqs)} requests finished")
-        res[policy] = {"steps": st["steps"], "wall_s": round(wall, 3),
+        res[policy] = {"decode": mode, "steps": st["steps"], "wall_s": round(wall, 3),
                        "ms_per_step": round(wall / st["steps"] * 1e3, 4),
                        "generated_tokens_per_s": round(dec_rows / wall, 1),
                        "prompt_tokens_per_s": round(pre_tok / wall, 1),
@@ -739,7 +742,9 @@ def serve_leg(args, torch, pkv, workloads):
         "max_num_seqs": t.max_num_seqs, "max_num_batched_tokens": t.max_num_batched_tokens,
         "chunk_size": t.chunk_size, "policies": res,
         "generated_tokens_per_s_ratio": round(res["paged"]["generated_tokens_per_s"] /
-                                              res["reservation"]["generated_tokens_per_s"], 3)}),
+                                              res["reservation"]["generated_tokens_per_s"], 3),
+        "step_decode_vs_upload_ms_per_step": [res["paged"]["ms_per_step"],
+                                              res["paged_upload"]["ms_per_step"]]}),
         flush=True)
 
 

@@ -562,18 +562,41 @@ int32_t pkv_paged_attention_decode_append_partials(
  *   key, value     [num_seqs][num_kv_heads][head_dim] new rows, or both
  *                  NULL for no append
  * The metadata rides in kernel arguments: one launch of each kernel serves
- * 256 sequences of the work order (longest first), so a larger batch takes
- * ceil(num_seqs / 256) launches of each.  Limits: num_seqs <= 65535; the
- * changes of the sequences one launch serves at most 256
- * (PKV_ERR_UNSUPPORTED beyond) -- a step of one token per sequence makes
- * at most one change per sequence, always within it.  Other arguments,
- * semantics and errors as pkv_paged_attention_decode_append. */
+ * at most 256 sequences of the work order (longest first) and their
+ * changes, at most 192; a larger batch, or one with more changes, takes
+ * more launches of each (consecutive ranks of the work order).  Limits:
+ * num_seqs <= 65535; at most 192 changes per sequence (PKV_ERR_UNSUPPORTED
+ * beyond) -- a step of one token per sequence makes at most one.  Other
+ * arguments, semantics and errors as pkv_paged_attention_decode_append. */
 int32_t pkv_paged_attention_decode_step(
     const void* query, const void* key, const void* value, void* key_cache,
     void* value_cache, int32_t* block_tables, const int32_t* context_lens,
     const int32_t* changes, int32_t num_changes, int32_t num_seqs,
     int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
     int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+    int32_t max_context_len, float scale, int32_t partition_size, float* out,
+    void* workspace, size_t workspace_bytes, int32_t dtype, void* stream);
+
+/* pkv_paged_attention_decode_step for a caller that keeps each sequence's
+ * block table in a row of its own choosing -- a serving loop whose batch
+ * changes from step to step gives each running request a fixed row for its
+ * lifetime, so only the entries a step sets travel (explainer,
+ * continuous-batching section: requests join and leave the running batch
+ * at every step).
+ *   block_tables   device [num_table_rows][max_blocks_per_seq]
+ *   table_rows     HOST [num_seqs] int32: batch row b (its query, output
+ *                  and new K/V rows) reads and updates table row
+ *                  table_rows[b]; distinct, in [0, num_table_rows)
+ *   changes        (b, logical block index, physical block), b a batch row;
+ *                  applied to row table_rows[b]
+ * num_table_rows <= 65536.  Otherwise exactly pkv_paged_attention_decode_step
+ * on a table whose row b is block_tables[table_rows[b]]. */
+int32_t pkv_paged_attention_decode_step_mapped(
+    const void* query, const void* key, const void* value, void* key_cache,
+    void* value_cache, int32_t* block_tables, int32_t num_table_rows,
+    const int32_t* table_rows, const int32_t* context_lens, const int32_t* changes,
+    int32_t num_changes, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
     int32_t max_context_len, float scale, int32_t partition_size, float* out,
     void* workspace, size_t workspace_bytes, int32_t dtype, void* stream);
 

@@ -27,6 +27,7 @@ __all__ = [
     "paged_attention_decode_workspace_size", "paged_attention_decode_partition_size",
     "paged_attention_decode", "paged_attention_decode_append",
     "paged_attention_decode_append_partials", "paged_attention_decode_step",
+    "paged_attention_decode_step_mapped",
     "paged_attention_decode_partials", "paged_attention_decode_merge",
     "paged_attention_prefill", "paged_kv_append_fp8", "paged_attention_decode_fp8",
     "paged_attention_decode_fp8_partials", "paged_attention_decode_shared_prefix",
@@ -98,6 +99,9 @@ _SIGNATURES = {
     "pkv_paged_attention_decode_step": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32,
                                                _I32, _I32, _I32, _I32, _I32, ctypes.c_float, _I32,
                                                _P, _P, ctypes.c_size_t, _I32, _P]),
+    "pkv_paged_attention_decode_step_mapped": (
+        _I32, [_P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
+               _I32, _I32, _I32, ctypes.c_float, _I32, _P, _P, ctypes.c_size_t, _I32, _P]),
     "pkv_paged_attention_decode_step_partials": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32,
                                                         _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                                                         ctypes.c_float, _I32, _P, _P,
@@ -751,7 +755,7 @@ def paged_attention_decode_workspace_size(num_seqs, num_heads, num_kv_heads, hea
 
 
 def _decode_args(query, key_cache, value_cache, block_tables, context_lens, max_context_len,
-                 partition_size, out, workspace, fp8=False):
+                 partition_size, out, workspace, fp8=False, mapped=False):
     nb, hkv, bs, d = _cache_dims(key_cache, value_cache)
     if fp8:
         if key_cache.dtype not in _FP8_TYPES:
@@ -767,7 +771,7 @@ def _decode_args(query, key_cache, value_cache, block_tables, context_lens, max_
         _dev(context_lens, "context_lens", dtype=torch.int32, ndim=1)
         if context_lens.shape[0] != b:
             raise InvalidArgument("query and context_lens disagree on shape")
-    if dq != d or block_tables.shape[0] != b:
+    if dq != d or (block_tables.shape[0] != b and not mapped):
         raise InvalidArgument("query and block_tables disagree on shape")
     if out is None:
         out = torch.empty((b, hq, d), dtype=torch.float32, device=query.device)
@@ -1038,6 +1042,39 @@ def paged_attention_decode_step(query, key, value, key_cache, value_cache, block
         block_tables.data_ptr(), lens.ctypes.data, changes.ctypes.data, changes.shape[0], b, hq,
         hkv, d, bs, block_tables.shape[1], nb, int(max_context_len), float(scale),
         int(partition_size), out.data_ptr(), ws_ptr, ws_bytes,
+        _decode_code(key_cache, shared_blocks), _stream(query)))
+    return out
+
+
+def paged_attention_decode_step_mapped(query, key, value, key_cache, value_cache, block_tables,
+                                       table_rows, context_lens, changes, scale,
+                                       max_context_len, partition_size=0, out=None,
+                                       workspace=None, shared_blocks=False):
+    """paged_attention_decode_step with the block tables in rows of the
+    caller's choosing (pkv_paged_attention_decode_step_mapped): batch row b
+    reads and updates row table_rows[b] (host int32 [B], distinct) of
+    block_tables (device int32 [rows, max_blocks]); changes name batch
+    rows."""
+    (nb, hkv, bs, d, b, hq), out, workspace, ws_ptr, ws_bytes = _decode_args(
+        query, key_cache, value_cache, block_tables, None, max_context_len, partition_size, out,
+        workspace, mapped=True)
+    lens = np.ascontiguousarray(np.asarray(context_lens, dtype=np.int32))
+    rows = np.ascontiguousarray(np.asarray(table_rows, dtype=np.int32))
+    changes = np.ascontiguousarray(np.asarray(changes, dtype=np.int32).reshape(-1, 3))
+    if lens.shape != (b,) or rows.shape != (b,):
+        raise InvalidArgument("context_lens and table_rows must hold one entry per sequence")
+    kp = vp = None
+    if key is not None or value is not None:
+        _dev(key, "key", dtype=key_cache.dtype, ndim=3)
+        _dev(value, "value", dtype=key_cache.dtype, ndim=3)
+        if tuple(key.shape) != (b, hkv, d) or value.shape != key.shape:
+            raise InvalidArgument("key/value must be [B, num_kv_heads, head_dim]")
+        kp, vp = key.data_ptr(), value.data_ptr()
+    _check(_lib.pkv_paged_attention_decode_step_mapped(
+        query.data_ptr(), kp, vp, key_cache.data_ptr(), value_cache.data_ptr(),
+        block_tables.data_ptr(), block_tables.shape[0], rows.ctypes.data, lens.ctypes.data,
+        changes.ctypes.data, changes.shape[0], b, hq, hkv, d, bs, block_tables.shape[1], nb,
+        int(max_context_len), float(scale), int(partition_size), out.data_ptr(), ws_ptr, ws_bytes,
         _decode_code(key_cache, shared_blocks), _stream(query)))
     return out
 

@@ -474,10 +474,11 @@ struct DecodeParams {
 // path) -- the lengths, and the table entries this step's appends set,
 // which the kernels apply while staging block ids and persist to the
 // device table for later launches.  One launch carries the metadata of at
-// most kStepRanks sequences (kernel-argument space); a larger batch is
-// served by consecutive launches over consecutive ranks of its work order.
+// most kStepRanks sequences and kStepMaxChanges table changes (kernel-
+// argument space); a larger batch is served by consecutive launches over
+// consecutive ranks of its work order.
 constexpr int kStepRanks = 256;
-constexpr int kStepMaxChanges = 256;  // per launch
+constexpr int kStepMaxChanges = 192;  // per launch
 
 struct DeviceMeta {
   static constexpr bool kHost = false;
@@ -489,11 +490,13 @@ struct DeviceMeta {
   }
   // merge grid (query head, sequence)
   __device__ int merge_seq(int y) const { return y; }
+  // the block-table row of batch row b
+  __device__ int table_row(int b, int) const { return b; }
 };
 
 struct StepMeta {
   static constexpr bool kHost = true;
-  // Work order: rank r of this launch serves batch row seq[r], longest
+  // Work order: rank r of this launch serves batch row row[r], longest
   // first over the whole batch, so the longest partitions start first and
   // the short ones fill the end of the launch.  With parts_per_rank > 0
   // the grid is (kv head, rank * parts_per_rank + partition, 1): a
@@ -503,13 +506,17 @@ struct StepMeta {
   int32_t lens[kStepRanks];                // by rank
   int32_t change_key[kStepMaxChanges];     // logical block index << 8 | rank
   int32_t change_block[kStepMaxChanges];   // physical block
-  uint16_t seq[kStepRanks];
+  // by rank: the batch row (bits 0-15: its query, output and new K/V rows)
+  // and the block-table row it reads (bits 16-31: the batch row itself
+  // unless the caller keeps the tables in rows of its own)
+  uint32_t row[kStepRanks];
   int32_t num_changes;
   int32_t parts_per_rank;
   __device__ int len(const DecodeParams&, int, int rank) const { return lens[rank]; }
   // merge grid (query head, rank): the launch covers only the ranks up to
   // the last sequence that spans two partitions
-  __device__ int merge_seq(int y) const { return seq[y]; }
+  __device__ int merge_seq(int y) const { return int(row[y] & 0xFFFFu); }
+  __device__ int table_row(int, int rank) const { return int(row[rank] >> 16); }
   __device__ void work(int& b, int& p, int& rank) const {
     if (parts_per_rank > 0) {
       const int y = blockIdx.y;
@@ -519,7 +526,7 @@ struct StepMeta {
       rank = blockIdx.y;
       p = blockIdx.z;
     }
-    b = seq[rank];
+    b = int(row[rank] & 0xFFFFu);
   }
 };
 
@@ -570,6 +577,7 @@ __global__ __launch_bounds__(kThreads, (decode_min_blocks<DT, G>())) void decode
   const int num_heads = num_kv_heads * G;
 
   const int n = meta.len(prm, b, rank);
+  const int64_t trow = meta.table_row(b, rank);  // this sequence's block-table row
   const bool suffix = prm.row_info != nullptr;
   const int slot_base = prm.slot_base;
   const int start = suffix ? prm.row_info[4 * int64_t(b)] : 0;
@@ -583,7 +591,7 @@ __global__ __launch_bounds__(kThreads, (decode_min_blocks<DT, G>())) void decode
     // for it is inconsistent input: its first prefix partial's max becomes
     // NaN, so the merge writes a NaN row (first partition of each kv head;
     // the prefix launch that wrote the partial has completed).
-    const int32_t* own = prm.block_tables + int64_t(b) * max_blocks;
+    const int32_t* own = prm.block_tables + trow * max_blocks;
     const int32_t* first =
         prm.block_tables + int64_t(prm.row_info[4 * int64_t(b) + 1]) * max_blocks;
     bool differs = false;
@@ -610,7 +618,7 @@ __global__ __launch_bounds__(kThreads, (decode_min_blocks<DT, G>())) void decode
   const int p0 = start + p_idx * part;
   const int ntok = min(part, n - p0);
   const int nblk = (ntok + bs - 1) >> log2_bs;
-  const int32_t* table = prm.block_tables + int64_t(b) * max_blocks + (p0 >> log2_bs);
+  const int32_t* table = prm.block_tables + trow * max_blocks + (p0 >> log2_bs);
   for (int i = tid; i < nblk; i += kThreads) s_blk[i] = table[i];
   if constexpr (Meta::kHost) {
     // this step's table changes for this sequence and partition: staged,
@@ -622,7 +630,7 @@ __global__ __launch_bounds__(kThreads, (decode_min_blocks<DT, G>())) void decode
       const int j = (key >> 8) - j0;
       if ((key & 255) == rank && j >= 0 && j < nblk) {
         s_blk[j] = meta.change_block[t];
-        if (kvh == 0) prm.block_tables_rw[int64_t(b) * max_blocks + j0 + j] = meta.change_block[t];
+        if (kvh == 0) prm.block_tables_rw[trow * max_blocks + j0 + j] = meta.change_block[t];
       }
     }
   }
@@ -1147,11 +1155,10 @@ namespace {
 // The launches of one step call (see make_step_plan).
 struct StepPlan {
   std::vector<StepMeta> chunks;
+  std::vector<int32_t> chunk_ranks;    // ranks of each launch
   const int32_t* host_lens = nullptr;  // [num_seqs], batch order
   int32_t num_seqs = 0;
-  int32_t ranks(size_t c) const {
-    return std::min<int32_t>(kStepRanks, num_seqs - int32_t(c) * kStepRanks);
-  }
+  int32_t ranks(size_t c) const { return chunk_ranks[c]; }
   // ranks of launch c up to the last one whose length exceeds `part`
   int32_t rows_above(size_t c, int32_t part) const {
     int32_t rows = 0;
@@ -1328,13 +1335,15 @@ int32_t run_decode(const void* query, const void* key_new, const void* value_new
 }
 
 // Makes a step's launch metadata from its host lengths and table changes:
-// the work order over the whole batch, cut into launches of kStepRanks
-// ranks, each carrying its ranks' lengths and the changes of their rows
-// (at most kStepMaxChanges per launch).
+// the work order over the whole batch, cut into launches of at most
+// kStepRanks ranks and kStepMaxChanges changes, each carrying its ranks'
+// lengths, batch and table rows, and the changes of their rows.
+// table_rows (may be null: the batch rows themselves) maps batch row b to
+// the block-table row it reads and whose changes it persists.
 int32_t make_step_plan(const int32_t* context_lens, const int32_t* changes,
                        int32_t num_changes, int32_t num_seqs, int32_t num_kv_heads,
                        int32_t max_blocks_per_seq, StepPlan* plan,
-                       const int32_t* skipped = nullptr) {
+                       const int32_t* skipped = nullptr, const int32_t* table_rows = nullptr) {
   if (num_seqs > 65535)
     return fail(PKV_ERR_UNSUPPORTED, "at most 65535 sequences per call (got %d)", num_seqs);
   if (num_changes < 0) return fail(PKV_ERR_INVALID, "negative num_changes");
@@ -1343,13 +1352,13 @@ int32_t make_step_plan(const int32_t* context_lens, const int32_t* changes,
   plan->host_lens = context_lens;
   // Longest first (stable), so long partitions start first -- by the tokens
   // the launch reads, the length less the shared prefix (skipped[i]) in a
-  // shared-prefix step; then, within
-  // each round of R = 256 / num_kv_heads sequences -- the sequences whose
-  // workgroups one pass of the dispatcher spreads over all 256 CUs -- every
-  // other round reversed ("snake"), so the CUs that get a round's longest
-  // sequence get the next round's shortest and the CUs' loads even out
-  // when the whole grid is resident at once (7B-shaped batch: partition
-  // kernel 1% faster than plain longest-first).
+  // shared-prefix step; then, within each round of R = 256 / num_kv_heads
+  // sequences -- the sequences whose workgroups one pass of the dispatcher
+  // spreads over all 256 CUs -- every other round reversed ("snake"), so
+  // the CUs that get a round's longest sequence get the next round's
+  // shortest and the CUs' loads even out when the whole grid is resident at
+  // once (7B-shaped batch: partition kernel 1% faster than plain
+  // longest-first).
   std::vector<int32_t> idx(num_seqs), order(num_seqs), rank_of(num_seqs);
   for (int32_t i = 0; i < num_seqs; ++i) idx[i] = i;
   auto work = [&](int32_t i) {
@@ -1364,25 +1373,45 @@ int32_t make_step_plan(const int32_t* context_lens, const int32_t* changes,
     order[i] = idx[src];
     rank_of[idx[src]] = i;
   }
-  const int32_t nchunks = (num_seqs + kStepRanks - 1) / kStepRanks;
-  plan->num_seqs = num_seqs;
-  plan->chunks.assign(nchunks, StepMeta{});
-  for (int32_t i = 0; i < num_seqs; ++i) {
-    StepMeta& m = plan->chunks[i / kStepRanks];
-    m.lens[i % kStepRanks] = context_lens[order[i]];
-    m.seq[i % kStepRanks] = static_cast<uint16_t>(order[i]);
-  }
+  std::vector<int32_t> per_row(num_seqs, 0);
   for (int32_t i = 0; i < num_changes; ++i) {
     const int32_t row = changes[3 * i], blk = changes[3 * i + 1];
     if (row < 0 || row >= num_seqs || blk < 0 || blk >= max_blocks_per_seq || blk >= (1 << 23))
       return fail(PKV_ERR_INVALID, "table change %d (row %d, index %d) out of range", i, row,
                   blk);
-    StepMeta& m = plan->chunks[rank_of[row] / kStepRanks];
-    if (m.num_changes == kStepMaxChanges)
-      return fail(PKV_ERR_UNSUPPORTED,
-                  "step calls take at most %d table changes per %d sequences of the work order",
-                  kStepMaxChanges, kStepRanks);
-    m.change_key[m.num_changes] = (blk << 8) | (rank_of[row] % kStepRanks);
+    if (++per_row[row] > kStepMaxChanges)
+      return fail(PKV_ERR_UNSUPPORTED, "step calls take at most %d table changes per sequence",
+                  kStepMaxChanges);
+  }
+  // launches: consecutive ranks, a new one when the ranks or the changes
+  // would not fit
+  std::vector<int32_t> chunk_of(num_seqs);
+  plan->num_seqs = num_seqs;
+  plan->chunks.clear();
+  plan->chunk_ranks.clear();
+  int32_t in_chunk = 0, changes_in_chunk = 0;
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    const int32_t b = order[i];
+    if (plan->chunks.empty() || in_chunk == kStepRanks ||
+        changes_in_chunk + per_row[b] > kStepMaxChanges) {
+      plan->chunks.emplace_back();
+      plan->chunk_ranks.push_back(0);
+      in_chunk = changes_in_chunk = 0;
+    }
+    StepMeta& m = plan->chunks.back();
+    const uint32_t trow = table_rows ? uint32_t(table_rows[b]) : uint32_t(b);
+    m.lens[in_chunk] = context_lens[b];
+    m.row[in_chunk] = uint32_t(b) | (trow << 16);
+    chunk_of[b] = int32_t(plan->chunks.size()) - 1;
+    rank_of[b] = in_chunk;  // now the rank within its launch
+    ++in_chunk;
+    ++plan->chunk_ranks.back();
+    changes_in_chunk += per_row[b];
+  }
+  for (int32_t i = 0; i < num_changes; ++i) {
+    const int32_t row = changes[3 * i], blk = changes[3 * i + 1];
+    StepMeta& m = plan->chunks[chunk_of[row]];
+    m.change_key[m.num_changes] = (blk << 8) | rank_of[row];
     m.change_block[m.num_changes] = changes[3 * i + 2];
     ++m.num_changes;
   }
@@ -1494,6 +1523,38 @@ extern "C" int32_t pkv_paged_attention_decode_step(
                    block_size, max_blocks_per_seq, num_blocks, max_context_len, scale,
                    partition_size, out, workspace, workspace_bytes_given, dtype, stream, true,
                    true);
+}
+
+extern "C" int32_t pkv_paged_attention_decode_step_mapped(
+    const void* query, const void* key, const void* value, void* key_cache,
+    void* value_cache, int32_t* block_tables, int32_t num_table_rows,
+    const int32_t* table_rows, const int32_t* context_lens, const int32_t* changes,
+    int32_t num_changes, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+    int32_t max_context_len, float scale, int32_t partition_size, float* out, void* workspace,
+    size_t workspace_bytes_given, int32_t dtype, void* stream) {
+  if (num_table_rows < 0 || num_table_rows > 65536)
+    return fail(PKV_ERR_INVALID, "num_table_rows %d must be in [0, 65536]", num_table_rows);
+  if (num_seqs > 0 && !table_rows) return fail(PKV_ERR_INVALID, "table_rows is NULL");
+  if (num_seqs > num_table_rows)
+    return fail(PKV_ERR_INVALID, "%d sequences cannot have distinct rows among %d", num_seqs,
+                num_table_rows);
+  // distinct rows: two sequences persisting changes into one row would race
+  std::vector<bool> used(size_t(std::max(num_table_rows, 0)), false);
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    const int32_t r = table_rows[b];
+    if (r < 0 || r >= num_table_rows || used[r])
+      return fail(PKV_ERR_INVALID, "table_rows[%d] = %d is out of range or repeated", b, r);
+    used[r] = true;
+  }
+  StepPlan plan;
+  int32_t st = make_step_plan(context_lens, changes, num_changes, num_seqs, num_kv_heads,
+                              max_blocks_per_seq, &plan, nullptr, table_rows);
+  if (st != PKV_OK) return st;
+  return run_decode(query, key, value, key_cache, value_cache, block_tables, nullptr, num_seqs,
+                    num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                    num_blocks, max_context_len, scale, partition_size, out, workspace,
+                    workspace_bytes_given, dtype, stream, true, true, &plan);
 }
 
 extern "C" int32_t pkv_paged_attention_decode_step_partials(

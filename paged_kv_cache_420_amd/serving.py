@@ -8,11 +8,21 @@ section; KV-cache article §4.1/§4.2 for the chunks):
   1b. blocks it swapped in or out (preemption into a host tier; KV-cache
      article §4.2, swap space) are copied: swap-ins first, then swap-outs,
      both before anything of this step writes the pool;
-  2. the plan's slot mapping, block tables, lengths and chunk offsets go to
-     the device in one copy from pinned host memory;
-  3. pkv_paged_kv_append stores every row's new K/V through the slots;
-  4. pkv_paged_attention_decode attends the decode rows,
-     pkv_paged_attention_prefill the prompt chunks (causal).
+  2. the prompt chunks' slot mapping, block tables, lengths and offsets go
+     to the device in one copy from pinned host memory;
+  3. pkv_paged_kv_append stores the chunks' new K/V through the slots;
+  4. pkv_paged_attention_decode_step_mapped attends the decode rows: every
+     running request keeps one row of a device-resident block table for
+     as long as it decodes (its lane), so a step sends only the lengths and
+     the table entries that changed since the lane's last step, by value in
+     the kernel arguments, and the decode kernel stores each decode row's
+     new K/V itself.  A request's first decode step copies its whole table
+     row (part of the one metadata copy) into its lane.
+     pkv_paged_attention_prefill attends the prompt chunks (causal).
+With decode="upload" the decode rows go the other way instead: their
+slots, full tables and lengths travel in the metadata copy every step and
+pkv_paged_attention_decode reads them there (the simpler form, kept for
+comparison).
 The caller supplies each step's query and new K/V rows (row order of the
 plan); this module only moves arguments and launches the library's calls.
 """
@@ -20,15 +30,19 @@ plan); this module only moves arguments and launches the library's calls.
 import numpy as np
 import torch
 
-from . import (Scheduler, paged_attention_decode, paged_attention_decode_workspace_size,
-               paged_attention_prefill, paged_kv_append, swap_blocks)
+from . import (Scheduler, paged_attention_decode, paged_attention_decode_step_mapped,
+               paged_attention_decode_workspace_size, paged_attention_prefill, paged_kv_append,
+               swap_blocks)
 
 
 class ServingDriver:
     def __init__(self, scheduler, key_cache, value_cache, num_heads, scale, max_request_tokens,
-                 partition_size=0, host_key_cache=None, host_value_cache=None):
+                 partition_size=0, host_key_cache=None, host_value_cache=None, decode="step"):
         if not isinstance(scheduler, Scheduler):
             raise TypeError("scheduler must be a paged_kv_cache_420_amd.Scheduler")
+        if decode not in ("step", "upload"):
+            raise ValueError("decode must be 'step' or 'upload'")
+        self.decode = decode
         self.sched = scheduler
         self.kc, self.vc = key_cache, value_cache
         self.hk, self.hv = host_key_cache, host_value_cache
@@ -51,6 +65,13 @@ class ServingDriver:
                                    device=self.dev)
         # packed metadata: slots | tables | lens | cu (prefill rows)
         self._meta_len = tokens + rows * self.max_blocks + rows + rows + 1
+        # lanes: one row of the device table per decoding request, and the
+        # host's copy of what each row holds
+        self._lane_table = torch.zeros((rows, self.max_blocks), dtype=torch.int32,
+                                       device=self.dev)
+        self._lane_host = np.zeros((rows, self.max_blocks), dtype=np.int32)
+        self._lane_of = {}
+        self._free_lanes = list(range(rows - 1, -1, -1))
         self._host = [torch.empty(self._meta_len, dtype=torch.int32, pin_memory=True)
                       for _ in range(2)]
         self._copied = [None, None]
@@ -69,20 +90,36 @@ class ServingDriver:
         if len(plan.swap_out):
             swap_blocks(self.kc, self.vc, self.hk, self.hv, plan.swap_out[:, 0],
                         plan.swap_out[:, 1])
+        for rid in list(plan.finished) + list(plan.preempted):  # lanes of requests that left
+            lane = self._lane_of.pop(rid, None)
+            if lane is not None:
+                self._free_lanes.append(lane)
         if plan.num_rows == 0:
             return plan, None, None
         nd, nr, nt = plan.num_decode, plan.num_rows, plan.num_tokens
+        step_form = self.decode == "step"
         mb = self.max_blocks
         host = self._host[self._flip]
         if self._copied[self._flip] is not None:
             self._copied[self._flip].synchronize()  # its previous copy has finished
         h = host.numpy()
-        o_tab = nt
-        o_len = o_tab + nr * mb
-        o_cu = o_len + nr
-        h[:nt] = plan.slots
-        h[o_tab:o_len] = plan.block_tables.reshape(-1)
-        h[o_len:o_cu] = plan.context_lens
+        # rows whose tables, lengths and slots travel: all of them, or (step
+        # form) the prompt chunks plus whole table rows of new lanes
+        first = nd if step_form else 0
+        lanes = changes = None
+        new_lanes = []
+        if step_form and nd:
+            lanes, changes, new_lanes = self._lane_step(plan)
+        nup = nr - first
+        o_tab = nt - first
+        o_new = o_tab + nup * mb
+        o_len = o_new + len(new_lanes) * mb
+        o_cu = o_len + nup
+        h[:o_tab] = plan.slots[first:]
+        h[o_tab:o_new] = plan.block_tables[first:].reshape(-1)
+        for i, (_, r) in enumerate(new_lanes):
+            h[o_new + i * mb:o_new + (i + 1) * mb] = plan.block_tables[r]
+        h[o_len:o_cu] = plan.context_lens[first:]
         npre = nr - nd
         h[o_cu] = 0
         if npre:
@@ -94,20 +131,57 @@ class ServingDriver:
         ev.record()
         self._copied[self._flip] = ev
         self._flip ^= 1
-        slots = dm[:nt]
-        tables = dm[o_tab:o_len].view(nr, mb)
+        for i, (lane, _) in enumerate(new_lanes):
+            self._lane_table[lane].copy_(dm[o_new + i * mb:o_new + (i + 1) * mb],
+                                         non_blocking=True)
+        slots = dm[:o_tab]
+        tables = dm[o_tab:o_new].view(nup, mb)
         lens = dm[o_len:o_cu]
         q, k, v = make_rows(plan)
-        paged_kv_append(k, v, self.kc, self.vc, slots)
+        if o_tab:
+            paged_kv_append(k[first:], v[first:], self.kc, self.vc, slots)
         out_dec = out_pre = None
         if nd:
             mc = int(plan.context_lens[:nd].max())
-            out_dec = paged_attention_decode(q[:nd], self.kc, self.vc, tables[:nd], lens[:nd],
-                                             self.scale, mc, self.part, self.out_dec[:nd],
-                                             self.workspace)
+            if step_form:
+                out_dec = paged_attention_decode_step_mapped(
+                    q[:nd], k[:nd], v[:nd], self.kc, self.vc, self._lane_table, lanes,
+                    plan.context_lens[:nd], changes, self.scale, mc, self.part,
+                    self.out_dec[:nd], self.workspace)
+            else:
+                out_dec = paged_attention_decode(q[:nd], self.kc, self.vc, tables[:nd],
+                                                 lens[:nd], self.scale, mc, self.part,
+                                                 self.out_dec[:nd], self.workspace)
         if npre:
             mq = int(plan.query_lens[nd:].max())
-            out_pre = paged_attention_prefill(q[nd:], self.kc, self.vc, tables[nd:], lens[nd:],
-                                              dm[o_cu:o_cu + 1 + npre], self.scale, mq,
-                                              self.out_pre[:nt - nd])
+            out_pre = paged_attention_prefill(q[nd:], self.kc, self.vc, tables[nd - first:],
+                                              lens[nd - first:], dm[o_cu:o_cu + 1 + npre],
+                                              self.scale, mq, self.out_pre[:nt - nd])
         return plan, out_dec, out_pre
+
+    def _lane_step(self, plan):
+        """Lanes of the decode rows (a free row of the device table for a
+        request's first decode step), the entries of the plan's tables that
+        differ from what the lanes hold (within each row's length), and the
+        (lane, plan row) pairs whose whole row must be copied."""
+        nd, mb, bs = plan.num_decode, self.max_blocks, self.block_size
+        lanes = np.empty(nd, dtype=np.int32)
+        new = []
+        for r in range(nd):
+            rid = int(plan.seq_ids[r])
+            lane = self._lane_of.get(rid)
+            if lane is None:
+                lane = self._free_lanes.pop()
+                self._lane_of[rid] = lane
+                new.append((lane, r))
+            lanes[r] = lane
+        want = plan.block_tables[:nd]
+        held = self._lane_host[lanes]
+        used = np.arange(mb)[None, :] < ((plan.context_lens[:nd] + bs - 1) // bs)[:, None]
+        for lane, r in new:
+            used[r] = False                     # copied whole
+            self._lane_host[lane] = want[r]
+        rows, cols = np.nonzero(used & (want != held))
+        changes = np.stack([rows, cols, want[rows, cols]], axis=1).astype(np.int32)
+        self._lane_host[lanes[rows], cols] = want[rows, cols]
+        return lanes, changes, new

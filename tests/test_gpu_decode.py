@@ -511,11 +511,10 @@ def test_step_call_limits():
     w = STEP["bf16_shared_cow"]
     kc = torch.zeros((8, 4, 16, 128), dtype=torch.bfloat16, device=DEV)
     q = torch.zeros((300, 4, 128), dtype=torch.bfloat16, device=DEV)
-    t = torch.zeros((300, 2), dtype=torch.int32, device=DEV)
+    t = torch.zeros((300, 200), dtype=torch.int32, device=DEV)
     lens = np.ones(300, dtype=np.int32)
-    # 257 changes for rows served by the first launch (ranks 0..255)
-    many = np.array([[r, 0, 1] for r in range(200)] + [[r, 1, 1] for r in range(57)],
-                    dtype=np.int32)
+    # 193 changes for one sequence: more than one launch can carry
+    many = np.array([[0, j, 1] for j in range(193)], dtype=np.int32)
     with pytest.raises(pkv.Unsupported):
         pkv.paged_attention_decode_step(q, None, None, kc, kc, t, lens, many, w.scale, 1)
     with pytest.raises(pkv.InvalidArgument):  # change row outside the batch
@@ -576,6 +575,67 @@ def test_step_call_past_256_sequences():
     worst = max(parallel_map(err, range(nb)))
     log("512-sequence step, every row: max abs err", worst)
     assert worst <= TOL[w.dtype]
+
+
+def test_step_mapped_is_step_on_mapped_rows():
+    """pkv_paged_attention_decode_step_mapped: 300 sequences whose tables
+    sit in scattered rows of a 400-row device table (the rest garbage),
+    lengths in lockstep so that every sequence opens a block at the first
+    step (300 changes: launches cut by the change limit) -- bitwise the
+    fused-append decode on freshly uploaded tables, over four steps; the
+    mapped rows end up holding the sequences' tables, the others
+    untouched."""
+    w = workloads.scaled(workloads.get("llama7b_bf16"), num_seqs=300, num_heads=4,
+                         num_kv_heads=2, lens="fixed:32,64,96,128,160,480", seed=4611)
+    p = workloads.plan(w)
+    a, b = GpuState(w, p), GpuState(w, p)
+    seqs = p.seqs
+    nb, steps = len(seqs), 4
+    mb = max(len(a.alloc.block_table(s)) for s in seqs) + 2
+    rows_total = 400
+    table_rows = np.random.default_rng(7).permutation(rows_total)[:nb].astype(np.int32)
+    th, _ = b.alloc.build_block_tables(seqs, mb)
+    lane = np.full((rows_total, mb), -7, dtype=np.int32)
+    lane[table_rows] = th
+    lane_d = torch.from_numpy(lane.copy()).to(DEV)
+    ones = np.ones(nb, dtype=np.int32)
+    for i in range(steps):
+        k, v = workloads.kv_rows(w, len(p.ops) + i, nb)
+        kt = workloads.to_dtype(k, w.dtype).to(DEV)
+        vt = workloads.to_dtype(v, w.dtype).to(DEV)
+        qt = workloads.to_dtype(workloads.normal([w.seed, 9, i], (nb, w.num_heads, w.head_dim),
+                                                 w.std), w.dtype).to(DEV)
+        a.alloc.append_batch(seqs, ones)
+        _, _, lens, changes = b.alloc.append_batch_changes(seqs, ones)
+        if i == 0:
+            assert len(changes) == nb        # every sequence opened a block
+        ta, la, _, lh = a.tables(seqs)
+        ta = torch.nn.functional.pad(ta, (0, mb - ta.shape[1]), value=-1).contiguous()
+        mc = int(lh.max())
+        want = pkv.paged_attention_decode_append(qt, kt, vt, a.kc, a.vc, ta, la, w.scale, mc,
+                                                 partition_size=128)
+        got = pkv.paged_attention_decode_step_mapped(qt, kt, vt, b.kc, b.vc, lane_d, table_rows,
+                                                     lens, changes, w.scale, mc,
+                                                     partition_size=128)
+        torch.cuda.synchronize()
+        assert torch.equal(got, want), f"step {i}"
+    assert torch.equal(a.kc.view(torch.uint8), b.kc.view(torch.uint8))
+    assert torch.equal(a.vc.view(torch.uint8), b.vc.view(torch.uint8))
+    th, _ = b.alloc.build_block_tables(seqs, mb)
+    lane_now = lane_d.cpu().numpy()
+    assert np.array_equal(lane_now[table_rows], th)
+    rest = np.setdiff1d(np.arange(rows_total), table_rows)
+    assert (lane_now[rest] == -7).all()
+    with pytest.raises(pkv.InvalidArgument):          # a repeated row
+        bad = table_rows.copy()
+        bad[1] = bad[0]
+        pkv.paged_attention_decode_step_mapped(qt, None, None, b.kc, b.vc, lane_d, bad, lens,
+                                               np.zeros((0, 3), np.int32), w.scale, mc)
+    with pytest.raises(pkv.InvalidArgument):          # a row outside the table
+        bad = table_rows.copy()
+        bad[3] = rows_total
+        pkv.paged_attention_decode_step_mapped(qt, None, None, b.kc, b.vc, lane_d, bad, lens,
+                                               np.zeros((0, 3), np.int32), w.scale, mc)
 
 
 def test_shared_prefix_step_past_256_sequences():

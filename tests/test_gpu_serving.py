@@ -79,10 +79,13 @@ class Tokens:
         return np.stack([r[2] for r in rows]), np.stack([r[3] for r in rows])
 
 
+@pytest.mark.parametrize("decode", ["step", "upload"])
 @pytest.mark.parametrize("host_blocks", [0, 24])
-def test_serving_trace_matches_oracle_every_step(host_blocks):
+def test_serving_trace_matches_oracle_every_step(host_blocks, decode):
     """host_blocks 0: preemption recomputes; 24: it swaps to a pinned host
-    pool and back, and the outputs must not notice."""
+    pool and back, and the outputs must not notice.  decode "step": the
+    decode rows' tables live in device lanes changed by value each step;
+    "upload": they travel whole every step."""
     t = SMALL
     reqs = workloads.serving_requests(t)
     max_tokens = max(p + o for _, p, o in reqs)
@@ -101,7 +104,7 @@ def test_serving_trace_matches_oracle_every_step(host_blocks):
         hk = torch.full(hshape, float("nan"), dtype=t.dtype).pin_memory()
         hv = torch.full(hshape, float("nan"), dtype=t.dtype).pin_memory()
     drv = ServingDriver(sched, kc, vc, t.num_heads, t.scale, max_tokens,
-                        host_key_cache=hk, host_value_cache=hv)
+                        host_key_cache=hk, host_value_cache=hv, decode=decode)
     tok = Tokens(t)
     worst, steps, rows_checked = 0.0, 0, 0
     while True:
