@@ -843,18 +843,33 @@ def cpu_baseline(w, workloads):
     return res
 
 
-def traffic_from_profiles(w, kernel_src):
-    """HBM bytes per launch of the decode partition kernel from the committed
-    counter summary (profiles/decode_partition_<workload>_traffic.md), when
-    it was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"decode_partition_{w.name}_traffic.md")
-    if not os.path.exists(path):
+def traffic_profile(w):
+    """The committed counter summary of the workload's roofline kernel:
+    profiles/decode_partition_<workload>_traffic.md, else the workload's
+    profiles/decode_partition_<workload>.md."""
+    for suffix in ("_traffic", ""):
+        path = os.path.join(ROOT, "profiles", f"decode_partition_{w.name}{suffix}.md")
+        if os.path.exists(path):
+            return path
+    return None
+
+
+def traffic_from_profiles(w):
+    """HBM bytes per launch (per call, for the prefix workloads) of the
+    roofline kernel from its committed counter summary, when it was taken on
+    the current kernel sources (decode.hip, and prefill.hip where listed);
+    else None."""
+    path = traffic_profile(w)
+    if path is None:
         return None
-    text = open(path).read()
-    fields = dict(re.findall(r"^- (\w+): (\S+)$", text, flags=re.M))
-    digest = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
-    if fields.get("kernel_source_sha256") != digest:
-        return None
+    fields = dict(re.findall(r"^- (\w+): (\S+)$", open(path).read(), flags=re.M))
+    csrc = os.path.join(ROOT, "paged_kv_cache_420_amd", "csrc")
+    for key, src in (("kernel_source_sha256", "decode.hip"),
+                     ("prefill_source_sha256", "prefill.hip")):
+        if key == "kernel_source_sha256" or key in fields:
+            digest = hashlib.sha256(open(os.path.join(csrc, src), "rb").read()).hexdigest()
+            if fields.get(key) != digest:
+                return None
     try:
         return int(fields["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
@@ -886,7 +901,6 @@ def main():
     w = workloads.get(args.workload)
     r = gpu_run(args, w, torch, pkv, workloads)
     leg = summarise(w, r)
-    src = os.path.join(ROOT, "paged_kv_cache_420_amd", "csrc", "decode.hip")
     line = {
         "metric": METRIC,
         "value": leg["gbps"],
@@ -915,11 +929,8 @@ def main():
         "roofline": {"bound": "hbm", "kernel": leg["kernel"],
                      "achieved": leg["kernel_gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": leg["kernel_hbm_peak_frac"],
-                     "traffic": traffic_from_profiles(w, src),
-                     "traffic_from": (f"profiles/decode_partition_{w.name}_traffic.md: "
-                                      "rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE of the same "
-                                      "kernel source, scaled by the block-copy calibration "
-                                      "(null when the source has changed since)"),
+                     "traffic": leg["traffic"],
+                     "traffic_from": leg["traffic_from"],
                      "bytes_per_launch": leg["kernel_bytes"],
                      "timing": "20 launches back to back between one pair of HIP events on "
                                "the kernel's stream, on the cache state after the timed steps"},
@@ -979,6 +990,11 @@ def summarise(w, r):
         "kv_loads": ("prefix: matrix-core contraction; suffixes: non-temporal"
                      if w.prefix or w.prefix_groups else
                      "cached (shared blocks)" if r["shared"] else "non-temporal"),
+        "traffic": traffic_from_profiles(w),
+        "traffic_from": (f"{os.path.relpath(traffic_profile(w), ROOT)}: rocprofv3 --pmc "
+                         "FETCH_SIZE and WRITE_SIZE of the same kernel sources, scaled by the "
+                         "block-copy calibration (null when a source has changed since)"
+                         if traffic_profile(w) else None),
     }
 
 
