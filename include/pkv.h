@@ -696,6 +696,25 @@ int32_t pkv_paged_attention_decode_fp8_partials(
     float v_scale, int32_t partition_size, float* out, void* workspace,
     size_t workspace_bytes, int32_t query_dtype, void* stream);
 
+/* The step form of pkv_paged_attention_decode_fp8, as
+ * pkv_paged_attention_decode_step is of the 16-bit decode: host lengths and
+ * this step's table changes by value, and each sequence's new K/V row (key,
+ * value [num_seqs][num_kv_heads][head_dim] in query_dtype, or both NULL)
+ * quantised by the decode kernel with k_scale / v_scale exactly as
+ * pkv_paged_kv_append_fp8 quantises (the same codes, bit for bit) and stored
+ * at its newest position before reading (article §4.2: an 8-bit cache;
+ * explainer, serving section: each step adds one K and one V row).
+ * Launches, limits and errors as pkv_paged_attention_decode_step; other
+ * arguments as pkv_paged_attention_decode_fp8. */
+int32_t pkv_paged_attention_decode_fp8_step(
+    const void* query, const void* key, const void* value, void* key_cache,
+    void* value_cache, int32_t* block_tables, const int32_t* context_lens,
+    const int32_t* changes, int32_t num_changes, int32_t num_seqs, int32_t num_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+    int32_t num_blocks, int32_t max_context_len, float scale, float k_scale, float v_scale,
+    int32_t partition_size, float* out, void* workspace, size_t workspace_bytes,
+    int32_t query_dtype, void* stream);
+
 /* Decode attention for a batch whose sequences all begin with the same
  * prefix_len tokens: forked from one parent, they share its blocks
  * (explainer, section on memory sharing: parallel samples and shared
@@ -858,6 +877,24 @@ int32_t pkv_paged_attention_prefill(
     int32_t max_blocks_per_seq, int32_t num_blocks, int32_t total_query_rows,
     int32_t max_query_len, float scale, float* out, int32_t dtype,
     void* stream);
+
+/* pkv_paged_attention_prefill over 8-bit E4M3 caches (article §4.2: an
+ * 8-bit cache; §4.1/§4.2: chunked prefill): K = code value * k_scale,
+ * V = code value * v_scale, the query (and so the matrix-core type of
+ * Q K^T) bfloat16 or float16 as query_dtype says.  Each code widens exactly
+ * to that type for K and to float16 for V as a tile is staged, so the
+ * products and the float16 weights are those of the 16-bit call; the K
+ * scale multiplies the scores, the V scale the output rows.  Other
+ * arguments, limits and errors as pkv_paged_attention_prefill;
+ * PKV_ERR_INVALID for a scale that is not positive and finite. */
+int32_t pkv_paged_attention_prefill_fp8(
+    const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, const int32_t* context_lens,
+    const int32_t* cu_query_lens, int32_t num_seqs, int32_t num_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t max_blocks_per_seq, int32_t num_blocks, int32_t total_query_rows,
+    int32_t max_query_len, float scale, float k_scale, float v_scale, float* out,
+    int32_t query_dtype, void* stream);
 
 /* ======================================================================
  * Measurement

@@ -29,8 +29,10 @@ __all__ = [
     "paged_attention_decode_append_partials", "paged_attention_decode_step",
     "paged_attention_decode_step_mapped",
     "paged_attention_decode_partials", "paged_attention_decode_merge",
-    "paged_attention_prefill", "paged_kv_append_fp8", "paged_attention_decode_fp8",
-    "paged_attention_decode_fp8_partials", "paged_attention_decode_shared_prefix",
+    "paged_attention_prefill", "paged_attention_prefill_fp8", "paged_kv_append_fp8",
+    "paged_attention_decode_fp8",
+    "paged_attention_decode_fp8_partials", "paged_attention_decode_fp8_step",
+    "paged_attention_decode_shared_prefix",
     "paged_attention_decode_shared_prefix_step",
     "paged_attention_decode_shared_prefix_workspace_size",
     "paged_attention_decode_grouped_prefix", "paged_attention_decode_grouped_prefix_step",
@@ -154,6 +156,10 @@ _SIGNATURES = {
                                                        _I32, _I32, _I32, _I32, ctypes.c_float,
                                                        ctypes.c_float, ctypes.c_float, _I32, _P,
                                                        _P, ctypes.c_size_t, _I32, _P]),
+    "pkv_paged_attention_decode_fp8_step": (
+        _I32, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+               _I32, ctypes.c_float, ctypes.c_float, ctypes.c_float, _I32, _P, _P,
+               ctypes.c_size_t, _I32, _P]),
     "pkv_paged_attention_decode_shared_prefix_workspace_size": (
         _I32, [_I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, ctypes.POINTER(ctypes.c_size_t)]),
     "pkv_paged_attention_decode_shared_prefix": (_I32, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32,
@@ -183,6 +189,9 @@ _SIGNATURES = {
     "pkv_scheduler_stats": (_I32, [_P, _P]),
     "pkv_paged_attention_prefill": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                                            _I32, ctypes.c_float, _P, _I32, _P]),
+    "pkv_paged_attention_prefill_fp8": (
+        _I32, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+               ctypes.c_float, ctypes.c_float, ctypes.c_float, _P, _I32, _P]),
 }
 
 
@@ -1137,6 +1146,38 @@ def paged_attention_decode_fp8(query, key_cache, value_cache, block_tables, cont
                        partition_size, out, workspace, shared_blocks)
 
 
+def paged_attention_decode_fp8_step(query, key, value, key_cache, value_cache, block_tables,
+                                    context_lens, changes, scale, k_scale, v_scale,
+                                    max_context_len, partition_size=0, out=None, workspace=None,
+                                    shared_blocks=False):
+    """Step form of paged_attention_decode_fp8 (pkv_paged_attention_decode_fp8_step):
+    block_tables is the device table kept across steps (updated in place
+    with ``changes``); context_lens host int32 [B]; changes host int32 [n, 3];
+    key/value the step's new rows [B, Hkv, D] in the query's dtype, quantised
+    with k_scale / v_scale as paged_kv_append_fp8 does, or None."""
+    (nb, hkv, bs, d, b, hq), out, workspace, ws_ptr, ws_bytes = _decode_args(
+        query, key_cache, value_cache, block_tables, None, max_context_len, partition_size, out,
+        workspace, fp8=True)
+    lens = np.ascontiguousarray(np.asarray(context_lens, dtype=np.int32))
+    changes = np.ascontiguousarray(np.asarray(changes, dtype=np.int32).reshape(-1, 3))
+    if lens.shape != (b,):
+        raise InvalidArgument("context_lens must hold one length per sequence")
+    kp = vp = None
+    if key is not None or value is not None:
+        _dev(key, "key", dtype=query.dtype, ndim=3)
+        _dev(value, "value", dtype=query.dtype, ndim=3)
+        if tuple(key.shape) != (b, hkv, d) or value.shape != key.shape:
+            raise InvalidArgument("key/value must be [B, num_kv_heads, head_dim]")
+        kp, vp = key.data_ptr(), value.data_ptr()
+    _check(_lib.pkv_paged_attention_decode_fp8_step(
+        query.data_ptr(), kp, vp, key_cache.data_ptr(), value_cache.data_ptr(),
+        block_tables.data_ptr(), lens.ctypes.data, changes.ctypes.data, changes.shape[0], b, hq,
+        hkv, d, bs, block_tables.shape[1], nb, int(max_context_len), float(scale),
+        float(k_scale), float(v_scale), int(partition_size), out.data_ptr(), ws_ptr, ws_bytes,
+        _decode_code(query, shared_blocks), _stream(query)))
+    return out
+
+
 def paged_attention_decode_fp8_partials(query, key_cache, value_cache, block_tables,
                                         context_lens, scale, k_scale, v_scale, max_context_len,
                                         partition_size, out, workspace):
@@ -1369,8 +1410,31 @@ def paged_attention_prefill(query, key_cache, value_cache, block_tables, context
     query [sum c_b, Hq, D] (cache dtype); cu_query_lens [B+1] int32;
     context_lens [B] int32 counting the chunk; returns out float32.
     """
+    return _prefill(query, key_cache, value_cache, block_tables, context_lens, cu_query_lens,
+                    scale, max_query_len, out)
+
+
+def paged_attention_prefill_fp8(query, key_cache, value_cache, block_tables, context_lens,
+                                cu_query_lens, scale, k_scale, v_scale, max_query_len, out=None):
+    """Causal chunked prefill over 8-bit E4M3 caches
+    (pkv_paged_attention_prefill_fp8): as paged_attention_prefill with
+    K = code value * k_scale, V = code value * v_scale; query bfloat16 or
+    float16."""
+    return _prefill(query, key_cache, value_cache, block_tables, context_lens, cu_query_lens,
+                    scale, max_query_len, out, fp8=(k_scale, v_scale))
+
+
+def _prefill(query, key_cache, value_cache, block_tables, context_lens, cu_query_lens, scale,
+             max_query_len, out, fp8=None):
     nb, hkv, bs, d = _cache_dims(key_cache, value_cache)
-    _dev(query, "query", dtype=key_cache.dtype, ndim=3)
+    if fp8 is None:
+        _dev(query, "query", dtype=key_cache.dtype, ndim=3)
+    else:
+        if key_cache.dtype not in _FP8_TYPES:
+            raise InvalidArgument("an 8-bit cache must be uint8 or float8_e4m3fn")
+        _dev(query, "query", ndim=3)
+        if query.dtype not in (torch.bfloat16, torch.float16):
+            raise InvalidArgument("the query of an 8-bit cache must be bfloat16 or float16")
     _dev(block_tables, "block_tables", dtype=torch.int32, ndim=2)
     _dev(context_lens, "context_lens", dtype=torch.int32, ndim=1)
     _dev(cu_query_lens, "cu_query_lens", dtype=torch.int32, ndim=1)
@@ -1383,9 +1447,14 @@ def paged_attention_prefill(query, key_cache, value_cache, block_tables, context
     _dev(out, "out", dtype=torch.float32, ndim=3)
     if tuple(out.shape) != (total, hq, d):
         raise InvalidArgument("out must be [sum c_b, Hq, D]")
-    _check(_lib.pkv_paged_attention_prefill(
-        query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(), block_tables.data_ptr(),
-        context_lens.data_ptr(), cu_query_lens.data_ptr(), b, hq, hkv, d, bs,
-        block_tables.shape[1], nb, total, int(max_query_len), float(scale), out.data_ptr(),
-        _dtype_code(key_cache), _stream(query)))
+    args = (query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+            block_tables.data_ptr(), context_lens.data_ptr(), cu_query_lens.data_ptr(), b, hq,
+            hkv, d, bs, block_tables.shape[1], nb, total, int(max_query_len), float(scale))
+    if fp8 is None:
+        _check(_lib.pkv_paged_attention_prefill(*args, out.data_ptr(), _dtype_code(key_cache),
+                                                _stream(query)))
+    else:
+        _check(_lib.pkv_paged_attention_prefill_fp8(*args, float(fp8[0]), float(fp8[1]),
+                                                    out.data_ptr(), _dtype_code(query),
+                                                    _stream(query)))
     return out

@@ -43,6 +43,7 @@
 #include <vector>
 
 #include "common.h"
+#include "fp8_codes.h"
 
 namespace pkv {
 namespace {
@@ -184,6 +185,7 @@ struct Slice32 {
 
 template <class Half>
 struct ElemFp8 {
+  static constexpr int kSrc = Half::kDtype;  // the query's (and new rows') type
   static constexpr int kBytes = 1;
   static constexpr int kPerLane = 16;
   static constexpr int kQBytes = 2;
@@ -219,6 +221,7 @@ struct ElemFp8 {
 // Codes 0, 1 (hi = false) or 2, 3 (hi = true) of a word as a 16-bit pair,
 // and the packed dot product with a pair of query elements.
 struct HalfBf16 {
+  static constexpr int kDtype = PKV_BF16;
   __device__ static bf16x2_t widen_pair(uint32_t w, bool hi) {
     return hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
               : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
@@ -229,6 +232,7 @@ struct HalfBf16 {
 };
 
 struct HalfF16 {
+  static constexpr int kDtype = PKV_F16;
   __device__ static f16x2_t widen_pair(uint32_t w, bool hi) {
     return hi ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true)
               : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
@@ -455,7 +459,7 @@ struct DecodeParams {
   int32_t num_kv_heads, log2_bs, max_blocks, num_blocks, max_ctx, part, max_parts;
   int32_t grid_parts;          // partitions per sequence in the grid (<= max_parts)
   float scale_log2;            // scale * log2(e), times the K scale of an 8-bit cache
-  float v_scale;               // V scale of an 8-bit cache (unused otherwise)
+  float k_scale, v_scale;      // scales of an 8-bit cache (unused otherwise)
   int32_t shared_blocks;       // nonzero: launch the cached-load kernel (shared blocks)
   // Suffix mode (shared-prefix decode), when row_info is set: the launch
   // covers tokens [start, len) of every sequence, start being the prefix
@@ -655,21 +659,33 @@ __global__ __launch_bounds__(kThreads, (decode_min_blocks<DT, G>())) void decode
   // its stores before its own loads (workgroup scope: the stores reach this
   // XCD's L2, the loads miss the L1, which starts every launch empty).  No
   // device-scope fence is needed -- on this GPU one writes back the XCD's
-  // whole L2.
-  if (!E::kQuantised && prm.key_new != nullptr && p_idx == nparts - 1) {
+  // whole L2.  An 8-bit cache takes the new rows in the query's 16-bit type
+  // and quantises each 16-element piece as the quantising append does.
+  // (8-bit caches: the step form only)
+  if constexpr (!E::kQuantised || Meta::kHost) {
+  if (prm.key_new != nullptr && p_idx == nparts - 1) {
     const int pos = n - 1 - p0;  // within the partition
     if (tid < 2 * C::kLpt && !bad_blk) {
       const int id = s_blk[pos >> log2_bs];
       const bool is_v = tid >= C::kLpt;
       const int piece = tid - (is_v ? C::kLpt : 0);
-      const int64_t src = (int64_t(b) * num_kv_heads + kvh) * C::kRow + piece * 16;
       const int64_t dst = int64_t(id) * blk_stride + int64_t(kvh) * tile_bytes +
                           int64_t(pos & (bs - 1)) * C::kRow + piece * 16;
       const uint8_t* from = is_v ? prm.value_new : prm.key_new;
       uint8_t* to = const_cast<uint8_t*>(is_v ? prm.value_cache : prm.key_cache);
-      *reinterpret_cast<uint4*>(to + dst) = *reinterpret_cast<const uint4*>(from + src);
+      if constexpr (E::kQuantised) {
+        // 16 codes from 16 elements of 2 bytes
+        const int64_t src = ((int64_t(b) * num_kv_heads + kvh) * D + piece * 16) * 2;
+        float f[16];
+        Src16<E::kSrc>::load(from + src, f);
+        *reinterpret_cast<uint4*>(to + dst) = quantize16(f, is_v ? prm.v_scale : prm.k_scale);
+      } else {
+        const int64_t src = (int64_t(b) * num_kv_heads + kvh) * C::kRow + piece * 16;
+        *reinterpret_cast<uint4*>(to + dst) = *reinterpret_cast<const uint4*>(from + src);
+      }
     }
     __syncthreads();
+  }
   }
 
   // q slices of the G heads: lane covers bytes (lane % LPT) * 16 of the row;
@@ -1077,16 +1093,11 @@ hipError_t dispatch_decode(int32_t dtype, int D, int G, const DecodeParams& prm,
       return D == 64 ? dispatch_group<PKV_F16, 64>(G, prm, meta, B, s)
                      : dispatch_group<PKV_F16, 128>(G, prm, meta, B, s);
     case kFp8QBf16:
+      return D == 64 ? dispatch_group<kFp8QBf16, 64>(G, prm, meta, B, s)
+                     : dispatch_group<kFp8QBf16, 128>(G, prm, meta, B, s);
     case kFp8QF16:
-      if constexpr (Meta::kHost) {
-        return hipErrorInvalidValue;  // 8-bit caches have no step form
-      } else if (dtype == kFp8QBf16) {
-        return D == 64 ? dispatch_group<kFp8QBf16, 64>(G, prm, meta, B, s)
-                       : dispatch_group<kFp8QBf16, 128>(G, prm, meta, B, s);
-      } else {
-        return D == 64 ? dispatch_group<kFp8QF16, 64>(G, prm, meta, B, s)
-                       : dispatch_group<kFp8QF16, 128>(G, prm, meta, B, s);
-      }
+      return D == 64 ? dispatch_group<kFp8QF16, 64>(G, prm, meta, B, s)
+                     : dispatch_group<kFp8QF16, 128>(G, prm, meta, B, s);
     default:
       return D == 64 ? dispatch_group<PKV_F32, 64>(G, prm, meta, B, s)
                      : dispatch_group<PKV_F32, 128>(G, prm, meta, B, s);
@@ -1303,6 +1314,7 @@ int32_t run_decode(const void* query, const void* key_new, const void* value_new
   prm.max_parts = a.max_parts;
   prm.grid_parts = a.max_parts;
   prm.scale_log2 = k_scale == 1.0f ? scale * kLog2e : (scale * k_scale) * kLog2e;
+  prm.k_scale = k_scale;
   prm.v_scale = v_scale;
   prm.shared_blocks = shared_blocks ? 1 : 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -1593,7 +1605,8 @@ int32_t fp8_call(const void* query, const void* key_cache, const void* value_cac
                  int32_t max_blocks_per_seq, int32_t num_blocks, int32_t max_context_len,
                  float scale, float k_scale, float v_scale, int32_t partition_size, float* out,
                  void* workspace, size_t workspace_bytes_given, int32_t query_dtype,
-                 void* stream, bool merge) {
+                 void* stream, bool merge, const void* key_new = nullptr,
+                 const void* value_new = nullptr, const StepPlan* step = nullptr) {
   const int32_t hint = query_dtype & int32_t(PKV_DECODE_SHARED_BLOCKS);
   query_dtype &= ~int32_t(PKV_DECODE_SHARED_BLOCKS);
   if (query_dtype != PKV_BF16 && query_dtype != PKV_F16)
@@ -1601,14 +1614,32 @@ int32_t fp8_call(const void* query, const void* key_cache, const void* value_cac
                 query_dtype);
   if (!(std::isfinite(k_scale) && k_scale > 0.0f && std::isfinite(v_scale) && v_scale > 0.0f))
     return fail(PKV_ERR_INVALID, "k_scale and v_scale must be positive and finite");
-  return run_decode(query, nullptr, nullptr, key_cache, value_cache, block_tables,
+  return run_decode(query, key_new, value_new, key_cache, value_cache, block_tables,
                     context_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                     max_blocks_per_seq, num_blocks, max_context_len, scale, partition_size,
                     out, workspace, workspace_bytes_given,
                     (query_dtype == PKV_BF16 ? kFp8QBf16 : kFp8QF16) | hint, stream, true, merge,
-                    nullptr, k_scale, v_scale);
+                    step, k_scale, v_scale);
 }
 }  // namespace
+
+extern "C" int32_t pkv_paged_attention_decode_fp8_step(
+    const void* query, const void* key, const void* value, void* key_cache,
+    void* value_cache, int32_t* block_tables, const int32_t* context_lens,
+    const int32_t* changes, int32_t num_changes, int32_t num_seqs, int32_t num_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+    int32_t num_blocks, int32_t max_context_len, float scale, float k_scale, float v_scale,
+    int32_t partition_size, float* out, void* workspace, size_t workspace_bytes_given,
+    int32_t query_dtype, void* stream) {
+  StepPlan plan;
+  int32_t st = make_step_plan(context_lens, changes, num_changes, num_seqs, num_kv_heads,
+                              max_blocks_per_seq, &plan);
+  if (st != PKV_OK) return st;
+  return fp8_call(query, key_cache, value_cache, block_tables, nullptr, num_seqs, num_heads,
+                  num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
+                  max_context_len, scale, k_scale, v_scale, partition_size, out, workspace,
+                  workspace_bytes_given, query_dtype, stream, true, key, value, &plan);
+}
 
 extern "C" int32_t pkv_paged_attention_decode_fp8(
     const void* query, const void* key_cache, const void* value_cache,

@@ -17,6 +17,7 @@
 #include <cmath>
 
 #include "common.h"
+#include "fp8_codes.h"
 
 namespace pkv {
 namespace {
@@ -46,89 +47,9 @@ __global__ __launch_bounds__(256) void append_kernel(
   value_cache[dst] = value[i];
 }
 
-// Quantising append into an 8-bit (E4M3) cache.  One lane per 16 elements
-// of a (token, kv-head) row: it reads them from K and from V in the source
-// type, divides each by the cache's scale (float32, correctly rounded),
-// clamps to the largest finite code value, and converts pairs with the
-// hardware conversion (round to nearest, ties to even); the 16 codes are
-// one 16-byte store.  The clamp first makes the conversion saturating,
-// as the stored format requires: a value above 448 rounds to 448 either
-// way, and a NaN passes the clamp and stays NaN.
-template <int SRC>
-struct Src16;
-
-template <>
-struct Src16<PKV_F32> {
-  static constexpr int kBytes = 64;
-  __device__ static void load(const uint8_t* p, float (&f)[16]) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint4 w = reinterpret_cast<const uint4*>(p)[j];
-      f[4 * j] = __uint_as_float(w.x);
-      f[4 * j + 1] = __uint_as_float(w.y);
-      f[4 * j + 2] = __uint_as_float(w.z);
-      f[4 * j + 3] = __uint_as_float(w.w);
-    }
-  }
-};
-
-template <>
-struct Src16<PKV_BF16> {
-  static constexpr int kBytes = 32;
-  __device__ static void load(const uint8_t* p, float (&f)[16]) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const uint4 w = reinterpret_cast<const uint4*>(p)[j];
-      const uint32_t x[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f[8 * j + 2 * i] = __uint_as_float(x[i] << 16);
-        f[8 * j + 2 * i + 1] = __uint_as_float(x[i] & 0xffff0000u);
-      }
-    }
-  }
-};
-
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-
-template <>
-struct Src16<PKV_F16> {
-  static constexpr int kBytes = 32;
-  __device__ static void load(const uint8_t* p, float (&f)[16]) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const uint4 w = reinterpret_cast<const uint4*>(p)[j];
-      const uint32_t x[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const half2_t h = __builtin_bit_cast(half2_t, x[i]);
-        f[8 * j + 2 * i] = float(h.x);
-        f[8 * j + 2 * i + 1] = float(h.y);
-      }
-    }
-  }
-};
-
-constexpr float kE4m3Max = 448.0f;
-
-__device__ __forceinline__ float to_code_range(float x, float scale) {
-  const float y = x / scale;
-  return y > kE4m3Max ? kE4m3Max : (y < -kE4m3Max ? -kE4m3Max : y);
-}
-
-__device__ __forceinline__ uint4 quantize16(const float (&f)[16], float scale) {
-  uint32_t w[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    // bytes 0, 1 from the low-word conversion, bytes 2, 3 from the high
-    const uint32_t lo = __builtin_amdgcn_cvt_pk_fp8_f32(
-        to_code_range(f[4 * j], scale), to_code_range(f[4 * j + 1], scale), 0, false);
-    w[j] = __builtin_amdgcn_cvt_pk_fp8_f32(to_code_range(f[4 * j + 2], scale),
-                                           to_code_range(f[4 * j + 3], scale), lo, true);
-  }
-  return make_uint4(w[0], w[1], w[2], w[3]);
-}
-
+// Quantising append into an 8-bit (E4M3) cache: one lane per 16 elements
+// of a (token, kv-head) row, quantised by quantize16 (fp8_codes.h) into one
+// 16-byte store.
 template <int SRC>
 __global__ __launch_bounds__(256) void append_fp8_kernel(
     const uint8_t* __restrict__ key, const uint8_t* __restrict__ value,

@@ -82,8 +82,21 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 template <int DT>
 struct Half;
 
+// Codes 0, 1 (hi = false) or 2, 3 (hi = true) of a word of E4M3 codes as
+// a float16 pair (exact: 3 mantissa bits, exponents within float16's).
+__device__ __forceinline__ uint32_t fp8_to_f16x2(uint32_t w, bool hi) {
+  return __builtin_bit_cast(uint32_t, hi ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true)
+                                         : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+}
+
 template <>
 struct Half<PKV_BF16> {
+  // two E4M3 codes as a bfloat16 pair (exact)
+  __device__ static uint32_t from_fp8(uint32_t w, bool hi) {
+    return __builtin_bit_cast(uint32_t,
+                              hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
+                                 : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+  }
   __device__ static f32x4 mma(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
@@ -96,6 +109,7 @@ struct Half<PKV_BF16> {
 
 template <>
 struct Half<PKV_F16> {
+  __device__ static uint32_t from_fp8(uint32_t w, bool hi) { return fp8_to_f16x2(w, hi); }
   __device__ static f32x4 mma(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
@@ -163,14 +177,19 @@ struct PrefixArgs {
   PrefixGroups groups;
 };
 
-template <int DT, bool kPrefix>
+// kFp8: the caches hold 8-bit E4M3 codes (DT is the query's type); the
+// gather widens each code exactly to DT for K and to float16 for V as it
+// stages the tile, so the products are those of the 16-bit path; the K scale
+// is in scale_log2 and the V scale (v_scale) multiplies the output rows.
+template <int DT, bool kPrefix, bool kFp8 = false>
 __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
     const uint16_t* __restrict__ query, const uint16_t* __restrict__ key_cache,
     const uint16_t* __restrict__ value_cache, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ context_lens, const int32_t* __restrict__ cu_query_lens,
     int32_t num_heads, int32_t group, int32_t log2_bs, int32_t max_blocks,
     int32_t num_blocks, int32_t total_q, int32_t max_q, float scale_log2,
-    float* __restrict__ out, const PrefixArgs pfx) {
+    float* __restrict__ out, const PrefixArgs pfx, float v_scale = 1.0f) {
+  static_assert(!(kFp8 && kPrefix), "8-bit caches: chunked prefill only");
   using H = Half<DT>;
   __shared__ __attribute__((aligned(16))) uint8_t s_k[2][kLdsK];
   __shared__ __attribute__((aligned(16))) uint8_t s_v[2][kLdsV];
@@ -280,8 +299,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
 
   // ---- tile gather ----------------------------------------------------------
   // piece i of this thread: key 16 i + pk of the tile, dims 8 pd .. + 7
-  // pieces per thread and tile; a piece row within its 16-key group
-  constexpr int kPieces = kKTile * 16 / kThreads;
+  // pieces per thread and tile; a piece row within its 16-key group.
+  // 8-bit caches: one piece per thread, key tid / 8 of the tile, dims
+  // 16 (tid % 8) .. + 15 (16 codes), widened to two 16-byte LDS pieces.
+  constexpr int kPieces = kFp8 ? 1 : kKTile * 16 / kThreads;
   constexpr int kPieceStride = kThreads / 16;  // keys between a thread's pieces
   const int pk = tid >> 4, pd = tid & 15;
   const int64_t tile_elems = int64_t(bs) * kD;
@@ -300,8 +321,28 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
   // re-reads the 16-aligned group holding key kv_end - 1 (a valid row range
   // of a checked block); keys past kv_end, whatever they read, are zeroed
   // when the last, partial tile is stored.
+  // 8-bit caches: the key of this thread's piece and its 16 codes' offset
+  const int fkey = tid >> 3, fpd = tid & 7;
+  const uint8_t* k8_head = reinterpret_cast<const uint8_t*>(key_cache) + int64_t(kvh) * tile_elems;
+  const uint8_t* v8_head =
+      reinterpret_cast<const uint8_t*>(value_cache) + int64_t(kvh) * tile_elems;
+  const uint32_t lane_bytes8 = uint32_t((fkey & 15) * kD + 16 * fpd);  // within a 16-key group
   auto load_tile = [&](int j) {
     const int key0 = j * kKTile;
+    if constexpr (kFp8) {
+      // the 16-key group of key tid / 8 is 16 (wave / 2): a scalar
+      const int gkey = min(key0 + 16 * (wave >> 1), kv_end - 1);
+      int id = __builtin_amdgcn_readfirstlane(table[gkey >> log2_bs]);
+      if (id < 0 || id >= num_blocks) {
+        bad_blk = true;
+        id = 0;
+      }
+      // element offsets are byte offsets for 1-byte codes
+      const int64_t grp8 = int64_t(id) * blk_elems + int64_t(gkey & (bs - 1) & ~15) * kD;
+      gk[0] = *reinterpret_cast<const u32x4*>(k8_head + grp8 + lane_bytes8);
+      gv[0] = *reinterpret_cast<const u32x4*>(v8_head + grp8 + lane_bytes8);
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < kPieces; ++i) {
       // the piece's 16-key group, 16 (pk >> 4) = 16 (tid >> 8), is the same
@@ -321,6 +362,24 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
 
   auto store_tile = [&](int buf, int j) {
     const int key0 = j * kKTile;
+    if constexpr (kFp8) {
+      if (key0 + fkey >= kv_end) gk[0] = gv[0] = u32x4{0, 0, 0, 0};  // code 0 is +0
+      u32x4 k2[2], v2[2];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        k2[w / 2][2 * (w % 2)] = H::from_fp8(gk[0][w], false);
+        k2[w / 2][2 * (w % 2) + 1] = H::from_fp8(gk[0][w], true);
+        v2[w / 2][2 * (w % 2)] = fp8_to_f16x2(gv[0][w], false);
+        v2[w / 2][2 * (w % 2) + 1] = fp8_to_f16x2(gv[0][w], true);
+      }
+      uint8_t* kr = s_k[buf] + fkey * kKRow + 32 * fpd;
+      uint8_t* vr = s_v[buf] + fkey * kVRow + 32 * fpd;
+      *reinterpret_cast<u32x4*>(kr) = k2[0];
+      *reinterpret_cast<u32x4*>(kr + 16) = k2[1];
+      *reinterpret_cast<u32x4*>(vr) = v2[0];
+      *reinterpret_cast<u32x4*>(vr + 16) = v2[1];
+      return;
+    }
     if (key0 + kKTile > kv_end) {  // last tile: zero the keys past the range
 #pragma unroll
       for (int i = 0; i < kPieces; ++i)
@@ -513,7 +572,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
       }
       continue;
     }
-    const float inv = bad_blk ? __builtin_nanf("") : 1.0f / l;
+    const float inv = bad_blk ? __builtin_nanf("") : (kFp8 ? v_scale / l : 1.0f / l);
     float* row = out + (int64_t(q0 + i) * num_heads + h) * kD;
 #pragma unroll
     for (int dt = 0; dt < kD / 16; ++dt)
@@ -526,17 +585,27 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
 
 using namespace pkv;
 
-extern "C" int32_t pkv_paged_attention_prefill(
-    const void* query, const void* key_cache, const void* value_cache,
-    const int32_t* block_tables, const int32_t* context_lens,
-    const int32_t* cu_query_lens, int32_t num_seqs, int32_t num_heads,
-    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-    int32_t max_blocks_per_seq, int32_t num_blocks, int32_t total_query_rows,
-    int32_t max_query_len, float scale, float* out, int32_t dtype, void* stream) {
+namespace {
+// The chunked prefill over 16-bit caches (dtype = the caches' and query's
+// type) or over 8-bit caches (fp8: dtype = the query's type, the caches
+// E4M3 codes with per-cache scales).
+int32_t prefill_call(const void* query, const void* key_cache, const void* value_cache,
+                     const int32_t* block_tables, const int32_t* context_lens,
+                     const int32_t* cu_query_lens, int32_t num_seqs, int32_t num_heads,
+                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                     int32_t max_blocks_per_seq, int32_t num_blocks, int32_t total_query_rows,
+                     int32_t max_query_len, float scale, float k_scale, float v_scale,
+                     float* out, int32_t dtype, void* stream, bool fp8) {
   if (dtype != PKV_BF16 && dtype != PKV_F16) {
+    if (fp8)
+      return fail(PKV_ERR_INVALID, "query_dtype %d must be BF16 or F16 for an 8-bit cache",
+                  dtype);
     if (dtype_bytes(dtype) == 0) return fail(PKV_ERR_INVALID, "unknown dtype %d", dtype);
     return fail(PKV_ERR_UNSUPPORTED, "chunked prefill needs a float16 or bfloat16 cache");
   }
+  if (fp8 && !(std::isfinite(k_scale) && k_scale > 0.0f && std::isfinite(v_scale) &&
+               v_scale > 0.0f))
+    return fail(PKV_ERR_INVALID, "k_scale and v_scale must be positive and finite");
   if (num_seqs < 0 || total_query_rows < 0 || max_query_len < 0)
     return fail(PKV_ERR_INVALID, "negative size");
   if (num_seqs > 65535) return fail(PKV_ERR_UNSUPPORTED, "at most 65535 sequences per call");
@@ -562,26 +631,57 @@ extern "C" int32_t pkv_paged_attention_prefill(
   if (tiles > 65535) return fail(PKV_ERR_UNSUPPORTED, "max_query_len too large");
   int log2_bs = 0;
   while ((1 << log2_bs) < block_size) ++log2_bs;
-  const float sl2 = scale * kLog2e;
+  const float sl2 = (fp8 ? scale * k_scale : scale) * kLog2e;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid(num_heads, unsigned(tiles), num_seqs);
   const int group = num_heads / num_kv_heads;
+  const auto* q = static_cast<const uint16_t*>(query);
+  const auto* kc = static_cast<const uint16_t*>(key_cache);
+  const auto* vc = static_cast<const uint16_t*>(value_cache);
+#define PKV_PREFILL_LAUNCH(DT, FP8)                                                           \
+  hipLaunchKernelGGL((prefill_kernel<DT, false, FP8>), grid, dim3(kThreads), 0, s, q, kc, vc, \
+                     block_tables, context_lens, cu_query_lens, num_heads, group, log2_bs,      \
+                     max_blocks_per_seq, num_blocks, total_query_rows, max_query_len, sl2, out, \
+                     PrefixArgs{}, v_scale)
   if (dtype == PKV_BF16) {
-    hipLaunchKernelGGL((prefill_kernel<PKV_BF16, false>), grid, dim3(kThreads), 0, s,
-                       static_cast<const uint16_t*>(query), static_cast<const uint16_t*>(key_cache),
-                       static_cast<const uint16_t*>(value_cache), block_tables, context_lens,
-                       cu_query_lens, num_heads, group, log2_bs, max_blocks_per_seq, num_blocks,
-                       total_query_rows, max_query_len, sl2, out, PrefixArgs{});
+    if (fp8) PKV_PREFILL_LAUNCH(PKV_BF16, true);
+    else PKV_PREFILL_LAUNCH(PKV_BF16, false);
   } else {
-    hipLaunchKernelGGL((prefill_kernel<PKV_F16, false>), grid, dim3(kThreads), 0, s,
-                       static_cast<const uint16_t*>(query), static_cast<const uint16_t*>(key_cache),
-                       static_cast<const uint16_t*>(value_cache), block_tables, context_lens,
-                       cu_query_lens, num_heads, group, log2_bs, max_blocks_per_seq, num_blocks,
-                       total_query_rows, max_query_len, sl2, out, PrefixArgs{});
+    if (fp8) PKV_PREFILL_LAUNCH(PKV_F16, true);
+    else PKV_PREFILL_LAUNCH(PKV_F16, false);
   }
+#undef PKV_PREFILL_LAUNCH
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
   return ok();
+}
+}  // namespace
+
+extern "C" int32_t pkv_paged_attention_prefill(
+    const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, const int32_t* context_lens,
+    const int32_t* cu_query_lens, int32_t num_seqs, int32_t num_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t max_blocks_per_seq, int32_t num_blocks, int32_t total_query_rows,
+    int32_t max_query_len, float scale, float* out, int32_t dtype, void* stream) {
+  return prefill_call(query, key_cache, value_cache, block_tables, context_lens, cu_query_lens,
+                      num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                      max_blocks_per_seq, num_blocks, total_query_rows, max_query_len, scale,
+                      1.0f, 1.0f, out, dtype, stream, false);
+}
+
+extern "C" int32_t pkv_paged_attention_prefill_fp8(
+    const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, const int32_t* context_lens,
+    const int32_t* cu_query_lens, int32_t num_seqs, int32_t num_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t max_blocks_per_seq, int32_t num_blocks, int32_t total_query_rows,
+    int32_t max_query_len, float scale, float k_scale, float v_scale, float* out,
+    int32_t query_dtype, void* stream) {
+  return prefill_call(query, key_cache, value_cache, block_tables, context_lens, cu_query_lens,
+                      num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                      max_blocks_per_seq, num_blocks, total_query_rows, max_query_len, scale,
+                      k_scale, v_scale, out, query_dtype, stream, true);
 }
 
 // The prefix part of the shared-prefix decode: the prefill kernel in

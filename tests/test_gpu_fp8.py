@@ -16,7 +16,7 @@ import torch
 import paged_kv_cache_420_amd as pkv
 import workloads
 from cases import (DEV, GpuStateFp8, OracleStateFp8, decode_queries, log, logical_kv_fp8,
-                   logical_segments, max_abs_err)
+                   logical_segments, max_abs_err, parallel_map)
 from oracle import dense_attention, fp8, paged_decode
 
 pytestmark = pytest.mark.gpu
@@ -199,10 +199,10 @@ def test_fp8_zero_length_and_inconsistent_rows():
     assert np.isnan(out[2]).all() and np.isnan(out[3]).all()
 
 
-def test_fp8_full_size_sampled_against_oracle():
+def test_fp8_full_size_every_sequence_against_oracle():
     """The LLaMA-7B-shaped batch at full size, in the launch configuration
-    the benchmark's 8-bit leg times, sampled sequences against oracle
-    attention over their dequantised logical K/V."""
+    the benchmark's 8-bit leg times: every sequence and head against oracle
+    attention over its dequantised logical K/V."""
     w = workloads.get("llama7b_bf16")
     ks, vs = workloads.FP8_SCALES
     p = workloads.plan(w)
@@ -212,17 +212,14 @@ def test_fp8_full_size_sampled_against_oracle():
     got = pkv.paged_attention_decode_fp8(q.to(DEV), g.kc, g.vc, tables, lens, w.scale, ks, vs,
                                          int(lh.max())).cpu().numpy()
     segs = logical_segments(p.ops)
-    rng = np.random.default_rng(8)
-    pick = sorted(set(rng.choice(len(p.seqs), size=6, replace=False).tolist())
-                  | {int(np.argmax(lh)), int(np.argmin(lh))})
-    worst = 0.0
-    for b in pick:
+
+    def err(b):
         k, v = logical_kv_fp8(w, segs[p.seqs[b]], ks, vs)
-        want = dense_attention(q64[b][None], k, v, w.scale)[0]
-        worst = max(worst, max_abs_err(got[b], want))
-    log("fp8 full size sampled max abs err", worst, "over", len(pick), "sequences")
+        return max_abs_err(got[b], dense_attention(q64[b][None], k, v, w.scale)[0])
+
+    worst = max(parallel_map(err, range(len(p.seqs))))
+    log("fp8 full size, every sequence and head: max abs err", worst)
     assert worst <= TOL_FP8
-    assert np.isfinite(got).all()
 
 
 def test_fp8_rejects_bad_arguments():
@@ -256,3 +253,158 @@ def test_fp8_shared_blocks_hint_changes_no_bit():
                                          partition_size=64, shared_blocks=True)
     torch.cuda.synchronize()
     assert torch.equal(got, want)
+
+
+STEP_FP8 = {
+    "bf16_g1_part64": (workloads.scaled(workloads.get("llama7b_bf16"), num_seqs=5, num_heads=4,
+                                        num_kv_heads=4, lens="uniform:1,400"), 0.013, 0.011, 64),
+    "f16_g8_part1024": (workloads.scaled(workloads.get("llama13b_fp16"), num_seqs=4,
+                                         num_heads=16, num_kv_heads=2, block_size=16,
+                                         lens="uniform:1,1500"), 0.0071, 0.0093, 1024),
+    "bf16_g4_d64": (workloads.scaled(workloads.get("llama7b_bf16"), num_seqs=6, num_heads=8,
+                                     num_kv_heads=2, head_dim=64, lens="uniform:1,300"),
+                    5.0 / 448, 4.5 / 448, 128),
+}
+
+
+@pytest.mark.parametrize("name", list(STEP_FP8))
+def test_fp8_step_is_quantising_append_then_decode(name):
+    """pkv_paged_attention_decode_fp8_step (host lengths and table changes
+    by value, the new rows quantised and stored by the decode kernel) ==
+    pkv_paged_kv_append_fp8 then pkv_paged_attention_decode_fp8 on freshly
+    uploaded tables, bit for bit (outputs, cache codes, device table), over
+    20 steps that open new blocks; the last step's every row against the
+    oracle over the dequantised cache, the new rows quantised by the
+    oracle."""
+    w, ks, vs, part = STEP_FP8[name]
+    log("case", name, w, ks, vs, part)
+    p = workloads.plan(w)
+    a, b = GpuStateFp8(w, p, ks, vs), GpuStateFp8(w, p, ks, vs)
+    seqs = p.seqs
+    steps = 20
+    mb = max(len(a.alloc.block_table(s)) for s in seqs) + steps // w.block_size + 2
+    th, _ = b.alloc.build_block_tables(seqs, mb)
+    dev_tables = torch.from_numpy(th.copy()).to(DEV)
+    ones = np.ones(len(seqs), dtype=np.int32)
+    new_k, new_v = [], []
+    for i in range(steps):
+        k, v = workloads.kv_rows(w, len(p.ops) + i, len(seqs))
+        kt, vt = workloads.to_dtype(k, w.dtype), workloads.to_dtype(v, w.dtype)
+        new_k.append(fp8.dequantize(fp8.quantize(workloads.as_f64(kt), ks), ks))
+        new_v.append(fp8.dequantize(fp8.quantize(workloads.as_f64(vt), vs), vs))
+        kt, vt = kt.to(DEV), vt.to(DEV)
+        qt = workloads.to_dtype(workloads.normal([w.seed, 31, i], (len(seqs), w.num_heads,
+                                                                    w.head_dim), w.std), w.dtype)
+        slots, pa = a.alloc.append_batch(seqs, ones)
+        _, pb, lens, changes = b.alloc.append_batch_changes(seqs, ones)
+        assert not pa and not pb
+        pkv.paged_kv_append_fp8(kt, vt, a.kc, a.vc, torch.from_numpy(slots).to(DEV), ks, vs)
+        ta, la, _, lh = a.tables(seqs)
+        ta = torch.nn.functional.pad(ta, (0, mb - ta.shape[1]), value=-1).contiguous()
+        mc = int(lh.max())
+        want = pkv.paged_attention_decode_fp8(qt.to(DEV), a.kc, a.vc, ta, la, w.scale, ks, vs, mc,
+                                              partition_size=part)
+        got = pkv.paged_attention_decode_fp8_step(qt.to(DEV), kt, vt, b.kc, b.vc, dev_tables,
+                                                  lens, changes, w.scale, ks, vs, mc,
+                                                  partition_size=part)
+        torch.cuda.synchronize()
+        assert torch.equal(got, want), f"step {i}"
+    assert torch.equal(a.kc, b.kc) and torch.equal(a.vc, b.vc)
+    th, _ = b.alloc.build_block_tables(seqs, mb)
+    assert np.array_equal(dev_tables.cpu().numpy(), th)
+    got = got.cpu().numpy()
+    q64 = workloads.as_f64(qt)
+    segs = logical_segments(p.ops)
+    worst = 0.0
+    for r, s in enumerate(seqs):
+        k, v = logical_kv_fp8(w, segs[s], ks, vs)
+        k = np.concatenate([k] + [x[r][None] for x in new_k])
+        v = np.concatenate([v] + [x[r][None] for x in new_v])
+        worst = max(worst, max_abs_err(got[r], dense_attention(q64[r][None], k, v, w.scale)[0]))
+    log(name, "last step, every row: max abs err", worst)
+    assert worst <= TOL_FP8
+
+
+# ---------------------------------------------------------------------------
+# chunked prefill over 8-bit caches
+# ---------------------------------------------------------------------------
+
+from test_gpu_prefill import chunk_queries, ragged_plan  # noqa: E402
+from oracle import paged_prefill  # noqa: E402
+
+_PRE_BF16 = workloads.scaled(workloads.get("shared_prefix_bf16"), num_heads=4, num_kv_heads=4,
+                             prefix=0, chunk=0)
+_PRE_F16 = workloads.scaled(workloads.get("llama13b_fp16"), num_heads=8, num_kv_heads=2)
+
+PREFILL_FP8 = {
+    # (workload, prior cached tokens, chunk rows, k_scale, v_scale)
+    "bf16_after_context": (_PRE_BF16, [5, 200, 1000], [130, 1, 257], 0.013, 0.011),
+    "f16_gqa4_from_empty_bs32": (_PRE_F16, [0, 0, 40], [1, 300, 77], 5.0 / 448, 4.5 / 448),
+    "bf16_bs64_saturating": (workloads.scaled(_PRE_BF16, num_heads=2, num_kv_heads=2,
+                                              block_size=64), [70, 500], [45, 300], 0.004, 0.0071),
+}
+
+
+def _fp8_prefill_state(w, prior, chunks, ks, vs):
+    p, cops = ragged_plan(w, prior, chunks)
+    g = GpuStateFp8(w, p, ks, vs)
+    g.run(cops, first_index=len(p.ops))
+    return p, cops, g
+
+
+@pytest.mark.parametrize("name", list(PREFILL_FP8))
+def test_fp8_prefill_matches_oracle(name):
+    """pkv_paged_attention_prefill_fp8 against the oracle's causal paged
+    prefill over the dequantised cache (codes written by the oracle's
+    quantiser from the same values, 0x7F NaN codes where unwritten)."""
+    w, prior, chunks, ks, vs = PREFILL_FP8[name]
+    log("case", name, prior, chunks, ks, vs)
+    p, cops, g = _fp8_prefill_state(w, prior, chunks, ks, vs)
+    o = OracleStateFp8(w, p, ks, vs)
+    o.run(cops, first_index=len(p.ops))
+    tables, lens, _, _ = g.tables(p.seqs)
+    q, cu = chunk_queries(w, p.seqs, chunks)
+    got = pkv.paged_attention_prefill_fp8(q.to(DEV), g.kc, g.vc, tables, lens,
+                                          torch.from_numpy(cu).to(DEV), w.scale, ks, vs,
+                                          max(chunks))
+    torch.cuda.synchronize()
+    ot, ol = o.tables()
+    want = paged_prefill(workloads.as_f64(q), o.kc, o.vc, ot, ol, cu, w.scale, w.block_size)
+    err = max_abs_err(got.cpu().numpy(), want)
+    log(name, "max abs err", err)
+    assert err <= TOL_FP8
+
+
+@pytest.mark.parametrize("name", list(PREFILL_FP8))
+def test_fp8_prefill_is_the_16bit_prefill_on_the_code_values(name):
+    """With unit scales the 8-bit prefill is, bit for bit, the 16-bit
+    prefill over a cache holding the code values (each code widens exactly
+    to bfloat16 / float16, and the staged tiles are then the same)."""
+    w, prior, chunks, _, _ = PREFILL_FP8[name]
+    p, cops, g = _fp8_prefill_state(w, prior, chunks, 1.0, 1.0)
+    tables, lens, _, _ = g.tables(p.seqs)
+    q, cu = chunk_queries(w, p.seqs, chunks)
+    cu_d = torch.from_numpy(cu).to(DEV)
+    got = pkv.paged_attention_prefill_fp8(q.to(DEV), g.kc, g.vc, tables, lens, cu_d, w.scale, 1.0,
+                                          1.0, max(chunks))
+    kc16 = g.kc.view(torch.float8_e4m3fn).to(w.dtype)
+    vc16 = g.vc.view(torch.float8_e4m3fn).to(w.dtype)
+    want = pkv.paged_attention_prefill(q.to(DEV), kc16, vc16, tables, lens, cu_d, w.scale,
+                                       max(chunks))
+    torch.cuda.synchronize()
+    assert torch.equal(got, want)
+
+
+def test_fp8_prefill_rejects_bad_arguments():
+    w, prior, chunks, ks, vs = PREFILL_FP8["bf16_after_context"]
+    p, cops, g = _fp8_prefill_state(w, prior, chunks, ks, vs)
+    tables, lens, _, _ = g.tables(p.seqs)
+    q, cu = chunk_queries(w, p.seqs, chunks)
+    cu_d = torch.from_numpy(cu).to(DEV)
+    for bad in ((0.0, vs), (ks, -1.0), (float("inf"), vs), (ks, float("nan"))):
+        with pytest.raises(pkv.InvalidArgument):
+            pkv.paged_attention_prefill_fp8(q.to(DEV), g.kc, g.vc, tables, lens, cu_d, w.scale,
+                                            bad[0], bad[1], max(chunks))
+    with pytest.raises(pkv.InvalidArgument):           # a float32 query
+        pkv.paged_attention_prefill_fp8(q.float().to(DEV), g.kc, g.vc, tables, lens, cu_d,
+                                        w.scale, ks, vs, max(chunks))
