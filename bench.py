@@ -32,9 +32,11 @@ after the timed steps, 20 launches back to back between one pair of HIP
 events on the stream it runs on; its ``traffic`` comes from the committed
 rocprofv3 counter summary of the same kernel source, when there is one.
 ``workloads`` carries the same figures for every other workload (20 steps
-after 5; their caches filled with values drawn on the device), and
+after 5; their caches filled with values drawn on the device),
 ``stream_read`` the achievable HBM read rate: a plain read of 4 GiB with
-the decode kernel's load width and policy.
+the decode kernel's load width and policy, and ``matrix_loop`` the
+matrix-core rate the GPU sustains with the prefill's product instruction in
+a register-only loop (each prefill entry then carries its fraction of it).
 ``cpu_baseline`` times the float64 CPU oracle on a small sample of the same
 workload (reported only; the host's CPU model and core count go into its
 ``sample``).  For the prefix workloads the line also carries
@@ -359,6 +361,23 @@ def stream_read_run(torch, pkv):
     del buf
     torch.cuda.empty_cache()
     return best
+
+
+def matrix_loop_run(torch, pkv):
+    """The matrix-core rate this GPU sustains: the chunked prefill's bf16
+    16 x 16 x 32 product in a register-only loop (pkv_matrix_loop), 2048
+    workgroups of four wavefronts (eight per CU) x 20000 iterations, mean of
+    5 back-to-back launches after 2 (the clock settles under the load)."""
+    dev = torch.device("cuda:0")
+    sink = torch.zeros(1, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    wg, iters = 2048, 20000
+    flops = wg * 4 * iters * 4 * 16384
+    ms = time_loop(torch, stream, lambda: pkv.matrix_loop(iters, wg, sink), 5, warm=2)
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {"instruction": "v_mfma_f32_16x16x32_bf16", "workgroups": wg, "iters": iters,
+            "flops_per_launch": flops, "ms": round(ms, 4), "tflops": round(tflops, 1),
+            "bf16_peak_frac": round(tflops / BF16_PEAK_TFLOPS, 4)}
 
 
 def shared_prefix_decode_run(w, p, alloc, kc, vc, torch, pkv, dev):
@@ -957,6 +976,11 @@ def main():
         sr = stream_read_run(torch, pkv)
         sr["decode_kernel_frac_of_stream_read"] = round(leg["kernel_gbps"] / sr["gbps"], 4)
         line["stream_read"] = sr
+        ml = matrix_loop_run(torch, pkv)
+        line["matrix_loop"] = ml
+        for pre in [line.get("prefill")] + [x.get("prefill") for x in extra.values()]:
+            if pre:
+                pre["frac_of_matrix_loop"] = round(pre["roofline"]["achieved"] / ml["tflops"], 4)
     line["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(w, workloads)
     print(json.dumps(line), flush=True)
 

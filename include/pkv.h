@@ -911,6 +911,18 @@ int32_t pkv_paged_attention_prefill_fp8(
 int32_t pkv_stream_read(const void* buffer, int64_t bytes, int32_t workgroups,
                         uint32_t* sink, void* stream);
 
+/* Run `iters` iterations of four independent v_mfma_f32_16x16x32_bf16
+ * products per wavefront -- the chunked prefill's product instruction --
+ * over `workgroups` workgroups of 256 threads, operands in registers and no
+ * memory traffic: the rate the matrix cores sustain on this GPU (at the
+ * clock they hold under that load), against which the prefill's share of
+ * the published peak is read.  One launch performs workgroups * 4 * iters
+ * * 4 * 16384 floating-point operations.  `sink` is a device float the
+ * kernel may write (it keeps the products live).  iters < 0 or workgroups
+ * outside [1, 2^20] is PKV_ERR_INVALID; iters == 0 launches nothing.
+ * Asynchronous on `stream`. */
+int32_t pkv_matrix_loop(int32_t iters, int32_t workgroups, float* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

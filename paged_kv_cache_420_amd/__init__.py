@@ -37,7 +37,7 @@ __all__ = [
     "paged_attention_decode_shared_prefix_workspace_size",
     "paged_attention_decode_grouped_prefix", "paged_attention_decode_grouped_prefix_step",
     "paged_attention_decode_grouped_prefix_workspace_size", "paged_attention_decode_noalloc",
-    "stream_read", "swap_blocks", "library_path", "version",
+    "stream_read", "matrix_loop", "swap_blocks", "library_path", "version",
 ]
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
@@ -143,6 +143,7 @@ _SIGNATURES = {
     "pkv_paged_attention_decode_merge": (_I32, [_P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P,
                                                 ctypes.c_size_t, _P]),
     "pkv_stream_read": (_I32, [_P, _I64, _I32, _P, _P]),
+    "pkv_matrix_loop": (_I32, [_I32, _I32, _P, _P]),
     "pkv_paged_attention_decode_noalloc": (_I32, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
                                                   _I32, _I32, _I32, ctypes.c_float, _I32, _P, _I32,
                                                   _P]),
@@ -847,6 +848,17 @@ def stream_read(buffer, workgroups, sink):
         raise InvalidArgument("sink must hold at least 4 bytes")
     _check(_lib.pkv_stream_read(buffer.data_ptr(), buffer.numel() * buffer.element_size(),
                                 int(workgroups), sink.data_ptr(), _stream(buffer)))
+
+
+def matrix_loop(iters, workgroups, sink):
+    """Run ``iters`` iterations of four independent bf16 16x16x32 matrix
+    products per wavefront over ``workgroups`` workgroups of 256 threads
+    (pkv_matrix_loop, a measurement aid: the matrix-core rate this GPU
+    sustains); ``sink`` is a float32 device tensor the kernel may write.
+    Returns the floating-point operations one launch performs."""
+    _dev(sink, "sink", dtype=torch.float32)
+    _check(_lib.pkv_matrix_loop(int(iters), int(workgroups), sink.data_ptr(), _stream(sink)))
+    return int(workgroups) * 4 * int(iters) * 4 * 16384
 
 
 def paged_attention_decode_noalloc(query, key_cache, value_cache, block_tables, context_lens,

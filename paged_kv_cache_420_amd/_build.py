@@ -32,6 +32,10 @@ HIP_FLAGS = [
     "-Wall", "-Wno-unused-function",
 ]
 CXX_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-Wall", "-Wextra"]
+# per-source additions: the measurement kernels keep MFMA accumulators in
+# ordinary VGPRs (the default puts the matrix loop's in AGPRs with copies
+# between iterations, which would measure the copies)
+HIP_FLAGS_FOR = {"measure.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _hip_runtime_dir():
@@ -62,7 +66,8 @@ def build(verbose=False):
     jobs = []
     for src in sorted(glob.glob(os.path.join(CSRC, "*.hip"))):
         obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
-        jobs.append([hipcc, "-x", "hip", "-c", src, "-o", obj, "-I", INCLUDE, "-I", CSRC] + HIP_FLAGS)
+        jobs.append([hipcc, "-x", "hip", "-c", src, "-o", obj, "-I", INCLUDE, "-I", CSRC] + HIP_FLAGS
+                    + HIP_FLAGS_FOR.get(os.path.basename(src), []))
     for src in sorted(glob.glob(os.path.join(CSRC, "*.cpp"))):
         obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
         jobs.append(["g++", "-c", src, "-o", obj, "-I", INCLUDE, "-I", CSRC] + CXX_FLAGS)

@@ -110,6 +110,15 @@ def test_device_calls_reject_bad_arguments_before_launch():
     assert lib.pkv_paged_kv_append(null, null, null, null, null, 0, 1, 64, 16, 4, 2, null) == 0
     assert lib.pkv_paged_attention_decode(null, null, null, null, null, 0, 4, 4, 128, 16, 8, 64,
                                           100, 1.0, 0, null, null, 0, 2, null) == 0
+    # measurement aids: sizes and the sink are checked before any launch
+    assert lib.pkv_stream_read(null, 24, 64, null, null) == 1      # not a multiple of 16
+    assert lib.pkv_stream_read(null, 64, 0, null, null) == 1       # no workgroups
+    assert lib.pkv_stream_read(null, 0, 64, null, null) == 0       # nothing to read
+    assert lib.pkv_matrix_loop(-1, 64, null, null) == 1
+    assert lib.pkv_matrix_loop(10, 0, null, null) == 1
+    assert lib.pkv_matrix_loop(10, (1 << 20) + 1, null, null) == 1
+    assert lib.pkv_matrix_loop(10, 64, null, null) == 1            # NULL sink
+    assert b"NULL" in lib.pkv_last_error()
 
 
 def test_shared_blocks_hint_is_checked_like_the_dtype_it_rides_on():

@@ -230,3 +230,15 @@ def test_full_size_shared_prefix_prefill():
     log("full-size prefill, all", w.chunk, "rows of", len(pick), "sequences: max abs err",
         max(errs))
     assert max(errs) <= TOL[w.dtype]
+
+
+@pytest.mark.gpu
+def test_matrix_loop_runs_and_counts_its_flops():
+    """The matrix-core ceiling bench.py reports next to the prefill: the
+    launch completes, reports the operations it performs, and leaves the
+    sink alone (its products never equal the guard value)."""
+    sink = torch.zeros(1, dtype=torch.float32, device=DEV)
+    flops = pkv.matrix_loop(100, 8, sink)
+    torch.cuda.synchronize()
+    assert flops == 8 * 4 * 100 * 4 * 16 * 16 * 32 * 2
+    assert sink.item() == 0.0
