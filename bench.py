@@ -595,7 +595,9 @@ def fp8_leg(args, torch, pkv, workloads):
     the same batch in its 16-bit dtype.  Each is timed as partials + merge
     on a fixed cache state (HIP events on the stream, mean over the timed
     calls after the warm-up); bytes are the KV bytes each cache holds for
-    the batch (1 byte per element for the 8-bit cache)."""
+    the batch (1 byte per element for the 8-bit cache).  Then the causal
+    chunked prefill over each cache: every sequence's last min(512, length)
+    tokens as its chunk."""
     dev = torch.device("cuda:0")
     w = workloads.get(args.workload)
     ks, vs = workloads.FP8_SCALES
@@ -675,12 +677,46 @@ def fp8_leg(args, torch, pkv, workloads):
                      "kernel_gbps": round(nbytes / (kern * 1e-3) / 1e9, 1),
                      "kernel_hbm_peak_frac": round(nbytes / (kern * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                      "tokens_per_s": round(b / (both * 1e-3), 1)}
-        del kc, vc, alloc
+
+        # causal chunked prefill over the same cache: each sequence's last
+        # min(512, length) cached tokens as its chunk (their K/V already in
+        # the cache), random queries; mean of 10 launches after 2
+        c_b = np.minimum(lh.astype(np.int64), 512)
+        cu_h = np.concatenate([[0], np.cumsum(c_b)]).astype(np.int32)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(w.seed + 9)
+        qp = (torch.randn((int(cu_h[-1]), w.num_heads, w.head_dim), generator=gen, device=dev)
+              * w.std).to(w.dtype)
+        cu = torch.from_numpy(cu_h).to(dev)
+        outp = torch.empty((int(cu_h[-1]), w.num_heads, w.head_dim), dtype=torch.float32,
+                           device=dev)
+        mq = int(c_b.max())
+
+        def prefill():
+            if kind == "fp8_e4m3":
+                pkv.paged_attention_prefill_fp8(qp, kc, vc, tables, lens, cu, w.scale, ks, vs, mq,
+                                                out=outp)
+            else:
+                pkv.paged_attention_prefill(qp, kc, vc, tables, lens, cu, w.scale, mq, out=outp)
+
+        pms = time_loop(torch, stream, prefill, 10, warm=2)
+        if not torch.isfinite(outp).all():
+            raise RuntimeError("prefill produced non-finite output")
+        keys = int(np.sum(c_b * (lh.astype(np.int64) - c_b) + c_b * (c_b + 1) // 2))
+        pflops = 4.0 * w.head_dim * w.num_heads * keys
+        res[kind]["prefill"] = {"rows": int(cu_h[-1]), "ms": round(pms, 4),
+                                "tflops": round(pflops / (pms * 1e-3) / 1e12, 1),
+                                "bf16_peak_frac": round(pflops / (pms * 1e-3) / 1e12
+                                                        / BF16_PEAK_TFLOPS, 4),
+                                "flops_per_launch": pflops}
+        del kc, vc, alloc, qp, outp
         torch.cuda.empty_cache()
     k8, k16 = res["fp8_e4m3"], res[DTYPE_NAMES[str(w.dtype)]]
     print(json.dumps({"leg": "fp8_kv_cache", "workload": w.name, "k_scale": ks, "v_scale": vs,
                       "steps": args.steps, "warmup": args.warmup, "caches": res,
-                      "decode_speedup_vs_16bit": round(k16["decode_us"] / k8["decode_us"], 3)}),
+                      "decode_speedup_vs_16bit": round(k16["decode_us"] / k8["decode_us"], 3),
+                      "prefill_speedup_vs_16bit": round(k16["prefill"]["ms"] / k8["prefill"]["ms"],
+                                                        3)}),
           flush=True)
 
 
