@@ -1,6 +1,6 @@
 // Measurement aid: a plain streaming read of device memory, the achievable
 // HBM read rate that the decode kernel's fraction of the published peak is
-// judged against.  The KV-cache article (intelliparadigm, §2.1) has the
+// read against.  The KV-cache article (intelliparadigm, §2.1) has the
 // paged kernel hide the cost of gathering non-contiguous pages; how close
 // the decode comes to a contiguous read of the same bytes is what that
 // costs on this GPU.

@@ -203,7 +203,7 @@ def logical_kv_fp8(w, segments, k_scale, v_scale):
 
 def host_threads():
     """Worker threads for the oracle on the host: the cores this process may
-    use, at most 16 (a GPU machine's share of its host)."""
+    use, at most 16 (the share of a shared host that one GPU gets)."""
     import os
     return max(1, min(16, len(os.sched_getaffinity(0))))
 
